@@ -1,0 +1,163 @@
+/*
+ * vla.h - C ABI of the MI355X (gfx950) Variational Linear Attention scan.
+ *
+ * The library exports two compute entry points:
+ *
+ *   vla_scan_forward  the VLA recurrence scan over a sequence, per (batch, head)
+ *   vla_project_u     the learned penalty directions u = normalize(W_u k_raw)
+ *
+ * plus parameter, workspace and status helpers.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers (memory on the current HIP device)
+ *   unless a comment says otherwise.  The caller owns every buffer; the library
+ *   never allocates, frees or retains device memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Work is enqueued asynchronously on it; no call synchronises the host,
+ *   except vla_scan_forward with `validate` set (documented there).
+ * - Layouts are row-major with the feature dimension contiguous.
+ * - Errors: every argument and shape check happens before anything is
+ *   launched.  A failed check returns VLA_EINVAL or VLA_EUNSUPPORTED and
+ *   writes nothing.  A failed launch returns VLA_EHIP.  Faults inside a kernel
+ *   surface at the caller's next synchronisation, as usual for HIP.  No C++
+ *   exception crosses this interface.  vla_last_error() gives a thread-local
+ *   message for the last failure on the calling thread.
+ * - Calls are thread-safe; calls on different streams may overlap.
+ */
+#ifndef VLA_H_
+#define VLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VLA_ABI_VERSION 1
+
+typedef enum {
+  VLA_OK = 0,
+  VLA_EINVAL = 1,        /* bad argument (null pointer, negative size, inconsistent shape) */
+  VLA_EUNSUPPORTED = 2,  /* well-formed but outside the supported set (d, r, dtype) */
+  VLA_EWORKSPACE = 3,    /* workspace missing or smaller than vla_scan_workspace_size() */
+  VLA_ENONFINITE = 4,    /* validate was set and an input holds NaN or Inf */
+  VLA_EHIP = 5           /* a HIP runtime call failed */
+} vla_status_t;
+
+typedef enum { VLA_F32 = 0, VLA_BF16 = 1 } vla_dtype_t;
+
+typedef enum {
+  VLA_SCHEDULE_AUTO = 0,        /* library picks */
+  VLA_SCHEDULE_SEQUENTIAL = 1   /* one workgroup owns a (batch, head) chain for the whole sequence */
+} vla_schedule_t;
+
+/* Parameters of one scan call.  Fill with vla_scan_params_init() first. */
+typedef struct {
+  int32_t B, H;          /* batch and heads: B*H independent chains */
+  int32_t T;             /* tokens in this call (0 copies the state through) */
+  int32_t d;             /* head dimension: 16, 32, 64 or 128 */
+  int32_t r;             /* penalty directions per token (Woodbury rank): 1..4 */
+  vla_dtype_t in_dtype;  /* storage of q, k, v, u and of the output o */
+  float eps;             /* guard threshold and nudge size (default 1e-6) */
+  int32_t nudge_period;  /* eps*I added to A every nudge_period tokens; 0 = off */
+  float s_cap;           /* Frobenius cap on S; <= 0 or +inf = off */
+  float den_eps;         /* readout denominator epsilon (default 1e-6) */
+  int64_t t0;            /* global index of this call's first token (nudge phase, resume) */
+  int32_t schedule;      /* vla_schedule_t */
+  int32_t validate;      /* nonzero: synchronous NaN/Inf pre-check of the inputs */
+} vla_scan_params_t;
+
+/* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
+ * den_eps = 1e-6, t0 = 0, automatic schedule, no validation. Host pointer. */
+void vla_scan_params_init(vla_scan_params_t* p);
+
+/* Bytes of device workspace vla_scan_forward needs for these parameters
+ * (host pointers in and out).  Zero for the sequential schedule. */
+vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
+
+/*
+ * vla_scan_forward: the VLA recurrence, sequential over tokens, independent
+ * per (batch, head) chain.
+ *
+ * Sources: "Mathematical Primitives" (VLA documentation), section 2
+ * (Sherman-Morrison rank-1 inverse tracking: z = A u, delta = 1 + u.z, the
+ * |delta| < eps guard that injects eps*I, A <- A - z z^T / delta, periodic
+ * eps*I spectrum stabilisation), section 3 (rank r as r sequential rank-1
+ * updates), section 4 (alpha_t = A_t k_t), section 5 (S_t = S_{t-1} + v alpha^T
+ * and Frobenius renormalisation of S); "Variational Linear Attention (VLA)"
+ * README, v3 notes (ELU+1 features applied upstream, normalised alpha, z.q
+ * readout denominator).
+ *
+ * Per chain, for each token t (tau = t0 + t + 1, 1-based):
+ *   for i = 1..r:  z = A u_{t,i};  delta = 1 + u_{t,i}.z
+ *                  if |delta| < eps:  A += eps*I  (update skipped, counted)
+ *                  else:              A -= z z^T / delta
+ *   if nudge_period > 0 and tau % nudge_period == 0:  A += eps*I
+ *   alpha = A k_t;  alpha_hat = alpha / max(|alpha|_2, 1)
+ *   S += v_t alpha_hat^T                      (S is [value, key])
+ *   if cap on and |S|_F > s_cap:  S *= s_cap / |S|_F   (counted)
+ *   n += k_t;  o_t = S q_t / (n.q_t + den_eps)
+ *
+ * Arguments (device pointers):
+ *   q, k, v  [B, H, T, d] in in_dtype, contiguous.  q and k are the positive
+ *            (ELU+1) features; the library does not apply the feature map.
+ *   u        [B, H, T, r, d] in in_dtype, contiguous; u[..., t, i, :] is the
+ *            i-th direction of token t, applied in index order.
+ *   A0, S0   [B, H, d, d] float32, n0 [B, H, d] float32: initial state.  Each
+ *            may be NULL, meaning I, 0 and 0 respectively.
+ *   o        [B, H, T, d] in in_dtype (written).
+ *   A_T, S_T [B, H, d, d] float32 and n_T [B, H, d] float32: final state
+ *            (written).  They may alias A0, S0, n0 exactly (in-place state
+ *            carry); no other aliasing is allowed.
+ *   stats    [B, H, 4] int32 or NULL: guard fires, cap fires, non-finite flag
+ *            (1 if any output or final state of the chain is NaN/Inf), and the
+ *            0-based index of the first cap fire in this call (-1 if none).
+ *   workspace, workspace_bytes: device scratch of at least
+ *            vla_scan_workspace_size() bytes (may be NULL when that is 0).
+ * State is float32 throughout; products accumulate in float32.
+ *
+ * With validate != 0 the call first checks q, k, v, u for NaN/Inf on the
+ * stream, synchronises the stream, and returns VLA_ENONFINITE (having
+ * launched nothing else) if any is found.
+ */
+vla_status_t vla_scan_forward(const vla_scan_params_t* p,
+                              const void* q, const void* k, const void* v, const void* u,
+                              const float* A0, const float* S0, const float* n0,
+                              void* o, float* A_T, float* S_T, float* n_T, int32_t* stats,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vla_project_u: learned penalty directions, u_{row, i} = normalize(W_u[i] k_raw[row]).
+ *
+ * Source: "Variational Linear Attention (VLA)" README, v3 notes item 2
+ * (u_t = normalize(W_u k_t^raw)).  normalize(x) = x / max(|x|_2, 1e-12).
+ *
+ *   rows      number of key rows (e.g. B*H*T), >= 0
+ *   d         head dimension (16, 32, 64 or 128); r directions (1..4)
+ *   in_dtype  storage of W_u and k_raw; out_dtype storage of u
+ *   W_u       [r, d, d] device pointer, row-major; applied as W_u[i] @ k_raw
+ *   k_raw     [rows, d] device pointer
+ *   u         [rows, r, d] device pointer (written)
+ * Products accumulate in float32 on the matrix cores; the norm, the scale and
+ * the final cast are float32.
+ */
+vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dtype,
+                           vla_dtype_t out_dtype, const void* W_u, const void* k_raw,
+                           void* u, void* stream);
+
+/* Static string naming a status code. */
+const char* vla_status_string(vla_status_t s);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char* vla_last_error(void);
+
+/* VLA_ABI_VERSION of the built library. */
+int vla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLA_H_ */

@@ -1,0 +1,118 @@
+"""Python front end of the VLA scan library (argument marshalling only).
+
+Torch provides device memory and the current HIP stream; every step of the
+scan and of the projection runs in the HIP kernels of libvla.so, called
+through the C ABI (``_lib``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.VLA_F32, torch.bfloat16: _lib.VLA_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("VLA tensors must live on a HIP device")
+
+
+def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
+                schedule="auto", validate=False) -> _lib.ScanParams:
+    p = _lib.ScanParams()
+    _lib.load().vla_scan_params_init(ctypes.byref(p))
+    p.B, p.H, p.T, p.d, p.r = B, H, T, d, r
+    p.in_dtype = _DT[dtype]
+    p.eps = eps
+    p.nudge_period = nudge_period
+    p.s_cap = 0.0 if (s_cap is None or not math.isfinite(s_cap) or s_cap <= 0) else float(s_cap)
+    p.den_eps = den_eps
+    p.t0 = t0
+    p.schedule = {"auto": _lib.VLA_SCHEDULE_AUTO, "sequential": _lib.VLA_SCHEDULE_SEQUENTIAL}[schedule]
+    p.validate = 1 if validate else 0
+    return p
+
+
+def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0, s_cap=None,
+                 den_eps=1e-6, t0=0, schedule="auto", validate=False, out=None):
+    """Run vla_scan_forward.
+
+    q, k, v: [B, H, T, d]; u: [B, H, T, r, d], all float32 or all bfloat16 on
+    the device.  A0, S0 [B, H, d, d] and n0 [B, H, d] are float32 or None.
+    ``out`` may pass preallocated (o, A_T, S_T, n_T, stats) tensors.
+    Returns (o, A_T, S_T, n_T, stats).
+    """
+    _need_cuda(q, k, v, u, A0, S0, n0)
+    B, H, T, d = q.shape
+    r = u.shape[3]
+    dt = q.dtype
+    if dt not in _DT or any(x.dtype != dt for x in (k, v, u)):
+        raise ValueError("q, k, v, u must share one dtype: float32 or bfloat16")
+    if k.shape != q.shape or v.shape != q.shape or tuple(u.shape) != (B, H, T, r, d):
+        raise ValueError("shape mismatch among q, k, v, u")
+    for t in (q, k, v, u):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    for t, shp in ((A0, (B, H, d, d)), (S0, (B, H, d, d)), (n0, (B, H, d))):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("A0/S0/n0 must be contiguous float32 of shape [B,H,d,d]/[B,H,d,d]/[B,H,d]")
+    dev = q.device
+    if out is None:
+        o = torch.empty_like(q)
+        A_T = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+        S_T = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+        n_T = torch.empty((B, H, d), device=dev, dtype=torch.float32)
+        stats = torch.empty((B, H, 4), device=dev, dtype=torch.int32)
+    else:
+        o, A_T, S_T, n_T, stats = out
+    p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
+                    t0=t0, schedule=schedule, validate=validate)
+    lib = _lib.load()
+    ws_bytes = ctypes.c_size_t(0)
+    _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    ws = torch.empty(max(ws_bytes.value, 1), device=dev, dtype=torch.uint8) if ws_bytes.value else None
+    with torch.cuda.device(dev):
+        _lib.check(lib.vla_scan_forward(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(A0), _ptr(S0), _ptr(n0),
+            _ptr(o), _ptr(A_T), _ptr(S_T), _ptr(n_T), _ptr(stats), _ptr(ws), ws_bytes.value,
+            _stream_ptr(dev)))
+    return o, A_T, S_T, n_T, stats
+
+
+def project_u(W_u, k_raw, out_dtype=None, out=None):
+    """Run vla_project_u: u[..., i, :] = normalize(W_u[i] @ k_raw[...]).
+
+    W_u: [r, d, d]; k_raw: [..., d] (same dtype, float32 or bfloat16).
+    Returns u: [..., r, d] in ``out_dtype`` (default: the input dtype).
+    """
+    _need_cuda(W_u, k_raw)
+    if W_u.dim() != 3 or W_u.shape[1] != W_u.shape[2] or k_raw.shape[-1] != W_u.shape[2]:
+        raise ValueError("W_u must be [r, d, d] and k_raw [..., d]")
+    if W_u.dtype not in _DT or k_raw.dtype != W_u.dtype:
+        raise ValueError("W_u and k_raw must share one dtype: float32 or bfloat16")
+    if not (W_u.is_contiguous() and k_raw.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    r, d = W_u.shape[0], W_u.shape[1]
+    rows = k_raw.numel() // d
+    odt = out_dtype or W_u.dtype
+    if out is None:
+        out = torch.empty(tuple(k_raw.shape[:-1]) + (r, d), device=k_raw.device, dtype=odt)
+    lib = _lib.load()
+    with torch.cuda.device(k_raw.device):
+        _lib.check(lib.vla_project_u(rows, d, r, _DT[W_u.dtype], _DT[odt], _ptr(W_u), _ptr(k_raw), _ptr(out),
+                                     _stream_ptr(k_raw.device)))
+    return out

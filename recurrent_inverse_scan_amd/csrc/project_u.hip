@@ -1,0 +1,194 @@
+// Penalty-direction projection u_{row,i} = normalize(W_u[i] k_raw[row]) on the
+// gfx950 matrix cores.
+//
+// Source: "Variational Linear Attention (VLA)" README, v3 notes item 2
+// (u_t = normalize(W_u k_t^raw)); normalize(x) = x / max(|x|_2, 1e-12).
+//
+// As a GEMM: Out[rows, r*d] = K_raw[rows, d] . W^T with W = W_u viewed as
+// [r*d, d]; K = d is short, so the kernel is bound by streaming k_raw in and
+// u out of HBM.  Each wave computes 32 rows x d columns of one direction with
+// 32x32 MFMA tiles (bf16: 32x32x16, fp32: 32x32x2, both accumulating in
+// fp32), keeps its k_raw rows in registers across the r directions, and
+// normalises in the epilogue: a row's d outputs live in the 32 lanes of one
+// half-wave (one column each, d/32 tiles), so its sum of squares is a
+// 32-lane reduction.
+//
+// MFMA 32x32 accumulator layout: lane l holds column l % 32 of the tile and,
+// in accumulator slot a, row 8*(a/4) + 4*(l/32) + a%4.  Operand A holds row
+// l % 32 and operand B column l % 32; both take the same k slice per lane, so
+// the k assignment inside a lane only has to agree between A and B.
+#include "vla_common.h"
+#include "vla_kernels.h"
+
+namespace vla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kProjWaves = 4;
+
+template <typename TOut>
+__device__ __forceinline__ void store_out(TOut* p, float x) { Elem<TOut>::store(p, x); }
+
+// Sum over the 32 lanes of each half-wave.
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x = group_sum<16>(x);
+  return x + __shfl_xor(x, 16, 64);
+}
+
+template <int D, typename TOut>
+__device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_base, int64_t rows, int r,
+                                            int i, int lane, TOut* u) {
+  const int col = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    float ss = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) ss = fmaf(acc[nb][s], acc[nb][s], ss);
+    ss = half_wave_sum(ss);
+    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+    const int64_t row = row_base + 8 * (s / 4) + 4 * hi + (s % 4);
+    if (row < rows) {
+      TOut* dst = u + (row * r + i) * D;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) store_out(dst + nb * 32 + col, acc[nb][s] * inv);
+    }
+  }
+}
+
+// bf16 inputs: v_mfma_f32_32x32x16_bf16, 8 bf16 of k per lane per tile.
+template <int D, typename TOut>
+__global__ void __launch_bounds__(64 * kProjWaves)
+project_u_bf16_kernel(int64_t rows, int r, const uint16_t* __restrict__ W, const uint16_t* __restrict__ kraw,
+                      TOut* __restrict__ u) {
+  constexpr int KB = D / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row_base = (static_cast<int64_t>(blockIdx.x) * kProjWaves + w) * 32;
+  const int64_t arow = row_base + (lane & 31);
+  const int koff = 8 * (lane >> 5);
+
+  bf16x8 a[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (arow < rows) x = *reinterpret_cast<const uint4*>(kraw + arow * D + kb * 16 + koff);
+    a[kb] = __builtin_bit_cast(bf16x8, x);
+  }
+  for (int i = 0; i < r; ++i) {
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      acc[nb] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const uint16_t* wrow = W + (static_cast<int64_t>(i) * D + nb * 32 + (lane & 31)) * D + koff;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + kb * 16));
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b, acc[nb], 0, 0, 0);
+      }
+    }
+    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u);
+  }
+}
+
+// fp32 inputs: v_mfma_f32_32x32x2_f32, one float of k per lane per tile.
+template <int D, typename TOut>
+__global__ void __launch_bounds__(64 * kProjWaves)
+project_u_f32_kernel(int64_t rows, int r, const float* __restrict__ W, const float* __restrict__ kraw,
+                     TOut* __restrict__ u) {
+  constexpr int KB = D / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row_base = (static_cast<int64_t>(blockIdx.x) * kProjWaves + w) * 32;
+  const int64_t arow = row_base + (lane & 31);
+  const int koff = lane >> 5;
+
+  float a[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) a[kb] = (arow < rows) ? kraw[arow * D + 2 * kb + koff] : 0.f;
+  for (int i = 0; i < r; ++i) {
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      acc[nb] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const float* wrow = W + (static_cast<int64_t>(i) * D + nb * 32 + (lane & 31)) * D + koff;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[kb], wrow[2 * kb], acc[nb], 0, 0, 0);
+    }
+    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u);
+  }
+}
+
+// d = 16 is narrower than one 32-column tile: plain fp32 FMAs, one row per
+// thread (the tiny head size only appears in small parity workloads).
+template <typename TIn, typename TOut>
+__global__ void __launch_bounds__(256)
+project_u_d16_kernel(int64_t rows, int r, const TIn* __restrict__ W, const TIn* __restrict__ kraw,
+                     TOut* __restrict__ u) {
+  constexpr int D = 16;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= rows) return;
+  float kv[D];
+#pragma unroll
+  for (int m = 0; m < D; ++m) kv[m] = Elem<TIn>::load(kraw + row * D + m);
+  for (int i = 0; i < r; ++i) {
+    float x[D];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < D; ++m) acc = fmaf(Elem<TIn>::load(W + (i * D + j) * D + m), kv[m], acc);
+      x[j] = acc;
+      ss = fmaf(acc, acc, ss);
+    }
+    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+    for (int j = 0; j < D; ++j) Elem<TOut>::store(u + (row * r + i) * D + j, x[j] * inv);
+  }
+}
+
+template <typename TIn, typename TOut, int D>
+hipError_t launch_proj(int64_t rows, int r, const void* W, const void* kraw, void* u, hipStream_t s) {
+  if constexpr (D == 16) {
+    const unsigned grid = static_cast<unsigned>((rows + 255) / 256);
+    hipLaunchKernelGGL((project_u_d16_kernel<TIn, TOut>), dim3(grid), dim3(256), 0, s, rows, r,
+                       static_cast<const TIn*>(W), static_cast<const TIn*>(kraw), static_cast<TOut*>(u));
+  } else {
+    const unsigned grid = static_cast<unsigned>((rows + 32 * kProjWaves - 1) / (32 * kProjWaves));
+    if constexpr (sizeof(TIn) == 2) {
+      hipLaunchKernelGGL((project_u_bf16_kernel<D, TOut>), dim3(grid), dim3(64 * kProjWaves), 0, s, rows, r,
+                         static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(kraw), static_cast<TOut*>(u));
+    } else {
+      hipLaunchKernelGGL((project_u_f32_kernel<D, TOut>), dim3(grid), dim3(64 * kProjWaves), 0, s, rows, r,
+                         static_cast<const float*>(W), static_cast<const float*>(kraw), static_cast<TOut*>(u));
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t dispatch_proj(int64_t rows, int d, int r, const void* W, const void* kraw, void* u, hipStream_t s) {
+  switch (d) {
+    case 16: return launch_proj<TIn, TOut, 16>(rows, r, W, kraw, u, s);
+    case 32: return launch_proj<TIn, TOut, 32>(rows, r, W, kraw, u, s);
+    case 64: return launch_proj<TIn, TOut, 64>(rows, r, W, kraw, u, s);
+    case 128: return launch_proj<TIn, TOut, 128>(rows, r, W, kraw, u, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_bf16, const void* W,
+                            const void* kraw, void* u, hipStream_t s) {
+  if (in_bf16) {
+    return out_bf16 ? dispatch_proj<uint16_t, uint16_t>(rows, d, r, W, kraw, u, s)
+                    : dispatch_proj<uint16_t, float>(rows, d, r, W, kraw, u, s);
+  }
+  return out_bf16 ? dispatch_proj<float, uint16_t>(rows, d, r, W, kraw, u, s)
+                  : dispatch_proj<float, float>(rows, d, r, W, kraw, u, s);
+}
+
+}  // namespace vla

@@ -1,0 +1,223 @@
+// C ABI of the VLA scan library: argument validation and kernel dispatch.
+// Every check runs before any launch; nothing here allocates device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/vla.h"
+#include "vla_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+vla_status_t fail(vla_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+vla_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(VLA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t dtype_size(vla_dtype_t t) { return t == VLA_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// True when byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// An output may alias its own input exactly, and must not partly overlap
+// anything else it is checked against.
+bool bad_alias(const void* out, size_t n_out, const void* in, size_t n_in, bool exact_ok) {
+  if (exact_ok && out == in) return false;
+  return overlap(out, n_out, in, n_in);
+}
+
+constexpr size_t kValidateBytes = 256;
+
+vla_status_t check_params(const vla_scan_params_t* p) {
+  if (!p) return fail(VLA_EINVAL, "params is NULL");
+  if (p->B < 0 || p->H < 0 || p->T < 0)
+    return fail(VLA_EINVAL, "B, H, T must be >= 0 (got %d, %d, %d)", p->B, p->H, p->T);
+  if (!supported_d(p->d)) return fail(VLA_EUNSUPPORTED, "d = %d unsupported (16, 32, 64, 128)", p->d);
+  if (p->r < 1 || p->r > 4) return fail(VLA_EUNSUPPORTED, "r = %d unsupported (1..4)", p->r);
+  if (p->in_dtype != VLA_F32 && p->in_dtype != VLA_BF16)
+    return fail(VLA_EUNSUPPORTED, "in_dtype %d unsupported", static_cast<int>(p->in_dtype));
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return fail(VLA_EINVAL, "eps must be finite and >= 0");
+  if (p->nudge_period < 0) return fail(VLA_EINVAL, "nudge_period must be >= 0");
+  if (!std::isfinite(p->den_eps)) return fail(VLA_EINVAL, "den_eps must be finite");
+  if (std::isnan(p->s_cap)) return fail(VLA_EINVAL, "s_cap is NaN");
+  if (p->t0 < 0) return fail(VLA_EINVAL, "t0 must be >= 0");
+  if (p->schedule != VLA_SCHEDULE_AUTO && p->schedule != VLA_SCHEDULE_SEQUENTIAL)
+    return fail(VLA_EUNSUPPORTED, "schedule %d unsupported", p->schedule);
+  const int64_t chains = static_cast<int64_t>(p->B) * p->H;
+  if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
+  return VLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void vla_scan_params_init(vla_scan_params_t* p) {
+  if (!p) return;
+  std::memset(p, 0, sizeof(*p));
+  p->d = 64;
+  p->r = 1;
+  p->in_dtype = VLA_F32;
+  p->eps = 1e-6f;
+  p->nudge_period = 0;
+  p->s_cap = 0.f;
+  p->den_eps = 1e-6f;
+  p->t0 = 0;
+  p->schedule = VLA_SCHEDULE_AUTO;
+  p->validate = 0;
+}
+
+vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(VLA_EINVAL, "bytes is NULL");
+  const vla_status_t s = check_params(p);
+  if (s != VLA_OK) return s;
+  *bytes = p->validate ? kValidateBytes : 0;
+  return VLA_OK;
+}
+
+vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const void* k, const void* v,
+                              const void* u, const float* A0, const float* S0, const float* n0, void* o,
+                              float* A_T, float* S_T, float* n_T, int32_t* stats, void* workspace,
+                              size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  vla_status_t s = check_params(p);
+  if (s != VLA_OK) return s;
+  const int64_t chains = static_cast<int64_t>(p->B) * p->H;
+  const int d = p->d, r = p->r;
+  const size_t es = dtype_size(p->in_dtype);
+  const size_t n_tok = static_cast<size_t>(chains) * static_cast<size_t>(p->T);
+  const size_t b_seq = n_tok * d * es, b_u = b_seq * r;
+  const size_t b_mat = static_cast<size_t>(chains) * d * d * sizeof(float);
+  const size_t b_vec = static_cast<size_t>(chains) * d * sizeof(float);
+  if (static_cast<uint64_t>(n_tok) * r * d > (1ull << 62)) return fail(VLA_EUNSUPPORTED, "problem too large");
+
+  if (chains == 0) return VLA_OK;
+  if (n_tok > 0 && (!q || !k || !v || !u || !o)) return fail(VLA_EINVAL, "q, k, v, u and o must be non-NULL");
+  if (!A_T || !S_T || !n_T) return fail(VLA_EINVAL, "A_T, S_T and n_T must be non-NULL");
+  const void* seq[5] = {q, k, v, u, o};
+  for (const void* x : seq)
+    if (n_tok > 0 && !aligned(x, 16)) return fail(VLA_EINVAL, "q, k, v, u, o must be 16-byte aligned");
+  if (!aligned(A0, 16) || !aligned(S0, 16) || !aligned(A_T, 16) || !aligned(S_T, 16))
+    return fail(VLA_EINVAL, "A0, S0, A_T, S_T must be 16-byte aligned");
+  if (!aligned(n0, 4) || !aligned(n_T, 4)) return fail(VLA_EINVAL, "n0, n_T must be 4-byte aligned");
+
+  // Aliasing: outputs may alias only their own initial state, exactly.
+  const struct { const void* p; size_t n; } ins[] = {{q, b_seq}, {k, b_seq}, {v, b_seq}, {u, b_u}};
+  const struct { const void* p; size_t n; const void* own; } outs[] = {
+      {o, b_seq, nullptr}, {A_T, b_mat, A0}, {S_T, b_mat, S0}, {n_T, b_vec, n0},
+      {stats, static_cast<size_t>(chains) * 16, nullptr}};
+  const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
+  for (int oi = 0; oi < n_outs; ++oi) {
+    const auto& ot = outs[oi];
+    if (!ot.p) continue;
+    for (const auto& in : ins)
+      if (bad_alias(ot.p, ot.n, in.p, in.n, false)) return fail(VLA_EINVAL, "an output overlaps q, k, v or u");
+    const struct { const void* p; size_t n; } st[] = {{A0, b_mat}, {S0, b_mat}, {n0, b_vec}};
+    for (const auto& sx : st)
+      if (bad_alias(ot.p, ot.n, sx.p, sx.n, ot.own == sx.p)) return fail(VLA_EINVAL, "outputs overlap the state");
+    for (int oj = oi + 1; oj < n_outs; ++oj)
+      if (overlap(ot.p, ot.n, outs[oj].p, outs[oj].n)) return fail(VLA_EINVAL, "outputs overlap each other");
+  }
+
+  size_t need = 0;
+  vla_scan_workspace_size(p, &need);
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned(workspace, 16))))
+    return fail(VLA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const bool bf16 = p->in_dtype == VLA_BF16;
+
+  if (p->validate && n_tok > 0) {
+    int32_t* flag = static_cast<int32_t*>(workspace);
+    hipError_t e = vla::launch_clear_flag(flag, stream);
+    if (e != hipSuccess) return hip_fail(e, "validate");
+    const int64_t n_seq = static_cast<int64_t>(n_tok) * d;
+    const void* bufs[4] = {q, k, v, u};
+    for (int i = 0; i < 4; ++i) {
+      e = vla::launch_nonfinite_check(bufs[i], i == 3 ? n_seq * r : n_seq, bf16, flag, stream);
+      if (e != hipSuccess) return hip_fail(e, "validate");
+    }
+    int32_t host_flag = 0;
+    e = hipMemcpyAsync(&host_flag, flag, sizeof(host_flag), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "validate");
+    if (host_flag) return fail(VLA_ENONFINITE, "an input holds NaN or Inf");
+  }
+
+  vla::ScanArgs a{};
+  a.q = q; a.k = k; a.v = v; a.u = u;
+  a.A0 = A0; a.S0 = S0; a.n0 = n0;
+  a.o = o; a.A_T = A_T; a.S_T = S_T; a.n_T = n_T; a.stats = stats;
+  a.T = p->T; a.r = r; a.eps = p->eps;
+  a.nudge_period = p->nudge_period;
+  a.nudge_phase0 = p->nudge_period > 0 ? static_cast<int32_t>((p->t0 + 1) % p->nudge_period) : 0;
+  a.cap_on = (p->s_cap > 0.f && std::isfinite(p->s_cap)) ? 1 : 0;
+  a.cap = a.cap_on ? p->s_cap : 0.f;
+  a.den_eps = p->den_eps;
+  const hipError_t e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), stream);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  return VLA_OK;
+}
+
+vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dtype, vla_dtype_t out_dtype,
+                           const void* W_u, const void* k_raw, void* u, void* stream_ptr) {
+  g_last_error.clear();
+  if (rows < 0) return fail(VLA_EINVAL, "rows must be >= 0");
+  if (!supported_d(d)) return fail(VLA_EUNSUPPORTED, "d = %d unsupported (16, 32, 64, 128)", d);
+  if (r < 1 || r > 4) return fail(VLA_EUNSUPPORTED, "r = %d unsupported (1..4)", r);
+  if ((in_dtype != VLA_F32 && in_dtype != VLA_BF16) || (out_dtype != VLA_F32 && out_dtype != VLA_BF16))
+    return fail(VLA_EUNSUPPORTED, "dtype unsupported");
+  if (rows == 0) return VLA_OK;
+  if (!W_u || !k_raw || !u) return fail(VLA_EINVAL, "W_u, k_raw and u must be non-NULL");
+  if (!aligned(W_u, 16) || !aligned(k_raw, 16) || !aligned(u, 16))
+    return fail(VLA_EINVAL, "W_u, k_raw and u must be 16-byte aligned");
+  const size_t b_in = dtype_size(in_dtype), b_out = dtype_size(out_dtype);
+  if (overlap(u, static_cast<size_t>(rows) * r * d * b_out, k_raw, static_cast<size_t>(rows) * d * b_in) ||
+      overlap(u, static_cast<size_t>(rows) * r * d * b_out, W_u, static_cast<size_t>(r) * d * d * b_in))
+    return fail(VLA_EINVAL, "u overlaps its inputs");
+  const hipError_t e = vla::launch_project_u(rows, d, r, in_dtype == VLA_BF16, out_dtype == VLA_BF16, W_u, k_raw,
+                                             u, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return VLA_OK;
+}
+
+const char* vla_status_string(vla_status_t s) {
+  switch (s) {
+    case VLA_OK: return "VLA_OK";
+    case VLA_EINVAL: return "VLA_EINVAL";
+    case VLA_EUNSUPPORTED: return "VLA_EUNSUPPORTED";
+    case VLA_EWORKSPACE: return "VLA_EWORKSPACE";
+    case VLA_ENONFINITE: return "VLA_ENONFINITE";
+    case VLA_EHIP: return "VLA_EHIP";
+  }
+  return "VLA_UNKNOWN";
+}
+
+const char* vla_last_error(void) { return g_last_error.c_str(); }
+
+int vla_abi_version(void) { return VLA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Shared device helpers for the VLA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vla {
+
+// ---- bfloat16 storage: raw 16-bit patterns ---------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kPer16B = 8;
+  __device__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ---- cross-lane reductions (DPP within rows of 16 lanes) -------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16
+
+// Sum over groups of G consecutive lanes (G = 4, 8 or 16); every lane of a
+// group receives the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  if constexpr (G >= 2) x += dpp_read<kQuadSwap1>(x);
+  if constexpr (G >= 4) x += dpp_read<kQuadSwap2>(x);
+  if constexpr (G >= 8) x += dpp_read<kRowHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp_read<kRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Sum over the whole wave; the result is wave-uniform and identical on every
+// wave that reduces the same values (fixed order).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
+}
+
+}  // namespace vla

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP scan and projection against the fp64 CPU oracle.
+
+Every case calls libvla.so through the C ABI (recurrent_inverse_scan_amd.api)
+and compares element by element with the oracle on the same seeded inputs.
+The bar is the normwise relative error (per output row, per state matrix):
+2e-3 for float32 storage, 1e-2 for bfloat16 storage.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from recurrent_inverse_scan_amd import CONFIGS, project_u, scan_forward
+from recurrent_inverse_scan_amd._lib import VLAError, VLA_ENONFINITE
+from tests.parity import TOL, case, flat, oracle_u, rel_err, run_oracle, to64
+from oracle.vla_oracle import oracle_project_u, oracle_scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _gpu(x, cfg, **kw):
+    args = dict(nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+    args.update(kw)
+    o, A, S, n, st = scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["u"].to(DEV), **args)
+    torch.cuda.synchronize()
+    return o, A, S, n, st
+
+
+def _check(cfg, out, ref, chains=None, tol=None):
+    tol = tol or TOL[cfg.in_dtype]
+    o, A, S, n, st = out
+    errs = {
+        "o": rel_err(flat(o, cfg, chains), ref["o"]),
+        "A": rel_err(flat(A, cfg, chains), ref["A"], axes=(-2, -1)),
+        "S": rel_err(flat(S, cfg, chains), ref["S"], axes=(-2, -1)),
+        "n": rel_err(flat(n, cfg, chains), ref["n"]),
+    }
+    _say(f"{cfg.name} B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} r={cfg.r} {cfg.in_dtype}: {errs}")
+    assert all(v <= tol for v in errs.values()), errs
+    st = flat(st, cfg, chains).cpu().numpy()
+    np.testing.assert_array_equal(st[:, 0], ref["guard_fires"])
+    assert (st[:, 2] == ref["nonfinite"]).all()
+    return errs, st
+
+
+# Reduced sizes that the oracle finishes in seconds but that still span several
+# LDS stages and a ragged tail (T not a multiple of the stage length).
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "base": CONFIGS["base"].with_(B=2, H=3, T=1029),
+    "recall": CONFIGS["recall"].with_(B=4, H=8),
+    "long": CONFIGS["long"].with_(B=1, H=3, T=2053, nudge_period=64, s_cap=40.0),
+    "wide": CONFIGS["wide"].with_(B=1, H=3, T=517, nudge_period=32),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_scan_parity_small(name):
+    cfg = SMALL[name]
+    _say(f"case small/{name}")
+    x = case(cfg)
+    out = _gpu(x, cfg)
+    ref = run_oracle(x, cfg)
+    _, st = _check(cfg, out, ref)
+    if cfg.s_cap:
+        # cap decisions may differ only where |S|_F is within rounding of the cap
+        assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_parity_shapes(d, r, dtype):
+    cfg = CONFIGS["base"].with_(name=f"shape-d{d}-r{r}", B=1, H=2, T=37, d=d, r=r, in_dtype=dtype,
+                                nudge_period=5, s_cap=6.0)
+    x = case(cfg, seed=d * 10 + r)
+    out = _gpu(x, cfg)
+    _check(cfg, out, run_oracle(x, cfg))
+
+
+@pytest.mark.parametrize("T", [0, 1, 7, 8, 9])
+def test_scan_edge_lengths(T):
+    cfg = CONFIGS["base"].with_(name=f"len{T}", B=1, H=2, T=T, nudge_period=3, s_cap=5.0)
+    x = case(cfg, seed=T)
+    g = torch.Generator().manual_seed(T)
+    A0 = torch.eye(cfg.d).expand(1, 2, cfg.d, cfg.d) * 0.5 + 0.01 * torch.randn(1, 2, cfg.d, cfg.d, generator=g)
+    A0 = ((A0 + A0.transpose(-1, -2)) / 2).contiguous()
+    S0 = torch.randn(1, 2, cfg.d, cfg.d, generator=g)
+    n0 = torch.rand(1, 2, cfg.d, generator=g)
+    out = _gpu(x, cfg, A0=A0.to(DEV), S0=S0.to(DEV), n0=n0.to(DEV), t0=5)
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, cfg.d, cfg.d), S0=S0.reshape(2, cfg.d, cfg.d),
+                     n0=n0.reshape(2, cfg.d), t0=5)
+    _check(cfg, out, ref)
+    if T == 0:
+        assert torch.equal(out[1].cpu(), A0) and torch.equal(out[2].cpu(), S0) and torch.equal(out[3].cpu(), n0)
+
+
+def test_guard_fire_householder_start():
+    """A0 = I - 2 u u^T with u the first direction: delta = 0 exactly, the guard fires."""
+    cfg = CONFIGS["base"].with_(name="guard", B=1, H=2, T=20, nudge_period=0, s_cap=None)
+    x = case(cfg, seed=3)
+    u = x["u"].clone()
+    e = torch.zeros(cfg.d)
+    e[5] = 1.0
+    u[:, :, 0, 0, :] = e
+    x["u"] = u
+    A0 = (torch.eye(cfg.d) - 2 * torch.outer(e, e)).expand(1, 2, cfg.d, cfg.d).contiguous()
+    out = _gpu(x, cfg, A0=A0.to(DEV))
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, cfg.d, cfg.d))
+    assert (ref["guard_fires"] == 1).all()
+    _check(cfg, out, ref)
+
+
+def test_cap_forced_every_step():
+    cfg = CONFIGS["base"].with_(name="cap1", B=1, H=2, T=50, nudge_period=0, s_cap=1.0)
+    x = case(cfg, seed=4)
+    out = _gpu(x, cfg)
+    ref = run_oracle(x, cfg)
+    _, st = _check(cfg, out, ref)
+    assert (st[:, 1] == cfg.T).all() and (st[:, 3] == 0).all()
+    assert (np.linalg.norm(to64(out[2]), axis=(-2, -1)) <= 1.0 + 1e-5).all()
+
+
+def test_resume_and_in_place_state_carry():
+    cfg = CONFIGS["base"].with_(name="resume", B=1, H=2, T=200)
+    x = case(cfg, seed=5)
+    full = _gpu(x, cfg)
+    T1 = 77
+    q, k, v, u = (x[n].to(DEV) for n in ("q", "k", "v", "u"))
+    o1, A, S, n, _ = scan_forward(q[:, :, :T1].contiguous(), k[:, :, :T1].contiguous(), v[:, :, :T1].contiguous(),
+                                  u[:, :, :T1].contiguous(), nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+    st = torch.empty((1, 2, 4), dtype=torch.int32, device=DEV)
+    o2 = torch.empty_like(q[:, :, T1:])
+    scan_forward(q[:, :, T1:].contiguous(), k[:, :, T1:].contiguous(), v[:, :, T1:].contiguous(),
+                 u[:, :, T1:].contiguous(), A, S, n, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, t0=T1,
+                 out=(o2, A, S, n, st))
+    torch.cuda.synchronize()
+    ref = run_oracle(x, cfg)
+    assert rel_err(torch.cat([o1, o2], dim=2).reshape(2, cfg.T, cfg.d), ref["o"]) <= 2e-3
+    assert rel_err(A.reshape(2, cfg.d, cfg.d), ref["A"], axes=(-2, -1)) <= 2e-3
+    assert rel_err(S.reshape(2, cfg.d, cfg.d), ref["S"], axes=(-2, -1)) <= 2e-3
+    # split and unsplit runs agree closely (same arithmetic, state round-tripped through HBM)
+    assert rel_err(torch.cat([o1, o2], dim=2), to64(full[0])) <= 1e-5
+
+
+def test_nonfinite_flag_and_validate():
+    cfg = CONFIGS["base"].with_(name="nan", B=1, H=2, T=40)
+    x = case(cfg, seed=6)
+    v = x["v"].clone()
+    v[0, 1, 10, 3] = float("nan")
+    x["v"] = v
+    out = _gpu(x, cfg)
+    st = out[4].cpu().numpy().reshape(2, 4)
+    assert list(st[:, 2]) == [0, 1]
+    with pytest.raises(VLAError) as ei:
+        scan_forward(x["q"].to(DEV), x["k"].to(DEV), v.to(DEV), x["u"].to(DEV), validate=True)
+    assert ei.value.status == VLA_ENONFINITE
+    clean = case(cfg, seed=6)
+    scan_forward(clean["q"].to(DEV), clean["k"].to(DEV), clean["v"].to(DEV), clean["u"].to(DEV), validate=True)
+
+
+def test_bitwise_repeatable():
+    cfg = CONFIGS["base"].with_(name="repeat", B=2, H=2, T=300)
+    x = case(cfg, seed=7)
+    a = _gpu(x, cfg)
+    b = _gpu(x, cfg)
+    for p, q_ in zip(a, b):
+        assert torch.equal(p, q_)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("r", [1, 4])
+@pytest.mark.parametrize("din,dout", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16")])
+def test_project_u_parity(d, r, din, dout):
+    g = torch.Generator().manual_seed(d + r)
+    rows = 1000 + 37   # several 128-row workgroups and a ragged tail
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    W = (torch.randn(r, d, d, generator=g) / d ** 0.5).to(dt[din])
+    kr = torch.randn(rows, d, generator=g).to(dt[din])
+    kr[3] = 0.0        # a zero row stays zero
+    u = project_u(W.to(DEV), kr.to(DEV), out_dtype=dt[dout])
+    torch.cuda.synchronize()
+    ref = oracle_project_u(W, kr)
+    tol = 2e-3 if dout == "f32" else 1e-2
+    err = rel_err(u.reshape(rows * r, d), ref.reshape(rows * r, d))
+    _say(f"project d={d} r={r} {din}->{dout}: {err}")
+    assert err <= (1e-5 if (din, dout) == ("f32", "f32") else tol)
+    assert (u[3] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times (GPU
+# projection then scan on all chains); the oracle runs on sampled chains.
+# ---------------------------------------------------------------------------
+FULL_SAMPLES = {"tiny": None, "base": [0, 31], "recall": [0, 511], "long": [0, 15], "wide": [0, 127]}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_full_size_sampled_chains(name):
+    cfg = CONFIGS[name]
+    chains = FULL_SAMPLES[name]
+    _say(f"case full/{name} chains={chains}")
+    from recurrent_inverse_scan_amd import make_inputs
+
+    x = make_inputs(cfg, seed=0)
+    u = project_u(x["W_u"].to(DEV), x["k_raw"].to(DEV))
+    o, A, S, n, st = scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), u,
+                                  nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+    torch.cuda.synchronize()
+    C = cfg.B * cfg.H
+    sel = list(range(C)) if chains is None else chains
+    kr = x["k_raw"].reshape(C, cfg.T, cfg.d)[sel]
+    u_ref = oracle_project_u(x["W_u"], kr.reshape(-1, cfg.d))
+    u_ref = torch.from_numpy(u_ref).to(x["q"].dtype).reshape(len(sel), cfg.T, cfg.r, cfg.d)
+    ref = oracle_scan(x["q"].reshape(C, cfg.T, cfg.d)[sel], x["k"].reshape(C, cfg.T, cfg.d)[sel],
+                      x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
+                      s_cap=cfg.s_cap)
+    _check(cfg, (o, A, S, n, st), ref, chains=sel)
