@@ -50,7 +50,9 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1 } vla_dtype_t;
 
 typedef enum {
   VLA_SCHEDULE_AUTO = 0,        /* library picks */
-  VLA_SCHEDULE_SEQUENTIAL = 1   /* one workgroup owns a (batch, head) chain for the whole sequence */
+  VLA_SCHEDULE_SEQUENTIAL = 1,  /* one workgroup owns a (batch, head) chain for the whole sequence */
+  VLA_SCHEDULE_CHUNKED = 2      /* time-parallel inverse pass over chunks, then a per-chain state
+                                   pass (d = 64; needs workspace; see vla_scan_forward) */
 } vla_schedule_t;
 
 /* Parameters of one scan call.  Fill with vla_scan_params_init() first. */
@@ -67,14 +69,17 @@ typedef struct {
   int64_t t0;            /* global index of this call's first token (nudge phase, resume) */
   int32_t schedule;      /* vla_schedule_t */
   int32_t validate;      /* nonzero: synchronous NaN/Inf pre-check of the inputs */
+  int32_t chunk_len;     /* tokens per chunk of the chunked schedule; 0 = library picks */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
- * den_eps = 1e-6, t0 = 0, automatic schedule, no validation. Host pointer. */
+ * den_eps = 1e-6, t0 = 0, automatic schedule, no validation, chunk_len = 0.
+ * Host pointer. */
 void vla_scan_params_init(vla_scan_params_t* p);
 
 /* Bytes of device workspace vla_scan_forward needs for these parameters
- * (host pointers in and out).  Zero for the sequential schedule. */
+ * (host pointers in and out), for the schedule the call would use.  Zero for
+ * the sequential schedule without validation. */
 vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
 
 /*
@@ -117,6 +122,19 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  *   workspace, workspace_bytes: device scratch of at least
  *            vla_scan_workspace_size() bytes (may be NULL when that is 0).
  * State is float32 throughout; products accumulate in float32.
+ *
+ * Schedules.  SEQUENTIAL runs each chain in one workgroup, token after token.
+ * CHUNKED (d = 64) splits the tokens into chunks of chunk_len: while no guard
+ * fires, A_t is the inverse of the accumulated penalty M_t = A0^{-1} + sum
+ * u u^T ("Mathematical Primitives", section 2), so each chunk's starting
+ * inverse follows in parallel from per-chunk Gram matrices (in float64,
+ * carrying the nudges exactly), the inverse recurrence of every chunk runs in
+ * parallel, and a per-chain pass applies the state update, cap and readout.
+ * A chain where the guard fires, or whose chunk-start inverse is not
+ * positive definite, is recomputed sequentially in the same call, so the
+ * result does not depend on the schedule beyond float32 rounding.  CHUNKED
+ * needs chunk_len to divide nudge_period (when nonzero) and t0; AUTO uses it
+ * for d = 64 when there are few chains and long sequences.
  *
  * With validate != 0 the call first checks q, k, v, u for NaN/Inf on the
  * stream, synchronises the stream, and returns VLA_ENONFINITE (having

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libvla.so")
 
 VLA_OK, VLA_EINVAL, VLA_EUNSUPPORTED, VLA_EWORKSPACE, VLA_ENONFINITE, VLA_EHIP = range(6)
 VLA_F32, VLA_BF16 = 0, 1
-VLA_SCHEDULE_AUTO, VLA_SCHEDULE_SEQUENTIAL = 0, 1
+VLA_SCHEDULE_AUTO, VLA_SCHEDULE_SEQUENTIAL, VLA_SCHEDULE_CHUNKED = 0, 1, 2
 
 # Every symbol include/vla.h declares.
 EXPORTED = (
@@ -35,6 +35,7 @@ class ScanParams(ctypes.Structure):
         ("t0", ctypes.c_int64),
         ("schedule", ctypes.c_int32),
         ("validate", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
     ]
 
 

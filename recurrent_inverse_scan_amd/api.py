@@ -32,7 +32,7 @@ def _need_cuda(*ts):
 
 
 def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
-                schedule="auto", validate=False) -> _lib.ScanParams:
+                schedule="auto", validate=False, chunk_len=0) -> _lib.ScanParams:
     p = _lib.ScanParams()
     _lib.load().vla_scan_params_init(ctypes.byref(p))
     p.B, p.H, p.T, p.d, p.r = B, H, T, d, r
@@ -42,19 +42,23 @@ def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, d
     p.s_cap = 0.0 if (s_cap is None or not math.isfinite(s_cap) or s_cap <= 0) else float(s_cap)
     p.den_eps = den_eps
     p.t0 = t0
-    p.schedule = {"auto": _lib.VLA_SCHEDULE_AUTO, "sequential": _lib.VLA_SCHEDULE_SEQUENTIAL}[schedule]
+    p.schedule = {"auto": _lib.VLA_SCHEDULE_AUTO, "sequential": _lib.VLA_SCHEDULE_SEQUENTIAL,
+                  "chunked": _lib.VLA_SCHEDULE_CHUNKED}[schedule]
     p.validate = 1 if validate else 0
+    p.chunk_len = chunk_len
     return p
 
 
 def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0, s_cap=None,
-                 den_eps=1e-6, t0=0, schedule="auto", validate=False, out=None):
+                 den_eps=1e-6, t0=0, schedule="auto", validate=False, chunk_len=0, out=None, workspace=None):
     """Run vla_scan_forward.
 
     q, k, v: [B, H, T, d]; u: [B, H, T, r, d], all float32 or all bfloat16 on
     the device.  A0, S0 [B, H, d, d] and n0 [B, H, d] are float32 or None.
-    ``out`` may pass preallocated (o, A_T, S_T, n_T, stats) tensors.
-    Returns (o, A_T, S_T, n_T, stats).
+    ``schedule`` is "auto", "sequential" or "chunked"; ``chunk_len`` 0 lets
+    the library pick.  ``out`` may pass preallocated (o, A_T, S_T, n_T,
+    stats) tensors and ``workspace`` a preallocated uint8 device buffer of at
+    least ``workspace_size(...)`` bytes.  Returns (o, A_T, S_T, n_T, stats).
     """
     _need_cuda(q, k, v, u, A0, S0, n0)
     B, H, T, d = q.shape
@@ -80,17 +84,28 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     else:
         o, A_T, S_T, n_T, stats = out
     p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
-                    t0=t0, schedule=schedule, validate=validate)
+                    t0=t0, schedule=schedule, validate=validate, chunk_len=chunk_len)
     lib = _lib.load()
     ws_bytes = ctypes.c_size_t(0)
     _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
-    ws = torch.empty(max(ws_bytes.value, 1), device=dev, dtype=torch.uint8) if ws_bytes.value else None
+    ws = workspace
+    if ws_bytes.value and (ws is None or ws.numel() < ws_bytes.value):
+        ws = torch.empty(ws_bytes.value, device=dev, dtype=torch.uint8)
     with torch.cuda.device(dev):
         _lib.check(lib.vla_scan_forward(
             ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(A0), _ptr(S0), _ptr(n0),
-            _ptr(o), _ptr(A_T), _ptr(S_T), _ptr(n_T), _ptr(stats), _ptr(ws), ws_bytes.value,
+            _ptr(o), _ptr(A_T), _ptr(S_T), _ptr(n_T), _ptr(stats), _ptr(ws) if ws_bytes.value else None,
+            ws_bytes.value,
             _stream_ptr(dev)))
     return o, A_T, S_T, n_T, stats
+
+
+def workspace_size(B, H, T, d, r, dtype, **kw) -> int:
+    """Bytes of workspace vla_scan_forward needs (keyword arguments as scan_forward)."""
+    p = make_params(B, H, T, d, r, dtype, **kw)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
 
 
 def project_u(W_u, k_raw, out_dtype=None, out=None):

@@ -1,0 +1,338 @@
+// Time-parallel ("chunked") schedule of the VLA inverse recurrence, d = 64.
+//
+// The pages fuse all T steps in one launch and mention a parallel
+// Blelloch-style formulation ("Variational Linear Attention: Stable
+// Associative Memory for Long-Context Transformers", technical summary 2.4).
+// This schedule is exact in exact arithmetic and built on the structure of
+// the penalty matrix ("Mathematical Primitives", section 2, theoretical
+// derivation): while no guard fires, A_t = M_t^{-1} with M_t = M_{t-1} +
+// u_t u_t^T, so the penalty over a chunk of L tokens adds the Gram matrix
+// G_c = sum u u^T.  The periodic nudge A <- A + eps*I is not additive in M;
+// writing A = N D^{-1}, both steps are linear in (N, D):
+//     rank-1 update:  D <- D + u u^T N
+//     nudge:          N <- N + eps D
+// so each chain carries (N, D) across chunks with one d x d x d product per
+// nudge period, and every chunk-start inverse A_c = N_p (D_p + Gpre_c N_p)^{-1}
+// follows in parallel.  From A_c, the existing sequential inverse recurrence
+// runs each chunk independently (kInverseOnly mode).
+//
+// Kernels, in stream order:
+//   vla_chunk_gram_kernel   G_c for every chunk (MFMA, fp32 accumulation)
+//   vla_chunk_chain_kernel  per chain, sequential over chunks, fp64: prefix
+//                           sums of G inside a nudge period, (N, D) at every
+//                           period start
+//   vla_chunk_start_kernel  per chunk, fp64: A_c by Gauss-Jordan elimination
+//                           of [ D_c^T | N_p^T ]; a non-positive pivot flags
+//                           the chain for the sequential fallback
+#include "vla_common.h"
+#include "vla_kernels.h"
+#include "vla_seq.h"
+
+namespace vla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 64;            // head dimension of this schedule
+constexpr int kChunkThreads = 256;
+
+__global__ void snapshot_kernel(const float* __restrict__ A0, const float* __restrict__ S0,
+                                const float* __restrict__ n0, float* __restrict__ A_copy,
+                                float* __restrict__ S_copy, float* __restrict__ n_copy,
+                                int32_t* __restrict__ chain_info, int64_t chains) {
+  const int64_t mat = chains * kD * kD;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < mat;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = i % (kD * kD);
+    A_copy[i] = A0 ? A0[i] : ((e / kD) == (e % kD) ? 1.f : 0.f);
+    S_copy[i] = S0 ? S0[i] : 0.f;
+    if (i < chains * kD) n_copy[i] = n0 ? n0[i] : 0.f;
+    if (i < chains * 4) chain_info[i] = 0;
+  }
+}
+
+// Period index of chunk c: the number of nudges at the ends of chunks < c.
+// Chunk c ends at global token index t0 + (c+1)L, so with o = t0/L and
+// q = P/L a nudge follows chunk c' when (o + c' + 1) % q == 0.
+__device__ __forceinline__ int period_of(int c, int o, int q) {
+  return q > 0 ? (o + c) / q - o / q : 0;
+}
+
+// ---- Gram matrices ---------------------------------------------------------
+// One workgroup per (chain, chunk); wave w accumulates 32x32 tiles of
+// G = U^T U, U the chunk's rows of u ([L*r, 64], contiguous).
+template <typename TIn>
+__global__ void __launch_bounds__(kChunkThreads)
+vla_chunk_gram_kernel(const TIn* __restrict__ u, float* __restrict__ G, int T, int r, int L, int nchunks) {
+  const int64_t chain = blockIdx.x / nchunks;
+  const int c = blockIdx.x % nchunks;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t_lo = c * L, t_hi = min(T, t_lo + L);
+  const int nrows = (t_hi - t_lo) * r;
+  const TIn* U = u + (chain * T + t_lo) * static_cast<int64_t>(r) * kD;
+  const int ib = w >> 1, jb = w & 1;     // 4 waves, 2x2 tiles
+  const int fa = ib * 32 + (lane & 31), fb = jb * 32 + (lane & 31);
+  f32x16 acc = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(TIn) == 2) {
+    const int koff = 8 * (lane >> 5);
+    for (int k0 = 0; k0 < nrows; k0 += 16) {
+      uint16_t av[8], bv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + koff + e;
+        const bool ok = k < nrows;
+        av[e] = ok ? U[static_cast<int64_t>(k) * kD + fa] : uint16_t(0);
+        bv[e] = ok ? U[static_cast<int64_t>(k) * kD + fb] : uint16_t(0);
+      }
+      const uint4 ap = make_uint4(av[0] | (uint32_t(av[1]) << 16), av[2] | (uint32_t(av[3]) << 16),
+                                  av[4] | (uint32_t(av[5]) << 16), av[6] | (uint32_t(av[7]) << 16));
+      const uint4 bp = make_uint4(bv[0] | (uint32_t(bv[1]) << 16), bv[2] | (uint32_t(bv[3]) << 16),
+                                  bv[4] | (uint32_t(bv[5]) << 16), bv[6] | (uint32_t(bv[7]) << 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, bp),
+                                                     acc, 0, 0, 0);
+    }
+  } else {
+    const int koff = lane >> 5;
+    for (int k0 = 0; k0 < nrows; k0 += 2) {
+      const int k = k0 + koff;
+      const bool ok = k < nrows;
+      const float a = ok ? U[static_cast<int64_t>(k) * kD + fa] : 0.f;
+      const float b = ok ? U[static_cast<int64_t>(k) * kD + fb] : 0.f;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+  }
+  float* g = G + (chain * nchunks + c) * kD * kD;
+  const int col = jb * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int row = ib * 32 + 8 * (s / 4) + 4 * (lane >> 5) + (s % 4);
+    g[row * kD + col] = acc[s];
+  }
+}
+
+// ---- (N, D) chain ---------------------------------------------------------
+// One workgroup per chain, 256 threads, thread t owns the 4x4 block
+// (t/16, t%16) of N, D and the running Gram prefix.
+__global__ void __launch_bounds__(kChunkThreads)
+vla_chunk_chain_kernel(const float* __restrict__ G, const float* __restrict__ A0, double* __restrict__ Gpre,
+                       double* __restrict__ ND, int nchunks, int nperiods, int o, int q, double eps) {
+  __shared__ double sG[kD * kD];   // Gram prefix, transposed: sG[m*kD + i] = Gacc[i][m]
+  __shared__ double sN[kD * kD];
+  const int64_t chain = blockIdx.x;
+  const int t = threadIdx.x, bi = t >> 4, bj = t & 15;
+  double N[4][4], Dm[4][4], Ga[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gi = 4 * bi + i, gj = 4 * bj + j;
+      N[i][j] = static_cast<double>(A0[(chain * kD + gi) * kD + gj]);
+      Dm[i][j] = gi == gj ? 1.0 : 0.0;
+      Ga[i][j] = 0.0;
+    }
+  auto store_nd = [&](int p) {
+    double* nd = ND + (chain * nperiods + p) * 2 * kD * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        nd[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
+        nd[kD * kD + (4 * bi + i) * kD + 4 * bj + j] = Dm[i][j];
+      }
+  };
+  store_nd(0);
+  int p = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    double* gp = Gpre + (chain * nchunks + c) * kD * kD;
+    const float* gc = G + (chain * nchunks + c) * kD * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = (4 * bi + i) * kD + 4 * bj + j;
+        gp[idx] = Ga[i][j];
+        Ga[i][j] += static_cast<double>(gc[idx]);
+      }
+    if (c + 1 < nchunks && q > 0 && (o + c + 1) % q == 0) {
+      // D += Gacc N, then the nudge N += eps D; a new period starts.
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sG[(4 * bj + j) * kD + 4 * bi + i] = Ga[i][j];
+          sN[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
+        }
+      __syncthreads();
+      for (int m = 0; m < kD; ++m) {
+        double gcol[4], nrow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gcol[i] = sG[m * kD + 4 * bi + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nrow[j] = sN[m * kD + 4 * bj + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Dm[i][j] = fma(gcol[i], nrow[j], Dm[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          N[i][j] = fma(eps, Dm[i][j], N[i][j]);
+          Ga[i][j] = 0.0;
+        }
+      ++p;
+      store_nd(p);
+    }
+  }
+}
+
+// ---- chunk-start inverses ---------------------------------------------------
+// One workgroup per (chain, chunk).  D_c = D_p + Gpre_c N_p, then Gauss-Jordan
+// elimination without pivoting turns [ D_c^T | N_p^T ] (64 x 128, thread t
+// owning rows 4*(t/16).. and columns 8*(t%16)..) into [ I | A_c^T ].
+__global__ void __launch_bounds__(kChunkThreads)
+vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
+                       int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q) {
+  // 64 KiB of LDS: Gpre^T and N_p for the product; afterwards the pivot row
+  // and column buffers reuse the N_p half, and the result block the first half.
+  __shared__ double smem[2 * kD * kD];
+  double* sA = smem;
+  double* sB = smem + kD * kD;
+  double (*rowbuf)[2 * kD] = reinterpret_cast<double (*)[2 * kD]>(sB);
+  double (*colbuf)[kD] = reinterpret_cast<double (*)[kD]>(sB + 4 * kD);
+  const int64_t chain = blockIdx.x / nchunks;
+  const int c = blockIdx.x % nchunks;
+  const int p = period_of(c, o, q);
+  const int t = threadIdx.x, rb = t >> 4, cb = t & 15;
+  const double* Np = ND + (chain * nperiods + p) * 2 * kD * kD;
+  const double* Dp = Np + kD * kD;
+  const double* gp = Gpre + (chain * nchunks + c) * kD * kD;
+
+  for (int e = t; e < kD * kD; e += kChunkThreads) {
+    const int i = e / kD, j = e % kD;
+    sA[j * kD + i] = gp[e];
+    sB[e] = Np[e];
+  }
+  __syncthreads();
+
+  // W[i][j] for i in 4rb..4rb+3, j in 8cb..8cb+7.
+  double W[4][8];
+  if (cb < 8) {
+    // Left block: W[i][j] = D_c[j][i] = D_p[j][i] + sum_m Gpre[j][m] N_p[m][i].
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = Dp[(8 * cb + jj) * kD + 4 * rb + ii];
+    for (int m = 0; m < kD; ++m) {
+      double gv[8], nv[4];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) gv[jj] = sA[m * kD + 8 * cb + jj];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) nv[ii] = sB[m * kD + 4 * rb + ii];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(gv[jj], nv[ii], W[ii][jj]);
+    }
+  } else {
+    // Right block: W[i][64 + j] = N_p[j][i].
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = sB[(8 * (cb - 8) + jj) * kD + 4 * rb + ii];
+  }
+
+  __syncthreads();   // every thread is done reading sB before it holds pivots
+  bool ok = true;
+  for (int k = 0; k < kD; ++k) {
+    const int par = k & 1;
+    if (rb == (k >> 2)) {
+      // Row k & 3 of this thread's block, selected without dynamic indexing.
+      double rowv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        rowv[jj] = W[0][jj];
+#pragma unroll
+        for (int ii = 1; ii < 4; ++ii) rowv[jj] = ((k & 3) == ii) ? W[ii][jj] : rowv[jj];
+        rowbuf[par][8 * cb + jj] = rowv[jj];
+      }
+    }
+    if (cb == (k >> 3)) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        double cv = W[ii][0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) cv = ((k & 7) == jj) ? W[ii][jj] : cv;
+        colbuf[par][4 * rb + ii] = cv;
+      }
+    }
+    __syncthreads();
+    const double piv = rowbuf[par][k];
+    ok = ok && (piv > 0.0) && isfinite(piv);
+    const double inv = 1.0 / piv;
+    double rv[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][8 * cb + jj] * inv;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * rb + ii;
+      if (i == k) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = rv[jj];
+      } else {
+        const double f = colbuf[par][i];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(-f, rv[jj], W[ii][jj]);
+      }
+    }
+  }
+  if (!ok && t == 0) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
+
+  // Symmetrise the result block (A_c^T, equal to A_c in exact arithmetic).
+  __syncthreads();
+  if (cb >= 8) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sA[(4 * rb + ii) * kD + 8 * (cb - 8) + jj] = W[ii][jj];
+  }
+  __syncthreads();
+  float* ac = Ac + (chain * nchunks + c) * kD * kD;
+  for (int e = t; e < kD * kD; e += kChunkThreads) {
+    const int i = e / kD, j = e % kD;
+    ac[e] = static_cast<float>(0.5 * (sA[i * kD + j] + sA[j * kD + i]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const float* S0, const float* n0,
+                                 const void* u, bool bf16, hipStream_t stream) {
+  const int64_t mat = static_cast<int64_t>(pl.chains) * kD * kD;
+  const int64_t want = (mat + 255) / 256;
+  const unsigned sgrid = static_cast<unsigned>(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(snapshot_kernel, dim3(sgrid), dim3(256), 0, stream, A0, S0, n0, pl.A_init, pl.S_init,
+                     pl.n_init, pl.chain_info, static_cast<int64_t>(pl.chains));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned units = static_cast<unsigned>(pl.chains * pl.nchunks);
+  if (bf16)
+    hipLaunchKernelGGL(vla_chunk_gram_kernel<uint16_t>, dim3(units), dim3(kChunkThreads), 0, stream,
+                       static_cast<const uint16_t*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
+  else
+    hipLaunchKernelGGL(vla_chunk_gram_kernel<float>, dim3(units), dim3(kChunkThreads), 0, stream,
+                       static_cast<const float*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains), dim3(kChunkThreads), 0, stream, pl.G, pl.A_init,
+                     pl.Gpre, pl.ND, pl.nchunks, pl.nperiods, pl.o, pl.q, static_cast<double>(pl.eps));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(units), dim3(kChunkThreads), 0, stream, pl.Gpre, pl.ND, pl.Ac,
+                     pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q);
+  return hipGetLastError();
+}
+
+}  // namespace vla

@@ -1,9 +1,9 @@
-// Sequential-schedule VLA scan kernel for gfx950 (CDNA4, wave64).
+// Sequential VLA scan kernels for gfx950 (CDNA4, wave64).
 //
 // One workgroup owns one (batch, head) chain for a run of tokens, starting
-// from a given state (A, S, n) and ending by writing the final state.  The
-// tracked inverse A and the fast-weight state S stay in registers for the
-// whole run; q, k, v, u stream through a double-buffered LDS stage.
+// from a given state and ending by writing the final state.  The tracked
+// inverse A and the fast-weight state S stay in registers for the whole run;
+// the per-token vectors stream through a double-buffered LDS stage.
 //
 // Method ("Mathematical Primitives", sections 2-5; "Variational Linear
 // Attention (VLA)" README, v3 notes): per token, r guarded Sherman-Morrison
@@ -11,13 +11,22 @@
 // norm <= 1, S += v alpha_hat^T, the Frobenius cap, n += k and the readout
 // o = S q / (n.q + den_eps).
 //
+// Three modes share this code:
+//  * kFull: the whole recurrence (the sequential schedule, and the per-chain
+//    fallback of the time-parallel schedule, gated by a per-chain flag);
+//  * kInverseOnly: the inverse recurrence of one chunk of tokens, started
+//    from the chunk-start inverse the time-parallel schedule computed, and
+//    writing alpha_hat (one workgroup per chunk);
+//  * kStateOnly: only the S/n recurrence, cap and readout, reading that
+//    alpha_hat (one workgroup per chain).
+//
 // Register layout.  The NW waves of a workgroup split the d rows of A and S
 // into slabs of RW = d/NW rows.  Inside a wave, lane = rg*CG + cg: the lane
 // owns R = RW/(64/CG) consecutive rows and C = d/CG columns, the columns
 // interleaved in float4 blocks, j = (m*CG + cg)*4 + e.  A row of a matrix
-// vector product is therefore split over the CG lanes of a row group and
-// summed with DPP; the column-indexed vectors every lane needs (u, k, q, z,
-// alpha) are read from LDS, conflict-free, as float4 blocks.
+// vector product is split over the CG lanes of a row group and summed with
+// DPP; the column-indexed vectors every lane needs (u, k, q, z, alpha) are
+// read from LDS, conflict-free, as float4 blocks.
 //
 // Fusion: the first matrix-vector sweep of a token computes both z = A u_r
 // and y = A k (same A), and alpha = A_t k follows as y - z (z.k)/delta (or
@@ -25,345 +34,293 @@
 // (product and update) instead of three times.
 #include "vla_common.h"
 #include "vla_kernels.h"
+#include "vla_seq.h"
 
 namespace vla {
 
-namespace {
-
-constexpr int kMaxStageVecs = 8;   // 16-byte staging registers per thread
-
-template <int D, int NW, int CG>
-struct Layout {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int RW = D / NW;    // rows per wave
-  static constexpr int RG = 64 / CG;   // row groups per wave
-  static constexpr int R = RW / RG;    // rows per lane
-  static constexpr int C = D / CG;     // columns per lane
-  static_assert(RW % RG == 0 && R >= 1, "each lane needs at least one row");
-  static_assert(C % 4 == 0, "columns come in float4 blocks");
-};
-
-// Reads this lane's C columns of an LDS vector.
-template <int D, int CG, int C>
-__device__ __forceinline__ void lds_cols(const float* vec, int cg, float (&out)[C]) {
-#pragma unroll
-  for (int m = 0; m < C / 4; ++m) {
-    const float4 x = *reinterpret_cast<const float4*>(vec + (m * CG + cg) * 4);
-    out[4 * m + 0] = x.x; out[4 * m + 1] = x.y; out[4 * m + 2] = x.z; out[4 * m + 3] = x.w;
-  }
-}
-
-// Reads this lane's R consecutive rows of an LDS vector.
-template <int R>
-__device__ __forceinline__ void lds_rows(const float* vec, float (&out)[R]) {
-  if constexpr (R % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < R / 4; ++i) {
-      const float4 x = *reinterpret_cast<const float4*>(vec + 4 * i);
-      out[4 * i + 0] = x.x; out[4 * i + 1] = x.y; out[4 * i + 2] = x.z; out[4 * i + 3] = x.w;
-    }
-  } else if constexpr (R == 2) {
-    const float2 x = *reinterpret_cast<const float2*>(vec);
-    out[0] = x.x; out[1] = x.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < R; ++i) out[i] = vec[i];
-  }
-}
-
-template <int R>
-__device__ __forceinline__ void lds_store_rows(float* vec, const float (&in)[R]) {
-  if constexpr (R % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < R / 4; ++i)
-      *reinterpret_cast<float4*>(vec + 4 * i) = make_float4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
-  } else if constexpr (R == 2) {
-    *reinterpret_cast<float2*>(vec) = make_float2(in[0], in[1]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < R; ++i) vec[i] = in[i];
-  }
-}
-
-// Streams tokens of one chain from HBM into an LDS stage [TT][NV][D] of
-// float32, NV = 3 + r vectors per token (q, k, v, u_1..u_r).  Each thread
-// moves up to kMaxStageVecs 16-byte vectors; tokens at or past T read as 0.
-template <typename TIn, int D, int NTH>
-struct Stager {
-  static constexpr int EPV = Elem<TIn>::kPer16B;  // elements per 16 bytes
-  static constexpr int VPR = D / EPV;             // 16-byte vectors per row
-  uint4 reg[kMaxStageVecs];
-
-  __device__ __forceinline__ void load(const ScanArgs& a, int64_t chain, int tb, int TT, int NV, int tid) {
-    const int nvec = TT * NV * VPR;
-#pragma unroll
-    for (int j = 0; j < kMaxStageVecs; ++j) {
-      const int e = tid + j * NTH;
-      reg[j] = make_uint4(0, 0, 0, 0);
-      if (e < nvec) {
-        const int rho = e / VPR, c = e % VPR;
-        const int tt = rho / NV, vv = rho - tt * NV;
-        const int t = tb + tt;
-        if (t < a.T) {
-          const TIn* base;
-          int64_t off;
-          if (vv < 3) {
-            base = static_cast<const TIn*>(vv == 0 ? a.q : (vv == 1 ? a.k : a.v));
-            off = (chain * a.T + t) * D;
-          } else {
-            base = static_cast<const TIn*>(a.u);
-            off = ((chain * a.T + t) * a.r + (vv - 3)) * D;
-          }
-          reg[j] = *reinterpret_cast<const uint4*>(base + off + c * EPV);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(float* stage, int TT, int NV, int tid) const {
-    const int nvec = TT * NV * VPR;
-#pragma unroll
-    for (int j = 0; j < kMaxStageVecs; ++j) {
-      const int e = tid + j * NTH;
-      if (e < nvec) {
-        const int rho = e / VPR, c = e % VPR;
-        float* dst = stage + rho * D + c * EPV;
-        if constexpr (EPV == 4) {
-          *reinterpret_cast<uint4*>(dst) = reg[j];
-        } else {
-          const uint32_t w[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
-          float f[8];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            f[2 * h] = __uint_as_float(w[h] << 16);
-            f[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
-          }
-          *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
-        }
-      }
-    }
-  }
-};
-
-}  // namespace
-
-// Number of tokens per LDS stage for this (D, NW, r, dtype): one stage fits
-// the per-thread staging registers and the two stages stay within 48 KiB.
-template <typename TIn, int D, int NW>
-__host__ __device__ constexpr int stage_tokens(int r) {
-  constexpr int VPR = D / Elem<TIn>::kPer16B;
-  int cap = (kMaxStageVecs * 64 * NW) / ((3 + r) * VPR);
-  const int lds_cap = (48 * 1024) / (2 * (3 + r) * D * static_cast<int>(sizeof(float)));
-  cap = cap < lds_cap ? cap : lds_cap;
-  return cap >= 8 ? 8 : (cap < 1 ? 1 : cap);
-}
-
-template <typename TIn, int D, int NW, int CG>
+template <typename TIn, int D, int NW, int CG, SeqMode MODE>
 __global__ void __launch_bounds__(64 * NW)
-vla_scan_seq_kernel(ScanArgs a) {
-  using L = Layout<D, NW, CG>;
-  constexpr int R = L::R, C = L::C, RW = L::RW;
+vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
+  using L = TileLayout<D, NW, CG>;
+  constexpr int R = L::R, C = L::C, RW = L::RW, NTH = L::kThreads;
+  constexpr bool kFull = MODE == SeqMode::kFull;
+  constexpr bool kInv = MODE == SeqMode::kInverseOnly;
+  constexpr bool kHasA = MODE != SeqMode::kStateOnly;   // runs the inverse recurrence
+  constexpr bool kHasS = MODE != SeqMode::kInverseOnly; // runs the state recurrence
   extern __shared__ float4 smem4[];
   float* smem = reinterpret_cast<float*>(smem4);
+
+  const int64_t chain = kInv ? blockIdx.x / x.nchunks : blockIdx.x;
+  const int chunk = kInv ? static_cast<int>(blockIdx.x % x.nchunks) : 0;
+  if constexpr (kFull) {
+    if (x.only_if && x.only_if[chain * 4 + kInfoFallback] == 0) return;   // uniform per workgroup
+  }
+  // Tokens [tbeg, tend) of the chain.
+  const int tbeg = kInv ? chunk * x.chunk_len : 0;
+  const int tend = kInv ? min(a.T, tbeg + x.chunk_len) : a.T;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int cg = lane % CG, rg = lane / CG;
   const int row0 = w * RW + rg * R;
-  const int64_t chain = blockIdx.x;
-  const int r = a.r, NV = 3 + r;
-  const int TT = stage_tokens<TIn, D, NW>(r);
+  const int r = a.r;
+  const int NV = seq_rows_per_token<TIn, D, NW>(MODE, r);
+  const int TT = seq_stage_tokens<TIn, D, NW>(MODE, r);
+  // Row of each stream inside a token's stage block.
+  const int row_q = 0, row_v = 2;
+  const int row_k = kInv ? 0 : 1;
+  const int row_u = kInv ? 1 : 3;
 
-  float* stage = smem;                              // [2][TT][NV][D]
-  float* zbuf = stage + 2 * TT * NV * D;            // [2][D]
-  float* abuf = zbuf + 2 * D;                       // [2][D]
-  float* red = abuf + 2 * D;                        // [2][NW][4]
+  float* stage = smem;                                       // [2][TT][NV][D]
+  float* astage = stage + 2 * TT * NV * D;                   // [2][TT][D]   (kStateOnly)
+  float* zbuf = astage + (kHasA ? 0 : 2 * TT * D);           // [2][D]
+  float* abuf = zbuf + 2 * D;                                // [2][D]
+  float* red = abuf + 2 * D;                                 // [2][NW][4]
 
   // ---- initial state --------------------------------------------------
-  float A[R][C], S[R][C], n[R];
+  float A[kHasA ? R : 1][kHasA ? C : 4];
+  float S[kHasS ? R : 1][kHasS ? C : 4], n[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int row = row0 + i;
 #pragma unroll
     for (int m = 0; m < C / 4; ++m) {
       const int col = (m * CG + cg) * 4;
-      float4 av = make_float4(row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f,
-                              row == col + 2 ? 1.f : 0.f, row == col + 3 ? 1.f : 0.f);
-      float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (a.A0) av = *reinterpret_cast<const float4*>(a.A0 + (chain * D + row) * D + col);
-      if (a.S0) sv = *reinterpret_cast<const float4*>(a.S0 + (chain * D + row) * D + col);
-      A[i][4 * m] = av.x; A[i][4 * m + 1] = av.y; A[i][4 * m + 2] = av.z; A[i][4 * m + 3] = av.w;
-      S[i][4 * m] = sv.x; S[i][4 * m + 1] = sv.y; S[i][4 * m + 2] = sv.z; S[i][4 * m + 3] = sv.w;
+      if constexpr (kHasA) {
+        float4 av = make_float4(row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f,
+                                row == col + 2 ? 1.f : 0.f, row == col + 3 ? 1.f : 0.f);
+        if constexpr (kInv) {
+          av = *reinterpret_cast<const float4*>(x.a_start + ((chain * x.nchunks + chunk) * D + row) * D + col);
+        } else {
+          if (a.A0) av = *reinterpret_cast<const float4*>(a.A0 + (chain * D + row) * D + col);
+        }
+        A[i][4 * m] = av.x; A[i][4 * m + 1] = av.y; A[i][4 * m + 2] = av.z; A[i][4 * m + 3] = av.w;
+      }
+      if constexpr (kHasS) {
+        float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.S0) sv = *reinterpret_cast<const float4*>(a.S0 + (chain * D + row) * D + col);
+        S[i][4 * m] = sv.x; S[i][4 * m + 1] = sv.y; S[i][4 * m + 2] = sv.z; S[i][4 * m + 3] = sv.w;
+      }
     }
-    n[i] = a.n0 ? a.n0[chain * D + row] : 0.f;
+    n[i] = (kHasS && a.n0) ? a.n0[chain * D + row] : 0.f;
   }
 
   int guard_fires = 0, cap_fires = 0, first_cap = -1;
   bool bad = false;
   int par = 0;
-  int phase = a.nudge_phase0;  // (t0 + 1 + t) mod P for the current token
+  // (t0 + 1 + t) mod P for the current token t.
+  int phase = a.nudge_period > 0 ? (a.nudge_phase0 + tbeg) % a.nudge_period : 0;
   const float cap2 = a.cap * a.cap;
 
-  Stager<TIn, D, L::kThreads> st;
-  const int nstage = (a.T + TT - 1) / TT;
+  // Per-token rows in TIn (see row_*), and alpha_hat in fp32 for kStateOnly.
+  const int64_t tok0 = chain * a.T;
+  RowSource<TIn, D> src;
+  src.n = NV;
+  if constexpr (kHasS) {
+    src.nfix = 3;
+    src.fix0 = static_cast<const TIn*>(a.q) + tok0 * D;
+    src.fix1 = static_cast<const TIn*>(a.k) + tok0 * D;
+    src.fix2 = static_cast<const TIn*>(a.v) + tok0 * D;
+  } else {
+    src.nfix = 1;
+    src.fix0 = static_cast<const TIn*>(a.k) + tok0 * D;
+    src.fix1 = src.fix2 = src.fix0;
+  }
+  src.ubase = kHasA ? static_cast<const TIn*>(a.u) + tok0 * r * D : src.fix0;
+  src.ustride = static_cast<int64_t>(r) * D;
+  RowSource<float, D> asrc;
+  asrc.n = 1;
+  asrc.nfix = 1;
+  asrc.fix0 = asrc.fix1 = asrc.fix2 = asrc.ubase = kHasA ? nullptr : x.alpha + tok0 * D;
+  asrc.ustride = D;
+
+  Stager<TIn, D, NTH> st;
+  Stager<float, D, NTH> ast;
+  const int nstage = (tend - tbeg + TT - 1) / TT;
   if (nstage > 0) {
-    st.load(a, chain, 0, TT, NV, tid);
+    st.load(src, tbeg, TT, tend, tid);
     st.store(stage, TT, NV, tid);
+    if constexpr (!kHasA) {
+      ast.load(asrc, tbeg, TT, tend, tid);
+      ast.store(astage, TT, 1, tid);
+    }
   }
   __syncthreads();
 
   for (int sidx = 0; sidx < nstage; ++sidx) {
-    const int tb = sidx * TT;
-    if (sidx + 1 < nstage) st.load(a, chain, tb + TT, TT, NV, tid);
+    const int tb = tbeg + sidx * TT;
+    if (sidx + 1 < nstage) {
+      st.load(src, tb + TT, TT, tend, tid);
+      if constexpr (!kHasA) ast.load(asrc, tb + TT, TT, tend, tid);
+    }
     const float* sbuf = stage + (sidx & 1) * TT * NV * D;
-    const int tcount = min(TT, a.T - tb);
+    const int tcount = min(TT, tend - tb);
 
     for (int tt = 0; tt < tcount; ++tt) {
       const int t = tb + tt;
-      const float* tq = sbuf + (tt * NV + 0) * D;
-      const float* tk = tq + D;
-      const float* tv = tq + 2 * D;
+      const float* tblk = sbuf + tt * NV * D;
+      const float* tq = tblk + row_q * D;
+      const float* tk = tblk + row_k * D;
+      const float* tv = tblk + row_v * D;
 
       float kI[R];
       lds_rows<R>(tk + row0, kI);
-      float y[R];
-      bool last_fired = false;
+      float aJ[C];
 
-      // ---- r guarded Sherman-Morrison sub-updates -------------------------
-      for (int i = 0; i < r; ++i) {
-        const float* tu = tq + (3 + i) * D;
-        const bool last = (i == r - 1);
-        float uJ[C];
-        lds_cols<D, CG, C>(tu, cg, uJ);
-        float z[R];
-#pragma unroll
-        for (int ii = 0; ii < R; ++ii) {
-          float acc = 0.f;
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], uJ[c], acc);
-          z[ii] = acc;
-        }
-        if (last) {
-          float kJ[C];
-          lds_cols<D, CG, C>(tk, cg, kJ);
+      if constexpr (kHasA) {
+        float y[R];
+        bool last_fired = false;
+
+        // ---- r guarded Sherman-Morrison sub-updates -----------------------
+        for (int i = 0; i < r; ++i) {
+          const float* tu = tblk + (row_u + i) * D;
+          const bool last = (i == r - 1);
+          float uJ[C];
+          lds_cols<CG, C>(tu, cg, uJ);
+          float z[R];
 #pragma unroll
           for (int ii = 0; ii < R; ++ii) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], kJ[c], acc);
-            y[ii] = acc;
+            for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], uJ[c], acc);
+            z[ii] = acc;
           }
-        }
+          if (last) {
+            float kJ[C];
+            lds_cols<CG, C>(tk, cg, kJ);
 #pragma unroll
-        for (int ii = 0; ii < R; ++ii) z[ii] = group_sum<CG>(z[ii]);
-        if (last) {
+            for (int ii = 0; ii < R; ++ii) {
+              float acc = 0.f;
 #pragma unroll
-          for (int ii = 0; ii < R; ++ii) y[ii] = group_sum<CG>(y[ii]);
-        }
-        float uI[R];
-        lds_rows<R>(tu + row0, uI);
-        float du = 0.f, dk = 0.f;
+              for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], kJ[c], acc);
+              y[ii] = acc;
+            }
+          }
 #pragma unroll
-        for (int ii = 0; ii < R; ++ii) {
-          du = fmaf(z[ii], uI[ii], du);
-          dk = fmaf(z[ii], kI[ii], dk);
+          for (int ii = 0; ii < R; ++ii) z[ii] = group_sum<CG>(z[ii]);
+          if (last) {
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) y[ii] = group_sum<CG>(y[ii]);
+          }
+          float uI[R];
+          lds_rows<R>(tu + row0, uI);
+          float du = 0.f, dk = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            du = fmaf(z[ii], uI[ii], du);
+            dk = fmaf(z[ii], kI[ii], dk);
+          }
+          du = wave_sum(cg == 0 ? du : 0.f);
+          if (last) dk = wave_sum(cg == 0 ? dk : 0.f);
+          float* zb = zbuf + par * D;
+          if (cg == 0) lds_store_rows<R>(zb + row0, z);
+          if constexpr (NW > 1) {
+            if (lane == 0) { red[(par * NW + w) * 4 + 0] = du; red[(par * NW + w) * 4 + 1] = dk; }
+          }
+          __syncthreads();
+          if constexpr (NW > 1) {
+            du = 0.f; dk = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) { du += red[(par * NW + ww) * 4 + 0]; dk += red[(par * NW + ww) * 4 + 1]; }
+          }
+          const float delta = 1.f + du;
+          if (fabsf(delta) < a.eps) {
+            // Singularity guard: inject eps*I and skip this rank-1 update.
+            ++guard_fires;
+            add_to_diagonal<R, C, CG>(A, row0, cg, a.eps);
+            if (last) last_fired = true;
+          } else {
+            float zJ[C];
+            lds_cols<CG, C>(zb, cg, zJ);
+            const float inv = 1.f / delta;
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) {
+              const float zs = z[ii] * inv;
+#pragma unroll
+              for (int c = 0; c < C; ++c) A[ii][c] = fmaf(-zs, zJ[c], A[ii][c]);
+            }
+            if (last) {
+              const float g = dk * inv;
+#pragma unroll
+              for (int ii = 0; ii < R; ++ii) y[ii] = fmaf(-z[ii], g, y[ii]);
+            }
+          }
+          par ^= 1;
         }
-        du = wave_sum(cg == 0 ? du : 0.f);
-        dk = wave_sum(cg == 0 ? dk : 0.f);
-        float* zb = zbuf + par * D;
-        if (cg == 0) lds_store_rows<R>(zb + row0, z);
+
+        // ---- nudge, coefficient and its clamp ------------------------------
+        float alpha[R];
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) alpha[ii] = last_fired ? fmaf(a.eps, kI[ii], y[ii]) : y[ii];
+        if (a.nudge_period > 0) {
+          if (phase == 0) {
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) alpha[ii] = fmaf(a.eps, kI[ii], alpha[ii]);
+            add_to_diagonal<R, C, CG>(A, row0, cg, a.eps);
+          }
+          phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
+        }
+        float an = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
+        an = wave_sum(cg == 0 ? an : 0.f);
+        if constexpr (kInv) {
+          static_assert(!kInv || NW == 1, "the inverse-only pass runs one wave per chunk");
+          // alpha_hat of this token goes to HBM for the state pass.
+          const float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+          if (cg == 0) {
+            float ah[R];
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) {
+              ah[ii] = alpha[ii] * ascale;
+              bad |= !isfinite(ah[ii]);
+            }
+            float* dst = x.alpha_out + (tok0 + t) * D + row0;
+            if constexpr (R % 4 == 0) {
+#pragma unroll
+              for (int ii = 0; ii < R; ii += 4)
+                *reinterpret_cast<float4*>(dst + ii) = make_float4(ah[ii], ah[ii + 1], ah[ii + 2], ah[ii + 3]);
+            } else {
+#pragma unroll
+              for (int ii = 0; ii < R; ++ii) dst[ii] = ah[ii];
+            }
+          }
+          continue;
+        }
+        float* ab = abuf + par * D;
+        if (cg == 0) lds_store_rows<R>(ab + row0, alpha);
         if constexpr (NW > 1) {
-          if (lane == 0) { red[(par * NW + w) * 4 + 0] = du; red[(par * NW + w) * 4 + 1] = dk; }
+          if (lane == 0) red[(par * NW + w) * 4 + 0] = an;
         }
         __syncthreads();
         if constexpr (NW > 1) {
-          du = 0.f; dk = 0.f;
+          an = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < NW; ++ww) { du += red[(par * NW + ww) * 4 + 0]; dk += red[(par * NW + ww) * 4 + 1]; }
+          for (int ww = 0; ww < NW; ++ww) an += red[(par * NW + ww) * 4 + 0];
         }
-        const float delta = 1.f + du;
-        if (fabsf(delta) < a.eps) {
-          // Singularity guard: inject eps*I and skip this rank-1 update.
-          ++guard_fires;
+        const float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+        lds_cols<CG, C>(ab, cg, aJ);
 #pragma unroll
-          for (int ii = 0; ii < R; ++ii)
-#pragma unroll
-            for (int m = 0; m < C / 4; ++m)
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (row0 + ii == (m * CG + cg) * 4 + e) A[ii][4 * m + e] += a.eps;
-          if (last) last_fired = true;
-        } else {
-          float zJ[C];
-          lds_cols<D, CG, C>(zb, cg, zJ);
-          const float inv = 1.f / delta;
-#pragma unroll
-          for (int ii = 0; ii < R; ++ii) {
-            const float zs = z[ii] * inv;
-#pragma unroll
-            for (int c = 0; c < C; ++c) A[ii][c] = fmaf(-zs, zJ[c], A[ii][c]);
-          }
-          if (last) {
-            const float g = dk * inv;
-#pragma unroll
-            for (int ii = 0; ii < R; ++ii) y[ii] = fmaf(-z[ii], g, y[ii]);
-          }
-        }
+        for (int c = 0; c < C; ++c) aJ[c] *= ascale;
         par ^= 1;
+      } else {
+        // alpha_hat of this token, precomputed by the inverse pass.
+        lds_cols<CG, C>(astage + ((sidx & 1) * TT + tt) * D, cg, aJ);
       }
-
-      // ---- nudge, coefficient and its clamp --------------------------------
-      float alpha[R];
-#pragma unroll
-      for (int ii = 0; ii < R; ++ii) alpha[ii] = last_fired ? fmaf(a.eps, kI[ii], y[ii]) : y[ii];
-      if (a.nudge_period > 0) {
-        if (phase == 0) {
-#pragma unroll
-          for (int ii = 0; ii < R; ++ii) {
-            alpha[ii] = fmaf(a.eps, kI[ii], alpha[ii]);
-#pragma unroll
-            for (int m = 0; m < C / 4; ++m)
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (row0 + ii == (m * CG + cg) * 4 + e) A[ii][4 * m + e] += a.eps;
-          }
-        }
-        phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
-      }
-      float an = 0.f;
-#pragma unroll
-      for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
-      an = wave_sum(cg == 0 ? an : 0.f);
-      float* ab = abuf + par * D;
-      if (cg == 0) lds_store_rows<R>(ab + row0, alpha);
-      if constexpr (NW > 1) {
-        if (lane == 0) red[(par * NW + w) * 4 + 0] = an;
-      }
-      __syncthreads();
-      if constexpr (NW > 1) {
-        an = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) an += red[(par * NW + ww) * 4 + 0];
-      }
-      const float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
-      float aJ[C];
-      lds_cols<D, CG, C>(ab, cg, aJ);
-      par ^= 1;
 
       // ---- state update, norm and readout ---------------------------------
+      if constexpr (kHasS) {
       float vI[R], qI[R], qJ[C];
       lds_rows<R>(tv + row0, vI);
       lds_rows<R>(tq + row0, qI);
-      lds_cols<D, CG, C>(tq, cg, qJ);
+      lds_cols<CG, C>(tq, cg, qJ);
       float ns = 0.f, po[R];
 #pragma unroll
       for (int ii = 0; ii < R; ++ii) {
-        const float vs = vI[ii] * ascale;
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          S[ii][c] = fmaf(vs, aJ[c], S[ii][c]);
+          S[ii][c] = fmaf(vI[ii], aJ[c], S[ii][c]);
           ns = fmaf(S[ii][c], S[ii][c], ns);
           acc = fmaf(S[ii][c], qJ[c], acc);
         }
@@ -400,7 +357,7 @@ vla_scan_seq_kernel(ScanArgs a) {
       }
       const float f = oscale / (nq + a.den_eps);
       if (cg == 0) {
-        TIn* op = static_cast<TIn*>(a.o) + (chain * a.T + t) * D + row0;
+        TIn* op = static_cast<TIn*>(a.o) + (tok0 + t) * D + row0;
 #pragma unroll
         for (int ii = 0; ii < R; ++ii) {
           const float ov = po[ii] * f;
@@ -408,44 +365,75 @@ vla_scan_seq_kernel(ScanArgs a) {
           Elem<TIn>::store(op + ii, ov);
         }
       }
+      }  // kHasS
     }
 
-    if (sidx + 1 < nstage) st.store(stage + ((sidx + 1) & 1) * TT * NV * D, TT, NV, tid);
+    if (sidx + 1 < nstage) {
+      st.store(stage + ((sidx + 1) & 1) * TT * NV * D, TT, NV, tid);
+      if constexpr (!kHasA) ast.store(astage + ((sidx + 1) & 1) * TT * D, TT, 1, tid);
+    }
     __syncthreads();
   }
 
   // ---- final state and statistics ---------------------------------------
+  const bool write_a = kFull || (kInv && chunk == x.nchunks - 1);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int row = row0 + i;
 #pragma unroll
     for (int m = 0; m < C / 4; ++m) {
       const int col = (m * CG + cg) * 4;
-      const float4 av = make_float4(A[i][4 * m], A[i][4 * m + 1], A[i][4 * m + 2], A[i][4 * m + 3]);
-      const float4 sv = make_float4(S[i][4 * m], S[i][4 * m + 1], S[i][4 * m + 2], S[i][4 * m + 3]);
-      *reinterpret_cast<float4*>(a.A_T + (chain * D + row) * D + col) = av;
-      *reinterpret_cast<float4*>(a.S_T + (chain * D + row) * D + col) = sv;
+      if constexpr (kHasA) {
+        if (write_a) {
+          const float4 av = make_float4(A[i][4 * m], A[i][4 * m + 1], A[i][4 * m + 2], A[i][4 * m + 3]);
+          *reinterpret_cast<float4*>(a.A_T + (chain * D + row) * D + col) = av;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bad |= !isfinite(A[i][4 * m + c]) || !isfinite(S[i][4 * m + c]);
+          for (int c = 0; c < 4; ++c) bad |= !isfinite(A[i][4 * m + c]);
+        }
+      }
+      if constexpr (kHasS) {
+        const float4 sv = make_float4(S[i][4 * m], S[i][4 * m + 1], S[i][4 * m + 2], S[i][4 * m + 3]);
+        *reinterpret_cast<float4*>(a.S_T + (chain * D + row) * D + col) = sv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bad |= !isfinite(S[i][4 * m + c]);
+      }
     }
-    if (cg == 0) {
-      a.n_T[chain * D + row] = n[i];
-      bad |= !isfinite(n[i]);
+    if constexpr (kHasS) {
+      if (cg == 0) {
+        a.n_T[chain * D + row] = n[i];
+        bad |= !isfinite(n[i]);
+      }
     }
+  }
+  if constexpr (kInv) {
+    // Guard fires break the chunk-start inverses of later chunks: flag the
+    // chain for the sequential fallback.  Non-finite values are recorded.
+    const bool wave_bad = __any(bad);
+    if (tid == 0) {
+      int32_t* info = x.chain_info + chain * 4;
+      if (guard_fires > 0) {
+        atomicAdd(info + kInfoGuard, guard_fires);
+        atomicOr(info + kInfoFallback, 1);
+      }
+      if (wave_bad) atomicOr(info + kInfoNonfinite, 1);
+    }
+    return;
   }
   if (a.stats) {
     const bool wave_bad = __any(bad);
-    if constexpr (NW > 1) {
-      if (lane == 0) red[w * 4] = wave_bad ? 1.f : 0.f;
-      __syncthreads();
-    }
+    __syncthreads();
+    if (lane == 0) red[w * 4] = wave_bad ? 1.f : 0.f;
+    __syncthreads();
     if (tid == 0) {
-      bool any_bad = wave_bad;
-      if constexpr (NW > 1) {
-        for (int ww = 0; ww < NW; ++ww) any_bad |= red[ww * 4] != 0.f;
+      bool any_bad = false;
+      for (int ww = 0; ww < NW; ++ww) any_bad |= red[ww * 4] != 0.f;
+      int32_t guards = guard_fires;
+      if constexpr (!kFull) {
+        guards = x.chain_info ? x.chain_info[chain * 4 + 0] : 0;
+        any_bad |= x.chain_info && x.chain_info[chain * 4 + 2] != 0;
       }
       int32_t* s = a.stats + chain * 4;
-      s[0] = guard_fires;
+      s[0] = guards;
       s[1] = cap_fires;
       s[2] = any_bad ? 1 : 0;
       s[3] = first_cap;
@@ -453,34 +441,70 @@ vla_scan_seq_kernel(ScanArgs a) {
   }
 }
 
-template <typename TIn, int D, int NW, int CG>
-static size_t seq_lds_bytes(int r) {
-  const int TT = stage_tokens<TIn, D, NW>(r);
-  return sizeof(float) * (2 * TT * (3 + r) * D + 4 * D + 2 * NW * 4);
-}
-
-template <typename TIn, int D, int NW, int CG>
-static hipError_t launch_seq(const ScanArgs& a, int chains, hipStream_t stream) {
-  const size_t lds = seq_lds_bytes<TIn, D, NW, CG>(a.r);
-  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG>), dim3(chains), dim3(64 * NW), lds, stream, a);
+template <typename TIn, int D, int NW, int CG, SeqMode MODE>
+static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, hipStream_t stream) {
+  const size_t lds = seq_lds_bytes<TIn, D, NW>(MODE, a.r);
+  const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.nchunks)
+                                                       : static_cast<unsigned>(chains);
+  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE>), dim3(grid), dim3(64 * NW), lds, stream, a, x);
   return hipGetLastError();
 }
 
-// Workgroup shape per head dimension: d <= 64 runs one wave per chain with
-// quads of lanes sharing a row; d = 128 splits the rows over 4 waves.
-template <typename TIn>
-static hipError_t dispatch_seq(const ScanArgs& a, int d, int chains, hipStream_t stream) {
-  switch (d) {
-    case 16: return launch_seq<TIn, 16, 1, 4>(a, chains, stream);
-    case 32: return launch_seq<TIn, 32, 1, 4>(a, chains, stream);
-    case 64: return launch_seq<TIn, 64, 1, 4>(a, chains, stream);
-    case 128: return launch_seq<TIn, 128, 4, 8>(a, chains, stream);
-    default: return hipErrorInvalidValue;
+// Workgroup shapes.  The full scan runs one wave per chain for d <= 64 (many
+// chains fill the chip) and four waves at d = 128.  The state-only chain of
+// the time-parallel schedule has few chains and spreads each one over a
+// whole compute unit.
+template <typename TIn, SeqMode MODE>
+static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int chains, hipStream_t stream) {
+  if constexpr (MODE == SeqMode::kFull) {
+    switch (d) {
+      case 16: return launch_seq<TIn, 16, 1, 4, MODE>(a, x, chains, stream);
+      case 32: return launch_seq<TIn, 32, 1, 4, MODE>(a, x, chains, stream);
+      case 64: return launch_seq<TIn, 64, 1, 4, MODE>(a, x, chains, stream);
+      case 128: return launch_seq<TIn, 128, 4, 8, MODE>(a, x, chains, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else if constexpr (MODE == SeqMode::kStateOnly) {
+    switch (d) {
+      case 64: return launch_seq<TIn, 64, 4, 4, MODE>(a, x, chains, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (d) {
+      case 64: return launch_seq<TIn, 64, 1, 4, MODE>(a, x, chains, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
-hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream) {
-  return bf16 ? dispatch_seq<uint16_t>(a, d, chains, stream) : dispatch_seq<float>(a, d, chains, stream);
+hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, const int32_t* only_if,
+                                  hipStream_t stream) {
+  SeqExtra x{};
+  x.only_if = only_if;
+  return bf16 ? dispatch_seq<uint16_t, SeqMode::kFull>(a, x, d, chains, stream)
+              : dispatch_seq<float, SeqMode::kFull>(a, x, d, chains, stream);
+}
+
+hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, float* alpha_out,
+                                     int32_t* chain_info, int chunk_len, int nchunks, int d, bool bf16, int chains,
+                                     hipStream_t stream) {
+  SeqExtra x{};
+  x.a_start = a_start;
+  x.alpha_out = alpha_out;
+  x.chain_info = chain_info;
+  x.chunk_len = chunk_len;
+  x.nchunks = nchunks;
+  return bf16 ? dispatch_seq<uint16_t, SeqMode::kInverseOnly>(a, x, d, chains, stream)
+              : dispatch_seq<float, SeqMode::kInverseOnly>(a, x, d, chains, stream);
+}
+
+hipError_t launch_scan_state_only(const ScanArgs& a, const float* alpha, int32_t* chain_info, int d,
+                                  bool bf16, int chains, hipStream_t stream) {
+  SeqExtra x{};
+  x.alpha = alpha;
+  x.chain_info = chain_info;
+  return bf16 ? dispatch_seq<uint16_t, SeqMode::kStateOnly>(a, x, d, chains, stream)
+              : dispatch_seq<float, SeqMode::kStateOnly>(a, x, d, chains, stream);
 }
 
 }  // namespace vla

@@ -49,6 +49,72 @@ bool bad_alias(const void* out, size_t n_out, const void* in, size_t n_in, bool 
 }
 
 constexpr size_t kValidateBytes = 256;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape of a chunked run and the workspace layout it uses.
+struct ChunkLayout {
+  bool use = false;
+  int L = 0, nchunks = 0, nperiods = 0, o = 0, q = 0;
+  size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_ND = 0, off_Ac = 0,
+         off_alpha = 0, off_flag = 0, total = 0;
+};
+
+// Whether the chunked schedule can run these parameters with chunk length L.
+bool chunk_len_fits(const vla_scan_params_t* p, int L) {
+  if (L < 16 || L % 16 != 0) return false;
+  if (p->nudge_period > 0 && p->nudge_period % L != 0) return false;
+  return p->t0 % L == 0;
+}
+
+ChunkLayout plan_schedule(const vla_scan_params_t* p) {
+  ChunkLayout cl;
+  const int64_t chains = static_cast<int64_t>(p->B) * p->H;
+  const bool possible = p->d == 64 && p->T > 0 && chains > 0;
+  int L = 0;
+  if (possible) {
+    if (p->chunk_len > 0) {
+      if (chunk_len_fits(p, p->chunk_len)) L = p->chunk_len;
+    } else {
+      for (int cand : {512, 256, 128, 64})
+        if (chunk_len_fits(p, cand)) { L = cand; break; }
+    }
+  }
+  bool use = false;
+  if (p->schedule == VLA_SCHEDULE_CHUNKED) {
+    use = L > 0;
+  } else if (p->schedule == VLA_SCHEDULE_AUTO && L > 0) {
+    // Few chains leave most compute units idle in the sequential schedule;
+    // chunking pays once every chain has several chunks.
+    const int64_t nch = (p->T + L - 1) / L;
+    use = chains <= 256 && nch >= 8;
+  }
+  size_t off = 0;
+  if (use) {
+    cl.use = true;
+    cl.L = L;
+    cl.nchunks = (p->T + L - 1) / L;
+    cl.o = static_cast<int>(p->t0 / L);
+    cl.q = p->nudge_period > 0 ? p->nudge_period / L : 0;
+    // Periods touched: 1 + nudges at the ends of chunks 0 .. nchunks-2.
+    cl.nperiods = 1 + (cl.q > 0 ? (cl.o + cl.nchunks - 1) / cl.q - cl.o / cl.q : 0);
+    const size_t d2 = 64 * 64, C = static_cast<size_t>(chains), nch = cl.nchunks;
+    cl.off_A = off; off = align_up(off + C * d2 * 4);
+    cl.off_S = off; off = align_up(off + C * d2 * 4);
+    cl.off_n = off; off = align_up(off + C * 64 * 4);
+    cl.off_info = off; off = align_up(off + C * 4 * 4);
+    cl.off_G = off; off = align_up(off + C * nch * d2 * 4);
+    cl.off_Gpre = off; off = align_up(off + C * nch * d2 * 8);
+    cl.off_ND = off; off = align_up(off + C * static_cast<size_t>(cl.nperiods) * 2 * d2 * 8);
+    cl.off_Ac = off; off = align_up(off + C * nch * d2 * 4);
+    cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * 64 * 4);
+  }
+  cl.off_flag = off;
+  if (p->validate) off += kValidateBytes;
+  cl.total = off;
+  return cl;
+}
 
 vla_status_t check_params(const vla_scan_params_t* p) {
   if (!p) return fail(VLA_EINVAL, "params is NULL");
@@ -63,8 +129,10 @@ vla_status_t check_params(const vla_scan_params_t* p) {
   if (!std::isfinite(p->den_eps)) return fail(VLA_EINVAL, "den_eps must be finite");
   if (std::isnan(p->s_cap)) return fail(VLA_EINVAL, "s_cap is NaN");
   if (p->t0 < 0) return fail(VLA_EINVAL, "t0 must be >= 0");
-  if (p->schedule != VLA_SCHEDULE_AUTO && p->schedule != VLA_SCHEDULE_SEQUENTIAL)
+  if (p->schedule != VLA_SCHEDULE_AUTO && p->schedule != VLA_SCHEDULE_SEQUENTIAL &&
+      p->schedule != VLA_SCHEDULE_CHUNKED)
     return fail(VLA_EUNSUPPORTED, "schedule %d unsupported", p->schedule);
+  if (p->chunk_len < 0) return fail(VLA_EINVAL, "chunk_len must be >= 0");
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
   if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
   return VLA_OK;
@@ -87,6 +155,7 @@ void vla_scan_params_init(vla_scan_params_t* p) {
   p->t0 = 0;
   p->schedule = VLA_SCHEDULE_AUTO;
   p->validate = 0;
+  p->chunk_len = 0;
 }
 
 vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
@@ -94,7 +163,10 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) 
   if (!bytes) return fail(VLA_EINVAL, "bytes is NULL");
   const vla_status_t s = check_params(p);
   if (s != VLA_OK) return s;
-  *bytes = p->validate ? kValidateBytes : 0;
+  if (p->schedule == VLA_SCHEDULE_CHUNKED && !plan_schedule(p).use)
+    return fail(VLA_EUNSUPPORTED, "chunked schedule needs d = 64, T > 0 and a chunk length dividing "
+                                  "nudge_period and t0");
+  *bytes = plan_schedule(p).total;
   return VLA_OK;
 }
 
@@ -143,15 +215,25 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   }
 
   size_t need = 0;
-  vla_scan_workspace_size(p, &need);
-  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned(workspace, 16))))
-    return fail(VLA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  s = vla_scan_workspace_size(p, &need);
+  if (s != VLA_OK) return s;
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned(workspace, kAlign))))
+    return fail(VLA_EWORKSPACE, "workspace of %zu bytes (256-byte aligned) needed (got %zu)", need,
+                workspace_bytes);
+  const ChunkLayout cl = plan_schedule(p);
+  if (cl.use && overlap(workspace, need, A0, b_mat) + overlap(workspace, need, S0, b_mat) +
+                        overlap(workspace, need, n0, b_vec) + overlap(workspace, need, q, b_seq) +
+                        overlap(workspace, need, k, b_seq) + overlap(workspace, need, v, b_seq) +
+                        overlap(workspace, need, u, b_u) + overlap(workspace, need, o, b_seq) +
+                        overlap(workspace, need, A_T, b_mat) + overlap(workspace, need, S_T, b_mat) +
+                        overlap(workspace, need, n_T, b_vec) > 0)
+    return fail(VLA_EINVAL, "workspace overlaps a tensor argument");
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const bool bf16 = p->in_dtype == VLA_BF16;
 
   if (p->validate && n_tok > 0) {
-    int32_t* flag = static_cast<int32_t*>(workspace);
+    int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cl.off_flag);
     hipError_t e = vla::launch_clear_flag(flag, stream);
     if (e != hipSuccess) return hip_fail(e, "validate");
     const int64_t n_seq = static_cast<int64_t>(n_tok) * d;
@@ -177,8 +259,48 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   a.cap_on = (p->s_cap > 0.f && std::isfinite(p->s_cap)) ? 1 : 0;
   a.cap = a.cap_on ? p->s_cap : 0.f;
   a.den_eps = p->den_eps;
-  const hipError_t e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), stream);
-  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  if (!cl.use) {
+    const hipError_t e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    return VLA_OK;
+  }
+
+  // Chunked schedule: prologue (state snapshot, Gram matrices, (N, D) chain,
+  // chunk-start inverses), inverse pass per chunk, state pass per chain, and
+  // the sequential fallback for any chain flagged on the way.
+  char* ws = static_cast<char*>(workspace);
+  vla::ChunkPlan pl{};
+  pl.chains = static_cast<int>(chains);
+  pl.T = p->T;
+  pl.r = r;
+  pl.L = cl.L;
+  pl.nchunks = cl.nchunks;
+  pl.nperiods = cl.nperiods;
+  pl.o = cl.o;
+  pl.q = cl.q;
+  pl.eps = p->eps;
+  pl.A_init = reinterpret_cast<float*>(ws + cl.off_A);
+  pl.S_init = reinterpret_cast<float*>(ws + cl.off_S);
+  pl.n_init = reinterpret_cast<float*>(ws + cl.off_n);
+  pl.chain_info = reinterpret_cast<int32_t*>(ws + cl.off_info);
+  pl.G = reinterpret_cast<float*>(ws + cl.off_G);
+  pl.Gpre = reinterpret_cast<double*>(ws + cl.off_Gpre);
+  pl.ND = reinterpret_cast<double*>(ws + cl.off_ND);
+  pl.Ac = reinterpret_cast<float*>(ws + cl.off_Ac);
+  pl.alpha = reinterpret_cast<float*>(ws + cl.off_alpha);
+  hipError_t e = vla::launch_chunk_prologue(pl, A0, S0, n0, u, bf16, stream);
+  if (e != hipSuccess) return hip_fail(e, "chunked prologue launch");
+  // Later passes read the snapshot, so outputs may alias the initial state.
+  a.A0 = pl.A_init;
+  a.S0 = pl.S_init;
+  a.n0 = pl.n_init;
+  e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, d, bf16,
+                                      static_cast<int>(chains), stream);
+  if (e != hipSuccess) return hip_fail(e, "chunked inverse launch");
+  e = vla::launch_scan_state_only(a, pl.alpha, pl.chain_info, d, bf16, static_cast<int>(chains), stream);
+  if (e != hipSuccess) return hip_fail(e, "chunked state launch");
+  e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
+  if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
   return VLA_OK;
 }
 

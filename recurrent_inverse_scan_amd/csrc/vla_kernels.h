@@ -29,7 +29,45 @@ struct ScanArgs {
   float den_eps;
 };
 
-hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream);
+// Whole recurrence, one workgroup per chain.  only_if (nullable) restricts
+// the run to chains whose flag is nonzero.
+hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, const int32_t* only_if,
+                                  hipStream_t stream);
+
+// State recurrence only (S, n, cap, readout) from precomputed alpha_hat.
+hipError_t launch_scan_state_only(const ScanArgs& a, const float* alpha, int32_t* chain_info, int d,
+                                  bool bf16, int chains, hipStream_t stream);
+
+// Time-parallel inverse schedule (d = 64): buffers live in the caller's
+// workspace; see chunked.hip.
+struct ChunkPlan {
+  int chains, T, r;
+  int L;          // tokens per chunk
+  int nchunks;    // ceil(T / L)
+  int nperiods;   // nudge periods touched by this call
+  int o, q;       // t0 / L and nudge_period / L (q = 0: no nudge)
+  float eps;
+  float* A_init;  // snapshots of the initial state [chains][64][64], [chains][64][64], [chains][64]
+  float* S_init;
+  float* n_init;
+  int32_t* chain_info;  // [chains][4]
+  float* G;       // [chains][nchunks][64][64]
+  double* Gpre;   // [chains][nchunks][64][64]
+  double* ND;     // [chains][nperiods][2][64][64]
+  float* Ac;      // [chains][nchunks][64][64]
+  float* alpha;   // [chains][T][64]
+};
+
+// Snapshot of the initial state, per-chunk Gram matrices, the (N, D) chain and
+// the chunk-start inverses.
+hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const float* S0, const float* n0,
+                                 const void* u, bool bf16, hipStream_t stream);
+
+// Inverse recurrence of every chunk from its chunk-start inverse; writes
+// alpha_hat and, from each chain's last chunk, A_T.
+hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, float* alpha_out,
+                                      int32_t* chain_info, int chunk_len, int nchunks, int d, bool bf16, int chains,
+                                      hipStream_t stream);
 
 hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_bf16, const void* W,
                             const void* kraw, void* u, hipStream_t stream);

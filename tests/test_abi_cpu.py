@@ -3,6 +3,7 @@ rejects bad arguments before launching anything (no compute calls here)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -38,15 +39,26 @@ def test_version_and_status_strings(lib):
     assert names == ["VLA_OK", "VLA_EINVAL", "VLA_EUNSUPPORTED", "VLA_EWORKSPACE", "VLA_ENONFINITE", "VLA_EHIP"]
 
 
-def test_params_struct_layout_matches_header(lib):
-    """vla_scan_params_init writes the header's defaults at the offsets ctypes expects."""
-    assert ctypes.sizeof(_lib.ScanParams) == 56
+def test_params_struct_layout_matches_header(lib, tmp_path):
+    """The ctypes mirror of vla_scan_params_t has the C compiler's size and
+    offsets, and vla_scan_params_init writes the header's defaults."""
+    fields = [f for f, _ in _lib.ScanParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "vla.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(vla_scan_params_t));\n'
+                   + "".join(f'  printf(" %zu", offsetof(vla_scan_params_t, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    c_layout = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    py_layout = [ctypes.sizeof(_lib.ScanParams)] + [getattr(_lib.ScanParams, f).offset for f in fields]
+    assert c_layout == py_layout
     p = _lib.ScanParams()
     ctypes.memset(ctypes.byref(p), 0x5A, ctypes.sizeof(p))
     lib.vla_scan_params_init(ctypes.byref(p))
     assert (p.B, p.H, p.T, p.d, p.r, p.in_dtype) == (0, 0, 0, 64, 1, 0)
     assert abs(p.eps - 1e-6) < 1e-12 and abs(p.den_eps - 1e-6) < 1e-12
-    assert (p.nudge_period, p.s_cap, p.t0, p.schedule, p.validate) == (0, 0.0, 0, 0, 0)
+    assert (p.nudge_period, p.s_cap, p.t0, p.schedule, p.validate, p.chunk_len) == (0, 0.0, 0, 0, 0, 0)
 
 
 def _params(lib, **kw):
@@ -74,7 +86,7 @@ def _scan(lib, p, **ptrs):
     ("in_dtype", 7, _lib.VLA_EUNSUPPORTED), ("T", -1, _lib.VLA_EINVAL), ("B", -2, _lib.VLA_EINVAL),
     ("nudge_period", -1, _lib.VLA_EINVAL), ("eps", float("nan"), _lib.VLA_EINVAL),
     ("eps", -1.0, _lib.VLA_EINVAL), ("s_cap", float("nan"), _lib.VLA_EINVAL), ("t0", -5, _lib.VLA_EINVAL),
-    ("schedule", 9, _lib.VLA_EUNSUPPORTED),
+    ("schedule", 9, _lib.VLA_EUNSUPPORTED), ("chunk_len", -3, _lib.VLA_EINVAL),
 ])
 def test_scan_rejects_bad_params(lib, field, value, status):
     p = _params(lib, **{field: value})
@@ -121,3 +133,21 @@ def test_workspace_size(lib):
 ])
 def test_project_rejects_bad_args(lib, rows, d, r, din, dout, status):
     assert lib.vla_project_u(rows, d, r, din, dout, None, None, None, None) == status
+
+
+def test_chunked_schedule_planning(lib):
+    n = ctypes.c_size_t(0)
+    # d = 64 with a chunk length dividing the nudge period: supported, needs workspace
+    p = _params(lib, B=2, H=8, T=65536, schedule=_lib.VLA_SCHEDULE_CHUNKED, nudge_period=1024)
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value > 0
+    big = n.value
+    # automatic choice takes it too for few chains and long sequences
+    p.schedule = _lib.VLA_SCHEDULE_AUTO
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == big
+    # many chains: automatic choice stays sequential (no workspace)
+    p.B, p.T = 64, 512
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+    # explicit chunked with an incompatible chunk length or head size is refused
+    for kw in (dict(chunk_len=96, nudge_period=1024), dict(d=128), dict(t0=100, nudge_period=0)):
+        q = _params(lib, B=1, H=2, T=4096, schedule=_lib.VLA_SCHEDULE_CHUNKED, **kw)
+        assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED

@@ -224,3 +224,89 @@ def test_full_size_sampled_chains(name):
                       x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
                       s_cap=cfg.s_cap)
     _check(cfg, (o, A, S, n, st), ref, chains=sel)
+
+
+# ---------------------------------------------------------------------------
+# Time-parallel (chunked) schedule.
+# ---------------------------------------------------------------------------
+CHUNKED = [
+    # (name, overrides, chunk_len)
+    ("f32-nudge", dict(B=1, H=3, T=1000, in_dtype="f32", nudge_period=128, s_cap=None), 64),
+    ("bf16-nudge-cap", dict(B=2, H=2, T=777, in_dtype="bf16", nudge_period=64, s_cap=25.0), 64),
+    ("f32-rank3", dict(B=1, H=2, T=300, r=3, in_dtype="f32", nudge_period=32, s_cap=None), 32),
+    ("bf16-rank4-nonudge", dict(B=1, H=2, T=333, r=4, in_dtype="bf16", nudge_period=0, s_cap=None), 64),
+    ("f32-cap-binding", dict(B=1, H=2, T=513, in_dtype="f32", nudge_period=0, s_cap=3.0), 128),
+]
+
+
+@pytest.mark.parametrize("name,over,L", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_chunked_matches_oracle(name, over, L):
+    cfg = CONFIGS["base"].with_(name=f"chunked-{name}", **over)
+    _say(f"case chunked/{name}")
+    x = case(cfg, seed=11)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L)
+    ref = run_oracle(x, cfg)
+    _, st = _check(cfg, out, ref)
+    if cfg.s_cap:
+        assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
+
+
+def test_chunked_with_initial_state_and_offset():
+    cfg = CONFIGS["base"].with_(name="chunked-state", B=1, H=2, T=640, nudge_period=128, s_cap=50.0)
+    x = case(cfg, seed=12)
+    g = torch.Generator().manual_seed(12)
+    X = torch.randn(2, cfg.d, cfg.d, generator=g) / cfg.d ** 0.5
+    A0 = (0.3 * torch.eye(cfg.d) + X @ X.transpose(-1, -2) / 4).reshape(1, 2, cfg.d, cfg.d).contiguous()
+    S0 = torch.randn(1, 2, cfg.d, cfg.d, generator=g)
+    n0 = torch.rand(1, 2, cfg.d, generator=g)
+    t0 = 256   # a multiple of the chunk length; the nudge phase follows t0
+    out = _gpu(x, cfg, A0=A0.to(DEV), S0=S0.to(DEV), n0=n0.to(DEV), t0=t0, schedule="chunked", chunk_len=64)
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, cfg.d, cfg.d), S0=S0.reshape(2, cfg.d, cfg.d),
+                     n0=n0.reshape(2, cfg.d), t0=t0)
+    _check(cfg, out, ref)
+
+
+def test_chunked_in_place_state_carry():
+    cfg = CONFIGS["base"].with_(name="chunked-inplace", B=1, H=2, T=512, nudge_period=64, s_cap=None)
+    x = case(cfg, seed=13)
+    q, k, v, u = (x[n].to(DEV) for n in ("q", "k", "v", "u"))
+    A = torch.eye(cfg.d, device=DEV).expand(1, 2, cfg.d, cfg.d).contiguous()
+    S = torch.zeros(1, 2, cfg.d, cfg.d, device=DEV)
+    n = torch.zeros(1, 2, cfg.d, device=DEV)
+    st = torch.empty(1, 2, 4, dtype=torch.int32, device=DEV)
+    o = torch.empty_like(q)
+    scan_forward(q, k, v, u, A, S, n, nudge_period=64, schedule="chunked", chunk_len=64, out=(o, A, S, n, st))
+    torch.cuda.synchronize()
+    ref = run_oracle(x, cfg)
+    assert rel_err(o.reshape(2, cfg.T, cfg.d), ref["o"]) <= 2e-3
+    assert rel_err(A.reshape(2, cfg.d, cfg.d), ref["A"], axes=(-2, -1)) <= 2e-3
+    assert rel_err(S.reshape(2, cfg.d, cfg.d), ref["S"], axes=(-2, -1)) <= 2e-3
+
+
+def test_chunked_falls_back_when_the_guard_fires():
+    """A Householder start makes delta = 0 in the first chunk: the chain is
+    recomputed sequentially inside the same call and still matches."""
+    cfg = CONFIGS["base"].with_(name="chunked-guard", B=1, H=2, T=256, nudge_period=0, s_cap=None)
+    x = case(cfg, seed=14)
+    u = x["u"].clone()
+    e = torch.zeros(cfg.d)
+    e[7] = 1.0
+    u[:, :, 0, 0, :] = e
+    x["u"] = u
+    A0 = torch.stack([torch.eye(cfg.d) - 2 * torch.outer(e, e), torch.eye(cfg.d)]).reshape(1, 2, cfg.d, cfg.d)
+    out = _gpu(x, cfg, A0=A0.contiguous().to(DEV), schedule="chunked", chunk_len=64)
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, cfg.d, cfg.d))
+    assert list(ref["guard_fires"]) == [1, 0]
+    _check(cfg, out, ref)
+
+
+def test_chunked_agrees_with_sequential():
+    cfg = CONFIGS["long"].with_(name="chunked-vs-seq", B=1, H=4, T=4096)
+    x = case(cfg, seed=15)
+    a = _gpu(x, cfg, schedule="chunked", chunk_len=512)
+    b = _gpu(x, cfg, schedule="sequential")
+    for name, p, q_ in zip("oASn", a[:4], b[:4]):
+        axes = (-2, -1) if name in "AS" else (-1,)
+        err = rel_err(p, to64(q_), axes=axes)
+        _say(f"chunked vs sequential {name}: {err}")
+        assert err <= (1e-2 if name == "o" else 1e-3), (name, err)
