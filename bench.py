@@ -52,7 +52,7 @@ def main(argv=None) -> int:
     import numpy as np
     import torch
 
-    from recurrent_inverse_scan_amd import CONFIGS, make_inputs, project_u, scan_forward
+    from recurrent_inverse_scan_amd import CONFIGS, make_inputs, project_u, scan_forward, workspace_size
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -63,13 +63,16 @@ def main(argv=None) -> int:
     u = torch.empty((B, H, T, r, d), device=dev, dtype=q.dtype)
     outs = (torch.empty_like(q), torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d, d), device=dev),
             torch.empty((B, H, d), device=dev), torch.empty((B, H, 4), device=dev, dtype=torch.int32))
+    ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+    schedule = "chunked" if ws_bytes > 0 else "sequential"
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     torch.cuda.synchronize()
 
     def step(ev=None):
         project_u(W, kr, out=u)
         if ev is not None:
             ev[0].record()
-        scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=outs)
+        scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=outs, workspace=ws)
         if ev is not None:
             ev[1].record()
 
@@ -118,7 +121,8 @@ def main(argv=None) -> int:
         "config": {"workload": f"{cfg.name}: VLA scan B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
                                f"f32 state, nudge every {cfg.nudge_period}, Frobenius cap {cfg.s_cap}",
                    "B": B, "H": H, "T": T, "d": d, "r": r, "storage": cfg.in_dtype,
-                   "nudge_period": cfg.nudge_period, "s_cap": cfg.s_cap, "schedule": "sequential"},
+                   "nudge_period": cfg.nudge_period, "s_cap": cfg.s_cap, "schedule": schedule,
+                   "workspace_bytes": ws_bytes},
         "roofline": {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None},
         "scan_ms": scan_ms,

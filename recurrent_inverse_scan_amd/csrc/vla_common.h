@@ -31,6 +31,10 @@ template <> struct Elem<uint16_t> {
 };
 
 // ---- cross-lane reductions (DPP within rows of 16 lanes) -------------------
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_read(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
@@ -52,8 +56,18 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float readlane_f(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+// Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... + x_i):
+// Hillis-Steele inside rows of 16 lanes with DPP row shifts, then the row
+// totals carried across rows.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+  x += dpp_read<kRowShr1>(x);
+  x += dpp_read<kRowShr2>(x);
+  x += dpp_read<kRowShr4>(x);
+  x += dpp_read<kRowShr8>(x);
+  const float r0 = readlane_f(x, 15), r1 = readlane_f(x, 31), r2 = readlane_f(x, 47);
+  x += (lane >= 16 ? r0 : 0.f) + (lane >= 32 ? r1 : 0.f) + (lane >= 48 ? r2 : 0.f);
+  return x;
 }
 
 // Sum over the whole wave; the result is wave-uniform and identical on every

@@ -63,6 +63,26 @@ struct ChunkPlan {
 hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const float* S0, const float* n0,
                                  const void* u, bool bf16, hipStream_t stream);
 
+// Blocked state pass (d = 64, blocks of 64 tokens); buffers in the workspace.
+struct StatePlan {
+  int T, nblk;
+  int bf16;              // storage of q, k, v, o
+  const void* v;
+  const float* alpha;    // [chains][T][64] alpha_hat from the inverse pass
+  float* Kmat;           // [chains][nblk][64][64] (v_t.v_s)(alpha_t.alpha_s)
+  float* Xsnap;          // [chains][nblk][64][64] S at each block start
+  float* wsig;           // [chains][T][2] block-local log2 scales: log2 sigma_{t-1}, log2 sigma_t
+  float* ld;             // [chains][T] sum_{s<=t in block} k_s.q_t
+  float* nblock;         // [chains][nblk][64] normaliser at each block start
+  float* ksum;           // [chains][nblk][64] sum of k over each block
+};
+
+// Prep (parallel), chain (one workgroup per chain) and readout (parallel):
+// writes o, S_T, n_T and stats (guard count and inverse-pass non-finite flag
+// taken from chain_info).
+hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
+                             hipStream_t stream);
+
 // Inverse recurrence of every chunk from its chunk-start inverse; writes
 // alpha_hat and, from each chain's last chunk, A_T.
 hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, float* alpha_out,
