@@ -30,6 +30,8 @@
 // (one workgroup per chain, sequential over blocks), vla_state_readout_kernel
 // (parallel over blocks).  Matrix products use 32x32x2 fp32 MFMA tiles: every
 // wave owns one 32x32 tile of a 64x64 result.
+#include <type_traits>
+
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
@@ -129,9 +131,16 @@ __device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, 
   }
 }
 
-// ---- prep: kernel matrix, local normaliser terms, block key sums -----------
-// K[t][s] = (v_t.v_s)(alpha_t.alpha_s); ld[t] = sum_{s<=t} k_s.q_t (block-local);
-// ksum = sum_t k_t over the block.
+// ---- prep: kernel matrices, local normaliser terms, block key sums ---------
+// Per block b of 64 tokens:
+//   CK[t][j]  = sum_{s<j} K(t,s),  K(t,s) = (v_t.v_s)(alpha_t.alpha_s)  (exclusive row prefix)
+//   kext      = K(t,t) and sum_s K(t,s)
+//   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
+//   ld[t]     = sum_{s<=t in block} k_s.q_t;  ksum = sum_t k_t
+//   VT, AT    = v and alpha_hat of the block regrouped as the chain kernel's
+//               matrix-core operands of its rank-64 update: fragment
+//               (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e, e < 8, of
+//               feature 32 c + lane % 32.
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
 vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -143,6 +152,7 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   float* Kl = Ql + kLb * kLd;
   const int64_t chain = blockIdx.x / pl.nblk;
   const int b = blockIdx.x % pl.nblk;
+  const int64_t blk = chain * pl.nblk + b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
   const int64_t row0 = chain * pl.T + tb;
@@ -157,204 +167,425 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   mma_rr(gv, Vl + ti * 32 * kLd, Vl + tj * 32 * kLd, lane);
   mma_rr(ga, Al + ti * 32 * kLd, Al + tj * 32 * kLd, lane);
   mma_rr(pk, Ql + ti * 32 * kLd, Kl + tj * 32 * kLd, lane);   // q_t . k_s
-  float* Kout = pl.Kmat + (chain * pl.nblk + b) * kLb * kLb;
-  const int col = tj * 32 + (lane & 31);
+  if (tid < kLb) {
+    float acc = 0.f;
+    for (int t = 0; t < tcount; ++t) acc += Kl[t * kLd + tid];
+    pl.ksum[blk * kD + tid] = acc;
+  }
+  // Matrix-core operands of the chain kernel's update (features of v and
+  // alpha_hat are LDS columns here).
 #pragma unroll
-  for (int s = 0; s < 16; ++s) Kout[(ti * 32 + acc_row(s, h)) * kLb + col] = gv[s] * ga[s];
-  __syncthreads();   // Vl is free from here on
+  for (int rep = 0; rep < 2; ++rep) {
+    const int f = tid + 256 * rep, c = f >> 8, kb = (f >> 6) & 3, fl = f & 63;
+    const int t0 = 16 * kb + 8 * (fl >> 5), feat = 32 * c + (fl & 31);
+    float xv[8], xa[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xv[e] = Vl[(t0 + e) * kLd + feat];
+      xa[e] = Al[(t0 + e) * kLd + feat];
+    }
+    float4* ad = reinterpret_cast<float4*>(pl.AT + (blk * 512 + f) * 8);
+    ad[0] = make_float4(xa[0], xa[1], xa[2], xa[3]);
+    ad[1] = make_float4(xa[4], xa[5], xa[6], xa[7]);
+    if constexpr (sizeof(TIn) == 2) {
+      uint32_t p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = (__float_as_uint(xv[2 * e]) >> 16) | (__float_as_uint(xv[2 * e + 1]) & 0xffff0000u);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(pl.VT) + (blk * 512 + f) * 8) = make_uint4(p[0], p[1], p[2], p[3]);
+    } else {
+      float4* vd = reinterpret_cast<float4*>(static_cast<float*>(pl.VT) + (blk * 512 + f) * 8);
+      vd[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      vd[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+    }
+  }
+  __syncthreads();   // Ql and Kl are free from here on
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    const int t = ti * 32 + acc_row(s, h);
-    Vl[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
+    const int t = ti * 32 + acc_row(s, h), col = tj * 32 + (lane & 31);
+    Ql[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
+    Kl[t * kLd + col] = gv[s] * ga[s];
   }
   __syncthreads();
   if (tid < kLb) {
-    float acc = 0.f;
-    for (int s = 0; s < kLb; ++s) acc += Vl[tid * kLd + s];
-    if (tid < tcount) pl.ld[row0 + tid] = acc;
+    // Row t of K -> exclusive prefix sums in place.
+    const int t = tid;
+    float run = 0.f, e_t = 0.f;
+    for (int s = 0; s < kLb; ++s) {
+      const float x = Kl[t * kLd + s];
+      e_t = (s == t) ? x : e_t;
+      Kl[t * kLd + s] = run;
+      run += x;
+    }
+    pl.kext[blk * 128 + t] = e_t;
+    pl.kext[blk * 128 + 64 + t] = run;
   } else if (tid < 2 * kLb) {
-    const int c = tid - kLb;
+    const int t = tid - kLb;
     float acc = 0.f;
-    for (int t = 0; t < tcount; ++t) acc += Kl[t * kLd + c];
-    pl.ksum[(chain * pl.nblk + b) * kD + c] = acc;
+    for (int s = 0; s < kLb; ++s) acc += Ql[t * kLd + s];
+    if (t < tcount) pl.ld[row0 + t] = acc;
   }
+  __syncthreads();
+  {
+    float* ck = pl.Kmat + blk * kLb * kLb;
+#pragma unroll
+    for (int rep = 0; rep < 4; ++rep) {
+      const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
+      *reinterpret_cast<float4*>(ck + r * kLb + c4) = *reinterpret_cast<const float4*>(Kl + r * kLd + c4);
+    }
+  }
+  if (b == 0) return;   // uniform
+  // Cross-block kernel, s in the previous (always full) block.
+  __syncthreads();
+  stage_block<TIn>(Kl, v + (row0 - kLb) * kD, kLb, tid);
+  stage_block<float>(Ql, pl.alpha + (row0 - kLb) * kD, kLb, tid);
+  __syncthreads();
+  f32x16 xv = zero16(), xa = zero16();
+  mma_rr(xv, Vl + ti * 32 * kLd, Kl + tj * 32 * kLd, lane);
+  mma_rr(xa, Al + ti * 32 * kLd, Ql + tj * 32 * kLd, lane);
+  float* Xout = pl.Kcross + blk * kLb * kLb;
+  const int col = tj * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < 16; ++s) Xout[(ti * 32 + acc_row(s, h)) * kLb + col] = xv[s] * xa[s];
 }
 
 // ---- chain: the sequential part, one workgroup per chain ---------------------
-// One block's v, alpha_hat and K held in registers, so the next block's loads
-// are in flight while the current block computes.
-template <typename TIn>
-struct BlockRegs {
-  static constexpr int kVVec = kLb * kD / Elem<TIn>::kPer16B / kThreads;   // 16-byte vectors per thread
-  static constexpr int kFVec = kLb * kD / 4 / kThreads;
-  uint4 v[kVVec], a[kFVec], k[kFVec];
-  float ks;   // threads 0..63: block sum of k, feature tid
+// Five waves.  Wave 0 (the recursion wave) runs the cap recursion of block b.
+// Waves 1-4 (the product waves) each own a 32x32 tile of S and, during the
+// same time, apply block b-1's rank-64 update (S_b from S_{b-1}) and compute
+// the next block's bilinear terms v_t^T S_b alpha_t, one block behind; the
+// recursion wave repairs the lag exactly with the cross-block kernel:
+//     v_t^T S_{b+1} alpha_t = sigma_end(b) v_t^T S_b alpha_t
+//                            + sum_{s in b} (sigma_end(b)/sigma_{s-1}) Kx(t,s).
+//
+// Both products run on the bf16 matrix cores at fp32-grade accuracy: an fp32
+// operand x is split into three bf16 terms x = x1 + x2 + x3 (each the
+// round-to-nearest bf16 of what remains; the residuals are exact in fp32, so
+// the split is exact to about 2^-27 |x|), bf16 v is exact as it stands, and
+// the partial products (all pairs of terms whose orders add up to at most 2)
+// accumulate in fp32.
+//
+// Staging is register-free: v and alpha_hat rows (for the bilinear terms) and
+// the prefix-summed K and Kx (for the recursion) go from memory straight into
+// LDS with buffer-to-LDS loads, two generations deep, in 16-byte chunks whose
+// position within a row is XOR-swizzled by the row index (conflict-free
+// row-per-lane reads).  The update's operands come from the prep kernel's
+// regrouped copies into registers, one block ahead.  One barrier per block.
+constexpr int kChainThreads = 320;
 
-  __device__ __forceinline__ void load(const StatePlan& pl, int64_t chain, int b, int tid) {
-    const int tcount = min(kLb, pl.T - b * kLb);
-    const int64_t row0 = chain * pl.T + b * kLb;
-    constexpr int vpr = kD / Elem<TIn>::kPer16B;
-    const TIn* vg = static_cast<const TIn*>(pl.v) + row0 * kD;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// x = t1 + t2 + t3 + O(2^-27 |x|), each term a bf16 (round to nearest even).
+struct Split3 {
+  bf16x8 t1, t2, t3;
+};
+__device__ __forceinline__ Split3 split3(const float (&x)[8]) {
+  Split3 s;
 #pragma unroll
-    for (int j = 0; j < kVVec; ++j) {
-      const int e = tid + j * kThreads, row = e / vpr;
-      v[j] = row < tcount ? *reinterpret_cast<const uint4*>(vg + row * kD + (e % vpr) * Elem<TIn>::kPer16B)
-                          : make_uint4(0, 0, 0, 0);
-    }
-    const float* ag = pl.alpha + row0 * kD;
-    const float* kg = pl.Kmat + (chain * pl.nblk + b) * kLb * kLb;
-#pragma unroll
-    for (int j = 0; j < kFVec; ++j) {
-      const int e = tid + j * kThreads, row = e / 16;
-      a[j] = row < tcount ? *reinterpret_cast<const uint4*>(ag + row * kD + (e % 16) * 4) : make_uint4(0, 0, 0, 0);
-      k[j] = *reinterpret_cast<const uint4*>(kg + e * 4);
-    }
-    ks = tid < kD ? pl.ksum[(chain * pl.nblk + b) * kD + tid] : 0.f;
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 a = static_cast<__bf16>(x[e]);
+    const float r = x[e] - static_cast<float>(a);
+    const __bf16 c = static_cast<__bf16>(r);
+    s.t1[e] = a;
+    s.t2[e] = c;
+    s.t3[e] = static_cast<__bf16>(r - static_cast<float>(c));
   }
+  return s;
+}
 
-  // Row-major copies of v, alpha_hat and K, plus transposed copies of v and
-  // alpha_hat (feature-major) for the state update's matrix product.
-  __device__ __forceinline__ void store(float* Vl, float* Al, float* Kl, float* Vt, float* At, int tid) const {
-    constexpr int EPV = Elem<TIn>::kPer16B, vpr = kD / EPV;
+// acc += A B with A and B given as three-term splits (terms of order >= 3 dropped).
+__device__ __forceinline__ f32x16 mma_split(const Split3& a, const Split3& b, f32x16 acc) {
+  acc = mfma_bf16(a.t2, b.t2, acc);
+  acc = mfma_bf16(a.t3, b.t1, acc);
+  acc = mfma_bf16(a.t1, b.t3, acc);
+  acc = mfma_bf16(a.t2, b.t1, acc);
+  acc = mfma_bf16(a.t1, b.t2, acc);
+  return mfma_bf16(a.t1, b.t1, acc);
+}
+// acc += A B with A exact in bf16.
+__device__ __forceinline__ f32x16 mma_split(bf16x8 a, const Split3& b, f32x16 acc) {
+  acc = mfma_bf16(a, b.t3, acc);
+  acc = mfma_bf16(a, b.t2, acc);
+  return mfma_bf16(a, b.t1, acc);
+}
+// acc += A B with B exact in bf16.
+__device__ __forceinline__ f32x16 mma_split(const Split3& a, bf16x8 b, f32x16 acc) {
+  acc = mfma_bf16(a.t3, b, acc);
+  acc = mfma_bf16(a.t2, b, acc);
+  return mfma_bf16(a.t1, b, acc);
+}
+
+__device__ __forceinline__ void to_floats(uint4 x, float (&f)[8]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int j = 0; j < kVVec; ++j) {
-      const int e = tid + j * kThreads, row = e / vpr, c = (e % vpr) * EPV;
-      float f[EPV];
-      if constexpr (EPV == 4) {
-        f[0] = __uint_as_float(v[j].x); f[1] = __uint_as_float(v[j].y);
-        f[2] = __uint_as_float(v[j].z); f[3] = __uint_as_float(v[j].w);
-      } else {
-        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(w[e] << 16);
+    f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+// Swizzled LDS image of a [64][64] fp32 matrix: chunk c (floats 4c..4c+3) of
+// row r sits at chunk position c ^ (r & 15).
+__device__ __forceinline__ int swz32(int r, int x) { return r * 64 + (((x >> 2) ^ (r & 15)) << 2) + (x & 3); }
+// The same for bf16 rows (8 values per chunk, 8 chunks per row): index in bf16 units.
+__device__ __forceinline__ int swz16(int r, int x) { return r * 64 + (((x >> 3) ^ (r & 7)) << 3) + (x & 7); }
+
+// Buffer-to-LDS copy of 1 KiB piece p of a matrix: lane l's 16 bytes land at
+// lds + 1024 p + 16 l; vo is the lane's source offset within the piece.
+__device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* lds, int p, int vo) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + 1024 * p), 16, vo, 1024 * p, 0, 0);
+}
+
+// The update's operands of one product wave for one block, from the prep kernel.
+template <typename TIn>
+struct UpdFrags {
+  static constexpr int kV = sizeof(TIn) / 2;   // uint4 per 8 values of v
+  uint4 v[4][kV];
+  uint4 a[4][2];
+  __device__ __forceinline__ void load(const StatePlan& pl, int64_t blk, int ti, int tj, int lane) {
+    const auto rv = make_rsrc(static_cast<const TIn*>(pl.VT) + blk * 512 * 8, 512 * 8 * static_cast<int>(sizeof(TIn)));
+    const auto ra = make_rsrc(pl.AT + blk * 512 * 8, 512 * 8 * 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f[2 * q] = __uint_as_float(w[q] << 16);
-          f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-        }
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      const int fv = (ti * 4 + kb) * 64 + lane, fa = (tj * 4 + kb) * 64 + lane;
 #pragma unroll
-      for (int q = 0; q < EPV; q += 4)
-        *reinterpret_cast<float4*>(Vl + row * kLd + c + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
-#pragma unroll
-      for (int q = 0; q < EPV; ++q) Vt[(c + q) * kLd + row] = f[q];
-    }
-#pragma unroll
-    for (int j = 0; j < kFVec; ++j) {
-      const int e = tid + j * kThreads, row = e / 16, c = (e % 16) * 4;
-      *reinterpret_cast<uint4*>(Al + row * kLd + c) = a[j];
-      *reinterpret_cast<uint4*>(Kl + row * kLd + c) = k[j];
-      At[(c + 0) * kLd + row] = __uint_as_float(a[j].x);
-      At[(c + 1) * kLd + row] = __uint_as_float(a[j].y);
-      At[(c + 2) * kLd + row] = __uint_as_float(a[j].z);
-      At[(c + 3) * kLd + row] = __uint_as_float(a[j].w);
+      for (int j = 0; j < kV; ++j) v[kb][j] = buf_load16(rv, (fv * 8 * static_cast<int>(sizeof(TIn))) + 16 * j);
+      a[kb][0] = buf_load16(ra, fa * 32);
+      a[kb][1] = buf_load16(ra, fa * 32 + 16);
     }
   }
 };
 
+// X <- se X + sum over the block of (v_t)_i w_t (alpha_t)_j on this wave's tile.
 template <typename TIn>
-__global__ void __launch_bounds__(kThreads)
+__device__ __forceinline__ void rank_update(f32x16& X, const UpdFrags<TIn>& fr, const float* wp, float se, int h) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) X[s] *= se;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float4 w0 = *reinterpret_cast<const float4*>(wp + 16 * kb + 8 * h);
+    const float4 w1 = *reinterpret_cast<const float4*>(wp + 16 * kb + 8 * h + 4);
+    const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t aw[8] = {fr.a[kb][0].x, fr.a[kb][0].y, fr.a[kb][0].z, fr.a[kb][0].w,
+                            fr.a[kb][1].x, fr.a[kb][1].y, fr.a[kb][1].z, fr.a[kb][1].w};
+    float bx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bx[e] = __uint_as_float(aw[e]) * ww[e];
+    const Split3 B = split3(bx);
+    if constexpr (sizeof(TIn) == 2) {
+      X = mma_split(__builtin_bit_cast(bf16x8, fr.v[kb][0]), B, X);
+    } else {
+      const uint32_t vw[8] = {fr.v[kb][0].x, fr.v[kb][0].y, fr.v[kb][0].z, fr.v[kb][0].w,
+                              fr.v[kb][1].x, fr.v[kb][1].y, fr.v[kb][1].z, fr.v[kb][1].w};
+      float vx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vx[e] = __uint_as_float(vw[e]);
+      X = mma_split(split3(vx), B, X);
+    }
+  }
+}
+
+// Partial v_t^T S alpha_t of one block over this wave's tile of S (rows
+// 32 ti.., columns 32 tj..), from the LDS rows of the block; lanes of the
+// lower half write hr[t].
+template <typename TIn>
+__device__ __forceinline__ void bilinear_terms(const f32x16& X, const char* VR, const float* AR, float* hr, int ti,
+                                               int tj, int lane) {
+  const int h = lane >> 5;
+  // S^T as the A operand: slots 8 kb2 + e of this lane are rows
+  // 16 kb2 + 8 (e / 4) + 4 h + e % 4 of the tile, column = lane % 32.
+  Split3 SA[2];
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    float xs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xs[e] = X[8 * kb2 + e];
+    SA[kb2] = split3(xs);
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = tt * 32 + (lane & 31);
+    f32x16 Z = zero16();
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int f0 = ti * 32 + 16 * kb2 + 4 * h;   // features f0..f0+3 and f0+8..f0+11
+      if constexpr (sizeof(TIn) == 2) {
+        const uint16_t* vr = reinterpret_cast<const uint16_t*>(VR);
+        const uint2 p0 = *reinterpret_cast<const uint2*>(vr + swz16(t, f0));
+        const uint2 p1 = *reinterpret_cast<const uint2*>(vr + swz16(t, f0 + 8));
+        Z = mma_split(SA[kb2], __builtin_bit_cast(bf16x8, make_uint4(p0.x, p0.y, p1.x, p1.y)), Z);
+      } else {
+        const float* vr = reinterpret_cast<const float*>(VR);
+        const float4 p0 = *reinterpret_cast<const float4*>(vr + swz32(t, f0));
+        const float4 p1 = *reinterpret_cast<const float4*>(vr + swz32(t, f0 + 8));
+        const float vx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        Z = mma_split(SA[kb2], split3(vx), Z);
+      }
+    }
+    // Z[j][t] = sum_i S_ij v_ti over the tile; contract with alpha_t over j.
+    float p = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 a = *reinterpret_cast<const float4*>(AR + swz32(t, tj * 32 + 8 * q4 + 4 * h));
+      p = fmaf(a.x, Z[4 * q4], fmaf(a.y, Z[4 * q4 + 1], fmaf(a.z, Z[4 * q4 + 2], fmaf(a.w, Z[4 * q4 + 3], p))));
+    }
+    p += __shfl_xor(p, 32, 64);
+    if (h == 0) hr[t] = p;
+  }
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(kChainThreads)
 vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* __restrict__ n0,
                        float* __restrict__ S_T, float* __restrict__ n_T, int32_t* __restrict__ stats,
                        const int32_t* __restrict__ chain_info, float cap, int cap_on) {
-  extern __shared__ float4 smem4[];
-  float* Xl = reinterpret_cast<float*>(smem4);     // [64][kLd] S at the block start
-  float* Vl = Xl + kD * kLd;                        // [64][kLd] v of the block
-  float* Al = Vl + kLb * kLd;                       // [64][kLd] alpha_hat of the block
-  float* Kl = Al + kLb * kLd;                       // [64][kLd] kernel matrix of the block
-  float* Vt = Kl + kLb * kLd;                       // [64][kLd] v, feature-major
-  float* At = Vt + kD * kLd;                        // [64][kLd] alpha_hat, feature-major
-  float* CKl = At + kD * kLd;                       // [64][kLd] row prefix sums of K (65 used)
-  float* hpart = CKl + kLb * kLd;                   // [2][64]
-  float* wbuf = hpart + 2 * kLb;                    // [64]
-  float* sbuf = wbuf + kLb;                         // [64]
-  float* red = sbuf + kLb;                          // [8]
+  // Every generation is an LDS object of its own: the compiler then sees that
+  // reads of one generation do not depend on buffer-to-LDS loads still in
+  // flight into the other, and waits for those loads only at the barrier.
+  constexpr int kVR4 = kLb * kD * static_cast<int>(sizeof(TIn)) / 16;   // float4s per v-row block
+  __shared__ float4 sCK0[kLb * kLb / 4], sCK1[kLb * kLb / 4];   // prefix-summed K, swizzled
+  __shared__ float4 sKX0[kLb * kLb / 4], sKX1[kLb * kLb / 4];   // Kx, swizzled
+  __shared__ float4 sAR0[kLb * kD / 4], sAR1[kLb * kD / 4];     // alpha_hat rows, swizzled
+  __shared__ float4 sVR0[kVR4], sVR1[kVR4];                     // v rows, swizzled
+  __shared__ float sH0[4 * kLb], sH1[4 * kLb];                  // partial v^T S alpha per product wave
+  __shared__ float sW0[kLb], sW1[kLb];                          // update weights sigma_end/sigma_{s-1}
+  __shared__ float sSig[2];                                     // sigma_end by block parity
+  __shared__ float sNrm[2][4];                                  // |S_b|^2 per product wave, by parity
+  __shared__ float sRed[8];
+
   const int64_t chain = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
-  const int ti = w >> 1, tj = w & 1;                // this wave's tile of S
+  // The wave index is uniform; saying so keeps LDS destinations and buffer
+  // descriptors derived from it in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool rwave = w == 0;
+  const int m = (w + 3) & 3;                           // product wave index (waves 1..4 -> 0..3)
+  const int ti = m >> 1, tj = m & 1;                   // product wave's S tile
   const int col = tj * 32 + (lane & 31);
   const float cap2 = cap * cap;
+  const int nblk = pl.nblk;
+  const int64_t blk0 = chain * nblk;
 
-  // S tile in accumulator layout.
-  f32x16 X;
-  const float* s0 = S0 + chain * kD * kD;
+  // Buffer-to-LDS copies: this wave takes pieces m, m+4, ...; vo32 / vo16
+  // are a lane's source offsets within a piece (fp32 / bf16 rows).
+  auto dma_mat = [&](const float* g, int bytes, float4* dst, int vo32) {
+    const auto r = make_rsrc(g, bytes);
 #pragma unroll
-  for (int s = 0; s < 16; ++s) X[s] = s0[(ti * 32 + acc_row(s, h)) * kD + col];
-  float nrm = 0.f;
+    for (int i = 0; i < 4; ++i) dma_piece(r, reinterpret_cast<char*>(dst), m + 4 * i, vo32);
+  };
+  auto dma_rows = [&](int j, float4* ar, float4* vr, int lane) {
+    const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
+    const int vo16 = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+    const int tcount = min(kLb, pl.T - j * kLb);
+    const int64_t row0 = chain * pl.T + j * kLb;
+    dma_mat(pl.alpha + row0 * kD, tcount * kD * 4, ar, vo32);
+    const auto r = make_rsrc(static_cast<const TIn*>(pl.v) + row0 * kD, tcount * kD * static_cast<int>(sizeof(TIn)));
+    if constexpr (sizeof(TIn) == 2) {
+      dma_piece(r, reinterpret_cast<char*>(vr), m, vo16);
+      dma_piece(r, reinterpret_cast<char*>(vr), m + 4, vo16);
+    } else {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    nrm = fmaf(X[s], X[s], nrm);
-    Xl[(ti * 32 + acc_row(s, h)) * kLd + col] = X[s];
-  }
-  nrm = wave_sum(nrm);
-  if (lane == 0) red[w] = nrm;
-  float nvec = (w == 0) ? n0[chain * kD + lane] : 0.f;   // wave 0, lane i: n_i
+      for (int i = 0; i < 4; ++i) dma_piece(r, reinterpret_cast<char*>(vr), m + 4 * i, vo32);
+    }
+  };
+  auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane) {
+    const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
+    dma_mat(pl.Kmat + (blk0 + j) * kLb * kLb, kLb * kLb * 4, ck, vo32);
+    if (j > 0) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
+  };
+
+  f32x16 X = zero16();
+  UpdFrags<TIn> fr;
+  float nvec = 0.f, N = 0.f, Nstart = 0.f;
+  float e_nx = 0.f, tot_nx = 0.f, ks_nx = 0.f;
   int fires = 0, first = -1;
   bool bad = false;
-  BlockRegs<TIn> regs;
-  regs.load(pl, chain, 0, tid);
-  regs.store(Vl, Al, Kl, Vt, At, tid);
-  float ks_cur = regs.ks;   // k summed over the current block (threads 0..63)
-  __syncthreads();
-  float N = (red[0] + red[1]) + (red[2] + red[3]);   // |S|^2, identical on every wave
 
-  for (int b = 0; b < pl.nblk; ++b) {
+  // ---- prologue ------------------------------------------------------------
+  if (rwave) {
+    nvec = n0[chain * kD + lane];
+    e_nx = pl.kext[blk0 * 128 + lane];
+    tot_nx = pl.kext[blk0 * 128 + 64 + lane];
+    ks_nx = pl.ksum[blk0 * kD + lane];
+  } else {
+    const float* s0 = S0 + chain * kD * kD;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      X[s] = s0[(ti * 32 + acc_row(s, h)) * kD + col];
+      part = fmaf(X[s], X[s], part);
+    }
+    part = wave_sum(part);
+    if (lane == 0) sRed[m] = part;
+    dma_kernels(0, sCK0, sKX0, lane);
+    dma_rows(0, sAR0, sVR0, lane);
+    if (nblk > 1) dma_rows(1, sAR1, sVR1, lane);
+    fr.load(pl, blk0, ti, tj, lane);
+  }
+  __syncthreads();
+  if (!rwave)
+    bilinear_terms<TIn>(X, reinterpret_cast<const char*>(sVR0), reinterpret_cast<const float*>(sAR0), sH0 + m * kLb,
+                        ti, tj, lane);
+  __syncthreads();
+  N = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+
+  // ---- one block; G = b & 1 selects the LDS generations at compile time -----
+  auto step = [&](auto gen, int b) {
+    constexpr int G = decltype(gen)::value;
+    const float4* CK4 = G ? sCK1 : sCK0;
+    const float4* KX4 = G ? sKX1 : sKX0;
+    const float* hr = G ? sH1 : sH0;
+    float* wcur = G ? sW1 : sW0;
+    const float* wprev = G ? sW0 : sW1;
     const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
     const int64_t row0 = chain * pl.T + tb;
-    if (b + 1 < pl.nblk) regs.load(pl, chain, b + 1, tid);   // in flight during this block
-    float* Xs = pl.Xsnap + (chain * pl.nblk + b) * kD * kD;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) Xs[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
-    if (w == 0) pl.nblock[(chain * pl.nblk + b) * kD + lane] = nvec;
-
-    // h_t = v_t^T S_b alpha_t: Y = S_b A^T (tile ti x tt, tt = tj), then
-    // contract Y's rows with v_t.
-    {
-      f32x16 Y = zero16();
-      mma_rr(Y, Xl + ti * 32 * kLd, Al + tj * 32 * kLd, lane);
-      const int t = tj * 32 + (lane & 31);
-      float p = 0.f;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) p = fmaf(Vl[t * kLd + ti * 32 + acc_row(s, h)], Y[s], p);
-      p += __shfl_xor(p, 32, 64);
-      if (h == 0) hpart[ti * kLb + t] = p;
-    }
-    __syncthreads();
-
-    // Cap recursion over the block's tokens (wave 0, lane t).  Invariant:
-    // acc_t = v_t^T S alpha_t for the state S after the last cap fire, and
-    // N = |S|^2.  Cap fires are rare, so each round assumes none for the rest
-    // of the block: token t's pre-cap norm is N plus the prefix sum over
-    // s0 <= s <= t of 2 g_s + e_s, with g_s = acc_s + sum_{s0<=r<s} K(s,r)
-    // taken from row prefix sums of K.  The first token that exceeds the cap
-    // ends the round; the accumulators of later tokens then move to the
-    // post-fire state, and the next round starts after it.
-    if (w == 0) {
-      const int t = lane;
-      float acc = hpart[t] + hpart[kLb + t];
-      const float e_t = Kl[t * kLd + t];
-      float own = 0.f;   // sum_{r<t} K(t,r)
-      {
-        float run = 0.f;
-#pragma unroll
-        for (int m = 0; m < kLb / 4; ++m) {
-          const float4 kv = *reinterpret_cast<const float4*>(Kl + t * kLd + 4 * m);
-          float4 o;
-          o.x = run; own = (t == 4 * m) ? run : own; run += kv.x;
-          o.y = run; own = (t == 4 * m + 1) ? run : own; run += kv.y;
-          o.z = run; own = (t == 4 * m + 2) ? run : own; run += kv.z;
-          o.w = run; own = (t == 4 * m + 3) ? run : own; run += kv.w;
-          *reinterpret_cast<float4*>(CKl + t * kLd + 4 * m) = o;
-        }
-        CKl[t * kLd + kLb] = run;
+    // A fresh copy of the lane index per block keeps the many lane-dependent
+    // LDS addresses from being hoisted out of the loop (and spilled).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (rwave) {
+      const int t = ln;
+      const float* CK = reinterpret_cast<const float*>(CK4);
+      const float e_t = e_nx, tot_t = tot_nx, ks = ks_nx;
+      if (b + 1 < nblk) {
+        e_nx = pl.kext[(blk0 + b + 1) * 128 + lane];
+        tot_nx = pl.kext[(blk0 + b + 1) * 128 + 64 + lane];
+        ks_nx = pl.ksum[(blk0 + b + 1) * kD + lane];
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // v_t^T S_b alpha_t, the one-block lag repaired with the cross kernel.
+      float acc = (hr[t] + hr[kLb + t]) + (hr[2 * kLb + t] + hr[3 * kLb + t]);
+      if (b > 0) {
+        const float se = sSig[G ^ 1];
+        // |S|^2 is carried through the recursion; re-anchor it on the exact
+        // norm of S_{b-1} as the product waves hold it (the carried value
+        // depends on the block-start norm linearly, with factor sigma_end^2).
+        const float* np = sNrm[G ^ 1];
+        N = fmaf(se * se, ((np[0] + np[1]) + (np[2] + np[3])) - Nstart, N);
+        const float* KX = reinterpret_cast<const float*>(KX4);
+        float cx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const float4 xv = *reinterpret_cast<const float4*>(KX + swz32(t, 4 * c));
+          const float4 wv = *reinterpret_cast<const float4*>(wprev + 4 * c);
+          cx[c & 3] = fmaf(xv.x, wv.x, fmaf(xv.y, wv.y, fmaf(xv.z, wv.z, fmaf(xv.w, wv.w, cx[c & 3]))));
+        }
+        acc = fmaf(se, acc, (cx[0] + cx[1]) + (cx[2] + cx[3]));
+      }
+      Nstart = N;
+      pl.nblock[(blk0 + b) * kD + lane] = nvec;
+      const float own = CK[swz32(t, t)];   // sum_{s<t} K(t,s)
+      // Cap recursion by rounds: each round assumes no fire for the rest of
+      // the block, and the first token whose norm would exceed the cap ends it.
       float base = 0.f, lprev_t = 0.f, l_t = 0.f, L = 0.f;
       int s0 = 0;
       while (s0 < tcount) {
         const bool act = t >= s0 && t < tcount;
-        const float g = acc + (own - base);
-        const float npre = N + wave_incl_scan(act ? fmaf(2.f, g, e_t) : 0.f, t);
+        const float gg = acc + (own - base);
+        const float npre = N + wave_incl_scan(act ? fmaf(2.f, gg, e_t) : 0.f, t);
         const uint64_t over = __ballot(act && cap_on && npre > cap2);
         if (over == 0) {
           N = readlane_f(npre, tcount - 1);
@@ -364,7 +595,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
         const float nf = readlane_f(npre, f);
         const float c = cap * __builtin_amdgcn_rsqf(nf);
         const float lg = __builtin_amdgcn_logf(c);   // log2
-        const float cf = CKl[t * kLd + f + 1];
+        const float cf = (f + 1 < kLb) ? CK[swz32(t, f + 1)] : tot_t;   // sum_{s<=f} K(t,s)
         acc = (t > f) ? c * (acc + (cf - base)) : acc;
         lprev_t += (t > f) ? lg : 0.f;
         l_t += (t >= f) ? lg : 0.f;
@@ -375,54 +606,67 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
         ++fires;
         s0 = f + 1;
       }
-      // GEMM weights sigma_end / sigma_{s-1}; the block's final scale in sbuf[0].
-      wbuf[t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
-      if (t == 0) sbuf[0] = exp2f(L);
+      wcur[t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
+      if (t == 0) sSig[G] = exp2f(L);
       if (t < tcount) {
         pl.wsig[2 * (row0 + t)] = lprev_t;
         pl.wsig[2 * (row0 + t) + 1] = l_t;
       }
-      nvec += ks_cur;
+      nvec += ks;
+    } else {
+      if (b > 0) {
+        // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.
+        rank_update<TIn>(X, fr, wprev, sSig[G ^ 1], ln >> 5);
+        fr.load(pl, blk0 + b, ti, tj, ln);
+      }
+      {
+        const int xs_off = ((ti * 32 + 4 * (ln >> 5)) * kD + tj * 32 + (ln & 31)) * 4;
+        const auto rs = make_rsrc(pl.Xsnap + (blk0 + b) * kD * kD, kD * kD * 4);
+        float part = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          buf_store_f32(rs, xs_off + acc_row(s, 0) * kD * 4, X[s]);
+          part = fmaf(X[s], X[s], part);
+        }
+        part = wave_sum(part);
+        if (ln == 0) sNrm[G][m] = part;
+      }
+      // Next block's K and Kx into the other generation (the recursion wave
+      // finished with it one block ago); rows of block b+2 into this one
+      // (block b's rows were last read one block ago).
+      if (b + 1 < nblk) dma_kernels(b + 1, G ? sCK0 : sCK1, G ? sKX0 : sKX1, ln);
+      if (b + 2 < nblk) dma_rows(b + 2, G ? sAR1 : sAR0, G ? sVR1 : sVR0, ln);
+      if (b + 1 < nblk)
+        bilinear_terms<TIn>(X, reinterpret_cast<const char*>(G ? sVR0 : sVR1),
+                            reinterpret_cast<const float*>(G ? sAR0 : sAR1), (G ? sH0 : sH1) + m * kLb, ti, tj, ln);
     }
     __syncthreads();
+  };
+  for (int b = 0; b < nblk; b += 2) {
+    step(std::integral_constant<int, 0>{}, b);
+    if (b + 1 < nblk) step(std::integral_constant<int, 1>{}, b + 1);
+  }
 
-    // S <- sigma_end S_b + V^T diag(sigma_end / sigma_{s-1}) A; N <- |S|^2 exactly.
-    const float sig_end = sbuf[0];
+  // ---- epilogue: the last block's update ------------------------------------
+  if (!rwave) {
+    const int g = (nblk - 1) & 1;
+    rank_update<TIn>(X, fr, g ? sW1 : sW0, sSig[g], h);
+    float* st = S_T + chain * kD * kD;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) X[s] *= sig_end;
-    mma_rr_w(X, Vt + ti * 32 * kLd, At + tj * 32 * kLd, wbuf, lane);
-    float part = 0.f;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) part = fmaf(X[s], X[s], part);
-    part = wave_sum(part);
-    if (lane == 0) red[4 + w] = part;
-    __syncthreads();
-    N = (red[4] + red[5]) + (red[6] + red[7]);
-#pragma unroll
-    for (int s = 0; s < 16; ++s) Xl[(ti * 32 + acc_row(s, h)) * kLd + col] = X[s];
-    if (b + 1 < pl.nblk) {
-      regs.store(Vl, Al, Kl, Vt, At, tid);
-      ks_cur = regs.ks;
+    for (int s = 0; s < 16; ++s) {
+      st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
+      bad |= !isfinite(X[s]);
     }
-    __syncthreads();
-  }
-
-  float* st = S_T + chain * kD * kD;
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
-    bad |= !isfinite(X[s]);
-  }
-  if (w == 0) {
+  } else {
     n_T[chain * kD + lane] = nvec;
     bad |= !isfinite(nvec);
   }
   const bool wave_bad = __any(bad);
-  if (lane == 0) red[w] = wave_bad ? 1.f : 0.f;
+  if (lane == 0) sRed[w] = wave_bad ? 1.f : 0.f;
   __syncthreads();
   if (tid == 0 && stats) {
-    const bool any_bad = red[0] != 0.f || red[1] != 0.f || red[2] != 0.f || red[3] != 0.f ||
-                         chain_info[chain * 4 + kInfoNonfinite] != 0;
+    bool any_bad = chain_info[chain * 4 + kInfoNonfinite] != 0;
+    for (int ww = 0; ww < 5; ++ww) any_bad |= sRed[ww] != 0.f;
     int32_t* s = stats + chain * 4;
     s[0] = chain_info[chain * 4 + kInfoGuard];
     s[1] = fires;
@@ -511,7 +755,7 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
 }  // namespace
 
 size_t state_prep_lds_bytes() { return sizeof(float) * 4 * kLb * kLd; }
-size_t state_chain_lds_bytes() { return sizeof(float) * (7 * kLb * kLd + 4 * kLb + 8); }
+
 size_t state_readout_lds_bytes() { return sizeof(float) * (5 * kLb * kLd + 4 * kLb); }
 
 template <typename K>
@@ -526,8 +770,6 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
   static const bool once = [] {
     allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes());
     allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes());
-    allow_lds(vla_state_chain_kernel<uint16_t>, state_chain_lds_bytes());
-    allow_lds(vla_state_chain_kernel<float>, state_chain_lds_bytes());
     allow_lds(vla_state_readout_kernel<uint16_t>, state_readout_lds_bytes());
     allow_lds(vla_state_readout_kernel<float>, state_readout_lds_bytes());
     return true;
@@ -545,10 +787,10 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kThreads), state_chain_lds_bytes(), stream,
+    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kChainThreads), 0, stream,
                        pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   else
-    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kThreads), state_chain_lds_bytes(), stream,
+    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kChainThreads), 0, stream,
                        pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.bf16)

@@ -77,4 +77,29 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
 }
 
+// ---- raw buffer access -----------------------------------------------------
+// A buffer resource (gfx9 layout: 32-bit dwords, no swizzle, no stride) over
+// `bytes` bytes at a wave-uniform base.  Each access takes a per-lane byte
+// offset, so unrolled loops keep one offset register plus immediates instead
+// of one 64-bit address per access.  Loads at or past `bytes` return zero and
+// stores there are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buf_load_elem(__amdgpu_buffer_rsrc_t r, int off, const float*) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_elem(__amdgpu_buffer_rsrc_t r, int off, const uint16_t*) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
 }  // namespace vla
