@@ -46,6 +46,11 @@ constexpr int kD = 64;     // head dimension
 constexpr int kLb = 64;    // tokens per block
 constexpr int kLd = 68;    // LDS row stride in floats (rows of 16 lanes hit distinct banks)
 constexpr int kThreads = 256;
+// Per-block pack the recursion wave consumes: rows 0..63 hold the exclusive
+// row prefix sums of K, row 64 K(t,t), row 65 the row totals, row 66 the
+// block's key sum; row 67 is padding.
+constexpr int kPackRows = 68;
+constexpr int kRowE = 64, kRowTot = 65, kRowKs = 66;
 
 __device__ __forceinline__ f32x16 zero16() {
   return f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -133,10 +138,11 @@ __device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, 
 
 // ---- prep: kernel matrices, local normaliser terms, block key sums ---------
 // Per block b of 64 tokens:
-//   CK[t][j]  = sum_{s<j} K(t,s),  K(t,s) = (v_t.v_s)(alpha_t.alpha_s)  (exclusive row prefix)
-//   kext      = K(t,t) and sum_s K(t,s)
+//   pack      = CK[t][j] = sum_{s<j} K(t,s), K(t,s) = (v_t.v_s)(alpha_t.alpha_s)
+//               (exclusive row prefix), then K(t,t), sum_s K(t,s) and
+//               sum_t k_t as three more rows
 //   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
-//   ld[t]     = sum_{s<=t in block} k_s.q_t;  ksum = sum_t k_t
+//   ld[t]     = sum_{s<=t in block} k_s.q_t
 //   VT, AT    = v and alpha_hat of the block regrouped as the chain kernel's
 //               matrix-core operands of its rank-64 update: fragment
 //               (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e, e < 8, of
@@ -167,10 +173,12 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   mma_rr(gv, Vl + ti * 32 * kLd, Vl + tj * 32 * kLd, lane);
   mma_rr(ga, Al + ti * 32 * kLd, Al + tj * 32 * kLd, lane);
   mma_rr(pk, Ql + ti * 32 * kLd, Kl + tj * 32 * kLd, lane);   // q_t . k_s
+  float* pack = pl.Kmat + blk * kPackRows * kLb;
   if (tid < kLb) {
     float acc = 0.f;
     for (int t = 0; t < tcount; ++t) acc += Kl[t * kLd + tid];
-    pl.ksum[blk * kD + tid] = acc;
+    pack[kRowKs * kLb + tid] = acc;
+    pack[67 * kLb + tid] = 0.f;
   }
   // Matrix-core operands of the chain kernel's update (features of v and
   // alpha_hat are LDS columns here).
@@ -216,8 +224,8 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
       Kl[t * kLd + s] = run;
       run += x;
     }
-    pl.kext[blk * 128 + t] = e_t;
-    pl.kext[blk * 128 + 64 + t] = run;
+    pack[kRowE * kLb + t] = e_t;
+    pack[kRowTot * kLb + t] = run;
   } else if (tid < 2 * kLb) {
     const int t = tid - kLb;
     float acc = 0.f;
@@ -225,13 +233,10 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
     if (t < tcount) pl.ld[row0 + t] = acc;
   }
   __syncthreads();
-  {
-    float* ck = pl.Kmat + blk * kLb * kLb;
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
-      *reinterpret_cast<float4*>(ck + r * kLb + c4) = *reinterpret_cast<const float4*>(Kl + r * kLd + c4);
-    }
+  for (int rep = 0; rep < 4; ++rep) {
+    const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<float4*>(pack + r * kLb + c4) = *reinterpret_cast<const float4*>(Kl + r * kLd + c4);
   }
   if (b == 0) return;   // uniform
   // Cross-block kernel, s in the previous (always full) block.
@@ -391,11 +396,38 @@ __device__ __forceinline__ void rank_update(f32x16& X, const UpdFrags<TIn>& fr, 
 
 // Partial v_t^T S alpha_t of one block over this wave's tile of S (rows
 // 32 ti.., columns 32 tj..), from the LDS rows of the block; lanes of the
-// lower half write hr[t].
+// lower half write hr[t].  All LDS operands are read before the products.
 template <typename TIn>
 __device__ __forceinline__ void bilinear_terms(const f32x16& X, const char* VR, const float* AR, float* hr, int ti,
                                                int tj, int lane) {
   const int h = lane >> 5;
+  constexpr int kVW = sizeof(TIn) == 2 ? 2 : 4;   // 32-bit words per 4 features of v
+  uint32_t vp[2][2][2][kVW];                       // [tt][kb2][piece][word]
+  float4 ar[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = tt * 32 + (lane & 31);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int f0 = ti * 32 + 16 * kb2 + 4 * h;   // features f0..f0+3 and f0+8..f0+11
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc) {
+        if constexpr (sizeof(TIn) == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(VR) + swz16(t, f0 + 8 * pc));
+          vp[tt][kb2][pc][0] = x.x;
+          vp[tt][kb2][pc][1] = x.y;
+        } else {
+          const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(VR) + swz32(t, f0 + 8 * pc));
+          vp[tt][kb2][pc][0] = x.x;
+          vp[tt][kb2][pc][1] = x.y;
+          vp[tt][kb2][pc][2] = x.z;
+          vp[tt][kb2][pc][3] = x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) ar[tt][q4] = *reinterpret_cast<const float4*>(AR + swz32(t, tj * 32 + 8 * q4 + 4 * h));
+  }
   // S^T as the A operand: slots 8 kb2 + e of this lane are rows
   // 16 kb2 + 8 (e / 4) + 4 h + e % 4 of the tile, column = lane % 32.
   Split3 SA[2];
@@ -408,21 +440,19 @@ __device__ __forceinline__ void bilinear_terms(const f32x16& X, const char* VR, 
   }
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int t = tt * 32 + (lane & 31);
     f32x16 Z = zero16();
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int f0 = ti * 32 + 16 * kb2 + 4 * h;   // features f0..f0+3 and f0+8..f0+11
       if constexpr (sizeof(TIn) == 2) {
-        const uint16_t* vr = reinterpret_cast<const uint16_t*>(VR);
-        const uint2 p0 = *reinterpret_cast<const uint2*>(vr + swz16(t, f0));
-        const uint2 p1 = *reinterpret_cast<const uint2*>(vr + swz16(t, f0 + 8));
-        Z = mma_split(SA[kb2], __builtin_bit_cast(bf16x8, make_uint4(p0.x, p0.y, p1.x, p1.y)), Z);
+        Z = mma_split(SA[kb2], __builtin_bit_cast(bf16x8, make_uint4(vp[tt][kb2][0][0], vp[tt][kb2][0][1],
+                                                                    vp[tt][kb2][1][0], vp[tt][kb2][1][1])), Z);
       } else {
-        const float* vr = reinterpret_cast<const float*>(VR);
-        const float4 p0 = *reinterpret_cast<const float4*>(vr + swz32(t, f0));
-        const float4 p1 = *reinterpret_cast<const float4*>(vr + swz32(t, f0 + 8));
-        const float vx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        float vx[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vx[e] = __uint_as_float(vp[tt][kb2][0][e]);
+          vx[4 + e] = __uint_as_float(vp[tt][kb2][1][e]);
+        }
         Z = mma_split(SA[kb2], split3(vx), Z);
       }
     }
@@ -430,11 +460,11 @@ __device__ __forceinline__ void bilinear_terms(const f32x16& X, const char* VR, 
     float p = 0.f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 a = *reinterpret_cast<const float4*>(AR + swz32(t, tj * 32 + 8 * q4 + 4 * h));
+      const float4 a = ar[tt][q4];
       p = fmaf(a.x, Z[4 * q4], fmaf(a.y, Z[4 * q4 + 1], fmaf(a.z, Z[4 * q4 + 2], fmaf(a.w, Z[4 * q4 + 3], p))));
     }
     p += __shfl_xor(p, 32, 64);
-    if (h == 0) hr[t] = p;
+    if (h == 0) hr[tt * 32 + (lane & 31)] = p;
   }
 }
 
@@ -443,19 +473,29 @@ __global__ void __launch_bounds__(kChainThreads)
 vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* __restrict__ n0,
                        float* __restrict__ S_T, float* __restrict__ n_T, int32_t* __restrict__ stats,
                        const int32_t* __restrict__ chain_info, float cap, int cap_on) {
-  // Every generation is an LDS object of its own: the compiler then sees that
-  // reads of one generation do not depend on buffer-to-LDS loads still in
-  // flight into the other, and waits for those loads only at the barrier.
+  // Buffers that buffer-to-LDS loads fill and that the same waves read (the
+  // v and alpha_hat rows) have one LDS object per generation, selected at
+  // compile time: the compiler then sees that reading one generation does not
+  // depend on loads still in flight into the other, and waits for those only
+  // at the barrier.  A generation is written only in the block after its last
+  // reader's barrier, and read only in the block after the one that wrote it:
+  // every cross-wave hand-off goes through a barrier.
+  constexpr bool kBf = sizeof(TIn) == 2;
+  constexpr int kRowGens = 2;
   constexpr int kVR4 = kLb * kD * static_cast<int>(sizeof(TIn)) / 16;   // float4s per v-row block
-  __shared__ float4 sCK0[kLb * kLb / 4], sCK1[kLb * kLb / 4];   // prefix-summed K, swizzled
+  __shared__ float4 sCK0[kPackRows * kLb / 4], sCK1[kPackRows * kLb / 4];   // the pack, swizzled
   __shared__ float4 sKX0[kLb * kLb / 4], sKX1[kLb * kLb / 4];   // Kx, swizzled
   __shared__ float4 sAR0[kLb * kD / 4], sAR1[kLb * kD / 4];     // alpha_hat rows, swizzled
   __shared__ float4 sVR0[kVR4], sVR1[kVR4];                     // v rows, swizzled
-  __shared__ float sH0[4 * kLb], sH1[4 * kLb];                  // partial v^T S alpha per product wave
-  __shared__ float sW0[kLb], sW1[kLb];                          // update weights sigma_end/sigma_{s-1}
-  __shared__ float sSig[2];                                     // sigma_end by block parity
-  __shared__ float sNrm[2][4];                                  // |S_b|^2 per product wave, by parity
+  __shared__ float sH[2][4 * kLb];                              // partial v^T S alpha per product wave
+  __shared__ float sW[2][kLb];                                  // update weights sigma_end/sigma_{s-1}
+  __shared__ float sSig[2];                                     // sigma_end
+  __shared__ float sNrm[2][4];                                  // |S_b|^2 per product wave
+  __shared__ float sLog[2][2 * kLb];                            // per-token log2 scales
+  __shared__ float sNb[2][kD];                                  // n at the block start
   __shared__ float sRed[8];
+  auto rows_ar = [&](auto rc) -> float4* { return decltype(rc)::value ? sAR1 : sAR0; };
+  auto rows_vr = [&](auto rc) -> float4* { return decltype(rc)::value ? sVR1 : sVR0; };
 
   const int64_t chain = blockIdx.x;
   // The wave index is uniform; saying so keeps LDS destinations and buffer
@@ -484,7 +524,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
     const int64_t row0 = chain * pl.T + j * kLb;
     dma_mat(pl.alpha + row0 * kD, tcount * kD * 4, ar, vo32);
     const auto r = make_rsrc(static_cast<const TIn*>(pl.v) + row0 * kD, tcount * kD * static_cast<int>(sizeof(TIn)));
-    if constexpr (sizeof(TIn) == 2) {
+    if constexpr (kBf) {
       dma_piece(r, reinterpret_cast<char*>(vr), m, vo16);
       dma_piece(r, reinterpret_cast<char*>(vr), m + 4, vo16);
     } else {
@@ -494,23 +534,31 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
   };
   auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane) {
     const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
-    dma_mat(pl.Kmat + (blk0 + j) * kLb * kLb, kLb * kLb * 4, ck, vo32);
+    dma_mat(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4, ck, vo32);
+    if (m == 0) dma_piece(make_rsrc(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4),
+                          reinterpret_cast<char*>(ck), 16, vo32);
     if (j > 0) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
+  };
+
+  // The recursion wave's per-block outputs, written from LDS by a product wave.
+  auto store_block_outputs = [&](int j, const float* lg, const float* nb, int lane) {
+    const int tc = min(kLb, pl.T - j * kLb);
+    const int64_t r0 = chain * pl.T + j * kLb;
+    const auto rw = make_rsrc(pl.wsig + 2 * r0, 2 * tc * 4);
+    buf_store_f32(rw, 4 * lane, lg[lane]);
+    buf_store_f32(rw, 4 * (lane + 64), lg[lane + 64]);
+    pl.nblock[(blk0 + j) * kD + lane] = nb[lane];
   };
 
   f32x16 X = zero16();
   UpdFrags<TIn> fr;
   float nvec = 0.f, N = 0.f, Nstart = 0.f;
-  float e_nx = 0.f, tot_nx = 0.f, ks_nx = 0.f;
   int fires = 0, first = -1;
   bool bad = false;
 
   // ---- prologue ------------------------------------------------------------
   if (rwave) {
     nvec = n0[chain * kD + lane];
-    e_nx = pl.kext[blk0 * 128 + lane];
-    tot_nx = pl.kext[blk0 * 128 + 64 + lane];
-    ks_nx = pl.ksum[blk0 * kD + lane];
   } else {
     const float* s0 = S0 + chain * kD * kD;
     float part = 0.f;
@@ -528,55 +576,56 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
   }
   __syncthreads();
   if (!rwave)
-    bilinear_terms<TIn>(X, reinterpret_cast<const char*>(sVR0), reinterpret_cast<const float*>(sAR0), sH0 + m * kLb,
+    bilinear_terms<TIn>(X, reinterpret_cast<const char*>(sVR0), reinterpret_cast<const float*>(sAR0), sH[0] + m * kLb,
                         ti, tj, lane);
   __syncthreads();
   N = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
 
-  // ---- one block; G = b & 1 selects the LDS generations at compile time -----
-  auto step = [&](auto gen, int b) {
-    constexpr int G = decltype(gen)::value;
-    const float4* CK4 = G ? sCK1 : sCK0;
-    const float4* KX4 = G ? sKX1 : sKX0;
-    const float* hr = G ? sH1 : sH0;
-    float* wcur = G ? sW1 : sW0;
-    const float* wprev = G ? sW0 : sW1;
+  // ---- one block; RG (compile time) is the row generation of block b -------
+  auto step = [&](auto rgc, int b) {
+    constexpr int RG = decltype(rgc)::value;
+    constexpr int RGp1 = (RG + 1) % kRowGens, RGp2 = (RG + 2) % kRowGens;
+    const int g = b & 1;
     const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
-    const int64_t row0 = chain * pl.T + tb;
     // A fresh copy of the lane index per block keeps the many lane-dependent
     // LDS addresses from being hoisted out of the loop (and spilled).
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (rwave) {
       const int t = ln;
-      const float* CK = reinterpret_cast<const float*>(CK4);
-      const float e_t = e_nx, tot_t = tot_nx, ks = ks_nx;
-      if (b + 1 < nblk) {
-        e_nx = pl.kext[(blk0 + b + 1) * 128 + lane];
-        tot_nx = pl.kext[(blk0 + b + 1) * 128 + 64 + lane];
-        ks_nx = pl.ksum[(blk0 + b + 1) * kD + lane];
-      }
+      const float* CK = reinterpret_cast<const float*>(g ? sCK1 : sCK0);
+      // The recursion wave touches no global memory inside the loop: its
+      // inputs come with the LDS pack and its outputs go to LDS.
+      const float e_t = CK[swz32(kRowE, t)], tot_t = CK[swz32(kRowTot, t)], ks = CK[swz32(kRowKs, t)];
+      const float* hr = sH[g];
       // v_t^T S_b alpha_t, the one-block lag repaired with the cross kernel.
       float acc = (hr[t] + hr[kLb + t]) + (hr[2 * kLb + t] + hr[3 * kLb + t]);
       if (b > 0) {
-        const float se = sSig[G ^ 1];
+        const float se = sSig[g ^ 1];
         // |S|^2 is carried through the recursion; re-anchor it on the exact
         // norm of S_{b-1} as the product waves hold it (the carried value
         // depends on the block-start norm linearly, with factor sigma_end^2).
-        const float* np = sNrm[G ^ 1];
+        const float* np = sNrm[g ^ 1];
         N = fmaf(se * se, ((np[0] + np[1]) + (np[2] + np[3])) - Nstart, N);
-        const float* KX = reinterpret_cast<const float*>(KX4);
+        const float* KX = reinterpret_cast<const float*>(g ? sKX1 : sKX0);
+        const float* wprev = sW[g ^ 1];
         float cx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const float4 xv = *reinterpret_cast<const float4*>(KX + swz32(t, 4 * c));
-          const float4 wv = *reinterpret_cast<const float4*>(wprev + 4 * c);
-          cx[c & 3] = fmaf(xv.x, wv.x, fmaf(xv.y, wv.y, fmaf(xv.z, wv.z, fmaf(xv.w, wv.w, cx[c & 3]))));
+        for (int half = 0; half < 2; ++half) {
+          float4 xv[8], wv[8];   // all reads of a half before its sums
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            xv[c] = *reinterpret_cast<const float4*>(KX + swz32(t, 32 * half + 4 * c));
+            wv[c] = *reinterpret_cast<const float4*>(wprev + 32 * half + 4 * c);
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            cx[c & 3] = fmaf(xv[c].x, wv[c].x, fmaf(xv[c].y, wv[c].y, fmaf(xv[c].z, wv[c].z, fmaf(xv[c].w, wv[c].w, cx[c & 3]))));
         }
         acc = fmaf(se, acc, (cx[0] + cx[1]) + (cx[2] + cx[3]));
       }
       Nstart = N;
-      pl.nblock[(blk0 + b) * kD + lane] = nvec;
+      sNb[g][t] = nvec;
       const float own = CK[swz32(t, t)];   // sum_{s<t} K(t,s)
       // Cap recursion by rounds: each round assumes no fire for the rest of
       // the block, and the first token whose norm would exceed the cap ends it.
@@ -606,18 +655,17 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
         ++fires;
         s0 = f + 1;
       }
-      wcur[t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
-      if (t == 0) sSig[G] = exp2f(L);
-      if (t < tcount) {
-        pl.wsig[2 * (row0 + t)] = lprev_t;
-        pl.wsig[2 * (row0 + t) + 1] = l_t;
-      }
+      sW[g][t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
+      if (t == 0) sSig[g] = exp2f(L);
+      sLog[g][2 * t] = lprev_t;
+      sLog[g][2 * t + 1] = l_t;
       nvec += ks;
     } else {
       if (b > 0) {
         // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.
-        rank_update<TIn>(X, fr, wprev, sSig[G ^ 1], ln >> 5);
+        rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
         fr.load(pl, blk0 + b, ti, tj, ln);
+        if (m == 0) store_block_outputs(b - 1, sLog[g ^ 1], sNb[g ^ 1], ln);
       }
       {
         const int xs_off = ((ti * 32 + 4 * (ln >> 5)) * kD + tj * 32 + (ln & 31)) * 4;
@@ -629,16 +677,19 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
           part = fmaf(X[s], X[s], part);
         }
         part = wave_sum(part);
-        if (ln == 0) sNrm[G][m] = part;
+        if (ln == 0) sNrm[g][m] = part;
       }
-      // Next block's K and Kx into the other generation (the recursion wave
-      // finished with it one block ago); rows of block b+2 into this one
-      // (block b's rows were last read one block ago).
-      if (b + 1 < nblk) dma_kernels(b + 1, G ? sCK0 : sCK1, G ? sKX0 : sKX1, ln);
-      if (b + 2 < nblk) dma_rows(b + 2, G ? sAR1 : sAR0, G ? sVR1 : sVR0, ln);
+      // Next block's pack and Kx into the other parity (the recursion wave
+      // finished with it one block ago).
+      if (b + 1 < nblk) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
+      // Rows of block b+2 into the generation block b used (last read one
+      // block ago).
+      if (b + 2 < nblk) dma_rows(b + 2, rows_ar(std::integral_constant<int, RGp2>{}),
+                                   rows_vr(std::integral_constant<int, RGp2>{}), ln);
       if (b + 1 < nblk)
-        bilinear_terms<TIn>(X, reinterpret_cast<const char*>(G ? sVR0 : sVR1),
-                            reinterpret_cast<const float*>(G ? sAR0 : sAR1), (G ? sH0 : sH1) + m * kLb, ti, tj, ln);
+        bilinear_terms<TIn>(X, reinterpret_cast<const char*>(rows_vr(std::integral_constant<int, RGp1>{})),
+                            reinterpret_cast<const float*>(rows_ar(std::integral_constant<int, RGp1>{})),
+                            sH[g ^ 1] + m * kLb, ti, tj, ln);
     }
     __syncthreads();
   };
@@ -650,7 +701,8 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
   // ---- epilogue: the last block's update ------------------------------------
   if (!rwave) {
     const int g = (nblk - 1) & 1;
-    rank_update<TIn>(X, fr, g ? sW1 : sW0, sSig[g], h);
+    if (m == 0) store_block_outputs(nblk - 1, sLog[g], sNb[g], lane);
+    rank_update<TIn>(X, fr, sW[g], sSig[g], h);
     float* st = S_T + chain * kD * kD;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {

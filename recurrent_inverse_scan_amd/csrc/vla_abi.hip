@@ -59,7 +59,7 @@ struct ChunkLayout {
   int L = 0, nchunks = 0, nperiods = 0, o = 0, q = 0;
   int nblk = 0;   // 64-token blocks of the state pass
   size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_ND = 0, off_Ac = 0,
-         off_alpha = 0, off_K = 0, off_Kx = 0, off_kext = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0, off_ks = 0, off_flag = 0,
+         off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0, off_flag = 0,
          total = 0;
 };
 
@@ -113,16 +113,14 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * 64 * 4);
     cl.nblk = (p->T + 63) / 64;
     const size_t nb = cl.nblk, T = static_cast<size_t>(p->T);
-    cl.off_K = off; off = align_up(off + C * nb * d2 * 4);
+    cl.off_K = off; off = align_up(off + C * nb * 68 * 64 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
-    cl.off_kext = off; off = align_up(off + C * nb * 128 * 4);
     cl.off_VT = off; off = align_up(off + C * nb * d2 * (p->in_dtype == VLA_BF16 ? 2 : 4));
     cl.off_AT = off; off = align_up(off + C * nb * d2 * 4);
     cl.off_X = off; off = align_up(off + C * nb * d2 * 4);
     cl.off_wsig = off; off = align_up(off + C * T * 2 * 4);
     cl.off_ld = off; off = align_up(off + C * T * 4);
     cl.off_nb = off; off = align_up(off + C * nb * 64 * 4);
-    cl.off_ks = off; off = align_up(off + C * nb * 64 * 4);
   }
   cl.off_flag = off;
   if (p->validate) off += kValidateBytes;
@@ -319,14 +317,12 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   sp.alpha = pl.alpha;
   sp.Kmat = reinterpret_cast<float*>(ws + cl.off_K);
   sp.Kcross = reinterpret_cast<float*>(ws + cl.off_Kx);
-  sp.kext = reinterpret_cast<float*>(ws + cl.off_kext);
   sp.VT = ws + cl.off_VT;
   sp.AT = reinterpret_cast<float*>(ws + cl.off_AT);
   sp.Xsnap = reinterpret_cast<float*>(ws + cl.off_X);
   sp.wsig = reinterpret_cast<float*>(ws + cl.off_wsig);
   sp.ld = reinterpret_cast<float*>(ws + cl.off_ld);
   sp.nblock = reinterpret_cast<float*>(ws + cl.off_nb);
-  sp.ksum = reinterpret_cast<float*>(ws + cl.off_ks);
   e = vla::launch_state_pass(sp, a, pl.chain_info, static_cast<int>(chains), stream);
   if (e != hipSuccess) return hip_fail(e, "chunked state launch");
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);

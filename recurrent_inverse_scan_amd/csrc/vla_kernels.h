@@ -69,16 +69,15 @@ struct StatePlan {
   int bf16;              // storage of q, k, v, o
   const void* v;
   const float* alpha;    // [chains][T][64] alpha_hat from the inverse pass
-  float* Kmat;           // [chains][nblk][64][64] row prefix sums over s<j of (v_t.v_s)(alpha_t.alpha_s)
+  float* Kmat;           // [chains][nblk][68][64] row prefix sums over s<j of K(t,s) = (v_t.v_s)(alpha_t.alpha_s),
+                         // then rows K(t,t), sum_s K(t,s), sum_t k_t and one padding row
   float* Kcross;         // [chains][nblk][64][64] (v_t.v_s)(alpha_t.alpha_s), s in the previous block
-  float* kext;           // [chains][nblk][2][64] K(t,t) and sum_s K(t,s)
   void* VT;              // [chains][nblk][512][8] v regrouped as matrix-core operands (storage dtype)
   float* AT;             // [chains][nblk][512][8] alpha_hat regrouped the same way
   float* Xsnap;          // [chains][nblk][64][64] S at each block start
   float* wsig;           // [chains][T][2] block-local log2 scales: log2 sigma_{t-1}, log2 sigma_t
   float* ld;             // [chains][T] sum_{s<=t in block} k_s.q_t
   float* nblock;         // [chains][nblk][64] normaliser at each block start
-  float* ksum;           // [chains][nblk][64] sum of k over each block
 };
 
 // Prep (parallel), chain (one workgroup per chain) and readout (parallel):

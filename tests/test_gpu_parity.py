@@ -223,7 +223,36 @@ def test_full_size_sampled_chains(name):
     ref = oracle_scan(x["q"].reshape(C, cfg.T, cfg.d)[sel], x["k"].reshape(C, cfg.T, cfg.d)[sel],
                       x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
                       s_cap=cfg.s_cap)
-    _check(cfg, (o, A, S, n, st), ref, chains=sel)
+    _, st = _check(cfg, (o, A, S, n, st), ref, chains=sel)
+    if cfg.s_cap:
+        # cap decisions may differ only where |S|_F is within rounding of the cap
+        _say(f"cap fires gpu {st[:, 1].tolist()} oracle {ref['cap_fires'].tolist()}")
+        assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
+
+
+def test_full_size_long_repeatable_on_reused_buffers():
+    """The long workload, run twice on the same workspace and output buffers
+    exactly as the benchmark does, gives bit-identical results."""
+    from recurrent_inverse_scan_amd import make_inputs, workspace_size
+
+    cfg = CONFIGS["long"]
+    _say("case full/long repeat")
+    x = make_inputs(cfg, seed=0)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    u = project_u(x["W_u"].to(DEV), x["k_raw"].to(DEV))
+    B, H, d = cfg.B, cfg.H, cfg.d
+    outs = (torch.empty_like(q), torch.empty((B, H, d, d), device=DEV), torch.empty((B, H, d, d), device=DEV),
+            torch.empty((B, H, d), device=DEV), torch.empty((B, H, 4), device=DEV, dtype=torch.int32))
+    ws = torch.empty(workspace_size(B, H, cfg.T, d, cfg.r, q.dtype, nudge_period=cfg.nudge_period,
+                                    s_cap=cfg.s_cap), device=DEV, dtype=torch.uint8)
+    runs = []
+    for _ in range(3):
+        scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=outs, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in outs])
+    for later in runs[1:]:
+        for a, b in zip(runs[0], later):
+            assert torch.equal(a, b)
 
 
 # ---------------------------------------------------------------------------
