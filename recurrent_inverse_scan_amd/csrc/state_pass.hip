@@ -728,69 +728,125 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
 }
 
 // ---- readout: o for every block in parallel --------------------------------
+// Per block, with tiles tt (tokens) x ti (features) of 32 x 32, one per wave:
+//   o_t = (sigma_t (S_b q_t) + sum_{s<=t} P'[t][s] v_s) / den_t,
+//   P'[t][s] = (alpha_s . q_t) sigma_t / sigma_{s-1},  den_t = q_t . n_b + ld_t + den_eps.
+// The three products run on the bf16 matrix cores with three-term splits of
+// their fp32 operands (q and v are exact when stored as bf16).  Wave (tt, ts)
+// with ts <= tt computes the P' tile (tt, ts); the tile above the diagonal
+// is zero.  LDS rows are padded so row-per-lane 16-byte reads do not collide.
+template <typename TIn>
+struct ReadoutLds {
+  static constexpr int kQd = sizeof(TIn) == 2 ? 72 : 68;   // row stride (elements) of q and v^T rows
+  static constexpr size_t kBytes = 2 * kLb * kQd * sizeof(TIn) + 3 * kLb * kLd * sizeof(float) + 4 * kLb * sizeof(float);
+};
+
+// Operand of 8 consecutive values at p: exact bf16 for bf16 storage, a
+// three-term split for fp32.
+__device__ __forceinline__ bf16x8 operand8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ Split3 operand8(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split3(x);
+}
+
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
 vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
                          int32_t* __restrict__ stats) {
+  constexpr int kQd = ReadoutLds<TIn>::kQd;
   extern __shared__ float4 smem4[];
-  float* Ql = reinterpret_cast<float*>(smem4);
-  float* Xl = Ql + kLb * kLd;
-  float* Al = Xl + kD * kLd;
-  float* Vl = Al + kLb * kLd;
-  float* Pl = Vl + kLb * kLd;
-  float* wl = Pl + kLb * kLd;      // [64] log2 sigma_{s-1} (block-local)
-  float* sl = wl + kLb;            // [64] log2 sigma_t
-  float* dl = sl + kLb;            // [64] den_t
-  float* nl = dl + kLb;            // [64] n at the block start
+  TIn* Qs = reinterpret_cast<TIn*>(smem4);          // [64 t][kQd] q rows
+  TIn* Vt = Qs + kLb * kQd;                         // [64 i][kQd] v transposed (rows = features)
+  float* Xs = reinterpret_cast<float*>(Vt + kD * kQd);   // [64 i][kLd] S_b rows
+  float* As = Xs + kD * kLd;                        // [64 s][kLd] alpha_hat rows
+  float* Ps = As + kLb * kLd;                       // [64 t][kLd] P'
+  float* wl = Ps + kLb * kLd;                       // [64] log2 sigma_{s-1} (block-local)
+  float* sl = wl + kLb;                             // [64] log2 sigma_t
+  float* dl = sl + kLb;                             // [64] den_t
+  float* nl = dl + kLb;                             // [64] n at the block start
   const int64_t chain = blockIdx.x / pl.nblk;
   const int b = blockIdx.x % pl.nblk;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
   const int64_t row0 = chain * pl.T + tb;
-  stage_block<TIn>(Ql, q + row0 * kD, tcount, tid);
-  stage_block<float>(Xl, pl.Xsnap + (chain * pl.nblk + b) * kD * kD, kD, tid);
-  stage_block<float>(Al, pl.alpha + row0 * kD, tcount, tid);
-  if (pl.bf16)
-    stage_block<uint16_t>(Vl, static_cast<const uint16_t*>(pl.v) + row0 * kD, tcount, tid);
-  else
-    stage_block<float>(Vl, static_cast<const float*>(pl.v) + row0 * kD, tcount, tid);
+  const int64_t blk = chain * pl.nblk + b;
+  constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));   // elements per 16 bytes
+  {
+    // q rows and v^T (v is read as rows and written transposed).
+    const TIn* qg = q + row0 * kD;
+    const TIn* vg = static_cast<const TIn*>(pl.v) + row0 * kD;
+    for (int e = tid; e < kLb * kD / EPV; e += kThreads) {
+      const int r = e / (kD / EPV), c = (e % (kD / EPV)) * EPV;
+      uint4 xq = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+      if (r < tcount) {
+        xq = *reinterpret_cast<const uint4*>(qg + r * kD + c);
+        xv = *reinterpret_cast<const uint4*>(vg + r * kD + c);
+      }
+      *reinterpret_cast<uint4*>(Qs + r * kQd + c) = xq;
+      const TIn* xe = reinterpret_cast<const TIn*>(&xv);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) Vt[(c + k) * kQd + r] = xe[k];
+    }
+    stage_block<float>(Xs, pl.Xsnap + blk * kD * kD, kD, tid);
+    stage_block<float>(As, pl.alpha + row0 * kD, tcount, tid);
+  }
   if (tid < kLb) {
     const bool ok = tid < tcount;
     wl[tid] = ok ? pl.wsig[2 * (row0 + tid)] : 0.f;
     sl[tid] = ok ? pl.wsig[2 * (row0 + tid) + 1] : 0.f;
-    nl[tid] = pl.nblock[(chain * pl.nblk + b) * kD + tid];
+    nl[tid] = pl.nblock[blk * kD + tid];
   }
   __syncthreads();
   if (tid < kLb) {
     float acc = 0.f;
-    for (int i = 0; i < kD; ++i) acc = fmaf(Ql[tid * kLd + i], nl[i], acc);
+    for (int i = 0; i < kD; ++i) acc = fmaf(Elem<TIn>::load(Qs + tid * kQd + i), nl[i], acc);
     dl[tid] = acc + (tid < tcount ? pl.ld[row0 + tid] : 0.f) + den_eps;
   }
 
-  const int tt = w >> 1, ti = w & 1;   // output tile: tokens tt, features ti
-  f32x16 Z = zero16();
-  mma_rr(Z, Ql + tt * 32 * kLd, Xl + ti * 32 * kLd, lane);   // (X_b q_t)_i
-  if (ti == 0) {
-    // P'[t][s] = (sigma_t / sigma_{s-1}) (alpha_s . q_t) for s <= t.
-    const int scol = lane & 31;
-    for (int ts = 0; ts < 2; ++ts) {
-      f32x16 P = zero16();
-      mma_rr(P, Ql + tt * 32 * kLd, Al + ts * 32 * kLd, lane);
-      const int s = ts * 32 + scol;
+  const int tt = w >> 1, ti = w & 1;   // this wave's output tile; its P' tile is (tt, ts = ti)
+  const int rl = lane & 31;
+  // P'(tt, ts) for ts <= tt: A = q rows of tile tt, B[k=j][n=s] = alpha_hat[s][j].
+  if (ti <= tt) {
+    f32x16 P = zero16();
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int t = tt * 32 + acc_row(a, h);
-        Pl[t * kLd + s] = (s <= t) ? P[a] * exp2f(sl[t] - wl[s]) : 0.f;
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      const auto a = operand8(Qs + (tt * 32 + rl) * kQd + 16 * kb + 8 * h);
+      const Split3 bb = operand8(As + (ti * 32 + rl) * kLd + 16 * kb + 8 * h);
+      P = mma_split(a, bb, P);
+    }
+    const int s = ti * 32 + rl;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int t = tt * 32 + acc_row(a, h);
+      Ps[t * kLd + s] = (s <= t) ? P[a] * exp2f(sl[t] - wl[s]) : 0.f;
     }
   }
-  // sigma_t S_b q_t
+  // sigma_t S_b q_t: A = q rows, B[k=j][n=i] = S_b[i][j].
+  f32x16 Z = zero16();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const auto a = operand8(Qs + (tt * 32 + rl) * kQd + 16 * kb + 8 * h);
+    const Split3 bb = operand8(Xs + (ti * 32 + rl) * kLd + 16 * kb + 8 * h);
+    Z = mma_split(a, bb, Z);
+  }
 #pragma unroll
   for (int a = 0; a < 16; ++a) Z[a] *= exp2f(sl[tt * 32 + acc_row(a, h)]);
   __syncthreads();
-  mma_rc(Z, Pl + tt * 32 * kLd, Vl + ti * 32, lane);
+  // + sum_s P'[t][s] v_s over the tiles ts <= tt: A = P' rows, B[k=s][n=i] = v^T[i][s].
+  for (int ts = 0; ts <= tt; ++ts) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const Split3 a = operand8(Ps + (tt * 32 + rl) * kLd + ts * 32 + 16 * kb + 8 * h);
+      const auto bb = operand8(Vt + (ti * 32 + rl) * kQd + ts * 32 + 16 * kb + 8 * h);
+      Z = mma_split(a, bb, Z);
+    }
+  }
   bool bad = false;
-  const int fcol = ti * 32 + (lane & 31);
+  const int fcol = ti * 32 + rl;
 #pragma unroll
   for (int a = 0; a < 16; ++a) {
     const int t = tt * 32 + acc_row(a, h);
@@ -808,7 +864,8 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
 
 size_t state_prep_lds_bytes() { return sizeof(float) * 4 * kLb * kLd; }
 
-size_t state_readout_lds_bytes() { return sizeof(float) * (5 * kLb * kLd + 4 * kLb); }
+template <typename TIn>
+size_t state_readout_lds_bytes() { return ReadoutLds<TIn>::kBytes; }
 
 template <typename K>
 static void allow_lds(K kernel, size_t bytes) {
@@ -822,8 +879,8 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
   static const bool once = [] {
     allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes());
     allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes());
-    allow_lds(vla_state_readout_kernel<uint16_t>, state_readout_lds_bytes());
-    allow_lds(vla_state_readout_kernel<float>, state_readout_lds_bytes());
+    allow_lds(vla_state_readout_kernel<uint16_t>, state_readout_lds_bytes<uint16_t>());
+    allow_lds(vla_state_readout_kernel<float>, state_readout_lds_bytes<float>());
     return true;
   }();
   (void)once;
@@ -846,11 +903,11 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
                        pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes(),
+    hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<uint16_t>(),
                        stream, pl, static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.o), a.den_eps,
                        a.stats);
   else
-    hipLaunchKernelGGL(vla_state_readout_kernel<float>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes(),
+    hipLaunchKernelGGL(vla_state_readout_kernel<float>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<float>(),
                        stream, pl, static_cast<const float*>(a.q), static_cast<float*>(a.o), a.den_eps, a.stats);
   return hipGetLastError();
 }
