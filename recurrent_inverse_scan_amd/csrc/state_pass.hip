@@ -113,170 +113,7 @@ __device__ __forceinline__ void mma_rc(f32x16& acc, const float* A, const float*
   }
 }
 
-// Copies rows [0, nvalid) of a [64][64] block (global, contiguous rows of 64)
-// into LDS as float32 with stride kLd; rows past nvalid become zero.
-template <typename T>
-__device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, int tid) {
-  constexpr int EPV = Elem<T>::kPer16B;
-  for (int e = tid; e < kLb * kD / EPV; e += kThreads) {
-    const int row = e / (kD / EPV), c = (e % (kD / EPV)) * EPV;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (row < nvalid) x = *reinterpret_cast<const uint4*>(g + row * kD + c);
-    float* dst = lds + row * kLd + c;
-    if constexpr (EPV == 4) {
-      *reinterpret_cast<uint4*>(dst) = x;
-    } else {
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        dst[2 * h] = __uint_as_float(w[h] << 16);
-        dst[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
-      }
-    }
-  }
-}
-
-// ---- prep: kernel matrices, local normaliser terms, block key sums ---------
-// Per block b of 64 tokens:
-//   pack      = CK[t][j] = sum_{s<j} K(t,s), K(t,s) = (v_t.v_s)(alpha_t.alpha_s)
-//               (exclusive row prefix), then K(t,t), sum_s K(t,s) and
-//               sum_t k_t as three more rows
-//   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
-//   ld[t]     = sum_{s<=t in block} k_s.q_t
-//   VT, AT    = v and alpha_hat of the block regrouped as the chain kernel's
-//               matrix-core operands of its rank-64 update: fragment
-//               (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e, e < 8, of
-//               feature 32 c + lane % 32.
-template <typename TIn>
-__global__ void __launch_bounds__(kThreads)
-vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
-                      const TIn* __restrict__ v) {
-  extern __shared__ float4 smem4[];
-  float* Vl = reinterpret_cast<float*>(smem4);
-  float* Al = Vl + kLb * kLd;
-  float* Ql = Al + kLb * kLd;
-  float* Kl = Ql + kLb * kLd;
-  const int64_t chain = blockIdx.x / pl.nblk;
-  const int b = blockIdx.x % pl.nblk;
-  const int64_t blk = chain * pl.nblk + b;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
-  const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
-  const int64_t row0 = chain * pl.T + tb;
-  stage_block<TIn>(Vl, v + row0 * kD, tcount, tid);
-  stage_block<float>(Al, pl.alpha + row0 * kD, tcount, tid);
-  stage_block<TIn>(Ql, q + row0 * kD, tcount, tid);
-  stage_block<TIn>(Kl, k + row0 * kD, tcount, tid);
-  __syncthreads();
-
-  const int ti = w >> 1, tj = w & 1;
-  f32x16 gv = zero16(), ga = zero16(), pk = zero16();
-  mma_rr(gv, Vl + ti * 32 * kLd, Vl + tj * 32 * kLd, lane);
-  mma_rr(ga, Al + ti * 32 * kLd, Al + tj * 32 * kLd, lane);
-  mma_rr(pk, Ql + ti * 32 * kLd, Kl + tj * 32 * kLd, lane);   // q_t . k_s
-  float* pack = pl.Kmat + blk * kPackRows * kLb;
-  if (tid < kLb) {
-    float acc = 0.f;
-    for (int t = 0; t < tcount; ++t) acc += Kl[t * kLd + tid];
-    pack[kRowKs * kLb + tid] = acc;
-    pack[67 * kLb + tid] = 0.f;
-  }
-  // Matrix-core operands of the chain kernel's update (features of v and
-  // alpha_hat are LDS columns here).
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int f = tid + 256 * rep, c = f >> 8, kb = (f >> 6) & 3, fl = f & 63;
-    const int t0 = 16 * kb + 8 * (fl >> 5), feat = 32 * c + (fl & 31);
-    float xv[8], xa[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xv[e] = Vl[(t0 + e) * kLd + feat];
-      xa[e] = Al[(t0 + e) * kLd + feat];
-    }
-    float4* ad = reinterpret_cast<float4*>(pl.AT + (blk * 512 + f) * 8);
-    ad[0] = make_float4(xa[0], xa[1], xa[2], xa[3]);
-    ad[1] = make_float4(xa[4], xa[5], xa[6], xa[7]);
-    if constexpr (sizeof(TIn) == 2) {
-      uint32_t p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = (__float_as_uint(xv[2 * e]) >> 16) | (__float_as_uint(xv[2 * e + 1]) & 0xffff0000u);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(pl.VT) + (blk * 512 + f) * 8) = make_uint4(p[0], p[1], p[2], p[3]);
-    } else {
-      float4* vd = reinterpret_cast<float4*>(static_cast<float*>(pl.VT) + (blk * 512 + f) * 8);
-      vd[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
-      vd[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
-    }
-  }
-  __syncthreads();   // Ql and Kl are free from here on
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int t = ti * 32 + acc_row(s, h), col = tj * 32 + (lane & 31);
-    Ql[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
-    Kl[t * kLd + col] = gv[s] * ga[s];
-  }
-  __syncthreads();
-  if (tid < kLb) {
-    // Row t of K -> exclusive prefix sums in place.
-    const int t = tid;
-    float run = 0.f, e_t = 0.f;
-    for (int s = 0; s < kLb; ++s) {
-      const float x = Kl[t * kLd + s];
-      e_t = (s == t) ? x : e_t;
-      Kl[t * kLd + s] = run;
-      run += x;
-    }
-    pack[kRowE * kLb + t] = e_t;
-    pack[kRowTot * kLb + t] = run;
-  } else if (tid < 2 * kLb) {
-    const int t = tid - kLb;
-    float acc = 0.f;
-    for (int s = 0; s < kLb; ++s) acc += Ql[t * kLd + s];
-    if (t < tcount) pl.ld[row0 + t] = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rep = 0; rep < 4; ++rep) {
-    const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
-    *reinterpret_cast<float4*>(pack + r * kLb + c4) = *reinterpret_cast<const float4*>(Kl + r * kLd + c4);
-  }
-  if (b == 0) return;   // uniform
-  // Cross-block kernel, s in the previous (always full) block.
-  __syncthreads();
-  stage_block<TIn>(Kl, v + (row0 - kLb) * kD, kLb, tid);
-  stage_block<float>(Ql, pl.alpha + (row0 - kLb) * kD, kLb, tid);
-  __syncthreads();
-  f32x16 xv = zero16(), xa = zero16();
-  mma_rr(xv, Vl + ti * 32 * kLd, Kl + tj * 32 * kLd, lane);
-  mma_rr(xa, Al + ti * 32 * kLd, Ql + tj * 32 * kLd, lane);
-  float* Xout = pl.Kcross + blk * kLb * kLb;
-  const int col = tj * 32 + (lane & 31);
-#pragma unroll
-  for (int s = 0; s < 16; ++s) Xout[(ti * 32 + acc_row(s, h)) * kLb + col] = xv[s] * xa[s];
-}
-
-// ---- chain: the sequential part, one workgroup per chain ---------------------
-// Five waves.  Wave 0 (the recursion wave) runs the cap recursion of block b.
-// Waves 1-4 (the product waves) each own a 32x32 tile of S and, during the
-// same time, apply block b-1's rank-64 update (S_b from S_{b-1}) and compute
-// the next block's bilinear terms v_t^T S_b alpha_t, one block behind; the
-// recursion wave repairs the lag exactly with the cross-block kernel:
-//     v_t^T S_{b+1} alpha_t = sigma_end(b) v_t^T S_b alpha_t
-//                            + sum_{s in b} (sigma_end(b)/sigma_{s-1}) Kx(t,s).
-//
-// Both products run on the bf16 matrix cores at fp32-grade accuracy: an fp32
-// operand x is split into three bf16 terms x = x1 + x2 + x3 (each the
-// round-to-nearest bf16 of what remains; the residuals are exact in fp32, so
-// the split is exact to about 2^-27 |x|), bf16 v is exact as it stands, and
-// the partial products (all pairs of terms whose orders add up to at most 2)
-// accumulate in fp32.
-//
-// Staging is register-free: v and alpha_hat rows (for the bilinear terms) and
-// the prefix-summed K and Kx (for the recursion) go from memory straight into
-// LDS with buffer-to-LDS loads, two generations deep, in 16-byte chunks whose
-// position within a row is XOR-swizzled by the row index (conflict-free
-// row-per-lane reads).  The update's operands come from the prep kernel's
-// regrouped copies into registers, one block ahead.  One barrier per block.
-constexpr int kChainThreads = 320;
-
+// ---- bf16 matrix-core products at fp32-grade accuracy ------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -323,6 +160,214 @@ __device__ __forceinline__ f32x16 mma_split(const Split3& a, bf16x8 b, f32x16 ac
   acc = mfma_bf16(a.t2, b, acc);
   return mfma_bf16(a.t1, b, acc);
 }
+
+// acc += A B with both operands exact in bf16.
+__device__ __forceinline__ f32x16 mma_split(bf16x8 a, bf16x8 b, f32x16 acc) { return mfma_bf16(a, b, acc); }
+
+// Operand of 8 consecutive values at p: exact bf16 for bf16 storage, a
+// three-term split for fp32.
+__device__ __forceinline__ bf16x8 operand8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ Split3 operand8(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split3(x);
+}
+
+// Copies rows [0, nvalid) of a [64][64] block (global, contiguous rows of 64)
+// into LDS as float32 with stride kLd; rows past nvalid become zero.
+template <typename T>
+__device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, int tid) {
+  constexpr int EPV = Elem<T>::kPer16B;
+  for (int e = tid; e < kLb * kD / EPV; e += kThreads) {
+    const int row = e / (kD / EPV), c = (e % (kD / EPV)) * EPV;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (row < nvalid) x = *reinterpret_cast<const uint4*>(g + row * kD + c);
+    float* dst = lds + row * kLd + c;
+    if constexpr (EPV == 4) {
+      *reinterpret_cast<uint4*>(dst) = x;
+    } else {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        dst[2 * h] = __uint_as_float(w[h] << 16);
+        dst[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// ---- prep: kernel matrices, local normaliser terms, block key sums ---------
+// Per block b of 64 tokens:
+//   pack      = CK[t][j] = sum_{s<j} K(t,s), K(t,s) = (v_t.v_s)(alpha_t.alpha_s)
+//               (exclusive row prefix), then K(t,t), sum_s K(t,s) and
+//               sum_t k_t as three more rows
+//   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
+//   ld[t]     = sum_{s<=t in block} k_s.q_t
+//   VT, AT    = v and alpha_hat of the block regrouped as the chain kernel's
+//               matrix-core operands of its rank-64 update: fragment
+//               (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e, e < 8, of
+//               feature 32 c + lane % 32.
+// The Gram products run on the bf16 matrix cores: v.v and q.k exactly when
+// stored as bf16, alpha.alpha (and fp32-stored inputs) through three-term splits.
+template <typename TIn>
+struct PrepLds {
+  static constexpr int kRd = sizeof(TIn) == 2 ? 72 : 68;   // row stride of storage-dtype rows (16-byte aligned)
+  static constexpr size_t kBytes = 4 * kLb * kRd * sizeof(TIn) + 2 * kLb * kLd * sizeof(float);
+};
+
+// Copies rows [0, nvalid) of a [64][64] block in its own dtype into LDS rows
+// of the given stride; rows past nvalid become zero.
+template <typename T>
+__device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int tid, int stride) {
+  constexpr int EPV = 16 / static_cast<int>(sizeof(T));
+  for (int e = tid; e < kLb * kD / EPV; e += kThreads) {
+    const int row = e / (kD / EPV), c = (e % (kD / EPV)) * EPV;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (row < nvalid) x = *reinterpret_cast<const uint4*>(g + row * kD + c);
+    *reinterpret_cast<uint4*>(lds + row * stride + c) = x;
+  }
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
+                      const TIn* __restrict__ v) {
+  constexpr int kRd = PrepLds<TIn>::kRd;
+  extern __shared__ float4 smem4[];
+  TIn* Vb = reinterpret_cast<TIn*>(smem4);    // [64][kRd] v rows of the block
+  TIn* Qb = Vb + kLb * kRd;                   // q rows
+  TIn* Kb = Qb + kLb * kRd;                   // k rows
+  TIn* Vp = Kb + kLb * kRd;                   // v rows of the previous block
+  float* Af = reinterpret_cast<float*>(Vp + kLb * kRd);   // [64][kLd] alpha_hat rows, later K
+  float* Ap = Af + kLb * kLd;                 // previous block's alpha_hat rows, later masked q.k
+  const int64_t chain = blockIdx.x / pl.nblk;
+  const int b = blockIdx.x % pl.nblk;
+  const int64_t blk = chain * pl.nblk + b;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
+  const int64_t row0 = chain * pl.T + tb;
+  stage_rows<TIn>(Vb, v + row0 * kD, tcount, tid, kRd);
+  stage_rows<TIn>(Qb, q + row0 * kD, tcount, tid, kRd);
+  stage_rows<TIn>(Kb, k + row0 * kD, tcount, tid, kRd);
+  stage_block<float>(Af, pl.alpha + row0 * kD, tcount, tid);
+  if (b > 0) {   // uniform; the previous block is always full
+    stage_rows<TIn>(Vp, v + (row0 - kLb) * kD, kLb, tid, kRd);
+    stage_block<float>(Ap, pl.alpha + (row0 - kLb) * kD, kLb, tid);
+  }
+  __syncthreads();
+
+  const int ti = w >> 1, tj = w & 1, rl = lane & 31;
+  f32x16 gv = zero16(), ga = zero16(), pk = zero16(), xv = zero16(), xa = zero16();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int c0 = 16 * kb + 8 * h;
+    const auto va = operand8(Vb + (ti * 32 + rl) * kRd + c0);
+    gv = mma_split(va, operand8(Vb + (tj * 32 + rl) * kRd + c0), gv);
+    const Split3 aa = operand8(Af + (ti * 32 + rl) * kLd + c0);
+    ga = mma_split(aa, operand8(Af + (tj * 32 + rl) * kLd + c0), ga);
+    pk = mma_split(operand8(Qb + (ti * 32 + rl) * kRd + c0), operand8(Kb + (tj * 32 + rl) * kRd + c0), pk);   // q_t . k_s
+    if (b > 0) {
+      xv = mma_split(va, operand8(Vp + (tj * 32 + rl) * kRd + c0), xv);
+      xa = mma_split(aa, operand8(Ap + (tj * 32 + rl) * kLd + c0), xa);
+    }
+  }
+  float* pack = pl.Kmat + blk * kPackRows * kLb;
+  if (tid < kLb) {
+    float acc = 0.f;
+    for (int t = 0; t < tcount; ++t) acc += Elem<TIn>::load(Kb + t * kRd + tid);
+    pack[kRowKs * kLb + tid] = acc;
+    pack[67 * kLb + tid] = 0.f;
+  }
+  // Matrix-core operands of the chain kernel's update (features of v and
+  // alpha_hat are LDS columns here).
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int f = tid + 256 * rep, c = f >> 8, kb = (f >> 6) & 3, fl = f & 63;
+    const int t0 = 16 * kb + 8 * (fl >> 5), feat = 32 * c + (fl & 31);
+    float xa8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xa8[e] = Af[(t0 + e) * kLd + feat];
+    float4* ad = reinterpret_cast<float4*>(pl.AT + (blk * 512 + f) * 8);
+    ad[0] = make_float4(xa8[0], xa8[1], xa8[2], xa8[3]);
+    ad[1] = make_float4(xa8[4], xa8[5], xa8[6], xa8[7]);
+    if constexpr (sizeof(TIn) == 2) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pw[e] = static_cast<uint32_t>(Vb[(t0 + 2 * e) * kRd + feat]) | (static_cast<uint32_t>(Vb[(t0 + 2 * e + 1) * kRd + feat]) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(pl.VT) + (blk * 512 + f) * 8) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    } else {
+      float4* vd = reinterpret_cast<float4*>(static_cast<float*>(pl.VT) + (blk * 512 + f) * 8);
+      vd[0] = make_float4(Vb[t0 * kRd + feat], Vb[(t0 + 1) * kRd + feat], Vb[(t0 + 2) * kRd + feat], Vb[(t0 + 3) * kRd + feat]);
+      vd[1] = make_float4(Vb[(t0 + 4) * kRd + feat], Vb[(t0 + 5) * kRd + feat], Vb[(t0 + 6) * kRd + feat], Vb[(t0 + 7) * kRd + feat]);
+    }
+  }
+  const int col = tj * 32 + rl;
+  if (b > 0) {
+    float* Xout = pl.Kcross + blk * kLb * kLb;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) Xout[(ti * 32 + acc_row(s, h)) * kLb + col] = xv[s] * xa[s];
+  }
+  __syncthreads();   // Af and Ap are free from here on
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int t = ti * 32 + acc_row(s, h);
+    Ap[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
+    Af[t * kLd + col] = gv[s] * ga[s];
+  }
+  __syncthreads();
+  if (tid < kLb) {
+    // Row t of K -> exclusive prefix sums in place.
+    const int t = tid;
+    float run = 0.f, e_t = 0.f;
+    for (int s = 0; s < kLb; ++s) {
+      const float x = Af[t * kLd + s];
+      e_t = (s == t) ? x : e_t;
+      Af[t * kLd + s] = run;
+      run += x;
+    }
+    pack[kRowE * kLb + t] = e_t;
+    pack[kRowTot * kLb + t] = run;
+  } else if (tid < 2 * kLb) {
+    const int t = tid - kLb;
+    float acc = 0.f;
+    for (int s = 0; s < kLb; ++s) acc += Ap[t * kLd + s];
+    if (t < tcount) pl.ld[row0 + t] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rep = 0; rep < 4; ++rep) {
+    const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<float4*>(pack + r * kLb + c4) = *reinterpret_cast<const float4*>(Af + r * kLd + c4);
+  }
+}
+
+// ---- chain: the sequential part, one workgroup per chain ---------------------
+// Five waves.  Wave 0 (the recursion wave) runs the cap recursion of block b.
+// Waves 1-4 (the product waves) each own a 32x32 tile of S and, during the
+// same time, apply block b-1's rank-64 update (S_b from S_{b-1}) and compute
+// the next block's bilinear terms v_t^T S_b alpha_t, one block behind; the
+// recursion wave repairs the lag exactly with the cross-block kernel:
+//     v_t^T S_{b+1} alpha_t = sigma_end(b) v_t^T S_b alpha_t
+//                            + sum_{s in b} (sigma_end(b)/sigma_{s-1}) Kx(t,s).
+//
+// Both products run on the bf16 matrix cores at fp32-grade accuracy: an fp32
+// operand x is split into three bf16 terms x = x1 + x2 + x3 (each the
+// round-to-nearest bf16 of what remains; the residuals are exact in fp32, so
+// the split is exact to about 2^-27 |x|), bf16 v is exact as it stands, and
+// the partial products (all pairs of terms whose orders add up to at most 2)
+// accumulate in fp32.
+//
+// Staging is register-free: v and alpha_hat rows (for the bilinear terms) and
+// the prefix-summed K and Kx (for the recursion) go from memory straight into
+// LDS with buffer-to-LDS loads, two generations deep, in 16-byte chunks whose
+// position within a row is XOR-swizzled by the row index (conflict-free
+// row-per-lane reads).  The update's operands come from the prep kernel's
+// regrouped copies into registers, one block ahead.  One barrier per block.
+constexpr int kChainThreads = 320;
 
 __device__ __forceinline__ void to_floats(uint4 x, float (&f)[8]) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -741,17 +786,6 @@ struct ReadoutLds {
   static constexpr size_t kBytes = 2 * kLb * kQd * sizeof(TIn) + 3 * kLb * kLd * sizeof(float) + 4 * kLb * sizeof(float);
 };
 
-// Operand of 8 consecutive values at p: exact bf16 for bf16 storage, a
-// three-term split for fp32.
-__device__ __forceinline__ bf16x8 operand8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-__device__ __forceinline__ Split3 operand8(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  return split3(x);
-}
-
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
 vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
@@ -862,7 +896,8 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
 
 }  // namespace
 
-size_t state_prep_lds_bytes() { return sizeof(float) * 4 * kLb * kLd; }
+template <typename TIn>
+size_t state_prep_lds_bytes() { return PrepLds<TIn>::kBytes; }
 
 template <typename TIn>
 size_t state_readout_lds_bytes() { return ReadoutLds<TIn>::kBytes; }
@@ -877,8 +912,8 @@ static void allow_lds(K kernel, size_t bytes) {
 hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
                              hipStream_t stream) {
   static const bool once = [] {
-    allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes());
-    allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes());
+    allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes<uint16_t>());
+    allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes<float>());
     allow_lds(vla_state_readout_kernel<uint16_t>, state_readout_lds_bytes<uint16_t>());
     allow_lds(vla_state_readout_kernel<float>, state_readout_lds_bytes<float>());
     return true;
@@ -886,11 +921,11 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
   (void)once;
   const unsigned blocks = static_cast<unsigned>(chains * pl.nblk);
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_prep_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes(), stream,
+    hipLaunchKernelGGL(vla_state_prep_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<uint16_t>(), stream,
                        pl, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v));
   else
-    hipLaunchKernelGGL(vla_state_prep_kernel<float>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes(), stream,
+    hipLaunchKernelGGL(vla_state_prep_kernel<float>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<float>(), stream,
                        pl, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                        static_cast<const float*>(a.v));
   hipError_t e = hipGetLastError();
