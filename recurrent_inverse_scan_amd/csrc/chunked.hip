@@ -18,9 +18,10 @@
 //
 // Kernels, in stream order:
 //   vla_chunk_gram_kernel   G_c for every chunk (MFMA, fp32 accumulation)
-//   vla_chunk_chain_kernel  per chain, sequential over chunks, fp64: prefix
-//                           sums of G inside a nudge period, (N, D) at every
-//                           period start
+//   vla_chunk_scan_kernel   fp64 prefix sums of G inside each nudge period and
+//                           each period's total, in parallel over elements
+//   vla_chunk_chain_kernel  per chain, sequential over periods, fp64: (N, D)
+//                           at every period start
 //   vla_chunk_start_kernel  per chunk, fp64: A_c by Gauss-Jordan elimination
 //                           of [ D_c^T | N_p^T ]; a non-positive pivot flags
 //                           the chain for the sequential fallback
@@ -112,17 +113,59 @@ vla_chunk_gram_kernel(const TIn* __restrict__ u, float* __restrict__ G, int T, i
   }
 }
 
+// ---- Gram prefixes ----------------------------------------------------------
+// Segmented exclusive prefix over the chunks of each nudge period, in fp64:
+// Gpre_c = sum of G_c' over the earlier chunks c' of c's period, and Gtot_p =
+// the whole period's sum.  One thread per (chain, matrix element); the chunk
+// loop is sequential only through the running sum, so loads are issued eight
+// chunks ahead.
+__global__ void __launch_bounds__(256)
+vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, double* __restrict__ Gtot,
+                      int64_t chains, int nchunks, int nperiods, int o, int q) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= chains * kD * kD) return;
+  const int64_t chain = idx / (kD * kD);
+  const int e = static_cast<int>(idx % (kD * kD));
+  const float* g = G + chain * nchunks * kD * kD + e;
+  double* gp = Gpre + chain * nchunks * kD * kD + e;
+  double* gt = Gtot + chain * nperiods * kD * kD + e;
+  double acc = 0.0;
+  int p = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {
+    float gv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gv[k] = (c0 + k < nchunks) ? g[static_cast<int64_t>(c0 + k) * kD * kD] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = c0 + k;
+      if (c < nchunks) {
+        const int pc = period_of(c, o, q);
+        if (pc != p) {
+          gt[static_cast<int64_t>(p) * kD * kD] = acc;
+          acc = 0.0;
+          p = pc;
+        }
+        gp[static_cast<int64_t>(c) * kD * kD] = acc;
+        acc += static_cast<double>(gv[k]);
+      }
+    }
+  }
+  gt[static_cast<int64_t>(p) * kD * kD] = acc;
+}
+
 // ---- (N, D) chain ---------------------------------------------------------
 // One workgroup per chain, 256 threads, thread t owns the 4x4 block
-// (t/16, t%16) of N, D and the running Gram prefix.
+// (t/16, t%16) of N and D.  Between periods p and p+1: D += Gtot_p N, then
+// the nudge N += eps D.  The next period's Gram total is loaded one period
+// ahead.
 __global__ void __launch_bounds__(kChunkThreads)
-vla_chunk_chain_kernel(const float* __restrict__ G, const float* __restrict__ A0, double* __restrict__ Gpre,
-                       double* __restrict__ ND, int nchunks, int nperiods, int o, int q, double eps) {
-  __shared__ double sG[kD * kD];   // Gram prefix, transposed: sG[m*kD + i] = Gacc[i][m]
+vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
+                       int nperiods, double eps) {
+  __shared__ double sG[kD * kD];   // period total, transposed: sG[m*kD + i] = Gtot[i][m]
   __shared__ double sN[kD * kD];
   const int64_t chain = blockIdx.x;
   const int t = threadIdx.x, bi = t >> 4, bj = t & 15;
-  double N[4][4], Dm[4][4], Ga[4][4];
+  double N[4][4], Dm[4][4], Gn[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -130,7 +173,6 @@ vla_chunk_chain_kernel(const float* __restrict__ G, const float* __restrict__ A0
       const int gi = 4 * bi + i, gj = 4 * bj + j;
       N[i][j] = static_cast<double>(A0[(chain * kD + gi) * kD + gj]);
       Dm[i][j] = gi == gj ? 1.0 : 0.0;
-      Ga[i][j] = 0.0;
     }
   auto store_nd = [&](int p) {
     double* nd = ND + (chain * nperiods + p) * 2 * kD * kD;
@@ -142,51 +184,42 @@ vla_chunk_chain_kernel(const float* __restrict__ G, const float* __restrict__ A0
         nd[kD * kD + (4 * bi + i) * kD + 4 * bj + j] = Dm[i][j];
       }
   };
+  auto load_g = [&](int p) {
+    const double* gt = Gtot + (chain * nperiods + p) * kD * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Gn[i][j] = gt[(4 * bi + i) * kD + 4 * bj + j];
+  };
   store_nd(0);
-  int p = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    double* gp = Gpre + (chain * nchunks + c) * kD * kD;
-    const float* gc = G + (chain * nchunks + c) * kD * kD;
+  if (nperiods > 1) load_g(0);
+  for (int p = 0; p + 1 < nperiods; ++p) {
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int idx = (4 * bi + i) * kD + 4 * bj + j;
-        gp[idx] = Ga[i][j];
-        Ga[i][j] += static_cast<double>(gc[idx]);
+        sG[(4 * bj + j) * kD + 4 * bi + i] = Gn[i][j];
+        sN[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
       }
-    if (c + 1 < nchunks && q > 0 && (o + c + 1) % q == 0) {
-      // D += Gacc N, then the nudge N += eps D; a new period starts.
-      __syncthreads();
+    __syncthreads();
+    if (p + 2 < nperiods) load_g(p + 1);
+    for (int m = 0; m < kD; ++m) {
+      double gcol[4], nrow[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gcol[i] = sG[m * kD + 4 * bi + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nrow[j] = sN[m * kD + 4 * bj + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sG[(4 * bj + j) * kD + 4 * bi + i] = Ga[i][j];
-          sN[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
-        }
-      __syncthreads();
-      for (int m = 0; m < kD; ++m) {
-        double gcol[4], nrow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gcol[i] = sG[m * kD + 4 * bi + i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) nrow[j] = sN[m * kD + 4 * bj + j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Dm[i][j] = fma(gcol[i], nrow[j], Dm[i][j]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          N[i][j] = fma(eps, Dm[i][j], N[i][j]);
-          Ga[i][j] = 0.0;
-        }
-      ++p;
-      store_nd(p);
+        for (int j = 0; j < 4; ++j) Dm[i][j] = fma(gcol[i], nrow[j], Dm[i][j]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) N[i][j] = fma(eps, Dm[i][j], N[i][j]);
+    store_nd(p + 1);
   }
 }
 
@@ -327,8 +360,14 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
     hipLaunchKernelGGL(vla_chunk_gram_kernel<float>, dim3(units), dim3(kChunkThreads), 0, stream,
                        static_cast<const float*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains), dim3(kChunkThreads), 0, stream, pl.G, pl.A_init,
-                     pl.Gpre, pl.ND, pl.nchunks, pl.nperiods, pl.o, pl.q, static_cast<double>(pl.eps));
+  {
+    const int64_t n = static_cast<int64_t>(pl.chains) * kD * kD;
+    hipLaunchKernelGGL(vla_chunk_scan_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains), dim3(kChunkThreads), 0, stream, pl.Gtot, pl.A_init,
+                     pl.ND, pl.nperiods, static_cast<double>(pl.eps));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(units), dim3(kChunkThreads), 0, stream, pl.Gpre, pl.ND, pl.Ac,
                      pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q);

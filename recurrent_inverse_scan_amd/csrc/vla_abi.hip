@@ -58,7 +58,7 @@ struct ChunkLayout {
   bool use = false;
   int L = 0, nchunks = 0, nperiods = 0, o = 0, q = 0;
   int nblk = 0;   // 64-token blocks of the state pass
-  size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_ND = 0, off_Ac = 0,
+  size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_Gtot = 0, off_ND = 0, off_Ac = 0,
          off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0, off_flag = 0,
          total = 0;
 };
@@ -108,6 +108,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_info = off; off = align_up(off + C * 4 * 4);
     cl.off_G = off; off = align_up(off + C * nch * d2 * 4);
     cl.off_Gpre = off; off = align_up(off + C * nch * d2 * 8);
+    cl.off_Gtot = off; off = align_up(off + C * static_cast<size_t>(cl.nperiods) * d2 * 8);
     cl.off_ND = off; off = align_up(off + C * static_cast<size_t>(cl.nperiods) * 2 * d2 * 8);
     cl.off_Ac = off; off = align_up(off + C * nch * d2 * 4);
     cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * 64 * 4);
@@ -297,6 +298,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   pl.chain_info = reinterpret_cast<int32_t*>(ws + cl.off_info);
   pl.G = reinterpret_cast<float*>(ws + cl.off_G);
   pl.Gpre = reinterpret_cast<double*>(ws + cl.off_Gpre);
+  pl.Gtot = reinterpret_cast<double*>(ws + cl.off_Gtot);
   pl.ND = reinterpret_cast<double*>(ws + cl.off_ND);
   pl.Ac = reinterpret_cast<float*>(ws + cl.off_Ac);
   pl.alpha = reinterpret_cast<float*>(ws + cl.off_alpha);

@@ -52,7 +52,8 @@ struct ChunkPlan {
   float* n_init;
   int32_t* chain_info;  // [chains][4]
   float* G;       // [chains][nchunks][64][64]
-  double* Gpre;   // [chains][nchunks][64][64]
+  double* Gpre;   // [chains][nchunks][64][64] Gram sum of the earlier chunks of the chunk's period
+  double* Gtot;   // [chains][nperiods][64][64] Gram sum of each period
   double* ND;     // [chains][nperiods][2][64][64]
   float* Ac;      // [chains][nchunks][64][64]
   float* alpha;   // [chains][T][64]
