@@ -8,16 +8,24 @@ already resident in HBM.  The workload is the long-context configuration
 tokens, Frobenius cap 1e3).
 
 Prints one JSON line.  ``value`` is tokens*heads per second of the whole step.
-``roofline`` reports the scan kernel (the dominant one) against the fp32
-vector ALU peak, with algorithmic flops 2*(2r+3)*d^2 per token*head.
-``cpu_baseline`` times the fp64 CPU oracle on a bounded prefix of the same
-workload.
+``roofline`` reports the dominant kernel, the state-chain kernel of the
+chunked schedule (the sequential S/cap recursion): its algorithmic flops are
+those of the memory update and the cap's norm, 2 d^2 + 2 d^2 per token*head,
+over its duration from HIP events the library records on the kernel's own
+stream during the timed steps; ``traffic`` is its HBM bytes per launch from
+rocprofv3 counters (profiles/state_chain_long_traffic.md), or null when the
+kernel sources have changed since they were taken.  ``scan_valu_frac`` is the
+whole scan's algorithmic flops 2 (2r+3) d^2 per token*head against the fp32
+vector peak.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded prefix
+of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,8 +38,41 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3   # 256 CU x 4 SIMD x 16 lanes x 2 (dual fp32) x
 HBM_PEAK_GBS = 8000.0
 
 
+CHAIN_SOURCES = ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_seq.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_chain_long_traffic.md")
+
+
 def alg_flops_per_token_head(d: int, r: int) -> int:
     return 2 * (2 * r + 3) * d * d
+
+
+def chain_flops_per_token_head(d: int, cap_on: bool) -> int:
+    """Memory update S += v alpha^T (d^2 FMA) plus the cap's |S|^2 (d^2 FMA)."""
+    return 2 * d * d + (2 * d * d if cap_on else 0)
+
+
+def chain_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in CHAIN_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_inverse_scan_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the chain kernel from the committed counter
+    summary, if it was taken on the current kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
+    if vals.get("source_sha256") != chain_source_sha():
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main(argv=None) -> int:
@@ -40,9 +81,12 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="long")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, one device-to-device copy of this many MiB (a known-size kernel "
+                         "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -52,7 +96,8 @@ def main(argv=None) -> int:
     import numpy as np
     import torch
 
-    from recurrent_inverse_scan_amd import CONFIGS, make_inputs, project_u, scan_forward, workspace_size
+    from recurrent_inverse_scan_amd import (CONFIGS, make_inputs, project_u, scan_forward, timing_collect,
+                                            timing_enable, workspace_size)
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -82,6 +127,7 @@ def main(argv=None) -> int:
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timing_enable(True)   # the library records HIP events around the chain kernel on its stream
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
@@ -89,14 +135,40 @@ def main(argv=None) -> int:
         print(f"[bench] step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
     t_end.record()
     torch.cuda.synchronize()
+    chain_ms_all = timing_collect()
+    timing_enable(False)
     total_ms = t_start.elapsed_time(t_end)
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms_per_step = total_ms / args.steps
+    chain_ms = sum(chain_ms_all) / len(chain_ms_all) if chain_ms_all else None
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read and written", file=sys.stderr,
+              flush=True)
+        del src, dst
 
     tok_heads = B * H * T
     value = tok_heads / (ms_per_step * 1e-3)
     flops = alg_flops_per_token_head(d, r) * tok_heads
     scan_tflops = flops / (scan_ms * 1e-3) / 1e12
+    cap_on = cfg.s_cap is not None and cfg.s_cap > 0
+    chain_flops = chain_flops_per_token_head(d, cap_on) * tok_heads
+    if chain_ms:
+        roofline = {"bound": "alu", "achieved": chain_flops / (chain_ms * 1e-3) / 1e12,
+                    "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": chain_flops / (chain_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                    "traffic": measured_traffic(),
+                    "kernel": "vla_state_chain_kernel", "kernel_ms": chain_ms,
+                    "flops_per_launch": chain_flops}
+    else:   # the sequential schedule has no chain kernel: the scan kernel is the dominant one
+        roofline = {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                    "kernel": "vla_scan_seq_kernel", "kernel_ms": scan_ms, "flops_per_launch": flops}
     es = 2 if cfg.in_dtype == "bf16" else 4
     scan_bytes = tok_heads * d * es * (4 + r) + 2 * B * H * (2 * d * d + d) * 4   # q,k,v,u in, o out, state
     stats = outs[4].cpu().numpy()
@@ -123,9 +195,10 @@ def main(argv=None) -> int:
                    "B": B, "H": H, "T": T, "d": d, "r": r, "storage": cfg.in_dtype,
                    "nudge_period": cfg.nudge_period, "s_cap": cfg.s_cap, "schedule": schedule,
                    "workspace_bytes": ws_bytes},
-        "roofline": {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None},
+        "roofline": roofline,
         "scan_ms": scan_ms,
+        "scan_tflops": scan_tflops,
+        "scan_valu_frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS,
         "projection_ms": ms_per_step - scan_ms,
         "scan_hbm_gbs": scan_bytes / (scan_ms * 1e-3) / 1e9,
         "guard_fires": int(stats[..., 0].sum()),
@@ -137,8 +210,9 @@ def main(argv=None) -> int:
 
 
 def cpu_baseline(cfg, x, budget_s: float):
-    """Time the fp64 oracle on all chains over a bounded prefix of the tokens."""
-    import numpy as np
+    """Time the fp64 oracle on all chains over a bounded prefix of the tokens,
+    with its BLAS held to one thread (the oracle's loops are single-threaded)."""
+    from threadpoolctl import threadpool_limits
 
     from oracle.vla_oracle import oracle_project_u, oracle_scan
 
@@ -152,17 +226,19 @@ def cpu_baseline(cfg, x, budget_s: float):
                     x["v"].reshape(C, cfg.T, d)[:, :n_tok], u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
         return time.perf_counter() - t0
 
-    probe = min(cfg.T, 256)
-    dt = run(probe)
-    n_tok = int(min(cfg.T, max(probe, probe * budget_s / max(dt, 1e-6))))
-    dt = run(n_tok)
+    with threadpool_limits(limits=1):
+        probe = min(cfg.T, 512)
+        dt = run(probe)
+        n_tok = int(min(cfg.T, max(probe, probe * budget_s / max(dt, 1e-6))))
+        if n_tok > probe:
+            dt = run(n_tok)
     try:
-        cores = len(os.sched_getaffinity(0))
+        visible = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count()
+        visible = os.cpu_count()
     return {"value": C * n_tok / dt, "unit": "tokens*heads/s", "cores": 1, "kind": "oracle",
             "sample": f"all {C} chains, first {n_tok} of {cfg.T} tokens (projection + scan), fp64 NumPy, "
-                      f"{dt:.1f} s wall; single-threaded loops ({cores} cores visible)"}
+                      f"{dt:.1f} s wall on 1 thread (BLAS limited to 1; {visible} cores visible)"}
 
 
 if __name__ == "__main__":

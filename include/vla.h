@@ -165,6 +165,28 @@ vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dt
                            vla_dtype_t out_dtype, const void* W_u, const void* k_raw,
                            void* u, void* stream);
 
+/*
+ * Measurement hook for the dominant kernel: the state-chain kernel of the
+ * chunked schedule (the sequential S/cap recursion, one workgroup per chain).
+ * Not part of the method; it serves benchmarks that must time that kernel on
+ * the stream it runs on.
+ *
+ * vla_timing_enable(1) creates VLA_TIMING_SLOTS pairs of HIP events on the
+ * device current at that moment and makes each following vla_scan_forward
+ * that runs the chunked schedule record one pair on its stream, immediately
+ * before and after that kernel, until the slots are used up (later calls are
+ * not recorded).  vla_timing_enable(0) stops recording and releases the
+ * events.  vla_timing_collect waits for the recorded events, writes up to
+ * `cap` durations in milliseconds to `ms` (oldest first), stores how many it
+ * wrote in *n and clears the record; recording continues if enabled.
+ *
+ * Errors: VLA_EINVAL for a NULL `ms` or `n` or a negative `cap`; VLA_EHIP if
+ * an event call fails.  The calls take a process-wide lock.
+ */
+#define VLA_TIMING_SLOTS 256
+vla_status_t vla_timing_enable(int32_t enable);
+vla_status_t vla_timing_collect(float* ms, int32_t cap, int32_t* n);
+
 /* Static string naming a status code. */
 const char* vla_status_string(vla_status_t s);
 

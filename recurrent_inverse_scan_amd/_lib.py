@@ -19,7 +19,7 @@ VLA_SCHEDULE_AUTO, VLA_SCHEDULE_SEQUENTIAL, VLA_SCHEDULE_CHUNKED = 0, 1, 2
 # Every symbol include/vla.h declares.
 EXPORTED = (
     "vla_scan_params_init", "vla_scan_workspace_size", "vla_scan_forward", "vla_project_u",
-    "vla_status_string", "vla_last_error", "vla_abi_version",
+    "vla_status_string", "vla_last_error", "vla_abi_version", "vla_timing_enable", "vla_timing_collect",
 )
 
 
@@ -73,6 +73,10 @@ def load() -> ctypes.CDLL:
     lib.vla_last_error.restype = ctypes.c_char_p
     lib.vla_abi_version.argtypes = []
     lib.vla_abi_version.restype = ctypes.c_int
+    lib.vla_timing_enable.argtypes = [i32]
+    lib.vla_timing_enable.restype = i32
+    lib.vla_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+    lib.vla_timing_collect.restype = i32
     _lib = lib
     return lib
 

@@ -131,3 +131,19 @@ def project_u(W_u, k_raw, out_dtype=None, out=None):
         _lib.check(lib.vla_project_u(rows, d, r, _DT[W_u.dtype], _DT[odt], _ptr(W_u), _ptr(k_raw), _ptr(out),
                                      _stream_ptr(k_raw.device)))
     return out
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop) recording HIP events around the state-chain kernel of
+    every chunked scan (the library's measurement hook)."""
+    _lib.check(_lib.load().vla_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> list:
+    """Durations in ms of the state-chain kernel for the recorded scans, oldest first."""
+    lib = _lib.load()
+    cap = 256
+    buf = (ctypes.c_float * cap)()
+    n = ctypes.c_int32(0)
+    _lib.check(lib.vla_timing_collect(buf, cap, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]

@@ -910,7 +910,7 @@ static void allow_lds(K kernel, size_t bytes) {
 }
 
 hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
-                             hipStream_t stream) {
+                             hipStream_t stream, hipEvent_t chain_start, hipEvent_t chain_stop) {
   static const bool once = [] {
     allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes<uint16_t>());
     allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes<float>());
@@ -930,6 +930,7 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
                        static_cast<const float*>(a.v));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (chain_start && (e = hipEventRecord(chain_start, stream)) != hipSuccess) return e;
   if (pl.bf16)
     hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kChainThreads), 0, stream,
                        pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
@@ -937,6 +938,7 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
     hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kChainThreads), 0, stream,
                        pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (chain_stop && (e = hipEventRecord(chain_stop, stream)) != hipSuccess) return e;
   if (pl.bf16)
     hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<uint16_t>(),
                        stream, pl, static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.o), a.den_eps,

@@ -4,7 +4,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/vla.h"
 #include "vla_kernels.h"
@@ -12,6 +14,26 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Event pairs of the chain-kernel timing hook (see vla_timing_enable).
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+void timing_release(Timing& t) {
+  for (hipEvent_t e : t.start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t.stop) (void)hipEventDestroy(e);
+  t.start.clear();
+  t.stop.clear();
+  t.used = 0;
+  t.on = false;
+}
 
 vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 vla_status_t fail(vla_status_t s, const char* fmt, ...) {
@@ -325,7 +347,17 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   sp.wsig = reinterpret_cast<float*>(ws + cl.off_wsig);
   sp.ld = reinterpret_cast<float*>(ws + cl.off_ld);
   sp.nblock = reinterpret_cast<float*>(ws + cl.off_nb);
-  e = vla::launch_state_pass(sp, a, pl.chain_info, static_cast<int>(chains), stream);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  {
+    Timing& tm = timing();
+    std::lock_guard<std::mutex> lock(tm.mu);
+    if (tm.on && tm.used < VLA_TIMING_SLOTS) {
+      ev0 = tm.start[tm.used];
+      ev1 = tm.stop[tm.used];
+      ++tm.used;
+    }
+  }
+  e = vla::launch_state_pass(sp, a, pl.chain_info, static_cast<int>(chains), stream, ev0, ev1);
   if (e != hipSuccess) return hip_fail(e, "chunked state launch");
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
   if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
@@ -367,6 +399,48 @@ const char* vla_status_string(vla_status_t s) {
 }
 
 const char* vla_last_error(void) { return g_last_error.c_str(); }
+
+vla_status_t vla_timing_enable(int32_t enable) {
+  g_last_error.clear();
+  Timing& tm = timing();
+  std::lock_guard<std::mutex> lock(tm.mu);
+  timing_release(tm);
+  if (!enable) return VLA_OK;
+  for (int i = 0; i < VLA_TIMING_SLOTS; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) {
+      e = hipEventCreate(&b);
+      if (e != hipSuccess) (void)hipEventDestroy(a);
+    }
+    if (e != hipSuccess) {
+      timing_release(tm);
+      return hip_fail(e, "timing event creation");
+    }
+    tm.start.push_back(a);
+    tm.stop.push_back(b);
+  }
+  tm.on = true;
+  return VLA_OK;
+}
+
+vla_status_t vla_timing_collect(float* ms, int32_t cap, int32_t* n) {
+  g_last_error.clear();
+  if (!ms || !n || cap < 0) return fail(VLA_EINVAL, "vla_timing_collect: ms and n must be non-NULL, cap >= 0");
+  Timing& tm = timing();
+  std::lock_guard<std::mutex> lock(tm.mu);
+  int written = 0;
+  for (int i = 0; i < tm.used && written < cap; ++i) {
+    hipError_t e = hipEventSynchronize(tm.stop[i]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, tm.start[i], tm.stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "timing event readout");
+    ms[written++] = t;
+  }
+  tm.used = 0;
+  *n = written;
+  return VLA_OK;
+}
 
 int vla_abi_version(void) { return VLA_ABI_VERSION; }
 

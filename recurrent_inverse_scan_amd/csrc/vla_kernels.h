@@ -83,9 +83,10 @@ struct StatePlan {
 
 // Prep (parallel), chain (one workgroup per chain) and readout (parallel):
 // writes o, S_T, n_T and stats (guard count and inverse-pass non-finite flag
-// taken from chain_info).
+// taken from chain_info).  Non-null events are recorded on the stream right
+// before and after the chain kernel.
 hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
-                             hipStream_t stream);
+                             hipStream_t stream, hipEvent_t chain_start = nullptr, hipEvent_t chain_stop = nullptr);
 
 // Inverse recurrence of every chunk from its chunk-start inverse; writes
 // alpha_hat and, from each chain's last chunk, A_T.

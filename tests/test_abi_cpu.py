@@ -39,6 +39,18 @@ def test_version_and_status_strings(lib):
     assert names == ["VLA_OK", "VLA_EINVAL", "VLA_EUNSUPPORTED", "VLA_EWORKSPACE", "VLA_ENONFINITE", "VLA_EHIP"]
 
 
+def test_timing_collect_rejects_bad_arguments(lib):
+    import ctypes
+
+    n = ctypes.c_int32(-1)
+    buf = (ctypes.c_float * 4)()
+    assert lib.vla_timing_collect(None, 4, ctypes.byref(n)) == _lib.VLA_EINVAL
+    assert lib.vla_timing_collect(buf, 4, None) == _lib.VLA_EINVAL
+    assert lib.vla_timing_collect(buf, -1, ctypes.byref(n)) == _lib.VLA_EINVAL
+    # nothing recorded: an empty, successful collection that needs no device
+    assert lib.vla_timing_collect(buf, 4, ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+
+
 def test_params_struct_layout_matches_header(lib, tmp_path):
     """The ctypes mirror of vla_scan_params_t has the C compiler's size and
     offsets, and vla_scan_params_init writes the header's defaults."""

@@ -339,3 +339,21 @@ def test_chunked_agrees_with_sequential():
         err = rel_err(p, to64(q_), axes=axes)
         _say(f"chunked vs sequential {name}: {err}")
         assert err <= (1e-2 if name == "o" else 1e-3), (name, err)
+
+
+def test_timing_hook_records_the_chain_kernel():
+    """The measurement hook returns one positive duration per chunked scan."""
+    from recurrent_inverse_scan_amd import timing_collect, timing_enable
+
+    cfg = CONFIGS["base"].with_(name="timing", B=1, H=2, T=640, nudge_period=128, s_cap=50.0)
+    x = case(cfg, seed=3)
+    timing_enable(True)
+    try:
+        for _ in range(3):
+            _gpu(x, cfg, schedule="chunked")
+        ms = timing_collect()
+    finally:
+        timing_enable(False)
+    _say(f"chain kernel ms {ms}")
+    assert len(ms) == 3 and all(t > 0 for t in ms)
+    assert timing_collect() == []
