@@ -140,7 +140,10 @@ def main(argv=None) -> int:
     total_ms = t_start.elapsed_time(t_end)
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms_per_step = total_ms / args.steps
-    chain_ms = sum(chain_ms_all) / len(chain_ms_all) if chain_ms_all else None
+    # The chunked schedule runs the chain kernel as a few pipelined segment
+    # launches per scan: its time per step is the sum over those launches.
+    chain_ms = sum(chain_ms_all) / args.steps if chain_ms_all else None
+    chain_launches = len(chain_ms_all) // args.steps if chain_ms_all else 0
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev, dtype=torch.float32)
@@ -164,11 +167,12 @@ def main(argv=None) -> int:
                     "frac": chain_flops / (chain_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                     "traffic": measured_traffic(),
                     "kernel": "vla_state_chain_kernel", "kernel_ms": chain_ms,
-                    "flops_per_launch": chain_flops}
+                    "launches_per_step": chain_launches, "flops_per_step": chain_flops}
     else:   # the sequential schedule has no chain kernel: the scan kernel is the dominant one
         roofline = {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
-                    "kernel": "vla_scan_seq_kernel", "kernel_ms": scan_ms, "flops_per_launch": flops}
+                    "kernel": "vla_scan_seq_kernel", "kernel_ms": scan_ms, "launches_per_step": 1,
+                    "flops_per_step": flops}
     es = 2 if cfg.in_dtype == "bf16" else 4
     scan_bytes = tok_heads * d * es * (4 + r) + 2 * B * H * (2 * d * d + d) * 4   # q,k,v,u in, o out, state
     stats = outs[4].cpu().numpy()

@@ -229,7 +229,7 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
 // owning rows 4*(t/16).. and columns 8*(t%16)..) into [ I | A_c^T ].
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
-                       int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q) {
+                       int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo, int c_cnt) {
   // 64 KiB of LDS: Gpre^T and N_p for the product; afterwards the pivot row
   // and column buffers reuse the N_p half, and the result block the first half.
   __shared__ double smem[2 * kD * kD];
@@ -237,8 +237,8 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
   double* sB = smem + kD * kD;
   double (*rowbuf)[2 * kD] = reinterpret_cast<double (*)[2 * kD]>(sB);
   double (*colbuf)[kD] = reinterpret_cast<double (*)[kD]>(sB + 4 * kD);
-  const int64_t chain = blockIdx.x / nchunks;
-  const int c = blockIdx.x % nchunks;
+  const int64_t chain = blockIdx.x / c_cnt;
+  const int c = c_lo + static_cast<int>(blockIdx.x % c_cnt);
   const int p = period_of(c, o, q);
   const int t = threadIdx.x, rb = t >> 4, cb = t & 15;
   const double* Np = ND + (chain * nperiods + p) * 2 * kD * kD;
@@ -368,9 +368,13 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
   }
   hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains), dim3(kChunkThreads), 0, stream, pl.Gtot, pl.A_init,
                      pl.ND, pl.nperiods, static_cast<double>(pl.eps));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(units), dim3(kChunkThreads), 0, stream, pl.Gpre, pl.ND, pl.Ac,
-                     pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_start(const ChunkPlan& pl, int c_lo, int c_cnt, hipStream_t stream) {
+  if (c_cnt <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)), dim3(kChunkThreads), 0,
+                     stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q, c_lo, c_cnt);
   return hipGetLastError();
 }
 

@@ -50,8 +50,8 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   extern __shared__ float4 smem4[];
   float* smem = reinterpret_cast<float*>(smem4);
 
-  const int64_t chain = kInv ? blockIdx.x / x.nchunks : blockIdx.x;
-  const int chunk = kInv ? static_cast<int>(blockIdx.x % x.nchunks) : 0;
+  const int64_t chain = kInv ? blockIdx.x / x.chunk_cnt : blockIdx.x;
+  const int chunk = kInv ? x.chunk_lo + static_cast<int>(blockIdx.x % x.chunk_cnt) : 0;
   if constexpr (kFull) {
     if (x.only_if && x.only_if[chain * 4 + kInfoFallback] == 0) return;   // uniform per workgroup
   }
@@ -444,7 +444,7 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
 template <typename TIn, int D, int NW, int CG, SeqMode MODE>
 static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, hipStream_t stream) {
   const size_t lds = seq_lds_bytes<TIn, D, NW>(MODE, a.r);
-  const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.nchunks)
+  const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.chunk_cnt)
                                                        : static_cast<unsigned>(chains);
   hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE>), dim3(grid), dim3(64 * NW), lds, stream, a, x);
   return hipGetLastError();
@@ -486,25 +486,19 @@ hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chain
 }
 
 hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, float* alpha_out,
-                                     int32_t* chain_info, int chunk_len, int nchunks, int d, bool bf16, int chains,
-                                     hipStream_t stream) {
+                                     int32_t* chain_info, int chunk_len, int nchunks, int chunk_lo, int chunk_cnt,
+                                     int d, bool bf16, int chains, hipStream_t stream) {
+  if (chunk_cnt <= 0) return hipSuccess;
   SeqExtra x{};
   x.a_start = a_start;
   x.alpha_out = alpha_out;
   x.chain_info = chain_info;
   x.chunk_len = chunk_len;
   x.nchunks = nchunks;
+  x.chunk_lo = chunk_lo;
+  x.chunk_cnt = chunk_cnt;
   return bf16 ? dispatch_seq<uint16_t, SeqMode::kInverseOnly>(a, x, d, chains, stream)
               : dispatch_seq<float, SeqMode::kInverseOnly>(a, x, d, chains, stream);
-}
-
-hipError_t launch_scan_state_only(const ScanArgs& a, const float* alpha, int32_t* chain_info, int d,
-                                  bool bf16, int chains, hipStream_t stream) {
-  SeqExtra x{};
-  x.alpha = alpha;
-  x.chain_info = chain_info;
-  return bf16 ? dispatch_seq<uint16_t, SeqMode::kStateOnly>(a, x, d, chains, stream)
-              : dispatch_seq<float, SeqMode::kStateOnly>(a, x, d, chains, stream);
 }
 
 }  // namespace vla

@@ -233,7 +233,7 @@ __device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int t
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
 vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
-                      const TIn* __restrict__ v) {
+                      const TIn* __restrict__ v, int b_lo, int nb) {
   constexpr int kRd = PrepLds<TIn>::kRd;
   extern __shared__ float4 smem4[];
   TIn* Vb = reinterpret_cast<TIn*>(smem4);    // [64][kRd] v rows of the block
@@ -242,8 +242,8 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   TIn* Vp = Kb + kLb * kRd;                   // v rows of the previous block
   float* Af = reinterpret_cast<float*>(Vp + kLb * kRd);   // [64][kLd] alpha_hat rows, later K
   float* Ap = Af + kLb * kLd;                 // previous block's alpha_hat rows, later masked q.k
-  const int64_t chain = blockIdx.x / pl.nblk;
-  const int b = blockIdx.x % pl.nblk;
+  const int64_t chain = blockIdx.x / nb;
+  const int b = b_lo + static_cast<int>(blockIdx.x % nb);
   const int64_t blk = chain * pl.nblk + b;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,9 +515,8 @@ __device__ __forceinline__ void bilinear_terms(const f32x16& X, const char* VR, 
 
 template <typename TIn>
 __global__ void __launch_bounds__(kChainThreads)
-vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* __restrict__ n0,
-                       float* __restrict__ S_T, float* __restrict__ n_T, int32_t* __restrict__ stats,
-                       const int32_t* __restrict__ chain_info, float cap, int cap_on) {
+vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float* __restrict__ n_T,
+                       int32_t* __restrict__ stats, const int32_t* __restrict__ chain_info, float cap, int cap_on) {
   // Buffers that buffer-to-LDS loads fill and that the same waves read (the
   // v and alpha_hat rows) have one LDS object per generation, selected at
   // compile time: the compiler then sees that reading one generation does not
@@ -554,6 +553,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
   const float cap2 = cap * cap;
   const int nblk = pl.nblk;
   const int64_t blk0 = chain * nblk;
+  const int b_lo = sg.b_lo, b_hi = sg.b_hi;
 
   // Buffer-to-LDS copies: this wave takes pieces m, m+4, ...; vo32 / vo16
   // are a lane's source offsets within a piece (fp32 / bf16 rows).
@@ -582,7 +582,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
     dma_mat(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4, ck, vo32);
     if (m == 0) dma_piece(make_rsrc(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4),
                           reinterpret_cast<char*>(ck), 16, vo32);
-    if (j > 0) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
+    if (j > b_lo) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
   };
 
   // The recursion wave's per-block outputs, written from LDS by a product wave.
@@ -601,11 +601,15 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
   int fires = 0, first = -1;
   bool bad = false;
 
-  // ---- prologue ------------------------------------------------------------
+  // ---- prologue: continue from S and n at block b_lo -------------------------
   if (rwave) {
-    nvec = n0[chain * kD + lane];
+    nvec = sg.n_in[chain * sg.n_in_stride + lane];
+    if (b_lo > 0) {
+      fires = sg.counters[chain * 2];
+      first = sg.counters[chain * 2 + 1];
+    }
   } else {
-    const float* s0 = S0 + chain * kD * kD;
+    const float* s0 = sg.S_in + chain * sg.S_in_stride;
     float part = 0.f;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
@@ -614,10 +618,10 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
     }
     part = wave_sum(part);
     if (lane == 0) sRed[m] = part;
-    dma_kernels(0, sCK0, sKX0, lane);
-    dma_rows(0, sAR0, sVR0, lane);
-    if (nblk > 1) dma_rows(1, sAR1, sVR1, lane);
-    fr.load(pl, blk0, ti, tj, lane);
+    dma_kernels(b_lo, sCK0, sKX0, lane);
+    dma_rows(b_lo, sAR0, sVR0, lane);
+    if (b_lo + 1 < b_hi) dma_rows(b_lo + 1, sAR1, sVR1, lane);
+    fr.load(pl, blk0 + b_lo, ti, tj, lane);
   }
   __syncthreads();
   if (!rwave)
@@ -645,7 +649,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
       const float* hr = sH[g];
       // v_t^T S_b alpha_t, the one-block lag repaired with the cross kernel.
       float acc = (hr[t] + hr[kLb + t]) + (hr[2 * kLb + t] + hr[3 * kLb + t]);
-      if (b > 0) {
+      if (b > b_lo) {
         const float se = sSig[g ^ 1];
         // |S|^2 is carried through the recursion; re-anchor it on the exact
         // norm of S_{b-1} as the product waves hold it (the carried value
@@ -706,7 +710,7 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
       sLog[g][2 * t + 1] = l_t;
       nvec += ks;
     } else {
-      if (b > 0) {
+      if (b > b_lo) {
         // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.
         rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
         fr.load(pl, blk0 + b, ti, tj, ln);
@@ -725,39 +729,52 @@ vla_state_chain_kernel(StatePlan pl, const float* __restrict__ S0, const float* 
         if (ln == 0) sNrm[g][m] = part;
       }
       // Next block's pack and Kx into the other parity (the recursion wave
-      // finished with it one block ago).
-      if (b + 1 < nblk) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
-      // Rows of block b+2 into the generation block b used (last read one
-      // block ago).
-      if (b + 2 < nblk) dma_rows(b + 2, rows_ar(std::integral_constant<int, RGp2>{}),
-                                   rows_vr(std::integral_constant<int, RGp2>{}), ln);
-      if (b + 1 < nblk)
+      // finished with it one block ago); rows of block b+2 into the
+      // generation block b used (last read one block ago).
+      if (b + 1 < b_hi) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
+      if (b + 2 < b_hi) dma_rows(b + 2, rows_ar(std::integral_constant<int, RGp2>{}),
+                                 rows_vr(std::integral_constant<int, RGp2>{}), ln);
+      if (b + 1 < b_hi)
         bilinear_terms<TIn>(X, reinterpret_cast<const char*>(rows_vr(std::integral_constant<int, RGp1>{})),
                             reinterpret_cast<const float*>(rows_ar(std::integral_constant<int, RGp1>{})),
                             sH[g ^ 1] + m * kLb, ti, tj, ln);
     }
     __syncthreads();
   };
-  for (int b = 0; b < nblk; b += 2) {
+  for (int b = b_lo; b < b_hi; b += 2) {   // b_lo is even: parity 0 first
     step(std::integral_constant<int, 0>{}, b);
-    if (b + 1 < nblk) step(std::integral_constant<int, 1>{}, b + 1);
+    if (b + 1 < b_hi) step(std::integral_constant<int, 1>{}, b + 1);
   }
 
-  // ---- epilogue: the last block's update ------------------------------------
+  // ---- epilogue: the segment's last block update ----------------------------
   if (!rwave) {
-    const int g = (nblk - 1) & 1;
-    if (m == 0) store_block_outputs(nblk - 1, sLog[g], sNb[g], lane);
+    const int g = (b_hi - 1) & 1;
+    if (m == 0) store_block_outputs(b_hi - 1, sLog[g], sNb[g], lane);
     rank_update<TIn>(X, fr, sW[g], sSig[g], h);
-    float* st = S_T + chain * kD * kD;
+    if (sg.last) {
+      float* st = S_T + chain * kD * kD;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
-      bad |= !isfinite(X[s]);
+      for (int s = 0; s < 16; ++s) {
+        st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
+        bad |= !isfinite(X[s]);
+      }
+    } else {
+      // S at the next segment's first block (also that block's readout input).
+      float* st = pl.Xsnap + (blk0 + b_hi) * kD * kD;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
     }
-  } else {
+  } else if (sg.last) {
     n_T[chain * kD + lane] = nvec;
     bad |= !isfinite(nvec);
+  } else {
+    sg.n_carry[chain * kD + lane] = nvec;
+    if (lane == 0) {
+      sg.counters[chain * 2] = fires;
+      sg.counters[chain * 2 + 1] = first;
+    }
   }
+  if (!sg.last) return;   // uniform
   const bool wave_bad = __any(bad);
   if (lane == 0) sRed[w] = wave_bad ? 1.f : 0.f;
   __syncthreads();
@@ -789,7 +806,7 @@ struct ReadoutLds {
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
 vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
-                         int32_t* __restrict__ stats) {
+                         int32_t* __restrict__ chain_info, int b_lo, int nb) {
   constexpr int kQd = ReadoutLds<TIn>::kQd;
   extern __shared__ float4 smem4[];
   TIn* Qs = reinterpret_cast<TIn*>(smem4);          // [64 t][kQd] q rows
@@ -801,8 +818,8 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
   float* sl = wl + kLb;                             // [64] log2 sigma_t
   float* dl = sl + kLb;                             // [64] den_t
   float* nl = dl + kLb;                             // [64] n at the block start
-  const int64_t chain = blockIdx.x / pl.nblk;
-  const int b = blockIdx.x % pl.nblk;
+  const int64_t chain = blockIdx.x / nb;
+  const int b = b_lo + static_cast<int>(blockIdx.x % nb);
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
@@ -890,8 +907,7 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
       Elem<TIn>::store(o + (row0 + t) * kD + fcol, ov);
     }
   }
-  // The chain kernel has written this chain's statistics already.
-  if (__any(bad) && lane == 0 && stats) atomicOr(stats + chain * 4 + 2, 1);
+  if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
 }
 
 }  // namespace
@@ -909,8 +925,7 @@ static void allow_lds(K kernel, size_t bytes) {
                             static_cast<int>(bytes));
 }
 
-hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
-                             hipStream_t stream, hipEvent_t chain_start, hipEvent_t chain_stop) {
+static void allow_state_lds() {
   static const bool once = [] {
     allow_lds(vla_state_prep_kernel<uint16_t>, state_prep_lds_bytes<uint16_t>());
     allow_lds(vla_state_prep_kernel<float>, state_prep_lds_bytes<float>());
@@ -919,33 +934,52 @@ hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* ch
     return true;
   }();
   (void)once;
-  const unsigned blocks = static_cast<unsigned>(chains * pl.nblk);
+}
+
+hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb,
+                             hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
+  allow_state_lds();
+  const unsigned blocks = static_cast<unsigned>(chains * nb);
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_prep_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<uint16_t>(), stream,
-                       pl, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v));
+    hipLaunchKernelGGL(vla_state_prep_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<uint16_t>(),
+                       stream, pl, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), b_lo, nb);
   else
     hipLaunchKernelGGL(vla_state_prep_kernel<float>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<float>(), stream,
                        pl, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                       static_cast<const float*>(a.v));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (chain_start && (e = hipEventRecord(chain_start, stream)) != hipSuccess) return e;
+                       static_cast<const float*>(a.v), b_lo, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,
+                              int chains, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  hipError_t e = hipSuccess;
+  if (ev_start && (e = hipEventRecord(ev_start, stream)) != hipSuccess) return e;
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kChainThreads), 0, stream,
-                       pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
+    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
+                       a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   else
-    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kChainThreads), 0, stream,
-                       pl, a.S0, a.n0, a.S_T, a.n_T, a.stats, chain_info, a.cap, a.cap_on);
+    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
+                       a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (chain_stop && (e = hipEventRecord(chain_stop, stream)) != hipSuccess) return e;
+  if (ev_stop && (e = hipEventRecord(ev_stop, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains, int b_lo,
+                                int nb, hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
+  allow_state_lds();
+  const unsigned blocks = static_cast<unsigned>(chains * nb);
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<uint16_t>(),
-                       stream, pl, static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.o), a.den_eps,
-                       a.stats);
+    hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads),
+                       state_readout_lds_bytes<uint16_t>(), stream, pl, static_cast<const uint16_t*>(a.q),
+                       static_cast<uint16_t*>(a.o), a.den_eps, chain_info, b_lo, nb);
   else
     hipLaunchKernelGGL(vla_state_readout_kernel<float>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<float>(),
-                       stream, pl, static_cast<const float*>(a.q), static_cast<float*>(a.o), a.den_eps, a.stats);
+                       stream, pl, static_cast<const float*>(a.q), static_cast<float*>(a.o), a.den_eps, chain_info,
+                       b_lo, nb);
   return hipGetLastError();
 }
 

@@ -1,7 +1,9 @@
 // Opt-in NaN/Inf pre-check of the scan inputs.  Source: "Mathematical
 // Primitives", section 1 (finite-state enforcement before evaluation).
+// Also the last step of the chunked schedule's statistics.
 #include "vla_common.h"
 #include "vla_kernels.h"
+#include "vla_seq.h"
 
 namespace vla {
 
@@ -18,7 +20,22 @@ __global__ void __launch_bounds__(256) nonfinite_kernel(const T* __restrict__ p,
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
 }
 
+// stats[c][2] |= the non-finite flag that the chunked schedule's passes left
+// in chain_info[c].
+__global__ void __launch_bounds__(256) stats_finalize_kernel(int32_t* __restrict__ stats,
+                                                             const int32_t* __restrict__ chain_info, int chains) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < chains && chain_info[c * 4 + kInfoNonfinite]) stats[c * 4 + 2] = 1;
+}
+
 }  // namespace
+
+hipError_t launch_stats_finalize(int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream) {
+  if (!stats || chains <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stats_finalize_kernel, dim3((chains + 255) / 256), dim3(256), 0, stream, stats, chain_info,
+                     chains);
+  return hipGetLastError();
+}
 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
   hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, stream, flag);

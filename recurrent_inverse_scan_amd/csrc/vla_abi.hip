@@ -1,5 +1,6 @@
 // C ABI of the VLA scan library: argument validation and kernel dispatch.
 // Every check runs before any launch; nothing here allocates device memory.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -81,7 +82,8 @@ struct ChunkLayout {
   int L = 0, nchunks = 0, nperiods = 0, o = 0, q = 0;
   int nblk = 0;   // 64-token blocks of the state pass
   size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_Gtot = 0, off_ND = 0, off_Ac = 0,
-         off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0, off_flag = 0,
+         off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0,
+         off_ncarry = 0, off_cnt = 0, off_flag = 0,
          total = 0;
 };
 
@@ -144,6 +146,8 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_wsig = off; off = align_up(off + C * T * 2 * 4);
     cl.off_ld = off; off = align_up(off + C * T * 4);
     cl.off_nb = off; off = align_up(off + C * nb * 64 * 4);
+    cl.off_ncarry = off; off = align_up(off + C * 64 * 4);
+    cl.off_cnt = off; off = align_up(off + C * 2 * 4);
   }
   cl.off_flag = off;
   if (p->validate) off += kValidateBytes;
@@ -330,9 +334,6 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   a.A0 = pl.A_init;
   a.S0 = pl.S_init;
   a.n0 = pl.n_init;
-  e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, d, bf16,
-                                      static_cast<int>(chains), stream);
-  if (e != hipSuccess) return hip_fail(e, "chunked inverse launch");
   vla::StatePlan sp{};
   sp.T = p->T;
   sp.nblk = cl.nblk;
@@ -347,6 +348,34 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   sp.wsig = reinterpret_cast<float*>(ws + cl.off_wsig);
   sp.ld = reinterpret_cast<float*>(ws + cl.off_ld);
   sp.nblock = reinterpret_cast<float*>(ws + cl.off_nb);
+  float* n_carry = reinterpret_cast<float*>(ws + cl.off_ncarry);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + cl.off_cnt);
+
+  // Chunk-start inverses and the inverse pass over all chunks at once: each
+  // chunk's recurrence is sequential, so its wall time is one chunk's,
+  // whatever the number of chunks that run side by side.
+  if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
+  if ((e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
+                                           static_cast<int>(chains), stream)) != hipSuccess)
+    return hip_fail(e, "chunked inverse launch");
+
+  // State pass: prep, the chain kernel over the whole sequence, readout.
+  // (Cutting the sequence into segments to overlap prep and readout with the
+  // chain on other streams was measured slower: the chain kernel loses more
+  // to the shared memory system than the overlap saves.)
+  const int nblk = cl.nblk;
+  if ((e = vla::launch_state_prep(sp, a, static_cast<int>(chains), 0, nblk, stream)) != hipSuccess)
+    return hip_fail(e, "state prep launch");
+  vla::ChainSeg sg{};
+  sg.b_lo = 0;
+  sg.b_hi = nblk;
+  sg.S_in = pl.S_init;
+  sg.S_in_stride = 64 * 64;
+  sg.n_in = pl.n_init;
+  sg.n_in_stride = 64;
+  sg.n_carry = n_carry;
+  sg.counters = counters;
+  sg.last = 1;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
     Timing& tm = timing();
@@ -357,8 +386,12 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
       ++tm.used;
     }
   }
-  e = vla::launch_state_pass(sp, a, pl.chain_info, static_cast<int>(chains), stream, ev0, ev1);
-  if (e != hipSuccess) return hip_fail(e, "chunked state launch");
+  if ((e = vla::launch_state_chain(sp, sg, a, pl.chain_info, static_cast<int>(chains), stream, ev0, ev1)) != hipSuccess)
+    return hip_fail(e, "state chain launch");
+  if ((e = vla::launch_state_readout(sp, a, pl.chain_info, static_cast<int>(chains), 0, nblk, stream)) != hipSuccess)
+    return hip_fail(e, "state readout launch");
+  if ((e = vla::launch_stats_finalize(stats, pl.chain_info, static_cast<int>(chains), stream)) != hipSuccess)
+    return hip_fail(e, "stats launch");
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
   if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
   return VLA_OK;

@@ -34,10 +34,6 @@ struct ScanArgs {
 hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, const int32_t* only_if,
                                   hipStream_t stream);
 
-// State recurrence only (S, n, cap, readout) from precomputed alpha_hat.
-hipError_t launch_scan_state_only(const ScanArgs& a, const float* alpha, int32_t* chain_info, int d,
-                                  bool bf16, int chains, hipStream_t stream);
-
 // Time-parallel inverse schedule (d = 64): buffers live in the caller's
 // workspace; see chunked.hip.
 struct ChunkPlan {
@@ -59,10 +55,13 @@ struct ChunkPlan {
   float* alpha;   // [chains][T][64]
 };
 
-// Snapshot of the initial state, per-chunk Gram matrices, the (N, D) chain and
-// the chunk-start inverses.
+// Snapshot of the initial state, per-chunk Gram matrices, their per-period
+// prefixes and the (N, D) chain.
 hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const float* S0, const float* n0,
                                  const void* u, bool bf16, hipStream_t stream);
+
+// Chunk-start inverses of chunks [c_lo, c_lo + c_cnt).
+hipError_t launch_chunk_start(const ChunkPlan& pl, int c_lo, int c_cnt, hipStream_t stream);
 
 // Blocked state pass (d = 64, blocks of 64 tokens); buffers in the workspace.
 struct StatePlan {
@@ -81,18 +80,38 @@ struct StatePlan {
   float* nblock;         // [chains][nblk][64] normaliser at each block start
 };
 
-// Prep (parallel), chain (one workgroup per chain) and readout (parallel):
-// writes o, S_T, n_T and stats (guard count and inverse-pass non-finite flag
-// taken from chain_info).  Non-null events are recorded on the stream right
-// before and after the chain kernel.
-hipError_t launch_state_pass(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains,
-                             hipStream_t stream, hipEvent_t chain_start = nullptr, hipEvent_t chain_stop = nullptr);
+// One segment of the chain kernel: blocks [b_lo, b_hi), b_lo even, continuing
+// from S and n at block b_lo.  A segment that does not end the sequence leaves
+// S at b_hi in Xsnap, n in n_carry and its counters for the next one; the last
+// writes S_T, n_T and stats (guard count and non-finite flag of the inverse
+// pass taken from chain_info).
+struct ChainSeg {
+  int b_lo, b_hi;
+  const float* S_in;      // S at block b_lo, chain c at S_in + c * S_in_stride
+  int64_t S_in_stride;
+  const float* n_in;      // n at block b_lo, chain c at n_in + c * n_in_stride
+  int64_t n_in_stride;
+  float* n_carry;         // [chains][64] n after block b_hi - 1
+  int32_t* counters;      // [chains][2] cap fires so far and the first cap step (-1: none)
+  int last;
+};
 
-// Inverse recurrence of every chunk from its chunk-start inverse; writes
-// alpha_hat and, from each chain's last chunk, A_T.
+// Prep and readout of blocks [b_lo, b_lo + nb) of every chain (parallel); the
+// readout flags non-finite outputs in chain_info.
+hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb,
+                             hipStream_t stream);
+hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains, int b_lo,
+                                int nb, hipStream_t stream);
+// The chain kernel over one segment (one workgroup per chain).  Non-null
+// events are recorded on the stream right before and after it.
+hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,
+                              int chains, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// Inverse recurrence of chunks [chunk_lo, chunk_lo + chunk_cnt) from their
+// chunk-start inverses; writes alpha_hat and, from each chain's last chunk, A_T.
 hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, float* alpha_out,
-                                      int32_t* chain_info, int chunk_len, int nchunks, int d, bool bf16, int chains,
-                                      hipStream_t stream);
+                                      int32_t* chain_info, int chunk_len, int nchunks, int chunk_lo, int chunk_cnt,
+                                      int d, bool bf16, int chains, hipStream_t stream);
 
 hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_bf16, const void* W,
                             const void* kraw, void* u, hipStream_t stream);
@@ -100,6 +119,8 @@ hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_b
 // Sets *flag (device int) to 1 if any of the n elements at the given buffers
 // is NaN or Inf; *flag must be cleared first with launch_clear_flag.
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream);
+// stats[c][2] |= chain_info[c] non-finite flag (stats nullable).
+hipError_t launch_stats_finalize(int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream);
 hipError_t launch_nonfinite_check(const void* p, int64_t n, bool bf16, int32_t* flag, hipStream_t stream);
 
 }  // namespace vla

@@ -24,6 +24,8 @@ struct SeqExtra {
                               // with the fallback flag set run (nullable: all run)
   int32_t chunk_len;          // kInverseOnly: tokens per chunk
   int32_t nchunks;            // kInverseOnly: chunks per chain
+  int32_t chunk_lo;           // kInverseOnly: this launch runs chunks [chunk_lo, chunk_lo + chunk_cnt)
+  int32_t chunk_cnt;
 };
 
 constexpr int kMaxStageVecs = 8;   // 16-byte staging registers per thread

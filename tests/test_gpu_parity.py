@@ -342,7 +342,8 @@ def test_chunked_agrees_with_sequential():
 
 
 def test_timing_hook_records_the_chain_kernel():
-    """The measurement hook returns one positive duration per chunked scan."""
+    """The measurement hook returns positive durations, the same number of
+    chain-kernel launches for every chunked scan."""
     from recurrent_inverse_scan_amd import timing_collect, timing_enable
 
     cfg = CONFIGS["base"].with_(name="timing", B=1, H=2, T=640, nudge_period=128, s_cap=50.0)
@@ -355,5 +356,5 @@ def test_timing_hook_records_the_chain_kernel():
     finally:
         timing_enable(False)
     _say(f"chain kernel ms {ms}")
-    assert len(ms) == 3 and all(t > 0 for t in ms)
+    assert len(ms) >= 3 and len(ms) % 3 == 0 and all(t > 0 for t in ms)
     assert timing_collect() == []
