@@ -20,8 +20,8 @@
 //   vla_chunk_gram_kernel   G_c for every chunk (MFMA, fp32 accumulation)
 //   vla_chunk_scan_kernel   fp64 prefix sums of G inside each nudge period and
 //                           each period's total, in parallel over elements
-//   vla_chunk_chain_kernel  per chain, sequential over periods, fp64: (N, D)
-//                           at every period start
+//   vla_chunk_chain_kernel  per chain and column block, sequential over
+//                           periods, fp64: (N, D) at every period start
 //   vla_chunk_start_kernel  per chunk, fp64: A_c by Gauss-Jordan elimination
 //                           of [ D_c^T | N_p^T ]; a non-positive pivot flags
 //                           the chain for the sequential fallback
@@ -154,72 +154,75 @@ vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, do
 }
 
 // ---- (N, D) chain ---------------------------------------------------------
-// One workgroup per chain, 256 threads, thread t owns the 4x4 block
-// (t/16, t%16) of N and D.  Between periods p and p+1: D += Gtot_p N, then
-// the nudge N += eps D.  The next period's Gram total is loaded one period
-// ahead.
+// Between periods p and p+1: D += Gtot_p N, then the nudge N += eps D.  Both
+// steps act on each column of (N, D) separately, so a chain runs as
+// kNdSplit independent workgroups, one per block of 64/kNdSplit columns.
+// Thread t owns rows 4*(t/16).. of column t%16 of the block; the period's
+// Gram total is staged in LDS (transposed) and the next one is loaded while
+// the current product runs.
+constexpr int kNdSplit = 4;
+constexpr int kNdCols = kD / kNdSplit;   // 16
+
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
                        int nperiods, double eps) {
-  __shared__ double sG[kD * kD];   // period total, transposed: sG[m*kD + i] = Gtot[i][m]
-  __shared__ double sN[kD * kD];
-  const int64_t chain = blockIdx.x;
-  const int t = threadIdx.x, bi = t >> 4, bj = t & 15;
-  double N[4][4], Dm[4][4], Gn[4][4];
+  __shared__ double sG[kD * kD];        // sG[m*kD + i] = Gtot[i][m]
+  __shared__ double sN[kD * kNdCols];   // sN[m*kNdCols + c] = N[m][c0 + c]
+  const int64_t chain = blockIdx.x / kNdSplit;
+  const int c0 = (blockIdx.x % kNdSplit) * kNdCols;
+  const int t = threadIdx.x, rb = t >> 4, cc = t & 15;
+  const int col = c0 + cc;
+  double N[4], Dm[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gi = 4 * bi + i, gj = 4 * bj + j;
-      N[i][j] = static_cast<double>(A0[(chain * kD + gi) * kD + gj]);
-      Dm[i][j] = gi == gj ? 1.0 : 0.0;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int gi = 4 * rb + i;
+    N[i] = static_cast<double>(A0[(chain * kD + gi) * kD + col]);
+    Dm[i] = gi == col ? 1.0 : 0.0;
+  }
   auto store_nd = [&](int p) {
     double* nd = ND + (chain * nperiods + p) * 2 * kD * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        nd[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
-        nd[kD * kD + (4 * bi + i) * kD + 4 * bj + j] = Dm[i][j];
-      }
+    for (int i = 0; i < 4; ++i) {
+      nd[(4 * rb + i) * kD + col] = N[i];
+      nd[kD * kD + (4 * rb + i) * kD + col] = Dm[i];
+    }
   };
-  auto load_g = [&](int p) {
+  // 16 of the 64x64 total per thread: rows 4*(t/16).., columns 4*(t%16)..;
+  // two register sets, so each total is loaded two periods ahead.
+  double ga[16], gb[16];
+  auto load_g = [&](double (&g)[16], int p) {
+    if (p + 1 >= nperiods) return;   // the last period's total is not needed
     const double* gt = Gtot + (chain * nperiods + p) * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Gn[i][j] = gt[(4 * bi + i) * kD + 4 * bj + j];
+      for (int j = 0; j < 4; ++j) g[4 * i + j] = gt[(4 * rb + i) * kD + 4 * cc + j];
   };
-  store_nd(0);
-  if (nperiods > 1) load_g(0);
-  for (int p = 0; p + 1 < nperiods; ++p) {
-    __syncthreads();
+  auto advance = [&](double (&g)[16], int p) {
+    __syncthreads();   // the previous product is done with sG and sN
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sG[(4 * bj + j) * kD + 4 * bi + i] = Gn[i][j];
-        sN[(4 * bi + i) * kD + 4 * bj + j] = N[i][j];
-      }
+      for (int j = 0; j < 4; ++j) sG[(4 * cc + j) * kD + 4 * rb + i] = g[4 * i + j];
+      sN[(4 * rb + i) * kNdCols + cc] = N[i];
+    }
     __syncthreads();
-    if (p + 2 < nperiods) load_g(p + 1);
+    load_g(g, p + 2);
     for (int m = 0; m < kD; ++m) {
-      double gcol[4], nrow[4];
+      const double nm = sN[m * kNdCols + cc];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gcol[i] = sG[m * kD + 4 * bi + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nrow[j] = sN[m * kD + 4 * bj + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Dm[i][j] = fma(gcol[i], nrow[j], Dm[i][j]);
+      for (int i = 0; i < 4; ++i) Dm[i] = fma(sG[m * kD + 4 * rb + i], nm, Dm[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) N[i][j] = fma(eps, Dm[i][j], N[i][j]);
+    for (int i = 0; i < 4; ++i) N[i] = fma(eps, Dm[i], N[i]);
     store_nd(p + 1);
+  };
+  store_nd(0);
+  load_g(ga, 0);
+  load_g(gb, 1);
+  for (int p = 0; p + 1 < nperiods; p += 2) {
+    advance(ga, p);
+    if (p + 2 < nperiods) advance(gb, p + 1);
   }
 }
 
@@ -244,10 +247,12 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
   const double* Np = ND + (chain * nperiods + p) * 2 * kD * kD;
   const double* Dp = Np + kD * kD;
   const double* gp = Gpre + (chain * nchunks + c) * kD * kD;
+  // The first chunk of a period has no Gram prefix: D_c = D_p.
+  const bool has_pre = c > 0 && (q == 0 || (o + c) % q != 0);
 
   for (int e = t; e < kD * kD; e += kChunkThreads) {
     const int i = e / kD, j = e % kD;
-    sA[j * kD + i] = gp[e];
+    if (has_pre) sA[j * kD + i] = gp[e];
     sB[e] = Np[e];
   }
   __syncthreads();
@@ -260,7 +265,7 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) W[ii][jj] = Dp[(8 * cb + jj) * kD + 4 * rb + ii];
-    for (int m = 0; m < kD; ++m) {
+    for (int m = 0; has_pre && m < kD; ++m) {
       double gv[8], nv[4];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) gv[jj] = sA[m * kD + 8 * cb + jj];
@@ -280,46 +285,42 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
   }
 
   __syncthreads();   // every thread is done reading sB before it holds pivots
+  // Pivot k = 8 k8 + kk: unrolled over kk, so the pivot row's place in the
+  // owner's block (kk % 4) and the pivot column's (kk) are compile-time.
   bool ok = true;
-  for (int k = 0; k < kD; ++k) {
-    const int par = k & 1;
-    if (rb == (k >> 2)) {
-      // Row k & 3 of this thread's block, selected without dynamic indexing.
-      double rowv[8];
+  for (int k8 = 0; k8 < kD / 8; ++k8) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        rowv[jj] = W[0][jj];
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = 8 * k8 + kk;
+      const int par = kk & 1;
+      const bool row_owner = rb == 2 * k8 + (kk >> 2);
+      if (row_owner) {
 #pragma unroll
-        for (int ii = 1; ii < 4; ++ii) rowv[jj] = ((k & 3) == ii) ? W[ii][jj] : rowv[jj];
-        rowbuf[par][8 * cb + jj] = rowv[jj];
+        for (int jj = 0; jj < 8; ++jj) rowbuf[par][8 * cb + jj] = W[kk & 3][jj];
       }
-    }
-    if (cb == (k >> 3)) {
+      if (cb == k8) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) colbuf[par][4 * rb + ii] = W[ii][kk];
+      }
+      __syncthreads();
+      const double piv = rowbuf[par][k];
+      ok = ok && (piv > 0.0) && isfinite(piv);
+      // 1/piv: the hardware reciprocal refined by one Newton step.
+      double inv = __builtin_amdgcn_rcp(piv);
+      inv = fma(inv, fma(-piv, inv, 1.0), inv);
+      double rv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][8 * cb + jj] * inv;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        double cv = W[ii][0];
+        if (row_owner && ii == (kk & 3)) {
 #pragma unroll
-        for (int jj = 1; jj < 8; ++jj) cv = ((k & 7) == jj) ? W[ii][jj] : cv;
-        colbuf[par][4 * rb + ii] = cv;
-      }
-    }
-    __syncthreads();
-    const double piv = rowbuf[par][k];
-    ok = ok && (piv > 0.0) && isfinite(piv);
-    const double inv = 1.0 / piv;
-    double rv[8];
+          for (int jj = 0; jj < 8; ++jj) W[ii][jj] = rv[jj];
+        } else {
+          const double f = colbuf[par][4 * rb + ii];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][8 * cb + jj] * inv;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 4 * rb + ii;
-      if (i == k) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = rv[jj];
-      } else {
-        const double f = colbuf[par][i];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(-f, rv[jj], W[ii][jj]);
+          for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(-f, rv[jj], W[ii][jj]);
+        }
       }
     }
   }
@@ -366,8 +367,8 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
                        pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains), dim3(kChunkThreads), 0, stream, pl.Gtot, pl.A_init,
-                     pl.ND, pl.nperiods, static_cast<double>(pl.eps));
+  hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains * kNdSplit), dim3(kChunkThreads), 0, stream, pl.Gtot,
+                     pl.A_init, pl.ND, pl.nperiods, static_cast<double>(pl.eps));
   return hipGetLastError();
 }
 
