@@ -121,21 +121,34 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// x = t1 + t2 + t3 + O(2^-27 |x|), each term a bf16 (round to nearest even).
+// x = t1 + t2 + t3 exactly, each term a bf16: t1 is x with the low 16 bits
+// of its encoding cleared, r = x - t1 (exact: the low 16 significand bits),
+// t2 is r cleared the same way and t3 = r - t2 holds at most 8 significant
+// bits, so it is a bf16 as well.  Each term is the upper half of an fp32
+// encoding; byte permutes pack two of them per word.
 struct Split3 {
   bf16x8 t1, t2, t3;
 };
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
 __device__ __forceinline__ Split3 split3(const float (&x)[8]) {
-  Split3 s;
+#pragma clang fp contract(off)   // x is what the caller rounded, not an exact product
+  uint32_t a[8], r[8], c[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const __bf16 a = static_cast<__bf16>(x[e]);
-    const float r = x[e] - static_cast<float>(a);
-    const __bf16 c = static_cast<__bf16>(r);
-    s.t1[e] = a;
-    s.t2[e] = c;
-    s.t3[e] = static_cast<__bf16>(r - static_cast<float>(c));
+    a[e] = __float_as_uint(x[e]);
+    const float rf = x[e] - __uint_as_float(a[e] & 0xffff0000u);
+    r[e] = __float_as_uint(rf);
+    c[e] = __float_as_uint(rf - __uint_as_float(r[e] & 0xffff0000u));
   }
+  Split3 s;
+  s.t1 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(a[0], a[1]), pack_hi16(a[2], a[3]), pack_hi16(a[4], a[5]),
+                                               pack_hi16(a[6], a[7])));
+  s.t2 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(r[0], r[1]), pack_hi16(r[2], r[3]), pack_hi16(r[4], r[5]),
+                                               pack_hi16(r[6], r[7])));
+  s.t3 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(c[0], c[1]), pack_hi16(c[2], c[3]), pack_hi16(c[4], c[5]),
+                                               pack_hi16(c[6], c[7])));
   return s;
 }
 
@@ -205,10 +218,10 @@ __device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, 
 //               sum_t k_t as three more rows
 //   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
 //   ld[t]     = sum_{s<=t in block} k_s.q_t
-//   VT, AT    = v and alpha_hat of the block regrouped as the chain kernel's
-//               matrix-core operands of its rank-64 update: fragment
-//               (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e, e < 8, of
-//               feature 32 c + lane % 32.
+//   VT, AT    = (fp32 storage only) v and alpha_hat of the block regrouped as
+//               the chain kernel's matrix-core operands of its rank-64 update:
+//               fragment (c, kb, lane) holds tokens 16 kb + 8 (lane / 32) + e,
+//               e < 8, of feature 32 c + lane % 32.
 // The Gram products run on the bf16 matrix cores: v.v and q.k exactly when
 // stored as bf16, alpha.alpha (and fp32-stored inputs) through three-term splits.
 template <typename TIn>
@@ -281,25 +294,20 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
     pack[kRowKs * kLb + tid] = acc;
     pack[67 * kLb + tid] = 0.f;
   }
-  // Matrix-core operands of the chain kernel's update (features of v and
-  // alpha_hat are LDS columns here).
+  // Matrix-core operands of the chain kernel's update for fp32 storage
+  // (features of v and alpha_hat are LDS columns here); with bf16 storage the
+  // chain kernel reads them from its own LDS rows.
+  if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int f = tid + 256 * rep, c = f >> 8, kb = (f >> 6) & 3, fl = f & 63;
-    const int t0 = 16 * kb + 8 * (fl >> 5), feat = 32 * c + (fl & 31);
-    float xa8[8];
+    for (int rep = 0; rep < 2; ++rep) {
+      const int f = tid + 256 * rep, c = f >> 8, kb = (f >> 6) & 3, fl = f & 63;
+      const int t0 = 16 * kb + 8 * (fl >> 5), feat = 32 * c + (fl & 31);
+      float xa8[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xa8[e] = Af[(t0 + e) * kLd + feat];
-    float4* ad = reinterpret_cast<float4*>(pl.AT + (blk * 512 + f) * 8);
-    ad[0] = make_float4(xa8[0], xa8[1], xa8[2], xa8[3]);
-    ad[1] = make_float4(xa8[4], xa8[5], xa8[6], xa8[7]);
-    if constexpr (sizeof(TIn) == 2) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pw[e] = static_cast<uint32_t>(Vb[(t0 + 2 * e) * kRd + feat]) | (static_cast<uint32_t>(Vb[(t0 + 2 * e + 1) * kRd + feat]) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(pl.VT) + (blk * 512 + f) * 8) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-    } else {
+      for (int e = 0; e < 8; ++e) xa8[e] = Af[(t0 + e) * kLd + feat];
+      float4* ad = reinterpret_cast<float4*>(pl.AT + (blk * 512 + f) * 8);
+      ad[0] = make_float4(xa8[0], xa8[1], xa8[2], xa8[3]);
+      ad[1] = make_float4(xa8[4], xa8[5], xa8[6], xa8[7]);
       float4* vd = reinterpret_cast<float4*>(static_cast<float*>(pl.VT) + (blk * 512 + f) * 8);
       vd[0] = make_float4(Vb[t0 * kRd + feat], Vb[(t0 + 1) * kRd + feat], Vb[(t0 + 2) * kRd + feat], Vb[(t0 + 3) * kRd + feat]);
       vd[1] = make_float4(Vb[(t0 + 4) * kRd + feat], Vb[(t0 + 5) * kRd + feat], Vb[(t0 + 6) * kRd + feat], Vb[(t0 + 7) * kRd + feat]);
@@ -390,12 +398,15 @@ __device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* lds, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + 1024 * p), 16, vo, 1024 * p, 0, 0);
 }
 
-// The update's operands of one product wave for one block, from the prep kernel.
+// The update's operands of one product wave for one block (fp32 storage):
+// slot (kb, e) of lane l holds token 16 kb + 8 (l / 32) + e of feature
+// 32 ti + l % 32 (v) and of feature 32 tj + l % 32 (alpha_hat).
 template <typename TIn>
 struct UpdFrags {
   static constexpr int kV = sizeof(TIn) / 2;   // uint4 per 8 values of v
   uint4 v[4][kV];
   uint4 a[4][2];
+  // From the prep kernel's regrouped copies (fp32 storage).
   __device__ __forceinline__ void load(const StatePlan& pl, int64_t blk, int ti, int tj, int lane) {
     const auto rv = make_rsrc(static_cast<const TIn*>(pl.VT) + blk * 512 * 8, 512 * 8 * static_cast<int>(sizeof(TIn)));
     const auto ra = make_rsrc(pl.AT + blk * 512 * 8, 512 * 8 * 4);
@@ -436,6 +447,49 @@ __device__ __forceinline__ void rank_update(f32x16& X, const UpdFrags<TIn>& fr, 
       for (int e = 0; e < 8; ++e) vx[e] = __uint_as_float(vw[e]);
       X = mma_split(split3(vx), B, X);
     }
+  }
+}
+
+// The same update with bf16 storage, its operands read from the block's
+// swizzled LDS rows (column reads: slot (kb, e) of lane l is token
+// 16 kb + 8 (l / 32) + e).  The lane's byte offsets of rows 8 (l / 32) + e
+// come precomputed (UpdOffsets); rows 16 kb further are constant offsets.
+struct UpdOffsets {
+  int v[8], a[8];
+  __device__ __forceinline__ void init(int ti, int tj, int lane) {
+    const int h = lane >> 5, fv = ti * 32 + (lane & 31), fa = tj * 32 + (lane & 31);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = 2 * swz16(8 * h + e, fv);   // bf16 rows
+      a[e] = 4 * swz32(8 * h + e, fa);   // fp32 rows
+    }
+  }
+};
+__device__ __forceinline__ void rank_update_lds(f32x16& X, const char* VR, const char* AR, const UpdOffsets& off,
+                                                const float* wp, float se, int h) {
+  uint32_t vr[4][8];
+  float ar[4][8];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vr[kb][e] = *reinterpret_cast<const uint16_t*>(VR + off.v[e] + 2 * swz16(16 * kb, 0));
+      ar[kb][e] = *reinterpret_cast<const float*>(AR + off.a[e] + 4 * swz32(16 * kb, 0));
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 16; ++s) X[s] *= se;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float4 w0 = *reinterpret_cast<const float4*>(wp + 16 * kb + 8 * h);
+    const float4 w1 = *reinterpret_cast<const float4*>(wp + 16 * kb + 8 * h + 4);
+    const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float bx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bx[e] = ar[kb][e] * ww[e];
+    const uint4 va = make_uint4(vr[kb][0] | (vr[kb][1] << 16), vr[kb][2] | (vr[kb][3] << 16),
+                                vr[kb][4] | (vr[kb][5] << 16), vr[kb][6] | (vr[kb][7] << 16));
+    X = mma_split(__builtin_bit_cast(bf16x8, va), split3(bx), X);
   }
 }
 
@@ -517,20 +571,28 @@ template <typename TIn>
 __global__ void __launch_bounds__(kChainThreads)
 vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float* __restrict__ n_T,
                        int32_t* __restrict__ stats, const int32_t* __restrict__ chain_info, float cap, int cap_on) {
-  // Buffers that buffer-to-LDS loads fill and that the same waves read (the
-  // v and alpha_hat rows) have one LDS object per generation, selected at
-  // compile time: the compiler then sees that reading one generation does not
-  // depend on loads still in flight into the other, and waits for those only
-  // at the barrier.  A generation is written only in the block after its last
-  // reader's barrier, and read only in the block after the one that wrote it:
-  // every cross-wave hand-off goes through a barrier.
+  // Buffers that buffer-to-LDS loads fill have one LDS object per
+  // generation, every one selected at compile time: the compiler then sees
+  // that reading one does not depend on loads still in flight into another.
+  // A block's copies are issued when it starts, into buffers whose last
+  // reader passed the previous barrier.  Each product wave waits for its own
+  // copies before the block's closing barrier (the barrier alone does not
+  // wait for them), so what one wave copies is complete for every wave after
+  // that barrier; the recursion wave copies Kx, which only it reads, into
+  // the one buffer right after reading it.
+  // The v and alpha_hat rows of block j arrive during block j-2, give the
+  // bilinear terms in block j-1 and, with bf16 storage, the update's
+  // operands in block j+1: four generations.  With fp32 storage the update's
+  // operands come from the prep kernel's regrouped copies instead, and two
+  // generations (twice the bytes each) suffice.
   constexpr bool kBf = sizeof(TIn) == 2;
-  constexpr int kRowGens = 2;
+  constexpr int kRowGens = kBf ? 4 : 2;
   constexpr int kVR4 = kLb * kD * static_cast<int>(sizeof(TIn)) / 16;   // float4s per v-row block
+  constexpr int kAR4x = kBf ? kLb * kD / 4 : 1, kVR4x = kBf ? kVR4 : 1;  // generations 2 and 3
   __shared__ float4 sCK0[kPackRows * kLb / 4], sCK1[kPackRows * kLb / 4];   // the pack, swizzled
-  __shared__ float4 sKX0[kLb * kLb / 4], sKX1[kLb * kLb / 4];   // Kx, swizzled
-  __shared__ float4 sAR0[kLb * kD / 4], sAR1[kLb * kD / 4];     // alpha_hat rows, swizzled
-  __shared__ float4 sVR0[kVR4], sVR1[kVR4];                     // v rows, swizzled
+  __shared__ float4 sKX[kLb * kLb / 4];                         // Kx, swizzled
+  __shared__ float4 sAR0[kLb * kD / 4], sAR1[kLb * kD / 4], sAR2[kAR4x], sAR3[kAR4x];   // alpha_hat rows, swizzled
+  __shared__ float4 sVR0[kVR4], sVR1[kVR4], sVR2[kVR4x], sVR3[kVR4x];                   // v rows, swizzled
   __shared__ float sH[2][4 * kLb];                              // partial v^T S alpha per product wave
   __shared__ float sW[2][kLb];                                  // update weights sigma_end/sigma_{s-1}
   __shared__ float sSig[2];                                     // sigma_end
@@ -538,8 +600,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   __shared__ float sLog[2][2 * kLb];                            // per-token log2 scales
   __shared__ float sNb[2][kD];                                  // n at the block start
   __shared__ float sRed[8];
-  auto rows_ar = [&](auto rc) -> float4* { return decltype(rc)::value ? sAR1 : sAR0; };
-  auto rows_vr = [&](auto rc) -> float4* { return decltype(rc)::value ? sVR1 : sVR0; };
+  auto rows_ar = [&](int r) -> float4* { return r == 0 ? sAR0 : (r == 1 ? sAR1 : (r == 2 ? sAR2 : sAR3)); };
+  auto rows_vr = [&](int r) -> float4* { return r == 0 ? sVR0 : (r == 1 ? sVR1 : (r == 2 ? sVR2 : sVR3)); };
 
   const int64_t chain = blockIdx.x;
   // The wave index is uniform; saying so keeps LDS destinations and buffer
@@ -577,12 +639,19 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       for (int i = 0; i < 4; ++i) dma_piece(r, reinterpret_cast<char*>(vr), m + 4 * i, vo32);
     }
   };
-  auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane) {
+  auto dma_pack = [&](int j, float4* ck, int lane) {
     const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
     dma_mat(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4, ck, vo32);
     if (m == 0) dma_piece(make_rsrc(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4),
                           reinterpret_cast<char*>(ck), 16, vo32);
-    if (j > b_lo) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
+  };
+  // Kx of block j, all 16 pieces, by the recursion wave.
+  auto dma_kx = [&](int j, int lane) {
+    const auto r = make_rsrc(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4);
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      dma_piece(r, reinterpret_cast<char*>(sKX), p,
+                (lane >> 4) * 256 + (((lane & 15) ^ ((4 * p + (lane >> 4)) & 15)) << 4));
   };
 
   // The recursion wave's per-block outputs, written from LDS by a product wave.
@@ -597,6 +666,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 
   f32x16 X = zero16();
   UpdFrags<TIn> fr;
+  UpdOffsets uoff;   // loop-invariant LDS offsets of the update's column reads
+  uoff.init(ti, tj, lane);
   float nvec = 0.f, N = 0.f, Nstart = 0.f;
   int fires = 0, first = -1;
   bool bad = false;
@@ -618,10 +689,10 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     }
     part = wave_sum(part);
     if (lane == 0) sRed[m] = part;
-    dma_kernels(b_lo, sCK0, sKX0, lane);
+    dma_pack(b_lo, sCK0, lane);
     dma_rows(b_lo, sAR0, sVR0, lane);
     if (b_lo + 1 < b_hi) dma_rows(b_lo + 1, sAR1, sVR1, lane);
-    fr.load(pl, blk0 + b_lo, ti, tj, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
   if (!rwave)
@@ -630,11 +701,13 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   __syncthreads();
   N = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
 
-  // ---- one block; RG (compile time) is the row generation of block b -------
+  // ---- one block; RG (compile time) is the row generation of block b, and
+  // its parity the generation of the pack and of the per-block LDS outputs.
   auto step = [&](auto rgc, int b) {
     constexpr int RG = decltype(rgc)::value;
     constexpr int RGp1 = (RG + 1) % kRowGens, RGp2 = (RG + 2) % kRowGens;
-    const int g = b & 1;
+    constexpr int RGm1 = (RG + kRowGens - 1) % kRowGens;
+    constexpr int g = RG & 1;   // = b & 1, as b_lo is even
     const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
     // A fresh copy of the lane index per block keeps the many lane-dependent
     // LDS addresses from being hoisted out of the loop (and spilled).
@@ -656,7 +729,10 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         // depends on the block-start norm linearly, with factor sigma_end^2).
         const float* np = sNrm[g ^ 1];
         N = fmaf(se * se, ((np[0] + np[1]) + (np[2] + np[3])) - Nstart, N);
-        const float* KX = reinterpret_cast<const float*>(g ? sKX1 : sKX0);
+        // This wave's own copies of Kx, issued one block ago (the compiler
+        // does not order these reads after them by itself).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const float* KX = reinterpret_cast<const float*>(sKX);
         const float* wprev = sW[g ^ 1];
         float cx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -672,6 +748,11 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
             cx[c & 3] = fmaf(xv[c].x, wv[c].x, fmaf(xv[c].y, wv[c].y, fmaf(xv[c].z, wv[c].z, fmaf(xv[c].w, wv[c].w, cx[c & 3]))));
         }
         acc = fmaf(se, acc, (cx[0] + cx[1]) + (cx[2] + cx[3]));
+      }
+      // The next block's Kx into the buffer just read (its reads complete first).
+      if (b + 1 < b_hi) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        dma_kx(b + 1, ln);
       }
       Nstart = N;
       sNb[g][t] = nvec;
@@ -710,12 +791,21 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       sLog[g][2 * t + 1] = l_t;
       nvec += ks;
     } else {
+      // Next block's pack into the other parity (the recursion wave finished
+      // with it one block ago); rows of block b+2 into the generation whose
+      // last reader was the previous block.
+      if (b + 1 < b_hi) dma_pack(b + 1, g ? sCK0 : sCK1, ln);
+      if (b + 2 < b_hi) dma_rows(b + 2, rows_ar(RGp2), rows_vr(RGp2), ln);
       if (b > b_lo) {
         // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.
-        rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
-        fr.load(pl, blk0 + b, ti, tj, ln);
+        if constexpr (kBf)
+          rank_update_lds(X, reinterpret_cast<const char*>(rows_vr(RGm1)), reinterpret_cast<const char*>(rows_ar(RGm1)),
+                          uoff, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
+        else
+          rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
         if (m == 0) store_block_outputs(b - 1, sLog[g ^ 1], sNb[g ^ 1], ln);
       }
+      if constexpr (!kBf) fr.load(pl, blk0 + b, ti, tj, ln);   // block b's, for the next update
       {
         const int xs_off = ((ti * 32 + 4 * (ln >> 5)) * kD + tj * 32 + (ln & 31)) * 4;
         const auto rs = make_rsrc(pl.Xsnap + (blk0 + b) * kD * kD, kD * kD * 4);
@@ -728,29 +818,36 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         part = wave_sum(part);
         if (ln == 0) sNrm[g][m] = part;
       }
-      // Next block's pack and Kx into the other parity (the recursion wave
-      // finished with it one block ago); rows of block b+2 into the
-      // generation block b used (last read one block ago).
-      if (b + 1 < b_hi) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
-      if (b + 2 < b_hi) dma_rows(b + 2, rows_ar(std::integral_constant<int, RGp2>{}),
-                                 rows_vr(std::integral_constant<int, RGp2>{}), ln);
       if (b + 1 < b_hi)
-        bilinear_terms<TIn>(X, reinterpret_cast<const char*>(rows_vr(std::integral_constant<int, RGp1>{})),
-                            reinterpret_cast<const float*>(rows_ar(std::integral_constant<int, RGp1>{})),
+        bilinear_terms<TIn>(X, reinterpret_cast<const char*>(rows_vr(RGp1)), reinterpret_cast<const float*>(rows_ar(RGp1)),
                             sH[g ^ 1] + m * kLb, ti, tj, ln);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies have landed
     }
-    __syncthreads();
+    // The block's closing barrier, without the fence of __syncthreads: that
+    // fence would also hold the recursion wave until its Kx copies land.
+    // LDS writes are complete first; the asm is a compiler memory barrier.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  for (int b = b_lo; b < b_hi; b += 2) {   // b_lo is even: parity 0 first
+  for (int b = b_lo; b < b_hi; b += kRowGens) {   // b_lo is even: parity 0 first
     step(std::integral_constant<int, 0>{}, b);
     if (b + 1 < b_hi) step(std::integral_constant<int, 1>{}, b + 1);
+    if constexpr (kRowGens == 4) {
+      if (b + 2 < b_hi) step(std::integral_constant<int, 2>{}, b + 2);
+      if (b + 3 < b_hi) step(std::integral_constant<int, 3>{}, b + 3);
+    }
   }
 
   // ---- epilogue: the segment's last block update ----------------------------
   if (!rwave) {
     const int g = (b_hi - 1) & 1;
     if (m == 0) store_block_outputs(b_hi - 1, sLog[g], sNb[g], lane);
-    rank_update<TIn>(X, fr, sW[g], sSig[g], h);
+    if constexpr (kBf) {
+      const int r = (b_hi - 1 - b_lo) % kRowGens;
+      rank_update_lds(X, reinterpret_cast<const char*>(rows_vr(r)), reinterpret_cast<const char*>(rows_ar(r)), uoff,
+                      sW[g], sSig[g], h);
+    } else {
+      rank_update<TIn>(X, fr, sW[g], sSig[g], h);
+    }
     if (sg.last) {
       float* st = S_T + chain * kD * kD;
 #pragma unroll

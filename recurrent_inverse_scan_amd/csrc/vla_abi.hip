@@ -140,8 +140,10 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     const size_t nb = cl.nblk, T = static_cast<size_t>(p->T);
     cl.off_K = off; off = align_up(off + C * nb * 68 * 64 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
-    cl.off_VT = off; off = align_up(off + C * nb * d2 * (p->in_dtype == VLA_BF16 ? 2 : 4));
-    cl.off_AT = off; off = align_up(off + C * nb * d2 * 4);
+    // Regrouped update operands: fp32 storage only (bf16 reads its LDS rows).
+    const size_t nreg = p->in_dtype == VLA_BF16 ? 0 : C * nb * d2;
+    cl.off_VT = off; off = align_up(off + nreg * 4);
+    cl.off_AT = off; off = align_up(off + nreg * 4);
     cl.off_X = off; off = align_up(off + C * nb * d2 * 4);
     cl.off_wsig = off; off = align_up(off + C * T * 2 * 4);
     cl.off_ld = off; off = align_up(off + C * T * 4);
