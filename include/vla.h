@@ -15,7 +15,12 @@
  *   never allocates, frees or retains device memory.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Work is enqueued asynchronously on it; no call synchronises the host,
- *   except vla_scan_forward with `validate` set (documented there).
+ *   except vla_scan_forward with `validate` set (documented there).  The
+ *   chunked schedule also runs part of its work on a side stream the library
+ *   owns (one per device, default priority, created on first use and kept):
+ *   that work is ordered after what `stream` already holds and joined back
+ *   into `stream` with events before the call returns, so whatever is
+ *   enqueued on `stream` later sees all of it.
  * - Layouts are row-major with the feature dimension contiguous.
  * - Errors: every argument and shape check happens before anything is
  *   launched.  A failed check returns VLA_EINVAL or VLA_EUNSUPPORTED and
@@ -70,11 +75,16 @@ typedef struct {
   int32_t schedule;      /* vla_schedule_t */
   int32_t validate;      /* nonzero: synchronous NaN/Inf pre-check of the inputs */
   int32_t chunk_len;     /* tokens per chunk of the chunked schedule; 0 = library picks */
+  int32_t segment_blocks; /* chunked schedule: blocks of 64 tokens per state-pass
+                             segment, rounded up to even and to at most 16
+                             segments (the chain kernel runs one segment while a
+                             side stream preps the next and reads out the last);
+                             0 = library picks (256), < 0 = one segment */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
- * den_eps = 1e-6, t0 = 0, automatic schedule, no validation, chunk_len = 0.
- * Host pointer. */
+ * den_eps = 1e-6, t0 = 0, automatic schedule, no validation, chunk_len = 0,
+ * segment_blocks = 0.  Host pointer. */
 void vla_scan_params_init(vla_scan_params_t* p);
 
 /* Bytes of device workspace vla_scan_forward needs for these parameters
@@ -132,7 +142,10 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  * parallel, and a per-chain pass applies the state update, cap and readout.
  * A chain where the guard fires, or whose chunk-start inverse is not
  * positive definite, is recomputed sequentially in the same call, so the
- * result does not depend on the schedule beyond float32 rounding.  CHUNKED
+ * result does not depend on the schedule beyond float32 rounding.  The
+ * per-chain pass runs in segments of segment_blocks blocks of 64 tokens: a
+ * segment's chain kernel overlaps the next segment's preparation and the
+ * previous one's readout on the side stream.  CHUNKED
  * needs chunk_len to divide nudge_period (when nonzero) and t0; AUTO uses it
  * for d = 64 when there are few chains and long sequences.
  *
@@ -174,8 +187,8 @@ vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dt
  * vla_timing_enable(1) creates VLA_TIMING_SLOTS pairs of HIP events on the
  * device current at that moment and makes each following vla_scan_forward
  * that runs the chunked schedule record one pair on its stream, immediately
- * before and after that kernel, until the slots are used up (later calls are
- * not recorded).  vla_timing_enable(0) stops recording and releases the
+ * before and after each launch of that kernel (one per segment), until the
+ * slots are used up (later launches are not recorded).  vla_timing_enable(0) stops recording and releases the
  * events.  vla_timing_collect waits for the recorded events, writes up to
  * `cap` durations in milliseconds to `ms` (oldest first), stores how many it
  * wrote in *n and clears the record; recording continues if enabled.

@@ -36,6 +36,7 @@ class ScanParams(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("validate", ctypes.c_int32),
         ("chunk_len", ctypes.c_int32),
+        ("segment_blocks", ctypes.c_int32),
     ]
 
 

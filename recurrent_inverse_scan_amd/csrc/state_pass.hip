@@ -244,9 +244,8 @@ __device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int t
 }
 
 template <typename TIn>
-__global__ void __launch_bounds__(kThreads)
-vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
-                      const TIn* __restrict__ v, int b_lo, int nb) {
+__device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                           const TIn* __restrict__ v, int b_lo, int nb, int64_t item) {
   constexpr int kRd = PrepLds<TIn>::kRd;
   extern __shared__ float4 smem4[];
   TIn* Vb = reinterpret_cast<TIn*>(smem4);    // [64][kRd] v rows of the block
@@ -255,8 +254,8 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   TIn* Vp = Kb + kLb * kRd;                   // v rows of the previous block
   float* Af = reinterpret_cast<float*>(Vp + kLb * kRd);   // [64][kLd] alpha_hat rows, later K
   float* Ap = Af + kLb * kLd;                 // previous block's alpha_hat rows, later masked q.k
-  const int64_t chain = blockIdx.x / nb;
-  const int b = b_lo + static_cast<int>(blockIdx.x % nb);
+  const int64_t chain = item / nb;
+  const int b = b_lo + static_cast<int>(item % nb);
   const int64_t blk = chain * pl.nblk + b;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -350,6 +349,18 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
   for (int rep = 0; rep < 4; ++rep) {
     const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
     *reinterpret_cast<float4*>(pack + r * kLb + c4) = *reinterpret_cast<const float4*>(Af + r * kLd + c4);
+  }
+}
+
+// Blocks [b_lo, b_lo + nb) of every chain; a grid smaller than chains * nb
+// strides over them.
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
+                      const TIn* __restrict__ v, int b_lo, int nb, int64_t items) {
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    prep_block<TIn>(pl, q, k, v, b_lo, nb, item);
+    __syncthreads();   // LDS is restaged by the next item
   }
 }
 
@@ -901,9 +912,9 @@ struct ReadoutLds {
 };
 
 template <typename TIn>
-__global__ void __launch_bounds__(kThreads)
-vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
-                         int32_t* __restrict__ chain_info, int b_lo, int nb) {
+__device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __restrict__ q, TIn* __restrict__ o,
+                                              float den_eps, int32_t* __restrict__ chain_info, int b_lo, int nb,
+                                              int64_t item) {
   constexpr int kQd = ReadoutLds<TIn>::kQd;
   extern __shared__ float4 smem4[];
   TIn* Qs = reinterpret_cast<TIn*>(smem4);          // [64 t][kQd] q rows
@@ -915,8 +926,8 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
   float* sl = wl + kLb;                             // [64] log2 sigma_t
   float* dl = sl + kLb;                             // [64] den_t
   float* nl = dl + kLb;                             // [64] n at the block start
-  const int64_t chain = blockIdx.x / nb;
-  const int b = b_lo + static_cast<int>(blockIdx.x % nb);
+  const int64_t chain = item / nb;
+  const int b = b_lo + static_cast<int>(item % nb);
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
@@ -1007,6 +1018,16 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
   if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
 }
 
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
+                         int32_t* __restrict__ chain_info, int b_lo, int nb, int64_t items) {
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    readout_block<TIn>(pl, q, o, den_eps, chain_info, b_lo, nb, item);
+    __syncthreads();   // LDS is restaged by the next item
+  }
+}
+
 }  // namespace
 
 template <typename TIn>
@@ -1033,19 +1054,20 @@ static void allow_state_lds() {
   (void)once;
 }
 
-hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb,
+hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb, int max_wg,
                              hipStream_t stream) {
   if (nb <= 0) return hipSuccess;
   allow_state_lds();
-  const unsigned blocks = static_cast<unsigned>(chains * nb);
+  const int64_t items = static_cast<int64_t>(chains) * nb;
+  const unsigned blocks = static_cast<unsigned>(max_wg > 0 ? std::min<int64_t>(items, max_wg) : items);
   if (pl.bf16)
     hipLaunchKernelGGL(vla_state_prep_kernel<uint16_t>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<uint16_t>(),
                        stream, pl, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), b_lo, nb);
+                       static_cast<const uint16_t*>(a.v), b_lo, nb, items);
   else
     hipLaunchKernelGGL(vla_state_prep_kernel<float>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<float>(), stream,
                        pl, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                       static_cast<const float*>(a.v), b_lo, nb);
+                       static_cast<const float*>(a.v), b_lo, nb, items);
   return hipGetLastError();
 }
 
@@ -1065,18 +1087,19 @@ hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const Sca
 }
 
 hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains, int b_lo,
-                                int nb, hipStream_t stream) {
+                                int nb, int max_wg, hipStream_t stream) {
   if (nb <= 0) return hipSuccess;
   allow_state_lds();
-  const unsigned blocks = static_cast<unsigned>(chains * nb);
+  const int64_t items = static_cast<int64_t>(chains) * nb;
+  const unsigned blocks = static_cast<unsigned>(max_wg > 0 ? std::min<int64_t>(items, max_wg) : items);
   if (pl.bf16)
     hipLaunchKernelGGL(vla_state_readout_kernel<uint16_t>, dim3(blocks), dim3(kThreads),
                        state_readout_lds_bytes<uint16_t>(), stream, pl, static_cast<const uint16_t*>(a.q),
-                       static_cast<uint16_t*>(a.o), a.den_eps, chain_info, b_lo, nb);
+                       static_cast<uint16_t*>(a.o), a.den_eps, chain_info, b_lo, nb, items);
   else
     hipLaunchKernelGGL(vla_state_readout_kernel<float>, dim3(blocks), dim3(kThreads), state_readout_lds_bytes<float>(),
                        stream, pl, static_cast<const float*>(a.q), static_cast<float*>(a.o), a.den_eps, chain_info,
-                       b_lo, nb);
+                       b_lo, nb, items);
   return hipGetLastError();
 }
 

@@ -36,6 +36,60 @@ void timing_release(Timing& t) {
   t.on = false;
 }
 
+// A side stream per device (default priority, non-blocking) and the events
+// that order the state pass's parallel kernels on it against the chain
+// kernel segments on the caller's stream.  Created on first use and kept
+// until the process ends; enqueueing on them is serialised by the mutex.
+constexpr int kMaxChainSegs = 16;
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[2 * kMaxChainSegs + 2] = {};
+  int side_wg = 0;   // workgroups of a prep or readout launch beside the chain kernel
+  bool ready = false;
+};
+struct SidePool {
+  std::mutex mu;
+  SideStream dev[64];
+};
+SidePool& side_pool() {
+  static SidePool p;
+  return p;
+}
+// Needs side_pool().mu held; nullptr (and the HIP error in *err) on failure.
+SideStream* side_stream(hipError_t* err) {
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  SideStream& ss = side_pool().dev[dev];
+  if (!ss.ready) {
+    int ncu = 0;
+    if ((*err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return nullptr;
+    // Five eighths of the compute units: the side work still keeps ahead of
+    // the chain kernel, which loses a quarter of its speed to a full-width
+    // side launch (measured on the 16-chain, 65536-token workload).
+    ss.side_wg = std::max(1, ncu * 5 / 8);
+    if ((*err = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return nullptr;
+    for (hipEvent_t& e : ss.ev)
+      if ((*err = hipEventCreateWithFlags(&e, hipEventDisableTiming)) != hipSuccess) return nullptr;
+    ss.ready = true;
+  }
+  *err = hipSuccess;
+  return &ss;
+}
+
+// Blocks per chain-kernel segment for nblk blocks of 64 tokens: seg_blocks
+// (default 256; < 0: all in one) rounded up to even, and large enough for at
+// most kMaxChainSegs segments (a launch per segment costs a few microseconds).
+int chain_segment_len(int nblk, int seg_blocks) {
+  if (seg_blocks < 0 || seg_blocks > nblk) seg_blocks = nblk;
+  if (seg_blocks == 0) seg_blocks = 256;
+  seg_blocks = std::max(seg_blocks, (nblk + kMaxChainSegs - 1) / kMaxChainSegs);
+  return (seg_blocks + 1) & ~1;
+}
+
 vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 vla_status_t fail(vla_status_t s, const char* fmt, ...) {
   char buf[512];
@@ -197,6 +251,7 @@ void vla_scan_params_init(vla_scan_params_t* p) {
   p->schedule = VLA_SCHEDULE_AUTO;
   p->validate = 0;
   p->chunk_len = 0;
+  p->segment_blocks = 0;
 }
 
 vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
@@ -361,37 +416,86 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
                                            static_cast<int>(chains), stream)) != hipSuccess)
     return hip_fail(e, "chunked inverse launch");
 
-  // State pass: prep, the chain kernel over the whole sequence, readout.
-  // (Cutting the sequence into segments to overlap prep and readout with the
-  // chain on other streams was measured slower: the chain kernel loses more
-  // to the shared memory system than the overlap saves.)
+  // State pass: prep, the chain kernel, readout.  The sequence is cut into
+  // segments (even block counts): the chain kernel runs them one after
+  // another on the caller's stream while a side stream preps the next
+  // segment and reads out the previous one, so only the first prep and the
+  // last readout stay outside the chain kernel's time.  The side launches
+  // between are held to a part of the chip (SideStream::side_wg).
   const int nblk = cl.nblk;
-  if ((e = vla::launch_state_prep(sp, a, static_cast<int>(chains), 0, nblk, stream)) != hipSuccess)
-    return hip_fail(e, "state prep launch");
-  vla::ChainSeg sg{};
-  sg.b_lo = 0;
-  sg.b_hi = nblk;
-  sg.S_in = pl.S_init;
-  sg.S_in_stride = 64 * 64;
-  sg.n_in = pl.n_init;
-  sg.n_in_stride = 64;
-  sg.n_carry = n_carry;
-  sg.counters = counters;
-  sg.last = 1;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  {
+  const int seg_len = chain_segment_len(nblk, p->segment_blocks);   // even: segments start on even blocks
+  const int nseg = (nblk + seg_len - 1) / seg_len;                   // none empty
+  auto seg_lo = [&](int sidx) { return std::min(nblk, sidx * seg_len); };
+  auto next_timing = [&](hipEvent_t* ev0, hipEvent_t* ev1) {
     Timing& tm = timing();
     std::lock_guard<std::mutex> lock(tm.mu);
+    *ev0 = *ev1 = nullptr;
     if (tm.on && tm.used < VLA_TIMING_SLOTS) {
-      ev0 = tm.start[tm.used];
-      ev1 = tm.stop[tm.used];
+      *ev0 = tm.start[tm.used];
+      *ev1 = tm.stop[tm.used];
       ++tm.used;
     }
+  };
+  auto chain_seg = [&](int sidx) {
+    vla::ChainSeg sg{};
+    sg.b_lo = seg_lo(sidx);
+    sg.b_hi = seg_lo(sidx + 1);
+    if (sidx == 0) {
+      sg.S_in = pl.S_init;
+      sg.S_in_stride = 64 * 64;
+      sg.n_in = pl.n_init;
+    } else {   // S and n where the previous segment left them
+      sg.S_in = sp.Xsnap + static_cast<int64_t>(sg.b_lo) * 64 * 64;
+      sg.S_in_stride = static_cast<int64_t>(nblk) * 64 * 64;
+      sg.n_in = n_carry;
+    }
+    sg.n_in_stride = 64;
+    sg.n_carry = n_carry;
+    sg.counters = counters;
+    sg.last = sg.b_hi == nblk ? 1 : 0;
+    return sg;
+  };
+  const int nch = static_cast<int>(chains);
+  if (nseg == 1) {
+    if ((e = vla::launch_state_prep(sp, a, nch, 0, nblk, 0, stream)) != hipSuccess) return hip_fail(e, "state prep launch");
+    hipEvent_t ev0, ev1;
+    next_timing(&ev0, &ev1);
+    if ((e = vla::launch_state_chain(sp, chain_seg(0), a, pl.chain_info, nch, stream, ev0, ev1)) != hipSuccess)
+      return hip_fail(e, "state chain launch");
+    if ((e = vla::launch_state_readout(sp, a, pl.chain_info, nch, 0, nblk, 0, stream)) != hipSuccess)
+      return hip_fail(e, "state readout launch");
+  } else {
+    std::lock_guard<std::mutex> lock(side_pool().mu);
+    SideStream* ss = side_stream(&e);
+    if (!ss) return hip_fail(e, "side stream setup");
+    hipStream_t side = ss->stream;
+    hipEvent_t ev_in = ss->ev[0], ev_end = ss->ev[1];
+    hipEvent_t* ev_prep = ss->ev + 2;
+    hipEvent_t* ev_chain = ss->ev + 2 + kMaxChainSegs;
+    auto prep = [&](int sidx) {
+      hipError_t r = vla::launch_state_prep(sp, a, nch, seg_lo(sidx), seg_lo(sidx + 1) - seg_lo(sidx),
+                                            sidx == 0 ? 0 : ss->side_wg, side);
+      return r != hipSuccess ? r : hipEventRecord(ev_prep[sidx], side);
+    };
+    if ((e = hipEventRecord(ev_in, stream)) != hipSuccess || (e = hipStreamWaitEvent(side, ev_in, 0)) != hipSuccess ||
+        (e = prep(0)) != hipSuccess)
+      return hip_fail(e, "state prep launch");
+    for (int sidx = 0; sidx < nseg; ++sidx) {
+      if (sidx + 1 < nseg && (e = prep(sidx + 1)) != hipSuccess) return hip_fail(e, "state prep launch");
+      hipEvent_t ev0, ev1;
+      next_timing(&ev0, &ev1);
+      if ((e = hipStreamWaitEvent(stream, ev_prep[sidx], 0)) != hipSuccess ||
+          (e = vla::launch_state_chain(sp, chain_seg(sidx), a, pl.chain_info, nch, stream, ev0, ev1)) != hipSuccess ||
+          (e = hipEventRecord(ev_chain[sidx], stream)) != hipSuccess)
+        return hip_fail(e, "state chain launch");
+      if ((e = hipStreamWaitEvent(side, ev_chain[sidx], 0)) != hipSuccess ||
+          (e = vla::launch_state_readout(sp, a, pl.chain_info, nch, seg_lo(sidx), seg_lo(sidx + 1) - seg_lo(sidx),
+                                         sidx + 1 == nseg ? 0 : ss->side_wg, side)) != hipSuccess)
+        return hip_fail(e, "state readout launch");
+    }
+    if ((e = hipEventRecord(ev_end, side)) != hipSuccess || (e = hipStreamWaitEvent(stream, ev_end, 0)) != hipSuccess)
+      return hip_fail(e, "side stream join");
   }
-  if ((e = vla::launch_state_chain(sp, sg, a, pl.chain_info, static_cast<int>(chains), stream, ev0, ev1)) != hipSuccess)
-    return hip_fail(e, "state chain launch");
-  if ((e = vla::launch_state_readout(sp, a, pl.chain_info, static_cast<int>(chains), 0, nblk, stream)) != hipSuccess)
-    return hip_fail(e, "state readout launch");
   if ((e = vla::launch_stats_finalize(stats, pl.chain_info, static_cast<int>(chains), stream)) != hipSuccess)
     return hip_fail(e, "stats launch");
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);

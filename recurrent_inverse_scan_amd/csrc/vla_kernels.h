@@ -96,12 +96,13 @@ struct ChainSeg {
   int last;
 };
 
-// Prep and readout of blocks [b_lo, b_lo + nb) of every chain (parallel); the
-// readout flags non-finite outputs in chain_info.
-hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb,
+// Prep and readout of blocks [b_lo, b_lo + nb) of every chain (parallel, at
+// most max_wg workgroups if max_wg > 0); the readout flags non-finite outputs
+// in chain_info.
+hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains, int b_lo, int nb, int max_wg,
                              hipStream_t stream);
 hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains, int b_lo,
-                                int nb, hipStream_t stream);
+                                int nb, int max_wg, hipStream_t stream);
 // The chain kernel over one segment (one workgroup per chain).  Non-null
 // events are recorded on the stream right before and after it.
 hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,

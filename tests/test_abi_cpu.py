@@ -71,6 +71,7 @@ def test_params_struct_layout_matches_header(lib, tmp_path):
     assert (p.B, p.H, p.T, p.d, p.r, p.in_dtype) == (0, 0, 0, 64, 1, 0)
     assert abs(p.eps - 1e-6) < 1e-12 and abs(p.den_eps - 1e-6) < 1e-12
     assert (p.nudge_period, p.s_cap, p.t0, p.schedule, p.validate, p.chunk_len) == (0, 0.0, 0, 0, 0, 0)
+    assert p.segment_blocks == 0
 
 
 def _params(lib, **kw):

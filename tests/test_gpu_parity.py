@@ -341,6 +341,24 @@ def test_chunked_agrees_with_sequential():
         assert err <= (1e-2 if name == "o" else 1e-3), (name, err)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("seg", [2, 6, 10])
+def test_chunked_segments_match_oracle(dtype, seg):
+    """The per-chain pass cut into segments of `seg` blocks (the last one
+    ragged) with prep and readout on the side stream: every segment boundary
+    carries S, n and the cap counters; outputs match the oracle."""
+    cfg = CONFIGS["base"].with_(name=f"chunked-seg{seg}-{dtype}", B=1, H=3, T=2000, in_dtype=dtype,
+                                nudge_period=128, s_cap=30.0)
+    _say(f"case chunked segments {seg} {dtype}")
+    x = case(cfg, seed=16)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, segment_blocks=seg)
+    ref = run_oracle(x, cfg)
+    _, st = _check(cfg, out, ref)
+    assert ref["cap_fires"].min() > 10
+    assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
+    assert (np.abs(st[:, 3] - ref["first_cap_step"]) <= 1).all(), (st[:, 3], ref["first_cap_step"])
+
+
 def test_timing_hook_records_the_chain_kernel():
     """The measurement hook returns positive durations, the same number of
     chain-kernel launches for every chunked scan."""
@@ -358,3 +376,11 @@ def test_timing_hook_records_the_chain_kernel():
     _say(f"chain kernel ms {ms}")
     assert len(ms) >= 3 and len(ms) % 3 == 0 and all(t > 0 for t in ms)
     assert timing_collect() == []
+    timing_enable(True)
+    try:
+        for _ in range(2):
+            _gpu(x, cfg, schedule="chunked", segment_blocks=4)   # 10 blocks: segments of 4, 4, 2
+        ms = timing_collect()
+    finally:
+        timing_enable(False)
+    assert len(ms) == 6 and all(t > 0 for t in ms), ms
