@@ -408,9 +408,10 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   float* n_carry = reinterpret_cast<float*>(ws + cl.off_ncarry);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + cl.off_cnt);
 
-  // Chunk-start inverses and the inverse pass over all chunks at once: each
-  // chunk's recurrence is sequential, so its wall time is one chunk's,
-  // whatever the number of chunks that run side by side.
+  // Chunk-start inverses and the inverse pass over all chunks at once.  The
+  // pass keeps every SIMD busy only with all chunks side by side: on a part
+  // of them (a segment's) it takes nearly as long, so it is not pipelined
+  // with the chain kernel below.
   if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
   if ((e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
                                            static_cast<int>(chains), stream)) != hipSuccess)
@@ -423,8 +424,8 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // last readout stay outside the chain kernel's time.  The side launches
   // between are held to a part of the chip (SideStream::side_wg).
   const int nblk = cl.nblk;
-  const int seg_len = chain_segment_len(nblk, p->segment_blocks);   // even: segments start on even blocks
-  const int nseg = (nblk + seg_len - 1) / seg_len;                   // none empty
+  const int seg_len = chain_segment_len(nblk, p->segment_blocks);
+  const int nseg = (nblk + seg_len - 1) / seg_len;   // none empty
   auto seg_lo = [&](int sidx) { return std::min(nblk, sidx * seg_len); };
   auto next_timing = [&](hipEvent_t* ev0, hipEvent_t* ev1) {
     Timing& tm = timing();
@@ -474,7 +475,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     hipEvent_t* ev_chain = ss->ev + 2 + kMaxChainSegs;
     auto prep = [&](int sidx) {
       hipError_t r = vla::launch_state_prep(sp, a, nch, seg_lo(sidx), seg_lo(sidx + 1) - seg_lo(sidx),
-                                            sidx == 0 ? 0 : ss->side_wg, side);
+                                 sidx == 0 ? 0 : ss->side_wg, side);
       return r != hipSuccess ? r : hipEventRecord(ev_prep[sidx], side);
     };
     if ((e = hipEventRecord(ev_in, stream)) != hipSuccess || (e = hipStreamWaitEvent(side, ev_in, 0)) != hipSuccess ||

@@ -342,16 +342,18 @@ def test_chunked_agrees_with_sequential():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("seg", [2, 6, 10])
-def test_chunked_segments_match_oracle(dtype, seg):
-    """The per-chain pass cut into segments of `seg` blocks (the last one
-    ragged) with prep and readout on the side stream: every segment boundary
-    carries S, n and the cap counters; outputs match the oracle."""
-    cfg = CONFIGS["base"].with_(name=f"chunked-seg{seg}-{dtype}", B=1, H=3, T=2000, in_dtype=dtype,
-                                nudge_period=128, s_cap=30.0)
-    _say(f"case chunked segments {seg} {dtype}")
+@pytest.mark.parametrize("L,period,seg", [(64, 128, 2), (64, 128, 6), (64, 128, 10), (128, 128, 3), (96, 192, 5)])
+def test_chunked_segments_match_oracle(dtype, L, period, seg):
+    """The per-chain pass cut into segments (an even number of blocks: seg
+    rounds up to 2, 6, 10, 4 and 6 blocks here; the last segment ragged and
+    boundaries inside chunks for L = 96 and 128), the next segment's prep and
+    the last one's readout on the side stream: every segment boundary carries
+    S, n and the cap counters; outputs match the oracle."""
+    cfg = CONFIGS["base"].with_(name=f"chunked-L{L}-seg{seg}-{dtype}", B=1, H=3, T=2000, in_dtype=dtype,
+                                nudge_period=period, s_cap=30.0)
+    _say(f"case chunked L={L} segments {seg} {dtype}")
     x = case(cfg, seed=16)
-    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, segment_blocks=seg)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg)
     ref = run_oracle(x, cfg)
     _, st = _check(cfg, out, ref)
     assert ref["cap_fires"].min() > 10
