@@ -9,12 +9,14 @@ tokens, Frobenius cap 1e3).
 
 Prints one JSON line.  ``value`` is tokens*heads per second of the whole step.
 ``roofline`` reports the dominant kernel, the state-chain kernel of the
-chunked schedule (the sequential S/cap recursion): its algorithmic flops are
-those of the memory update and the cap's norm, 2 d^2 + 2 d^2 per token*head,
-over its duration from HIP events the library records on the kernel's own
-stream during the timed steps; ``traffic`` is its HBM bytes per launch from
-rocprofv3 counters (profiles/state_chain_long_traffic.md), or null when the
-kernel sources have changed since they were taken.  ``scan_valu_frac`` is the
+chunked schedule (the sequential S/cap recursion, launched once per segment
+of the sequence): its algorithmic flops per launch are those of the memory
+update and the cap's norm, 2 d^2 + 2 d^2 per token*head of the launch's
+segment, over the launch's mean duration from HIP events the library records
+on the kernel's own stream during the timed steps; ``traffic`` is its HBM
+bytes per launch from rocprofv3 counters
+(profiles/state_chain_long_traffic.md), or null when the kernel sources have
+changed since they were taken.  ``scan_valu_frac`` is the
 whole scan's algorithmic flops 2 (2r+3) d^2 per token*head against the fp32
 vector peak.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded prefix
 of the same workload.
@@ -162,12 +164,14 @@ def main(argv=None) -> int:
     cap_on = cfg.s_cap is not None and cfg.s_cap > 0
     chain_flops = chain_flops_per_token_head(d, cap_on) * tok_heads
     if chain_ms:
-        roofline = {"bound": "alu", "achieved": chain_flops / (chain_ms * 1e-3) / 1e12,
+        launch_ms = chain_ms / chain_launches   # the segments are of equal length on this workload
+        launch_flops = chain_flops / chain_launches
+        roofline = {"bound": "alu", "achieved": launch_flops / (launch_ms * 1e-3) / 1e12,
                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": chain_flops / (chain_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                    "frac": launch_flops / (launch_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                     "traffic": measured_traffic(),
-                    "kernel": "vla_state_chain_kernel", "kernel_ms": chain_ms,
-                    "launches_per_step": chain_launches, "flops_per_step": chain_flops}
+                    "kernel": "vla_state_chain_kernel", "kernel_ms": launch_ms, "flops_per_launch": launch_flops,
+                    "launches_per_step": chain_launches, "kernel_ms_per_step": chain_ms}
     else:   # the sequential schedule has no chain kernel: the scan kernel is the dominant one
         roofline = {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
