@@ -58,15 +58,17 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... + x_i):
 // Hillis-Steele inside rows of 16 lanes with DPP row shifts, then the row
-// totals carried across rows.
+// totals carried across rows with the gfx9 row broadcasts (lane 15 of each
+// row into rows 1 and 3, then lane 31 into rows 2 and 3).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+__device__ __forceinline__ float wave_incl_scan(float x, int /*lane*/) {
   x += dpp_read<kRowShr1>(x);
   x += dpp_read<kRowShr2>(x);
   x += dpp_read<kRowShr4>(x);
   x += dpp_read<kRowShr8>(x);
-  const float r0 = readlane_f(x, 15), r1 = readlane_f(x, 31), r2 = readlane_f(x, 47);
-  x += (lane >= 16 ? r0 : 0.f) + (lane >= 32 ? r1 : 0.f) + (lane >= 48 ? r2 : 0.f);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast15, 0xA, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast31, 0xC, 0xF, false));
   return x;
 }
 
