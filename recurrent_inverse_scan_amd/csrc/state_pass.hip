@@ -46,11 +46,17 @@ constexpr int kD = 64;     // head dimension
 constexpr int kLb = 64;    // tokens per block
 constexpr int kLd = 68;    // LDS row stride in floats (rows of 16 lanes hit distinct banks)
 constexpr int kThreads = 256;
-// Per-block pack the recursion wave consumes: rows 0..63 hold the exclusive
-// row prefix sums of K, row 64 K(t,t), row 65 the row totals, row 66 the
-// block's key sum; row 67 is padding.
-constexpr int kPackRows = 68;
-constexpr int kRowE = 64, kRowTot = 65, kRowKs = 66;
+// Per-block pack the recursion wave consumes: the lower triangle of the
+// exclusive row prefix sums of K, row t's entries j = 0..t at t(t+1)/2 + j
+// (the sum over s < j of K(t,s); j = t is the sum before the diagonal), then
+// 64 values each of K(t,t), the row totals and the block's key sum; padded to
+// whole KiB.  Triangular numbers are distinct modulo 64, so lanes reading row
+// t's entry t(t+1)/2 + j for one j hit distinct LDS banks.
+constexpr int kTriN = kLb * (kLb + 1) / 2;
+constexpr int kPackE = kTriN, kPackTot = kTriN + kLb, kPackKs = kTriN + 2 * kLb;
+constexpr int kPackFloats = 2304;
+constexpr int kPackPieces = kPackFloats / 256;   // 1 KiB pieces
+static_assert(kPackKs + kLb <= kPackFloats, "pack layout");
 
 __device__ __forceinline__ f32x16 zero16() {
   return f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -213,9 +219,9 @@ __device__ __forceinline__ void stage_block(float* lds, const T* g, int nvalid, 
 
 // ---- prep: kernel matrices, local normaliser terms, block key sums ---------
 // Per block b of 64 tokens:
-//   pack      = CK[t][j] = sum_{s<j} K(t,s), K(t,s) = (v_t.v_s)(alpha_t.alpha_s)
-//               (exclusive row prefix), then K(t,t), sum_s K(t,s) and
-//               sum_t k_t as three more rows
+//   pack      = CK[t][j] = sum_{s<j} K(t,s) for j <= t, K(t,s) =
+//               (v_t.v_s)(alpha_t.alpha_s) (exclusive row prefix, lower
+//               triangle), then K(t,t), sum_s K(t,s) and sum_t k_t
 //   Kx[t][s]  = (v_t.v_s)(alpha_t.alpha_s) with s in block b-1 (b >= 1)
 //   ld[t]     = sum_{s<=t in block} k_s.q_t
 //   VT, AT    = (fp32 storage only) v and alpha_hat of the block regrouped as
@@ -286,12 +292,13 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
       xa = mma_split(aa, operand8(Ap + (tj * 32 + rl) * kLd + c0), xa);
     }
   }
-  float* pack = pl.Kmat + blk * kPackRows * kLb;
+  float* pack = pl.Kmat + blk * kPackFloats;
   if (tid < kLb) {
     float acc = 0.f;
     for (int t = 0; t < tcount; ++t) acc += Elem<TIn>::load(Kb + t * kRd + tid);
-    pack[kRowKs * kLb + tid] = acc;
-    pack[67 * kLb + tid] = 0.f;
+    pack[kPackKs + tid] = acc;
+  } else if (tid < kLb + (kPackFloats - kPackKs - kLb)) {
+    pack[kPackKs + tid] = 0.f;   // padding
   }
   // Matrix-core operands of the chain kernel's update for fp32 storage
   // (features of v and alpha_hat are LDS columns here); with bf16 storage the
@@ -336,8 +343,8 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
       Af[t * kLd + s] = run;
       run += x;
     }
-    pack[kRowE * kLb + t] = e_t;
-    pack[kRowTot * kLb + t] = run;
+    pack[kPackE + t] = e_t;
+    pack[kPackTot + t] = run;
   } else if (tid < 2 * kLb) {
     const int t = tid - kLb;
     float acc = 0.f;
@@ -345,10 +352,11 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
     if (t < tcount) pl.ld[row0 + t] = acc;
   }
   __syncthreads();
-#pragma unroll
-  for (int rep = 0; rep < 4; ++rep) {
-    const int e = tid + 256 * rep, r = e >> 4, c4 = (e & 15) * 4;
-    *reinterpret_cast<float4*>(pack + r * kLb + c4) = *reinterpret_cast<const float4*>(Af + r * kLd + c4);
+  for (int e = tid; e < kTriN; e += kThreads) {   // the triangle, row t at t(t+1)/2
+    int r = static_cast<int>((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+    r -= (r * (r + 1) / 2 > e) ? 1 : 0;
+    r += ((r + 1) * (r + 2) / 2 <= e) ? 1 : 0;
+    pack[e] = Af[r * kLd + (e - r * (r + 1) / 2)];
   }
 }
 
@@ -589,8 +597,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   // reader passed the previous barrier.  Each product wave waits for its own
   // copies before the block's closing barrier (the barrier alone does not
   // wait for them), so what one wave copies is complete for every wave after
-  // that barrier; the recursion wave copies Kx, which only it reads, into
-  // the one buffer right after reading it.
+  // that barrier.  The recursion wave touches no global memory inside the
+  // loop.
   // The v and alpha_hat rows of block j arrive during block j-2, give the
   // bilinear terms in block j-1 and, with bf16 storage, the update's
   // operands in block j+1: four generations.  With fp32 storage the update's
@@ -600,8 +608,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   constexpr int kRowGens = kBf ? 4 : 2;
   constexpr int kVR4 = kLb * kD * static_cast<int>(sizeof(TIn)) / 16;   // float4s per v-row block
   constexpr int kAR4x = kBf ? kLb * kD / 4 : 1, kVR4x = kBf ? kVR4 : 1;  // generations 2 and 3
-  __shared__ float4 sCK0[kPackRows * kLb / 4], sCK1[kPackRows * kLb / 4];   // the pack, swizzled
-  __shared__ float4 sKX[kLb * kLb / 4];                         // Kx, swizzled
+  __shared__ float4 sCK0[kPackFloats / 4], sCK1[kPackFloats / 4];   // the pack
+  __shared__ float4 sKX0[kLb * kLb / 4], sKX1[kLb * kLb / 4];   // Kx, swizzled
   __shared__ float4 sAR0[kLb * kD / 4], sAR1[kLb * kD / 4], sAR2[kAR4x], sAR3[kAR4x];   // alpha_hat rows, swizzled
   __shared__ float4 sVR0[kVR4], sVR1[kVR4], sVR2[kVR4x], sVR3[kVR4x];                   // v rows, swizzled
   __shared__ float sH[2][4 * kLb];                              // partial v^T S alpha per product wave
@@ -650,19 +658,12 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       for (int i = 0; i < 4; ++i) dma_piece(r, reinterpret_cast<char*>(vr), m + 4 * i, vo32);
     }
   };
-  auto dma_pack = [&](int j, float4* ck, int lane) {
-    const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
-    dma_mat(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4, ck, vo32);
-    if (m == 0) dma_piece(make_rsrc(pl.Kmat + (blk0 + j) * kPackRows * kLb, kPackRows * kLb * 4),
-                          reinterpret_cast<char*>(ck), 16, vo32);
-  };
-  // Kx of block j, all 16 pieces, by the recursion wave.
-  auto dma_kx = [&](int j, int lane) {
-    const auto r = make_rsrc(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4);
+  auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane) {
+    const auto r = make_rsrc(pl.Kmat + (blk0 + j) * kPackFloats, kPackFloats * 4);
 #pragma unroll
-    for (int p = 0; p < 16; ++p)
-      dma_piece(r, reinterpret_cast<char*>(sKX), p,
-                (lane >> 4) * 256 + (((lane & 15) ^ ((4 * p + (lane >> 4)) & 15)) << 4));
+    for (int p = m; p < kPackPieces; p += 4) dma_piece(r, reinterpret_cast<char*>(ck), p, 16 * lane);
+    const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
+    if (j > b_lo) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
   };
 
   // The recursion wave's per-block outputs, written from LDS by a product wave.
@@ -685,6 +686,10 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 
   // ---- prologue: continue from S and n at block b_lo -------------------------
   if (rwave) {
+    // The recursion wave is the kernel's critical path when the cap binds; it
+    // shares a SIMD with one product wave, whose long VALU runs would
+    // otherwise delay it.
+    __builtin_amdgcn_s_setprio(3);
     nvec = sg.n_in[chain * sg.n_in_stride + lane];
     if (b_lo > 0) {
       fires = sg.counters[chain * 2];
@@ -700,7 +705,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     }
     part = wave_sum(part);
     if (lane == 0) sRed[m] = part;
-    dma_pack(b_lo, sCK0, lane);
+    dma_kernels(b_lo, sCK0, sKX0, lane);
     dma_rows(b_lo, sAR0, sVR0, lane);
     if (b_lo + 1 < b_hi) dma_rows(b_lo + 1, sAR1, sVR1, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -729,7 +734,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       const float* CK = reinterpret_cast<const float*>(g ? sCK1 : sCK0);
       // The recursion wave touches no global memory inside the loop: its
       // inputs come with the LDS pack and its outputs go to LDS.
-      const float e_t = CK[swz32(kRowE, t)], tot_t = CK[swz32(kRowTot, t)], ks = CK[swz32(kRowKs, t)];
+      const int tri = t * (t + 1) / 2;   // row t of the pack's triangle
+      const float e_t = CK[kPackE + t], ks = CK[kPackKs + t];
       const float* hr = sH[g];
       // v_t^T S_b alpha_t, the one-block lag repaired with the cross kernel.
       float acc = (hr[t] + hr[kLb + t]) + (hr[2 * kLb + t] + hr[3 * kLb + t]);
@@ -740,10 +746,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         // depends on the block-start norm linearly, with factor sigma_end^2).
         const float* np = sNrm[g ^ 1];
         N = fmaf(se * se, ((np[0] + np[1]) + (np[2] + np[3])) - Nstart, N);
-        // This wave's own copies of Kx, issued one block ago (the compiler
-        // does not order these reads after them by itself).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const float* KX = reinterpret_cast<const float*>(sKX);
+        const float* KX = reinterpret_cast<const float*>(g ? sKX1 : sKX0);
         const float* wprev = sW[g ^ 1];
         float cx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -760,23 +763,19 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         }
         acc = fmaf(se, acc, (cx[0] + cx[1]) + (cx[2] + cx[3]));
       }
-      // The next block's Kx into the buffer just read (its reads complete first).
-      if (b + 1 < b_hi) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        dma_kx(b + 1, ln);
-      }
       Nstart = N;
       sNb[g][t] = nvec;
-      const float own = CK[swz32(t, t)];   // sum_{s<t} K(t,s)
+      const float own = CK[tri + t];   // sum_{s<t} K(t,s)
       // Cap recursion by rounds: each round assumes no fire for the rest of
       // the block, and the first token whose norm would exceed the cap ends it.
+      const uint64_t valid = tcount >= 64 ? ~0ull : ((1ull << tcount) - 1ull);
       float base = 0.f, lprev_t = 0.f, l_t = 0.f, L = 0.f;
       int s0 = 0;
       while (s0 < tcount) {
         const bool act = t >= s0 && t < tcount;
         const float gg = acc + (own - base);
         const float npre = N + wave_incl_scan(act ? fmaf(2.f, gg, e_t) : 0.f, t);
-        const uint64_t over = __ballot(act && cap_on && npre > cap2);
+        const uint64_t over = cap_on ? (__ballot(npre > cap2) & valid & (~0ull << s0)) : 0ull;
         if (over == 0) {
           N = readlane_f(npre, tcount - 1);
           break;
@@ -785,7 +784,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         const float nf = readlane_f(npre, f);
         const float c = cap * __builtin_amdgcn_rsqf(nf);
         const float lg = __builtin_amdgcn_logf(c);   // log2
-        const float cf = (f + 1 < kLb) ? CK[swz32(t, f + 1)] : tot_t;   // sum_{s<=f} K(t,s)
+        // sum_{s<=f} K(t,s), needed on lanes t > f only (others read their own entry)
+        const float cf = CK[tri + min(f + 1, t)];
         acc = (t > f) ? c * (acc + (cf - base)) : acc;
         lprev_t += (t > f) ? lg : 0.f;
         l_t += (t >= f) ? lg : 0.f;
@@ -802,10 +802,10 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       sLog[g][2 * t + 1] = l_t;
       nvec += ks;
     } else {
-      // Next block's pack into the other parity (the recursion wave finished
-      // with it one block ago); rows of block b+2 into the generation whose
-      // last reader was the previous block.
-      if (b + 1 < b_hi) dma_pack(b + 1, g ? sCK0 : sCK1, ln);
+      // Next block's pack and Kx into the other parity (the recursion wave
+      // finished with it one block ago); rows of block b+2 into the
+      // generation whose last reader was the previous block.
+      if (b + 1 < b_hi) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
       if (b + 2 < b_hi) dma_rows(b + 2, rows_ar(RGp2), rows_vr(RGp2), ln);
       if (b > b_lo) {
         // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.

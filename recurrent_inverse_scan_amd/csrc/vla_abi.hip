@@ -192,7 +192,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * 64 * 4);
     cl.nblk = (p->T + 63) / 64;
     const size_t nb = cl.nblk, T = static_cast<size_t>(p->T);
-    cl.off_K = off; off = align_up(off + C * nb * 68 * 64 * 4);
+    cl.off_K = off; off = align_up(off + C * nb * 2304 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
     // Regrouped update operands: fp32 storage only (bf16 reads its LDS rows).
     const size_t nreg = p->in_dtype == VLA_BF16 ? 0 : C * nb * d2;

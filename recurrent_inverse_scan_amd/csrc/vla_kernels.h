@@ -69,8 +69,9 @@ struct StatePlan {
   int bf16;              // storage of q, k, v, o
   const void* v;
   const float* alpha;    // [chains][T][64] alpha_hat from the inverse pass
-  float* Kmat;           // [chains][nblk][68][64] row prefix sums over s<j of K(t,s) = (v_t.v_s)(alpha_t.alpha_s),
-                         // then rows K(t,t), sum_s K(t,s), sum_t k_t and one padding row
+  float* Kmat;           // [chains][nblk][2304] lower triangle of the row prefix sums over s<j of
+                         // K(t,s) = (v_t.v_s)(alpha_t.alpha_s) (row t's j = 0..t at t(t+1)/2 + j), then
+                         // K(t,t), sum_s K(t,s), sum_t k_t (64 each) and padding
   float* Kcross;         // [chains][nblk][64][64] (v_t.v_s)(alpha_t.alpha_s), s in the previous block
   void* VT;              // [chains][nblk][512][8] v regrouped as matrix-core operands (storage dtype)
   float* AT;             // [chains][nblk][512][8] alpha_hat regrouped the same way
