@@ -76,9 +76,10 @@ typedef struct {
   int32_t validate;      /* nonzero: synchronous NaN/Inf pre-check of the inputs */
   int32_t chunk_len;     /* tokens per chunk of the chunked schedule; 0 = library picks */
   int32_t segment_blocks; /* chunked schedule: blocks of 64 tokens per state-pass
-                             segment, rounded up to even and to at most 16
-                             segments (the chain kernel runs one segment while a
-                             side stream preps the next and reads out the last);
+                             segment, rounded up to a multiple of 4 and to at
+                             most 16 segments, the first one half as long (the
+                             chain kernel runs one segment while a side stream
+                             preps the next and reads out the last);
                              0 = library picks (256), < 0 = one segment */
 } vla_scan_params_t;
 

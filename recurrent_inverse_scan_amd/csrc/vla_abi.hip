@@ -81,13 +81,14 @@ SideStream* side_stream(hipError_t* err) {
 }
 
 // Blocks per chain-kernel segment for nblk blocks of 64 tokens: seg_blocks
-// (default 256; < 0: all in one) rounded up to even, and large enough for at
-// most kMaxChainSegs segments (a launch per segment costs a few microseconds).
+// (default 256; < 0: all in one) rounded up to a multiple of 4, and large
+// enough for at most kMaxChainSegs segments (a launch per segment costs a few
+// microseconds).  The first segment takes half of that (an even count).
 int chain_segment_len(int nblk, int seg_blocks) {
-  if (seg_blocks < 0 || seg_blocks > nblk) seg_blocks = nblk;
+  if (seg_blocks < 0 || seg_blocks > 2 * nblk) seg_blocks = 2 * nblk;
   if (seg_blocks == 0) seg_blocks = 256;
-  seg_blocks = std::max(seg_blocks, (nblk + kMaxChainSegs - 1) / kMaxChainSegs);
-  return (seg_blocks + 1) & ~1;
+  seg_blocks = std::max(seg_blocks, (nblk + kMaxChainSegs - 2) / (kMaxChainSegs - 1));
+  return (seg_blocks + 3) & ~3;
 }
 
 vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -424,9 +425,12 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // last readout stay outside the chain kernel's time.  The side launches
   // between are held to a part of the chip (SideStream::side_wg).
   const int nblk = cl.nblk;
+  // The first segment is half a segment, so that its prep (on the full chip,
+  // before the chain kernel can start) is short; the last is what remains.
   const int seg_len = chain_segment_len(nblk, p->segment_blocks);
-  const int nseg = (nblk + seg_len - 1) / seg_len;   // none empty
-  auto seg_lo = [&](int sidx) { return std::min(nblk, sidx * seg_len); };
+  const int seg_first = seg_len / 2;   // even
+  const int nseg = nblk <= seg_first ? 1 : 1 + (nblk - seg_first + seg_len - 1) / seg_len;   // none empty
+  auto seg_lo = [&](int sidx) { return sidx == 0 ? 0 : std::min(nblk, seg_first + (sidx - 1) * seg_len); };
   auto next_timing = [&](hipEvent_t* ev0, hipEvent_t* ev1) {
     Timing& tm = timing();
     std::lock_guard<std::mutex> lock(tm.mu);

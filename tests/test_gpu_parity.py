@@ -344,8 +344,8 @@ def test_chunked_agrees_with_sequential():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("L,period,seg", [(64, 128, 2), (64, 128, 6), (64, 128, 10), (128, 128, 3), (96, 192, 5)])
 def test_chunked_segments_match_oracle(dtype, L, period, seg):
-    """The per-chain pass cut into segments (an even number of blocks: seg
-    rounds up to 2, 6, 10, 4 and 6 blocks here; the last segment ragged and
+    """The per-chain pass cut into segments (seg rounds up to 4, 8, 12, 4 and
+    8 blocks here, the first segment half of that, the last one ragged, and
     boundaries inside chunks for L = 96 and 128), the next segment's prep and
     the last one's readout on the side stream: every segment boundary carries
     S, n and the cap counters; outputs match the oracle."""
@@ -381,7 +381,7 @@ def test_timing_hook_records_the_chain_kernel():
     timing_enable(True)
     try:
         for _ in range(2):
-            _gpu(x, cfg, schedule="chunked", segment_blocks=4)   # 10 blocks: segments of 4, 4, 2
+            _gpu(x, cfg, schedule="chunked", segment_blocks=4)   # 10 blocks: segments of 2, 4, 4
         ms = timing_collect()
     finally:
         timing_enable(False)
