@@ -156,22 +156,26 @@ vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, do
 // ---- (N, D) chain ---------------------------------------------------------
 // Between periods p and p+1: D += Gtot_p N, then the nudge N += eps D.  Both
 // steps act on each column of (N, D) separately, so a chain runs as
-// kNdSplit independent workgroups, one per block of 64/kNdSplit columns.
-// Thread t owns rows 4*(t/16).. of column t%16 of the block; the period's
-// Gram total is staged in LDS (transposed) and the next one is loaded while
-// the current product runs.
-constexpr int kNdSplit = 4;
-constexpr int kNdCols = kD / kNdSplit;   // 16
+// kNdSplit independent workgroups, one per block of 64/kNdSplit = 4 columns.
+// The four waves of a workgroup each take a quarter of the product's inner
+// dimension (thread (q, rb, c): rows 4 rb.. of column c, inner indices
+// 16 q..); the waves' partial sums meet in LDS, where the first wave, which
+// owns (N, D), adds them.  The period's Gram total is staged in LDS
+// (transposed) and the next one is loaded while the current product runs.
+constexpr int kNdSplit = 16;
+constexpr int kNdCols = kD / kNdSplit;   // 4
 
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
                        int nperiods, double eps) {
-  __shared__ double sG[kD * kD];        // sG[m*kD + i] = Gtot[i][m]
-  __shared__ double sN[kD * kNdCols];   // sN[m*kNdCols + c] = N[m][c0 + c]
+  __shared__ double sG[kD * kD];            // sG[m*kD + i] = Gtot[i][m]
+  __shared__ double sN[kD * kNdCols];       // sN[m*kNdCols + c] = N[m][c0 + c]
+  __shared__ double sP[4][kD * kNdCols];    // partial products of each wave
   const int64_t chain = blockIdx.x / kNdSplit;
   const int c0 = (blockIdx.x % kNdSplit) * kNdCols;
-  const int t = threadIdx.x, rb = t >> 4, cc = t & 15;
+  const int t = threadIdx.x, q = t >> 6, rb = (t & 63) >> 2, cc = t & 3;
   const int col = c0 + cc;
+  const bool owner = q == 0;   // wave-uniform
   double N[4], Dm[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -187,8 +191,9 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
       nd[kD * kD + (4 * rb + i) * kD + col] = Dm[i];
     }
   };
-  // 16 of the 64x64 total per thread: rows 4*(t/16).., columns 4*(t%16)..;
-  // two register sets, so each total is loaded two periods ahead.
+  // Staging of the 64x64 total: thread t loads rows 4*(t/16).., columns
+  // 4*(t%16)..; two register sets, so each total is loaded two periods ahead.
+  const int sr = t >> 4, sc = t & 15;
   double ga[16], gb[16];
   auto load_g = [&](double (&g)[16], int p) {
     if (p + 1 >= nperiods) return;   // the last period's total is not needed
@@ -196,28 +201,43 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) g[4 * i + j] = gt[(4 * rb + i) * kD + 4 * cc + j];
+      for (int j = 0; j < 4; ++j) g[4 * i + j] = gt[(4 * sr + i) * kD + 4 * sc + j];
   };
   auto advance = [&](double (&g)[16], int p) {
-    __syncthreads();   // the previous product is done with sG and sN
+    __syncthreads();   // the previous step is done with sG, sN and sP
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sG[(4 * cc + j) * kD + 4 * rb + i] = g[4 * i + j];
-      sN[(4 * rb + i) * kNdCols + cc] = N[i];
+      for (int j = 0; j < 4; ++j) sG[(4 * sc + j) * kD + 4 * sr + i] = g[4 * i + j];
+    if (owner) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sN[(4 * rb + i) * kNdCols + cc] = N[i];
     }
     __syncthreads();
     load_g(g, p + 2);
-    for (int m = 0; m < kD; ++m) {
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int m = 16 * q; m < 16 * q + 16; ++m) {
       const double nm = sN[m * kNdCols + cc];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Dm[i] = fma(sG[m * kD + 4 * rb + i], nm, Dm[i]);
+      for (int i = 0; i < 4; ++i) part[i] = fma(sG[m * kD + 4 * rb + i], nm, part[i]);
     }
+    if (!owner) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) N[i] = fma(eps, Dm[i], N[i]);
-    store_nd(p + 1);
+      for (int i = 0; i < 4; ++i) sP[q][(4 * rb + i) * kNdCols + cc] = part[i];
+    }
+    __syncthreads();
+    if (owner) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (4 * rb + i) * kNdCols + cc;
+        Dm[i] += (part[i] + sP[1][e]) + (sP[2][e] + sP[3][e]);
+        N[i] = fma(eps, Dm[i], N[i]);
+      }
+      store_nd(p + 1);
+    }
   };
-  store_nd(0);
+  if (owner) store_nd(0);
   load_g(ga, 0);
   load_g(gb, 1);
   for (int p = 0; p + 1 < nperiods; p += 2) {
