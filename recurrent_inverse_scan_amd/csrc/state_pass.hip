@@ -597,8 +597,8 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   // reader passed the previous barrier.  Each product wave waits for its own
   // copies before the block's closing barrier (the barrier alone does not
   // wait for them), so what one wave copies is complete for every wave after
-  // that barrier.  The recursion wave touches no global memory inside the
-  // loop.
+  // that barrier.  The recursion wave copies the pack and Kx, which only it
+  // reads, one block ahead and waits for them itself.
   // The v and alpha_hat rows of block j arrive during block j-2, give the
   // bilinear terms in block j-1 and, with bf16 storage, the update's
   // operands in block j+1: four generations.  With fp32 storage the update's
@@ -616,8 +616,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   __shared__ float sW[2][kLb];                                  // update weights sigma_end/sigma_{s-1}
   __shared__ float sSig[2];                                     // sigma_end
   __shared__ float sNrm[2][4];                                  // |S_b|^2 per product wave
-  __shared__ float sLog[2][2 * kLb];                            // per-token log2 scales
-  __shared__ float sNb[2][kD];                                  // n at the block start
   __shared__ float sRed[8];
   auto rows_ar = [&](int r) -> float4* { return r == 0 ? sAR0 : (r == 1 ? sAR1 : (r == 2 ? sAR2 : sAR3)); };
   auto rows_vr = [&](int r) -> float4* { return r == 0 ? sVR0 : (r == 1 ? sVR1 : (r == 2 ? sVR2 : sVR3)); };
@@ -658,22 +656,22 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       for (int i = 0; i < 4; ++i) dma_piece(r, reinterpret_cast<char*>(vr), m + 4 * i, vo32);
     }
   };
-  auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane) {
+  // The pack and Kx of block j: pieces m, m+4, ... when a product wave calls
+  // it (m = 0..3, the prologue), every piece when the recursion wave does
+  // (all = true).
+  auto dma_kernels = [&](int j, float4* ck, float4* kx, int lane, auto all) {
+    constexpr bool kAll = decltype(all)::value;
+    const int p0 = kAll ? 0 : m, dp = kAll ? 1 : 4;
     const auto r = make_rsrc(pl.Kmat + (blk0 + j) * kPackFloats, kPackFloats * 4);
 #pragma unroll
-    for (int p = m; p < kPackPieces; p += 4) dma_piece(r, reinterpret_cast<char*>(ck), p, 16 * lane);
-    const int vo32 = (lane >> 4) * 256 + (((lane & 15) ^ (4 * m + (lane >> 4))) << 4);
-    if (j > b_lo) dma_mat(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4, kx, vo32);
-  };
-
-  // The recursion wave's per-block outputs, written from LDS by a product wave.
-  auto store_block_outputs = [&](int j, const float* lg, const float* nb, int lane) {
-    const int tc = min(kLb, pl.T - j * kLb);
-    const int64_t r0 = chain * pl.T + j * kLb;
-    const auto rw = make_rsrc(pl.wsig + 2 * r0, 2 * tc * 4);
-    buf_store_f32(rw, 4 * lane, lg[lane]);
-    buf_store_f32(rw, 4 * (lane + 64), lg[lane + 64]);
-    pl.nblock[(blk0 + j) * kD + lane] = nb[lane];
+    for (int p = p0; p < kPackPieces; p += dp) dma_piece(r, reinterpret_cast<char*>(ck), p, 16 * lane);
+    if (j > b_lo) {
+      const auto rx = make_rsrc(pl.Kcross + (blk0 + j) * kLb * kLb, kLb * kLb * 4);
+#pragma unroll
+      for (int p = p0; p < 16; p += dp)
+        dma_piece(rx, reinterpret_cast<char*>(kx), p,
+                  (lane >> 4) * 256 + (((lane & 15) ^ ((4 * p + (lane >> 4)) & 15)) << 4));
+    }
   };
 
   f32x16 X = zero16();
@@ -686,10 +684,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 
   // ---- prologue: continue from S and n at block b_lo -------------------------
   if (rwave) {
-    // The recursion wave is the kernel's critical path when the cap binds; it
-    // shares a SIMD with one product wave, whose long VALU runs would
-    // otherwise delay it.
-    __builtin_amdgcn_s_setprio(3);
     nvec = sg.n_in[chain * sg.n_in_stride + lane];
     if (b_lo > 0) {
       fires = sg.counters[chain * 2];
@@ -705,7 +699,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     }
     part = wave_sum(part);
     if (lane == 0) sRed[m] = part;
-    dma_kernels(b_lo, sCK0, sKX0, lane);
+    dma_kernels(b_lo, sCK0, sKX0, lane, std::false_type{});
     dma_rows(b_lo, sAR0, sVR0, lane);
     if (b_lo + 1 < b_hi) dma_rows(b_lo + 1, sAR1, sVR1, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -731,9 +725,13 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     asm volatile("" : "+v"(ln));
     if (rwave) {
       const int t = ln;
+      // The product waves carry the longer share of a block, so this wave
+      // also copies the next block's pack and Kx (only it reads them) and
+      // stores its own per-block outputs.  Its copies for this block were
+      // issued one block ago; wait for them before issuing the next ones.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (b + 1 < b_hi) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln, std::true_type{});
       const float* CK = reinterpret_cast<const float*>(g ? sCK1 : sCK0);
-      // The recursion wave touches no global memory inside the loop: its
-      // inputs come with the LDS pack and its outputs go to LDS.
       const int tri = t * (t + 1) / 2;   // row t of the pack's triangle
       const float e_t = CK[kPackE + t], ks = CK[kPackKs + t];
       const float* hr = sH[g];
@@ -764,7 +762,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         acc = fmaf(se, acc, (cx[0] + cx[1]) + (cx[2] + cx[3]));
       }
       Nstart = N;
-      sNb[g][t] = nvec;
+      const float nstart = nvec;   // n at the block start
       const float own = CK[tri + t];   // sum_{s<t} K(t,s)
       // Cap recursion by rounds: each round assumes no fire for the rest of
       // the block, and the first token whose norm would exceed the cap ends it.
@@ -798,14 +796,17 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       }
       sW[g][t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
       if (t == 0) sSig[g] = exp2f(L);
-      sLog[g][2 * t] = lprev_t;
-      sLog[g][2 * t + 1] = l_t;
+      {
+        const int64_t r0 = chain * pl.T + tb;
+        const auto rw = make_rsrc(pl.wsig + 2 * r0, 2 * tcount * 4);
+        buf_store_f32(rw, 8 * t, lprev_t);
+        buf_store_f32(rw, 8 * t + 4, l_t);
+        pl.nblock[(blk0 + b) * kD + t] = nstart;
+      }
       nvec += ks;
     } else {
-      // Next block's pack and Kx into the other parity (the recursion wave
-      // finished with it one block ago); rows of block b+2 into the
-      // generation whose last reader was the previous block.
-      if (b + 1 < b_hi) dma_kernels(b + 1, g ? sCK0 : sCK1, g ? sKX0 : sKX1, ln);
+      // Rows of block b+2 into the generation whose last reader was the
+      // previous block.
       if (b + 2 < b_hi) dma_rows(b + 2, rows_ar(RGp2), rows_vr(RGp2), ln);
       if (b > b_lo) {
         // S_b = sigma_end(b-1) S_{b-1} + V^T diag(w) A_hat over block b-1.
@@ -814,7 +815,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
                           uoff, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
         else
           rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
-        if (m == 0) store_block_outputs(b - 1, sLog[g ^ 1], sNb[g ^ 1], ln);
       }
       if constexpr (!kBf) fr.load(pl, blk0 + b, ti, tj, ln);   // block b's, for the next update
       {
@@ -851,7 +851,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   // ---- epilogue: the segment's last block update ----------------------------
   if (!rwave) {
     const int g = (b_hi - 1) & 1;
-    if (m == 0) store_block_outputs(b_hi - 1, sLog[g], sNb[g], lane);
     if constexpr (kBf) {
       const int r = (b_hi - 1 - b_lo) % kRowGens;
       rank_update_lds(X, reinterpret_cast<const char*>(rows_vr(r)), reinterpret_cast<const char*>(rows_ar(r)), uoff,
