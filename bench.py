@@ -164,7 +164,7 @@ def main(argv=None) -> int:
     cap_on = cfg.s_cap is not None and cfg.s_cap > 0
     chain_flops = chain_flops_per_token_head(d, cap_on) * tok_heads
     if chain_ms:
-        launch_ms = chain_ms / chain_launches   # the segments are of equal length on this workload
+        launch_ms = chain_ms / chain_launches   # mean launch: the segments differ in length
         launch_flops = chain_flops / chain_launches
         roofline = {"bound": "alu", "achieved": launch_flops / (launch_ms * 1e-3) / 1e12,
                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
