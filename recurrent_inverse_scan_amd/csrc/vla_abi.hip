@@ -414,9 +414,13 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // of them (a segment's) it takes nearly as long, so it is not pipelined
   // with the chain kernel below.
   if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
-  if ((e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
-                                           static_cast<int>(chains), stream)) != hipSuccess)
-    return hip_fail(e, "chunked inverse launch");
+  if (bf16 && p->r == 1)
+    e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
+                               static_cast<int>(chains), stream);
+  else
+    e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
+                                        static_cast<int>(chains), stream);
+  if (e != hipSuccess) return hip_fail(e, "chunked inverse launch");
 
   // State pass: prep, the chain kernel, readout.  The sequence is cut into
   // segments (even block counts): the chain kernel runs them one after
