@@ -40,7 +40,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3   # 256 CU x 4 SIMD x 16 lanes x 2 (dual fp32) x
 HBM_PEAK_GBS = 8000.0
 
 
-CHAIN_SOURCES = ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_seq.h")
+CHAIN_SOURCES = ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_chain_long_traffic.md")
 
 

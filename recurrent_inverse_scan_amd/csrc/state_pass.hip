@@ -34,13 +34,12 @@
 
 #include "vla_common.h"
 #include "vla_kernels.h"
+#include "vla_mfma.h"
 #include "vla_seq.h"
 
 namespace vla {
 
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 64;     // head dimension
 constexpr int kLb = 64;    // tokens per block
@@ -58,16 +57,9 @@ constexpr int kPackFloats = 2304;
 constexpr int kPackPieces = kPackFloats / 256;   // 1 KiB pieces
 static_assert(kPackKs + kLb <= kPackFloats, "pack layout");
 
-__device__ __forceinline__ f32x16 zero16() {
-  return f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-}
-
 __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
-
-// Row (within the tile) held by accumulator slot s of a lane in half h.
-__device__ __forceinline__ int acc_row(int s, int h) { return 8 * (s / 4) + 4 * h + (s % 4); }
 
 // acc[m][n] += sum_k A[m][k] B[n][k]; A and B point at the tile's first row in
 // LDS (row stride kLd), K = 64.  Lane half h covers k = 32h .. 32h+31.
@@ -119,69 +111,8 @@ __device__ __forceinline__ void mma_rc(f32x16& acc, const float* A, const float*
   }
 }
 
-// ---- bf16 matrix-core products at fp32-grade accuracy ------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// ---- bf16 operands and buffer-to-LDS copies ----------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// x = t1 + t2 + t3 exactly, each term a bf16: t1 is x with the low 16 bits
-// of its encoding cleared, r = x - t1 (exact: the low 16 significand bits),
-// t2 is r cleared the same way and t3 = r - t2 holds at most 8 significant
-// bits, so it is a bf16 as well.  Each term is the upper half of an fp32
-// encoding; byte permutes pack two of them per word.
-struct Split3 {
-  bf16x8 t1, t2, t3;
-};
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t lo, uint32_t hi) {
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-}
-__device__ __forceinline__ Split3 split3(const float (&x)[8]) {
-#pragma clang fp contract(off)   // x is what the caller rounded, not an exact product
-  uint32_t a[8], r[8], c[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = __float_as_uint(x[e]);
-    const float rf = x[e] - __uint_as_float(a[e] & 0xffff0000u);
-    r[e] = __float_as_uint(rf);
-    c[e] = __float_as_uint(rf - __uint_as_float(r[e] & 0xffff0000u));
-  }
-  Split3 s;
-  s.t1 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(a[0], a[1]), pack_hi16(a[2], a[3]), pack_hi16(a[4], a[5]),
-                                               pack_hi16(a[6], a[7])));
-  s.t2 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(r[0], r[1]), pack_hi16(r[2], r[3]), pack_hi16(r[4], r[5]),
-                                               pack_hi16(r[6], r[7])));
-  s.t3 = __builtin_bit_cast(bf16x8, make_uint4(pack_hi16(c[0], c[1]), pack_hi16(c[2], c[3]), pack_hi16(c[4], c[5]),
-                                               pack_hi16(c[6], c[7])));
-  return s;
-}
-
-// acc += A B with A and B given as three-term splits (terms of order >= 3 dropped).
-__device__ __forceinline__ f32x16 mma_split(const Split3& a, const Split3& b, f32x16 acc) {
-  acc = mfma_bf16(a.t2, b.t2, acc);
-  acc = mfma_bf16(a.t3, b.t1, acc);
-  acc = mfma_bf16(a.t1, b.t3, acc);
-  acc = mfma_bf16(a.t2, b.t1, acc);
-  acc = mfma_bf16(a.t1, b.t2, acc);
-  return mfma_bf16(a.t1, b.t1, acc);
-}
-// acc += A B with A exact in bf16.
-__device__ __forceinline__ f32x16 mma_split(bf16x8 a, const Split3& b, f32x16 acc) {
-  acc = mfma_bf16(a, b.t3, acc);
-  acc = mfma_bf16(a, b.t2, acc);
-  return mfma_bf16(a, b.t1, acc);
-}
-// acc += A B with B exact in bf16.
-__device__ __forceinline__ f32x16 mma_split(const Split3& a, bf16x8 b, f32x16 acc) {
-  acc = mfma_bf16(a.t3, b, acc);
-  acc = mfma_bf16(a.t2, b, acc);
-  return mfma_bf16(a.t1, b, acc);
-}
-
-// acc += A B with both operands exact in bf16.
-__device__ __forceinline__ f32x16 mma_split(bf16x8 a, bf16x8 b, f32x16 acc) { return mfma_bf16(a, b, acc); }
 
 // Operand of 8 consecutive values at p: exact bf16 for bf16 storage, a
 // three-term split for fp32.

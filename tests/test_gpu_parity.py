@@ -265,6 +265,11 @@ CHUNKED = [
     ("f32-rank3", dict(B=1, H=2, T=300, r=3, in_dtype="f32", nudge_period=32, s_cap=None), 32),
     ("bf16-rank4-nonudge", dict(B=1, H=2, T=333, r=4, in_dtype="bf16", nudge_period=0, s_cap=None), 64),
     ("f32-cap-binding", dict(B=1, H=2, T=513, in_dtype="f32", nudge_period=0, s_cap=3.0), 128),
+    # bf16 with one direction per token takes the blocked (32-token) inverse
+    # pass: a chunk of 48 ends in a half block, and the last chunk is ragged.
+    ("bf16-blocked-half-block", dict(B=1, H=2, T=500, in_dtype="bf16", nudge_period=96, s_cap=30.0), 48),
+    # Long chunks with the nudge on every other chunk's last token.
+    ("bf16-blocked-long-chunks", dict(B=1, H=2, T=2100, in_dtype="bf16", nudge_period=1024, s_cap=None), 512),
 ]
 
 
@@ -280,8 +285,10 @@ def test_chunked_matches_oracle(name, over, L):
         assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
 
 
-def test_chunked_with_initial_state_and_offset():
-    cfg = CONFIGS["base"].with_(name="chunked-state", B=1, H=2, T=640, nudge_period=128, s_cap=50.0)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_with_initial_state_and_offset(dtype):
+    cfg = CONFIGS["base"].with_(name=f"chunked-state-{dtype}", B=1, H=2, T=640, in_dtype=dtype, nudge_period=128,
+                                s_cap=50.0)
     x = case(cfg, seed=12)
     g = torch.Generator().manual_seed(12)
     X = torch.randn(2, cfg.d, cfg.d, generator=g) / cfg.d ** 0.5
@@ -295,8 +302,10 @@ def test_chunked_with_initial_state_and_offset():
     _check(cfg, out, ref)
 
 
-def test_chunked_in_place_state_carry():
-    cfg = CONFIGS["base"].with_(name="chunked-inplace", B=1, H=2, T=512, nudge_period=64, s_cap=None)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_in_place_state_carry(dtype):
+    cfg = CONFIGS["base"].with_(name=f"chunked-inplace-{dtype}", B=1, H=2, T=512, in_dtype=dtype, nudge_period=64,
+                                s_cap=None)
     x = case(cfg, seed=13)
     q, k, v, u = (x[n].to(DEV) for n in ("q", "k", "v", "u"))
     A = torch.eye(cfg.d, device=DEV).expand(1, 2, cfg.d, cfg.d).contiguous()
@@ -307,15 +316,17 @@ def test_chunked_in_place_state_carry():
     scan_forward(q, k, v, u, A, S, n, nudge_period=64, schedule="chunked", chunk_len=64, out=(o, A, S, n, st))
     torch.cuda.synchronize()
     ref = run_oracle(x, cfg)
-    assert rel_err(o.reshape(2, cfg.T, cfg.d), ref["o"]) <= 2e-3
+    assert rel_err(o.reshape(2, cfg.T, cfg.d), ref["o"]) <= TOL[cfg.in_dtype]
     assert rel_err(A.reshape(2, cfg.d, cfg.d), ref["A"], axes=(-2, -1)) <= 2e-3
     assert rel_err(S.reshape(2, cfg.d, cfg.d), ref["S"], axes=(-2, -1)) <= 2e-3
 
 
-def test_chunked_falls_back_when_the_guard_fires():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_falls_back_when_the_guard_fires(dtype):
     """A Householder start makes delta = 0 in the first chunk: the chain is
     recomputed sequentially inside the same call and still matches."""
-    cfg = CONFIGS["base"].with_(name="chunked-guard", B=1, H=2, T=256, nudge_period=0, s_cap=None)
+    cfg = CONFIGS["base"].with_(name=f"chunked-guard-{dtype}", B=1, H=2, T=256, in_dtype=dtype, nudge_period=0,
+                                s_cap=None)
     x = case(cfg, seed=14)
     u = x["u"].clone()
     e = torch.zeros(cfg.d)
