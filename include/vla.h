@@ -77,10 +77,12 @@ typedef struct {
   int32_t chunk_len;     /* tokens per chunk of the chunked schedule; 0 = library picks */
   int32_t segment_blocks; /* chunked schedule: blocks of 64 tokens per state-pass
                              segment, rounded up to a multiple of 4 and to at
-                             most 16 segments, the first one half as long (the
-                             chain kernel runs one segment while a side stream
-                             preps the next and reads out the last);
-                             0 = library picks (256), < 0 = one segment */
+                             most 16 segments; the first is five eighths as
+                             long and a remainder under half a segment is
+                             shared with the one before (the chain kernel runs
+                             one segment while a side stream preps the next
+                             and reads out the last); 0 = library picks (256),
+                             < 0 = one segment */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,

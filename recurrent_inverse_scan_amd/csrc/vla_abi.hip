@@ -83,12 +83,42 @@ SideStream* side_stream(hipError_t* err) {
 // Blocks per chain-kernel segment for nblk blocks of 64 tokens: seg_blocks
 // (default 256; < 0: all in one) rounded up to a multiple of 4, and large
 // enough for at most kMaxChainSegs segments (a launch per segment costs a few
-// microseconds).  The first segment takes half of that (an even count).
+// microseconds).
 int chain_segment_len(int nblk, int seg_blocks) {
   if (seg_blocks < 0 || seg_blocks > 2 * nblk) seg_blocks = 2 * nblk;
   if (seg_blocks == 0) seg_blocks = 256;
   seg_blocks = std::max(seg_blocks, (nblk + kMaxChainSegs - 2) / (kMaxChainSegs - 1));
   return (seg_blocks + 3) & ~3;
+}
+
+// Segment boundaries bnd[0] = 0 < ... < bnd[n] = nblk of the state pass; returns
+// n.  Segment s's chain kernel runs beside the next segment's prep and the
+// previous one's readout, so neighbours must not be much longer than it:
+// the first segment is five eighths of a segment (its prep runs alone on the
+// chip before the chain kernel, while the second segment's prep runs beside
+// it), and a remainder under half a segment is shared with the segment
+// before it so that the last one stays at least half a segment long (the
+// readout of the one before runs beside it).
+int chain_segments(int nblk, int seg_blocks, int* bnd) {
+  const int len = chain_segment_len(nblk, seg_blocks);
+  const int first = std::max(2, (len * 5 / 8 + 1) & ~1);
+  int n = 0;
+  bnd[n++] = 0;
+  if (nblk <= first) {
+    bnd[n++] = nblk;
+    return n - 1;
+  }
+  bnd[n++] = first;
+  const int rest = nblk - first, full = rest / len, rem = rest % len;
+  const bool share = full >= 1 && rem > 0 && rem < len / 2;
+  for (int i = 0; i < full - (share ? 1 : 0); ++i) bnd[n] = bnd[n - 1] + len, ++n;
+  if (share) {
+    bnd[n] = bnd[n - 1] + len / 2 + rem, ++n;
+    bnd[n] = bnd[n - 1] + len / 2, ++n;
+  } else if (rem > 0) {
+    bnd[n] = bnd[n - 1] + rem, ++n;
+  }
+  return n - 1;
 }
 
 vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -429,12 +459,9 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // last readout stay outside the chain kernel's time.  The side launches
   // between are held to a part of the chip (SideStream::side_wg).
   const int nblk = cl.nblk;
-  // The first segment is half a segment, so that its prep (on the full chip,
-  // before the chain kernel can start) is short; the last is what remains.
-  const int seg_len = chain_segment_len(nblk, p->segment_blocks);
-  const int seg_first = seg_len / 2;   // even
-  const int nseg = nblk <= seg_first ? 1 : 1 + (nblk - seg_first + seg_len - 1) / seg_len;   // none empty
-  auto seg_lo = [&](int sidx) { return sidx == 0 ? 0 : std::min(nblk, seg_first + (sidx - 1) * seg_len); };
+  int bnd[kMaxChainSegs + 1];
+  const int nseg = chain_segments(nblk, p->segment_blocks, bnd);
+  auto seg_lo = [&](int sidx) { return bnd[sidx]; };
   auto next_timing = [&](hipEvent_t* ev0, hipEvent_t* ev1) {
     Timing& tm = timing();
     std::lock_guard<std::mutex> lock(tm.mu);
@@ -556,9 +583,10 @@ vla_status_t vla_timing_enable(int32_t enable) {
   if (!enable) return VLA_OK;
   for (int i = 0; i < VLA_TIMING_SLOTS; ++i) {
     hipEvent_t a = nullptr, b = nullptr;
-    hipError_t e = hipEventCreate(&a);
+    // Timing only: no system-scope fence when they are recorded.
+    hipError_t e = hipEventCreateWithFlags(&a, hipEventDisableSystemFence);
     if (e == hipSuccess) {
-      e = hipEventCreate(&b);
+      e = hipEventCreateWithFlags(&b, hipEventDisableSystemFence);
       if (e != hipSuccess) (void)hipEventDestroy(a);
     }
     if (e != hipSuccess) {

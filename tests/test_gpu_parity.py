@@ -356,10 +356,12 @@ def test_chunked_agrees_with_sequential():
 @pytest.mark.parametrize("L,period,seg", [(64, 128, 2), (64, 128, 6), (64, 128, 10), (128, 128, 3), (96, 192, 5)])
 def test_chunked_segments_match_oracle(dtype, L, period, seg):
     """The per-chain pass cut into segments (seg rounds up to 4, 8, 12, 4 and
-    8 blocks here, the first segment half of that, the last one ragged, and
-    boundaries inside chunks for L = 96 and 128), the next segment's prep and
-    the last one's readout on the side stream: every segment boundary carries
-    S, n and the cap counters; outputs match the oracle."""
+    8 blocks here; over the 32 blocks of T = 2000 that gives segments of
+    2 4 4 4 4 4 4 4 2, 6 8 8 6 4 and 8 12 12 blocks: a short first segment,
+    a remainder shared with the segment before, and boundaries inside chunks
+    for L = 96 and 128), the next segment's prep and the last one's readout on
+    the side stream: every segment boundary carries S, n and the cap counters;
+    outputs match the oracle."""
     cfg = CONFIGS["base"].with_(name=f"chunked-L{L}-seg{seg}-{dtype}", B=1, H=3, T=2000, in_dtype=dtype,
                                 nudge_period=period, s_cap=30.0)
     _say(f"case chunked L={L} segments {seg} {dtype}")
