@@ -25,7 +25,8 @@
 // Products with fp32 operands use three-term bf16 splits (fp32-grade); u and
 // k enter exactly.  The LDL^T elimination of I + C, carried along on E =
 // U^T A_b K and on the identity (giving L^{-1} E and L^{-1}), runs in the
-// wave over 32 pivots: the pivot column and row reach every lane through LDS.
+// wave over 32 pivots, two per round trip: pivot columns and rows reach
+// every lane through LDS.
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_mfma.h"
@@ -64,8 +65,8 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
                       const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
                       int32_t* __restrict__ chain_info, int T, int L, int nchunks, int chunk_lo, int chunk_cnt,
                       float eps, int nudge_period, int nudge_phase0) {
-  __shared__ float4 sCol[2][4];   // pivot column: [lane half][16 rows in slot order]
-  __shared__ float4 sRow[kM];     // pivot row of (I + C, E, T) at column t
+  __shared__ float4 sCol[2][2][4];   // pivot columns k, k + 1: [which][lane half][16 rows in slot order]
+  __shared__ float4 sRow[kM][2];     // pivot rows k, k + 1 of (I + C, E, T) at column t
   __shared__ __align__(16) float sDinv[kM];     // 1 / pivot
   __shared__ float4 sTok[2][4][kD];   // the block's u and k operands: [u / k][k step][lane]
 
@@ -183,38 +184,67 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
       tm[s] = dg ? 1.f : 0.f;
     }
     const float hf = static_cast<float>(h);
+    // Two pivots per LDS round trip: the lanes get columns k and k + 1 and
+    // rows k and k + 1 as they stood before pivot k, and apply pivot k to
+    // their copies of column and row k + 1 themselves.
 #pragma unroll
-    for (int k = 0; k < kM; ++k) {
-      const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3);
-      if (c == k) {
+    for (int k = 0; k < kM; k += 2) {
+      const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3);   // pivots k, k + 1: slots sk, sk + 1
+      if (c == k || c == k + 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sCol[h][q] = make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
+        for (int q = 0; q < 4; ++q)
+          sCol[c - k][h][q] = make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
       }
-      if (h == hk) sRow[c] = make_float4(cm[sk], em[sk], tm[sk], 0.f);
+      if (h == hk) {
+        sRow[c][0] = make_float4(cm[sk], em[sk], tm[sk], cm[sk + 1]);
+        sRow[c][1] = make_float4(em[sk + 1], tm[sk + 1], 0.f, 0.f);
+      }
       lds_order();
-      float num[16];
+      float na[16], nb[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = sCol[h][q];
-        num[4 * q] = v.x; num[4 * q + 1] = v.y; num[4 * q + 2] = v.z; num[4 * q + 3] = v.w;
+        const float4 v = sCol[0][h][q], w = sCol[1][h][q];
+        na[4 * q] = v.x; na[4 * q + 1] = v.y; na[4 * q + 2] = v.z; na[4 * q + 3] = v.w;
+        nb[4 * q] = w.x; nb[4 * q + 1] = w.y; nb[4 * q + 2] = w.z; nb[4 * q + 3] = w.w;
       }
-      const float piv = reinterpret_cast<const float*>(sCol[hk])[sk];
-      const float4 rk = sRow[c];
-      float inv = __builtin_amdgcn_rcpf(piv);
-      inv = fmaf(fmaf(-piv, inv, 1.f), inv, inv);
-      guard += fabsf(piv) < eps ? 1 : 0;
+      // M[k][k], M[k+1][k] from column k; M[k][k+1], M[k+1][k+1] from column k + 1.
+      const float2 pa = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sCol[0][hk]) + sk);
+      const float2 pb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sCol[1][hk]) + sk);
+      const float4 r0 = sRow[c][0], r1 = sRow[c][1];
+      float ia = __builtin_amdgcn_rcpf(pa.x);
+      ia = fmaf(fmaf(-pa.x, ia, 1.f), ia, ia);
+      const float a0 = r0.x * ia, a1 = r0.y * ia, a2 = r0.z * ia;
+      // Row k + 1 at column c and pivot k + 1, as pivot k leaves them.
+      const float q0 = fmaf(-pa.y, a0, r0.w), q1 = fmaf(-pa.y, a1, r1.x), q2 = fmaf(-pa.y, a2, r1.y);
+      const float gab = pb.x * ia;
+      const float pk1 = fmaf(-pa.y, gab, pb.y);
+      float ib = __builtin_amdgcn_rcpf(pk1);
+      ib = fmaf(fmaf(-pk1, ib, 1.f), ib, ib);
+      const float b0 = q0 * ib, b1 = q1 * ib, b2 = q2 * ib;
+      guard += (fabsf(pa.x) < eps ? 1 : 0) + (fabsf(pk1) < eps ? 1 : 0);
       asm volatile("" : "+v"(guard));
-      if (lane == 0) sDinv[k] = inv;
+      if (lane == 0) {
+        sDinv[k] = ia;
+        sDinv[k + 1] = ib;
+      }
       lds_order();
-      const float a0 = rk.x * inv, a1 = rk.y * inv, a2 = rk.z * inv;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int base = 8 * (s >> 2) + (s & 3);   // row of slot s is base + 4 h
         if (base + 4 <= k) continue;                // row <= k in both halves
-        const float nv = base > k ? num[s] : num[s] * hf;
-        cm[s] = fmaf(-nv, a0, cm[s]);
-        em[s] = fmaf(-nv, a1, em[s]);
-        tm[s] = fmaf(-nv, a2, tm[s]);
+        // Pivot k on the rows below it.
+        const float xa = base > k ? na[s] : na[s] * hf;
+        cm[s] = fmaf(-xa, a0, cm[s]);
+        em[s] = fmaf(-xa, a1, em[s]);
+        tm[s] = fmaf(-xa, a2, tm[s]);
+        // Pivot k + 1 on the rows below it, with column k + 1 as pivot k left it.
+        if (base + 4 > k + 1) {
+          const float nk = fmaf(-na[s], gab, nb[s]);
+          const float xb = base > k + 1 ? nk : nk * hf;
+          cm[s] = fmaf(-xb, b0, cm[s]);
+          em[s] = fmaf(-xb, b1, em[s]);
+          tm[s] = fmaf(-xb, b2, tm[s]);
+        }
         // Pin the updated values: left alone, the compiler defers these
         // products to the values' next uses and keeps every factor live.
         asm volatile("" : "+v"(cm[s]), "+v"(em[s]), "+v"(tm[s]));
