@@ -43,6 +43,17 @@ reason in the design notes):
   ||S||_F > cap rescales S to exactly cap.  cap None, <= 0 or inf disables it.
 * Readout uses the post-update S_t and n_t: o_t = S_t q_t / (n_t . q_t + den_eps).
 * normalize(x) = x / max(||x||_2, 1e-12).
+
+The residual (delta-rule) update ("Variational Linear Attention: Stable
+Associative Memory for Long-Context Transformers", technical summary 2.3,
+recursive update rule) replaces the coefficient and state steps with:
+
+* k_hat = normalize(k_t), alpha_hat = normalize(A_t k_hat), with A_t taken
+  after the rank-1 updates and the nudge as above;
+* S_t = S_{t-1} + (v_t - S_{t-1} k_hat) alpha_hat^T.
+
+The inverse recurrence, the nudge, the cap and the readout (n accumulates the
+raw feature k_t; o_t = S_t q_t / (n_t . q_t + den_eps)) are unchanged.
 """
 from __future__ import annotations
 
@@ -69,9 +80,22 @@ def _cap_enabled(s_cap) -> bool:
     return s_cap is not None and s_cap > 0 and math.isfinite(s_cap)
 
 
+def _normalize_rows(x):
+    """x / max(||x||_2, 1e-12) along the last axis."""
+    nrm = np.sqrt(np.einsum("ci,ci->c", x, x))
+    return x / np.maximum(nrm, 1e-12)[:, None]
+
+
 def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0,
-                s_cap=None, den_eps=1e-6, t0=0):
+                s_cap=None, den_eps=1e-6, t0=0, update="additive", normalize=True):
     """Run the VLA scan sequentially over tokens, independently per chain.
+
+    ``update`` selects the state step: "additive" (S += v alpha_hat^T with the
+    clamp alpha_hat = alpha / max(||alpha||, 1)) or "residual" (the delta-rule
+    form with unit k_hat and unit alpha_hat).  ``normalize=False`` (residual
+    only) drops both unit normalisations, i.e. alpha = A_t k and
+    S += (v - S k) alpha^T: the recursive-least-squares form, which has a
+    closed form and serves as a check of the residual step.
 
     Shapes: q, k, v are [*batch, T, d]; u is [*batch, T, r, d] (u[..., t, i, :] is
     the i-th penalty direction of token t, applied in index order).  A0 and S0
@@ -87,6 +111,10 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
     batch = q.shape[:-2]
     T, d = q.shape[-2], q.shape[-1]
     r = u.shape[-2]
+    if update not in ("additive", "residual"):
+        raise ValueError(f"unknown update {update!r}")
+    if not normalize and update != "residual":
+        raise ValueError("normalize=False applies to the residual update only")
     if k.shape != q.shape or v.shape != q.shape or u.shape != batch + (T, r, d):
         raise ValueError("shape mismatch among q, k, v, u")
     C = int(np.prod(batch)) if batch else 1
@@ -123,12 +151,21 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
         tau = t0 + t + 1
         if nudge_period > 0 and tau % nudge_period == 0:
             A = A + eps * eye
-        # Optimal coefficient alpha = A_t k_t, clamped to norm <= 1.
-        alpha = np.einsum("cij,cj->ci", A, k[:, t, :])
-        anorm = np.sqrt(np.einsum("ci,ci->c", alpha, alpha))
-        alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]
-        # Additive fast-weight update S += v alpha_hat^T ([value, key] layout).
-        S = S + v[:, t, :, None] * alpha_hat[:, None, :]
+        if update == "additive":
+            # Optimal coefficient alpha = A_t k_t, clamped to norm <= 1.
+            alpha = np.einsum("cij,cj->ci", A, k[:, t, :])
+            anorm = np.sqrt(np.einsum("ci,ci->c", alpha, alpha))
+            alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]
+            # Additive fast-weight update S += v alpha_hat^T ([value, key] layout).
+            S = S + v[:, t, :, None] * alpha_hat[:, None, :]
+        else:
+            # Residual update: gating vector from the unit key, and the
+            # prediction error of the previous state written along it.
+            khat = _normalize_rows(k[:, t, :]) if normalize else k[:, t, :]
+            alpha = np.einsum("cij,cj->ci", A, khat)
+            alpha_hat = _normalize_rows(alpha) if normalize else alpha
+            resid = v[:, t, :] - np.einsum("cij,cj->ci", S, khat)
+            S = S + resid[:, :, None] * alpha_hat[:, None, :]
         # Frobenius renormalisation of S.
         fn = np.sqrt(np.einsum("cij,cij->c", S, S))
         if cap_on:

@@ -53,8 +53,9 @@ MUTANTS = [
     ("readout with the transposed state", 'o[:, t, :] = np.einsum("cij,cj->ci", S, q[:, t, :])',
      'o[:, t, :] = np.einsum("cji,cj->ci", S, q[:, t, :])'),
     ("readout before the update of S",
-     "        S = S + v[:, t, :, None] * alpha_hat[:, None, :]\n",
-     "        o_prev = np.einsum(\"cij,cj->ci\", S, q[:, t, :])\n        S = S + v[:, t, :, None] * alpha_hat[:, None, :]\n"),
+     "            S = S + v[:, t, :, None] * alpha_hat[:, None, :]\n",
+     "            o_prev = np.einsum(\"cij,cj->ci\", S, q[:, t, :])\n"
+     "            S = S + v[:, t, :, None] * alpha_hat[:, None, :]\n"),
     ("alpha from the inverse before the token's updates",
      "        for i in range(r):\n", "        A_prev = A\n        for i in range(r):\n"),
     ("nudge applied after alpha",
@@ -62,6 +63,22 @@ MUTANTS = [
     ("cap applied after the readout",
      "        fn = np.sqrt(np.einsum(\"cij,cij->c\", S, S))\n        if cap_on:",
      "        fn = np.sqrt(np.einsum(\"cij,cij->c\", S, S))\n        if False:"),
+    ("residual with the wrong sign", "resid = v[:, t, :] - np.einsum", "resid = v[:, t, :] + np.einsum"),
+    ("residual predicted from the raw key", 'resid = v[:, t, :] - np.einsum("cij,cj->ci", S, khat)',
+     'resid = v[:, t, :] - np.einsum("cij,cj->ci", S, k[:, t, :])'),
+    ("residual key not normalised", "khat = _normalize_rows(k[:, t, :]) if normalize else k[:, t, :]",
+     "khat = k[:, t, :]"),
+    ("residual gate clamped instead of unit", "alpha_hat = _normalize_rows(alpha) if normalize else alpha",
+     "alpha_hat = alpha / np.maximum(np.sqrt(np.einsum('ci,ci->c', alpha, alpha)), 1.0)[:, None] "
+     "if normalize else alpha"),
+    ("residual written along the key instead of the gate",
+     "S = S + resid[:, :, None] * alpha_hat[:, None, :]", "S = S + resid[:, :, None] * khat[:, None, :]"),
+    ("residual update transposed", "S = S + resid[:, :, None] * alpha_hat[:, None, :]",
+     "S = S + resid[:, None, :] * alpha_hat[:, :, None]"),
+    ("residual gate from the inverse before the token's updates",
+     "        for i in range(r):\n", "        A_prev = A\n        for i in range(r):\n"),
+    ("residual written from the initial state", "resid = v[:, t, :] - np.einsum(\"cij,cj->ci\", S, khat)",
+     "resid = v[:, t, :] - np.einsum(\"cij,cj->ci\", S0c, khat)"),
     ("projection applies W^T", "x = rows @ W[i].T", "x = rows @ W[i]"),
     ("projection not normalised", "out[:, i, :] = x / np.maximum(nrm, 1e-12)[:, None]",
      "out[:, i, :] = x"),
@@ -71,9 +88,9 @@ _EXTRA = {
     "alpha from the inverse before the token's updates": [
         ('alpha = np.einsum("cij,cj->ci", A, k[:, t, :])', 'alpha = np.einsum("cij,cj->ci", A_prev, k[:, t, :])')],
     "nudge applied after alpha": [
-        ("        alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]\n",
-         "        alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]\n"
-         "        if nudge_period > 0 and tau % nudge_period == 0:\n            A = A + eps * eye\n")],
+        ("            alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]\n",
+         "            alpha_hat = alpha / np.maximum(anorm, 1.0)[:, None]\n"
+         "            if nudge_period > 0 and tau % nudge_period == 0:\n                A = A + eps * eye\n")],
     "cap applied after the readout": [
         ("        o[:, t, :] = np.einsum(\"cij,cj->ci\", S, q[:, t, :]) / den[:, None]\n",
          "        o[:, t, :] = np.einsum(\"cij,cj->ci\", S, q[:, t, :]) / den[:, None]\n"
@@ -84,6 +101,10 @@ _EXTRA = {
          "            first_cap = np.where(over & (first_cap < 0), t, first_cap)\n"
          "            capf += over\n"
          "            fn = np.where(over, s_cap, fn)\n")],
+    "residual gate from the inverse before the token's updates": [
+        ('alpha = np.einsum("cij,cj->ci", A, khat)', 'alpha = np.einsum("cij,cj->ci", A_prev, khat)')],
+    "residual written from the initial state": [
+        ("    guard = np.zeros(C, dtype=np.int64)\n", "    S0c = S.copy()\n    guard = np.zeros(C, dtype=np.int64)\n")],
     "readout before the update of S": [
         ('o[:, t, :] = np.einsum("cij,cj->ci", S, q[:, t, :]) / den[:, None]',
          'o[:, t, :] = o_prev / den[:, None]')],
@@ -106,6 +127,10 @@ PINS = [
     ("test_linearity_in_values_and_initial_state", {}),
     ("test_resume_equivalence", {}),
     ("test_project_u_closed_forms", {}),
+    ("test_residual_unnormalised_is_recursive_least_squares", {}),
+    ("test_residual_orthogonal_keys_closed_form", {"with_u": True}),
+    ("test_residual_first_step_gate_is_unit_and_nudged", {}),
+    ("test_residual_invariants_linearity_resume_cap", {}),
 ]
 
 

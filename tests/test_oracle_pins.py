@@ -431,3 +431,155 @@ def test_project_u_closed_forms():
     assert (oracle_project_u(np.zeros((1, d, d)), kr) == 0).all()
     tiny = oracle_project_u(np.eye(d)[None] * 1e-14, np.ones((1, d)))
     np.testing.assert_allclose(tiny[0, 0], np.full(d, 1e-14 / 1e-12), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Residual (delta-rule) update ("Variational Linear Attention: Stable
+# Associative Memory for Long-Context Transformers", technical summary 2.3;
+# its section 5 ties the method to recursive least squares).
+# --------------------------------------------------------------------------
+def test_residual_unnormalised_is_recursive_least_squares():
+    # With u = k and both unit normalisations dropped, the residual scan is
+    # recursive least squares: S_t M_t = S0 A0^{-1} + sum_s v_s k_s^T with
+    # M_t = A0^{-1} + sum_s k_s k_s^T, i.e. S_t solves the regularised
+    # least-squares problem in closed form.
+    C, T, d = 2, 30, 6
+    q, k, v, _ = _rand_inputs(C, T, d, 1, seed=30)
+    g = _rng(31)
+    A0 = np.stack([_spd(d, 32), _spd(d, 33)])
+    S0 = g.standard_normal((C, d, d))
+    res = oracle_scan(q, k, v, k[:, :, None, :], A0=A0, S0=S0, update="residual", normalize=False)
+    for c in range(C):
+        M = np.linalg.inv(A0[c])
+        Y = S0[c] @ M
+        n = np.zeros(d)
+        for t in range(T):
+            M = M + np.outer(k[c, t], k[c, t])
+            Y = Y + np.outer(v[c, t], k[c, t])
+            n = n + k[c, t]
+            St = np.linalg.solve(M.T, Y.T).T            # Y M^{-1}
+            np.testing.assert_allclose(res["o"][c, t], St @ q[c, t] / (n @ q[c, t] + 1e-6),
+                                       rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(res["S"][c], St, rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(res["A"][c], np.linalg.inv(M), rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("with_u", [True, False])
+def test_residual_orthogonal_keys_closed_form(with_u):
+    # Keys along orthonormal directions e_t with non-unit lengths c_t.  With
+    # u_t = e_t (or u = 0) and A0 = I, A_t k_hat_t is a positive multiple of
+    # e_t, so the unit gate is e_t itself and the update is the delta rule:
+    # S_T = S0 (I - sum e e^T) + sum v e^T, each key's value recalled exactly.
+    d, T = 8, 6
+    g = _rng(34)
+    E, _ = np.linalg.qr(g.standard_normal((d, d)))
+    E = E[:, :T].T                                        # rows e_t, orthonormal
+    c = g.uniform(0.4, 3.0, size=T)
+    k = (c[:, None] * E)[None]
+    v = g.standard_normal((1, T, d))
+    q = np.abs(g.standard_normal((1, T, d))) + 0.5
+    u = E[None, :, None, :] if with_u else np.zeros((1, T, 1, d))
+    S0 = g.standard_normal((1, d, d))
+    res = oracle_scan(q, k, v, u, S0=S0, update="residual")
+    P = np.eye(d)
+    Y = np.zeros((d, d))
+    n = np.zeros(d)
+    for t in range(T):
+        P = P - np.outer(E[t], E[t])
+        Y = Y + np.outer(v[0, t], E[t])
+        n = n + k[0, t]
+        St = S0[0] @ P + Y
+        np.testing.assert_allclose(St @ E[t], v[0, t], rtol=1e-12, atol=1e-12)
+        den = n @ q[0, t] + 1e-6
+        np.testing.assert_allclose(res["o"][0, t] * den, St @ q[0, t], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(res["S"][0], St, rtol=1e-12, atol=1e-12)
+    A_expect = np.eye(d) - 0.5 * E.T @ E if with_u else np.eye(d)
+    np.testing.assert_allclose(res["A"][0], A_expect, rtol=1e-13, atol=1e-14)
+
+
+def test_residual_first_step_gate_is_unit_and_nudged():
+    # From S0 = 0 the first state is v alpha_hat^T with a unit gate along
+    # A_1 k, where A_1 = (A0^{-1} + sum_i u_i u_i^T)^{-1} + eps I (a nudge at
+    # tau = 1 with nudge_period = 1), computed here by direct inversion.
+    C, d, r, eps = 3, 6, 2, 1e-2
+    q, k, v, u = _rand_inputs(C, 1, d, r, seed=35)
+    A0 = np.stack([_spd(d, 36 + c) for c in range(C)])
+    res = oracle_scan(q, k, v, u, A0=A0, nudge_period=1, eps=eps, update="residual")
+    for c in range(C):
+        M = np.linalg.inv(A0[c]) + sum(np.outer(u[c, 0, i], u[c, 0, i]) for i in range(r))
+        A1 = np.linalg.inv(M) + eps * np.eye(d)
+        gate = A1 @ k[c, 0]
+        gate = gate / np.linalg.norm(gate)
+        np.testing.assert_allclose(res["S"][c], np.outer(v[c, 0], gate), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(np.linalg.norm(res["S"][c]), np.linalg.norm(v[c, 0]), rtol=1e-13)
+        np.testing.assert_allclose(res["A"][c], A1, rtol=1e-12, atol=1e-14)
+
+
+def test_residual_invariants_linearity_resume_cap():
+    C, T, T1, d = 3, 60, 23, 8
+    q, k, v1, u = _rand_inputs(C, T, d, 2, seed=37)
+    g = _rng(38)
+    v2 = g.standard_normal(v1.shape)
+    S1, S2 = g.standard_normal((C, d, d)), g.standard_normal((C, d, d))
+    kw = dict(update="residual", nudge_period=8, eps=1e-3)
+    # linear in (v, S0) with the cap off; A does not depend on v
+    a = oracle_scan(q, k, v1, u, S0=S1, **kw)
+    b = oracle_scan(q, k, v2, u, S0=S2, **kw)
+    cc = oracle_scan(q, k, v1 - 2.5 * v2, u, S0=S1 - 2.5 * S2, **kw)
+    np.testing.assert_allclose(cc["o"], a["o"] - 2.5 * b["o"], rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(cc["S"], a["S"] - 2.5 * b["S"], rtol=1e-9, atol=1e-10)
+    np.testing.assert_array_equal(a["A"], b["A"])
+    # the inverse side is the same as in the additive scan
+    np.testing.assert_array_equal(a["A"], oracle_scan(q, k, v1, u, S0=S1, nudge_period=8, eps=1e-3)["A"])
+    # resume with the state carried and t0 = T1, cap on
+    kw["s_cap"] = 1.5
+    full = oracle_scan(q, k, v1, u, **kw)
+    assert (full["cap_fires"] > 0).all()
+    assert (full["max_s_norm"] <= 1.5 * (1 + 1e-12)).all()
+    x = oracle_scan(q[:, :T1], k[:, :T1], v1[:, :T1], u[:, :T1], **kw)
+    y = oracle_scan(q[:, T1:], k[:, T1:], v1[:, T1:], u[:, T1:], A0=x["A"], S0=x["S"], n0=x["n"], t0=T1, **kw)
+    np.testing.assert_allclose(np.concatenate([x["o"], y["o"]], axis=1), full["o"], rtol=1e-12, atol=1e-14)
+    for key in ("A", "S", "n"):
+        np.testing.assert_allclose(y[key], full[key], rtol=1e-12, atol=1e-14)
+
+
+def test_residual_mpmath_brute_force_tiny():
+    # 50 digits, direct inverses of the accumulated penalty, the residual
+    # state step written from the summary's recursive update rule.
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    C, T, d, r = 2, 10, 4, 2
+    q, k, v, u = _rand_inputs(C, T, d, r, seed=39)
+    P, cap, eps = 4, 1.2, 1e-2
+    res = oracle_scan(q, k, v, u, nudge_period=P, s_cap=cap, eps=eps, update="residual")
+    mp = mpmath.mpf
+    for c in range(C):
+        M = mpmath.eye(d)
+        S = mpmath.zeros(d, d)
+        n = mpmath.zeros(d, 1)
+        nudges = 0
+        for t in range(T):
+            for i in range(r):
+                uu = mpmath.matrix([mp(x) for x in u[c, t, i]])
+                M = M + uu * uu.T
+            if (t + 1) % P == 0:
+                nudges += 1
+                # A + eps I = (M^{-1} + eps I): carry M as the inverse of that
+                M = (M ** -1 + mp(eps) * mpmath.eye(d)) ** -1
+            A = M ** -1
+            kk = mpmath.matrix([mp(x) for x in k[c, t]])
+            kh = kk / mpmath.sqrt(sum(x * x for x in kk))
+            gate = A * kh
+            gate = gate / mpmath.sqrt(sum(x * x for x in gate))
+            vv = mpmath.matrix([mp(x) for x in v[c, t]])
+            S = S + (vv - S * kh) * gate.T
+            fn = mpmath.sqrt(sum(S[i, j] ** 2 for i in range(d) for j in range(d)))
+            if fn > cap:
+                S = S * (mp(cap) / fn)
+            n = n + kk
+            qq = mpmath.matrix([mp(x) for x in q[c, t]])
+            o = S * qq / ((n.T * qq)[0] + mp("1e-6"))
+            np.testing.assert_allclose([float(x) for x in o], res["o"][c, t], rtol=1e-11, atol=1e-13)
+        assert nudges == T // P
+        np.testing.assert_allclose(np.array(S.tolist(), dtype=float), res["S"][c], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(np.array(A.tolist(), dtype=float), res["A"][c], rtol=1e-11, atol=1e-13)
