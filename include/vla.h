@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define VLA_ABI_VERSION 1
+#define VLA_ABI_VERSION 2
 
 typedef enum {
   VLA_OK = 0,
@@ -59,6 +59,18 @@ typedef enum {
   VLA_SCHEDULE_CHUNKED = 2      /* time-parallel inverse pass over chunks, then a per-chain state
                                    pass (d = 64; needs workspace; see vla_scan_forward) */
 } vla_schedule_t;
+
+/* The state step of the recurrence.  ADDITIVE is the update of "Mathematical
+ * Primitives", section 5 (S += v alpha_hat^T, alpha_hat = alpha / max(|alpha|, 1)).
+ * RESIDUAL is the recursive update rule of "Variational Linear Attention:
+ * Stable Associative Memory for Long-Context Transformers", technical summary
+ * 2.3: k_hat = k / |k|, alpha_hat = A_t k_hat / |A_t k_hat| (unit), and
+ * S += (v - S k_hat) alpha_hat^T with the prediction S k_hat taken before the
+ * update; normalisations divide by max(|x|, 1e-12). */
+typedef enum {
+  VLA_UPDATE_ADDITIVE = 0,
+  VLA_UPDATE_RESIDUAL = 1
+} vla_update_t;
 
 /* Parameters of one scan call.  Fill with vla_scan_params_init() first. */
 typedef struct {
@@ -83,11 +95,14 @@ typedef struct {
                              one segment while a side stream preps the next
                              and reads out the last); 0 = library picks (256),
                              < 0 = one segment */
+  int32_t update;        /* vla_update_t; RESIDUAL runs the SEQUENTIAL schedule
+                            only (CHUNKED returns VLA_EUNSUPPORTED, AUTO picks
+                            SEQUENTIAL) */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
  * den_eps = 1e-6, t0 = 0, automatic schedule, no validation, chunk_len = 0,
- * segment_blocks = 0.  Host pointer. */
+ * segment_blocks = 0, additive update.  Host pointer. */
 void vla_scan_params_init(vla_scan_params_t* p);
 
 /* Bytes of device workspace vla_scan_forward needs for these parameters
@@ -115,6 +130,8 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  *   if nudge_period > 0 and tau % nudge_period == 0:  A += eps*I
  *   alpha = A k_t;  alpha_hat = alpha / max(|alpha|_2, 1)
  *   S += v_t alpha_hat^T                      (S is [value, key])
+ *     (update = RESIDUAL instead: k_hat = k_t / |k_t|,
+ *      alpha_hat = A k_hat / |A k_hat|, S += (v_t - S k_hat) alpha_hat^T)
  *   if cap on and |S|_F > s_cap:  S *= s_cap / |S|_F   (counted)
  *   n += k_t;  o_t = S q_t / (n.q_t + den_eps)
  *

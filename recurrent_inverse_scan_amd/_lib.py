@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(_PKG, "libvla.so")
 VLA_OK, VLA_EINVAL, VLA_EUNSUPPORTED, VLA_EWORKSPACE, VLA_ENONFINITE, VLA_EHIP = range(6)
 VLA_F32, VLA_BF16 = 0, 1
 VLA_SCHEDULE_AUTO, VLA_SCHEDULE_SEQUENTIAL, VLA_SCHEDULE_CHUNKED = 0, 1, 2
+VLA_UPDATE_ADDITIVE, VLA_UPDATE_RESIDUAL = 0, 1
+ABI_VERSION = 2
 
 # Every symbol include/vla.h declares.
 EXPORTED = (
@@ -37,6 +39,7 @@ class ScanParams(ctypes.Structure):
         ("validate", ctypes.c_int32),
         ("chunk_len", ctypes.c_int32),
         ("segment_blocks", ctypes.c_int32),
+        ("update", ctypes.c_int32),
     ]
 
 

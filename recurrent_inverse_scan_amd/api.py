@@ -32,7 +32,8 @@ def _need_cuda(*ts):
 
 
 def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
-                schedule="auto", validate=False, chunk_len=0, segment_blocks=0) -> _lib.ScanParams:
+                schedule="auto", validate=False, chunk_len=0, segment_blocks=0,
+                update="additive") -> _lib.ScanParams:
     p = _lib.ScanParams()
     _lib.load().vla_scan_params_init(ctypes.byref(p))
     p.B, p.H, p.T, p.d, p.r = B, H, T, d, r
@@ -47,12 +48,13 @@ def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, d
     p.validate = 1 if validate else 0
     p.chunk_len = chunk_len
     p.segment_blocks = segment_blocks
+    p.update = {"additive": _lib.VLA_UPDATE_ADDITIVE, "residual": _lib.VLA_UPDATE_RESIDUAL}[update]
     return p
 
 
 def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0, s_cap=None,
                  den_eps=1e-6, t0=0, schedule="auto", validate=False, chunk_len=0, segment_blocks=0, out=None,
-                 workspace=None):
+                 workspace=None, update="additive"):
     """Run vla_scan_forward.
 
     q, k, v: [B, H, T, d]; u: [B, H, T, r, d], all float32 or all bfloat16 on
@@ -60,7 +62,8 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     ``schedule`` is "auto", "sequential" or "chunked"; ``chunk_len`` 0 lets
     the library pick; ``segment_blocks`` (chunked schedule) sets the blocks of
     64 tokens per state-pass segment, 0 lets the library pick and -1 keeps one
-    segment.  ``out`` may pass preallocated (o, A_T, S_T, n_T,
+    segment.  ``update`` is "additive" or "residual" (the delta-rule state
+    step; sequential schedule only).  ``out`` may pass preallocated (o, A_T, S_T, n_T,
     stats) tensors and ``workspace`` a preallocated uint8 device buffer of at
     least ``workspace_size(...)`` bytes.  Returns (o, A_T, S_T, n_T, stats).
     """
@@ -89,7 +92,7 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
         o, A_T, S_T, n_T, stats = out
     p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
                     t0=t0, schedule=schedule, validate=validate, chunk_len=chunk_len,
-                    segment_blocks=segment_blocks)
+                    segment_blocks=segment_blocks, update=update)
     lib = _lib.load()
     ws_bytes = ctypes.c_size_t(0)
     _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))

@@ -11,6 +11,14 @@
 // norm <= 1, S += v alpha_hat^T, the Frobenius cap, n += k and the readout
 // o = S q / (n.q + den_eps).
 //
+// The residual (delta-rule) update ("Variational Linear Attention: Stable
+// Associative Memory for Long-Context Transformers", technical summary 2.3)
+// is a variant of kFull (template flag RES): the gate is the unit vector
+// along A_t k_hat with k_hat = k / |k|, and S += (v - S k_hat) alpha_hat^T,
+// the prediction S_{t-1} k_hat taken before the update.  Since A_t k_hat is a
+// multiple of A_t k, the gate comes from the same fused y = A k; the
+// prediction is one more sweep of S per token.
+//
 // Three modes share this code:
 //  * kFull: the whole recurrence (the sequential schedule, and the per-chain
 //    fallback of the time-parallel schedule, gated by a per-chain flag);
@@ -38,9 +46,10 @@
 
 namespace vla {
 
-template <typename TIn, int D, int NW, int CG, SeqMode MODE>
+template <typename TIn, int D, int NW, int CG, SeqMode MODE, bool RES>
 __global__ void __launch_bounds__(64 * NW)
 vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
+  static_assert(!RES || MODE == SeqMode::kFull, "the residual update runs in the full recurrence only");
   using L = TileLayout<D, NW, CG>;
   constexpr int R = L::R, C = L::C, RW = L::RW, NTH = L::kThreads;
   constexpr bool kFull = MODE == SeqMode::kFull;
@@ -166,6 +175,26 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
       float kI[R];
       lds_rows<R>(tk + row0, kI);
       float aJ[C];
+      // Residual update: 1/|k| and the prediction S_{t-1} k (rows of this lane).
+      float kinv = 1.f, pred[RES ? R : 1];
+      if constexpr (RES) {
+        float kJ[C];
+        lds_cols<CG, C>(tk, cg, kJ);
+        float kn = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) kn = fmaf(kJ[c], kJ[c], kn);
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          float acc = 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc = fmaf(S[ii][c], kJ[c], acc);
+          pred[ii] = acc;
+        }
+        kn = group_sum<CG>(kn);
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) pred[ii] = group_sum<CG>(pred[ii]);
+        kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+      }
 
       if constexpr (kHasA) {
         float y[R];
@@ -298,7 +327,9 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
 #pragma unroll
           for (int ww = 0; ww < NW; ++ww) an += red[(par * NW + ww) * 4 + 0];
         }
-        const float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+        // Additive: alpha / max(|alpha|, 1).  Residual: the unit vector along
+        // A k_hat = kinv * A k, i.e. kinv / max(kinv |A k|, 1e-12) times A k.
+        const float ascale = RES ? kinv / fmaxf(kinv * sqrtf(an), 1e-12f) : (an > 1.f ? 1.f / sqrtf(an) : 1.f);
         lds_cols<CG, C>(ab, cg, aJ);
 #pragma unroll
         for (int c = 0; c < C; ++c) aJ[c] *= ascale;
@@ -312,6 +343,10 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
       if constexpr (kHasS) {
       float vI[R], qI[R], qJ[C];
       lds_rows<R>(tv + row0, vI);
+      if constexpr (RES) {
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) vI[ii] = fmaf(-pred[ii], kinv, vI[ii]);   // v - S_{t-1} k_hat
+      }
       lds_rows<R>(tq + row0, qI);
       lds_cols<CG, C>(tq, cg, qJ);
       float ns = 0.f, po[R];
@@ -446,7 +481,17 @@ static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, h
   const size_t lds = seq_lds_bytes<TIn, D, NW>(MODE, a.r);
   const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.chunk_cnt)
                                                        : static_cast<unsigned>(chains);
-  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE>), dim3(grid), dim3(64 * NW), lds, stream, a, x);
+  if constexpr (MODE == SeqMode::kFull) {
+    if (a.residual) {
+      hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, true>), dim3(grid), dim3(64 * NW), lds, stream,
+                         a, x);
+      return hipGetLastError();
+    }
+  } else {
+    if (a.residual) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, false>), dim3(grid), dim3(64 * NW), lds, stream, a,
+                     x);
   return hipGetLastError();
 }
 

@@ -182,7 +182,7 @@ bool chunk_len_fits(const vla_scan_params_t* p, int L) {
 ChunkLayout plan_schedule(const vla_scan_params_t* p) {
   ChunkLayout cl;
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
-  const bool possible = p->d == 64 && p->T > 0 && chains > 0;
+  const bool possible = p->d == 64 && p->T > 0 && chains > 0 && p->update == VLA_UPDATE_ADDITIVE;
   int L = 0;
   if (possible) {
     if (p->chunk_len > 0) {
@@ -259,6 +259,10 @@ vla_status_t check_params(const vla_scan_params_t* p) {
       p->schedule != VLA_SCHEDULE_CHUNKED)
     return fail(VLA_EUNSUPPORTED, "schedule %d unsupported", p->schedule);
   if (p->chunk_len < 0) return fail(VLA_EINVAL, "chunk_len must be >= 0");
+  if (p->update != VLA_UPDATE_ADDITIVE && p->update != VLA_UPDATE_RESIDUAL)
+    return fail(VLA_EUNSUPPORTED, "update %d unsupported", p->update);
+  if (p->update == VLA_UPDATE_RESIDUAL && p->schedule == VLA_SCHEDULE_CHUNKED)
+    return fail(VLA_EUNSUPPORTED, "the residual update runs on the sequential schedule only");
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
   if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
   return VLA_OK;
@@ -283,6 +287,7 @@ void vla_scan_params_init(vla_scan_params_t* p) {
   p->validate = 0;
   p->chunk_len = 0;
   p->segment_blocks = 0;
+  p->update = VLA_UPDATE_ADDITIVE;
 }
 
 vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
@@ -386,6 +391,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   a.cap_on = (p->s_cap > 0.f && std::isfinite(p->s_cap)) ? 1 : 0;
   a.cap = a.cap_on ? p->s_cap : 0.f;
   a.den_eps = p->den_eps;
+  a.residual = p->update == VLA_UPDATE_RESIDUAL ? 1 : 0;
   if (!cl.use) {
     const hipError_t e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");

@@ -27,6 +27,7 @@ struct ScanArgs {
   float cap;
   int32_t cap_on;
   float den_eps;
+  int32_t residual;       // nonzero: residual (delta-rule) state update; full recurrence only
 };
 
 // Whole recurrence, one workgroup per chain.  only_if (nullable) restricts

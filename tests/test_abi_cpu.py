@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vla_abi_version() == 1
+    assert lib.vla_abi_version() == _lib.ABI_VERSION == 2
     names = [lib.vla_status_string(i).decode() for i in range(6)]
     assert names == ["VLA_OK", "VLA_EINVAL", "VLA_EUNSUPPORTED", "VLA_EWORKSPACE", "VLA_ENONFINITE", "VLA_EHIP"]
 
@@ -71,7 +71,7 @@ def test_params_struct_layout_matches_header(lib, tmp_path):
     assert (p.B, p.H, p.T, p.d, p.r, p.in_dtype) == (0, 0, 0, 64, 1, 0)
     assert abs(p.eps - 1e-6) < 1e-12 and abs(p.den_eps - 1e-6) < 1e-12
     assert (p.nudge_period, p.s_cap, p.t0, p.schedule, p.validate, p.chunk_len) == (0, 0.0, 0, 0, 0, 0)
-    assert p.segment_blocks == 0
+    assert p.segment_blocks == 0 and p.update == _lib.VLA_UPDATE_ADDITIVE
 
 
 def _params(lib, **kw):
@@ -100,6 +100,7 @@ def _scan(lib, p, **ptrs):
     ("nudge_period", -1, _lib.VLA_EINVAL), ("eps", float("nan"), _lib.VLA_EINVAL),
     ("eps", -1.0, _lib.VLA_EINVAL), ("s_cap", float("nan"), _lib.VLA_EINVAL), ("t0", -5, _lib.VLA_EINVAL),
     ("schedule", 9, _lib.VLA_EUNSUPPORTED), ("chunk_len", -3, _lib.VLA_EINVAL),
+    ("update", 2, _lib.VLA_EUNSUPPORTED), ("update", -1, _lib.VLA_EUNSUPPORTED),
 ])
 def test_scan_rejects_bad_params(lib, field, value, status):
     p = _params(lib, **{field: value})
@@ -164,3 +165,16 @@ def test_chunked_schedule_planning(lib):
     for kw in (dict(chunk_len=96, nudge_period=1024), dict(d=128), dict(t0=100, nudge_period=0)):
         q = _params(lib, B=1, H=2, T=4096, schedule=_lib.VLA_SCHEDULE_CHUNKED, **kw)
         assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
+
+
+def test_residual_update_runs_sequentially(lib):
+    """The residual update has no chunked form: AUTO plans the sequential
+    schedule (no workspace) where the additive update would chunk, and an
+    explicit CHUNKED request is refused before anything runs."""
+    n = ctypes.c_size_t(7)
+    p = _params(lib, B=2, H=8, T=65536, nudge_period=1024, update=_lib.VLA_UPDATE_RESIDUAL)
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+    p.schedule = _lib.VLA_SCHEDULE_CHUNKED
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
+    assert _scan(lib, p) == _lib.VLA_EUNSUPPORTED
+    assert "residual" in lib.vla_last_error().decode()

@@ -1,0 +1,159 @@
+"""GPU parity of the residual (delta-rule) update against the fp64 oracle.
+
+The residual update ("Variational Linear Attention: Stable Associative Memory
+for Long-Context Transformers", technical summary 2.3) runs on the sequential
+schedule.  Every case calls libvla.so through the C ABI and compares with
+``oracle_scan(..., update="residual")`` on the same seeded inputs, to the
+normwise bars of the additive scan (2e-3 float32 storage, 1e-2 bfloat16).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.vla_oracle import oracle_project_u, oracle_scan
+from recurrent_inverse_scan_amd import CONFIGS, make_inputs, project_u, scan_forward
+from recurrent_inverse_scan_amd._lib import VLAError, VLA_EUNSUPPORTED
+from tests.parity import TOL, case, flat, rel_err, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(f"[gpu-residual] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _gpu(x, cfg, **kw):
+    args = dict(nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, update="residual")
+    args.update(kw)
+    out = scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["u"].to(DEV), **args)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(cfg, out, ref, chains=None):
+    tol = TOL[cfg.in_dtype]
+    o, A, S, n, st = out
+    errs = {
+        "o": rel_err(flat(o, cfg, chains), ref["o"]),
+        "A": rel_err(flat(A, cfg, chains), ref["A"], axes=(-2, -1)),
+        "S": rel_err(flat(S, cfg, chains), ref["S"], axes=(-2, -1)),
+        "n": rel_err(flat(n, cfg, chains), ref["n"]),
+    }
+    _say(f"{cfg.name} B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} r={cfg.r} {cfg.in_dtype}: {errs}")
+    assert all(v <= tol for v in errs.values()), errs
+    st = flat(st, cfg, chains).cpu().numpy()
+    np.testing.assert_array_equal(st[:, 0], ref["guard_fires"])
+    assert (st[:, 2] == ref["nonfinite"]).all()
+    if cfg.s_cap:
+        # cap decisions may differ only where |S|_F is within rounding of the cap
+        assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
+    return st
+
+
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "base": CONFIGS["base"].with_(B=2, H=3, T=1029),
+    "recall": CONFIGS["recall"].with_(B=4, H=8),
+    "long": CONFIGS["long"].with_(B=1, H=3, T=2053, nudge_period=64, s_cap=20.0),
+    "wide": CONFIGS["wide"].with_(B=1, H=3, T=517, nudge_period=32),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_residual_parity_small(name):
+    cfg = SMALL[name]
+    _say(f"case small/{name}")
+    x = case(cfg)
+    st = _check(cfg, _gpu(x, cfg), run_oracle(x, cfg, update="residual"))
+    if name == "long":
+        assert st[:, 1].min() > 0, "the reduced long case is meant to exercise the cap"
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("r", [1, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_residual_parity_shapes(d, r, dtype):
+    cfg = CONFIGS["base"].with_(name=f"res-d{d}-r{r}", B=1, H=2, T=37, d=d, r=r, in_dtype=dtype,
+                                nudge_period=5, s_cap=3.0)
+    x = case(cfg, seed=d * 10 + r)
+    _check(cfg, _gpu(x, cfg), run_oracle(x, cfg, update="residual"))
+
+
+@pytest.mark.parametrize("T", [0, 1, 9])
+def test_residual_initial_state_and_offset(T):
+    cfg = CONFIGS["base"].with_(name=f"res-len{T}", B=1, H=2, T=T, nudge_period=3, s_cap=50.0)
+    x = case(cfg, seed=100 + T)
+    g = torch.Generator().manual_seed(T)
+    A0 = torch.eye(cfg.d).expand(1, 2, cfg.d, cfg.d) * 0.5 + 0.01 * torch.randn(1, 2, cfg.d, cfg.d, generator=g)
+    A0 = ((A0 + A0.transpose(-1, -2)) / 2).contiguous()
+    S0 = torch.randn(1, 2, cfg.d, cfg.d, generator=g)
+    n0 = torch.rand(1, 2, cfg.d, generator=g)
+    out = _gpu(x, cfg, A0=A0.to(DEV), S0=S0.to(DEV), n0=n0.to(DEV), t0=5)
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, cfg.d, cfg.d), S0=S0.reshape(2, cfg.d, cfg.d),
+                     n0=n0.reshape(2, cfg.d), t0=5, update="residual")
+    _check(cfg, out, ref)
+
+
+def test_residual_resume_in_place():
+    """Two calls with the state carried in place (A_T, S_T, n_T aliasing A0,
+    S0, n0) and t0 advanced equal one call over the whole sequence."""
+    cfg = CONFIGS["base"].with_(name="res-resume", B=1, H=4, T=300, nudge_period=16, s_cap=30.0)
+    x = case(cfg, seed=7)
+    whole = _gpu(x, cfg)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    A = torch.eye(d, device=DEV).expand(B, H, d, d).contiguous()
+    S = torch.zeros(B, H, d, d, device=DEV)
+    n = torch.zeros(B, H, d, device=DEV)
+    outs = []
+    for lo, hi in ((0, 112), (112, 300)):
+        sl = {key: x[key][:, :, lo:hi].contiguous().to(DEV) for key in ("q", "k", "v", "u")}
+        o = torch.empty_like(sl["q"])
+        st = torch.empty(B, H, 4, device=DEV, dtype=torch.int32)
+        scan_forward(sl["q"], sl["k"], sl["v"], sl["u"], A, S, n, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap,
+                     t0=lo, update="residual", out=(o, A, S, n, st))
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat(outs, dim=2), whole[0].cpu().numpy()) <= 1e-5
+    assert rel_err(S, whole[2].cpu().numpy(), axes=(-2, -1)) <= 1e-5
+    assert rel_err(A, whole[1].cpu().numpy(), axes=(-2, -1)) <= 1e-5
+
+
+def test_residual_bitwise_repeatable_and_chunked_refused():
+    cfg = CONFIGS["base"].with_(name="res-repeat", B=2, H=2, T=200)
+    x = case(cfg, seed=3)
+    a, b = _gpu(x, cfg), _gpu(x, cfg)
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
+    with pytest.raises(VLAError) as e:
+        _gpu(x, cfg, schedule="chunked")
+    assert e.value.status == VLA_EUNSUPPORTED
+
+
+# Full-size workloads with the residual update, the GPU projection then the
+# scan on every chain; the oracle runs on sampled chains.
+FULL_SAMPLES = {"base": [0, 31], "recall": [0, 511], "long": [0, 15], "wide": [0, 127]}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_residual_full_size_sampled_chains(name):
+    cfg = CONFIGS[name]
+    sel = FULL_SAMPLES[name]
+    _say(f"case full/{name} chains={sel}")
+    x = make_inputs(cfg, seed=0)
+    u = project_u(x["W_u"].to(DEV), x["k_raw"].to(DEV))
+    out = scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), u, nudge_period=cfg.nudge_period,
+                       s_cap=cfg.s_cap, update="residual")
+    torch.cuda.synchronize()
+    C = cfg.B * cfg.H
+    kr = x["k_raw"].reshape(C, cfg.T, cfg.d)[sel]
+    u_ref = oracle_project_u(x["W_u"], kr.reshape(-1, cfg.d))
+    u_ref = torch.from_numpy(u_ref).to(x["q"].dtype).reshape(len(sel), cfg.T, cfg.r, cfg.d)
+    ref = oracle_scan(x["q"].reshape(C, cfg.T, cfg.d)[sel], x["k"].reshape(C, cfg.T, cfg.d)[sel],
+                      x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
+                      s_cap=cfg.s_cap, update="residual")
+    _check(cfg, out, ref, chains=sel)
