@@ -86,6 +86,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary measurements (residual update, decode step)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, one device-to-device copy of this many MiB (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
@@ -181,6 +183,8 @@ def main(argv=None) -> int:
     scan_bytes = tok_heads * d * es * (4 + r) + 2 * B * H * (2 * d * d + d) * 4   # q,k,v,u in, o out, state
     stats = outs[4].cpu().numpy()
 
+    extra = None if args.no_extra else extra_measurements(CONFIGS, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, x, args.cpu_baseline_seconds)
@@ -212,9 +216,97 @@ def main(argv=None) -> int:
         "guard_fires": int(stats[..., 0].sum()),
         "cap_fires": int(stats[..., 1].sum()),
         "cpu_baseline": cpu,
+        "extra": extra,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _time_ms(fn, reps: int, warmup: int = 2) -> float:
+    """Mean milliseconds of fn() over reps calls, from events on torch's
+    current stream (the sequential schedule launches only there)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extra_measurements(CONFIGS, dev):
+    """Secondary workloads, each timed on its own with inputs resident:
+
+    * residual: the residual (delta-rule) update, on the 512-chain recall
+      workload (sequential schedule) and on the long workload (time-parallel
+      schedule); algorithmic
+      flops 2 (2r+4) d^2 per token*head (one more d^2 sweep than additive);
+    * decode: one token per call (T = 1) for 4096 chains with the state read
+      from and written back to HBM in place; its bound is HBM, with
+      algorithmic bytes per chain of A, S (read and written, fp32), n, and
+      the token's q, k, v, u in and o out.
+    """
+    import torch
+
+    from recurrent_inverse_scan_amd import make_inputs, project_u, scan_forward, workspace_size
+
+    out = {}
+    for name, reps in (("recall", 20), ("long", 2)):
+        cfg = CONFIGS[name]
+        x = make_inputs(cfg, seed=0)
+        q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+        u = project_u(x["W_u"].to(dev), x["k_raw"].to(dev))
+        B, H, T, d, r = cfg.B, cfg.H, cfg.T, cfg.d, cfg.r
+        o = (torch.empty_like(q), torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d, d), device=dev),
+             torch.empty((B, H, d), device=dev), torch.empty((B, H, 4), device=dev, dtype=torch.int32))
+        ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap,
+                                  update="residual")
+        sched = "chunked" if ws_bytes > 0 else "sequential"
+        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+        fn = lambda: scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, update="residual",
+                                  out=o, workspace=ws)
+        ms = _time_ms(fn, reps, warmup=1)
+        th = B * H * T
+        tfl = 2 * (2 * r + 4) * d * d * th / (ms * 1e-3) / 1e12
+        out[f"residual_{name}"] = {
+            "workload": f"{name}: residual update, B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
+                        f"{sched} schedule", "ms": ms, "tokens_heads_per_s": th / (ms * 1e-3),
+            "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
+            "kernel": "vla_res_chain_kernel" if sched == "chunked" else "vla_scan_seq_kernel"}
+        del q, k, v, u, o, x, ws
+
+    # Decode: 4096 chains, one token per call, state carried in place.
+    B, H, d, r = 256, 16, 64, 1
+    g = torch.Generator(device="cpu").manual_seed(0)
+    elu1 = lambda z: torch.nn.functional.elu(z) + 1.0
+    q = elu1(torch.randn(B, H, 1, d, generator=g)).to(torch.bfloat16).to(dev)
+    k = elu1(torch.randn(B, H, 1, d, generator=g)).to(torch.bfloat16).to(dev)
+    v = torch.randn(B, H, 1, d, generator=g).to(torch.bfloat16).to(dev)
+    uu = torch.randn(B, H, 1, r, d, generator=g)
+    u = (uu / uu.norm(dim=-1, keepdim=True)).to(torch.bfloat16).to(dev)
+    A = torch.eye(d, device=dev).expand(B, H, d, d).contiguous()
+    S = torch.zeros(B, H, d, d, device=dev)
+    n = torch.zeros(B, H, d, device=dev)
+    o = torch.empty_like(q)
+    st = torch.empty(B, H, 4, device=dev, dtype=torch.int32)
+    for upd in ("additive", "residual"):
+        fn = lambda: scan_forward(q, k, v, u, A, S, n, nudge_period=1024, s_cap=1e3, update=upd,
+                                  out=(o, A, S, n, st))
+        ms = _time_ms(fn, 50, warmup=5)
+        chains = B * H
+        alg_bytes = chains * (2 * (2 * d * d + d) * 4 + (4 + r) * d * 2)
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        out[f"decode_{upd}"] = {
+            "workload": f"decode: {upd} update, T=1 per call, B={B} H={H} d={d} r={r}, bf16 "
+                        f"token storage, f32 state in HBM carried in place", "ms": ms,
+            "tokens_heads_per_s": chains / (ms * 1e-3), "alg_bytes": alg_bytes, "hbm_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "kernel": "vla_scan_seq_kernel"}
+    return out
 
 
 def cpu_baseline(cfg, x, budget_s: float):

@@ -95,9 +95,7 @@ typedef struct {
                              one segment while a side stream preps the next
                              and reads out the last); 0 = library picks (256),
                              < 0 = one segment */
-  int32_t update;        /* vla_update_t; RESIDUAL runs the SEQUENTIAL schedule
-                            only (CHUNKED returns VLA_EUNSUPPORTED, AUTO picks
-                            SEQUENTIAL) */
+  int32_t update;        /* vla_update_t (both schedules) */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
@@ -168,6 +166,14 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  * previous one's readout on the side stream.  CHUNKED
  * needs chunk_len to divide nudge_period (when nonzero) and t0; AUTO uses it
  * for d = 64 when there are few chains and long sequences.
+ *
+ * With update = RESIDUAL the chunked schedule's inverse pass writes the unit
+ * gates, and the state pass uses that, inside a block of 64 tokens, the
+ * prediction errors solve a unit lower-triangular system, so each block maps
+ * its starting state affinely, S -> S (I + N) + Q, with N and Q computed for
+ * all blocks in parallel; a per-chain pass chains those maps, and a parallel
+ * readout recovers every token's state and output.  A chain with a token
+ * whose state exceeds s_cap is recomputed sequentially with the cap applied.
  *
  * With validate != 0 the call first checks q, k, v, u for NaN/Inf on the
  * stream, synchronises the stream, and returns VLA_ENONFINITE (having

@@ -60,6 +60,7 @@ __device__ __forceinline__ float frag_elem(const uint4& f, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+template <bool UNIT_GATE>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restrict__ ux,
                       const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
@@ -306,7 +307,18 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 #pragma unroll
       for (int s = 0; s < 16; ++s) nrm = fmaf(XK[I][s], XK[I][s], nrm);
     nrm += __shfl_xor(nrm, 32);
-    const float ascale = nrm > 1.f ? 1.f / sqrtf(nrm) : 1.f;
+    float ascale = nrm > 1.f ? 1.f / sqrtf(nrm) : 1.f;
+    if constexpr (UNIT_GATE) {
+      // The residual update's gate: the unit vector along A k_hat, k_hat = k / |k|.
+      float kn = 0.f;
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kn = fmaf(frag_elem(kf[kp], e), frag_elem(kf[kp], e), kn);
+      kn += __shfl_xor(kn, 32);
+      const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+      ascale = kinv / fmaxf(kinv * sqrtf(nrm), 1e-12f);
+    }
     if (c < tcount) {
       float* dst = alpha_out + (chain * T + tb + c) * kD;
 #pragma unroll
@@ -367,10 +379,15 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 hipError_t launch_inverse_wy(const ScanArgs& a, const float* a_start, float* alpha_out, int32_t* chain_info,
                              int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, int chains, hipStream_t stream) {
   if (chunk_cnt <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vla_inverse_wy_kernel, dim3(static_cast<unsigned>(chains * chunk_cnt)), dim3(64), 0, stream,
-                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.u), a_start, alpha_out, a.A_T,
-                     chain_info, a.T, chunk_len, nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period,
-                     a.nudge_phase0);
+  const dim3 grid(static_cast<unsigned>(chains * chunk_cnt));
+  if (a.residual)
+    hipLaunchKernelGGL(vla_inverse_wy_kernel<true>, grid, dim3(64), 0, stream, static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.u), a_start, alpha_out, a.A_T, chain_info, a.T, chunk_len,
+                       nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period, a.nudge_phase0);
+  else
+    hipLaunchKernelGGL(vla_inverse_wy_kernel<false>, grid, dim3(64), 0, stream, static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.u), a_start, alpha_out, a.A_T, chain_info, a.T, chunk_len,
+                       nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period, a.nudge_phase0);
   return hipGetLastError();
 }
 

@@ -295,8 +295,18 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
         an = wave_sum(cg == 0 ? an : 0.f);
         if constexpr (kInv) {
           static_assert(!kInv || NW == 1, "the inverse-only pass runs one wave per chunk");
-          // alpha_hat of this token goes to HBM for the state pass.
-          const float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+          // alpha_hat of this token goes to HBM for the state pass: the
+          // clamped coefficient, or for the residual update the unit vector
+          // along A k_hat with k_hat = k / |k|.
+          float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+          if (a.residual) {
+            float kn = 0.f;
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) kn = fmaf(kI[ii], kI[ii], kn);
+            kn = wave_sum(cg == 0 ? kn : 0.f);
+            const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+            ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
+          }
           if (cg == 0) {
             float ah[R];
 #pragma unroll
@@ -487,7 +497,7 @@ static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, h
                          a, x);
       return hipGetLastError();
     }
-  } else {
+  } else if constexpr (MODE == SeqMode::kStateOnly) {
     if (a.residual) return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, false>), dim3(grid), dim3(64 * NW), lds, stream, a,

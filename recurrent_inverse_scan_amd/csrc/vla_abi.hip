@@ -170,6 +170,8 @@ struct ChunkLayout {
          off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0,
          off_ncarry = 0, off_cnt = 0, off_flag = 0,
          total = 0;
+  // Residual update's state pass (replaces the additive one's buffers).
+  size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0;
 };
 
 // Whether the chunked schedule can run these parameters with chunk length L.
@@ -182,7 +184,7 @@ bool chunk_len_fits(const vla_scan_params_t* p, int L) {
 ChunkLayout plan_schedule(const vla_scan_params_t* p) {
   ChunkLayout cl;
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
-  const bool possible = p->d == 64 && p->T > 0 && chains > 0 && p->update == VLA_UPDATE_ADDITIVE;
+  const bool possible = p->d == 64 && p->T > 0 && chains > 0;
   int L = 0;
   if (possible) {
     if (p->chunk_len > 0) {
@@ -223,6 +225,19 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * 64 * 4);
     cl.nblk = (p->T + 63) / 64;
     const size_t nb = cl.nblk, T = static_cast<size_t>(p->T);
+    if (p->update == VLA_UPDATE_RESIDUAL) {
+      cl.off_rW = off; off = align_up(off + C * nb * d2 * 4);
+      cl.off_rU = off; off = align_up(off + C * nb * d2 * 4);
+      cl.off_rN = off; off = align_up(off + C * nb * 3 * d2 * 2);
+      cl.off_rQ = off; off = align_up(off + C * nb * d2 * 4);
+      cl.off_rks = off; off = align_up(off + C * nb * 64 * 4);
+      cl.off_rS = off; off = align_up(off + C * nb * d2 * 4);
+      cl.off_rnb = off; off = align_up(off + C * nb * 64 * 4);
+      cl.off_flag = off;
+      if (p->validate) off += kValidateBytes;
+      cl.total = off;
+      return cl;
+    }
     cl.off_K = off; off = align_up(off + C * nb * 2304 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
     // Regrouped update operands: fp32 storage only (bf16 reads its LDS rows).
@@ -261,8 +276,6 @@ vla_status_t check_params(const vla_scan_params_t* p) {
   if (p->chunk_len < 0) return fail(VLA_EINVAL, "chunk_len must be >= 0");
   if (p->update != VLA_UPDATE_ADDITIVE && p->update != VLA_UPDATE_RESIDUAL)
     return fail(VLA_EUNSUPPORTED, "update %d unsupported", p->update);
-  if (p->update == VLA_UPDATE_RESIDUAL && p->schedule == VLA_SCHEDULE_CHUNKED)
-    return fail(VLA_EUNSUPPORTED, "the residual update runs on the sequential schedule only");
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
   if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
   return VLA_OK;
@@ -450,6 +463,8 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // of them (a segment's) it takes nearly as long, so it is not pipelined
   // with the chain kernel below.
   if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
+  // (The inverse pass below writes the residual update's unit gates when
+  // a.residual is set.)
   if (bf16 && p->r == 1)
     e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
                                static_cast<int>(chains), stream);
@@ -457,6 +472,45 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
                                         static_cast<int>(chains), stream);
   if (e != hipSuccess) return hip_fail(e, "chunked inverse launch");
+
+  if (p->update == VLA_UPDATE_RESIDUAL) {
+    // Residual state pass: per-block affine maps of S, their chain, readout.
+    vla::ResPlan rp{};
+    rp.T = p->T;
+    rp.nblk = cl.nblk;
+    rp.bf16 = bf16 ? 1 : 0;
+    rp.q = q; rp.k = k; rp.v = v; rp.o = o;
+    rp.alpha = pl.alpha;
+    rp.W = reinterpret_cast<float*>(ws + cl.off_rW);
+    rp.U = reinterpret_cast<float*>(ws + cl.off_rU);
+    rp.NTF = reinterpret_cast<uint16_t*>(ws + cl.off_rN);
+    rp.QT = reinterpret_cast<float*>(ws + cl.off_rQ);
+    rp.ksum = reinterpret_cast<float*>(ws + cl.off_rks);
+    rp.Ssnap = reinterpret_cast<float*>(ws + cl.off_rS);
+    rp.nblock = reinterpret_cast<float*>(ws + cl.off_rnb);
+    const int nch = static_cast<int>(chains);
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    {
+      Timing& tm = timing();
+      std::lock_guard<std::mutex> lock(tm.mu);
+      if (tm.on && tm.used < VLA_TIMING_SLOTS) {
+        ev0 = tm.start[tm.used];
+        ev1 = tm.stop[tm.used];
+        ++tm.used;
+      }
+    }
+    if ((e = vla::launch_res_prep(rp, nch, stream)) != hipSuccess) return hip_fail(e, "residual prep launch");
+    if ((e = vla::launch_res_chain(rp, pl.S_init, pl.n_init, S_T, n_T, stats, pl.chain_info, nch, stream, ev0, ev1)) !=
+        hipSuccess)
+      return hip_fail(e, "residual chain launch");
+    if ((e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, pl.chain_info, stream)) != hipSuccess)
+      return hip_fail(e, "residual readout launch");
+    if ((e = vla::launch_stats_finalize(stats, pl.chain_info, nch, stream)) != hipSuccess)
+      return hip_fail(e, "stats launch");
+    e = vla::launch_scan_sequential(a, d, bf16, nch, pl.chain_info, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
+    return VLA_OK;
+  }
 
   // State pass: prep, the chain kernel, readout.  The sequence is cut into
   // segments (even block counts): the chain kernel runs them one after

@@ -167,14 +167,19 @@ def test_chunked_schedule_planning(lib):
         assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
 
 
-def test_residual_update_runs_sequentially(lib):
-    """The residual update has no chunked form: AUTO plans the sequential
-    schedule (no workspace) where the additive update would chunk, and an
-    explicit CHUNKED request is refused before anything runs."""
+def test_residual_update_schedules(lib):
+    """The residual update plans like the additive one: AUTO chunks few long
+    chains at d = 64 (with its own state-pass buffers), stays sequential for
+    many chains, and an explicit CHUNKED request at d = 128 is refused."""
     n = ctypes.c_size_t(7)
     p = _params(lib, B=2, H=8, T=65536, nudge_period=1024, update=_lib.VLA_UPDATE_RESIDUAL)
-    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value > 0
+    auto = n.value
     p.schedule = _lib.VLA_SCHEDULE_CHUNKED
-    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
-    assert _scan(lib, p) == _lib.VLA_EUNSUPPORTED
-    assert "residual" in lib.vla_last_error().decode()
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == auto
+    p.update = _lib.VLA_UPDATE_ADDITIVE
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value != auto
+    q = _params(lib, B=64, H=8, T=512, update=_lib.VLA_UPDATE_RESIDUAL)
+    assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+    q = _params(lib, B=1, H=2, T=4096, d=128, schedule=_lib.VLA_SCHEDULE_CHUNKED, update=_lib.VLA_UPDATE_RESIDUAL)
+    assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED

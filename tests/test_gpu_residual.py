@@ -1,8 +1,11 @@
 """GPU parity of the residual (delta-rule) update against the fp64 oracle.
 
 The residual update ("Variational Linear Attention: Stable Associative Memory
-for Long-Context Transformers", technical summary 2.3) runs on the sequential
-schedule.  Every case calls libvla.so through the C ABI and compares with
+for Long-Context Transformers", technical summary 2.3) runs on both schedules:
+token by token, and time-parallel (d = 64: unit gates from the chunked inverse
+pass, per-block affine maps of the state, their chain and a parallel readout,
+with a sequential fallback for chains whose state exceeds the cap).  Every
+case calls libvla.so through the C ABI and compares with
 ``oracle_scan(..., update="residual")`` on the same seeded inputs, to the
 normwise bars of the additive scan (2e-3 float32 storage, 1e-2 bfloat16).
 """
@@ -64,14 +67,76 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("schedule", ["sequential", "auto"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_residual_parity_small(name):
+def test_residual_parity_small(name, schedule):
     cfg = SMALL[name]
-    _say(f"case small/{name}")
+    _say(f"case small/{name} {schedule}")
     x = case(cfg)
-    st = _check(cfg, _gpu(x, cfg), run_oracle(x, cfg, update="residual"))
+    st = _check(cfg, _gpu(x, cfg, schedule=schedule), run_oracle(x, cfg, update="residual"))
     if name == "long":
         assert st[:, 1].min() > 0, "the reduced long case is meant to exercise the cap"
+
+
+# Time-parallel schedule: (name, overrides, chunk length).  Ragged lengths,
+# several chunks and blocks, both storage types, a cap that never binds and
+# one that binds (its chains fall back to the sequential kernel).
+CHUNKED = [
+    ("long-bf16", dict(B=1, H=3, T=2053, nudge_period=128, s_cap=1e3), 64),
+    ("long-bf16-L128", dict(B=2, H=1, T=1000, nudge_period=256, s_cap=None), 128),
+    ("long-bf16-cap-binds", dict(B=1, H=2, T=700, nudge_period=64, s_cap=15.0), 64),
+    ("base-f32", dict(B=1, H=2, T=1500, nudge_period=256, s_cap=1e3), 256),
+    ("base-f32-r2", dict(B=1, H=2, T=777, nudge_period=0, s_cap=None, r=2), 64),
+    ("base-f32-short", dict(B=2, H=2, T=65, nudge_period=0, s_cap=None), 16),
+]
+
+
+@pytest.mark.parametrize("name,over,L", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_residual_chunked_matches_oracle(name, over, L):
+    base = CONFIGS["long"] if name.startswith("long") else CONFIGS["base"]
+    cfg = base.with_(name=f"res-chunked-{name}", **over)
+    _say(f"case chunked/{name} L={L}")
+    x = case(cfg, seed=11)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L)
+    ref = run_oracle(x, cfg, update="residual")
+    st = _check(cfg, out, ref)
+    if "cap-binds" in name:
+        assert (ref["cap_fires"] > 0).all() and (st[:, 1] > 0).all()
+    else:
+        assert (ref["cap_fires"] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_residual_chunked_initial_state_offset_and_in_place(dtype):
+    cfg = CONFIGS["long"].with_(name=f"res-chunked-state-{dtype}", B=1, H=2, T=640, nudge_period=128,
+                                s_cap=1e3, in_dtype=dtype)
+    x = case(cfg, seed=12)
+    g = torch.Generator().manual_seed(12)
+    d = cfg.d
+    A0 = torch.eye(d).expand(1, 2, d, d) * 0.5 + 0.01 * torch.randn(1, 2, d, d, generator=g)
+    A0 = ((A0 + A0.transpose(-1, -2)) / 2).contiguous()
+    S0 = torch.randn(1, 2, d, d, generator=g)
+    n0 = torch.rand(1, 2, d, generator=g)
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, d, d), S0=S0.reshape(2, d, d), n0=n0.reshape(2, d), t0=128,
+                     update="residual")
+    A, S, n = A0.to(DEV), S0.to(DEV), n0.to(DEV)
+    o = torch.empty_like(x["q"]).to(DEV)
+    st = torch.empty(1, 2, 4, device=DEV, dtype=torch.int32)
+    scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["u"].to(DEV), A, S, n,
+                 nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, t0=128, schedule="chunked", chunk_len=64,
+                 update="residual", out=(o, A, S, n, st))
+    torch.cuda.synchronize()
+    _check(cfg, (o, A, S, n, st), ref)
+
+
+def test_residual_chunked_agrees_with_sequential():
+    cfg = CONFIGS["long"].with_(name="res-chunked-vs-seq", B=2, H=2, T=1536, nudge_period=256, s_cap=1e3)
+    x = case(cfg, seed=13)
+    a = _gpu(x, cfg, schedule="sequential")
+    b = _gpu(x, cfg, schedule="chunked", chunk_len=256)
+    assert rel_err(b[0], a[0].float().cpu().numpy()) <= 1e-2
+    assert rel_err(b[2], a[2].cpu().numpy(), axes=(-2, -1)) <= 2e-3
+    assert rel_err(b[1], a[1].cpu().numpy(), axes=(-2, -1)) <= 2e-3
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
@@ -123,12 +188,14 @@ def test_residual_resume_in_place():
     assert rel_err(A, whole[1].cpu().numpy(), axes=(-2, -1)) <= 1e-5
 
 
-def test_residual_bitwise_repeatable_and_chunked_refused():
+def test_residual_bitwise_repeatable_and_chunked_d128_refused():
     cfg = CONFIGS["base"].with_(name="res-repeat", B=2, H=2, T=200)
     x = case(cfg, seed=3)
     a, b = _gpu(x, cfg), _gpu(x, cfg)
     for ta, tb in zip(a, b):
         assert torch.equal(ta, tb)
+    cfg = CONFIGS["wide"].with_(name="res-d128", B=1, H=1, T=64, r=1)
+    x = case(cfg, seed=3)
     with pytest.raises(VLAError) as e:
         _gpu(x, cfg, schedule="chunked")
     assert e.value.status == VLA_EUNSUPPORTED
