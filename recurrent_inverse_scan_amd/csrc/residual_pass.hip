@@ -25,8 +25,8 @@
 //    Y_{b+1} = Y_b + N^T Y_b + Q^T for Y = S^T, one 64x64x64 product per
 //    block on the bf16 matrix cores with three-term splits of the fp32
 //    operands (four waves, one 32x32 tile of Y each; the two waves of a
-//    column block swap tiles through LDS).  Stores S_b and the block-start
-//    normaliser for the readout.
+//    column block swap tiles through LDS).  Stores S_b for the readout; a
+//    small kernel beside it sums the key sums into block-start normalisers.
 //  * vla_res_readout_kernel, parallel over blocks: E = U - W S_b^T, then the
 //    block's tokens in order, S_t = S_{t-1} + e_t alpha_t^T,
 //    o_t = S_t q_t / (n_t . q_t + den_eps) and, with the cap on, |S_t|_F:
@@ -39,6 +39,8 @@
 
 namespace vla {
 namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 64;        // head dimension
 constexpr int kB = 64;        // tokens per block
@@ -122,10 +124,11 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
     float x[kB];
 #pragma unroll
     for (int t = 0; t < kB; ++t) {
-      float acc = col[t * kP];
+      // Four interleaved partial sums keep the FMAs independent.
+      float acc[4] = {col[t * kP], 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < t; ++s) acc = fmaf(-sL[t * kP + s], x[s], acc);
-      x[t] = acc;
+      for (int s = 0; s < t; ++s) acc[s & 3] = fmaf(-sL[t * kP + s], x[s], acc[s & 3]);
+      x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
 #pragma unroll
     for (int t = 0; t < kB; ++t) col[t * kP] = x[t];
@@ -184,14 +187,15 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
     dst[128] = __builtin_bit_cast(uint4, sp.t3);
   }
   // Q^T in accumulator order: tile w = jb + 2 c, lane l = (h, i), slot s holds
-  // Q^T[32 jb + acc_row(s, h)][32 c + i] = Q[32 c + i][32 jb + acc_row(s, h)].
+  // Q^T[32 jb + acc_row(s, h)][32 c + i] = Q[32 c + i][32 jb + acc_row(s, h)];
+  // stored as [w][q][lane] float4 of slots 4 q .. 4 q + 3.
   {
     const int w = tid >> 6, lane = tid & 63, h = lane >> 5, i = lane & 31;
     const int jb = w & 1, c = w >> 1;
-    float4* dst = reinterpret_cast<float4*>(pl.QT + ((blk * 4 + w) * 64 + lane) * 16);
+    float4* dst = reinterpret_cast<float4*>(pl.QT + blk * kD * kD) + w * 256 + lane;
     const float* src = sK + (32 * c + i) * kP + 32 * jb + 4 * h;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = *reinterpret_cast<const float4*>(src + 8 * q);
+    for (int q = 0; q < 4; ++q) dst[64 * q] = *reinterpret_cast<const float4*>(src + 8 * q);
   }
 }
 
@@ -199,41 +203,122 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
 // Chain: one workgroup of four waves per chain.  Wave w owns tile
 // (jb, c) = (w & 1, w >> 1) of Y = S^T in accumulator layout: lane l = (h, i),
 // slot s holds Y[32 jb + acc_row(s, h)][32 c + i] = S[32 c + i][32 jb + acc_row(s, h)].
+//
+// A block's operands (N^T fragments of both row blocks, 24 KiB, and Q^T,
+// 16 KiB) travel by buffer-to-LDS copies into a three-slot ring, issued two
+// blocks ahead, ten 1 KiB pieces per wave.  Each wave waits for its own copies
+// of the next block with a counted s_waitcnt before the block's closing
+// barrier (a bare s_barrier: __syncthreads would also drain the copies
+// issued for the block after); per block a wave issues exactly ten copies and
+// four stores, so the copies for block b + 1, issued during block b - 1, are
+// complete once at most 14 of its memory operations are outstanding at the
+// end of block b.
 // ---------------------------------------------------------------------------
-struct ChainOperands {
-  uint4 n[2][2][3];   // N^T fragments [mb][g][term]
-  float4 q[4];        // Q^T tile
+constexpr int kRing = 3;
+constexpr int kSlotBytes = 40 * 1024;       // N^T fragments (24 KiB), then Q^T (16 KiB)
+constexpr int kSlotVecs = kSlotBytes / 16;
+constexpr int kXFloats = 4 * 16 * 64;       // each wave's Y tile, [wave][slot][lane]
+
+__device__ __forceinline__ void ring_copy(const ResPlan& pl, uint4 (&slot)[kSlotVecs], int64_t blk, int w, int lane) {
+  const auto rn = make_rsrc(pl.NTF + blk * 3 * kD * kD, 24 * 1024);
+  const auto rq = make_rsrc(pl.QT + blk * kD * kD, 16 * 1024);
+  char* base = reinterpret_cast<char*>(slot);
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int p = 10 * w + k;
+    if (p < 24) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void*)(base + 1024 * p), 16, 16 * lane, 1024 * p, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(base + 1024 * p), 16, 16 * lane, 1024 * (p - 24), 0,
+                                               0);
+    }
+  }
+}
+
+struct ChainLane {
+  int64_t chain, soff;
+  int nblk, w, lane, jb;
 };
 
-__device__ __forceinline__ void load_operands(ChainOperands& op, const ResPlan& pl, int64_t blk, int w, int jb,
-                                              int lane) {
-  const uint4* nf = reinterpret_cast<const uint4*>(pl.NTF);
+// Block b: copies for block b + 2 into `ahead`, operands from `cur`, the
+// partner's tile from `xr`, this wave's new tile to `xw`.  Distinct LDS
+// objects let the compiler see that reading `cur` does not wait for the
+// copies into `ahead`.
+__device__ __forceinline__ void chain_block(const ResPlan& pl, const ChainLane& cl, int b, f32x16& Y,
+                                            uint4 (&cur)[kSlotVecs], uint4 (&ahead)[kSlotVecs],
+                                            const float (&xr)[kXFloats], float (&xw)[kXFloats]) {
+  const int w = cl.w, lane = cl.lane, jb = cl.jb, nblk = cl.nblk;
+  const int64_t blk = cl.chain * nblk + b;
+  if (b + 2 < nblk) ring_copy(pl, ahead, blk + 2, w, lane);
+  f32x16 Yp;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int s = 0; s < 16; ++s) Yp[s] = xr[((w ^ 1) * 16 + s) * 64 + lane];
+  // The block-start state for the readout.
+  {
+    float* dst = pl.Ssnap + blk * kD * kD + cl.soff;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(dst + 8 * q) = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
+  }
+  // Y + Q^T + N^T Y: contraction block mb = jb pairs with this wave's own
+  // tile, mb = 1 - jb with its partner's.
+  const float4* qt = reinterpret_cast<const float4*>(cur + 24 * 64) + w * 256 + lane;
+  f32x16 acc0 = Y, acc1;
 #pragma unroll
-      for (int term = 0; term < 3; ++term)
-        op.n[mb][g][term] = nf[(((((blk * 2 + jb) * 2 + mb) * 2 + g) * 3 + term) * 64) + lane];
-  const float4* qt = reinterpret_cast<const float4*>(pl.QT + ((blk * 4 + w) * 64 + lane) * 16);
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = qt[64 * q];
+    acc1[4 * q] = x.x; acc1[4 * q + 1] = x.y; acc1[4 * q + 2] = x.z; acc1[4 * q + 3] = x.w;
+  }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) op.q[q] = qt[q];
+  for (int g = 0; g < 2; ++g) {
+    const Split3 b0 = split_slots(Y, g), b1 = split_slots(Yp, g);
+    Split3 a0, a1;
+    const int f0 = ((jb * 2 + jb) * 2 + g) * 3, f1 = ((jb * 2 + (1 - jb)) * 2 + g) * 3;
+    a0.t1 = __builtin_bit_cast(bf16x8, cur[(f0 + 0) * 64 + lane]);
+    a0.t2 = __builtin_bit_cast(bf16x8, cur[(f0 + 1) * 64 + lane]);
+    a0.t3 = __builtin_bit_cast(bf16x8, cur[(f0 + 2) * 64 + lane]);
+    a1.t1 = __builtin_bit_cast(bf16x8, cur[(f1 + 0) * 64 + lane]);
+    a1.t2 = __builtin_bit_cast(bf16x8, cur[(f1 + 1) * 64 + lane]);
+    a1.t3 = __builtin_bit_cast(bf16x8, cur[(f1 + 2) * 64 + lane]);
+    acc0 = mma_split(a0, b0, acc0);
+    acc1 = mma_split(a1, b1, acc1);
+  }
+#pragma unroll
+  for (int s = 0; s < 16; ++s) Y[s] = acc0[s] + acc1[s];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) xw[(w * 16 + s) * 64 + lane] = Y[s];
+  // The next block's operands (copied during block b - 1) have landed once
+  // at most this block's ten copies and four stores are outstanding, in
+  // whichever order the two were issued.
+  if (b >= 1 && b + 2 < nblk)
+    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const float* __restrict__ S_in,
-                                                            const float* __restrict__ n_in, float* __restrict__ S_T,
-                                                            float* __restrict__ n_T, int32_t* __restrict__ stats,
+                                                            float* __restrict__ S_T, int32_t* __restrict__ stats,
                                                             const int32_t* __restrict__ chain_info) {
-  __shared__ float xbuf[2][4][16][64];   // each wave's Y tile, double-buffered, [slot][lane]
-  const int64_t chain = blockIdx.x;
-  const int nblk = pl.nblk;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, i = lane & 31;
+  __shared__ uint4 sR0[kSlotVecs], sR1[kSlotVecs], sR2[kSlotVecs];   // operand ring
+  __shared__ float sX0[kXFloats], sX1[kXFloats];                     // tile exchange, by block parity
+  __shared__ int sbad[4];
+  ChainLane cl;
+  cl.chain = blockIdx.x;
+  cl.nblk = pl.nblk;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, i = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar copy offsets
   const int jb = w & 1, c = w >> 1;
-  const int64_t soff = (32 * c + i) * kD + 32 * jb + 4 * h;   // this lane's S entries: soff + 8 q + 0..3
+  cl.w = w;
+  cl.lane = lane;
+  cl.jb = jb;
+  cl.soff = (32 * c + i) * kD + 32 * jb + 4 * h;   // this lane's S entries: soff + 8 q + 0..3
+  const int64_t chain = cl.chain;
+  const int nblk = cl.nblk;
 
   f32x16 Y;
   {
-    const float* src = S_in + chain * kD * kD + soff;
+    const float* src = S_in + chain * kD * kD + cl.soff;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 x = *reinterpret_cast<const float4*>(src + 8 * q);
@@ -241,64 +326,25 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const fl
     }
   }
 #pragma unroll
-  for (int s = 0; s < 16; ++s) xbuf[0][w][s][lane] = Y[s];
-  float nval = w == 0 ? n_in[chain * kD + lane] : 0.f;
-  ChainOperands cur, nxt;
-  if (nblk > 0) load_operands(cur, pl, chain * nblk, w, jb, lane);
+  for (int s = 0; s < 16; ++s) sX0[(w * 16 + s) * 64 + lane] = Y[s];
+  ring_copy(pl, sR0, chain * nblk, w, lane);
+  if (nblk > 1) ring_copy(pl, sR1, chain * nblk + 1, w, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int b = 0; b < nblk; ++b) {
-    const int p = b & 1;
-    const int64_t blk = chain * nblk + b;
-    f32x16 Yp;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) Yp[s] = xbuf[p][w ^ 1][s][lane];
-    if (b + 1 < nblk) load_operands(nxt, pl, blk + 1, w, jb, lane);
-    // The block-start state for the readout.
-    {
-      float* dst = pl.Ssnap + blk * kD * kD + soff;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(dst + 8 * q) = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
-    }
-    if (w == 0) {
-      pl.nblock[blk * kD + lane] = nval;
-      nval += pl.ksum[blk * kD + lane];
-    }
-    // Y + Q^T + N^T Y: contraction block mb uses Y's tile (mb, c), which is
-    // this wave's own for mb = jb and its partner's otherwise.
-    f32x16 acc0 = Y, acc1 = zero16();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc0[4 * q] += cur.q[q].x; acc0[4 * q + 1] += cur.q[q].y;
-      acc0[4 * q + 2] += cur.q[q].z; acc0[4 * q + 3] += cur.q[q].w;
-    }
-    const f32x16 B0 = jb == 0 ? Y : Yp;
-    const f32x16 B1 = jb == 0 ? Yp : Y;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const Split3 b0 = split_slots(B0, g), b1 = split_slots(B1, g);
-      Split3 a0, a1;
-      a0.t1 = __builtin_bit_cast(bf16x8, cur.n[0][g][0]);
-      a0.t2 = __builtin_bit_cast(bf16x8, cur.n[0][g][1]);
-      a0.t3 = __builtin_bit_cast(bf16x8, cur.n[0][g][2]);
-      a1.t1 = __builtin_bit_cast(bf16x8, cur.n[1][g][0]);
-      a1.t2 = __builtin_bit_cast(bf16x8, cur.n[1][g][1]);
-      a1.t3 = __builtin_bit_cast(bf16x8, cur.n[1][g][2]);
-      acc0 = mma_split(a0, b0, acc0);
-      acc1 = mma_split(a1, b1, acc1);
-    }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) Y[s] = acc0[s] + acc1[s];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) xbuf[p ^ 1][w][s][lane] = Y[s];
-    if (b + 1 < nblk) cur = nxt;
-    __syncthreads();
+  // Block b reads ring slot b % 3 and exchange buffer b % 2.
+  for (int b = 0; b < nblk; b += 6) {
+    chain_block(pl, cl, b, Y, sR0, sR2, sX0, sX1);
+    if (b + 1 < nblk) chain_block(pl, cl, b + 1, Y, sR1, sR0, sX1, sX0);
+    if (b + 2 < nblk) chain_block(pl, cl, b + 2, Y, sR2, sR1, sX0, sX1);
+    if (b + 3 < nblk) chain_block(pl, cl, b + 3, Y, sR0, sR2, sX1, sX0);
+    if (b + 4 < nblk) chain_block(pl, cl, b + 4, Y, sR1, sR0, sX0, sX1);
+    if (b + 5 < nblk) chain_block(pl, cl, b + 5, Y, sR2, sR1, sX1, sX0);
   }
 
   bool bad = false;
   {
-    float* dst = S_T + chain * kD * kD + soff;
+    float* dst = S_T + chain * kD * kD + cl.soff;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 x = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
@@ -306,39 +352,104 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const fl
       *reinterpret_cast<float4*>(dst + 8 * q) = x;
     }
   }
-  if (w == 0) {
-    n_T[chain * kD + lane] = nval;
-    bad |= !isfinite(nval);
-  }
   const bool wave_bad = __any(bad);
-  __syncthreads();
-  __shared__ int sbad[4];
   if (lane == 0) sbad[w] = wave_bad ? 1 : 0;
   __syncthreads();
   if (tid == 0 && stats) {
-    int32_t* s = stats + chain * 4;
-    s[0] = chain_info[chain * 4 + kInfoGuard];
-    s[1] = 0;
-    s[2] = (sbad[0] | sbad[1] | sbad[2] | sbad[3] | chain_info[chain * 4 + kInfoNonfinite]) ? 1 : 0;
-    s[3] = -1;
+    int32_t* st = stats + chain * 4;
+    st[0] = chain_info[chain * 4 + kInfoGuard];
+    st[1] = 0;
+    st[2] = (sbad[0] | sbad[1] | sbad[2] | sbad[3] | chain_info[chain * 4 + kInfoNonfinite]) ? 1 : 0;
+    st[3] = -1;
+  }
+}
+
+// Normalisers at block starts, n_b = n_0 + sum_{b' < b} (key sum of b'), and
+// n_T: one workgroup of 1024 threads per chain, thread (g, f) = (tid >> 6,
+// tid & 63) takes feature f over the blocks of segment g of 16.
+__global__ void __launch_bounds__(1024) vla_res_nprefix_kernel(ResPlan pl, const float* __restrict__ n_in,
+                                                               float* __restrict__ n_T) {
+  __shared__ float part[16][kD];
+  const int64_t chain = blockIdx.x;
+  const int nblk = pl.nblk;
+  const int f = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int per = (nblk + 15) / 16;
+  const int lo = min(nblk, g * per), hi = min(nblk, lo + per);
+  const float* ks = pl.ksum + chain * nblk * kD + f;
+  float sum = 0.f;
+  for (int b = lo; b < hi; ++b) sum += ks[b * kD];
+  part[g][f] = sum;
+  __syncthreads();
+  float n = n_in[chain * kD + f];
+  for (int x = 0; x < g; ++x) n += part[x][f];
+  float* nb = pl.nblock + chain * nblk * kD + f;
+  for (int b = lo; b < hi; ++b) {
+    nb[b * kD] = n;
+    n += ks[b * kD];
+  }
+  if (g == 15) {
+    float t = n_in[chain * kD + f];
+    for (int x = 0; x < 16; ++x) t += part[x][f];
+    n_T[chain * kD + f] = t;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Readout: one workgroup of 512 threads per (chain, block).  Thread tid owns
-// row i = tid >> 3 of S and the columns (tid & 7) + 8 m, m = 0..7.
+// Readout: one workgroup of 512 threads per (chain, block).  In the token
+// loop thread tid owns row i = tid >> 3 of S and the eight consecutive
+// columns 8 (tid & 7) .. 8 (tid & 7) + 7.
 // ---------------------------------------------------------------------------
+// 16 bytes of a [64][64] row-major block (index v of 1024 float4 / 512
+// 8-value bf16 chunks) into a padded LDS matrix as fp32.
+__device__ __forceinline__ void put4(float* m, int v, float4 x) {
+  *reinterpret_cast<float4*>(m + (v >> 4) * kP + 4 * (v & 15)) = x;
+}
+__device__ __forceinline__ void put8(float* m, int v, uint4 x) {
+  float* dst = m + (v >> 3) * kP + 8 * (v & 7);
+  *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                                                __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+  *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xffff0000u),
+                                                    __uint_as_float(x.w << 16), __uint_as_float(x.w & 0xffff0000u));
+}
+
+// Rows [0, nvalid) of a [64][64] block of token vectors in the storage dtype,
+// as fp32 into a padded LDS matrix; rows past nvalid read as zero.
+template <typename TIn>
+struct TokRows {
+  static constexpr int kVecs = sizeof(TIn) == 4 ? 2 : 1;   // 16-byte vectors per thread
+  uint4 r[kVecs];
+  __device__ __forceinline__ void load(const TIn* g, int nvalid, int tid) {
+    constexpr int kPerVec = 16 / sizeof(TIn);
+#pragma unroll
+    for (int x = 0; x < kVecs; ++x) {
+      const int v = tid + 512 * x;
+      r[x] = (v * kPerVec) / kD < nvalid ? reinterpret_cast<const uint4*>(g)[v] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void put(float* m, int tid) const {
+#pragma unroll
+    for (int x = 0; x < kVecs; ++x) {
+      const int v = tid + 512 * x;
+      if constexpr (sizeof(TIn) == 4) {
+        put4(m, v, make_float4(__uint_as_float(r[x].x), __uint_as_float(r[x].y), __uint_as_float(r[x].z),
+                               __uint_as_float(r[x].w)));
+      } else {
+        put8(m, v, r[x]);
+      }
+    }
+  }
+};
+
 template <typename TIn, bool CAP>
 __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float den_eps, float cap2, int chains,
                                                               int32_t* __restrict__ chain_info) {
   extern __shared__ float4 smem4[];
-  float* sS = reinterpret_cast<float*>(smem4);   // S_b
-  float* sE = sS + kMat;                          // U, then E
-  float* sX = sE + kMat;                          // W, then k, then n_t, then o
-  float* sA = sX + kMat;                          // alpha
-  float* sQ = sA + kMat;                          // q
+  float* R0 = reinterpret_cast<float*>(smem4);   // S_b, then q
+  float* R1 = R0 + kMat;                          // W, then k, then o
+  float* R2 = R1 + kMat;                          // U, then E
+  float* R3 = R2 + kMat;                          // alpha
   __shared__ float sDen[kB];
-  __shared__ float sNorm[kB][32];                 // per-token partial |S_t|^2 of each 16-lane row
+  __shared__ float sNorm[kB][32];                 // per-token partial |S_t|^2 of each 16-lane group
   __shared__ float sNb[kD];
 
   const int nblk = pl.nblk;
@@ -351,85 +462,119 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   const int64_t blk = chain * nblk + b;
   const int64_t tok0 = chain * pl.T + t0;
 
-  // Phase 1: E = U - W S_b^T.
-  for (int e = tid; e < kB * kD; e += 512) {
-    const int t = e >> 6, j = e & 63;
-    sS[t * kP + j] = pl.Ssnap[blk * kD * kD + e];
-    sE[t * kP + j] = pl.U[blk * kB * kD + e];
-    sX[t * kP + j] = pl.W[blk * kB * kD + e];
-  }
-  if (tid < kD) sNb[tid] = pl.nblock[blk * kD + tid];
-  __syncthreads();
+  // Every global load up front: S_b, W, U, alpha (fp32) and q, k.
+  float4 gS[2], gW[2], gU[2], gA[2];
   {
-    const int t = tid >> 3;
+    const float4* s4 = reinterpret_cast<const float4*>(pl.Ssnap + blk * kD * kD);
+    const float4* w4 = reinterpret_cast<const float4*>(pl.W + blk * kB * kD);
+    const float4* u4 = reinterpret_cast<const float4*>(pl.U + blk * kB * kD);
+    const float4* a4 = reinterpret_cast<const float4*>(pl.alpha + tok0 * kD);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int v = tid + 512 * x;
+      gS[x] = s4[v];
+      gW[x] = w4[v];
+      gU[x] = u4[v];
+      gA[x] = (v >> 4) < nvalid ? a4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  TokRows<TIn> gq, gk;
+  gq.load(static_cast<const TIn*>(pl.q) + tok0 * kD, nvalid, tid);
+  gk.load(static_cast<const TIn*>(pl.k) + tok0 * kD, nvalid, tid);
+  if (tid < kD) sNb[tid] = pl.nblock[blk * kD + tid];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    put4(R0, tid + 512 * x, gS[x]);
+    put4(R1, tid + 512 * x, gW[x]);
+    put4(R2, tid + 512 * x, gU[x]);
+    put4(R3, tid + 512 * x, gA[x]);
+  }
+  __syncthreads();
+
+  // E = U - W S_b^T: thread (t, jc) computes E[t][jc + 8 m], m = 0..7.
+  const int i = tid >> 3, jc = tid & 7;
+  {
+    const int t = i;
     float acc[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = sE[t * kP + (tid & 7) + 8 * m];
-    for (int j = 0; j < kD; ++j) {
-      const float wv = sX[t * kP + j];
+    for (int m = 0; m < 8; ++m) acc[m] = R2[t * kP + jc + 8 * m];
+#pragma unroll 4
+    for (int j = 0; j < kD; j += 4) {
+      const float4 wv = *reinterpret_cast<const float4*>(R1 + t * kP + j);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] = fmaf(-wv, sS[((tid & 7) + 8 * m) * kP + j], acc[m]);
+      for (int m = 0; m < 8; ++m) {
+        const float4 sv = *reinterpret_cast<const float4*>(R0 + (jc + 8 * m) * kP + j);
+        acc[m] = fmaf(-wv.x, sv.x, acc[m]);
+        acc[m] = fmaf(-wv.y, sv.y, acc[m]);
+        acc[m] = fmaf(-wv.z, sv.z, acc[m]);
+        acc[m] = fmaf(-wv.w, sv.w, acc[m]);
+      }
     }
+    __syncthreads();   // every thread has read its U entries before E overwrites them
 #pragma unroll
-    for (int m = 0; m < 8; ++m) sE[t * kP + (tid & 7) + 8 * m] = acc[m];
+    for (int m = 0; m < 8; ++m) R2[t * kP + jc + 8 * m] = acc[m];
   }
+  // This thread's row of S_b for the token loop.
+  float S[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(R0 + i * kP + 8 * jc);
+    const float4 c = *reinterpret_cast<const float4*>(R0 + i * kP + 8 * jc + 4);
+    S[0] = a.x; S[1] = a.y; S[2] = a.z; S[3] = a.w; S[4] = c.x; S[5] = c.y; S[6] = c.z; S[7] = c.w;
+  }
+  __syncthreads();
+  gq.put(R0, tid);
+  gk.put(R1, tid);
   __syncthreads();
 
-  // Phase 2: alpha, q, k; the normalisers n_t = n_b + sum_{s<=t} k_s and the
-  // denominators n_t . q_t + den_eps.
-  const TIn* qg = static_cast<const TIn*>(pl.q) + tok0 * kD;
-  const TIn* kg = static_cast<const TIn*>(pl.k) + tok0 * kD;
-  for (int e = tid; e < kB * kD; e += 512) {
-    const int t = e >> 6, j = e & 63;
-    float qv = 0.f, kv = 0.f, av = 0.f;
-    if (t < nvalid) {
-      qv = Elem<TIn>::load(qg + e);
-      kv = Elem<TIn>::load(kg + e);
-      av = pl.alpha[tok0 * kD + e];
-    }
-    sQ[t * kP + j] = qv;
-    sX[t * kP + j] = kv;
-    sA[t * kP + j] = av;
-  }
-  __syncthreads();
-  if (tid < kD) {
-    float nv = sNb[tid];
-    for (int t = 0; t < kB; ++t) {
-      nv += sX[t * kP + tid];
-      sX[t * kP + tid] = nv;
-    }
-  }
-  __syncthreads();
+  // Denominators n_t . q_t + den_eps, n_t = n_b + sum_{s<=t} k_s: thread
+  // (t, jc) takes n_b's features 8 jc .. 8 jc + 7 and the keys s = jc + 8 m <= t.
   {
-    const int t = tid >> 3;
+    const int t = i;
     float d = 0.f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) d = fmaf(sX[t * kP + (tid & 7) + 8 * m], sQ[t * kP + (tid & 7) + 8 * m], d);
+    for (int e = 0; e < 8; ++e) d = fmaf(sNb[8 * jc + e], R0[t * kP + 8 * jc + e], d);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int s = jc + 8 * m;
+      if (s <= t) {
+#pragma unroll 4
+        for (int j = 0; j < kD; j += 4) {
+          const float4 qv = *reinterpret_cast<const float4*>(R0 + t * kP + j);
+          const float4 kv = *reinterpret_cast<const float4*>(R1 + s * kP + j);
+          d = fmaf(qv.x, kv.x, d);
+          d = fmaf(qv.y, kv.y, d);
+          d = fmaf(qv.z, kv.z, d);
+          d = fmaf(qv.w, kv.w, d);
+        }
+      }
+    }
     d = group_sum<8>(d);
-    if ((tid & 7) == 0) sDen[t] = d + den_eps;
+    if (jc == 0) sDen[t] = d + den_eps;
   }
   __syncthreads();
 
-  // Phase 3: the block's tokens in order.
-  const int i = tid >> 3, jc = tid & 7;
-  float S[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) S[m] = sS[i * kP + jc + 8 * m];
+  // The block's tokens in order: S_t = S_{t-1} + e_t alpha_t^T, o_t, |S_t|^2.
   bool bad = false;
   for (int t = 0; t < nvalid; ++t) {
-    const float ev = sE[t * kP + i];
+    const float ev = R2[t * kP + i];
+    const float4 a0 = *reinterpret_cast<const float4*>(R3 + t * kP + 8 * jc);
+    const float4 a1 = *reinterpret_cast<const float4*>(R3 + t * kP + 8 * jc + 4);
+    const float4 q0 = *reinterpret_cast<const float4*>(R0 + t * kP + 8 * jc);
+    const float4 q1 = *reinterpret_cast<const float4*>(R0 + t * kP + 8 * jc + 4);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     float po = 0.f, ns = 0.f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      S[m] = fmaf(ev, sA[t * kP + jc + 8 * m], S[m]);
-      po = fmaf(S[m], sQ[t * kP + jc + 8 * m], po);
+      S[m] = fmaf(ev, av[m], S[m]);
+      po = fmaf(S[m], qv[m], po);
       if constexpr (CAP) ns = fmaf(S[m], S[m], ns);
     }
     po = group_sum<8>(po);
     if (jc == 0) {
       const float ov = po / sDen[t];
       bad |= !isfinite(ov);
-      sX[t * kP + i] = ov;
+      R1[t * kP + i] = ov;
     }
     if constexpr (CAP) {
       ns = group_sum<16>(ns);
@@ -439,8 +584,25 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   __syncthreads();
 
   // Outputs, and the cap test on every token's |S_t|_F.
-  TIn* og = static_cast<TIn*>(pl.o) + tok0 * kD;
-  for (int e = tid; e < nvalid * kD; e += 512) Elem<TIn>::store(og + e, sX[(e >> 6) * kP + (e & 63)]);
+  {
+    TIn* og = static_cast<TIn*>(pl.o) + tok0 * kD;
+    const int t = tid >> 3, c8 = 8 * (tid & 7);
+    if (t < nvalid) {
+      const float4 x0 = *reinterpret_cast<const float4*>(R1 + t * kP + c8);
+      const float4 x1 = *reinterpret_cast<const float4*>(R1 + t * kP + c8 + 4);
+      if constexpr (sizeof(TIn) == 4) {
+        *reinterpret_cast<float4*>(og + t * kD + c8) = x0;
+        *reinterpret_cast<float4*>(og + t * kD + c8 + 4) = x1;
+      } else {
+        const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          wv[e] = static_cast<uint32_t>(f32_to_bf16(f[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * e + 1])) << 16);
+        *reinterpret_cast<uint4*>(og + t * kD + c8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+    }
+  }
   bool over = false;
   if constexpr (CAP) {
     if (tid < nvalid) {
@@ -481,10 +643,13 @@ hipError_t launch_res_prep(const ResPlan& pl, int chains, hipStream_t stream) {
 hipError_t launch_res_chain(const ResPlan& pl, const float* S_in, const float* n_in, float* S_T, float* n_T,
                             int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop) {
-  hipError_t e = hipSuccess;
+  hipLaunchKernelGGL(vla_res_nprefix_kernel, dim3(static_cast<unsigned>(chains)), dim3(1024), 0, stream, pl, n_in,
+                     n_T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (ev_start && (e = hipEventRecord(ev_start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(vla_res_chain_kernel, dim3(static_cast<unsigned>(chains)), dim3(256), 0, stream, pl, S_in, n_in,
-                     S_T, n_T, stats, chain_info);
+  hipLaunchKernelGGL(vla_res_chain_kernel, dim3(static_cast<unsigned>(chains)), dim3(256), 0, stream, pl, S_in,
+                     S_T, stats, chain_info);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_stop) e = hipEventRecord(ev_stop, stream);
   return e;
@@ -492,7 +657,7 @@ hipError_t launch_res_chain(const ResPlan& pl, const float* S_in, const float* n
 
 hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains,
                               int32_t* chain_info, hipStream_t stream) {
-  const size_t lds = 5 * kMat * sizeof(float);
+  const size_t lds = 4 * kMat * sizeof(float);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(chains) * pl.nblk));
   const float cap2 = cap * cap;
 #define VLA_RES_READOUT(T, C)                                                                             \

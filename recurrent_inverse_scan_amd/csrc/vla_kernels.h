@@ -134,7 +134,7 @@ struct ResPlan {
   float* W;              // [chains][nblk][64][64] (I + L)^{-1} K_hat
   float* U;              // [chains][nblk][64][64] (I + L)^{-1} V
   uint16_t* NTF;         // [chains][nblk][2][2][2][3][64][8] N^T as split bf16 matrix-core operands
-  float* QT;             // [chains][nblk][4][64][16] Q^T in accumulator order
+  float* QT;             // [chains][nblk][4 tiles][4][64 lanes][4] Q^T in accumulator order
   float* ksum;           // [chains][nblk][64] sum of the block's keys
   float* Ssnap;          // [chains][nblk][64][64] S at each block start
   float* nblock;         // [chains][nblk][64] normaliser at each block start

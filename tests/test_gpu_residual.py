@@ -88,6 +88,8 @@ CHUNKED = [
     ("base-f32", dict(B=1, H=2, T=1500, nudge_period=256, s_cap=1e3), 256),
     ("base-f32-r2", dict(B=1, H=2, T=777, nudge_period=0, s_cap=None, r=2), 64),
     ("base-f32-short", dict(B=2, H=2, T=65, nudge_period=0, s_cap=None), 16),
+    ("base-f32-one-block", dict(B=1, H=3, T=40, nudge_period=0, s_cap=None), 16),
+    ("long-bf16-seven-blocks", dict(B=1, H=2, T=416, nudge_period=32, s_cap=1e3), 32),
 ]
 
 
