@@ -20,6 +20,10 @@ changed since they were taken.  ``scan_valu_frac`` is the
 whole scan's algorithmic flops 2 (2r+3) d^2 per token*head against the fp32
 vector peak.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded prefix
 of the same workload.
+
+``--update residual`` times the residual (delta-rule) update on the same
+workload instead (its chunked schedule's dominant kernel is the residual
+chain kernel); the headline line is the default additive update.
 """
 from __future__ import annotations
 
@@ -40,36 +44,52 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3   # 256 CU x 4 SIMD x 16 lanes x 2 (dual fp32) x
 HBM_PEAK_GBS = 8000.0
 
 
-CHAIN_SOURCES = ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "state_chain_long_traffic.md")
+# The dominant kernel of each update's chunked schedule, the sources it is
+# built from, and the committed counter summary of its HBM traffic.
+CHAIN = {
+    "additive": ("vla_state_chain_kernel",
+                 ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h"),
+                 os.path.join(ROOT, "profiles", "state_chain_long_traffic.md")),
+    "residual": ("vla_res_chain_kernel",
+                 ("residual_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h"),
+                 os.path.join(ROOT, "profiles", "residual_chain_long_traffic.md")),
+}
 
 
-def alg_flops_per_token_head(d: int, r: int) -> int:
-    return 2 * (2 * r + 3) * d * d
+def alg_flops_per_token_head(d: int, r: int, update: str = "additive") -> int:
+    """2 (2r + 3) d^2: r rank-1 updates (product and update, 2 d^2 each), the
+    coefficient A k, the state update and the readout; the residual update
+    adds the prediction S k_hat (one more d^2 product)."""
+    return 2 * (2 * r + 3 + (1 if update == "residual" else 0)) * d * d
 
 
-def chain_flops_per_token_head(d: int, cap_on: bool) -> int:
-    """Memory update S += v alpha^T (d^2 FMA) plus the cap's |S|^2 (d^2 FMA)."""
+def chain_flops_per_token_head(d: int, cap_on: bool, update: str = "additive") -> int:
+    """The state recurrence the chain kernel carries: additive, the memory
+    update S += v alpha^T (d^2 FMA) plus the cap's |S|^2 (d^2 FMA); residual,
+    the prediction S k_hat and the update (2 d^2 FMA; its cap test runs in
+    the readout)."""
+    if update == "residual":
+        return 4 * d * d
     return 2 * d * d + (2 * d * d if cap_on else 0)
 
 
-def chain_source_sha() -> str:
+def chain_source_sha(update: str = "additive") -> str:
     h = hashlib.sha256()
-    for name in CHAIN_SOURCES:
+    for name in CHAIN[update][1]:
         with open(os.path.join(ROOT, "recurrent_inverse_scan_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(update: str = "additive"):
     """HBM bytes per launch of the chain kernel from the committed counter
     summary, if it was taken on the current kernel sources."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(CHAIN[update][2]).read()
     except OSError:
         return None
     vals = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
-    if vals.get("source_sha256") != chain_source_sha():
+    if vals.get("source_sha256") != chain_source_sha(update):
         return None
     try:
         return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
@@ -83,6 +103,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="long")
+    ap.add_argument("--update", default="additive", choices=("additive", "residual"),
+                    help="state update of the timed scan (the headline is the additive update)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,7 +134,8 @@ def main(argv=None) -> int:
     u = torch.empty((B, H, T, r, d), device=dev, dtype=q.dtype)
     outs = (torch.empty_like(q), torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d, d), device=dev),
             torch.empty((B, H, d), device=dev), torch.empty((B, H, 4), device=dev, dtype=torch.int32))
-    ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+    upd = args.update
+    ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, update=upd)
     schedule = "chunked" if ws_bytes > 0 else "sequential"
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     torch.cuda.synchronize()
@@ -121,7 +144,7 @@ def main(argv=None) -> int:
         project_u(W, kr, out=u)
         if ev is not None:
             ev[0].record()
-        scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=outs, workspace=ws)
+        scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=outs, workspace=ws, update=upd)
         if ev is not None:
             ev[1].record()
 
@@ -161,18 +184,18 @@ def main(argv=None) -> int:
 
     tok_heads = B * H * T
     value = tok_heads / (ms_per_step * 1e-3)
-    flops = alg_flops_per_token_head(d, r) * tok_heads
+    flops = alg_flops_per_token_head(d, r, upd) * tok_heads
     scan_tflops = flops / (scan_ms * 1e-3) / 1e12
     cap_on = cfg.s_cap is not None and cfg.s_cap > 0
-    chain_flops = chain_flops_per_token_head(d, cap_on) * tok_heads
+    chain_flops = chain_flops_per_token_head(d, cap_on, upd) * tok_heads
     if chain_ms:
         launch_ms = chain_ms / chain_launches   # mean launch: the segments differ in length
         launch_flops = chain_flops / chain_launches
         roofline = {"bound": "alu", "achieved": launch_flops / (launch_ms * 1e-3) / 1e12,
                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": launch_flops / (launch_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                    "traffic": measured_traffic(),
-                    "kernel": "vla_state_chain_kernel", "kernel_ms": launch_ms, "flops_per_launch": launch_flops,
+                    "traffic": measured_traffic(upd),
+                    "kernel": CHAIN[upd][0], "kernel_ms": launch_ms, "flops_per_launch": launch_flops,
                     "launches_per_step": chain_launches, "kernel_ms_per_step": chain_ms}
     else:   # the sequential schedule has no chain kernel: the scan kernel is the dominant one
         roofline = {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -183,11 +206,11 @@ def main(argv=None) -> int:
     scan_bytes = tok_heads * d * es * (4 + r) + 2 * B * H * (2 * d * d + d) * 4   # q,k,v,u in, o out, state
     stats = outs[4].cpu().numpy()
 
-    extra = None if args.no_extra else extra_measurements(CONFIGS, dev)
+    extra = None if (args.no_extra or upd != "additive") else extra_measurements(CONFIGS, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, x, args.cpu_baseline_seconds)
+        cpu = cpu_baseline(cfg, x, args.cpu_baseline_seconds, upd)
 
     line = {
         "metric": METRIC,
@@ -203,7 +226,9 @@ def main(argv=None) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: VLA scan B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
-                               f"f32 state, nudge every {cfg.nudge_period}, Frobenius cap {cfg.s_cap}",
+                               f"f32 state, nudge every {cfg.nudge_period}, Frobenius cap {cfg.s_cap}"
+                               + ("" if upd == "additive" else f", {upd} update"),
+                   "update": upd,
                    "B": B, "H": H, "T": T, "d": d, "r": r, "storage": cfg.in_dtype,
                    "nudge_period": cfg.nudge_period, "s_cap": cfg.s_cap, "schedule": schedule,
                    "workspace_bytes": ws_bytes},
@@ -309,7 +334,7 @@ def extra_measurements(CONFIGS, dev):
     return out
 
 
-def cpu_baseline(cfg, x, budget_s: float):
+def cpu_baseline(cfg, x, budget_s: float, update: str = "additive"):
     """Time the fp64 oracle on all chains over a bounded prefix of the tokens,
     with its BLAS held to one thread (the oracle's loops are single-threaded)."""
     from threadpoolctl import threadpool_limits
@@ -323,7 +348,8 @@ def cpu_baseline(cfg, x, budget_s: float):
         t0 = time.perf_counter()
         u = oracle_project_u(x["W_u"], kr.reshape(-1, d)).reshape(C, n_tok, r, d)
         oracle_scan(x["q"].reshape(C, cfg.T, d)[:, :n_tok], x["k"].reshape(C, cfg.T, d)[:, :n_tok],
-                    x["v"].reshape(C, cfg.T, d)[:, :n_tok], u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+                    x["v"].reshape(C, cfg.T, d)[:, :n_tok], u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap,
+                    update=update)
         return time.perf_counter() - t0
 
     with threadpool_limits(limits=1):
