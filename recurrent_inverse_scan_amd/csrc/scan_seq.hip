@@ -493,25 +493,38 @@ static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, h
                                                        : static_cast<unsigned>(chains);
   if constexpr (MODE == SeqMode::kFull) {
     if (a.residual) {
-      hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, true>), dim3(grid), dim3(64 * NW), lds, stream,
-                         a, x);
+      hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, true>), dim3(grid), dim3(64 * NW), lds,
+                         stream, a, x);
       return hipGetLastError();
     }
   } else if constexpr (MODE == SeqMode::kStateOnly) {
     if (a.residual) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, false>), dim3(grid), dim3(64 * NW), lds, stream, a,
-                     x);
+  hipLaunchKernelGGL((vla_scan_seq_kernel<TIn, D, NW, CG, MODE, false>), dim3(grid), dim3(64 * NW), lds, stream,
+                     a, x);
   return hipGetLastError();
 }
 
 // Workgroup shapes.  The full scan runs one wave per chain for d <= 64 (many
-// chains fill the chip) and four waves at d = 128.  The state-only chain of
+// chains fill the chip) and four waves at d = 128; short calls see below.  The state-only chain of
 // the time-parallel schedule has few chains and spreads each one over a
 // whole compute unit.
+// Below this many tokens per call (decode-like calls, where the state's trip
+// through HBM dominates) the full scan spreads a chain over more waves, so
+// each wave holds fewer rows of A and S and more waves share a SIMD, which
+// overlaps one chain's state loads with another's arithmetic.
+constexpr int kShortCallTokens = 16;
+
 template <typename TIn, SeqMode MODE>
 static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int chains, hipStream_t stream) {
   if constexpr (MODE == SeqMode::kFull) {
+    if (a.T <= kShortCallTokens) {
+      switch (d) {
+        case 32: return launch_seq<TIn, 32, 2, 4, MODE>(a, x, chains, stream);
+        case 64: return launch_seq<TIn, 64, 4, 4, MODE>(a, x, chains, stream);
+        default: break;
+      }
+    }
     switch (d) {
       case 16: return launch_seq<TIn, 16, 1, 4, MODE>(a, x, chains, stream);
       case 32: return launch_seq<TIn, 32, 1, 4, MODE>(a, x, chains, stream);

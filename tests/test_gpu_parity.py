@@ -399,3 +399,25 @@ def test_timing_hook_records_the_chain_kernel():
     finally:
         timing_enable(False)
     assert len(ms) == 6 and all(t > 0 for t in ms), ms
+
+
+# Short calls (T <= 16 tokens, the decode-like case) run the full scan with
+# more waves per chain at d = 32 and 64; both updates, from a carried state.
+@pytest.mark.parametrize("update", ["additive", "residual"])
+@pytest.mark.parametrize("d,r,dtype", [(16, 1, "f32"), (32, 3, "bf16"), (64, 1, "bf16"), (64, 4, "f32"),
+                                       (128, 2, "bf16")])
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_short_calls_match_oracle(update, d, r, dtype, T):
+    cfg = CONFIGS["base"].with_(name=f"short-{update}-d{d}-r{r}-{dtype}-T{T}", B=3, H=5, T=T, d=d, r=r,
+                                in_dtype=dtype, nudge_period=4, s_cap=25.0)
+    x = case(cfg, seed=T * 100 + d + r)
+    g = torch.Generator().manual_seed(d + T)
+    C = cfg.B * cfg.H
+    A0 = torch.eye(d).expand(cfg.B, cfg.H, d, d) * 0.7 + 0.02 * torch.randn(cfg.B, cfg.H, d, d, generator=g)
+    A0 = ((A0 + A0.transpose(-1, -2)) / 2).contiguous()
+    S0 = torch.randn(cfg.B, cfg.H, d, d, generator=g)
+    n0 = torch.rand(cfg.B, cfg.H, d, generator=g) * 10
+    out = _gpu(x, cfg, A0=A0.to(DEV), S0=S0.to(DEV), n0=n0.to(DEV), t0=3, update=update)
+    ref = run_oracle(x, cfg, A0=A0.reshape(C, d, d), S0=S0.reshape(C, d, d), n0=n0.reshape(C, d), t0=3,
+                     update=update)
+    _check(cfg, out, ref)
