@@ -51,7 +51,7 @@ constexpr int kMat = kB * kP; // floats per padded LDS matrix
 // Prep: one workgroup of 256 threads per (chain, block).
 // ---------------------------------------------------------------------------
 template <typename TIn>
-__global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chains) {
+__global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chains, int b_lo, int nb) {
   extern __shared__ float4 smem4[];
   float* sK = reinterpret_cast<float*>(smem4);   // k, then k_hat, then W, then Q
   float* sV = sK + kMat;                         // v, then U
@@ -60,9 +60,10 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
   __shared__ float sKinv[kB];
 
   const int nblk = pl.nblk;
-  const int64_t chain = blockIdx.x / nblk;
-  const int b = static_cast<int>(blockIdx.x % nblk);
-  if (chain >= chains) return;
+  // Blocks [b_lo, b_lo + nb) of every chain, grid-stride.
+  for (int64_t x = blockIdx.x; x < static_cast<int64_t>(chains) * nb; x += gridDim.x) {
+  const int64_t chain = x / nb;
+  const int b = b_lo + static_cast<int>(x % nb);
   const int tid = threadIdx.x;
   const int t0 = b * kB;
   const int nvalid = min(kB, pl.T - t0);
@@ -197,6 +198,8 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[64 * q] = *reinterpret_cast<const float4*>(src + 8 * q);
   }
+  __syncthreads();   // the next block overwrites the LDS this one read last
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -237,19 +240,19 @@ __device__ __forceinline__ void ring_copy(const ResPlan& pl, uint4 (&slot)[kSlot
 
 struct ChainLane {
   int64_t chain, soff;
-  int nblk, w, lane, jb;
+  int nblk, nb, b_lo, w, lane, jb;   // nb blocks from b_lo in this segment
 };
 
-// Block b: copies for block b + 2 into `ahead`, operands from `cur`, the
-// partner's tile from `xr`, this wave's new tile to `xw`.  Distinct LDS
-// objects let the compiler see that reading `cur` does not wait for the
-// copies into `ahead`.
-__device__ __forceinline__ void chain_block(const ResPlan& pl, const ChainLane& cl, int b, f32x16& Y,
+// Block lb of the segment (block b_lo + lb): copies for block lb + 2 into
+// `ahead`, operands from `cur`, the partner's tile from `xr`, this wave's new
+// tile to `xw`.  Distinct LDS objects let the compiler see that reading `cur`
+// does not wait for the copies into `ahead`.
+__device__ __forceinline__ void chain_block(const ResPlan& pl, const ChainLane& cl, int lb, f32x16& Y,
                                             uint4 (&cur)[kSlotVecs], uint4 (&ahead)[kSlotVecs],
                                             const float (&xr)[kXFloats], float (&xw)[kXFloats]) {
-  const int w = cl.w, lane = cl.lane, jb = cl.jb, nblk = cl.nblk;
-  const int64_t blk = cl.chain * nblk + b;
-  if (b + 2 < nblk) ring_copy(pl, ahead, blk + 2, w, lane);
+  const int w = cl.w, lane = cl.lane, jb = cl.jb, nb = cl.nb;
+  const int64_t blk = cl.chain * cl.nblk + cl.b_lo + lb;
+  if (lb + 2 < nb) ring_copy(pl, ahead, blk + 2, w, lane);
   f32x16 Yp;
 #pragma unroll
   for (int s = 0; s < 16; ++s) Yp[s] = xr[((w ^ 1) * 16 + s) * 64 + lane];
@@ -290,22 +293,28 @@ __device__ __forceinline__ void chain_block(const ResPlan& pl, const ChainLane& 
   // The next block's operands (copied during block b - 1) have landed once
   // at most this block's ten copies and four stores are outstanding, in
   // whichever order the two were issued.
-  if (b >= 1 && b + 2 < nblk)
+  if (lb >= 1 && lb + 2 < nb)
     asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const float* __restrict__ S_in,
+// Segment [b_lo, b_hi) from S_in (chain c at S_in + c * S_in_stride).  The
+// last segment writes S_T and stats; the others leave S at b_hi in the
+// snapshot of block b_hi, where the next segment starts.
+__global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, int b_lo, int b_hi,
+                                                            const float* __restrict__ S_in, int64_t S_in_stride,
                                                             float* __restrict__ S_T, int32_t* __restrict__ stats,
-                                                            const int32_t* __restrict__ chain_info) {
+                                                            const int32_t* __restrict__ chain_info, int last) {
   __shared__ uint4 sR0[kSlotVecs], sR1[kSlotVecs], sR2[kSlotVecs];   // operand ring
   __shared__ float sX0[kXFloats], sX1[kXFloats];                     // tile exchange, by block parity
   __shared__ int sbad[4];
   ChainLane cl;
   cl.chain = blockIdx.x;
   cl.nblk = pl.nblk;
+  cl.b_lo = b_lo;
+  cl.nb = b_hi - b_lo;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, i = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar copy offsets
   const int jb = w & 1, c = w >> 1;
@@ -314,11 +323,11 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const fl
   cl.jb = jb;
   cl.soff = (32 * c + i) * kD + 32 * jb + 4 * h;   // this lane's S entries: soff + 8 q + 0..3
   const int64_t chain = cl.chain;
-  const int nblk = cl.nblk;
+  const int nblk = cl.nblk, nb = cl.nb;
 
   f32x16 Y;
   {
-    const float* src = S_in + chain * kD * kD + cl.soff;
+    const float* src = S_in + chain * S_in_stride + cl.soff;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 x = *reinterpret_cast<const float4*>(src + 8 * q);
@@ -327,21 +336,29 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const fl
   }
 #pragma unroll
   for (int s = 0; s < 16; ++s) sX0[(w * 16 + s) * 64 + lane] = Y[s];
-  ring_copy(pl, sR0, chain * nblk, w, lane);
-  if (nblk > 1) ring_copy(pl, sR1, chain * nblk + 1, w, lane);
+  const int64_t blk0 = chain * nblk + b_lo;
+  if (nb > 0) ring_copy(pl, sR0, blk0, w, lane);
+  if (nb > 1) ring_copy(pl, sR1, blk0 + 1, w, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Block b reads ring slot b % 3 and exchange buffer b % 2.
-  for (int b = 0; b < nblk; b += 6) {
-    chain_block(pl, cl, b, Y, sR0, sR2, sX0, sX1);
-    if (b + 1 < nblk) chain_block(pl, cl, b + 1, Y, sR1, sR0, sX1, sX0);
-    if (b + 2 < nblk) chain_block(pl, cl, b + 2, Y, sR2, sR1, sX0, sX1);
-    if (b + 3 < nblk) chain_block(pl, cl, b + 3, Y, sR0, sR2, sX1, sX0);
-    if (b + 4 < nblk) chain_block(pl, cl, b + 4, Y, sR1, sR0, sX0, sX1);
-    if (b + 5 < nblk) chain_block(pl, cl, b + 5, Y, sR2, sR1, sX1, sX0);
+  // Block lb of the segment reads ring slot lb % 3 and exchange buffer lb % 2.
+  for (int lb = 0; lb < nb; lb += 6) {
+    chain_block(pl, cl, lb, Y, sR0, sR2, sX0, sX1);
+    if (lb + 1 < nb) chain_block(pl, cl, lb + 1, Y, sR1, sR0, sX1, sX0);
+    if (lb + 2 < nb) chain_block(pl, cl, lb + 2, Y, sR2, sR1, sX0, sX1);
+    if (lb + 3 < nb) chain_block(pl, cl, lb + 3, Y, sR0, sR2, sX1, sX0);
+    if (lb + 4 < nb) chain_block(pl, cl, lb + 4, Y, sR1, sR0, sX0, sX1);
+    if (lb + 5 < nb) chain_block(pl, cl, lb + 5, Y, sR2, sR1, sX1, sX0);
   }
 
+  if (!last) {
+    float* dst = pl.Ssnap + (chain * nblk + b_hi) * kD * kD + cl.soff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(dst + 8 * q) = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
+    return;
+  }
   bool bad = false;
   {
     float* dst = S_T + chain * kD * kD + cl.soff;
@@ -364,33 +381,37 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, const fl
   }
 }
 
-// Normalisers at block starts, n_b = n_0 + sum_{b' < b} (key sum of b'), and
-// n_T: one workgroup of 1024 threads per chain, thread (g, f) = (tid >> 6,
-// tid & 63) takes feature f over the blocks of segment g of 16.
-__global__ void __launch_bounds__(1024) vla_res_nprefix_kernel(ResPlan pl, const float* __restrict__ n_in,
-                                                               float* __restrict__ n_T) {
+// Normalisers at the starts of blocks [b_lo, b_hi), n_b = n_{b_lo} + the key
+// sums of the blocks before b, from n_in (n at b_lo, [chains][64]); writes n
+// at b_hi to n_out.  One workgroup of 1024 threads per chain, thread (g, f) =
+// (tid >> 6, tid & 63) takes feature f over segment g of 16.
+__global__ void __launch_bounds__(1024) vla_res_nprefix_kernel(ResPlan pl, int b_lo, int b_hi,
+                                                               const float* __restrict__ n_in,
+                                                               float* __restrict__ n_out) {
   __shared__ float part[16][kD];
   const int64_t chain = blockIdx.x;
   const int nblk = pl.nblk;
   const int f = threadIdx.x & 63, g = threadIdx.x >> 6;
-  const int per = (nblk + 15) / 16;
-  const int lo = min(nblk, g * per), hi = min(nblk, lo + per);
+  const int nb = b_hi - b_lo;
+  const int per = (nb + 15) / 16;
+  const int lo = b_lo + min(nb, g * per), hi = b_lo + min(nb, g * per + per);
   const float* ks = pl.ksum + chain * nblk * kD + f;
   float sum = 0.f;
   for (int b = lo; b < hi; ++b) sum += ks[b * kD];
   part[g][f] = sum;
   __syncthreads();
-  float n = n_in[chain * kD + f];
+  const float n0 = n_in[chain * kD + f];
+  float n = n0;
   for (int x = 0; x < g; ++x) n += part[x][f];
-  float* nb = pl.nblock + chain * nblk * kD + f;
+  float* nbk = pl.nblock + chain * nblk * kD + f;
   for (int b = lo; b < hi; ++b) {
-    nb[b * kD] = n;
+    nbk[b * kD] = n;
     n += ks[b * kD];
   }
   if (g == 15) {
-    float t = n_in[chain * kD + f];
+    float t = n0;
     for (int x = 0; x < 16; ++x) t += part[x][f];
-    n_T[chain * kD + f] = t;
+    n_out[chain * kD + f] = t;
   }
 }
 
@@ -441,7 +462,7 @@ struct TokRows {
 };
 
 template <typename TIn, bool CAP>
-__global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float den_eps, float cap2, int chains,
+__global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float den_eps, float cap2, int chains, int b_lo, int nb,
                                                               int32_t* __restrict__ chain_info) {
   extern __shared__ float4 smem4[];
   float* R0 = reinterpret_cast<float*>(smem4);   // S_b, then q
@@ -453,9 +474,10 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   __shared__ float sNb[kD];
 
   const int nblk = pl.nblk;
-  const int64_t chain = blockIdx.x / nblk;
-  const int b = static_cast<int>(blockIdx.x % nblk);
-  if (chain >= chains) return;
+  // Blocks [b_lo, b_lo + nb) of every chain, grid-stride.
+  for (int64_t x = blockIdx.x; x < static_cast<int64_t>(chains) * nb; x += gridDim.x) {
+  const int64_t chain = x / nb;
+  const int b = b_lo + static_cast<int>(x % nb);
   const int tid = threadIdx.x;
   const int t0 = b * kB;
   const int nvalid = min(kB, pl.T - t0);
@@ -617,6 +639,8 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
     if (any_over) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
     if (any_bad) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
   }
+  __syncthreads();   // the next block overwrites the LDS this one read last
+  }
 }
 
 template <typename K>
@@ -627,44 +651,55 @@ void allow_lds(K kernel, size_t bytes) {
 
 }  // namespace
 
-hipError_t launch_res_prep(const ResPlan& pl, int chains, hipStream_t stream) {
+static unsigned side_grid(int64_t units, int max_wg) {
+  if (max_wg > 0 && units > max_wg) units = max_wg;
+  return static_cast<unsigned>(units);
+}
+
+hipError_t launch_res_prep(const ResPlan& pl, int chains, int b_lo, int nb, int max_wg, hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
   const size_t lds = 4 * kMat * sizeof(float);
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(chains) * pl.nblk));
+  const dim3 grid(side_grid(static_cast<int64_t>(chains) * nb, max_wg));
   if (pl.bf16) {
     allow_lds(vla_res_prep_kernel<uint16_t>, lds);
-    hipLaunchKernelGGL(vla_res_prep_kernel<uint16_t>, grid, dim3(256), lds, stream, pl, chains);
+    hipLaunchKernelGGL(vla_res_prep_kernel<uint16_t>, grid, dim3(256), lds, stream, pl, chains, b_lo, nb);
   } else {
     allow_lds(vla_res_prep_kernel<float>, lds);
-    hipLaunchKernelGGL(vla_res_prep_kernel<float>, grid, dim3(256), lds, stream, pl, chains);
+    hipLaunchKernelGGL(vla_res_prep_kernel<float>, grid, dim3(256), lds, stream, pl, chains, b_lo, nb);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_res_chain(const ResPlan& pl, const float* S_in, const float* n_in, float* S_T, float* n_T,
-                            int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop) {
-  hipLaunchKernelGGL(vla_res_nprefix_kernel, dim3(static_cast<unsigned>(chains)), dim3(1024), 0, stream, pl, n_in,
-                     n_T);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_res_nprefix(const ResPlan& pl, int b_lo, int b_hi, const float* n_in, float* n_out, int chains,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(vla_res_nprefix_kernel, dim3(static_cast<unsigned>(chains)), dim3(1024), 0, stream, pl, b_lo,
+                     b_hi, n_in, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_res_chain(const ResPlan& pl, int b_lo, int b_hi, const float* S_in, int64_t S_in_stride,
+                            float* S_T, int32_t* stats, const int32_t* chain_info, int last, int chains,
+                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  hipError_t e = hipSuccess;
   if (ev_start && (e = hipEventRecord(ev_start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(vla_res_chain_kernel, dim3(static_cast<unsigned>(chains)), dim3(256), 0, stream, pl, S_in,
-                     S_T, stats, chain_info);
+  hipLaunchKernelGGL(vla_res_chain_kernel, dim3(static_cast<unsigned>(chains)), dim3(256), 0, stream, pl, b_lo, b_hi,
+                     S_in, S_in_stride, S_T, stats, chain_info, last);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_stop) e = hipEventRecord(ev_stop, stream);
   return e;
 }
 
-hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains,
-                              int32_t* chain_info, hipStream_t stream) {
+hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains, int b_lo, int nb,
+                              int max_wg, int32_t* chain_info, hipStream_t stream) {
+  if (nb <= 0) return hipSuccess;
   const size_t lds = 4 * kMat * sizeof(float);
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(chains) * pl.nblk));
+  const dim3 grid(side_grid(static_cast<int64_t>(chains) * nb, max_wg));
   const float cap2 = cap * cap;
-#define VLA_RES_READOUT(T, C)                                                                             \
-  do {                                                                                                    \
-    allow_lds(vla_res_readout_kernel<T, C>, lds);                                                         \
+#define VLA_RES_READOUT(T, C)                                                                                  \
+  do {                                                                                                         \
+    allow_lds(vla_res_readout_kernel<T, C>, lds);                                                              \
     hipLaunchKernelGGL((vla_res_readout_kernel<T, C>), grid, dim3(512), lds, stream, pl, den_eps, cap2, chains, \
-                       chain_info);                                                                       \
+                       b_lo, nb, chain_info);                                                                  \
   } while (0)
   if (pl.bf16) {
     if (cap_on) VLA_RES_READOUT(uint16_t, true); else VLA_RES_READOUT(uint16_t, false);

@@ -171,7 +171,7 @@ struct ChunkLayout {
          off_ncarry = 0, off_cnt = 0, off_flag = 0,
          total = 0;
   // Residual update's state pass (replaces the additive one's buffers).
-  size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0;
+  size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0;
 };
 
 // Whether the chunked schedule can run these parameters with chunk length L.
@@ -233,6 +233,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       cl.off_rks = off; off = align_up(off + C * nb * 64 * 4);
       cl.off_rS = off; off = align_up(off + C * nb * d2 * 4);
       cl.off_rnb = off; off = align_up(off + C * nb * 64 * 4);
+      cl.off_rnc = off; off = align_up(off + 2 * C * 64 * 4);   // normaliser carries between segments
       cl.off_flag = off;
       if (p->validate) off += kValidateBytes;
       cl.total = off;
@@ -489,22 +490,74 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     rp.Ssnap = reinterpret_cast<float*>(ws + cl.off_rS);
     rp.nblock = reinterpret_cast<float*>(ws + cl.off_rnb);
     const int nch = static_cast<int>(chains);
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    {
-      Timing& tm = timing();
-      std::lock_guard<std::mutex> lock(tm.mu);
-      if (tm.on && tm.used < VLA_TIMING_SLOTS) {
-        ev0 = tm.start[tm.used];
-        ev1 = tm.stop[tm.used];
-        ++tm.used;
+    const int nblk = cl.nblk;
+    // Segments as for the additive pass: the chain kernel runs them in order
+    // on the caller's stream while the side stream preps the next one and
+    // reads out the previous one.  The side kernels cannot share a compute
+    // unit with the chain kernel (neither fits beside the other's LDS), and
+    // here they carry more work than the chain, so they run uncapped.
+    int bnd[kMaxChainSegs + 1];
+    const int nseg = chain_segments(nblk, p->segment_blocks, bnd);
+    float* ncar[2] = {reinterpret_cast<float*>(ws + cl.off_rnc),
+                      reinterpret_cast<float*>(ws + cl.off_rnc) + static_cast<size_t>(chains) * 64};
+    auto nprefix = [&](int sidx, hipStream_t st) {
+      const float* nin = sidx == 0 ? pl.n_init : ncar[(sidx - 1) & 1];
+      float* nout = sidx + 1 == nseg ? n_T : ncar[sidx & 1];
+      return vla::launch_res_nprefix(rp, bnd[sidx], bnd[sidx + 1], nin, nout, nch, st);
+    };
+    auto chain = [&](int sidx, hipStream_t st) {
+      hipEvent_t ev0 = nullptr, ev1 = nullptr;
+      {
+        Timing& tm = timing();
+        std::lock_guard<std::mutex> lock(tm.mu);
+        if (tm.on && tm.used < VLA_TIMING_SLOTS) {
+          ev0 = tm.start[tm.used];
+          ev1 = tm.stop[tm.used];
+          ++tm.used;
+        }
       }
+      const bool first = sidx == 0;
+      const float* S_in = first ? pl.S_init : rp.Ssnap + static_cast<int64_t>(bnd[sidx]) * 64 * 64;
+      const int64_t stride = first ? 64 * 64 : static_cast<int64_t>(nblk) * 64 * 64;
+      return vla::launch_res_chain(rp, bnd[sidx], bnd[sidx + 1], S_in, stride, S_T, stats, pl.chain_info,
+                                   sidx + 1 == nseg ? 1 : 0, nch, st, ev0, ev1);
+    };
+    if (nseg == 1) {
+      if ((e = vla::launch_res_prep(rp, nch, 0, nblk, 0, stream)) != hipSuccess || (e = nprefix(0, stream)) != hipSuccess)
+        return hip_fail(e, "residual prep launch");
+      if ((e = chain(0, stream)) != hipSuccess) return hip_fail(e, "residual chain launch");
+      if ((e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, 0, nblk, 0, pl.chain_info, stream)) !=
+          hipSuccess)
+        return hip_fail(e, "residual readout launch");
+    } else {
+      std::lock_guard<std::mutex> lock(side_pool().mu);
+      SideStream* ss = side_stream(&e);
+      if (!ss) return hip_fail(e, "side stream setup");
+      hipStream_t side = ss->stream;
+      hipEvent_t ev_in = ss->ev[0], ev_end = ss->ev[1];
+      hipEvent_t* ev_prep = ss->ev + 2;
+      hipEvent_t* ev_chain = ss->ev + 2 + kMaxChainSegs;
+      auto prep = [&](int sidx) {
+        hipError_t r = vla::launch_res_prep(rp, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx], 0, side);
+        if (r == hipSuccess) r = nprefix(sidx, side);
+        return r != hipSuccess ? r : hipEventRecord(ev_prep[sidx], side);
+      };
+      if ((e = hipEventRecord(ev_in, stream)) != hipSuccess || (e = hipStreamWaitEvent(side, ev_in, 0)) != hipSuccess ||
+          (e = prep(0)) != hipSuccess)
+        return hip_fail(e, "residual prep launch");
+      for (int sidx = 0; sidx < nseg; ++sidx) {
+        if (sidx + 1 < nseg && (e = prep(sidx + 1)) != hipSuccess) return hip_fail(e, "residual prep launch");
+        if ((e = hipStreamWaitEvent(stream, ev_prep[sidx], 0)) != hipSuccess || (e = chain(sidx, stream)) != hipSuccess ||
+            (e = hipEventRecord(ev_chain[sidx], stream)) != hipSuccess)
+          return hip_fail(e, "residual chain launch");
+        if ((e = hipStreamWaitEvent(side, ev_chain[sidx], 0)) != hipSuccess ||
+            (e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx], 0,
+                                         pl.chain_info, side)) != hipSuccess)
+          return hip_fail(e, "residual readout launch");
+      }
+      if ((e = hipEventRecord(ev_end, side)) != hipSuccess || (e = hipStreamWaitEvent(stream, ev_end, 0)) != hipSuccess)
+        return hip_fail(e, "side stream join");
     }
-    if ((e = vla::launch_res_prep(rp, nch, stream)) != hipSuccess) return hip_fail(e, "residual prep launch");
-    if ((e = vla::launch_res_chain(rp, pl.S_init, pl.n_init, S_T, n_T, stats, pl.chain_info, nch, stream, ev0, ev1)) !=
-        hipSuccess)
-      return hip_fail(e, "residual chain launch");
-    if ((e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, pl.chain_info, stream)) != hipSuccess)
-      return hip_fail(e, "residual readout launch");
     if ((e = vla::launch_stats_finalize(stats, pl.chain_info, nch, stream)) != hipSuccess)
       return hip_fail(e, "stats launch");
     e = vla::launch_scan_sequential(a, d, bf16, nch, pl.chain_info, stream);

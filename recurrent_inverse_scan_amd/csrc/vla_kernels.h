@@ -139,15 +139,23 @@ struct ResPlan {
   float* Ssnap;          // [chains][nblk][64][64] S at each block start
   float* nblock;         // [chains][nblk][64] normaliser at each block start
 };
-hipError_t launch_res_prep(const ResPlan& pl, int chains, hipStream_t stream);
-// The chain kernel from S_in, n_in ([chains][64][64], [chains][64]) to S_T, n_T
-// and stats (guard count and non-finite flag from chain_info; no cap fires:
-// a token over the cap makes the readout flag the chain for the fallback).
-hipError_t launch_res_chain(const ResPlan& pl, const float* S_in, const float* n_in, float* S_T, float* n_T,
-                            int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains,
-                              int32_t* chain_info, hipStream_t stream);
+// Block ranges [b_lo, b_lo + nb) of every chain; at most max_wg workgroups
+// if max_wg > 0 (grid-stride).
+hipError_t launch_res_prep(const ResPlan& pl, int chains, int b_lo, int nb, int max_wg, hipStream_t stream);
+// Block-start normalisers of blocks [b_lo, b_hi) from n at b_lo (n_in,
+// [chains][64]); n at b_hi goes to n_out (which must not alias n_in).
+hipError_t launch_res_nprefix(const ResPlan& pl, int b_lo, int b_hi, const float* n_in, float* n_out, int chains,
+                              hipStream_t stream);
+// The chain kernel over blocks [b_lo, b_hi) from S_in (chain c at
+// S_in + c * S_in_stride).  The last segment writes S_T and stats (guard count
+// and non-finite flag from chain_info; no cap fires: a token over the cap
+// makes the readout flag the chain for the fallback); the others leave S at
+// b_hi in that block's snapshot.
+hipError_t launch_res_chain(const ResPlan& pl, int b_lo, int b_hi, const float* S_in, int64_t S_in_stride,
+                            float* S_T, int32_t* stats, const int32_t* chain_info, int last, int chains,
+                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains, int b_lo, int nb,
+                              int max_wg, int32_t* chain_info, hipStream_t stream);
 
 hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_bf16, const void* W,
                             const void* kraw, void* u, hipStream_t stream);

@@ -226,3 +226,25 @@ def test_residual_full_size_sampled_chains(name):
                       x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
                       s_cap=cfg.s_cap, update="residual")
     _check(cfg, out, ref, chains=sel)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L,period,seg,cap", [(64, 128, 2, 1e3), (64, 128, 6, 1e3), (128, 128, 3, 1e3),
+                                              (96, 192, 5, None), (64, 64, 4, 12.0)])
+def test_residual_chunked_segments_match_oracle(dtype, L, period, seg, cap):
+    """The residual state pass in several segments (chain kernel on the
+    caller's stream, prep and readout of neighbouring segments on the side
+    stream) against the oracle; the last case's cap binds, so its chains fall
+    back to the sequential kernel."""
+    cfg = CONFIGS["long"].with_(name=f"res-seg-{dtype}-{L}-{seg}", B=1, H=3, T=1700, nudge_period=period,
+                                s_cap=cap, in_dtype=dtype)
+    _say(f"case segments {dtype} L={L} P={period} seg={seg} cap={cap}")
+    x = case(cfg, seed=21)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg)
+    ref = run_oracle(x, cfg, update="residual")
+    st = _check(cfg, out, ref)
+    if cap is not None and cap < 100:
+        assert (ref["cap_fires"] > 0).all() and (st[:, 1] > 0).all()
+    again = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg)
+    for a_, b_ in zip(out, again):
+        assert torch.equal(a_, b_)
