@@ -472,6 +472,9 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   __shared__ float sDen[kB];
   __shared__ float sNorm[kB][32];                 // per-token partial |S_t|^2 of each 16-lane group
   __shared__ float sNb[kD];
+  __shared__ float sEn[kB];      // |e_t|^2
+  __shared__ float sSp[32];      // partial |S_b|^2 of each 16-lane group
+  __shared__ int sExact;         // the block needs the exact per-token norms
 
   const int nblk = pl.nblk;
   // Blocks [b_lo, b_lo + nb) of every chain, grid-stride.
@@ -533,8 +536,16 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
       }
     }
     __syncthreads();   // every thread has read its U entries before E overwrites them
+    float e2 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) R2[t * kP + jc + 8 * m] = acc[m];
+    for (int m = 0; m < 8; ++m) {
+      R2[t * kP + jc + 8 * m] = acc[m];
+      e2 = fmaf(acc[m], acc[m], e2);
+    }
+    if constexpr (CAP) {
+      e2 = group_sum<8>(e2);
+      if (jc == 0) sEn[t] = e2;
+    }
   }
   // This thread's row of S_b for the token loop.
   float S[8];
@@ -542,6 +553,13 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
     const float4 a = *reinterpret_cast<const float4*>(R0 + i * kP + 8 * jc);
     const float4 c = *reinterpret_cast<const float4*>(R0 + i * kP + 8 * jc + 4);
     S[0] = a.x; S[1] = a.y; S[2] = a.z; S[3] = a.w; S[4] = c.x; S[5] = c.y; S[6] = c.z; S[7] = c.w;
+  }
+  if constexpr (CAP) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s2 = fmaf(S[m], S[m], s2);
+    s2 = group_sum<16>(s2);
+    if ((tid & 15) == 0) sSp[tid >> 4] = s2;
   }
   __syncthreads();
   gq.put(R0, tid);
@@ -573,7 +591,17 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
     d = group_sum<8>(d);
     if (jc == 0) sDen[t] = d + den_eps;
   }
+  if constexpr (CAP) {
+    // |S_t|_F <= |S_b|_F + sum_{s<=t} |e_s| |alpha_s| and |alpha_s| <= 1: when
+    // that bound stays under the cap for the whole block, no token can fire.
+    if (tid < 64) {
+      const float ssq = wave_sum(tid < 32 ? sSp[tid] : 0.f);
+      const float esum = wave_sum(sqrtf(sEn[tid]));
+      if (tid == 0) sExact = (sqrtf(ssq) + esum) * (1.f + 1e-5f) > sqrtf(cap2) ? 1 : 0;
+    }
+  }
   __syncthreads();
+  const bool exact = CAP && sExact != 0;
 
   // The block's tokens in order: S_t = S_{t-1} + e_t alpha_t^T, o_t, |S_t|^2.
   bool bad = false;
@@ -590,7 +618,7 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
     for (int m = 0; m < 8; ++m) {
       S[m] = fmaf(ev, av[m], S[m]);
       po = fmaf(S[m], qv[m], po);
-      if constexpr (CAP) ns = fmaf(S[m], S[m], ns);
+      if (exact) ns = fmaf(S[m], S[m], ns);
     }
     po = group_sum<8>(po);
     if (jc == 0) {
@@ -598,7 +626,7 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
       bad |= !isfinite(ov);
       R1[t * kP + i] = ov;
     }
-    if constexpr (CAP) {
+    if (exact) {
       ns = group_sum<16>(ns);
       if ((tid & 15) == 0) sNorm[t][tid >> 4] = ns;
     }
@@ -626,7 +654,7 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
     }
   }
   bool over = false;
-  if constexpr (CAP) {
+  if (exact) {
     if (tid < nvalid) {
       float ns = 0.f;
 #pragma unroll

@@ -85,6 +85,7 @@ CHUNKED = [
     ("long-bf16", dict(B=1, H=3, T=2053, nudge_period=128, s_cap=1e3), 64),
     ("long-bf16-L128", dict(B=2, H=1, T=1000, nudge_period=256, s_cap=None), 128),
     ("long-bf16-cap-binds", dict(B=1, H=2, T=700, nudge_period=64, s_cap=15.0), 64),
+    ("long-bf16-cap-checked", dict(B=1, H=2, T=1100, nudge_period=64, s_cap=150.0), 64),
     ("base-f32", dict(B=1, H=2, T=1500, nudge_period=256, s_cap=1e3), 256),
     ("base-f32-r2", dict(B=1, H=2, T=777, nudge_period=0, s_cap=None, r=2), 64),
     ("base-f32-short", dict(B=2, H=2, T=65, nudge_period=0, s_cap=None), 16),
