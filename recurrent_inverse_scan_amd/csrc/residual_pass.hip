@@ -17,10 +17,11 @@
 // an affine map of S_b whose coefficients need no state.
 //
 // Kernels:
-//  * vla_res_prep_kernel, parallel over blocks: k_hat, L, W and U by forward
-//    substitution (one thread per column), N and Q.  Stores W and U for the
-//    readout, N^T as pre-split bf16 matrix-core operands and Q^T in
-//    accumulator order for the chain kernel, and the block's key sum.
+//  * vla_res_prep_kernel, parallel over blocks: k_hat, L (matrix cores), W
+//    and U by forward substitution (one thread per column), N and Q (matrix
+//    cores).  Stores W and U for the readout, N^T as pre-split bf16
+//    matrix-core operands and Q^T in accumulator order for the chain kernel,
+//    and the block's key sum.
 //  * vla_res_chain_kernel, one workgroup per chain, sequential over blocks:
 //    Y_{b+1} = Y_b + N^T Y_b + Q^T for Y = S^T, one 64x64x64 product per
 //    block on the bf16 matrix cores with three-term splits of the fp32
@@ -46,6 +47,20 @@ constexpr int kD = 64;        // head dimension
 constexpr int kB = 64;        // tokens per block
 constexpr int kP = 68;        // padded LDS row (16-byte aligned rows)
 constexpr int kMat = kB * kP; // floats per padded LDS matrix
+
+// 8 consecutive floats of a padded LDS row as a three-term split, and 8
+// entries of a column (rows r0 .. r0 + 7, column c), optionally negated.
+__device__ __forceinline__ Split3 row_frag(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split3(x);
+}
+__device__ __forceinline__ Split3 col_frag(const float* m, int r0, int c, float sign) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = sign * m[(r0 + e) * kP + c];
+  return split3(x);
+}
 
 // ---------------------------------------------------------------------------
 // Prep: one workgroup of 256 threads per (chain, block).
@@ -104,17 +119,22 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
   }
   __syncthreads();
 
-  // L_ts = k_hat_t . alpha_s for s < t, 0 elsewhere.
-  {
-    const int t = tid >> 2;
-#pragma unroll 4
-    for (int m = 0; m < 16; ++m) {
-      const int s = (tid & 3) + 4 * m;
-      float acc = 0.f;
-      if (s < t) {
-        for (int j = 0; j < kD; ++j) acc = fmaf(sK[t * kP + j], sA[s * kP + j], acc);
-      }
-      sL[t * kP + s] = acc;
+  // L_ts = k_hat_t . alpha_s for s < t (the strictly lower tiles (tb, sb) =
+  // (0, 0), (1, 0), (1, 1), one per wave, on the matrix cores).
+  const int wv = tid >> 6, ln = tid & 63, lh = ln >> 5, li = ln & 31;
+  if (wv < 3) {
+    const int tb = wv == 0 ? 0 : 1, sb = wv == 2 ? 1 : 0;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const Split3 a = row_frag(sK + (32 * tb + li) * kP + 16 * ks + 8 * lh);
+      const Split3 bb = row_frag(sA + (32 * sb + li) * kP + 16 * ks + 8 * lh);
+      acc = mma_split(a, bb, acc);
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int t = 32 * tb + acc_row(s, lh), sc = 32 * sb + li;
+      sL[t * kP + sc] = t > sc ? acc[s] : 0.f;
     }
   }
   __syncthreads();
@@ -136,67 +156,42 @@ __global__ void __launch_bounds__(256) vla_res_prep_kernel(ResPlan pl, int chain
   }
   __syncthreads();
 
-  // W and U to HBM; N = -W^T A and Q = U^T A (rows m, columns (tid & 3) + 4 q).
+  // W and U to HBM for the readout.
   for (int e = tid; e < kB * kD; e += 256) {
     const int t = e >> 6, j = e & 63;
     pl.W[blk * kB * kD + e] = sK[t * kP + j];
     pl.U[blk * kB * kD + e] = sV[t * kP + j];
   }
-  float nacc[16], qacc[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) nacc[q] = qacc[q] = 0.f;
+  // N = -W^T A (tile (mb, jb) = (wv >> 1, wv & 1)) and Q^T = A^T U (tile
+  // (jb, c) = (wv & 1, wv >> 1)) on the matrix cores, contracting over the
+  // block's tokens.  A lane's column fragment of A serves as the B operand of
+  // the first and the A operand of the second.  In accumulator layout N's
+  // tile is already N^T's A-operand fragments for the chain kernel (slots
+  // 8 g .. 8 g + 7 are contraction step g) and Q^T's tile is its
+  // accumulator tile: both go to HBM from registers.
   {
-    const int m = tid >> 2;
-    for (int t = 0; t < kB; ++t) {
-      const float wv = sK[t * kP + m], uv = sV[t * kP + m];
+    const int mb = wv >> 1, jb = wv & 1;
+    f32x16 aN = zero16(), aQ = zero16();
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float av = sA[t * kP + (tid & 3) + 4 * q];
-        nacc[q] = fmaf(-wv, av, nacc[q]);
-        qacc[q] = fmaf(uv, av, qacc[q]);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r0 = 16 * ks + 8 * lh;
+      const Split3 fw = col_frag(sK, r0, 32 * mb + li, -1.f);
+      const Split3 fu = col_frag(sV, r0, 32 * mb + li, 1.f);
+      const Split3 fa = col_frag(sA, r0, 32 * jb + li, 1.f);
+      aN = mma_split(fw, fa, aN);
+      aQ = mma_split(fa, fu, aQ);
     }
-  }
-  __syncthreads();
-  {
-    const int m = tid >> 2;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      sL[m * kP + (tid & 3) + 4 * q] = nacc[q];
-      sK[m * kP + (tid & 3) + 4 * q] = qacc[q];
+    for (int g = 0; g < 2; ++g) {
+      const Split3 sp = split_slots(aN, g);
+      uint4* dst = reinterpret_cast<uint4*>(pl.NTF) + ((((blk * 2 + jb) * 2 + mb) * 2 + g) * 3) * 64 + ln;
+      dst[0] = __builtin_bit_cast(uint4, sp.t1);
+      dst[64] = __builtin_bit_cast(uint4, sp.t2);
+      dst[128] = __builtin_bit_cast(uint4, sp.t3);
     }
-  }
-  __syncthreads();
-
-  // N^T as A operands: fragment (jb, mb, g) of lane l = (h, i) holds
-  // N^T[32 jb + i][32 mb + 16 g + 8 (e >> 2) + 4 h + (e & 3)], e = 0..7, the
-  // contraction order in which an accumulator tile of Y serves as the B
-  // operand (see vla_mfma.h), split into three bf16 terms.
-  for (int f = tid; f < 512; f += 256) {
-    const int lane = f & 63, g = (f >> 6) & 1, mb = (f >> 7) & 1, jb = (f >> 8) & 1;
-    const int h = lane >> 5, i = lane & 31;
-    float x[8];
+    float4* qdst = reinterpret_cast<float4*>(pl.QT + blk * kD * kD) + wv * 256 + ln;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int mrow = 32 * mb + 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
-      x[e] = sL[mrow * kP + 32 * jb + i];
-    }
-    const Split3 sp = split3(x);
-    uint4* dst = reinterpret_cast<uint4*>(pl.NTF) + ((((blk * 2 + jb) * 2 + mb) * 2 + g) * 3) * 64 + lane;
-    dst[0] = __builtin_bit_cast(uint4, sp.t1);
-    dst[64] = __builtin_bit_cast(uint4, sp.t2);
-    dst[128] = __builtin_bit_cast(uint4, sp.t3);
-  }
-  // Q^T in accumulator order: tile w = jb + 2 c, lane l = (h, i), slot s holds
-  // Q^T[32 jb + acc_row(s, h)][32 c + i] = Q[32 c + i][32 jb + acc_row(s, h)];
-  // stored as [w][q][lane] float4 of slots 4 q .. 4 q + 3.
-  {
-    const int w = tid >> 6, lane = tid & 63, h = lane >> 5, i = lane & 31;
-    const int jb = w & 1, c = w >> 1;
-    float4* dst = reinterpret_cast<float4*>(pl.QT + blk * kD * kD) + w * 256 + lane;
-    const float* src = sK + (32 * c + i) * kP + 32 * jb + 4 * h;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[64 * q] = *reinterpret_cast<const float4*>(src + 8 * q);
+    for (int q = 0; q < 4; ++q) qdst[64 * q] = make_float4(aQ[4 * q], aQ[4 * q + 1], aQ[4 * q + 2], aQ[4 * q + 3]);
   }
   __syncthreads();   // the next block overwrites the LDS this one read last
   }
