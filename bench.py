@@ -51,7 +51,7 @@ CHAIN = {
                  ("state_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h"),
                  os.path.join(ROOT, "profiles", "state_chain_long_traffic.md")),
     "residual": ("vla_res_chain_kernel",
-                 ("residual_pass.hip", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h"),
+                 ("residual_pass.hip", "vla_residual.h", "vla_common.h", "vla_kernels.h", "vla_mfma.h", "vla_seq.h"),
                  os.path.join(ROOT, "profiles", "residual_chain_long_traffic.md")),
 }
 

@@ -35,6 +35,7 @@
 //    recomputes it with the cap applied.
 #include "vla_common.h"
 #include "vla_kernels.h"
+#include "vla_residual.h"
 #include "vla_mfma.h"
 #include "vla_seq.h"
 

@@ -11,6 +11,7 @@
 
 #include "../../include/vla.h"
 #include "vla_kernels.h"
+#include "vla_residual.h"
 
 namespace {
 
