@@ -164,11 +164,15 @@ vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, do
 // (transposed) and the next one is loaded while the current product runs.
 constexpr int kNdSplit = 16;
 constexpr int kNdCols = kD / kNdSplit;   // 4
+// fp64 LDS rows padded to 65 doubles: a column of a row-major 64x64 block
+// then spreads over the banks instead of landing on one (transposed stores,
+// column reads).
+constexpr int kPad = kD + 1;
 
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
                        int nperiods, double eps) {
-  __shared__ double sG[kD * kD];            // sG[m*kD + i] = Gtot[i][m]
+  __shared__ double sG[kD * kPad];          // sG[m*kPad + i] = Gtot[i][m]
   __shared__ double sN[kD * kNdCols];       // sN[m*kNdCols + c] = N[m][c0 + c]
   __shared__ double sP[4][kD * kNdCols];    // partial products of each wave
   const int64_t chain = blockIdx.x / kNdSplit;
@@ -208,7 +212,7 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sG[(4 * sc + j) * kD + 4 * sr + i] = g[4 * i + j];
+      for (int j = 0; j < 4; ++j) sG[(4 * sc + j) * kPad + 4 * sr + i] = g[4 * i + j];
     if (owner) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sN[(4 * rb + i) * kNdCols + cc] = N[i];
@@ -220,7 +224,7 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
     for (int m = 16 * q; m < 16 * q + 16; ++m) {
       const double nm = sN[m * kNdCols + cc];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = fma(sG[m * kD + 4 * rb + i], nm, part[i]);
+      for (int i = 0; i < 4; ++i) part[i] = fma(sG[m * kPad + 4 * rb + i], nm, part[i]);
     }
     if (!owner) {
 #pragma unroll
@@ -253,13 +257,16 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
                        int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo, int c_cnt) {
-  // 64 KiB of LDS: Gpre^T and N_p for the product; afterwards the pivot row
+  // 65 KiB of LDS: Gpre^T and N_p for the product; afterwards the pivot row
   // and column buffers reuse the N_p half, and the result block the first half.
-  __shared__ double smem[2 * kD * kD];
-  double* sA = smem;
-  double* sB = smem + kD * kD;
-  double (*rowbuf)[2 * kD] = reinterpret_cast<double (*)[2 * kD]>(sB);
-  double (*colbuf)[kD] = reinterpret_cast<double (*)[kD]>(sB + 4 * kD);
+  __shared__ double smem[2 * kD * kPad];
+  double* sA = smem;                 // rows of kPad doubles
+  double* sB = smem + kD * kPad;
+  // Pivot rows at padded positions rbx(j) = j + 2 (j / 32): the 16 threads
+  // reading 8-double runs 8 cb + jj at once hit distinct banks.
+  double (*rowbuf)[2 * kD + 8] = reinterpret_cast<double (*)[2 * kD + 8]>(sB);
+  double (*colbuf)[kD] = reinterpret_cast<double (*)[kD]>(sB + 2 * (2 * kD + 8));
+  auto rbx = [](int j) { return j + 2 * (j >> 5); };
   const int64_t chain = blockIdx.x / c_cnt;
   const int c = c_lo + static_cast<int>(blockIdx.x % c_cnt);
   const int p = period_of(c, o, q);
@@ -272,8 +279,8 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
 
   for (int e = t; e < kD * kD; e += kChunkThreads) {
     const int i = e / kD, j = e % kD;
-    if (has_pre) sA[j * kD + i] = gp[e];
-    sB[e] = Np[e];
+    if (has_pre) sA[j * kPad + i] = gp[e];
+    sB[i * kPad + j] = Np[e];
   }
   __syncthreads();
 
@@ -288,9 +295,9 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
     for (int m = 0; has_pre && m < kD; ++m) {
       double gv[8], nv[4];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) gv[jj] = sA[m * kD + 8 * cb + jj];
+      for (int jj = 0; jj < 8; ++jj) gv[jj] = sA[m * kPad + 8 * cb + jj];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) nv[ii] = sB[m * kD + 4 * rb + ii];
+      for (int ii = 0; ii < 4; ++ii) nv[ii] = sB[m * kPad + 4 * rb + ii];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
@@ -301,7 +308,7 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = sB[(8 * (cb - 8) + jj) * kD + 4 * rb + ii];
+      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = sB[(8 * (cb - 8) + jj) * kPad + 4 * rb + ii];
   }
 
   __syncthreads();   // every thread is done reading sB before it holds pivots
@@ -316,21 +323,21 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
       const bool row_owner = rb == 2 * k8 + (kk >> 2);
       if (row_owner) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) rowbuf[par][8 * cb + jj] = W[kk & 3][jj];
+        for (int jj = 0; jj < 8; ++jj) rowbuf[par][rbx(8 * cb + jj)] = W[kk & 3][jj];
       }
       if (cb == k8) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) colbuf[par][4 * rb + ii] = W[ii][kk];
       }
       __syncthreads();
-      const double piv = rowbuf[par][k];
+      const double piv = rowbuf[par][rbx(k)];
       ok = ok && (piv > 0.0) && isfinite(piv);
       // 1/piv: the hardware reciprocal refined by one Newton step.
       double inv = __builtin_amdgcn_rcp(piv);
       inv = fma(inv, fma(-piv, inv, 1.0), inv);
       double rv[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][8 * cb + jj] * inv;
+      for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][rbx(8 * cb + jj)] * inv;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         if (row_owner && ii == (kk & 3)) {
@@ -352,13 +359,13 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sA[(4 * rb + ii) * kD + 8 * (cb - 8) + jj] = W[ii][jj];
+      for (int jj = 0; jj < 8; ++jj) sA[(4 * rb + ii) * kPad + 8 * (cb - 8) + jj] = W[ii][jj];
   }
   __syncthreads();
   float* ac = Ac + (chain * nchunks + c) * kD * kD;
   for (int e = t; e < kD * kD; e += kChunkThreads) {
     const int i = e / kD, j = e % kD;
-    ac[e] = static_cast<float>(0.5 * (sA[i * kD + j] + sA[j * kD + i]));
+    ac[e] = static_cast<float>(0.5 * (sA[i * kPad + j] + sA[j * kPad + i]));
   }
 }
 
