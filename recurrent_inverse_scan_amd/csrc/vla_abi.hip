@@ -537,10 +537,18 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
       hipEvent_t ev_in = ss->ev[0], ev_end = ss->ev[1];
       hipEvent_t* ev_prep = ss->ev + 2;
       hipEvent_t* ev_chain = ss->ev + 2 + kMaxChainSegs;
-      // The side launches run uncapped: capped at two workgroups on each of
-      // five eighths of the compute units they took longer and the chain
-      // kernel was no faster (4.72 against 4.20 ms per step on the
-      // 65536-token, 16-chain workload).
+      // A chain workgroup needs a whole compute unit, so each segment's chain
+      // launch must find free units when it starts, which is also when the
+      // previous segment's readout becomes ready: that readout is held to
+      // (units - chains) workgroups, which leaves enough units empty.  The
+      // next prep starts after the readout, when the chain kernel already
+      // holds its units, and runs uncapped.  (Uncapped readouts kept the
+      // chain's workgroups waiting: 2.85 against 1.93 ms of chain time per
+      // scan on the 65536-token, 16-chain workload.)
+      int ncu = 0;
+      if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0)) != hipSuccess)
+        return hip_fail(e, "device query");
+      const int res_wg = std::max(1, ncu - nch);
       auto prep = [&](int sidx) {
         hipError_t r = vla::launch_res_prep(rp, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx], 0, side);
         if (r == hipSuccess) r = nprefix(sidx, side);
@@ -555,8 +563,8 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
             (e = hipEventRecord(ev_chain[sidx], stream)) != hipSuccess)
           return hip_fail(e, "residual chain launch");
         if ((e = hipStreamWaitEvent(side, ev_chain[sidx], 0)) != hipSuccess ||
-            (e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx], 0,
-                                         pl.chain_info, side)) != hipSuccess)
+            (e = vla::launch_res_readout(rp, p->den_eps, a.cap, a.cap_on, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx],
+                                         sidx + 1 == nseg ? 0 : res_wg, pl.chain_info, side)) != hipSuccess)
           return hip_fail(e, "residual readout launch");
       }
       if ((e = hipEventRecord(ev_end, side)) != hipSuccess || (e = hipStreamWaitEvent(stream, ev_end, 0)) != hipSuccess)
