@@ -421,3 +421,53 @@ def test_short_calls_match_oracle(update, d, r, dtype, T):
     ref = run_oracle(x, cfg, A0=A0.reshape(C, d, d), S0=S0.reshape(C, d, d), n0=n0.reshape(C, d), t0=3,
                      update=update)
     _check(cfg, out, ref)
+
+
+# One-token calls at d = 64 run a dedicated decode kernel.
+@pytest.mark.parametrize("update", ["additive", "residual"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_guard_fire_householder_start(update, dtype):
+    """T = 1 from A0 = I - 2 u u^T with u the token's direction: delta = 0
+    exactly, so the guard fires in the decode kernel too."""
+    cfg = CONFIGS["base"].with_(name=f"decode-guard-{update}-{dtype}", B=2, H=3, T=1, nudge_period=0, s_cap=None,
+                                in_dtype=dtype)
+    x = case(cfg, seed=31)
+    e = torch.zeros(cfg.d)
+    e[9] = 1.0
+    u = x["u"].clone()
+    u[:, :, 0, 0, :] = e.to(u.dtype)
+    x["u"] = u
+    A0 = (torch.eye(cfg.d) - 2 * torch.outer(e, e)).expand(cfg.B, cfg.H, cfg.d, cfg.d).contiguous()
+    out = _gpu(x, cfg, A0=A0.to(DEV), update=update)
+    ref = run_oracle(x, cfg, A0=A0.reshape(cfg.B * cfg.H, cfg.d, cfg.d), update=update)
+    assert (ref["guard_fires"] == 1).all()
+    _check(cfg, out, ref)
+
+
+@pytest.mark.parametrize("update", ["additive", "residual"])
+def test_decode_steps_match_one_call(update):
+    """Twenty-four one-token calls with the state carried in place (A_T, S_T,
+    n_T aliasing A0, S0, n0; t0 advancing, so the nudge phase moves) equal one
+    24-token call and the oracle."""
+    cfg = CONFIGS["long"].with_(name=f"decode-steps-{update}", B=4, H=8, T=24, nudge_period=5, s_cap=12.0)
+    x = case(cfg, seed=32)
+    whole = _gpu(x, cfg, update=update)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    A = torch.eye(d, device=DEV).expand(B, H, d, d).contiguous()
+    S = torch.zeros(B, H, d, d, device=DEV)
+    n = torch.zeros(B, H, d, device=DEV)
+    st = torch.empty(B, H, 4, device=DEV, dtype=torch.int32)
+    outs, fires = [], 0
+    for t in range(cfg.T):
+        sl = {key: x[key][:, :, t:t + 1].contiguous().to(DEV) for key in ("q", "k", "v", "u")}
+        o = torch.empty_like(sl["q"])
+        scan_forward(sl["q"], sl["k"], sl["v"], sl["u"], A, S, n, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap,
+                     t0=t, update=update, out=(o, A, S, n, st))
+        torch.cuda.synchronize()
+        fires += st[..., 1].cpu().numpy()
+        outs.append(o)
+    o_steps = torch.cat(outs, dim=2)
+    ref = run_oracle(x, cfg, update=update)
+    _check(cfg, (o_steps, A, S, n, whole[4]), ref)
+    assert rel_err(o_steps, whole[0].float().cpu().numpy()) <= 1e-2
+    assert np.abs(fires.reshape(-1) - ref["cap_fires"]).max() <= 1
