@@ -271,6 +271,8 @@ def extra_measurements(CONFIGS, dev):
       workload (sequential schedule) and on the long workload (time-parallel
       schedule); algorithmic
       flops 2 (2r+4) d^2 per token*head (one more d^2 sweep than additive);
+    * the other workloads (tiny, base, recall, wide) with the additive update,
+      each on the schedule the library picks for it;
     * decode: one token per call (T = 1) for 4096 chains with the state read
       from and written back to HBM in place; its bound is HBM, with
       algorithmic bytes per chain of A, S (read and written, fp32), n, and
@@ -303,6 +305,29 @@ def extra_measurements(CONFIGS, dev):
                         f"{sched} schedule", "ms": ms, "tokens_heads_per_s": th / (ms * 1e-3),
             "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
             "kernel": "vla_res_chain_kernel" if sched == "chunked" else "vla_scan_seq_kernel"}
+        del q, k, v, u, o, x, ws
+
+    # The other workloads (additive update), each on the schedule the library
+    # picks for it.
+    for name, reps in (("tiny", 20), ("base", 20), ("recall", 20), ("wide", 2)):
+        cfg = CONFIGS[name]
+        x = make_inputs(cfg, seed=0)
+        q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+        u = project_u(x["W_u"].to(dev), x["k_raw"].to(dev))
+        B, H, T, d, r = cfg.B, cfg.H, cfg.T, cfg.d, cfg.r
+        o = (torch.empty_like(q), torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d, d), device=dev),
+             torch.empty((B, H, d), device=dev), torch.empty((B, H, 4), device=dev, dtype=torch.int32))
+        ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+        sched = "chunked" if ws_bytes > 0 else "sequential"
+        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+        fn = lambda: scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=o, workspace=ws)
+        ms = _time_ms(fn, reps, warmup=1)
+        th = B * H * T
+        tfl = 2 * (2 * r + 3) * d * d * th / (ms * 1e-3) / 1e12
+        out[f"additive_{name}"] = {
+            "workload": f"{name}: additive update, B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
+                        f"{sched} schedule", "ms": ms, "tokens_heads_per_s": th / (ms * 1e-3),
+            "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS}
         del q, k, v, u, o, x, ws
 
     # Decode: 4096 chains, one token per call, state carried in place.

@@ -506,7 +506,8 @@ static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, h
 }
 
 // Workgroup shapes.  The full scan runs one wave per chain for d <= 64 (many
-// chains fill the chip) and four waves at d = 128; short calls see below.  The state-only chain of
+// chains fill the chip) and eight waves at d = 128 (two rows per lane; four
+// waves took 8 % longer on 128 chains of 8192 tokens); short calls see below.  The state-only chain of
 // the time-parallel schedule has few chains and spreads each one over a
 // whole compute unit.
 // Below this many tokens per call (decode-like calls, where the state's trip
@@ -529,7 +530,7 @@ static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int 
       case 16: return launch_seq<TIn, 16, 1, 4, MODE>(a, x, chains, stream);
       case 32: return launch_seq<TIn, 32, 1, 4, MODE>(a, x, chains, stream);
       case 64: return launch_seq<TIn, 64, 1, 4, MODE>(a, x, chains, stream);
-      case 128: return launch_seq<TIn, 128, 4, 8, MODE>(a, x, chains, stream);
+      case 128: return launch_seq<TIn, 128, 8, 8, MODE>(a, x, chains, stream);
       default: return hipErrorInvalidValue;
     }
   } else if constexpr (MODE == SeqMode::kStateOnly) {
