@@ -191,8 +191,17 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     if (p->chunk_len > 0) {
       if (chunk_len_fits(p, p->chunk_len)) L = p->chunk_len;
     } else {
-      for (int cand : {512, 256, 128, 64})
-        if (chunk_len_fits(p, cand)) { L = cand; break; }
+      // The longest chunk that still gives at least kMinChunks chunks over
+      // all chains (the inverse pass keeps the SIMDs busy only with many
+      // chunks side by side), else the shortest that fits: 512 tokens for 16
+      // chains of 65536, 128 for 32 chains of 2048 (0.52 against 0.64 ms
+      // with 256).
+      constexpr int64_t kMinChunks = 512;
+      for (int cand : {512, 256, 128, 64}) {
+        if (!chunk_len_fits(p, cand)) continue;
+        L = cand;
+        if (chains * ((p->T + cand - 1) / cand) >= kMinChunks) break;
+      }
     }
   }
   bool use = false;
