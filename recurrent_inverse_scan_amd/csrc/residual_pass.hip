@@ -459,7 +459,8 @@ struct TokRows {
 
 template <typename TIn, bool CAP>
 __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float den_eps, float cap2, int chains, int b_lo, int nb,
-                                                              int32_t* __restrict__ chain_info) {
+                                                              int32_t* __restrict__ chain_info,
+                                                              const int32_t* __restrict__ only_flagged) {
   extern __shared__ float4 smem4[];
   float* R0 = reinterpret_cast<float*>(smem4);   // S_b, then q
   float* R1 = R0 + kMat;                          // W, then k, then o
@@ -482,6 +483,7 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   const int nvalid = min(kB, pl.T - t0);
   const int64_t blk = chain * nblk + b;
   const int64_t tok0 = chain * pl.T + t0;
+  if (only_flagged && only_flagged[blk] == 0) continue;   // uniform per workgroup
 
   // Every global load up front: S_b, W, U, alpha (fp32) and q, k.
   float4 gS[2], gW[2], gU[2], gA[2];
@@ -667,6 +669,229 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Readout on the matrix cores: one workgroup of four waves per (chain, block);
+// wave w computes output tile (tb, ib) = (w >> 1, w & 1) (tokens x values):
+//   E = U - W S_b^T,   O = Q S_b^T + (M o (A_hat Q^T))^T E,
+//   den_t = n_b . q_t + sum_{s <= t} k_s . q_t + den_eps,
+// with M the causal mask s <= t.  A_hat Q^T is computed as its transpose
+// tile CT[s][t] (rows s in accumulator slots, columns t in lanes), which read
+// as the A operand is the (t, s) operand of the product with E.  q and k
+// enter as matrix-core operands loaded straight from HBM (bf16 storage
+// exactly, fp32 as three-term splits).  The per-token norms of the cap test
+// are not formed here: a block whose bound |S_b|_F + sum_s |e_s| exceeds the
+// cap is flagged, and the per-token readout above recomputes it exactly.
+// ---------------------------------------------------------------------------
+template <typename TIn> struct QFrag;
+template <> struct QFrag<uint16_t> {
+  bf16x8 f;
+  __device__ __forceinline__ void load(const uint16_t* p, bool ok) {
+    f = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0));
+  }
+  __device__ __forceinline__ const bf16x8& op() const { return f; }
+};
+template <> struct QFrag<float> {
+  Split3 f;
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    float x[8];
+    const float4 a = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    f = split3(x);
+  }
+  __device__ __forceinline__ const Split3& op() const { return f; }
+};
+__device__ __forceinline__ float frag_dot(const bf16x8& f, const float* nb) {
+  const uint4 u = __builtin_bit_cast(uint4, f);
+  const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    d = fmaf(__uint_as_float(w4[e] << 16), nb[2 * e], d);
+    d = fmaf(__uint_as_float(w4[e] & 0xffff0000u), nb[2 * e + 1], d);
+  }
+  return d;
+}
+__device__ __forceinline__ float frag_dot(const Split3& f, const float* nb) {
+  // t1 + t2 + t3 is the fp32 value exactly.
+  return frag_dot(f.t1, nb) + (frag_dot(f.t2, nb) + frag_dot(f.t3, nb));
+}
+
+template <typename TIn, bool CAP>
+__global__ void __launch_bounds__(256) vla_res_readout_mma_kernel(ResPlan pl, float den_eps, float cap2, int chains,
+                                                                  int b_lo, int nb, int32_t* __restrict__ chain_info,
+                                                                  int32_t* __restrict__ exact_flags) {
+  extern __shared__ float4 smem4[];
+  float* R0 = reinterpret_cast<float*>(smem4);   // S_b
+  float* R1 = R0 + kMat;                          // W, then o
+  float* R2 = R1 + kMat;                          // U, then E
+  float* R3 = R2 + kMat;                          // alpha
+  __shared__ float sNb[kD];
+  __shared__ float sDen[kB];
+  __shared__ float sEn[kB];
+  __shared__ float sSp[4];
+  __shared__ int sFlag;
+
+  const int nblk = pl.nblk;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, lh = lane >> 5;
+  const int w = tid >> 6, tb = w >> 1, ib = w & 1;
+  for (int64_t x = blockIdx.x; x < static_cast<int64_t>(chains) * nb; x += gridDim.x) {
+  const int64_t chain = x / nb;
+  const int b = b_lo + static_cast<int>(x % nb);
+  const int t0 = b * kB;
+  const int nvalid = min(kB, pl.T - t0);
+  const int64_t blk = chain * nblk + b;
+  const int64_t tok0 = chain * pl.T + t0;
+
+  // HBM: S_b, W, U, alpha into LDS; q rows of token block tb and k rows of
+  // blocks sb <= tb as operand fragments.
+  {
+    const float4* s4 = reinterpret_cast<const float4*>(pl.Ssnap + blk * kD * kD);
+    const float4* w4 = reinterpret_cast<const float4*>(pl.W + blk * kB * kD);
+    const float4* u4 = reinterpret_cast<const float4*>(pl.U + blk * kB * kD);
+    const float4* a4 = reinterpret_cast<const float4*>(pl.alpha + tok0 * kD);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int v = tid + 256 * r;
+      put4(R0, v, s4[v]);
+      put4(R1, v, w4[v]);
+      put4(R2, v, u4[v]);
+      put4(R3, v, (v >> 4) < nvalid ? a4[v] : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+  }
+  if (tid < kD) sNb[tid] = pl.nblock[blk * kD + tid];
+  const TIn* qg = static_cast<const TIn*>(pl.q) + tok0 * kD;
+  const TIn* kg = static_cast<const TIn*>(pl.k) + tok0 * kD;
+  QFrag<TIn> qf[4], kf[2][4];
+  {
+    const int tq = 32 * tb + li;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks].load(qg + tq * kD + 16 * ks + 8 * lh, tq < nvalid);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int ts = 32 * sb + li;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[sb][ks].load(kg + ts * kD + 16 * ks + 8 * lh, sb <= tb && ts < nvalid);
+    }
+  }
+  __syncthreads();
+
+  // E tile (tb, ib) = U - W S_b^T, and Q S_b^T into the output accumulator.
+  f32x16 E, O = zero16();
+#pragma unroll
+  for (int s = 0; s < 16; ++s) E[s] = R2[(32 * tb + acc_row(s, lh)) * kP + 32 * ib + li];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const Split3 bs = row_frag(R0 + (32 * ib + li) * kP + 16 * ks + 8 * lh);
+    float wv[8];
+    {
+      const float* p = R1 + (32 * tb + li) * kP + 16 * ks + 8 * lh;
+      const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+      wv[0] = -a.x; wv[1] = -a.y; wv[2] = -a.z; wv[3] = -a.w; wv[4] = -c.x; wv[5] = -c.y; wv[6] = -c.z; wv[7] = -c.w;
+    }
+    E = mma_split(split3(wv), bs, E);
+    O = mma_split(qf[ks].op(), bs, O);
+  }
+  __syncthreads();   // every wave has read its U tile and the W rows
+#pragma unroll
+  for (int s = 0; s < 16; ++s) R2[(32 * tb + acc_row(s, lh)) * kP + 32 * ib + li] = E[s];
+  __syncthreads();
+
+  // (M o (A_hat Q^T))^T E, and the denominators from (M o (K Q^T)).
+  float kq = 0.f;   // sum_{s <= t} k_s . q_t for t = 32 tb + li (this lane's half of s)
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    if (sb > tb) continue;
+    f32x16 CT = zero16(), KQ = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const Split3 af = row_frag(R3 + (32 * sb + li) * kP + 16 * ks + 8 * lh);
+      CT = mma_split(af, qf[ks].op(), CT);
+      KQ = mma_split(kf[sb][ks].op(), qf[ks].op(), KQ);
+    }
+    const int tg = 32 * tb + li;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bool keep = 32 * sb + acc_row(s, lh) <= tg;
+      CT[s] = keep ? CT[s] : 0.f;
+      kq += keep ? KQ[s] : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float ev[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ev[e] = R2[(32 * sb + acc_row(8 * g + e, lh)) * kP + 32 * ib + li];
+      O = mma_split(split_slots(CT, g), split3(ev), O);
+    }
+  }
+  if (ib == 0) {
+    float nq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) nq += frag_dot(qf[ks].op(), sNb + 16 * ks + 8 * lh);
+    float d = kq + nq;
+    d += __shfl_xor(d, 32);
+    if (lh == 0) sDen[32 * tb + li] = d + den_eps;
+  }
+  // Norm bound: |S_b|^2 and |e_t|^2 (thread t = tid >> 2 takes 16 columns).
+  if constexpr (CAP) {
+    const int t = tid >> 2, c16 = 16 * (tid & 3);
+    float e2 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const float ev = R2[t * kP + c16 + c], sv = R0[t * kP + c16 + c];
+      e2 = fmaf(ev, ev, e2);
+      s2 = fmaf(sv, sv, s2);
+    }
+    e2 = group_sum<4>(e2);
+    if ((tid & 3) == 0) sEn[t] = e2;
+    s2 = wave_sum(s2);
+    if (lane == 0) sSp[w] = s2;
+  }
+  __syncthreads();
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int t = 32 * tb + acc_row(s, lh);
+    const float ov = O[s] / sDen[t];
+    bad |= t < nvalid && !isfinite(ov);
+    R1[t * kP + 32 * ib + li] = ov;
+  }
+  if constexpr (CAP) {
+    if (tid < 64) {
+      const float esum = wave_sum(sqrtf(sEn[tid]));
+      const float ssq = (sSp[0] + sSp[1]) + (sSp[2] + sSp[3]);
+      if (tid == 0) sFlag = (sqrtf(ssq) + esum) * (1.f + 1e-5f) > sqrtf(cap2) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) exact_flags[blk] = CAP ? sFlag : 0;
+  {
+    TIn* og = static_cast<TIn*>(pl.o) + tok0 * kD;
+    const int t = tid >> 2, c16 = 16 * (tid & 3);
+    if (t < nvalid) {
+      const float* src = R1 + t * kP + c16;
+      if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(og + t * kD + c16 + 4 * q) = *reinterpret_cast<const float4*>(src + 4 * q);
+      } else {
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wv[e] = static_cast<uint32_t>(f32_to_bf16(src[8 * h8 + 2 * e])) |
+                    (static_cast<uint32_t>(f32_to_bf16(src[8 * h8 + 2 * e + 1])) << 16);
+          *reinterpret_cast<uint4*>(og + t * kD + c16 + 8 * h8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+      }
+    }
+  }
+  if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
+  __syncthreads();   // the next block overwrites the LDS this one read last
+  }
+}
+
 template <typename K>
 void allow_lds(K kernel, size_t bytes) {
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -716,21 +941,35 @@ hipError_t launch_res_chain(const ResPlan& pl, int b_lo, int b_hi, const float* 
 hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains, int b_lo, int nb,
                               int max_wg, int32_t* chain_info, hipStream_t stream) {
   if (nb <= 0) return hipSuccess;
-  const size_t lds = 4 * kMat * sizeof(float);
   const dim3 grid(side_grid(static_cast<int64_t>(chains) * nb, max_wg));
   const float cap2 = cap * cap;
-#define VLA_RES_READOUT(T, C)                                                                                  \
-  do {                                                                                                         \
-    allow_lds(vla_res_readout_kernel<T, C>, lds);                                                              \
-    hipLaunchKernelGGL((vla_res_readout_kernel<T, C>), grid, dim3(512), lds, stream, pl, den_eps, cap2, chains, \
-                       b_lo, nb, chain_info);                                                                  \
+  const size_t lds_mma = 4 * kMat * sizeof(float);
+#define VLA_RES_READOUT_MMA(T, C)                                                                               \
+  do {                                                                                                          \
+    allow_lds(vla_res_readout_mma_kernel<T, C>, lds_mma);                                                       \
+    hipLaunchKernelGGL((vla_res_readout_mma_kernel<T, C>), grid, dim3(256), lds_mma, stream, pl, den_eps, cap2, \
+                       chains, b_lo, nb, chain_info, pl.exact);                                                 \
   } while (0)
   if (pl.bf16) {
-    if (cap_on) VLA_RES_READOUT(uint16_t, true); else VLA_RES_READOUT(uint16_t, false);
+    if (cap_on) VLA_RES_READOUT_MMA(uint16_t, true); else VLA_RES_READOUT_MMA(uint16_t, false);
   } else {
-    if (cap_on) VLA_RES_READOUT(float, true); else VLA_RES_READOUT(float, false);
+    if (cap_on) VLA_RES_READOUT_MMA(float, true); else VLA_RES_READOUT_MMA(float, false);
   }
-#undef VLA_RES_READOUT
+#undef VLA_RES_READOUT_MMA
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !cap_on) return e;
+  // Blocks whose norm bound exceeds the cap: the per-token readout, with the
+  // exact cap test (the others return at once).
+  const size_t lds = 4 * kMat * sizeof(float);
+  if (pl.bf16) {
+    allow_lds(vla_res_readout_kernel<uint16_t, true>, lds);
+    hipLaunchKernelGGL((vla_res_readout_kernel<uint16_t, true>), grid, dim3(512), lds, stream, pl, den_eps, cap2,
+                       chains, b_lo, nb, chain_info, pl.exact);
+  } else {
+    allow_lds(vla_res_readout_kernel<float, true>, lds);
+    hipLaunchKernelGGL((vla_res_readout_kernel<float, true>), grid, dim3(512), lds, stream, pl, den_eps, cap2,
+                       chains, b_lo, nb, chain_info, pl.exact);
+  }
   return hipGetLastError();
 }
 

@@ -172,7 +172,7 @@ struct ChunkLayout {
          off_ncarry = 0, off_cnt = 0, off_flag = 0,
          total = 0;
   // Residual update's state pass (replaces the additive one's buffers).
-  size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0;
+  size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0, off_rex = 0;
 };
 
 // Whether the chunked schedule can run these parameters with chunk length L.
@@ -244,6 +244,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       cl.off_rS = off; off = align_up(off + C * nb * d2 * 4);
       cl.off_rnb = off; off = align_up(off + C * nb * 64 * 4);
       cl.off_rnc = off; off = align_up(off + 2 * C * 64 * 4);   // normaliser carries between segments
+      cl.off_rex = off; off = align_up(off + C * nb * 4);       // per-block exact cap-test flags
       cl.off_flag = off;
       if (p->validate) off += kValidateBytes;
       cl.total = off;
@@ -499,6 +500,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     rp.ksum = reinterpret_cast<float*>(ws + cl.off_rks);
     rp.Ssnap = reinterpret_cast<float*>(ws + cl.off_rS);
     rp.nblock = reinterpret_cast<float*>(ws + cl.off_rnb);
+    rp.exact = reinterpret_cast<int32_t*>(ws + cl.off_rex);
     const int nch = static_cast<int>(chains);
     const int nblk = cl.nblk;
     // Segments as for the additive pass: the chain kernel runs them in order

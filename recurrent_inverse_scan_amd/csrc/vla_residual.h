@@ -22,6 +22,7 @@ struct ResPlan {
   float* ksum;           // [chains][nblk][64] sum of the block's keys
   float* Ssnap;          // [chains][nblk][64][64] S at each block start
   float* nblock;         // [chains][nblk][64] normaliser at each block start
+  int32_t* exact;        // [chains][nblk] the block needs the per-token cap test
 };
 // Block ranges [b_lo, b_lo + nb) of every chain; at most max_wg workgroups
 // if max_wg > 0 (grid-stride).
