@@ -46,12 +46,17 @@
 
 namespace vla {
 
+// Scalars of the blocked rank-r update: u_i . w_l (4 x 4) and k . w_l (4).
+constexpr int kBlkScalars = 20;
+
 template <typename TIn, int D, int NW, int CG, SeqMode MODE, bool RES>
 __global__ void __launch_bounds__(64 * NW)
 vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   static_assert(!RES || MODE == SeqMode::kFull, "the residual update runs in the full recurrence only");
   using L = TileLayout<D, NW, CG>;
   constexpr int R = L::R, C = L::C, RW = L::RW, NTH = L::kThreads;
+  constexpr int kGroups = NW * 64 / CG;          // row groups of the workgroup
+  constexpr int kBlkStride = kGroups + 4;         // LDS row of one blocked-update scalar
   constexpr bool kFull = MODE == SeqMode::kFull;
   constexpr bool kInv = MODE == SeqMode::kInverseOnly;
   constexpr bool kHasA = MODE != SeqMode::kStateOnly;   // runs the inverse recurrence
@@ -85,6 +90,8 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   float* zbuf = astage + (kHasA ? 0 : 2 * TT * D);           // [2][D]
   float* abuf = zbuf + 2 * D;                                // [2][D]
   float* red = abuf + 2 * D;                                 // [2][NW][4]
+  float* zb4 = red + 2 * NW * 4;                             // [4][D] z rows of the blocked rank-r update
+  float* scl = zb4 + 4 * D;                                  // [kBlkScalars][kBlkStride] row-group partials
 
   // ---- initial state --------------------------------------------------
   float A[kHasA ? R : 1][kHasA ? C : 4];
@@ -200,8 +207,146 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
         float y[R];
         bool last_fired = false;
 
+        // ---- r > 1: the r sub-updates in one sweep and one rank-r update ----
+        // With w_l = A u_l (A before the token), the sequential steps satisfy
+        // z_i = w_i - sum_{j<i} z_j (z_j . u_i) / delta_j: each z_i is a
+        // combination of the w_l, so every z_j . u_i, z_i . k and delta_i
+        // follow from the products u_i . w_l and k . w_l by the same
+        // recurrence.  A then takes the whole update A - sum_i z_i z_i^T / delta_i
+        // and A_t k = A k - sum_i z_i (z_i . k) / delta_i.  One chain-wide
+        // reduction and one broadcast replace r of each.  Should any delta
+        // trip the guard, the token runs the sub-updates one by one instead
+        // (A is untouched until then).
+        bool blocked = false;
+        if (r > 1) {
+          float wl[4][R], wk[R];
+          float kJ[C];
+          lds_cols<CG, C>(tk, cg, kJ);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], kJ[c], acc);
+            wk[ii] = group_sum<CG>(acc);
+          }
+#pragma unroll
+          for (int l = 0; l < 4; ++l) {
+            if (l < r) {
+              float uJ[C];
+              lds_cols<CG, C>(tblk + (row_u + l) * D, cg, uJ);
+#pragma unroll
+              for (int ii = 0; ii < R; ++ii) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], uJ[c], acc);
+                wl[l][ii] = group_sum<CG>(acc);
+              }
+            } else {
+#pragma unroll
+              for (int ii = 0; ii < R; ++ii) wl[l][ii] = 0.f;
+            }
+          }
+          // Scalars: sc[4 i + l] = u_i . w_l (i, l < r) and sc[16 + l] = k . w_l.
+          // Each row group's leader writes its partials to LDS, lane e of every
+          // wave sums scalar e over the row groups, and readlane broadcasts.
+          float sc[kBlkScalars];
+          if (cg == 0) {
+            float* dst = scl + w * (64 / CG) + rg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float uI[R];
+              if (i < r) lds_rows<R>(tblk + (row_u + i) * D + row0, uI);
+#pragma unroll
+              for (int l = 0; l < 4; ++l) {
+                float acc = 0.f;
+                if (i < r && l < r) {
+#pragma unroll
+                  for (int ii = 0; ii < R; ++ii) acc = fmaf(uI[ii], wl[l][ii], acc);
+                }
+                dst[(4 * i + l) * kBlkStride] = acc;
+              }
+            }
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+              float acc = 0.f;
+#pragma unroll
+              for (int ii = 0; ii < R; ++ii) acc = fmaf(kI[ii], wl[l][ii], acc);
+              dst[(16 + l) * kBlkStride] = acc;
+            }
+          }
+          __syncthreads();
+          {
+            float t = 0.f;
+            if (lane < kBlkScalars) {
+              const float4* src4 = reinterpret_cast<const float4*>(scl + lane * kBlkStride);
+              float4 acc4 = src4[0];
+#pragma unroll
+              for (int g = 1; g < kGroups / 4; ++g) {
+                const float4 v4 = src4[g];
+                acc4.x += v4.x; acc4.y += v4.y; acc4.z += v4.z; acc4.w += v4.w;
+              }
+              t = (acc4.x + acc4.y) + (acc4.z + acc4.w);
+            }
+#pragma unroll
+            for (int e = 0; e < kBlkScalars; ++e)
+              sc[e] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), e));
+          }
+          // The recurrence, in place: row i of wl becomes z_i, and the scalars
+          // follow it (sc[4 m + i] = u_m . z_i, sc[16 + i] = k . z_i).
+          float dl[4], dinv[4];
+          bool fire = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dl[i] = 1.f;
+            dinv[i] = 1.f;
+            if (i < r) {
+#pragma unroll
+              for (int j = 0; j < i; ++j) {
+                const float f = sc[4 * i + j] * dinv[j];   // (z_j . u_i) / delta_j
+#pragma unroll
+                for (int ii = 0; ii < R; ++ii) wl[i][ii] = fmaf(-f, wl[j][ii], wl[i][ii]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) sc[4 * m + i] = fmaf(-f, sc[4 * m + j], sc[4 * m + i]);
+                sc[16 + i] = fmaf(-f, sc[16 + j], sc[16 + i]);
+              }
+              dl[i] = 1.f + sc[4 * i + i];
+              dinv[i] = 1.f / dl[i];
+              fire |= fabsf(dl[i]) < a.eps;
+            }
+          }
+          if (!fire) {
+            blocked = true;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i < r && cg == 0) lds_store_rows<R>(zb4 + i * D + row0, wl[i]);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i < r) {
+                float zJ[C];
+                lds_cols<CG, C>(zb4 + i * D, cg, zJ);
+                const float inv = dinv[i];
+#pragma unroll
+                for (int ii = 0; ii < R; ++ii) {
+                  const float zs = wl[i][ii] * inv;
+#pragma unroll
+                  for (int c = 0; c < C; ++c) A[ii][c] = fmaf(-zs, zJ[c], A[ii][c]);
+                }
+              }
+            }
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) {
+              float yy = wk[ii];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (i < r) yy = fmaf(-wl[i][ii], sc[16 + i] * dinv[i], yy);
+              y[ii] = yy;
+            }
+          }
+        }
+
         // ---- r guarded Sherman-Morrison sub-updates -----------------------
-        for (int i = 0; i < r; ++i) {
+        for (int i = 0; i < (blocked ? 0 : r); ++i) {
           const float* tu = tblk + (row_u + i) * D;
           const bool last = (i == r - 1);
           float uJ[C];
@@ -488,7 +633,9 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
 
 template <typename TIn, int D, int NW, int CG, SeqMode MODE>
 static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, hipStream_t stream) {
-  const size_t lds = seq_lds_bytes<TIn, D, NW>(MODE, a.r);
+  // The stages and vectors, then the blocked rank-r update's z rows and scalars.
+  const size_t lds =
+      seq_lds_bytes<TIn, D, NW>(MODE, a.r) + sizeof(float) * (4 * D + kBlkScalars * (NW * 64 / CG + 4));
   const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.chunk_cnt)
                                                        : static_cast<unsigned>(chains);
   if constexpr (MODE == SeqMode::kFull) {

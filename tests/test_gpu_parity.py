@@ -119,6 +119,29 @@ def test_guard_fire_householder_start():
     _check(cfg, out, ref)
 
 
+# For r > 1 the kernels apply a token's r rank-1 updates as one rank-r update
+# unless a delta trips the guard; then the token runs them one at a time.
+@pytest.mark.parametrize("d,T", [(64, 20), (64, 5), (128, 20)])
+@pytest.mark.parametrize("r,at", [(2, 0), (2, 1), (3, 1), (4, 2)])
+def test_guard_fire_in_a_rank_r_token(d, T, r, at):
+    """A0 = I - 2 e e^T; direction `at` of the first token is e and the earlier
+    ones are orthogonal unit vectors, so that direction's delta is exactly 0."""
+    cfg = CONFIGS["base"].with_(name=f"guard-r{r}-at{at}-d{d}-T{T}", B=1, H=2, T=T, d=d, r=r, nudge_period=0,
+                                s_cap=None)
+    x = case(cfg, seed=40 + r + at)
+    u = x["u"].clone()
+    eye = torch.eye(d)
+    for j in range(at):
+        u[:, :, 0, j, :] = eye[11 + j]
+    u[:, :, 0, at, :] = eye[5]
+    x["u"] = u
+    A0 = (eye - 2 * torch.outer(eye[5], eye[5])).expand(1, 2, d, d).contiguous()
+    out = _gpu(x, cfg, A0=A0.to(DEV))
+    ref = run_oracle(x, cfg, A0=A0.reshape(2, d, d))
+    assert (ref["guard_fires"] == 1).all()
+    _check(cfg, out, ref)
+
+
 def test_cap_forced_every_step():
     cfg = CONFIGS["base"].with_(name="cap1", B=1, H=2, T=50, nudge_period=0, s_cap=1.0)
     x = case(cfg, seed=4)
