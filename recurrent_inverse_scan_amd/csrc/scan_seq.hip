@@ -122,6 +122,11 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   }
 
   int guard_fires = 0, cap_fires = 0, first_cap = -1;
+  // The eps*I shifts (guard and nudge) are carried as a scalar: the tracked
+  // inverse is A + shift*I, and the registers hold A.  Matrix-vector products
+  // add shift*x, rank-1 updates apply to A unchanged, and the final store
+  // folds shift into the diagonal.  The shifts then cost no register sweep.
+  float shift = 0.f;
   bool bad = false;
   int par = 0;
   // (t0 + 1 + t) mod P for the current token t.
@@ -227,19 +232,20 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
             float acc = 0.f;
 #pragma unroll
             for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], kJ[c], acc);
-            wk[ii] = group_sum<CG>(acc);
+            wk[ii] = fmaf(shift, kI[ii], group_sum<CG>(acc));
           }
 #pragma unroll
           for (int l = 0; l < 4; ++l) {
             if (l < r) {
-              float uJ[C];
+              float uJ[C], uR[R];
               lds_cols<CG, C>(tblk + (row_u + l) * D, cg, uJ);
+              lds_rows<R>(tblk + (row_u + l) * D + row0, uR);
 #pragma unroll
               for (int ii = 0; ii < R; ++ii) {
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < C; ++c) acc = fmaf(A[ii][c], uJ[c], acc);
-                wl[l][ii] = group_sum<CG>(acc);
+                wl[l][ii] = fmaf(shift, uR[ii], group_sum<CG>(acc));
               }
             } else {
 #pragma unroll
@@ -374,10 +380,12 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           for (int ii = 0; ii < R; ++ii) z[ii] = group_sum<CG>(z[ii]);
           if (last) {
 #pragma unroll
-            for (int ii = 0; ii < R; ++ii) y[ii] = group_sum<CG>(y[ii]);
+            for (int ii = 0; ii < R; ++ii) y[ii] = fmaf(shift, kI[ii], group_sum<CG>(y[ii]));
           }
           float uI[R];
           lds_rows<R>(tu + row0, uI);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) z[ii] = fmaf(shift, uI[ii], z[ii]);
           float du = 0.f, dk = 0.f;
 #pragma unroll
           for (int ii = 0; ii < R; ++ii) {
@@ -398,15 +406,19 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
             for (int ww = 0; ww < NW; ++ww) { du += red[(par * NW + ww) * 4 + 0]; dk += red[(par * NW + ww) * 4 + 1]; }
           }
           const float delta = 1.f + du;
-          if (fabsf(delta) < a.eps) {
+          const bool fire = fabsf(delta) < a.eps;
+          if (fire) {
             // Singularity guard: inject eps*I and skip this rank-1 update.
             ++guard_fires;
-            add_to_diagonal<R, C, CG>(A, row0, cg, a.eps);
+            shift += a.eps;
             if (last) last_fired = true;
-          } else {
+          }
+          // The update runs either way, with a zero coefficient when the guard
+          // fired: A then stays in the same registers on both paths.
+          const float inv = fire ? 0.f : 1.f / delta;
+          {
             float zJ[C];
             lds_cols<CG, C>(zb, cg, zJ);
-            const float inv = 1.f / delta;
 #pragma unroll
             for (int ii = 0; ii < R; ++ii) {
               const float zs = z[ii] * inv;
@@ -430,7 +442,7 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           if (phase == 0) {
 #pragma unroll
             for (int ii = 0; ii < R; ++ii) alpha[ii] = fmaf(a.eps, kI[ii], alpha[ii]);
-            add_to_diagonal<R, C, CG>(A, row0, cg, a.eps);
+            shift += a.eps;
           }
           phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
         }
@@ -567,6 +579,7 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
 
   // ---- final state and statistics ---------------------------------------
   const bool write_a = kFull || (kInv && chunk == x.nchunks - 1);
+  if constexpr (kHasA) add_to_diagonal<R, C, CG>(A, row0, cg, shift);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int row = row0 + i;
