@@ -708,10 +708,13 @@ static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int 
 
 // One-token calls at d = 64 (decode.hip).
 hipError_t launch_decode(const ScanArgs& a, bool bf16, int chains, hipStream_t stream);
+hipError_t launch_scan_split(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream);
 
 hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, const int32_t* only_if,
                                   hipStream_t stream) {
   if (a.T == 1 && d == 64 && only_if == nullptr) return launch_decode(a, bf16, chains, stream);
+  // Longer runs at d <= 64: the inverse and state recurrences on two waves.
+  if (a.T > kShortCallTokens && d <= 64 && only_if == nullptr) return launch_scan_split(a, d, bf16, chains, stream);
   SeqExtra x{};
   x.only_if = only_if;
   return bf16 ? dispatch_seq<uint16_t, SeqMode::kFull>(a, x, d, chains, stream)

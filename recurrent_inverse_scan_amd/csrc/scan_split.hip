@@ -1,0 +1,372 @@
+// Sequential VLA scan for d <= 64 with the two recurrences on two waves.
+//
+// Method as in the sequential kernel ("Mathematical Primitives", sections
+// 2-5; "Variational Linear Attention (VLA)" README, v3 notes; the residual
+// update from "Variational Linear Attention: Stable Associative Memory for
+// Long-Context Transformers", technical summary 2.3).  Per token the inverse
+// recurrence (r guarded Sherman-Morrison updates of A, the nudge, alpha = A k
+// and its normalisation) never reads the state S, and the state recurrence
+// (S += w alpha_hat^T, the cap, n += k, the readout) needs only alpha_hat
+// from it.  So one workgroup of two waves runs a chain: wave 0 the inverse
+// side, wave 1 the state side one LDS stage (8 tokens) behind, alpha_hat
+// passed through LDS.  A token then costs the longer of the two halves
+// instead of their sum; each wave keeps only its own matrix in registers.
+//
+// Synchronisation: every loop iteration ends with the one workgroup barrier,
+// taken by both waves the same number of times (the trip count depends on T
+// only).  Inside a side, the vector broadcasts go through LDS within one
+// wave: the hardware completes a wave's LDS operations in issue order, and
+// lds_order() keeps the compiler from moving a load above an earlier store.
+// Stage buffers rotate over three slots: the one being filled, the one the
+// inverse wave reads, the one the state wave reads.
+#include "vla_common.h"
+#include "vla_kernels.h"
+#include "vla_seq.h"
+
+namespace vla {
+
+namespace {
+
+constexpr int kSplitTT = 8;      // tokens per LDS stage
+constexpr int kSplitSlots = 3;   // stage buffers in rotation
+constexpr int kSplitThreads = 128;
+
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+template <typename TIn, int D, int CG, bool RES>
+__global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs a) {
+  using L = TileLayout<D, 1, CG>;
+  constexpr int R = L::R, C = L::C;
+  extern __shared__ float4 smem4[];
+  float* smem = reinterpret_cast<float*>(smem4);
+
+  const int64_t chain = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool inverse_side = tid < 64;
+  const int cg = lane % CG, rg = lane / CG;
+  const int row0 = rg * R;
+  const int r = a.r;
+  const int NV = 3 + r;   // q, k, v, u_1..u_r
+  constexpr int row_q = 0, row_k = 1, row_v = 2, row_u = 3;
+  const int slot_floats = kSplitTT * NV * D;
+
+  float* stage = smem;                                   // [3][TT][NV][D]
+  float* ahat = stage + kSplitSlots * slot_floats;       // [2][TT][D]
+  float* zb = ahat + 2 * kSplitTT * D;                   // [D]
+  float* fin = zb + D;                                   // [8] per-side statistics
+
+  const int64_t tok0 = chain * a.T;
+  RowSource<TIn, D> src;
+  src.n = NV;
+  src.nfix = 3;
+  src.fix0 = static_cast<const TIn*>(a.q) + tok0 * D;
+  src.fix1 = static_cast<const TIn*>(a.k) + tok0 * D;
+  src.fix2 = static_cast<const TIn*>(a.v) + tok0 * D;
+  src.ubase = static_cast<const TIn*>(a.u) + tok0 * r * D;
+  src.ustride = static_cast<int64_t>(r) * D;
+  Stager<TIn, D, kSplitThreads> st;
+
+  // Registers of each side: A on the inverse wave, S and n on the state wave.
+  float M[R][C], n[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int row = row0 + i;
+#pragma unroll
+    for (int m = 0; m < C / 4; ++m) {
+      const int col = (m * CG + cg) * 4;
+      float4 mv;
+      if (inverse_side) {
+        mv = make_float4(row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f, row == col + 2 ? 1.f : 0.f,
+                         row == col + 3 ? 1.f : 0.f);
+        if (a.A0) mv = *reinterpret_cast<const float4*>(a.A0 + (chain * D + row) * D + col);
+      } else {
+        mv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.S0) mv = *reinterpret_cast<const float4*>(a.S0 + (chain * D + row) * D + col);
+      }
+      M[i][4 * m] = mv.x; M[i][4 * m + 1] = mv.y; M[i][4 * m + 2] = mv.z; M[i][4 * m + 3] = mv.w;
+    }
+    n[i] = (!inverse_side && a.n0) ? a.n0[chain * D + row] : 0.f;
+  }
+
+  int guard_fires = 0, cap_fires = 0, first_cap = -1;
+  bool bad = false;
+  // The eps*I shifts are carried as a scalar: the inverse is M + shift*I.
+  float shift = 0.f;
+  int phase = a.nudge_period > 0 ? a.nudge_phase0 % a.nudge_period : 0;
+  const float cap2 = a.cap * a.cap;
+
+  const int nstage = (a.T + kSplitTT - 1) / kSplitTT;
+  if (nstage > 0) {
+    st.load(src, 0, kSplitTT, a.T, tid);
+    st.store(stage, kSplitTT, NV, tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it <= nstage; ++it) {
+    if (it + 1 < nstage) st.load(src, (it + 1) * kSplitTT, kSplitTT, a.T, tid);
+
+    if (inverse_side && it < nstage) {
+      // ---- inverse recurrence over stage it ------------------------------
+      const float* sbuf = stage + (it % kSplitSlots) * slot_floats;
+      float* aout = ahat + (it & 1) * kSplitTT * D;
+      const int tcount = min(kSplitTT, a.T - it * kSplitTT);
+      for (int tt = 0; tt < tcount; ++tt) {
+        const float* tblk = sbuf + tt * NV * D;
+        const float* tk = tblk + row_k * D;
+        float kI[R], y[R];
+        lds_rows<R>(tk + row0, kI);
+        bool last_fired = false;
+        for (int i = 0; i < r; ++i) {
+          const float* tu = tblk + (row_u + i) * D;
+          const bool last = i == r - 1;
+          float uJ[C], z[R];
+          lds_cols<CG, C>(tu, cg, uJ);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc = fmaf(M[ii][c], uJ[c], acc);
+            z[ii] = acc;
+          }
+          if (last) {
+            float kJ[C];
+            lds_cols<CG, C>(tk, cg, kJ);
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) {
+              float acc = 0.f;
+#pragma unroll
+              for (int c = 0; c < C; ++c) acc = fmaf(M[ii][c], kJ[c], acc);
+              y[ii] = fmaf(shift, kI[ii], group_sum<CG>(acc));
+            }
+          }
+          float uI[R];
+          lds_rows<R>(tu + row0, uI);
+          float du = 0.f, dk = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            z[ii] = fmaf(shift, uI[ii], group_sum<CG>(z[ii]));
+            du = fmaf(z[ii], uI[ii], du);
+            dk = fmaf(z[ii], kI[ii], dk);
+          }
+          du = wave_sum(cg == 0 ? du : 0.f);
+          if (last) dk = wave_sum(cg == 0 ? dk : 0.f);
+          lds_order();   // the previous sub-update's reads of zb come first
+          if (cg == 0) lds_store_rows<R>(zb + row0, z);
+          lds_order();
+          const float delta = 1.f + du;
+          const bool fire = fabsf(delta) < a.eps;
+          if (fire) {
+            // Singularity guard: inject eps*I and skip this rank-1 update.
+            ++guard_fires;
+            shift += a.eps;
+            if (last) last_fired = true;
+          }
+          // A zero coefficient when the guard fired keeps A in place.
+          const float inv = fire ? 0.f : 1.f / delta;
+          float zJ[C];
+          lds_cols<CG, C>(zb, cg, zJ);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            const float zs = z[ii] * inv;
+#pragma unroll
+            for (int c = 0; c < C; ++c) M[ii][c] = fmaf(-zs, zJ[c], M[ii][c]);
+          }
+          if (last) {
+            const float g = dk * inv;
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) y[ii] = fmaf(-z[ii], g, y[ii]);
+          }
+        }
+        // Nudge, coefficient and its normalisation.
+        float alpha[R];
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) alpha[ii] = last_fired ? fmaf(a.eps, kI[ii], y[ii]) : y[ii];
+        if (a.nudge_period > 0) {
+          if (phase == 0) {
+#pragma unroll
+            for (int ii = 0; ii < R; ++ii) alpha[ii] = fmaf(a.eps, kI[ii], alpha[ii]);
+            shift += a.eps;
+          }
+          phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
+        }
+        float an = 0.f, kn = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          an = fmaf(alpha[ii], alpha[ii], an);
+          kn = fmaf(kI[ii], kI[ii], kn);
+        }
+        an = wave_sum(cg == 0 ? an : 0.f);
+        float ascale;
+        if constexpr (RES) {
+          // The unit vector along A k_hat, k_hat = k / |k|.
+          kn = wave_sum(cg == 0 ? kn : 0.f);
+          const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+          ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
+        } else {
+          ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+        }
+        if (cg == 0) {
+          float ah[R];
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            ah[ii] = alpha[ii] * ascale;
+            bad |= !isfinite(ah[ii]);
+          }
+          lds_store_rows<R>(aout + tt * D + row0, ah);
+        }
+      }
+    } else if (!inverse_side && it >= 1) {
+      // ---- state recurrence over stage it - 1 ----------------------------
+      const int sidx = it - 1;
+      const float* sbuf = stage + (sidx % kSplitSlots) * slot_floats;
+      const float* ain = ahat + (sidx & 1) * kSplitTT * D;
+      const int tb = sidx * kSplitTT;
+      const int tcount = min(kSplitTT, a.T - tb);
+      for (int tt = 0; tt < tcount; ++tt) {
+        const int t = tb + tt;
+        const float* tblk = sbuf + tt * NV * D;
+        const float* tq = tblk + row_q * D;
+        const float* tk = tblk + row_k * D;
+        const float* tv = tblk + row_v * D;
+        float kI[R], vI[R], qI[R], qJ[C], aJ[C];
+        lds_rows<R>(tk + row0, kI);
+        lds_rows<R>(tv + row0, vI);
+        if constexpr (RES) {
+          // v - S_{t-1} k_hat, the prediction taken before the update.
+          float kJ[C];
+          lds_cols<CG, C>(tk, cg, kJ);
+          float kn = 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) kn = fmaf(kJ[c], kJ[c], kn);
+          kn = group_sum<CG>(kn);
+          const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc = fmaf(M[ii][c], kJ[c], acc);
+            vI[ii] = fmaf(-group_sum<CG>(acc), kinv, vI[ii]);
+          }
+        }
+        lds_rows<R>(tq + row0, qI);
+        lds_cols<CG, C>(tq, cg, qJ);
+        lds_cols<CG, C>(ain + tt * D, cg, aJ);
+        float ns = 0.f, po[R];
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          float acc = 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            M[ii][c] = fmaf(vI[ii], aJ[c], M[ii][c]);
+            ns = fmaf(M[ii][c], M[ii][c], ns);
+            acc = fmaf(M[ii][c], qJ[c], acc);
+          }
+          po[ii] = group_sum<CG>(acc);
+        }
+        float nq = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < R; ++ii) {
+          n[ii] += kI[ii];
+          nq = fmaf(n[ii], qI[ii], nq);
+        }
+        ns = wave_sum(ns);
+        nq = wave_sum(cg == 0 ? nq : 0.f);
+        float oscale = 1.f;
+        if (a.cap_on && ns > cap2) {
+          // Frobenius renormalisation: S <- S * cap / |S|_F.
+          oscale = a.cap / sqrtf(ns);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+            for (int c = 0; c < C; ++c) M[ii][c] *= oscale;
+          if (first_cap < 0) first_cap = t;
+          ++cap_fires;
+        }
+        const float f = oscale / (nq + a.den_eps);
+        if (cg == 0) {
+          TIn* op = static_cast<TIn*>(a.o) + (tok0 + t) * D + row0;
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) {
+            const float ov = po[ii] * f;
+            bad |= !isfinite(ov);
+            Elem<TIn>::store(op + ii, ov);
+          }
+        }
+      }
+    }
+
+    if (it + 1 < nstage) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, kSplitTT, NV, tid);
+    __syncthreads();
+  }
+
+  // ---- final state and statistics ---------------------------------------
+  if (inverse_side) add_to_diagonal<R, C, CG>(M, row0, cg, shift);
+  float* dstM = inverse_side ? a.A_T : a.S_T;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int row = row0 + i;
+#pragma unroll
+    for (int m = 0; m < C / 4; ++m) {
+      const int col = (m * CG + cg) * 4;
+      *reinterpret_cast<float4*>(dstM + (chain * D + row) * D + col) =
+          make_float4(M[i][4 * m], M[i][4 * m + 1], M[i][4 * m + 2], M[i][4 * m + 3]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bad |= !isfinite(M[i][4 * m + c]);
+    }
+    if (!inverse_side && cg == 0) {
+      a.n_T[chain * D + row] = n[i];
+      bad |= !isfinite(n[i]);
+    }
+  }
+  if (a.stats) {
+    const bool wave_bad = __any(bad);
+    if (lane == 0) {
+      if (inverse_side) {
+        fin[0] = static_cast<float>(guard_fires);
+        fin[1] = wave_bad ? 1.f : 0.f;
+      } else {
+        fin[2] = static_cast<float>(cap_fires);
+        fin[3] = static_cast<float>(first_cap);
+        fin[4] = wave_bad ? 1.f : 0.f;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int32_t* s = a.stats + chain * 4;
+      s[0] = static_cast<int32_t>(fin[0]);
+      s[1] = static_cast<int32_t>(fin[2]);
+      s[2] = (fin[1] != 0.f || fin[4] != 0.f) ? 1 : 0;
+      s[3] = static_cast<int32_t>(fin[3]);
+    }
+  }
+}
+
+template <typename TIn, int D, int CG>
+hipError_t launch_split(const ScanArgs& a, int chains, hipStream_t stream) {
+  using L = TileLayout<D, 1, CG>;
+  static_assert(L::R >= 1, "layout");
+  const int NV = 3 + a.r;
+  // Every stage fits the staging registers of the workgroup.
+  if (kSplitTT * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kSplitThreads) return hipErrorInvalidValue;
+  const size_t lds = sizeof(float) * (static_cast<size_t>(kSplitSlots) * kSplitTT * NV * D + 2 * kSplitTT * D + D + 8);
+  const dim3 grid(static_cast<unsigned>(chains));
+  if (a.residual)
+    hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, true>), grid, dim3(kSplitThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, false>), grid, dim3(kSplitThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_split(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream) {
+  if (chains <= 0) return hipSuccess;
+  switch (d) {
+    case 16: return bf16 ? launch_split<uint16_t, 16, 4>(a, chains, stream) : launch_split<float, 16, 4>(a, chains, stream);
+    case 32: return bf16 ? launch_split<uint16_t, 32, 4>(a, chains, stream) : launch_split<float, 32, 4>(a, chains, stream);
+    case 64: return bf16 ? launch_split<uint16_t, 64, 4>(a, chains, stream) : launch_split<float, 64, 4>(a, chains, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vla
