@@ -56,6 +56,14 @@ CHAIN = {
 }
 
 
+def seq_kernel_name(d: int, T: int) -> str:
+    """The kernel the sequential schedule launches: calls longer than 16 tokens
+    at d <= 64 run the two-wave kernel, T = 1 at d = 64 the decode kernel."""
+    if T == 1 and d == 64:
+        return "vla_decode_kernel"
+    return "vla_scan_split_kernel" if (d <= 64 and T > 16) else "vla_scan_seq_kernel"
+
+
 def alg_flops_per_token_head(d: int, r: int, update: str = "additive") -> int:
     """2 (2r + 3) d^2: r rank-1 updates (product and update, 2 d^2 each), the
     coefficient A k, the state update and the readout; the residual update
@@ -200,7 +208,7 @@ def main(argv=None) -> int:
     else:   # the sequential schedule has no chain kernel: the scan kernel is the dominant one
         roofline = {"bound": "alu", "achieved": scan_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": scan_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
-                    "kernel": "vla_scan_seq_kernel", "kernel_ms": scan_ms, "launches_per_step": 1,
+                    "kernel": seq_kernel_name(d, T), "kernel_ms": scan_ms, "launches_per_step": 1,
                     "flops_per_step": flops}
     es = 2 if cfg.in_dtype == "bf16" else 4
     scan_bytes = tok_heads * d * es * (4 + r) + 2 * B * H * (2 * d * d + d) * 4   # q,k,v,u in, o out, state
@@ -304,7 +312,7 @@ def extra_measurements(CONFIGS, dev):
             "workload": f"{name}: residual update, B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
                         f"{sched} schedule", "ms": ms, "tokens_heads_per_s": th / (ms * 1e-3),
             "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
-            "kernel": "vla_res_chain_kernel" if sched == "chunked" else "vla_scan_seq_kernel"}
+            "kernel": "vla_res_chain_kernel" if sched == "chunked" else seq_kernel_name(d, T)}
         del q, k, v, u, o, x, ws
 
     # The other workloads (additive update), each on the schedule the library
@@ -355,7 +363,7 @@ def extra_measurements(CONFIGS, dev):
             "workload": f"decode: {upd} update, T=1 per call, B={B} H={H} d={d} r={r}, bf16 "
                         f"token storage, f32 state in HBM carried in place", "ms": ms,
             "tokens_heads_per_s": chains / (ms * 1e-3), "alg_bytes": alg_bytes, "hbm_gbs": gbs,
-            "hbm_frac": gbs / HBM_PEAK_GBS, "kernel": "vla_scan_seq_kernel"}
+            "hbm_frac": gbs / HBM_PEAK_GBS, "kernel": seq_kernel_name(d, 1)}
     return out
 
 
