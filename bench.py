@@ -335,7 +335,8 @@ def extra_measurements(CONFIGS, dev):
         out[f"additive_{name}"] = {
             "workload": f"{name}: additive update, B={B} H={H} T={T} d={d} r={r}, {cfg.in_dtype} storage, "
                         f"{sched} schedule", "ms": ms, "tokens_heads_per_s": th / (ms * 1e-3),
-            "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS}
+            "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
+            "kernel": "vla_state_chain_kernel" if sched == "chunked" else seq_kernel_name(d, T)}
         del q, k, v, u, o, x, ws
 
     # Decode: 4096 chains, one token per call, state carried in place.

@@ -33,6 +33,16 @@ constexpr int kSplitThreads = 128;
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+// Sum over the wave by DPP alone: row sums, then the gfx9 row broadcasts
+// (lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and
+// 3), so lane 63 holds the total; one readlane makes it wave-uniform.
+__device__ __forceinline__ float wave_total(float x) {
+  x = group_sum<16>(x);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast15, 0xA, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast31, 0xC, 0xF, false));
+  return readlane_f(x, 63);
+}
+
 template <typename TIn, int D, int CG, bool RES>
 __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs a) {
   using L = TileLayout<D, 1, CG>;
@@ -148,8 +158,8 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
             du = fmaf(z[ii], uI[ii], du);
             dk = fmaf(z[ii], kI[ii], dk);
           }
-          du = wave_sum(cg == 0 ? du : 0.f);
-          if (last) dk = wave_sum(cg == 0 ? dk : 0.f);
+          du = wave_total(cg == 0 ? du : 0.f);
+          if (last) dk = wave_total(cg == 0 ? dk : 0.f);
           lds_order();   // the previous sub-update's reads of zb come first
           if (cg == 0) lds_store_rows<R>(zb + row0, z);
           lds_order();
@@ -195,11 +205,11 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           an = fmaf(alpha[ii], alpha[ii], an);
           kn = fmaf(kI[ii], kI[ii], kn);
         }
-        an = wave_sum(cg == 0 ? an : 0.f);
+        an = wave_total(cg == 0 ? an : 0.f);
         float ascale;
         if constexpr (RES) {
           // The unit vector along A k_hat, k_hat = k / |k|.
-          kn = wave_sum(cg == 0 ? kn : 0.f);
+          kn = wave_total(cg == 0 ? kn : 0.f);
           const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
           ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
         } else {
@@ -269,8 +279,8 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           n[ii] += kI[ii];
           nq = fmaf(n[ii], qI[ii], nq);
         }
-        ns = wave_sum(ns);
-        nq = wave_sum(cg == 0 ? nq : 0.f);
+        ns = wave_total(ns);
+        nq = wave_total(cg == 0 ? nq : 0.f);
         float oscale = 1.f;
         if (a.cap_on && ns > cap2) {
           // Frobenius renormalisation: S <- S * cap / |S|_F.
