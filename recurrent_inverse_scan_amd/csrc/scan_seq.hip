@@ -43,6 +43,7 @@
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
+#include "vla_wave.h"
 
 namespace vla {
 
@@ -392,8 +393,8 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
             du = fmaf(z[ii], uI[ii], du);
             dk = fmaf(z[ii], kI[ii], dk);
           }
-          du = wave_sum(cg == 0 ? du : 0.f);
-          if (last) dk = wave_sum(cg == 0 ? dk : 0.f);
+          du = wave_total(cg == 0 ? du : 0.f);
+          if (last) dk = wave_total(cg == 0 ? dk : 0.f);
           float* zb = zbuf + par * D;
           if (cg == 0) lds_store_rows<R>(zb + row0, z);
           if constexpr (NW > 1) {
@@ -449,7 +450,7 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
         float an = 0.f;
 #pragma unroll
         for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
-        an = wave_sum(cg == 0 ? an : 0.f);
+        an = wave_total(cg == 0 ? an : 0.f);
         if constexpr (kInv) {
           static_assert(!kInv || NW == 1, "the inverse-only pass runs one wave per chunk");
           // alpha_hat of this token goes to HBM for the state pass: the
@@ -460,7 +461,7 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
             float kn = 0.f;
 #pragma unroll
             for (int ii = 0; ii < R; ++ii) kn = fmaf(kI[ii], kI[ii], kn);
-            kn = wave_sum(cg == 0 ? kn : 0.f);
+            kn = wave_total(cg == 0 ? kn : 0.f);
             const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
             ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
           }
@@ -536,8 +537,8 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
         n[ii] += kI[ii];
         nq = fmaf(n[ii], qI[ii], nq);
       }
-      ns = wave_sum(ns);
-      nq = wave_sum(cg == 0 ? nq : 0.f);
+      ns = wave_total(ns);
+      nq = wave_total(cg == 0 ? nq : 0.f);
       if constexpr (NW > 1) {
         if (lane == 0) { red[(par * NW + w) * 4 + 0] = ns; red[(par * NW + w) * 4 + 1] = nq; }
         __syncthreads();

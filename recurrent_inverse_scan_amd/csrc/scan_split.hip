@@ -22,6 +22,7 @@
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
+#include "vla_wave.h"
 
 namespace vla {
 
@@ -32,16 +33,6 @@ constexpr int kSplitSlots = 3;   // stage buffers in rotation
 constexpr int kSplitThreads = 128;
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
-
-// Sum over the wave by DPP alone: row sums, then the gfx9 row broadcasts
-// (lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and
-// 3), so lane 63 holds the total; one readlane makes it wave-uniform.
-__device__ __forceinline__ float wave_total(float x) {
-  x = group_sum<16>(x);
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast15, 0xA, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowBcast31, 0xC, 0xF, false));
-  return readlane_f(x, 63);
-}
 
 template <typename TIn, int D, int CG, bool RES>
 __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs a) {
