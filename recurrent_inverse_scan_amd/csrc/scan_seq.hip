@@ -20,8 +20,10 @@
 // prediction is one more sweep of S per token.
 //
 // Three modes share this code:
-//  * kFull: the whole recurrence (the sequential schedule, and the per-chain
-//    fallback of the time-parallel schedule, gated by a per-chain flag);
+//  * kFull: the whole recurrence (the sequential schedule at d = 128 and for
+//    calls of at most 16 tokens, longer calls at d <= 64 running the
+//    two-wave kernel of scan_split.hip; and the per-chain fallback of the
+//    time-parallel schedule, gated by a per-chain flag);
 //  * kInverseOnly: the inverse recurrence of one chunk of tokens, started
 //    from the chunk-start inverse the time-parallel schedule computed, and
 //    writing alpha_hat (one workgroup per chunk);
