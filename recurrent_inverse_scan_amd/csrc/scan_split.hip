@@ -7,10 +7,15 @@
 // recurrence (r guarded Sherman-Morrison updates of A, the nudge, alpha = A k
 // and its normalisation) never reads the state S, and the state recurrence
 // (S += w alpha_hat^T, the cap, n += k, the readout) needs only alpha_hat
-// from it.  So one workgroup of two waves runs a chain: wave 0 the inverse
-// side, wave 1 the state side one LDS stage (8 tokens) behind, alpha_hat
-// passed through LDS.  A token then costs the longer of the two halves
-// instead of their sum; each wave keeps only its own matrix in registers.
+// from it.  So one workgroup runs a chain: wave 0 the inverse side, wave 2
+// the state side one LDS stage (8 tokens) behind, alpha_hat passed through
+// LDS.  A token then costs the longer of the two halves instead of their
+// sum; each wave keeps only its own matrix in registers.  Wave 1 does no
+// work and only takes part in the barriers: the waves of a workgroup are
+// placed on the compute unit's SIMDs in turn, and with the two sides as
+// waves 0 and 1 they were measured to compete for one SIMD's issue (recall
+// workload 0.73 ms, against 0.56 ms with the middle wave, which equals the
+// inverse side's time alone).
 //
 // Synchronisation: every loop iteration ends with the one workgroup barrier,
 // taken by both waves the same number of times (the trip count depends on T
@@ -30,7 +35,8 @@ namespace {
 
 constexpr int kSplitTT = 8;      // tokens per LDS stage
 constexpr int kSplitSlots = 3;   // stage buffers in rotation
-constexpr int kSplitThreads = 128;
+constexpr int kSplitThreads = 192;   // inverse wave, spacer wave, state wave
+constexpr int kStageThreads = 128;   // the two working waves stage the rows
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
@@ -42,8 +48,10 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   float* smem = reinterpret_cast<float*>(smem4);
 
   const int64_t chain = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool inverse_side = tid < 64;
+  const int wave = threadIdx.x >> 6;
+  const bool inverse_side = wave == 0, spacer = wave == 1;
+  const int tid = inverse_side ? threadIdx.x : threadIdx.x - 64;   // 0..127 over the working waves
+  const int lane = threadIdx.x & 63;
   const int cg = lane % CG, rg = lane / CG;
   const int row0 = rg * R;
   const int r = a.r;
@@ -65,7 +73,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   src.fix2 = static_cast<const TIn*>(a.v) + tok0 * D;
   src.ubase = static_cast<const TIn*>(a.u) + tok0 * r * D;
   src.ustride = static_cast<int64_t>(r) * D;
-  Stager<TIn, D, kSplitThreads> st;
+  Stager<TIn, D, kStageThreads> st;
 
   // Registers of each side: A on the inverse wave, S and n on the state wave.
   float M[R][C], n[R];
@@ -97,14 +105,14 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   const float cap2 = a.cap * a.cap;
 
   const int nstage = (a.T + kSplitTT - 1) / kSplitTT;
-  if (nstage > 0) {
+  if (nstage > 0 && !spacer) {
     st.load(src, 0, kSplitTT, a.T, tid);
     st.store(stage, kSplitTT, NV, tid);
   }
   __syncthreads();
 
   for (int it = 0; it <= nstage; ++it) {
-    if (it + 1 < nstage) st.load(src, (it + 1) * kSplitTT, kSplitTT, a.T, tid);
+    if (it + 1 < nstage && !spacer) st.load(src, (it + 1) * kSplitTT, kSplitTT, a.T, tid);
 
     if (inverse_side && it < nstage) {
       // ---- inverse recurrence over stage it ------------------------------
@@ -216,7 +224,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           lds_store_rows<R>(aout + tt * D + row0, ah);
         }
       }
-    } else if (!inverse_side && it >= 1) {
+    } else if (!inverse_side && !spacer && it >= 1) {
       // ---- state recurrence over stage it - 1 ----------------------------
       const int sidx = it - 1;
       const float* sbuf = stage + (sidx % kSplitSlots) * slot_floats;
@@ -296,7 +304,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
       }
     }
 
-    if (it + 1 < nstage) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, kSplitTT, NV, tid);
+    if (it + 1 < nstage && !spacer) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, kSplitTT, NV, tid);
     __syncthreads();
   }
 
@@ -304,7 +312,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   if (inverse_side) add_to_diagonal<R, C, CG>(M, row0, cg, shift);
   float* dstM = inverse_side ? a.A_T : a.S_T;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
+  for (int i = 0; i < (spacer ? 0 : R); ++i) {
     const int row = row0 + i;
 #pragma unroll
     for (int m = 0; m < C / 4; ++m) {
@@ -321,7 +329,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   }
   if (a.stats) {
     const bool wave_bad = __any(bad);
-    if (lane == 0) {
+    if (lane == 0 && !spacer) {
       if (inverse_side) {
         fin[0] = static_cast<float>(guard_fires);
         fin[1] = wave_bad ? 1.f : 0.f;
@@ -332,7 +340,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
       }
     }
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
       int32_t* s = a.stats + chain * 4;
       s[0] = static_cast<int32_t>(fin[0]);
       s[1] = static_cast<int32_t>(fin[2]);
@@ -348,7 +356,7 @@ hipError_t launch_split(const ScanArgs& a, int chains, hipStream_t stream) {
   static_assert(L::R >= 1, "layout");
   const int NV = 3 + a.r;
   // Every stage fits the staging registers of the workgroup.
-  if (kSplitTT * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kSplitThreads) return hipErrorInvalidValue;
+  if (kSplitTT * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kStageThreads) return hipErrorInvalidValue;
   const size_t lds = sizeof(float) * (static_cast<size_t>(kSplitSlots) * kSplitTT * NV * D + 2 * kSplitTT * D + D + 8);
   const dim3 grid(static_cast<unsigned>(chains));
   if (a.residual)
