@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   float* stage = smem;                                   // [3][TT][NV][D]
   float* ahat = stage + kSplitSlots * slot_floats;       // [2][TT][D]
   float* zb = ahat + 2 * kSplitTT * D;                   // [D]
-  float* fin = zb + D;                                   // [8] per-side statistics
+  int32_t* fin = reinterpret_cast<int32_t*>(zb + D);     // [8] per-side statistics (exact counts)
 
   const int64_t tok0 = chain * a.T;
   RowSource<TIn, D> src;
@@ -331,21 +331,21 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
     const bool wave_bad = __any(bad);
     if (lane == 0 && !spacer) {
       if (inverse_side) {
-        fin[0] = static_cast<float>(guard_fires);
-        fin[1] = wave_bad ? 1.f : 0.f;
+        fin[0] = guard_fires;
+        fin[1] = wave_bad ? 1 : 0;
       } else {
-        fin[2] = static_cast<float>(cap_fires);
-        fin[3] = static_cast<float>(first_cap);
-        fin[4] = wave_bad ? 1.f : 0.f;
+        fin[2] = cap_fires;
+        fin[3] = first_cap;
+        fin[4] = wave_bad ? 1 : 0;
       }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
       int32_t* s = a.stats + chain * 4;
-      s[0] = static_cast<int32_t>(fin[0]);
-      s[1] = static_cast<int32_t>(fin[2]);
-      s[2] = (fin[1] != 0.f || fin[4] != 0.f) ? 1 : 0;
-      s[3] = static_cast<int32_t>(fin[3]);
+      s[0] = fin[0];
+      s[1] = fin[2];
+      s[2] = (fin[1] | fin[4]) ? 1 : 0;
+      s[3] = fin[3];
     }
   }
 }
