@@ -8,7 +8,7 @@
 // and its normalisation) never reads the state S, and the state recurrence
 // (S += w alpha_hat^T, the cap, n += k, the readout) needs only alpha_hat
 // from it.  So one workgroup runs a chain: wave 0 the inverse side, wave 2
-// the state side one LDS stage (8 tokens) behind, alpha_hat passed through
+// the state side one LDS stage (8 or 16 tokens) behind, alpha_hat passed through
 // LDS.  A token then costs the longer of the two halves instead of their
 // sum; each wave keeps only its own matrix in registers.  Wave 1 does no
 // work and only takes part in the barriers: the waves of a workgroup are
@@ -33,12 +33,25 @@ namespace vla {
 
 namespace {
 
-constexpr int kSplitTT = 8;      // tokens per LDS stage
 constexpr int kSplitSlots = 3;   // stage buffers in rotation
 constexpr int kSplitThreads = 192;   // inverse wave, spacer wave, state wave
 constexpr int kStageThreads = 128;   // the two working waves stage the rows
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// Tokens per LDS stage: 16 when the stage fits the staging registers and the
+// three slots stay within 60 KiB, else 8.
+template <typename TIn, int D>
+__host__ __device__ constexpr int split_stage_tokens(int NV) {
+  const int vpr = D / Elem<TIn>::kPer16B;
+  const int lds16 = static_cast<int>(sizeof(float)) * (kSplitSlots * 16 * NV * D + 2 * 16 * D + D + 8);
+  return (16 * NV * vpr <= kMaxStageVecs * kStageThreads && lds16 <= 60 * 1024) ? 16 : 8;
+}
+template <typename TIn, int D>
+inline size_t split_lds_bytes(int NV) {
+  const int TT = split_stage_tokens<TIn, D>(NV);
+  return sizeof(float) * (static_cast<size_t>(kSplitSlots) * TT * NV * D + 2 * TT * D + D + 8);
+}
 
 template <typename TIn, int D, int CG, bool RES>
 __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs a) {
@@ -57,11 +70,12 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   const int r = a.r;
   const int NV = 3 + r;   // q, k, v, u_1..u_r
   constexpr int row_q = 0, row_k = 1, row_v = 2, row_u = 3;
-  const int slot_floats = kSplitTT * NV * D;
+  const int TT = split_stage_tokens<TIn, D>(NV);
+  const int slot_floats = TT * NV * D;
 
   float* stage = smem;                                   // [3][TT][NV][D]
   float* ahat = stage + kSplitSlots * slot_floats;       // [2][TT][D]
-  float* zb = ahat + 2 * kSplitTT * D;                   // [D]
+  float* zb = ahat + 2 * TT * D;                   // [D]
   int32_t* fin = reinterpret_cast<int32_t*>(zb + D);     // [8] per-side statistics (exact counts)
 
   const int64_t tok0 = chain * a.T;
@@ -104,21 +118,21 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   int phase = a.nudge_period > 0 ? a.nudge_phase0 % a.nudge_period : 0;
   const float cap2 = a.cap * a.cap;
 
-  const int nstage = (a.T + kSplitTT - 1) / kSplitTT;
+  const int nstage = (a.T + TT - 1) / TT;
   if (nstage > 0 && !spacer) {
-    st.load(src, 0, kSplitTT, a.T, tid);
-    st.store(stage, kSplitTT, NV, tid);
+    st.load(src, 0, TT, a.T, tid);
+    st.store(stage, TT, NV, tid);
   }
   __syncthreads();
 
   for (int it = 0; it <= nstage; ++it) {
-    if (it + 1 < nstage && !spacer) st.load(src, (it + 1) * kSplitTT, kSplitTT, a.T, tid);
+    if (it + 1 < nstage && !spacer) st.load(src, (it + 1) * TT, TT, a.T, tid);
 
     if (inverse_side && it < nstage) {
       // ---- inverse recurrence over stage it ------------------------------
       const float* sbuf = stage + (it % kSplitSlots) * slot_floats;
-      float* aout = ahat + (it & 1) * kSplitTT * D;
-      const int tcount = min(kSplitTT, a.T - it * kSplitTT);
+      float* aout = ahat + (it & 1) * TT * D;
+      const int tcount = min(TT, a.T - it * TT);
       for (int tt = 0; tt < tcount; ++tt) {
         const float* tblk = sbuf + tt * NV * D;
         const float* tk = tblk + row_k * D;
@@ -228,9 +242,9 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
       // ---- state recurrence over stage it - 1 ----------------------------
       const int sidx = it - 1;
       const float* sbuf = stage + (sidx % kSplitSlots) * slot_floats;
-      const float* ain = ahat + (sidx & 1) * kSplitTT * D;
-      const int tb = sidx * kSplitTT;
-      const int tcount = min(kSplitTT, a.T - tb);
+      const float* ain = ahat + (sidx & 1) * TT * D;
+      const int tb = sidx * TT;
+      const int tcount = min(TT, a.T - tb);
       for (int tt = 0; tt < tcount; ++tt) {
         const int t = tb + tt;
         const float* tblk = sbuf + tt * NV * D;
@@ -304,7 +318,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
       }
     }
 
-    if (it + 1 < nstage && !spacer) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, kSplitTT, NV, tid);
+    if (it + 1 < nstage && !spacer) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, TT, NV, tid);
     __syncthreads();
   }
 
@@ -356,8 +370,8 @@ hipError_t launch_split(const ScanArgs& a, int chains, hipStream_t stream) {
   static_assert(L::R >= 1, "layout");
   const int NV = 3 + a.r;
   // Every stage fits the staging registers of the workgroup.
-  if (kSplitTT * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kStageThreads) return hipErrorInvalidValue;
-  const size_t lds = sizeof(float) * (static_cast<size_t>(kSplitSlots) * kSplitTT * NV * D + 2 * kSplitTT * D + D + 8);
+  if (8 * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kStageThreads) return hipErrorInvalidValue;
+  const size_t lds = split_lds_bytes<TIn, D>(NV);
   const dim3 grid(static_cast<unsigned>(chains));
   if (a.residual)
     hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, true>), grid, dim3(kSplitThreads), lds, stream, a);

@@ -87,8 +87,9 @@ def test_scan_parity_shapes(d, r, dtype):
 
 
 # Up to 16 tokens the one-wave kernel runs; beyond, the two-wave kernel with
-# 8-token stages (its pipeline fill and drain at 17, 24, 25 and 40).
-@pytest.mark.parametrize("T", [0, 1, 7, 8, 9, 17, 24, 25, 40])
+# 16-token stages at r = 1 (its pipeline fill and drain at 17, 24, 25, 32, 33
+# and 40).
+@pytest.mark.parametrize("T", [0, 1, 7, 8, 9, 17, 24, 25, 32, 33, 40])
 def test_scan_edge_lengths(T):
     cfg = CONFIGS["base"].with_(name=f"len{T}", B=1, H=2, T=T, nudge_period=3, s_cap=5.0)
     x = case(cfg, seed=T)
