@@ -164,18 +164,22 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           }
           float uI[R];
           lds_rows<R>(tu + row0, uI);
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) z[ii] = fmaf(shift, uI[ii], group_sum<CG>(z[ii]));
+          // z goes to LDS first, so its round trip overlaps the reductions.
+          lds_order();   // the previous sub-update's reads of zb come first
+          if (cg == 0) lds_store_rows<R>(zb + row0, z);
+          lds_order();
           float du = 0.f, dk = 0.f;
 #pragma unroll
           for (int ii = 0; ii < R; ++ii) {
-            z[ii] = fmaf(shift, uI[ii], group_sum<CG>(z[ii]));
             du = fmaf(z[ii], uI[ii], du);
             dk = fmaf(z[ii], kI[ii], dk);
           }
           du = wave_total(cg == 0 ? du : 0.f);
           if (last) dk = wave_total(cg == 0 ? dk : 0.f);
-          lds_order();   // the previous sub-update's reads of zb come first
-          if (cg == 0) lds_store_rows<R>(zb + row0, z);
-          lds_order();
+          float zJ[C];
+          lds_cols<CG, C>(zb, cg, zJ);
           const float delta = 1.f + du;
           const bool fire = fabsf(delta) < a.eps;
           if (fire) {
@@ -186,8 +190,6 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           }
           // A zero coefficient when the guard fired keeps A in place.
           const float inv = fire ? 0.f : 1.f / delta;
-          float zJ[C];
-          lds_cols<CG, C>(zb, cg, zJ);
 #pragma unroll
           for (int ii = 0; ii < R; ++ii) {
             const float zs = z[ii] * inv;
@@ -200,7 +202,8 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
             for (int ii = 0; ii < R; ++ii) y[ii] = fmaf(-z[ii], g, y[ii]);
           }
         }
-        // Nudge, coefficient and its normalisation.
+        // Nudge and coefficient; the state wave normalises it (it holds the
+        // columns of alpha and of k, so both norms need no wave reduction).
         float alpha[R];
 #pragma unroll
         for (int ii = 0; ii < R; ++ii) alpha[ii] = last_fired ? fmaf(a.eps, kI[ii], y[ii]) : y[ii];
@@ -212,30 +215,10 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           }
           phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
         }
-        float an = 0.f, kn = 0.f;
-#pragma unroll
-        for (int ii = 0; ii < R; ++ii) {
-          an = fmaf(alpha[ii], alpha[ii], an);
-          kn = fmaf(kI[ii], kI[ii], kn);
-        }
-        an = wave_total(cg == 0 ? an : 0.f);
-        float ascale;
-        if constexpr (RES) {
-          // The unit vector along A k_hat, k_hat = k / |k|.
-          kn = wave_total(cg == 0 ? kn : 0.f);
-          const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
-          ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
-        } else {
-          ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
-        }
         if (cg == 0) {
-          float ah[R];
 #pragma unroll
-          for (int ii = 0; ii < R; ++ii) {
-            ah[ii] = alpha[ii] * ascale;
-            bad |= !isfinite(ah[ii]);
-          }
-          lds_store_rows<R>(aout + tt * D + row0, ah);
+          for (int ii = 0; ii < R; ++ii) bad |= !isfinite(alpha[ii]);
+          lds_store_rows<R>(aout + tt * D + row0, alpha);
         }
       }
     } else if (!inverse_side && !spacer && it >= 1) {
@@ -254,6 +237,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
         float kI[R], vI[R], qI[R], qJ[C], aJ[C];
         lds_rows<R>(tk + row0, kI);
         lds_rows<R>(tv + row0, vI);
+        float kinv = 1.f;
         if constexpr (RES) {
           // v - S_{t-1} k_hat, the prediction taken before the update.
           float kJ[C];
@@ -261,8 +245,8 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           float kn = 0.f;
 #pragma unroll
           for (int c = 0; c < C; ++c) kn = fmaf(kJ[c], kJ[c], kn);
-          kn = group_sum<CG>(kn);
-          const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
+          kn = group_sum<CG>(kn);   // a row group's lanes hold every column
+          kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
 #pragma unroll
           for (int ii = 0; ii < R; ++ii) {
             float acc = 0.f;
@@ -274,6 +258,17 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
         lds_rows<R>(tq + row0, qI);
         lds_cols<CG, C>(tq, cg, qJ);
         lds_cols<CG, C>(ain + tt * D, cg, aJ);
+        {
+          // alpha_hat: additive, alpha / max(|alpha|, 1); residual, the unit
+          // vector along A k_hat = kinv A k.
+          float an = 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) an = fmaf(aJ[c], aJ[c], an);
+          an = group_sum<CG>(an);
+          const float ascale = RES ? kinv / fmaxf(kinv * sqrtf(an), 1e-12f) : (an > 1.f ? 1.f / sqrtf(an) : 1.f);
+#pragma unroll
+          for (int c = 0; c < C; ++c) aJ[c] *= ascale;
+        }
         float ns = 0.f, po[R];
 #pragma unroll
         for (int ii = 0; ii < R; ++ii) {
