@@ -449,11 +449,11 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           }
           phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
         }
-        float an = 0.f;
-#pragma unroll
-        for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
-        an = wave_total(cg == 0 ? an : 0.f);
         if constexpr (kInv) {
+          float an = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
+          an = wave_total(cg == 0 ? an : 0.f);
           static_assert(!kInv || NW == 1, "the inverse-only pass runs one wave per chunk");
           // alpha_hat of this token goes to HBM for the state pass: the
           // clamped coefficient, or for the residual update the unit vector
@@ -488,19 +488,17 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
         }
         float* ab = abuf + par * D;
         if (cg == 0) lds_store_rows<R>(ab + row0, alpha);
-        if constexpr (NW > 1) {
-          if (lane == 0) red[(par * NW + w) * 4 + 0] = an;
-        }
         __syncthreads();
-        if constexpr (NW > 1) {
-          an = 0.f;
+        // |alpha|^2 from the columns: a row group's lanes hold every column,
+        // so a group sum replaces the reduction over the workgroup.
+        lds_cols<CG, C>(ab, cg, aJ);
+        float an = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < NW; ++ww) an += red[(par * NW + ww) * 4 + 0];
-        }
+        for (int c = 0; c < C; ++c) an = fmaf(aJ[c], aJ[c], an);
+        an = group_sum<CG>(an);
         // Additive: alpha / max(|alpha|, 1).  Residual: the unit vector along
         // A k_hat = kinv * A k, i.e. kinv / max(kinv |A k|, 1e-12) times A k.
         const float ascale = RES ? kinv / fmaxf(kinv * sqrtf(an), 1e-12f) : (an > 1.f ? 1.f / sqrtf(an) : 1.f);
-        lds_cols<CG, C>(ab, cg, aJ);
 #pragma unroll
         for (int c = 0; c < C; ++c) aJ[c] *= ascale;
         par ^= 1;
