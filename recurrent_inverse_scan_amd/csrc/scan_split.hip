@@ -1,25 +1,24 @@
-// Sequential VLA scan for d <= 64 with the two recurrences on two waves.
+// Sequential VLA scan for d <= 64 with the two recurrences on separate waves.
 //
 // Method as in the sequential kernel ("Mathematical Primitives", sections
 // 2-5; "Variational Linear Attention (VLA)" README, v3 notes; the residual
 // update from "Variational Linear Attention: Stable Associative Memory for
 // Long-Context Transformers", technical summary 2.3).  Per token the inverse
-// recurrence (r guarded Sherman-Morrison updates of A, the nudge, alpha = A k
-// and its normalisation) never reads the state S, and the state recurrence
-// (S += w alpha_hat^T, the cap, n += k, the readout) needs only alpha_hat
-// from it.  So one workgroup runs a chain: wave 0 the inverse side, wave 2
-// the state side one LDS stage (8 or 16 tokens) behind, alpha_hat passed through
-// LDS.  A token then costs the longer of the two halves instead of their
-// sum; each wave keeps only its own matrix in registers.  Wave 1 does no
-// work and only takes part in the barriers: the waves of a workgroup are
-// placed on the compute unit's SIMDs in turn, and with the two sides as
-// waves 0 and 1 they were measured to compete for one SIMD's issue (recall
-// workload 0.73 ms, against 0.56 ms with the middle wave, which equals the
-// inverse side's time alone).
+// recurrence (r guarded Sherman-Morrison updates of A, the nudge, alpha = A k)
+// never reads the state S, and the state recurrence (S += w alpha_hat^T, the
+// cap, n += k, the readout) needs only alpha from it.  So one workgroup runs
+// a chain: wave 0 the inverse side, wave 2 the state side one LDS stage (8
+// or 16 tokens) behind, alpha passed through LDS and normalised by the state
+// wave (it holds the columns of alpha and k, so both norms are group sums).
+// A token then costs the longer of the two halves instead of their sum; each
+// wave keeps only its own matrix in registers.  Wave 1 does no work and only
+// takes part in the barriers: with the two sides as waves 0 and 1 they were
+// measured to compete for issue (recall workload 0.73 ms, against 0.56 ms
+// with the middle wave, which equals the inverse side's time alone).
 //
 // Synchronisation: every loop iteration ends with the one workgroup barrier,
-// taken by both waves the same number of times (the trip count depends on T
-// only).  Inside a side, the vector broadcasts go through LDS within one
+// taken by all three waves the same number of times (the trip count depends
+// on T only).  Inside a side, the vector broadcasts go through LDS within one
 // wave: the hardware completes a wave's LDS operations in issue order, and
 // lds_order() keeps the compiler from moving a load above an earlier store.
 // Stage buffers rotate over three slots: the one being filled, the one the
