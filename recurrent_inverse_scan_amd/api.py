@@ -63,7 +63,7 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     the library pick; ``segment_blocks`` (chunked schedule) sets the blocks of
     64 tokens per state-pass segment, 0 lets the library pick and -1 keeps one
     segment.  ``update`` is "additive" or "residual" (the delta-rule state
-    step; sequential schedule only).  ``out`` may pass preallocated (o, A_T, S_T, n_T,
+    step; both schedules).  ``out`` may pass preallocated (o, A_T, S_T, n_T,
     stats) tensors and ``workspace`` a preallocated uint8 device buffer of at
     least ``workspace_size(...)`` bytes.  Returns (o, A_T, S_T, n_T, stats).
     """
