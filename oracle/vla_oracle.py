@@ -87,7 +87,7 @@ def _normalize_rows(x):
 
 
 def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0,
-                s_cap=None, den_eps=1e-6, t0=0, update="additive", normalize=True):
+                s_cap=None, den_eps=1e-6, t0=0, update="additive", normalize=True, trace_norms=False):
     """Run the VLA scan sequentially over tokens, independently per chain.
 
     ``update`` selects the state step: "additive" (S += v alpha_hat^T with the
@@ -105,7 +105,9 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
     [*batch, d, d], ``n`` [*batch, d] and per-chain statistics:
     ``guard_fires``, ``cap_fires``, ``first_cap_step`` (0-based local token
     index, -1 if none), ``max_s_norm`` (largest ||S_t||_F after the cap) and
-    ``nonfinite`` (any output or final state not finite).
+    ``nonfinite`` (any output or final state not finite).  With
+    ``trace_norms`` it also returns ``pre_cap_norm`` [*batch, T], each token's
+    ||S_t||_F after the state update and before the cap is applied.
     """
     q, k, v, u = as_f64(q), as_f64(k), as_f64(v), as_f64(u)
     batch = q.shape[:-2]
@@ -132,6 +134,7 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
     capf = np.zeros(C, dtype=np.int64)
     first_cap = np.full(C, -1, dtype=np.int64)
     max_norm = np.zeros(C)
+    pre_norm = np.zeros((C, T)) if trace_norms else None
     o = np.zeros((C, T, d))
     cap_on = _cap_enabled(s_cap)
 
@@ -168,6 +171,8 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
             S = S + resid[:, :, None] * alpha_hat[:, None, :]
         # Frobenius renormalisation of S.
         fn = np.sqrt(np.einsum("cij,cij->c", S, S))
+        if trace_norms:
+            pre_norm[:, t] = fn
         if cap_on:
             over = fn > s_cap
             scale = np.where(over, s_cap / np.where(over, fn, 1.0), 1.0)
@@ -183,7 +188,7 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
 
     nonfinite = ~(np.isfinite(o).all(axis=(1, 2)) & np.isfinite(A).all(axis=(1, 2))
                   & np.isfinite(S).all(axis=(1, 2)) & np.isfinite(n).all(axis=1))
-    return {
+    out = {
         "o": o.reshape(batch + (T, d)),
         "A": A.reshape(batch + (d, d)),
         "S": S.reshape(batch + (d, d)),
@@ -194,6 +199,9 @@ def oracle_scan(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period
         "max_s_norm": max_norm.reshape(batch),
         "nonfinite": nonfinite.reshape(batch),
     }
+    if trace_norms:
+        out["pre_cap_norm"] = pre_norm.reshape(batch + (T,))
+    return out
 
 
 def oracle_project_u(W_u, k_raw):

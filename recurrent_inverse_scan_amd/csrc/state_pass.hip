@@ -648,7 +648,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     constexpr int RG = decltype(rgc)::value;
     constexpr int RGp1 = (RG + 1) % kRowGens, RGp2 = (RG + 2) % kRowGens;
     constexpr int RGm1 = (RG + kRowGens - 1) % kRowGens;
-    constexpr int g = RG & 1;   // = b & 1, as b_lo is even
+    constexpr int g = RG & 1;   // = (b - b_lo) & 1: parity relative to the segment start
     const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
     // A fresh copy of the lane index per block keeps the many lane-dependent
     // LDS addresses from being hoisted out of the loop (and spilled).
@@ -770,7 +770,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     // LDS writes are complete first; the asm is a compiler memory barrier.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  for (int b = b_lo; b < b_hi; b += kRowGens) {   // b_lo is even: parity 0 first
+  for (int b = b_lo; b < b_hi; b += kRowGens) {   // block b_lo has relative parity 0
     step(std::integral_constant<int, 0>{}, b);
     if (b + 1 < b_hi) step(std::integral_constant<int, 1>{}, b + 1);
     if constexpr (kRowGens == 4) {
@@ -781,7 +781,9 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 
   // ---- epilogue: the segment's last block update ----------------------------
   if (!rwave) {
-    const int g = (b_hi - 1) & 1;
+    // The last block's LDS outputs sit in the buffer of its parity relative
+    // to b_lo, which may be odd (a remainder shared between two segments).
+    const int g = (b_hi - 1 - b_lo) & 1;
     if constexpr (kBf) {
       const int r = (b_hi - 1 - b_lo) % kRowGens;
       rank_update_lds(X, reinterpret_cast<const char*>(rows_vr(r)), reinterpret_cast<const char*>(rows_ar(r)), uoff,

@@ -18,7 +18,7 @@ import torch
 from oracle.vla_oracle import oracle_project_u, oracle_scan
 from recurrent_inverse_scan_amd import CONFIGS, make_inputs, project_u, scan_forward
 from recurrent_inverse_scan_amd._lib import VLAError, VLA_EUNSUPPORTED
-from tests.parity import TOL, case, flat, rel_err, run_oracle
+from tests.parity import TOL, case, check, flat, rel_err, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -39,23 +39,7 @@ def _gpu(x, cfg, **kw):
 
 
 def _check(cfg, out, ref, chains=None):
-    tol = TOL[cfg.in_dtype]
-    o, A, S, n, st = out
-    errs = {
-        "o": rel_err(flat(o, cfg, chains), ref["o"]),
-        "A": rel_err(flat(A, cfg, chains), ref["A"], axes=(-2, -1)),
-        "S": rel_err(flat(S, cfg, chains), ref["S"], axes=(-2, -1)),
-        "n": rel_err(flat(n, cfg, chains), ref["n"]),
-    }
-    _say(f"{cfg.name} B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} r={cfg.r} {cfg.in_dtype}: {errs}")
-    assert all(v <= tol for v in errs.values()), errs
-    st = flat(st, cfg, chains).cpu().numpy()
-    np.testing.assert_array_equal(st[:, 0], ref["guard_fires"])
-    assert (st[:, 2] == ref["nonfinite"]).all()
-    if cfg.s_cap:
-        # cap decisions may differ only where |S|_F is within rounding of the cap
-        assert np.abs(st[:, 1] - ref["cap_fires"]).max() <= max(2, 0.01 * ref["cap_fires"].max())
-    return st
+    return check("gpu-residual", cfg, out, ref, chains=chains, say=_say)[1]
 
 
 SMALL = {
@@ -225,7 +209,7 @@ def test_residual_full_size_sampled_chains(name):
     u_ref = torch.from_numpy(u_ref).to(x["q"].dtype).reshape(len(sel), cfg.T, cfg.r, cfg.d)
     ref = oracle_scan(x["q"].reshape(C, cfg.T, cfg.d)[sel], x["k"].reshape(C, cfg.T, cfg.d)[sel],
                       x["v"].reshape(C, cfg.T, cfg.d)[sel], u_ref, nudge_period=cfg.nudge_period,
-                      s_cap=cfg.s_cap, update="residual")
+                      s_cap=cfg.s_cap, update="residual", trace_norms=True)
     _check(cfg, out, ref, chains=sel)
 
 

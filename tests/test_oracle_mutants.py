@@ -61,8 +61,18 @@ MUTANTS = [
     ("nudge applied after alpha",
      "        if nudge_period > 0 and tau % nudge_period == 0:\n            A = A + eps * eye\n", ""),
     ("cap applied after the readout",
-     "        fn = np.sqrt(np.einsum(\"cij,cij->c\", S, S))\n        if cap_on:",
-     "        fn = np.sqrt(np.einsum(\"cij,cij->c\", S, S))\n        if False:"),
+     "        if cap_on:\n            over = fn > s_cap", "        if False:\n            over = fn > s_cap"),
+    ("first cap step off by one", "first_cap = np.where(over & (first_cap < 0), t, first_cap)",
+     "first_cap = np.where(over & (first_cap < 0), t + 1, first_cap)"),
+    ("first cap step records the latest fire", "first_cap = np.where(over & (first_cap < 0), t, first_cap)",
+     "first_cap = np.where(over, t, first_cap)"),
+    ("bfloat16 widened through float16",
+     "        if x.dtype in (torch.bfloat16, torch.float16):\n            x = x.to(torch.float32)",
+     "        if x.dtype in (torch.bfloat16, torch.float16):\n            x = x.to(torch.float16).to(torch.float32)"),
+    ("float32 tensors rounded through bfloat16",
+     "        if x.dtype in (torch.bfloat16, torch.float16):\n            x = x.to(torch.float32)",
+     "        if x.dtype in (torch.bfloat16, torch.float16, torch.float32):\n"
+     "            x = x.to(torch.bfloat16).to(torch.float32)"),
     ("residual with the wrong sign", "resid = v[:, t, :] - np.einsum", "resid = v[:, t, :] + np.einsum"),
     ("residual predicted from the raw key", 'resid = v[:, t, :] - np.einsum("cij,cj->ci", S, khat)',
      'resid = v[:, t, :] - np.einsum("cij,cj->ci", S, k[:, t, :])'),
@@ -112,6 +122,8 @@ _EXTRA = {
 
 PINS = [
     ("test_hand_worked_fixture", {"name": "hand_d2_plain.txt"}),
+    ("test_as_f64_widens_torch_tensors_exactly", {}),
+    ("test_first_cap_step_closed_form", {}),
     ("test_hand_worked_fixture", {"name": "hand_d2_guard_nudge_cap.txt"}),
     ("test_inverse_tracking_matches_direct_inverse", {"spd_start": True}),
     ("test_alpha_uses_post_update_inverse", {}),
@@ -156,6 +168,7 @@ def test_planted_mistake_is_caught(desc, old, new, monkeypatch):
     mod = _load_mutant(desc, old, new)
     monkeypatch.setattr(pins, "oracle_scan", mod.oracle_scan)
     monkeypatch.setattr(pins, "oracle_project_u", mod.oracle_project_u)
+    monkeypatch.setattr(pins, "as_f64", mod.as_f64)
     caught = []
     for name, kw in PINS:
         try:

@@ -13,7 +13,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle.vla_oracle import oracle_project_u, oracle_scan
+from oracle.vla_oracle import as_f64, oracle_project_u, oracle_scan
 from tests import golden_io
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -63,6 +63,101 @@ def test_hand_worked_fixture(name):
     np.testing.assert_allclose(res["n"].ravel(), g["expect_n"], rtol=0, atol=0)
     assert int(res["guard_fires"][0]) == int(g["expect_guard_fires"])
     assert int(res["cap_fires"][0]) == int(g["expect_cap_fires"])
+    assert int(res["first_cap_step"][0]) == int(g["expect_first_cap_step"])
+
+
+# --------------------------------------------------------------------------
+# Exact widening of stored inputs.  The workloads store q, k, v, u as float32
+# or bfloat16; the oracle must see exactly the stored values.  The expected
+# value of every encoding is decoded here from its bits (sign, exponent,
+# significand) with exact power-of-two scaling, independently of any float
+# conversion routine.
+# --------------------------------------------------------------------------
+def _decode_bits(bits, exp_bits, man_bits):
+    bits = bits.astype(np.int64)
+    bias = (1 << (exp_bits - 1)) - 1
+    sign = np.where((bits >> (exp_bits + man_bits)) & 1, -1.0, 1.0)
+    e = (bits >> man_bits) & ((1 << exp_bits) - 1)
+    m = (bits & ((1 << man_bits) - 1)).astype(np.float64)
+    normal = np.ldexp(1.0 + m / (1 << man_bits), (e - bias).astype(np.int32))
+    sub = np.ldexp(m, np.int32(1 - bias - man_bits))
+    val = sign * np.where(e == 0, sub, normal)
+    special = e == (1 << exp_bits) - 1
+    val = np.where(special & (m == 0), sign * np.inf, val)
+    return np.where(special & (m != 0), np.nan, val)
+
+
+def test_as_f64_widens_torch_tensors_exactly():
+    import torch
+
+    with np.errstate(invalid="ignore"):   # signalling NaN encodings warn when widened
+        _as_f64_checks(torch)
+
+
+def _as_f64_checks(torch):
+
+    # bfloat16 and float16: every one of the 65536 encodings, including the
+    # exponent extremes, subnormals, signed zeros, infinities and NaNs.
+    every16 = np.arange(1 << 16, dtype=np.int64)
+    as_i16 = torch.from_numpy(every16.astype(np.uint16).view(np.int16))
+    for dt, e_bits, m_bits in ((torch.bfloat16, 8, 7), (torch.float16, 5, 10)):
+        got = as_f64(as_i16.view(dt))
+        want = _decode_bits(every16, e_bits, m_bits)
+        assert got.dtype == np.float64 and got.shape == want.shape
+        assert np.array_equal(np.isnan(got), np.isnan(want)), dt
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok]), dt
+        assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok])), dt
+    # float32: the edge encodings plus a random sample of all others.
+    g = _rng(40)
+    edges = np.array([0, 1, 2, 0x007FFFFF, 0x00800000, 0x00800001, 0x3F800000, 0x3F800001, 0x7F7FFFFF,
+                      0x7F800000, 0x7FC00000, 0x80000000, 0x80000001, 0xFF7FFFFF, 0xFF800000], dtype=np.int64)
+    bits32 = np.concatenate([edges, g.integers(0, 1 << 32, 200_000, dtype=np.int64)])
+    t32 = torch.from_numpy(bits32.astype(np.uint32).view(np.int32)).view(torch.float32)
+    got, want = as_f64(t32), _decode_bits(bits32, 8, 23)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    # a view with a gradient, laid out non-contiguously, keeps shape and values
+    base = torch.arange(24, dtype=torch.float32, requires_grad=True).reshape(4, 6)
+    view = base.t()[1:5].to(torch.bfloat16)
+    np.testing.assert_array_equal(as_f64(view), np.arange(24.0).reshape(4, 6).T[1:5])
+    # the scan itself sees the stored bfloat16 values: one token, d = 1
+    # (u = 0 so A = 1; alpha = k; S = v min(1, 1/k) k; o = S q / (k q + eps))
+    kq = torch.tensor([[[3.0]]], dtype=torch.float32).to(torch.bfloat16)
+    vv = torch.tensor([[[1.0 / 3.0]]], dtype=torch.float32).to(torch.bfloat16)
+    res = oracle_scan(kq, kq, vv, torch.zeros(1, 1, 1, 1, dtype=torch.bfloat16))
+    v_stored = _decode_bits(np.array([int(vv.view(torch.int16).item()) & 0xFFFF]), 8, 7)[0]
+    assert v_stored != 1.0 / 3.0
+    np.testing.assert_allclose(res["S"][0, 0, 0], v_stored, rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# First cap step ("Mathematical Primitives", section 5, dynamic
+# renormalisation; strict test, checked after every state update).  With
+# u = 0, A0 = I, no nudge and k_t = e1 (so alpha_hat = e1), v_t = c e1 makes
+# S_t = t c e1 e1^T (t 1-based) until the first fire, which therefore comes
+# at the smallest 0-based index f with (f + 1) c > cap; after it S sits at
+# the cap and every later token fires again.
+# --------------------------------------------------------------------------
+def test_first_cap_step_closed_form():
+    d, T = 3, 12
+    rates = np.array([1.0, 2.0, 0.5, 4.0, 0.25])
+    C = len(rates)
+    e1 = np.eye(d)[0]
+    k = np.broadcast_to(e1, (C, T, d)).copy()
+    v = rates[:, None, None] * k
+    q = np.broadcast_to(np.array([1.0, 0.5, 0.25]), (C, T, d)).copy()
+    u = np.zeros((C, T, 1, d))
+    for cap in (0.1, 1.0, 2.0, 5.5, 6.0, 7.5, 100.0):
+        res = oracle_scan(q, k, v, u, s_cap=cap)
+        for c, rate in enumerate(rates):
+            f = next((i for i in range(T) if (i + 1) * rate > cap), -1)
+            assert int(res["first_cap_step"][c]) == f, (cap, rate)
+            assert int(res["cap_fires"][c]) == (T - f if f >= 0 else 0), (cap, rate)
+    # a chain that never reaches the cap reports -1, beside one that does
+    res = oracle_scan(q[:2], k[:2], v[:2] * np.array([1.0, 0.0])[:, None, None], u[:2], s_cap=3.0)
+    assert list(res["first_cap_step"]) == [3, -1]
 
 
 # --------------------------------------------------------------------------
