@@ -1,9 +1,11 @@
 /*
  * vla.h - C ABI of the MI355X (gfx950) Variational Linear Attention scan.
  *
- * The library exports two compute entry points:
+ * The library exports these compute entry points:
  *
  *   vla_scan_forward  the VLA recurrence scan over a sequence, per (batch, head)
+ *   vla_scan_step     one token per chain with the state updated in place
+ *                     (streaming decode)
  *   vla_project_u     the learned penalty directions u = normalize(W_u k_raw)
  *
  * plus parameter, workspace and status helpers.
@@ -40,7 +42,7 @@
 extern "C" {
 #endif
 
-#define VLA_ABI_VERSION 2
+#define VLA_ABI_VERSION 3
 
 typedef enum {
   VLA_OK = 0,
@@ -84,6 +86,9 @@ typedef struct {
   float s_cap;           /* Frobenius cap on S; <= 0 or +inf = off */
   float den_eps;         /* readout denominator epsilon (default 1e-6) */
   int64_t t0;            /* global index of this call's first token (nudge phase, resume) */
+  int64_t stride_b;      /* element strides of q, k and v (shared) over batch, head and */
+  int64_t stride_h;      /* token; the feature dimension is contiguous.  All three 0 means */
+  int64_t stride_t;      /* the contiguous [B, H, T, d] layout (see vla_scan_forward) */
   int32_t schedule;      /* vla_schedule_t */
   int32_t validate;      /* nonzero: synchronous NaN/Inf pre-check of the inputs */
   int32_t chunk_len;     /* tokens per chunk of the chunked schedule; 0 = library picks */
@@ -99,13 +104,14 @@ typedef struct {
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
- * den_eps = 1e-6, t0 = 0, automatic schedule, no validation, chunk_len = 0,
- * segment_blocks = 0, additive update.  Host pointer. */
+ * den_eps = 1e-6, t0 = 0, contiguous q, k, v (strides 0), automatic schedule,
+ * no validation, chunk_len = 0, segment_blocks = 0, additive update.  Host
+ * pointer. */
 void vla_scan_params_init(vla_scan_params_t* p);
 
 /* Bytes of device workspace vla_scan_forward needs for these parameters
  * (host pointers in and out), for the schedule the call would use.  Zero for
- * the sequential schedule without validation. */
+ * the sequential schedule with contiguous q, k, v and without validation. */
 vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
 
 /*
@@ -134,8 +140,16 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  *   n += k_t;  o_t = S q_t / (n.q_t + den_eps)
  *
  * Arguments (device pointers):
- *   q, k, v  [B, H, T, d] in in_dtype, contiguous.  q and k are the positive
- *            (ELU+1) features; the library does not apply the feature map.
+ *   q, k, v  [B, H, T, d] in in_dtype.  q and k are the positive (ELU+1)
+ *            features; the library does not apply the feature map.  With the
+ *            strides all 0 the three are contiguous.  Otherwise element
+ *            (b, h, t, i) of each sits at element b*stride_b + h*stride_h +
+ *            t*stride_t + i of its pointer (e.g. q, k, v sliced from one
+ *            packed [B, T, H, 3d] projection: stride_b = T*H*3d, stride_h = 3d,
+ *            stride_t = H*3d); each stride must be >= 0, stride_t >= d, and
+ *            stride * element size a multiple of 16 bytes.  Strided inputs are
+ *            first gathered into the workspace by a copy kernel, so the
+ *            kernels of both schedules read them contiguously.
  *   u        [B, H, T, r, d] in in_dtype, contiguous; u[..., t, i, :] is the
  *            i-th direction of token t, applied in index order.
  *   A0, S0   [B, H, d, d] float32, n0 [B, H, d] float32: initial state.  Each
@@ -176,14 +190,38 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  * whose state exceeds s_cap is recomputed sequentially with the cap applied.
  *
  * With validate != 0 the call first checks q, k, v, u for NaN/Inf on the
- * stream, synchronises the stream, and returns VLA_ENONFINITE (having
- * launched nothing else) if any is found.
+ * stream (after the gather of strided inputs), synchronises the stream, and
+ * returns VLA_ENONFINITE (having launched nothing else) if any is found.
  */
 vla_status_t vla_scan_forward(const vla_scan_params_t* p,
                               const void* q, const void* k, const void* v, const void* u,
                               const float* A0, const float* S0, const float* n0,
                               void* o, float* A_T, float* S_T, float* n_T, int32_t* stats,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vla_scan_step: one decode step, T = 1 token per chain, with the recurrent
+ * state read and written in place.
+ *
+ * Source: "Variational Linear Attention: Stable Associative Memory for
+ * Long-Context Transformers", technical summary (streaming inference with a
+ * constant-size state and no growing cache); README, v3 notes item 5 (the
+ * readout at decode time).  The token's arithmetic is vla_scan_forward's,
+ * with tau = t0 + 1 for the nudge.
+ *
+ *   p        parameters as for vla_scan_forward; p->T must be 1 (VLA_EINVAL
+ *            otherwise); p->t0 is the global index of this token
+ *   q, k, v  [B, H, 1, d] in in_dtype (strides as in vla_scan_forward)
+ *   u        [B, H, 1, r, d] in in_dtype
+ *   A, S     [B, H, d, d] float32 and n [B, H, d] float32: the state before
+ *            the token, overwritten with the state after it (non-NULL)
+ *   o        [B, H, 1, d] in in_dtype (written); stats as in vla_scan_forward
+ *   workspace as for vla_scan_forward (zero bytes unless strided or validated)
+ */
+vla_status_t vla_scan_step(const vla_scan_params_t* p,
+                           const void* q, const void* k, const void* v, const void* u,
+                           float* A, float* S, float* n, void* o, int32_t* stats,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vla_project_u: learned penalty directions, u_{row, i} = normalize(W_u[i] k_raw[row]).

@@ -16,11 +16,11 @@ VLA_OK, VLA_EINVAL, VLA_EUNSUPPORTED, VLA_EWORKSPACE, VLA_ENONFINITE, VLA_EHIP =
 VLA_F32, VLA_BF16 = 0, 1
 VLA_SCHEDULE_AUTO, VLA_SCHEDULE_SEQUENTIAL, VLA_SCHEDULE_CHUNKED = 0, 1, 2
 VLA_UPDATE_ADDITIVE, VLA_UPDATE_RESIDUAL = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/vla.h declares.
 EXPORTED = (
-    "vla_scan_params_init", "vla_scan_workspace_size", "vla_scan_forward", "vla_project_u",
+    "vla_scan_params_init", "vla_scan_workspace_size", "vla_scan_forward", "vla_scan_step", "vla_project_u",
     "vla_status_string", "vla_last_error", "vla_abi_version", "vla_timing_enable", "vla_timing_collect",
 )
 
@@ -35,6 +35,9 @@ class ScanParams(ctypes.Structure):
         ("s_cap", ctypes.c_float),
         ("den_eps", ctypes.c_float),
         ("t0", ctypes.c_int64),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
         ("schedule", ctypes.c_int32),
         ("validate", ctypes.c_int32),
         ("chunk_len", ctypes.c_int32),
@@ -69,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.vla_scan_workspace_size.restype = i32
     lib.vla_scan_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.vla_scan_forward.restype = i32
+    lib.vla_scan_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.vla_scan_step.restype = i32
     lib.vla_project_u.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.vla_project_u.restype = i32
     lib.vla_status_string.argtypes = [i32]

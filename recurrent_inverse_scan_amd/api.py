@@ -31,9 +31,26 @@ def _need_cuda(*ts):
             raise ValueError("VLA tensors must live on a HIP device")
 
 
+def _seq_strides(q, k, v):
+    """(stride_b, stride_h, stride_t) for the ABI: zeros when q, k, v are
+    contiguous, else their shared element strides (feature dimension
+    contiguous)."""
+    if all(t.is_contiguous() for t in (q, k, v)):
+        return (0, 0, 0)
+    if not (q.stride() == k.stride() == v.stride()) or q.stride(-1) != 1:
+        raise ValueError("strided q, k, v must share their strides and keep the feature dimension contiguous")
+    return tuple(int(x) for x in q.stride()[:3])
+
+
+def _check_out(t, shape, dtype, dev, name):
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev} "
+                         f"(got {t.dtype} {tuple(t.shape)} on {t.device}, contiguous={t.is_contiguous()})")
+
+
 def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
                 schedule="auto", validate=False, chunk_len=0, segment_blocks=0,
-                update="additive") -> _lib.ScanParams:
+                update="additive", strides=(0, 0, 0)) -> _lib.ScanParams:
     p = _lib.ScanParams()
     _lib.load().vla_scan_params_init(ctypes.byref(p))
     p.B, p.H, p.T, p.d, p.r = B, H, T, d, r
@@ -43,6 +60,7 @@ def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, d
     p.s_cap = 0.0 if (s_cap is None or not math.isfinite(s_cap) or s_cap <= 0) else float(s_cap)
     p.den_eps = den_eps
     p.t0 = t0
+    p.stride_b, p.stride_h, p.stride_t = strides
     p.schedule = {"auto": _lib.VLA_SCHEDULE_AUTO, "sequential": _lib.VLA_SCHEDULE_SEQUENTIAL,
                   "chunked": _lib.VLA_SCHEDULE_CHUNKED}[schedule]
     p.validate = 1 if validate else 0
@@ -58,7 +76,10 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     """Run vla_scan_forward.
 
     q, k, v: [B, H, T, d]; u: [B, H, T, r, d], all float32 or all bfloat16 on
-    the device.  A0, S0 [B, H, d, d] and n0 [B, H, d] are float32 or None.
+    the device.  q, k, v may be strided views (e.g. slices of one packed
+    projection) if they share their strides and keep the feature dimension
+    contiguous; the library gathers them into its workspace.  A0, S0
+    [B, H, d, d] and n0 [B, H, d] are float32 or None.
     ``schedule`` is "auto", "sequential" or "chunked"; ``chunk_len`` 0 lets
     the library pick; ``segment_blocks`` (chunked schedule) sets the blocks of
     64 tokens per state-pass segment, 0 lets the library pick and -1 keeps one
@@ -67,7 +88,8 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     stats) tensors and ``workspace`` a preallocated uint8 device buffer of at
     least ``workspace_size(...)`` bytes.  Returns (o, A_T, S_T, n_T, stats).
     """
-    _need_cuda(q, k, v, u, A0, S0, n0)
+    if q.dim() != 4 or u.dim() != 5:
+        raise ValueError("q, k, v must be [B, H, T, d] and u [B, H, T, r, d]")
     B, H, T, d = q.shape
     r = u.shape[3]
     dt = q.dtype
@@ -75,24 +97,36 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
         raise ValueError("q, k, v, u must share one dtype: float32 or bfloat16")
     if k.shape != q.shape or v.shape != q.shape or tuple(u.shape) != (B, H, T, r, d):
         raise ValueError("shape mismatch among q, k, v, u")
-    for t in (q, k, v, u):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    if not u.is_contiguous():
+        raise ValueError("u must be contiguous")
+    strides = _seq_strides(q, k, v)
+    dev = q.device
+    if any(t is not None and t.device != dev for t in (k, v, u, A0, S0, n0)):
+        raise ValueError("every tensor must be on the device of q")
     for t, shp in ((A0, (B, H, d, d)), (S0, (B, H, d, d)), (n0, (B, H, d))):
         if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("A0/S0/n0 must be contiguous float32 of shape [B,H,d,d]/[B,H,d,d]/[B,H,d]")
-    dev = q.device
     if out is None:
-        o = torch.empty_like(q)
+        o = torch.empty((B, H, T, d), device=dev, dtype=dt)
         A_T = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
         S_T = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
         n_T = torch.empty((B, H, d), device=dev, dtype=torch.float32)
         stats = torch.empty((B, H, 4), device=dev, dtype=torch.int32)
     else:
         o, A_T, S_T, n_T, stats = out
+        _check_out(o, (B, H, T, d), dt, dev, "o")
+        _check_out(A_T, (B, H, d, d), torch.float32, dev, "A_T")
+        _check_out(S_T, (B, H, d, d), torch.float32, dev, "S_T")
+        _check_out(n_T, (B, H, d), torch.float32, dev, "n_T")
+        if stats is not None:
+            _check_out(stats, (B, H, 4), torch.int32, dev, "stats")
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != dev
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {dev}")
+    _need_cuda(q, k, v, u, A0, S0, n0, o, A_T, S_T, n_T, stats, workspace)
     p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
                     t0=t0, schedule=schedule, validate=validate, chunk_len=chunk_len,
-                    segment_blocks=segment_blocks, update=update)
+                    segment_blocks=segment_blocks, update=update, strides=strides)
     lib = _lib.load()
     ws_bytes = ctypes.c_size_t(0)
     _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
@@ -106,6 +140,44 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
             ws_bytes.value,
             _stream_ptr(dev)))
     return o, A_T, S_T, n_T, stats
+
+
+def scan_step(q, k, v, u, A, S, n, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
+              validate=False, update="additive", o=None, stats=None):
+    """Run vla_scan_step: one token per chain (q, k, v [B, H, 1, d], u
+    [B, H, 1, r, d]) with the state A, S [B, H, d, d] and n [B, H, d] (float32)
+    updated in place.  ``t0`` is the token's global index (nudge phase).
+    Returns (o, stats)."""
+    _need_cuda(q, k, v, u, A, S, n)
+    B, H, T, d = q.shape
+    if T != 1:
+        raise ValueError("scan_step takes one token per chain (T = 1)")
+    r = u.shape[3]
+    dt = q.dtype
+    if dt not in _DT or any(x.dtype != dt for x in (k, v, u)):
+        raise ValueError("q, k, v, u must share one dtype: float32 or bfloat16")
+    if k.shape != q.shape or v.shape != q.shape or tuple(u.shape) != (B, H, 1, r, d) or not u.is_contiguous():
+        raise ValueError("shape mismatch among q, k, v, u (u contiguous)")
+    dev = q.device
+    _check_out(A, (B, H, d, d), torch.float32, dev, "A")
+    _check_out(S, (B, H, d, d), torch.float32, dev, "S")
+    _check_out(n, (B, H, d), torch.float32, dev, "n")
+    if o is None:
+        o = torch.empty((B, H, 1, d), device=dev, dtype=dt)
+    _check_out(o, (B, H, 1, d), dt, dev, "o")
+    if stats is None:
+        stats = torch.empty((B, H, 4), device=dev, dtype=torch.int32)
+    _check_out(stats, (B, H, 4), torch.int32, dev, "stats")
+    p = make_params(B, H, 1, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps, t0=t0,
+                    validate=validate, update=update, strides=_seq_strides(q, k, v))
+    lib = _lib.load()
+    ws_bytes = ctypes.c_size_t(0)
+    _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    ws = torch.empty(ws_bytes.value, device=dev, dtype=torch.uint8) if ws_bytes.value else None
+    with torch.cuda.device(dev):
+        _lib.check(lib.vla_scan_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(A), _ptr(S),
+                                     _ptr(n), _ptr(o), _ptr(stats), _ptr(ws), ws_bytes.value, _stream_ptr(dev)))
+    return o, stats
 
 
 def workspace_size(B, H, T, d, r, dtype, **kw) -> int:

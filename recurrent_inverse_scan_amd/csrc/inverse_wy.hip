@@ -101,10 +101,13 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
   // registers held while they fly): lane (c, h) takes features 16 kappa +
   // 8 h .. + 7 of token c of the block for k step kappa.  The buffers end at
   // the chunk's last token, so rows past it read as zero.
-  const auto ru = make_rsrc(ux + chain * T * kD, (tend - 0) * kD * 2);
-  const auto rk = make_rsrc(kx + chain * T * kD, (tend - 0) * kD * 2);
+  // Both buffers start at the chunk's first token, so their extents and
+  // offsets stay below one chunk (at most 512 tokens) whatever T is.
+  const int64_t row0 = chain * T + tbeg;
+  const auto ru = make_rsrc(ux + row0 * kD, (tend - tbeg) * kD * 2);
+  const auto rk = make_rsrc(kx + row0 * kD, (tend - tbeg) * kD * 2);
   auto copy_tokens = [&](int tb) {
-    const int vo = ((tb + c0) * kD + 8 * h0) * 2;
+    const int vo = ((tb - tbeg + c0) * kD + 8 * h0) * 2;
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)&sTok[0][kp][0], 16, vo + 32 * kp, 0, 0, 0);

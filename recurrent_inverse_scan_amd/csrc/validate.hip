@@ -1,6 +1,7 @@
-// Opt-in NaN/Inf pre-check of the scan inputs.  Source: "Mathematical
-// Primitives", section 1 (finite-state enforcement before evaluation).
-// Also the last step of the chunked schedule's statistics.
+// Input pre-passes: the opt-in NaN/Inf pre-check of the scan inputs (source:
+// "Mathematical Primitives", section 1, finite-state enforcement before
+// evaluation) and the gather of strided q, k, v into contiguous rows.  Also
+// the last step of the chunked schedule's statistics.
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
@@ -28,7 +29,36 @@ __global__ void __launch_bounds__(256) stats_finalize_kernel(int32_t* __restrict
   if (c < chains && chain_info[c * 4 + kInfoNonfinite]) stats[c * 4 + 2] = 1;
 }
 
+// q, k, v (blockIdx.y = 0, 1, 2) from strided [B, H, T, d] views into
+// contiguous [B, H, T, d] rows at dst (three tensors back to back), one
+// 16-byte piece per thread and step.  Strides are in elements and keep every
+// row 16-byte aligned (checked on the host).
+__global__ void __launch_bounds__(256) gather_rows_kernel(GatherArgs g) {
+  const char* src = blockIdx.y == 0 ? g.q : (blockIdx.y == 1 ? g.k : g.v);
+  uint4* dst = reinterpret_cast<uint4*>(g.dst + static_cast<int64_t>(blockIdx.y) * g.rows * g.row_bytes);
+  const int vpr = g.row_bytes / 16;
+  const int64_t nvec = g.rows * vpr;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < nvec;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t row = i / vpr;
+    const int piece = static_cast<int>(i - row * vpr);
+    const int64_t t = row % g.T, chain = row / g.T;
+    const int64_t b = chain / g.H, h = chain - b * g.H;
+    const int64_t off = (b * g.stride_b + h * g.stride_h + t * g.stride_t) * g.elem_bytes + 16 * piece;
+    dst[i] = *reinterpret_cast<const uint4*>(src + off);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t stream) {
+  const int64_t nvec = g.rows * (g.row_bytes / 16);
+  if (nvec <= 0) return hipSuccess;
+  const int64_t want = (nvec + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid, 3), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats_finalize(int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream) {
   if (!stats || chains <= 0) return hipSuccess;

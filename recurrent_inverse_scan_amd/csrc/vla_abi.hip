@@ -46,6 +46,7 @@ struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t ev[2 * kMaxChainSegs + 2] = {};
   int side_wg = 0;   // workgroups of a prep or readout launch beside the chain kernel
+  int ncu = 0;       // compute units of the device
   bool ready = false;
 };
 struct SidePool {
@@ -72,6 +73,7 @@ SideStream* side_stream(hipError_t* err) {
     // the chain kernel, which loses a quarter of its speed to a full-width
     // side launch (measured on the 16-chain, 65536-token workload).
     ss.side_wg = std::max(1, ncu * 5 / 8);
+    ss.ncu = ncu;
     if ((*err = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return nullptr;
     for (hipEvent_t& e : ss.ev)
       if ((*err = hipEventCreateWithFlags(&e, hipEventDisableTiming)) != hipSuccess) return nullptr;
@@ -162,6 +164,20 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Whether q, k, v come as strided views (any stride set) rather than contiguous.
+bool strided(const vla_scan_params_t* p) { return p->stride_b != 0 || p->stride_h != 0 || p->stride_t != 0; }
+
+// Bytes from the first to one past the last element a [B, H, T, d] view
+// touches: the contiguous size, or the strided extent.
+size_t seq_extent(const vla_scan_params_t* p, size_t es) {
+  const size_t n_tok = static_cast<size_t>(p->B) * p->H * p->T;
+  if (n_tok == 0) return 0;
+  if (!strided(p)) return n_tok * p->d * es;
+  const uint64_t last = static_cast<uint64_t>(p->B - 1) * p->stride_b + static_cast<uint64_t>(p->H - 1) * p->stride_h +
+                        static_cast<uint64_t>(p->T - 1) * p->stride_t + p->d;
+  return static_cast<size_t>(last) * es;
+}
+
 // Shape of a chunked run and the workspace layout it uses.
 struct ChunkLayout {
   bool use = false;
@@ -169,7 +185,7 @@ struct ChunkLayout {
   int nblk = 0;   // 64-token blocks of the state pass
   size_t off_A = 0, off_S = 0, off_n = 0, off_info = 0, off_G = 0, off_Gpre = 0, off_Gtot = 0, off_ND = 0, off_Ac = 0,
          off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0,
-         off_ncarry = 0, off_cnt = 0, off_flag = 0,
+         off_ncarry = 0, off_cnt = 0, off_flag = 0, off_gather = 0,
          total = 0;
   // Residual update's state pass (replaces the additive one's buffers).
   size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0, off_rex = 0;
@@ -180,6 +196,19 @@ bool chunk_len_fits(const vla_scan_params_t* p, int L) {
   if (L < 16 || L % 16 != 0) return false;
   if (p->nudge_period > 0 && p->nudge_period % L != 0) return false;
   return p->t0 % L == 0;
+}
+
+// The regions every schedule may add at the end: contiguous copies of
+// strided q, k, v, then the validation flag.
+ChunkLayout finish_layout(const vla_scan_params_t* p, ChunkLayout cl, size_t off) {
+  if (strided(p)) {
+    cl.off_gather = off;
+    off = align_up(off + 3 * static_cast<size_t>(p->B) * p->H * p->T * p->d * dtype_size(p->in_dtype));
+  }
+  cl.off_flag = off;
+  if (p->validate) off += kValidateBytes;
+  cl.total = off;
+  return cl;
 }
 
 ChunkLayout plan_schedule(const vla_scan_params_t* p) {
@@ -245,10 +274,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       cl.off_rnb = off; off = align_up(off + C * nb * 64 * 4);
       cl.off_rnc = off; off = align_up(off + 2 * C * 64 * 4);   // normaliser carries between segments
       cl.off_rex = off; off = align_up(off + C * nb * 4);       // per-block exact cap-test flags
-      cl.off_flag = off;
-      if (p->validate) off += kValidateBytes;
-      cl.total = off;
-      return cl;
+      return finish_layout(p, cl, off);
     }
     cl.off_K = off; off = align_up(off + C * nb * 2304 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
@@ -263,10 +289,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.off_ncarry = off; off = align_up(off + C * 64 * 4);
     cl.off_cnt = off; off = align_up(off + C * 2 * 4);
   }
-  cl.off_flag = off;
-  if (p->validate) off += kValidateBytes;
-  cl.total = off;
-  return cl;
+  return finish_layout(p, cl, off);
 }
 
 vla_status_t check_params(const vla_scan_params_t* p) {
@@ -290,6 +313,17 @@ vla_status_t check_params(const vla_scan_params_t* p) {
     return fail(VLA_EUNSUPPORTED, "update %d unsupported", p->update);
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
   if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
+  if (strided(p)) {
+    const int64_t es = static_cast<int64_t>(dtype_size(p->in_dtype));
+    if (p->stride_b < 0 || p->stride_h < 0 || p->stride_t < 0)
+      return fail(VLA_EINVAL, "strides must be >= 0 (got %lld, %lld, %lld)", static_cast<long long>(p->stride_b),
+                  static_cast<long long>(p->stride_h), static_cast<long long>(p->stride_t));
+    if (p->T > 1 && p->stride_t < p->d) return fail(VLA_EINVAL, "stride_t must be >= d when T > 1");
+    if ((p->stride_b * es) % 16 || (p->stride_h * es) % 16 || (p->stride_t * es) % 16)
+      return fail(VLA_EINVAL, "strides times the element size must be multiples of 16 bytes");
+    const int64_t lim = static_cast<int64_t>(1) << 50;
+    if (p->stride_b > lim || p->stride_h > lim || p->stride_t > lim) return fail(VLA_EUNSUPPORTED, "strides too large");
+  }
   return VLA_OK;
 }
 
@@ -339,6 +373,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   const size_t es = dtype_size(p->in_dtype);
   const size_t n_tok = static_cast<size_t>(chains) * static_cast<size_t>(p->T);
   const size_t b_seq = n_tok * d * es, b_u = b_seq * r;
+  const size_t b_in = seq_extent(p, es);   // bytes each of q, k, v spans (strided or not)
   const size_t b_mat = static_cast<size_t>(chains) * d * d * sizeof(float);
   const size_t b_vec = static_cast<size_t>(chains) * d * sizeof(float);
   if (static_cast<uint64_t>(n_tok) * r * d > (1ull << 62)) return fail(VLA_EUNSUPPORTED, "problem too large");
@@ -354,7 +389,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   if (!aligned(n0, 4) || !aligned(n_T, 4)) return fail(VLA_EINVAL, "n0, n_T must be 4-byte aligned");
 
   // Aliasing: outputs may alias only their own initial state, exactly.
-  const struct { const void* p; size_t n; } ins[] = {{q, b_seq}, {k, b_seq}, {v, b_seq}, {u, b_u}};
+  const struct { const void* p; size_t n; } ins[] = {{q, b_in}, {k, b_in}, {v, b_in}, {u, b_u}};
   const struct { const void* p; size_t n; const void* own; } outs[] = {
       {o, b_seq, nullptr}, {A_T, b_mat, A0}, {S_T, b_mat, S0}, {n_T, b_vec, n0},
       {stats, static_cast<size_t>(chains) * 16, nullptr}};
@@ -378,9 +413,9 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     return fail(VLA_EWORKSPACE, "workspace of %zu bytes (256-byte aligned) needed (got %zu)", need,
                 workspace_bytes);
   const ChunkLayout cl = plan_schedule(p);
-  if (cl.use && overlap(workspace, need, A0, b_mat) + overlap(workspace, need, S0, b_mat) +
-                        overlap(workspace, need, n0, b_vec) + overlap(workspace, need, q, b_seq) +
-                        overlap(workspace, need, k, b_seq) + overlap(workspace, need, v, b_seq) +
+  if (need > 0 && overlap(workspace, need, A0, b_mat) + overlap(workspace, need, S0, b_mat) +
+                        overlap(workspace, need, n0, b_vec) + overlap(workspace, need, q, b_in) +
+                        overlap(workspace, need, k, b_in) + overlap(workspace, need, v, b_in) +
                         overlap(workspace, need, u, b_u) + overlap(workspace, need, o, b_seq) +
                         overlap(workspace, need, A_T, b_mat) + overlap(workspace, need, S_T, b_mat) +
                         overlap(workspace, need, n_T, b_vec) > 0)
@@ -388,6 +423,29 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const bool bf16 = p->in_dtype == VLA_BF16;
+
+  // Strided q, k, v: gathered into contiguous rows in the workspace, which
+  // every kernel below then reads in place of the views.
+  if (strided(p) && n_tok > 0) {
+    vla::GatherArgs g{};
+    g.q = static_cast<const char*>(q);
+    g.k = static_cast<const char*>(k);
+    g.v = static_cast<const char*>(v);
+    g.dst = static_cast<char*>(workspace) + cl.off_gather;
+    g.rows = static_cast<int64_t>(n_tok);
+    g.T = p->T;
+    g.H = p->H;
+    g.stride_b = p->stride_b;
+    g.stride_h = p->stride_h;
+    g.stride_t = p->stride_t;
+    g.elem_bytes = static_cast<int32_t>(es);
+    g.row_bytes = static_cast<int32_t>(d * es);
+    const hipError_t e = vla::launch_gather_rows(g, stream);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    q = g.dst;
+    k = g.dst + b_seq;
+    v = g.dst + 2 * b_seq;
+  }
 
   if (p->validate && n_tok > 0) {
     int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cl.off_flag);
@@ -556,10 +614,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
       // holds its units, and runs uncapped.  (Uncapped readouts kept the
       // chain's workgroups waiting: 2.85 against 1.93 ms of chain time per
       // scan on the 65536-token, 16-chain workload.)
-      int ncu = 0;
-      if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0)) != hipSuccess)
-        return hip_fail(e, "device query");
-      const int res_wg = std::max(1, ncu - nch);
+      const int res_wg = std::max(1, ss->ncu - nch);
       auto prep = [&](int sidx) {
         hipError_t r = vla::launch_res_prep(rp, nch, bnd[sidx], bnd[sidx + 1] - bnd[sidx], 0, side);
         if (r == hipSuccess) r = nprefix(sidx, side);
@@ -673,6 +728,17 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
   if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
   return VLA_OK;
+}
+
+vla_status_t vla_scan_step(const vla_scan_params_t* p, const void* q, const void* k, const void* v, const void* u,
+                           float* A, float* S, float* n, void* o, int32_t* stats, void* workspace,
+                           size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  if (!p) return fail(VLA_EINVAL, "params is NULL");
+  if (p->T != 1) return fail(VLA_EINVAL, "vla_scan_step takes one token per chain (T = 1, got %d)", p->T);
+  if (static_cast<int64_t>(p->B) * p->H > 0 && (!A || !S || !n))
+    return fail(VLA_EINVAL, "A, S and n must be non-NULL (the state is updated in place)");
+  return vla_scan_forward(p, q, k, v, u, A, S, n, o, A, S, n, stats, workspace, workspace_bytes, stream_ptr);
 }
 
 vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dtype, vla_dtype_t out_dtype,

@@ -127,6 +127,20 @@ hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_b
 // Sets *flag (device int) to 1 if any of the n elements at the given buffers
 // is NaN or Inf; *flag must be cleared first with launch_clear_flag.
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream);
+
+// Strided q, k, v views gathered into contiguous rows (see gather_rows_kernel).
+struct GatherArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* dst;             // three [rows][row_bytes] tensors back to back
+  int64_t rows;          // B * H * T
+  int64_t T, H;
+  int64_t stride_b, stride_h, stride_t;   // elements
+  int32_t elem_bytes;    // 2 or 4
+  int32_t row_bytes;     // d * elem_bytes, a multiple of 16
+};
+hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t stream);
 // stats[c][2] |= chain_info[c] non-finite flag (stats nullable).
 hipError_t launch_stats_finalize(int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream);
 hipError_t launch_nonfinite_check(const void* p, int64_t n, bool bf16, int32_t* flag, hipStream_t stream);

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vla_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.vla_abi_version() == _lib.ABI_VERSION == 3
     names = [lib.vla_status_string(i).decode() for i in range(6)]
     assert names == ["VLA_OK", "VLA_EINVAL", "VLA_EUNSUPPORTED", "VLA_EWORKSPACE", "VLA_ENONFINITE", "VLA_EHIP"]
 
@@ -72,6 +72,7 @@ def test_params_struct_layout_matches_header(lib, tmp_path):
     assert abs(p.eps - 1e-6) < 1e-12 and abs(p.den_eps - 1e-6) < 1e-12
     assert (p.nudge_period, p.s_cap, p.t0, p.schedule, p.validate, p.chunk_len) == (0, 0.0, 0, 0, 0, 0)
     assert p.segment_blocks == 0 and p.update == _lib.VLA_UPDATE_ADDITIVE
+    assert (p.stride_b, p.stride_h, p.stride_t) == (0, 0, 0)
 
 
 def _params(lib, **kw):
@@ -183,3 +184,134 @@ def test_residual_update_schedules(lib):
     assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
     q = _params(lib, B=1, H=2, T=4096, d=128, schedule=_lib.VLA_SCHEDULE_CHUNKED, update=_lib.VLA_UPDATE_RESIDUAL)
     assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# Strided q, k, v (element strides over batch, head and token; d contiguous).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("strides,status", [
+    ((-64, 64, 64), _lib.VLA_EINVAL),          # negative
+    ((4096, 64, 32), _lib.VLA_EINVAL),         # stride_t < d with T > 1
+    ((4096, 66, 64), _lib.VLA_EINVAL),         # 66 * 4 bytes is not a multiple of 16
+    ((1 << 60, 64, 64), _lib.VLA_EUNSUPPORTED),
+])
+def test_scan_rejects_bad_strides(lib, strides, status):
+    p = _params(lib, stride_b=strides[0], stride_h=strides[1], stride_t=strides[2])
+    assert _scan(lib, p) == status
+    assert lib.vla_last_error().decode() != ""
+
+
+def test_strided_inputs_need_gather_workspace(lib):
+    """Strided views are gathered into the workspace: the sequential schedule
+    then needs 3 * B*H*T*d elements of it, and the extent a strided view spans
+    counts in the overlap checks."""
+    n = ctypes.c_size_t(0)
+    B, H, T, d = 2, 3, 5, 64
+    p = _params(lib, B=B, H=H, T=T, d=d)
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+    # q from a packed [B, T, H, 3d] float32 projection
+    p.stride_b, p.stride_h, p.stride_t = T * H * 3 * d, 3 * d, H * 3 * d
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK
+    assert n.value >= 3 * B * H * T * d * 4
+    p.in_dtype = _lib.VLA_BF16
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK
+    assert 3 * B * H * T * d * 2 <= n.value < 3 * B * H * T * d * 4
+    # no workspace given: refused before any launch
+    p.in_dtype = _lib.VLA_F32
+    assert _scan(lib, p, o=ctypes.c_void_p(0x7000000), A_T=ctypes.c_void_p(0x7100000),
+                 S_T=ctypes.c_void_p(0x7200000), n_T=ctypes.c_void_p(0x7300000)) == _lib.VLA_EWORKSPACE
+    # o inside the span of a strided q (between its rows) overlaps it
+    span = ((B - 1) * p.stride_b + (H - 1) * p.stride_h + (T - 1) * p.stride_t + d) * 4
+    assert span > B * H * T * d * 4
+    q0 = 0x10000000
+    ptrs = dict(q=ctypes.c_void_p(q0), k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x30000000),
+                u=ctypes.c_void_p(0x40000000), A_T=ctypes.c_void_p(0x7100000), S_T=ctypes.c_void_p(0x7200000),
+                n_T=ctypes.c_void_p(0x7300000))
+    assert _scan(lib, p, o=ctypes.c_void_p(q0 + span - 256), **ptrs) == _lib.VLA_EINVAL
+    assert "overlaps" in lib.vla_last_error().decode()
+    # just past the span: the aliasing checks pass and the missing workspace is what stops it
+    assert _scan(lib, p, o=ctypes.c_void_p(q0 + span), **ptrs) == _lib.VLA_EWORKSPACE
+
+
+def _step(lib, p, A=FAKE, S=FAKE, n=FAKE, **ptrs):
+    args = {x: FAKE for x in ("q", "k", "v", "u", "o")}
+    args.update(ptrs)
+    return lib.vla_scan_step(ctypes.byref(p), args["q"], args["k"], args["v"], args["u"], A, S, n, args["o"],
+                             None, None, 0, None)
+
+
+def test_scan_step_validates_before_launching(lib):
+    """vla_scan_step takes exactly one token and an in-place state."""
+    p = _params(lib, T=4)
+    assert _step(lib, p) == _lib.VLA_EINVAL and "T = 1" in lib.vla_last_error().decode()
+    p = _params(lib, T=1)
+    assert _step(lib, p, A=None) == _lib.VLA_EINVAL
+    assert _step(lib, p, n=None) == _lib.VLA_EINVAL
+    assert lib.vla_scan_step(None, None, None, None, None, None, None, None, None, None, None, 0,
+                             None) == _lib.VLA_EINVAL
+    p = _params(lib, T=1, d=48)
+    assert _step(lib, p) == _lib.VLA_EUNSUPPORTED
+    p = _params(lib, T=1, B=0)
+    assert lib.vla_scan_step(ctypes.byref(p), None, None, None, None, None, None, None, None, None, None, 0,
+                             None) == _lib.VLA_OK
+
+
+# --------------------------------------------------------------------------
+# The Python binding checks caller-supplied outputs and workspace before it
+# reaches the C ABI (the library sizes every write from the parameters, so a
+# wrong buffer would otherwise be written out of bounds).  CPU tensors stand
+# in for device ones: the shape, dtype and layout checks come first.
+# --------------------------------------------------------------------------
+def _cpu_args(B=1, H=2, T=3, d=16, r=1, dt=None):
+    import torch
+
+    dt = dt or torch.float32
+    q = torch.zeros(B, H, T, d, dtype=dt)
+    u = torch.zeros(B, H, T, r, d, dtype=dt)
+    outs = [torch.zeros(B, H, T, d, dtype=dt), torch.zeros(B, H, d, d), torch.zeros(B, H, d, d),
+            torch.zeros(B, H, d), torch.zeros(B, H, 4, dtype=torch.int32)]
+    return q, u, outs
+
+
+@pytest.mark.parametrize("which,bad,msg", [
+    (0, "bf16", "o must be"), (0, "shape", "o must be"), (1, "shape", "A_T must be"), (1, "f64", "A_T must be"),
+    (2, "noncontig", "S_T must be"), (3, "shape", "n_T must be"), (4, "i64", "stats must be"),
+    (4, "shape", "stats must be"),
+])
+def test_binding_rejects_bad_out_tensors(which, bad, msg):
+    import torch
+
+    from recurrent_inverse_scan_amd import scan_forward
+
+    q, u, outs = _cpu_args()
+    t = outs[which]
+    if bad == "bf16":
+        t = t.to(torch.bfloat16)
+    elif bad == "shape":
+        t = t.reshape(-1)[:-1].clone() if t.numel() > 1 else t
+    elif bad == "f64":
+        t = t.double()
+    elif bad == "i64":
+        t = t.long()
+    elif bad == "noncontig":
+        t = t.transpose(-1, -2)
+    outs[which] = t
+    with pytest.raises(ValueError, match=msg):
+        scan_forward(q, q, q, u, out=tuple(outs))
+
+
+def test_binding_rejects_bad_workspace_and_mixed_strides():
+    import torch
+
+    from recurrent_inverse_scan_amd import scan_forward
+
+    q, u, outs = _cpu_args()
+    with pytest.raises(ValueError, match="workspace"):
+        scan_forward(q, q, q, u, out=tuple(outs), workspace=torch.zeros(64, dtype=torch.float32))
+    packed = torch.zeros(1, 3, 2, 48)                  # [B, T, H, 3d]
+    qs = packed[..., :16].permute(0, 2, 1, 3)          # strided [B, H, T, d] views
+    with pytest.raises(ValueError, match="share their strides"):
+        scan_forward(qs, q, q, u)                       # q strided, k and v contiguous
+    # well-formed CPU tensors reach the device check last
+    with pytest.raises(ValueError, match="HIP device"):
+        scan_forward(qs, packed[..., 16:32].permute(0, 2, 1, 3), packed[..., 32:].permute(0, 2, 1, 3), u)

@@ -504,3 +504,59 @@ def test_decode_steps_match_one_call(update):
     _check(cfg, (o_steps, A, S, n, whole[4]), ref)
     assert rel_err(o_steps, whole[0].float().cpu().numpy()) <= 1e-2
     assert np.abs(fires.reshape(-1) - ref["cap_fires"]).max() <= 1
+
+
+# ---------------------------------------------------------------------------
+# Strided q, k, v (views of one packed projection) and the decode entry point.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("schedule,T", [("sequential", 77), ("chunked", 640), ("auto", 1)])
+def test_strided_views_of_a_packed_projection(dtype, schedule, T):
+    """q, k, v sliced from one [B, T, H, 3d] tensor and permuted to
+    [B, H, T, d] views (strides T*H*3d, 3d, H*3d) give the same result as
+    contiguous copies, and match the oracle."""
+    cfg = CONFIGS["base"].with_(name=f"strided-{schedule}-{dtype}-T{T}", B=2, H=3, T=T, in_dtype=dtype,
+                                nudge_period=64 if T > 1 else 0, s_cap=40.0)
+    _say(f"case strided {schedule} {dtype} T={T}")
+    x = case(cfg, seed=50 + T)
+    d = cfg.d
+    packed = torch.cat([x["q"], x["k"], x["v"]], dim=-1).permute(0, 2, 1, 3).contiguous().to(DEV)  # [B,T,H,3d]
+    qs, ks, vs = (packed[..., i * d:(i + 1) * d].permute(0, 2, 1, 3) for i in range(3))
+    assert not qs.is_contiguous() and qs.stride()[:2] == (T * cfg.H * 3 * d, 3 * d) and qs.stride(3) == 1
+    assert T == 1 or qs.stride(2) == cfg.H * 3 * d   # (torch normalises a size-1 dimension's stride)
+    kw = dict(nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, schedule=schedule)
+    if schedule == "chunked":
+        kw["chunk_len"] = 64
+    got = scan_forward(qs, ks, vs, x["u"].to(DEV), **kw)
+    want = _gpu(x, cfg, schedule=schedule, **({"chunk_len": 64} if schedule == "chunked" else {}))
+    for a_, b_ in zip(got, want):
+        assert torch.equal(a_, b_)
+    _check(cfg, got, run_oracle(x, cfg))
+
+
+@pytest.mark.parametrize("update", ["additive", "residual"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_step_entry_point(update, dtype):
+    """vla_scan_step over 20 tokens (state in place, t0 advancing through
+    nudges) equals the oracle's 20-token scan and one vla_scan_forward call."""
+    from recurrent_inverse_scan_amd import scan_step
+
+    cfg = CONFIGS["long"].with_(name=f"step-{update}-{dtype}", B=3, H=4, T=20, in_dtype=dtype, nudge_period=6,
+                                s_cap=10.0)
+    x = case(cfg, seed=60)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    A = torch.eye(d, device=DEV).expand(B, H, d, d).contiguous()
+    S = torch.zeros(B, H, d, d, device=DEV)
+    n = torch.zeros(B, H, d, device=DEV)
+    outs, fires = [], 0
+    for t in range(cfg.T):
+        sl = {key: x[key][:, :, t:t + 1].contiguous().to(DEV) for key in ("q", "k", "v", "u")}
+        o, st = scan_step(sl["q"], sl["k"], sl["v"], sl["u"], A, S, n, nudge_period=cfg.nudge_period,
+                          s_cap=cfg.s_cap, t0=t, update=update)
+        torch.cuda.synchronize()
+        fires = fires + st[..., 1].cpu().numpy()
+        outs.append(o)
+    whole = _gpu(x, cfg, update=update)
+    ref = run_oracle(x, cfg, update=update)
+    _check(cfg, (torch.cat(outs, dim=2), A, S, n, whole[4]), ref)
+    assert np.abs(fires.reshape(-1) - ref["cap_fires"]).max() <= 1
