@@ -224,6 +224,35 @@ vla_status_t vla_scan_step(const vla_scan_params_t* p,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * vla_scan_forward_noalloc: vla_scan_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no workspace argument: the
+ * scratch that vla_scan_forward would take from its workspace (the chunked
+ * schedule's buffers, the gather of strided inputs, the validation flag)
+ * comes from a static device array of VLA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends.  Its
+ * device address is looked up once per device, on the first call with that
+ * device current.
+ *
+ * Arguments, layouts, results and errors are those of vla_scan_forward.  A
+ * call whose vla_scan_workspace_size() exceeds VLA_NOALLOC_SCRATCH_BYTES is
+ * refused with VLA_EWORKSPACE before anything is launched (e.g. the chunked
+ * schedule on 16 chains of 65536 tokens, about 1.2 GB); the caller can then
+ * use vla_scan_forward with its own workspace.  The call allocates nothing
+ * (no hipMalloc or hipFree, no allocating library routine).  Every call on a
+ * device shares that device's array, and each call overwrites what the last
+ * one left there (the kernels initialise whatever they read back): calls that
+ * overlap in time on one device, on different streams or from different
+ * threads, race on it and must be serialised by the caller.
+ */
+#define VLA_NOALLOC_SCRATCH_BYTES (256ull << 20)
+vla_status_t vla_scan_forward_noalloc(const vla_scan_params_t* p,
+                                      const void* q, const void* k, const void* v, const void* u,
+                                      const float* A0, const float* S0, const float* n0,
+                                      void* o, float* A_T, float* S_T, float* n_T, int32_t* stats,
+                                      void* stream);
+
+/*
  * vla_project_u: learned penalty directions, u_{row, i} = normalize(W_u[i] k_raw[row]).
  *
  * Source: "Variational Linear Attention (VLA)" README, v3 notes item 2

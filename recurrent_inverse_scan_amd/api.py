@@ -142,6 +142,46 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     return o, A_T, S_T, n_T, stats
 
 
+def scan_forward_noalloc(q, k, v, u, A0=None, S0=None, n0=None, *, out, eps=1e-6, nudge_period=0, s_cap=None,
+                         den_eps=1e-6, t0=0, schedule="auto", validate=False, chunk_len=0, segment_blocks=0,
+                         update="additive"):
+    """Run vla_scan_forward_noalloc: scan_forward with the library's static
+    per-device scratch instead of a workspace.  ``out`` = (o, A_T, S_T, n_T,
+    stats) must be preallocated (stats may be None); nothing is allocated.
+    Calls that overlap on one device race on the shared scratch."""
+    if q.dim() != 4 or u.dim() != 5:
+        raise ValueError("q, k, v must be [B, H, T, d] and u [B, H, T, r, d]")
+    B, H, T, d = q.shape
+    r = u.shape[3]
+    dt = q.dtype
+    if dt not in _DT or any(x.dtype != dt for x in (k, v, u)):
+        raise ValueError("q, k, v, u must share one dtype: float32 or bfloat16")
+    if k.shape != q.shape or v.shape != q.shape or tuple(u.shape) != (B, H, T, r, d) or not u.is_contiguous():
+        raise ValueError("shape mismatch among q, k, v, u (u contiguous)")
+    dev = q.device
+    for t, shp in ((A0, (B, H, d, d)), (S0, (B, H, d, d)), (n0, (B, H, d))):
+        if t is not None:
+            _check_out(t, shp, torch.float32, dev, "A0/S0/n0")
+    o, A_T, S_T, n_T, stats = out
+    _check_out(o, (B, H, T, d), dt, dev, "o")
+    _check_out(A_T, (B, H, d, d), torch.float32, dev, "A_T")
+    _check_out(S_T, (B, H, d, d), torch.float32, dev, "S_T")
+    _check_out(n_T, (B, H, d), torch.float32, dev, "n_T")
+    if stats is not None:
+        _check_out(stats, (B, H, 4), torch.int32, dev, "stats")
+    strides = _seq_strides(q, k, v)
+    _need_cuda(q, k, v, u, A0, S0, n0, o, A_T, S_T, n_T, stats)
+    p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
+                    t0=t0, schedule=schedule, validate=validate, chunk_len=chunk_len,
+                    segment_blocks=segment_blocks, update=update, strides=strides)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check(lib.vla_scan_forward_noalloc(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(A0), _ptr(S0), _ptr(n0),
+            _ptr(o), _ptr(A_T), _ptr(S_T), _ptr(n_T), _ptr(stats), _stream_ptr(dev)))
+    return o, A_T, S_T, n_T, stats
+
+
 def scan_step(q, k, v, u, A, S, n, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
               validate=False, update="additive", o=None, stats=None):
     """Run vla_scan_step: one token per chain (q, k, v [B, H, 1, d], u

@@ -124,6 +124,20 @@ int chain_segments(int nblk, int seg_blocks, int* bnd) {
   return n - 1;
 }
 
+// Scratch of vla_scan_forward_noalloc: one static array per device, held
+// until the process ends.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and is kept here.
+__device__ __align__(256) unsigned char scratch[VLA_NOALLOC_SCRATCH_BYTES];
+struct ScratchTable {
+  std::mutex mu;
+  void* ptr[64] = {};
+};
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+
 vla_status_t fail(vla_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 vla_status_t fail(vla_status_t s, const char* fmt, ...) {
   char buf[512];
@@ -728,6 +742,39 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
   if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
   return VLA_OK;
+}
+
+vla_status_t vla_scan_forward_noalloc(const vla_scan_params_t* p, const void* q, const void* k, const void* v,
+                                      const void* u, const float* A0, const float* S0, const float* n0, void* o,
+                                      float* A_T, float* S_T, float* n_T, int32_t* stats, void* stream_ptr) {
+  g_last_error.clear();
+  size_t need = 0;
+  vla_status_t s = vla_scan_workspace_size(p, &need);
+  if (s != VLA_OK) return s;
+  if (need > VLA_NOALLOC_SCRATCH_BYTES)
+    return fail(VLA_EWORKSPACE,
+                "this call needs %zu bytes of scratch; vla_scan_forward_noalloc holds %llu (use vla_scan_forward "
+                "with a workspace)",
+                need, static_cast<unsigned long long>(VLA_NOALLOC_SCRATCH_BYTES));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  if (dev < 0 || dev >= 64) return fail(VLA_EUNSUPPORTED, "device ordinal %d out of range", dev);
+  void* ws = nullptr;
+  {
+    ScratchTable& tb = scratch_table();
+    std::lock_guard<std::mutex> lock(tb.mu);
+    if (!tb.ptr[dev]) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+      if (!addr || !aligned(addr, kAlign)) return fail(VLA_EHIP, "scratch address lookup returned a bad address");
+      tb.ptr[dev] = addr;
+    }
+    ws = tb.ptr[dev];
+  }
+  return vla_scan_forward(p, q, k, v, u, A0, S0, n0, o, A_T, S_T, n_T, stats, need > 0 ? ws : nullptr, need,
+                          stream_ptr);
 }
 
 vla_status_t vla_scan_step(const vla_scan_params_t* p, const void* q, const void* k, const void* v, const void* u,
