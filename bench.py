@@ -339,6 +339,34 @@ def extra_measurements(CONFIGS, dev):
             "kernel": "vla_state_chain_kernel" if sched == "chunked" else seq_kernel_name(d, T)}
         del q, k, v, u, o, x, ws
 
+    # Backward pass (additive update, sequential per chain): the recall and
+    # base workloads.  Algorithmic work of the reverse recurrence, 2 (5r + 10)
+    # d^2 flops per token*head: per rank-1 step (G + G^T) z, the gA and
+    # A^T gz products and rebuilding A_before (5 d^2 FMA); per token the
+    # readout's S q, S^T g_o and g_o q^T, the state step's gX alpha_hat and
+    # gX^T v, the coefficient's g_alpha k^T and A^T g_alpha, and the
+    # recomputed S (10 d^2 FMA).  The forward pass that records the tape is
+    # a recomputation and is not counted.
+    from recurrent_inverse_scan_amd import scan_backward
+
+    for name, reps in (("recall", 3), ("base", 2)):
+        cfg = CONFIGS[name]
+        x = make_inputs(cfg, seed=0)
+        q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+        u = project_u(x["W_u"].to(dev), x["k_raw"].to(dev))
+        B, H, T, d, r = cfg.B, cfg.H, cfg.T, cfg.d, cfg.r
+        go = torch.randn(B, H, T, d, device=dev)
+        fn = lambda: scan_backward(q, k, v, u, g_o=go, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+        ms = _time_ms(fn, reps, warmup=1)
+        th = B * H * T
+        tfl = 2 * (5 * r + 10) * d * d * th / (ms * 1e-3) / 1e12
+        out[f"backward_{name}"] = {
+            "workload": f"{name}: backward of the additive scan, B={B} H={H} T={T} d={d} r={r}, "
+                        f"{cfg.in_dtype} storage, float32 gradients", "ms": ms,
+            "tokens_heads_per_s": th / (ms * 1e-3), "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
+            "kernel": "vla_bwd_tape_kernel + vla_bwd_reverse_kernel"}
+        del q, k, v, u, x, go
+
     # Decode: 4096 chains, one token per call, state carried in place.
     B, H, d, r = 256, 16, 64, 1
     g = torch.Generator(device="cpu").manual_seed(0)
@@ -396,9 +424,21 @@ def cpu_baseline(cfg, x, budget_s: float, update: str = "additive"):
         visible = len(os.sched_getaffinity(0))
     except AttributeError:
         visible = os.cpu_count()
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import numpy
+
     return {"value": C * n_tok / dt, "unit": "tokens*heads/s", "cores": 1, "kind": "oracle",
             "sample": f"all {C} chains, first {n_tok} of {cfg.T} tokens (projection + scan), fp64 NumPy, "
-                      f"{dt:.1f} s wall on 1 thread (BLAS limited to 1; {visible} cores visible)"}
+                      f"{dt:.1f} s wall on 1 thread (BLAS limited to 1; {visible} cores visible)",
+            "cpu_model": cpu_model, "numpy": numpy.__version__}
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
  *   vla_scan_forward  the VLA recurrence scan over a sequence, per (batch, head)
  *   vla_scan_step     one token per chain with the state updated in place
  *                     (streaming decode)
+ *   vla_scan_backward the gradients of the scan (additive update)
  *   vla_project_u     the learned penalty directions u = normalize(W_u k_raw)
  *
  * plus parameter, workspace and status helpers.
@@ -222,6 +223,44 @@ vla_status_t vla_scan_step(const vla_scan_params_t* p,
                            const void* q, const void* k, const void* v, const void* u,
                            float* A, float* S, float* n, void* o, int32_t* stats,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vla_scan_backward: gradients of the scan with the ADDITIVE update.
+ *
+ * Source: "Variational Linear Attention (VLA)" README, v3 notes item 2 (the
+ * scan keeps full gradient flow) and "Running the Sub-Tests" (gradient
+ * checks); "Mathematical Primitives" section 5 (a stable backward pass).  The
+ * pages give only the forward recurrence of vla_scan_forward; this call
+ * returns its exact derivative (up to float32 rounding) for the loss
+ *   L = sum_t <g_o[t], o_t> + <g_AT, A_T> + <g_ST, S_T> + <g_nT, n_T>
+ * with respect to q, k, v, u, A0, S0 and n0, at the same parameters.  The
+ * derivative follows the forward's branches: a rank-1 step the guard skipped
+ * passes no gradient to its direction, and the cap contributes only on the
+ * tokens where it fired.
+ *
+ *   p        as for vla_scan_forward; supported: d in {16, 32, 64}, r 1..4,
+ *            f32 or bf16 storage, update = ADDITIVE, contiguous inputs (all
+ *            strides 0); the schedule field is ignored (one workgroup per
+ *            chain runs the forward again with a tape, then the reverse)
+ *   q..n0    the forward's inputs (A0, S0, n0 nullable: I, 0, 0)
+ *   g_o      [B, H, T, d] float32 (may be NULL only when T = 0)
+ *   g_AT, g_ST [B, H, d, d], g_nT [B, H, d] float32, each nullable (zero)
+ *   g_q, g_k, g_v [B, H, T, d], g_u [B, H, T, r, d], g_A0, g_S0 [B, H, d, d],
+ *   g_n0 [B, H, d]: float32 gradients (written; all non-NULL, none may
+ *            overlap an input or another output)
+ *   workspace at least vla_scan_backward_workspace_size() bytes, 256-byte
+ *            aligned: the tape (per token the r rank-1 steps' z and delta,
+ *            alpha_hat, |alpha|, the cap scale) and A, S, n every 32 tokens
+ * Errors as for vla_scan_forward: VLA_EUNSUPPORTED outside the supported set.
+ */
+vla_status_t vla_scan_backward_workspace_size(const vla_scan_params_t* p, size_t* bytes);
+vla_status_t vla_scan_backward(const vla_scan_params_t* p,
+                               const void* q, const void* k, const void* v, const void* u,
+                               const float* A0, const float* S0, const float* n0,
+                               const float* g_o, const float* g_AT, const float* g_ST, const float* g_nT,
+                               float* g_q, float* g_k, float* g_v, float* g_u,
+                               float* g_A0, float* g_S0, float* g_n0,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vla_scan_forward_noalloc: vla_scan_forward for callers that cannot

@@ -220,6 +220,49 @@ def scan_step(q, k, v, u, A, S, n, *, eps=1e-6, nudge_period=0, s_cap=None, den_
     return o, stats
 
 
+def scan_backward(q, k, v, u, A0=None, S0=None, n0=None, *, g_o, g_A=None, g_S=None, g_n=None, eps=1e-6,
+                  nudge_period=0, s_cap=None, den_eps=1e-6, t0=0):
+    """Run vla_scan_backward: gradients of sum <g_o, o> + <g_A, A_T> + <g_S, S_T>
+    + <g_n, n_T> for the additive scan with the same arguments as scan_forward.
+
+    g_o is [B, H, T, d] float32; g_A, g_S, g_n are float32 or None (zero).
+    Returns a dict of float32 gradients q, k, v, u, A0, S0, n0."""
+    if q.dim() != 4 or u.dim() != 5:
+        raise ValueError("q, k, v must be [B, H, T, d] and u [B, H, T, r, d]")
+    B, H, T, d = q.shape
+    r = u.shape[3]
+    dt = q.dtype
+    if dt not in _DT or any(x.dtype != dt for x in (k, v, u)):
+        raise ValueError("q, k, v, u must share one dtype: float32 or bfloat16")
+    if k.shape != q.shape or v.shape != q.shape or tuple(u.shape) != (B, H, T, r, d):
+        raise ValueError("shape mismatch among q, k, v, u")
+    if not all(t.is_contiguous() for t in (q, k, v, u)):
+        raise ValueError("scan_backward takes contiguous inputs")
+    dev = q.device
+    for t, shp, name in ((A0, (B, H, d, d), "A0"), (S0, (B, H, d, d), "S0"), (n0, (B, H, d), "n0"),
+                         (g_o, (B, H, T, d), "g_o"), (g_A, (B, H, d, d), "g_A"), (g_S, (B, H, d, d), "g_S"),
+                         (g_n, (B, H, d), "g_n")):
+        if t is not None:
+            _check_out(t, shp, torch.float32, dev, name)
+    _need_cuda(q, k, v, u, A0, S0, n0, g_o, g_A, g_S, g_n)
+    p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps, t0=t0)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check(lib.vla_scan_backward_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), device=dev, dtype=torch.uint8)
+    f32 = dict(device=dev, dtype=torch.float32)
+    g = {"q": torch.empty((B, H, T, d), **f32), "k": torch.empty((B, H, T, d), **f32),
+         "v": torch.empty((B, H, T, d), **f32), "u": torch.empty((B, H, T, r, d), **f32),
+         "A0": torch.empty((B, H, d, d), **f32), "S0": torch.empty((B, H, d, d), **f32),
+         "n0": torch.empty((B, H, d), **f32)}
+    with torch.cuda.device(dev):
+        _lib.check(lib.vla_scan_backward(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(A0), _ptr(S0), _ptr(n0), _ptr(g_o),
+            _ptr(g_A), _ptr(g_S), _ptr(g_n), _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["u"]), _ptr(g["A0"]),
+            _ptr(g["S0"]), _ptr(g["n0"]), _ptr(ws), nbytes.value, _stream_ptr(dev)))
+    return g
+
+
 def workspace_size(B, H, T, d, r, dtype, **kw) -> int:
     """Bytes of workspace vla_scan_forward needs (keyword arguments as scan_forward)."""
     p = make_params(B, H, T, d, r, dtype, **kw)

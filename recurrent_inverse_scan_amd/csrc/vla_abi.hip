@@ -744,6 +744,88 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   return VLA_OK;
 }
 
+namespace {
+vla_status_t check_backward(const vla_scan_params_t* p) {
+  vla_status_t s = check_params(p);
+  if (s != VLA_OK) return s;
+  if (p->d > 64) return fail(VLA_EUNSUPPORTED, "vla_scan_backward supports d = 16, 32, 64 (got %d)", p->d);
+  if (p->update != VLA_UPDATE_ADDITIVE) return fail(VLA_EUNSUPPORTED, "vla_scan_backward supports the additive update");
+  if (strided(p)) return fail(VLA_EUNSUPPORTED, "vla_scan_backward takes contiguous inputs (strides 0)");
+  return VLA_OK;
+}
+}  // namespace
+
+vla_status_t vla_scan_backward_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(VLA_EINVAL, "bytes is NULL");
+  const vla_status_t s = check_backward(p);
+  if (s != VLA_OK) return s;
+  *bytes = vla::bwd_workspace_bytes(static_cast<int64_t>(p->B) * p->H, p->T, p->d, p->r);
+  return VLA_OK;
+}
+
+vla_status_t vla_scan_backward(const vla_scan_params_t* p, const void* q, const void* k, const void* v,
+                               const void* u, const float* A0, const float* S0, const float* n0, const float* g_o,
+                               const float* g_AT, const float* g_ST, const float* g_nT, float* g_q, float* g_k,
+                               float* g_v, float* g_u, float* g_A0, float* g_S0, float* g_n0, void* workspace,
+                               size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  vla_status_t s = check_backward(p);
+  if (s != VLA_OK) return s;
+  const int64_t chains = static_cast<int64_t>(p->B) * p->H;
+  if (chains == 0) return VLA_OK;
+  const int d = p->d, r = p->r;
+  const size_t es = dtype_size(p->in_dtype);
+  const size_t n_tok = static_cast<size_t>(chains) * static_cast<size_t>(p->T);
+  const size_t b_seq = n_tok * d * es, b_u = b_seq * r, b_g = n_tok * d * 4, b_gu = b_g * r;
+  const size_t b_mat = static_cast<size_t>(chains) * d * d * 4, b_vec = static_cast<size_t>(chains) * d * 4;
+  if (n_tok > 0 && (!q || !k || !v || !u || !g_o || !g_q || !g_k || !g_v || !g_u))
+    return fail(VLA_EINVAL, "q, k, v, u, g_o and g_q, g_k, g_v, g_u must be non-NULL");
+  if (!g_A0 || !g_S0 || !g_n0) return fail(VLA_EINVAL, "g_A0, g_S0 and g_n0 must be non-NULL");
+  const void* al16[] = {q, k, v, u, g_o, g_q, g_k, g_v, g_u};
+  for (const void* x : al16)
+    if (n_tok > 0 && !aligned(x, 16)) return fail(VLA_EINVAL, "sequence tensors must be 16-byte aligned");
+  const void* al4[] = {A0, S0, n0, g_AT, g_ST, g_nT, g_A0, g_S0, g_n0};
+  for (const void* x : al4)
+    if (!aligned(x, 4)) return fail(VLA_EINVAL, "state tensors must be 4-byte aligned");
+  const struct { const void* p; size_t n; } ins[] = {{q, b_seq}, {k, b_seq}, {v, b_seq}, {u, b_u}, {A0, b_mat},
+                                                     {S0, b_mat}, {n0, b_vec}, {g_o, b_g}, {g_AT, b_mat},
+                                                     {g_ST, b_mat}, {g_nT, b_vec}};
+  const struct { const void* p; size_t n; } outs[] = {{g_q, b_g}, {g_k, b_g}, {g_v, b_g}, {g_u, b_gu},
+                                                      {g_A0, b_mat}, {g_S0, b_mat}, {g_n0, b_vec}};
+  const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
+  for (int oi = 0; oi < n_outs; ++oi) {
+    for (const auto& in : ins)
+      if (overlap(outs[oi].p, outs[oi].n, in.p, in.n)) return fail(VLA_EINVAL, "a gradient overlaps an input");
+    for (int oj = oi + 1; oj < n_outs; ++oj)
+      if (overlap(outs[oi].p, outs[oi].n, outs[oj].p, outs[oj].n))
+        return fail(VLA_EINVAL, "gradients overlap each other");
+  }
+  const size_t need = vla::bwd_workspace_bytes(chains, p->T, d, r);
+  if (workspace_bytes < need || !workspace || !aligned(workspace, kAlign))
+    return fail(VLA_EWORKSPACE, "workspace of %zu bytes (256-byte aligned) needed (got %zu)", need, workspace_bytes);
+  for (const auto& in : ins)
+    if (overlap(workspace, need, in.p, in.n)) return fail(VLA_EINVAL, "workspace overlaps an input");
+  for (const auto& ot : outs)
+    if (overlap(workspace, need, ot.p, ot.n)) return fail(VLA_EINVAL, "workspace overlaps a gradient");
+  vla::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.u = u;
+  a.A0 = A0; a.S0 = S0; a.n0 = n0;
+  a.go = g_o; a.gAT = g_AT; a.gST = g_ST; a.gnT = g_nT;
+  a.gq = g_q; a.gk = g_k; a.gv = g_v; a.gu = g_u; a.gA0 = g_A0; a.gS0 = g_S0; a.gn0 = g_n0;
+  a.T = p->T; a.r = r; a.eps = p->eps;
+  a.nudge_period = p->nudge_period;
+  a.nudge_phase0 = p->nudge_period > 0 ? static_cast<int32_t>((p->t0 + 1) % p->nudge_period) : 0;
+  a.cap_on = (p->s_cap > 0.f && std::isfinite(p->s_cap)) ? 1 : 0;
+  a.cap = a.cap_on ? p->s_cap : 0.f;
+  a.den_eps = p->den_eps;
+  vla::bwd_carve(a, workspace, chains, p->T, d, r);
+  const hipError_t e = vla::launch_backward(a, d, p->in_dtype == VLA_BF16, static_cast<int>(chains),
+                                            static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return VLA_OK;
+}
+
 vla_status_t vla_scan_forward_noalloc(const vla_scan_params_t* p, const void* q, const void* k, const void* v,
                                       const void* u, const float* A0, const float* S0, const float* n0, void* o,
                                       float* A_T, float* S_T, float* n_T, int32_t* stats, void* stream_ptr) {

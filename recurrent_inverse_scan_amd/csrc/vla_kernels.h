@@ -141,6 +141,47 @@ struct GatherArgs {
   int32_t row_bytes;     // d * elem_bytes, a multiple of 16
 };
 hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t stream);
+
+// Backward pass (backward.hip): inputs, cotangents, gradients and the tape.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* u;
+  const float* A0;    // nullable: I
+  const float* S0;    // nullable: 0
+  const float* n0;    // nullable: 0
+  const float* go;    // [chains][T][d] fp32
+  const float* gAT;   // nullable cotangents of the final state
+  const float* gST;
+  const float* gnT;
+  float* gq;          // [chains][T][d]
+  float* gk;
+  float* gv;
+  float* gu;          // [chains][T][r][d]
+  float* gA0;         // [chains][d][d]
+  float* gS0;
+  float* gn0;         // [chains][d]
+  int32_t T, r;
+  float eps;
+  int32_t nudge_period, nudge_phase0;
+  int32_t cap_on;
+  float cap, den_eps;
+  // tape and checkpoints (workspace)
+  float* ckA;
+  float* ckS;
+  float* ckn;
+  float* sbuf;
+  float* tz;
+  float* tdelta;
+  float* tfire;
+  float* tah;
+  float* tan_;
+  float* tc;
+};
+size_t bwd_workspace_bytes(int64_t chains, int T, int d, int r);
+void bwd_carve(BwdArgs& a, void* ws, int64_t chains, int T, int d, int r);
+hipError_t launch_backward(const BwdArgs& a, int d, bool bf16, int chains, hipStream_t stream);
 // stats[c][2] |= chain_info[c] non-finite flag (stats nullable).
 hipError_t launch_stats_finalize(int32_t* stats, const int32_t* chain_info, int chains, hipStream_t stream);
 hipError_t launch_nonfinite_check(const void* p, int64_t n, bool bf16, int32_t* flag, hipStream_t stream);

@@ -315,3 +315,42 @@ def test_binding_rejects_bad_workspace_and_mixed_strides():
     # well-formed CPU tensors reach the device check last
     with pytest.raises(ValueError, match="HIP device"):
         scan_forward(qs, packed[..., 16:32].permute(0, 2, 1, 3), packed[..., 32:].permute(0, 2, 1, 3), u)
+
+
+# --------------------------------------------------------------------------
+# vla_scan_backward: argument checks before any launch.
+# --------------------------------------------------------------------------
+def _bwd(lib, p, ws=None, nbytes=0, **ptrs):
+    names = ("q", "k", "v", "u", "A0", "S0", "n0", "g_o", "g_AT", "g_ST", "g_nT",
+             "g_q", "g_k", "g_v", "g_u", "g_A0", "g_S0", "g_n0")
+    base = 0x10000000
+    args = {}
+    for i, n in enumerate(names):   # distinct, non-overlapping fake addresses
+        args[n] = ctypes.c_void_p(base + i * 0x1000000)
+    for n in ("A0", "S0", "n0", "g_AT", "g_ST", "g_nT"):
+        args[n] = None
+    args.update(ptrs)
+    return lib.vla_scan_backward(ctypes.byref(p), *[args[n] for n in names], ws, nbytes, None)
+
+
+def test_backward_workspace_and_supported_set(lib):
+    n = ctypes.c_size_t(0)
+    p = _params(lib, B=2, H=3, T=100, d=64, r=2)
+    assert lib.vla_scan_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value > 0
+    # z (r d) + delta, fire (2r) + alpha_hat (d) + |alpha|, c (2) floats per token at least
+    assert n.value >= 2 * 3 * 100 * (2 * 64 + 4 + 64 + 2) * 4
+    for kw, status in ((dict(d=128), _lib.VLA_EUNSUPPORTED), (dict(update=_lib.VLA_UPDATE_RESIDUAL), _lib.VLA_EUNSUPPORTED),
+                       (dict(stride_b=0, stride_h=64, stride_t=64), _lib.VLA_EUNSUPPORTED), (dict(r=7), _lib.VLA_EUNSUPPORTED)):
+        q = _params(lib, **{**dict(B=2, H=3, T=100, d=64, r=1), **kw})
+        assert lib.vla_scan_backward_workspace_size(ctypes.byref(q), ctypes.byref(n)) == status
+        assert _bwd(lib, q) == status
+
+
+def test_backward_rejects_bad_pointers_and_workspace(lib):
+    p = _params(lib, B=1, H=2, T=10, d=32, r=1)
+    assert _bwd(lib, p, g_o=None) == _lib.VLA_EINVAL
+    assert _bwd(lib, p, g_A0=None) == _lib.VLA_EINVAL
+    assert _bwd(lib, p, g_k=ctypes.c_void_p(0x10000000 + 1 * 0x1000000 + 4)) == _lib.VLA_EINVAL   # g_k inside k
+    assert _bwd(lib, p, g_v=ctypes.c_void_p(0x10000000 + 11 * 0x1000000)) == _lib.VLA_EINVAL      # g_v == g_q
+    assert _bwd(lib, p) == _lib.VLA_EWORKSPACE
+    assert "workspace" in lib.vla_last_error().decode()
