@@ -367,6 +367,44 @@ def extra_measurements(CONFIGS, dev):
             "kernel": "vla_bwd_tape_kernel + vla_bwd_reverse_kernel"}
         del q, k, v, u, x, go
 
+    # Fused prologue: the scan from raw q, k and W_u (features and u built by
+    # the library), against the unfused projection + scan on the same data.
+    from recurrent_inverse_scan_amd import fused_workspace_size, scan_forward_fused
+
+    for name, reps in (("recall", 20), ("long", 3), ("wide", 2)):
+        cfg = CONFIGS[name]
+        x = make_inputs(cfg, seed=0)
+        qr, kr, v, W = x["q_raw"].to(dev), x["k_raw"].to(dev), x["v"].to(dev), x["W_u"].to(dev)
+        q, k = x["q"].to(dev), x["k"].to(dev)
+        B, H, T, d, r = cfg.B, cfg.H, cfg.T, cfg.d, cfg.r
+        o = (torch.empty_like(q), torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d, d), device=dev),
+             torch.empty((B, H, d), device=dev), torch.empty((B, H, 4), device=dev, dtype=torch.int32))
+        fws = fused_workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+        wsf = torch.empty(max(fws, 1), device=dev, dtype=torch.uint8)
+        fn = lambda: scan_forward_fused(qr, kr, v, W, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=o,
+                                        workspace=wsf)
+        ms = _time_ms(fn, reps, warmup=1)
+        u = torch.empty((B, H, T, r, d), device=dev, dtype=q.dtype)
+        ws_bytes = workspace_size(B, H, T, d, r, q.dtype, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap)
+        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+
+        def unfused():
+            project_u(W, kr, out=u)
+            scan_forward(q, k, v, u, nudge_period=cfg.nudge_period, s_cap=cfg.s_cap, out=o, workspace=ws)
+
+        ms_u = _time_ms(unfused, reps, warmup=1)
+        th = B * H * T
+        tfl = 2 * (2 * r + 3) * d * d * th / (ms * 1e-3) / 1e12
+        out[f"fused_{name}"] = {
+            "workload": f"{name}: fused feature map + projection + scan (additive), B={B} H={H} T={T} d={d} r={r}, "
+                        f"{cfg.in_dtype} storage, "
+                        + ("prologue in the scan kernel (u never in HBM)" if fws == 0 else
+                           "prologue pass into the workspace"),
+            "ms": ms, "unfused_projection_plus_scan_ms": ms_u, "tokens_heads_per_s": th / (ms * 1e-3),
+            "alg_tflops": tfl, "valu_frac": tfl / FP32_VECTOR_PEAK_TFLOPS,
+            "kernel": "vla_scan_split_kernel (fused)" if fws == 0 else "feature map + projection + scan"}
+        del qr, kr, v, W, q, k, o, x, ws, wsf, u
+
     # Decode: 4096 chains, one token per call, state carried in place.
     B, H, d, r = 256, 16, 64, 1
     g = torch.Generator(device="cpu").manual_seed(0)

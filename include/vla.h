@@ -6,6 +6,8 @@
  *   vla_scan_forward  the VLA recurrence scan over a sequence, per (batch, head)
  *   vla_scan_step     one token per chain with the state updated in place
  *                     (streaming decode)
+ *   vla_scan_forward_fused  the scan from raw q, k and W_u (feature map and
+ *                     projection fused in)
  *   vla_scan_backward the gradients of the scan (additive update)
  *   vla_project_u     the learned penalty directions u = normalize(W_u k_raw)
  *
@@ -223,6 +225,36 @@ vla_status_t vla_scan_step(const vla_scan_params_t* p,
                            const void* q, const void* k, const void* v, const void* u,
                            float* A, float* S, float* n, void* o, int32_t* stats,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vla_scan_forward_fused: the scan with its prologue fused in: the feature
+ * map and the penalty directions are computed from the raw inputs.
+ *
+ * Source: "Variational Linear Attention (VLA)" README, v3 notes items 1-2
+ * (Q, K = ELU(.) + 1; u_t = normalize(W_u k_t^raw)).  Equivalent to
+ *   q = ELU(q_raw) + 1, k = ELU(k_raw) + 1      (float32, ELU with alpha 1)
+ *   u = normalize(W_u[i] k_raw)                 (vla_project_u)
+ * each stored in in_dtype (bfloat16: round to nearest even), followed by
+ * vla_scan_forward(q, k, v, u, ...) with the same parameters.
+ *
+ * When the call takes the sequential schedule with d <= 64 and more than
+ * 16 tokens, the scan kernel itself streams q_raw, k_raw, v and builds each
+ * token's features and u in LDS on the matrix cores (u never exists in
+ * HBM; no workspace).  Otherwise a prologue pass writes q, k and u into the
+ * workspace and the scan reads them there.
+ *
+ *   q_raw, k_raw, v [B, H, T, d] and W_u [r, d, d] in in_dtype (device,
+ *   contiguous, 16-byte aligned); the rest as in vla_scan_forward.
+ *   workspace: at least vla_scan_fused_workspace_size() bytes.
+ * Strides must be 0 and validate 0 (VLA_EUNSUPPORTED otherwise); every other
+ * error as in vla_scan_forward.
+ */
+vla_status_t vla_scan_fused_workspace_size(const vla_scan_params_t* p, size_t* bytes);
+vla_status_t vla_scan_forward_fused(const vla_scan_params_t* p,
+                                    const void* q_raw, const void* k_raw, const void* v, const void* W_u,
+                                    const float* A0, const float* S0, const float* n0,
+                                    void* o, float* A_T, float* S_T, float* n_T, int32_t* stats,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vla_scan_backward: gradients of the scan with the ADDITIVE update.

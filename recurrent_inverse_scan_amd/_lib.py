@@ -22,7 +22,8 @@ NOALLOC_SCRATCH_BYTES = 256 << 20   # VLA_NOALLOC_SCRATCH_BYTES
 # Every symbol include/vla.h declares.
 EXPORTED = (
     "vla_scan_params_init", "vla_scan_workspace_size", "vla_scan_forward", "vla_scan_forward_noalloc",
-    "vla_scan_step", "vla_scan_backward", "vla_scan_backward_workspace_size", "vla_project_u",
+    "vla_scan_step", "vla_scan_backward", "vla_scan_backward_workspace_size", "vla_scan_forward_fused",
+    "vla_scan_fused_workspace_size", "vla_project_u",
     "vla_status_string", "vla_last_error", "vla_abi_version", "vla_timing_enable", "vla_timing_collect",
 )
 
@@ -80,6 +81,10 @@ def load() -> ctypes.CDLL:
     lib.vla_scan_backward_workspace_size.restype = i32
     lib.vla_scan_backward.argtypes = [P] + [vp] * 19 + [sz, vp]
     lib.vla_scan_backward.restype = i32
+    lib.vla_scan_fused_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.vla_scan_fused_workspace_size.restype = i32
+    lib.vla_scan_forward_fused.argtypes = [P] + [vp] * 13 + [sz, vp]
+    lib.vla_scan_forward_fused.restype = i32
     lib.vla_scan_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.vla_scan_step.restype = i32
     lib.vla_project_u.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp]

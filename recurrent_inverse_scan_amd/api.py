@@ -182,6 +182,65 @@ def scan_forward_noalloc(q, k, v, u, A0=None, S0=None, n0=None, *, out, eps=1e-6
     return o, A_T, S_T, n_T, stats
 
 
+def scan_forward_fused(q_raw, k_raw, v, W_u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0, s_cap=None,
+                       den_eps=1e-6, t0=0, schedule="auto", chunk_len=0, segment_blocks=0, update="additive",
+                       out=None, workspace=None):
+    """Run vla_scan_forward_fused: the scan from the raw inputs, with
+    q, k = ELU(.) + 1 and u = normalize(W_u[i] k_raw) computed by the library.
+
+    q_raw, k_raw, v: [B, H, T, d]; W_u: [r, d, d]; one dtype (float32 or
+    bfloat16), contiguous.  Other arguments and the result as scan_forward."""
+    if q_raw.dim() != 4 or W_u.dim() != 3:
+        raise ValueError("q_raw, k_raw, v must be [B, H, T, d] and W_u [r, d, d]")
+    B, H, T, d = q_raw.shape
+    r = W_u.shape[0]
+    dt = q_raw.dtype
+    if dt not in _DT or any(x.dtype != dt for x in (k_raw, v, W_u)):
+        raise ValueError("q_raw, k_raw, v, W_u must share one dtype: float32 or bfloat16")
+    if k_raw.shape != q_raw.shape or v.shape != q_raw.shape or tuple(W_u.shape) != (r, d, d):
+        raise ValueError("shape mismatch among q_raw, k_raw, v, W_u")
+    if not all(t.is_contiguous() for t in (q_raw, k_raw, v, W_u)):
+        raise ValueError("inputs must be contiguous")
+    dev = q_raw.device
+    for t, shp in ((A0, (B, H, d, d)), (S0, (B, H, d, d)), (n0, (B, H, d))):
+        if t is not None:
+            _check_out(t, shp, torch.float32, dev, "A0/S0/n0")
+    if out is None:
+        out = (torch.empty((B, H, T, d), device=dev, dtype=dt), torch.empty((B, H, d, d), device=dev),
+               torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d), device=dev),
+               torch.empty((B, H, 4), device=dev, dtype=torch.int32))
+    o, A_T, S_T, n_T, stats = out
+    _check_out(o, (B, H, T, d), dt, dev, "o")
+    _check_out(A_T, (B, H, d, d), torch.float32, dev, "A_T")
+    _check_out(S_T, (B, H, d, d), torch.float32, dev, "S_T")
+    _check_out(n_T, (B, H, d), torch.float32, dev, "n_T")
+    if stats is not None:
+        _check_out(stats, (B, H, 4), torch.int32, dev, "stats")
+    _need_cuda(q_raw, k_raw, v, W_u, A0, S0, n0, o, A_T, S_T, n_T, stats, workspace)
+    p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps, t0=t0,
+                    schedule=schedule, chunk_len=chunk_len, segment_blocks=segment_blocks, update=update)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check(lib.vla_scan_fused_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    ws = workspace
+    if nbytes.value and (ws is None or ws.numel() < nbytes.value):
+        ws = torch.empty(nbytes.value, device=dev, dtype=torch.uint8)
+    with torch.cuda.device(dev):
+        _lib.check(lib.vla_scan_forward_fused(
+            ctypes.byref(p), _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(W_u), _ptr(A0), _ptr(S0), _ptr(n0), _ptr(o),
+            _ptr(A_T), _ptr(S_T), _ptr(n_T), _ptr(stats), _ptr(ws) if nbytes.value else None, nbytes.value,
+            _stream_ptr(dev)))
+    return o, A_T, S_T, n_T, stats
+
+
+def fused_workspace_size(B, H, T, d, r, dtype, **kw) -> int:
+    """Bytes of workspace vla_scan_forward_fused needs (0 when the scan kernel runs the prologue)."""
+    p = make_params(B, H, T, d, r, dtype, **kw)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().vla_scan_fused_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
 def scan_step(q, k, v, u, A, S, n, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
               validate=False, update="additive", o=None, stats=None):
     """Run vla_scan_step: one token per chain (q, k, v [B, H, 1, d], u

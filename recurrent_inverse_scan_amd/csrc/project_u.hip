@@ -11,7 +11,8 @@
 // fp32), keeps its k_raw rows in registers across the r directions, and
 // normalises in the epilogue: a row's d outputs live in the 32 lanes of one
 // half-wave (one column each, d/32 tiles), so its sum of squares is a
-// 32-lane reduction.
+// 32-lane reduction; the normalised tile goes through the wave's LDS so that
+// the stores are whole 16-byte pieces of rows.
 //
 // MFMA 32x32 accumulator layout: lane l holds column l % 32 of the tile and,
 // in accumulator slot a, row 8*(a/4) + 4*(l/32) + a%4.  Operand A holds row
@@ -38,9 +39,17 @@ __device__ __forceinline__ float half_wave_sum(float x) {
   return x + __shfl_xor(x, 16, 64);
 }
 
+// LDS row stride (floats) of a wave's 32 x D staging tile.
+template <int D>
+constexpr int stage_ld() { return D + 4; }
+
+// Normalises the wave's 32 rows of direction i and writes them: through the
+// wave's LDS tile, so that each lane stores whole 16-byte pieces of rows
+// instead of one element of each of 16 rows.
 template <int D, typename TOut>
 __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_base, int64_t rows, int r,
-                                            int i, int lane, TOut* u) {
+                                            int i, int lane, TOut* u, float* tile) {
+  constexpr int LD = stage_ld<D>();
   const int col = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
@@ -49,13 +58,31 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_b
     for (int nb = 0; nb < D / 32; ++nb) ss = fmaf(acc[nb][s], acc[nb][s], ss);
     ss = half_wave_sum(ss);
     const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-    const int64_t row = row_base + 8 * (s / 4) + 4 * hi + (s % 4);
-    if (row < rows) {
-      TOut* dst = u + (row * r + i) * D;
+    const int rl = 8 * (s / 4) + 4 * hi + (s % 4);
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) store_out(dst + nb * 32 + col, acc[nb][s] * inv);
-    }
+    for (int nb = 0; nb < D / 32; ++nb) tile[rl * LD + nb * 32 + col] = acc[nb][s] * inv;
   }
+  asm volatile("" ::: "memory");   // one wave's LDS operations complete in order
+  constexpr int EPC = 16 / static_cast<int>(sizeof(TOut));   // elements per 16-byte piece
+  constexpr int PPR = D / EPC;                                // pieces per row
+#pragma unroll
+  for (int c = lane; c < 32 * PPR; c += 64) {
+    const int rl = c / PPR, pc = c % PPR;
+    const int64_t row = row_base + rl;
+    const float* src = tile + rl * LD + pc * EPC;
+    uint4 w;
+    if constexpr (EPC == 4) {
+      w = *reinterpret_cast<const uint4*>(src);
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h[e] = static_cast<uint32_t>(f32_to_bf16(src[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * e + 1])) << 16);
+      w = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    if (row < rows) *reinterpret_cast<uint4*>(u + (row * r + i) * D + pc * EPC) = w;
+  }
+  asm volatile("" ::: "memory");   // the reads finish before the next direction's writes
 }
 
 // bf16 inputs: v_mfma_f32_32x32x16_bf16, 8 bf16 of k per lane per tile.
@@ -64,6 +91,7 @@ __global__ void __launch_bounds__(64 * kProjWaves)
 project_u_bf16_kernel(int64_t rows, int r, const uint16_t* __restrict__ W, const uint16_t* __restrict__ kraw,
                       TOut* __restrict__ u) {
   constexpr int KB = D / 16;
+  __shared__ float tiles[kProjWaves][32 * stage_ld<D>()];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t row_base = (static_cast<int64_t>(blockIdx.x) * kProjWaves + w) * 32;
   const int64_t arow = row_base + (lane & 31);
@@ -88,7 +116,7 @@ project_u_bf16_kernel(int64_t rows, int r, const uint16_t* __restrict__ W, const
         acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b, acc[nb], 0, 0, 0);
       }
     }
-    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u);
+    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u, tiles[w]);
   }
 }
 
@@ -98,6 +126,7 @@ __global__ void __launch_bounds__(64 * kProjWaves)
 project_u_f32_kernel(int64_t rows, int r, const float* __restrict__ W, const float* __restrict__ kraw,
                      TOut* __restrict__ u) {
   constexpr int KB = D / 2;
+  __shared__ float tiles[kProjWaves][32 * stage_ld<D>()];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t row_base = (static_cast<int64_t>(blockIdx.x) * kProjWaves + w) * 32;
   const int64_t arow = row_base + (lane & 31);
@@ -116,7 +145,7 @@ project_u_f32_kernel(int64_t rows, int r, const float* __restrict__ W, const flo
       for (int kb = 0; kb < KB; ++kb)
         acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[kb], wrow[2 * kb], acc[nb], 0, 0, 0);
     }
-    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u);
+    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u, tiles[w]);
   }
 }
 

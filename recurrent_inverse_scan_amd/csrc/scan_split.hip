@@ -23,6 +23,16 @@
 // lds_order() keeps the compiler from moving a load above an earlier store.
 // Stage buffers rotate over three slots: the one being filled, the one the
 // inverse wave reads, the one the state wave reads.
+//
+// Fused prologue (FUSED): the kernel streams q_raw, k_raw and v and builds the
+// rest of each token itself: u_i = normalize(W_u[i] k_raw) ("Variational
+// Linear Attention (VLA)" README, v3 notes item 2) and q, k = ELU(.) + 1
+// (item 1), so u never exists in HBM.  Wave 1, otherwise idle, does it one
+// stage ahead of the inverse wave (a fourth slot): the projection of a
+// stage's 16-token tile on the matrix cores (bf16 storage: 16x16x32 bf16,
+// float32: 16x16x4 f32, accumulating in float32), the row norms by 16-lane
+// sums, then the feature map in place.  Features and u are rounded to the
+// storage dtype, as when they are computed upstream and stored.
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
@@ -33,6 +43,7 @@ namespace vla {
 namespace {
 
 constexpr int kSplitSlots = 3;   // stage buffers in rotation
+constexpr int kFusedSlots = 4;   // with the fused prologue: one more, for wave 1's stage
 constexpr int kSplitThreads = 192;   // inverse wave, spacer wave, state wave
 constexpr int kStageThreads = 128;   // the two working waves stage the rows
 
@@ -40,19 +51,100 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 // Tokens per LDS stage: 16 when the stage fits the staging registers and the
 // three slots stay within 60 KiB, else 8.
+// (NV rows per token in LDS, NL of them loaded from HBM, `slots` buffers;
+// two workgroups still fit a compute unit's 160 KiB with four slots.)
 template <typename TIn, int D>
-__host__ __device__ constexpr int split_stage_tokens(int NV) {
+__host__ __device__ constexpr int split_stage_tokens(int NV, int NL, int slots) {
   const int vpr = D / Elem<TIn>::kPer16B;
-  const int lds16 = static_cast<int>(sizeof(float)) * (kSplitSlots * 16 * NV * D + 2 * 16 * D + D + 8);
-  return (16 * NV * vpr <= kMaxStageVecs * kStageThreads && lds16 <= 60 * 1024) ? 16 : 8;
+  const int lds16 = static_cast<int>(sizeof(float)) * (slots * 16 * NV * D + 2 * 16 * D + D + 8);
+  const int cap = (slots == kFusedSlots ? 78 : 60) * 1024;
+  return (16 * NL * vpr <= kMaxStageVecs * kStageThreads && lds16 <= cap) ? 16 : 8;
 }
 template <typename TIn, int D>
-inline size_t split_lds_bytes(int NV) {
-  const int TT = split_stage_tokens<TIn, D>(NV);
-  return sizeof(float) * (static_cast<size_t>(kSplitSlots) * TT * NV * D + 2 * TT * D + D + 8);
+inline size_t split_lds_bytes(int NV, int NL, int slots) {
+  const int TT = split_stage_tokens<TIn, D>(NV, NL, slots);
+  return sizeof(float) * (static_cast<size_t>(slots) * TT * NV * D + 2 * TT * D + D + 8);
 }
 
-template <typename TIn, int D, int CG, bool RES>
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float round_to(float x, const float*) { return x; }
+__device__ __forceinline__ float round_to(float x, const uint16_t*) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// Wave 1's prologue for one stage (fused mode): slot rows per token are
+// q_raw, k_raw, v, then u_1..u_r to be written; tokens >= TT do not exist.
+// The projection runs on 16-token tiles: lane l is token l % 16 of the A
+// operand and output column l % 16 of the B operand, k slice by l / 16; the
+// accumulator holds rows 4 (l / 16) + s.
+template <typename TIn, int D>
+__device__ __forceinline__ void fused_prologue(float* sb, int NV, int TT, int r, const TIn* __restrict__ W,
+                                               int lane) {
+  const int tok = lane & 15, grp = lane >> 4;
+  constexpr int NB = D / 16 > 0 ? D / 16 : 1;   // 16-column output tiles
+  for (int i = 0; i < r; ++i) {
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const TIn* Wi = W + static_cast<int64_t>(i) * D * D;
+    if constexpr (sizeof(TIn) == 2) {
+      constexpr int KS = (D + 31) / 32;   // 32-wide k steps (d = 16 pads with zeros)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int k0 = 32 * ks + 8 * grp;
+        uint32_t aw[4] = {0u, 0u, 0u, 0u};
+        if (tok < TT && k0 < D) {
+          const float* src = sb + (tok * NV + 1) * D + k0;   // k_raw row: exact bf16 values
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            aw[h] = (__float_as_uint(src[2 * h]) >> 16) | (__float_as_uint(src[2 * h + 1]) & 0xffff0000u);
+        }
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          uint4 bw = make_uint4(0u, 0u, 0u, 0u);
+          if (k0 < D) bw = *reinterpret_cast<const uint4*>(Wi + (nb * 16 + tok) * D + k0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bw), acc[nb], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < D / 4; ++kb) {
+        const int kk = 4 * kb + grp;
+        const float a = tok < TT ? sb[(tok * NV + 1) * D + kk] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Wi[(nb * 16 + tok) * D + kk], acc[nb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float ss = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ss = fmaf(acc[nb][s], acc[nb][s], ss);
+      ss = group_sum<16>(ss);   // the 16 lanes of this row's columns
+      const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+      const int t = 4 * grp + s;
+      if (t < TT) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          if (nb * 16 + tok < D)
+            sb[(t * NV + 3 + i) * D + nb * 16 + tok] = round_to(acc[nb][s] * inv, static_cast<const TIn*>(nullptr));
+      }
+    }
+  }
+  // The projection's reads of k_raw come before the feature map overwrites it
+  // (one wave's LDS operations complete in order).
+  asm volatile("" ::: "memory");
+  for (int e = lane; e < TT * 2 * D; e += 64) {
+    const int t = e / (2 * D), rr = (e / D) & 1, c = e % D;
+    float* p = sb + (t * NV + rr) * D + c;
+    const float x = *p;
+    *p = round_to((x > 0.f ? x : expm1f(x)) + 1.f, static_cast<const TIn*>(nullptr));
+  }
+}
+
+template <typename TIn, int D, int CG, bool RES, bool FUSED>
 __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs a) {
   using L = TileLayout<D, 1, CG>;
   constexpr int R = L::R, C = L::C;
@@ -68,23 +160,26 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   const int row0 = rg * R;
   const int r = a.r;
   const int NV = 3 + r;   // q, k, v, u_1..u_r
+  const int NL = FUSED ? 3 : NV;   // rows per token loaded from HBM
+  constexpr int kSlots = FUSED ? kFusedSlots : kSplitSlots;
+  constexpr int kLag = FUSED ? 1 : 0;   // stages between staging and the inverse wave
   constexpr int row_q = 0, row_k = 1, row_v = 2, row_u = 3;
-  const int TT = split_stage_tokens<TIn, D>(NV);
+  const int TT = split_stage_tokens<TIn, D>(NV, NL, kSlots);
   const int slot_floats = TT * NV * D;
 
-  float* stage = smem;                                   // [3][TT][NV][D]
-  float* ahat = stage + kSplitSlots * slot_floats;       // [2][TT][D]
+  float* stage = smem;                                   // [kSlots][TT][NV][D]
+  float* ahat = stage + kSlots * slot_floats;            // [2][TT][D]
   float* zb = ahat + 2 * TT * D;                   // [D]
   int32_t* fin = reinterpret_cast<int32_t*>(zb + D);     // [8] per-side statistics (exact counts)
 
   const int64_t tok0 = chain * a.T;
   RowSource<TIn, D> src;
-  src.n = NV;
+  src.n = NL;
   src.nfix = 3;
   src.fix0 = static_cast<const TIn*>(a.q) + tok0 * D;
   src.fix1 = static_cast<const TIn*>(a.k) + tok0 * D;
   src.fix2 = static_cast<const TIn*>(a.v) + tok0 * D;
-  src.ubase = static_cast<const TIn*>(a.u) + tok0 * r * D;
+  src.ubase = FUSED ? nullptr : static_cast<const TIn*>(a.u) + tok0 * r * D;
   src.ustride = static_cast<int64_t>(r) * D;
   Stager<TIn, D, kStageThreads> st;
 
@@ -120,18 +215,23 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
   const int nstage = (a.T + TT - 1) / TT;
   if (nstage > 0 && !spacer) {
     st.load(src, 0, TT, a.T, tid);
-    st.store(stage, TT, NV, tid);
+    st.store(stage, TT, NL, tid, NV);
   }
   __syncthreads();
 
-  for (int it = 0; it <= nstage; ++it) {
+  for (int it = 0; it <= nstage + kLag; ++it) {
     if (it + 1 < nstage && !spacer) st.load(src, (it + 1) * TT, TT, a.T, tid);
+    const int si = it - kLag;   // the inverse wave's stage
 
-    if (inverse_side && it < nstage) {
-      // ---- inverse recurrence over stage it ------------------------------
-      const float* sbuf = stage + (it % kSplitSlots) * slot_floats;
-      float* aout = ahat + (it & 1) * TT * D;
-      const int tcount = min(TT, a.T - it * TT);
+    if constexpr (FUSED) {
+      if (spacer && it < nstage)
+        fused_prologue<TIn, D>(stage + (it % kSlots) * slot_floats, NV, TT, r, static_cast<const TIn*>(a.W_u), lane);
+    }
+    if (inverse_side && si >= 0 && si < nstage) {
+      // ---- inverse recurrence over stage si ------------------------------
+      const float* sbuf = stage + (si % kSlots) * slot_floats;
+      float* aout = ahat + (si & 1) * TT * D;
+      const int tcount = min(TT, a.T - si * TT);
       for (int tt = 0; tt < tcount; ++tt) {
         const float* tblk = sbuf + tt * NV * D;
         const float* tk = tblk + row_k * D;
@@ -220,10 +320,10 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
           lds_store_rows<R>(aout + tt * D + row0, alpha);
         }
       }
-    } else if (!inverse_side && !spacer && it >= 1) {
-      // ---- state recurrence over stage it - 1 ----------------------------
-      const int sidx = it - 1;
-      const float* sbuf = stage + (sidx % kSplitSlots) * slot_floats;
+    } else if (!inverse_side && !spacer && si >= 1) {
+      // ---- state recurrence over stage si - 1 ----------------------------
+      const int sidx = si - 1;
+      const float* sbuf = stage + (sidx % kSlots) * slot_floats;
       const float* ain = ahat + (sidx & 1) * TT * D;
       const int tb = sidx * TT;
       const int tcount = min(TT, a.T - tb);
@@ -312,7 +412,7 @@ __global__ void __launch_bounds__(kSplitThreads) vla_scan_split_kernel(ScanArgs 
       }
     }
 
-    if (it + 1 < nstage && !spacer) st.store(stage + ((it + 1) % kSplitSlots) * slot_floats, TT, NV, tid);
+    if (it + 1 < nstage && !spacer) st.store(stage + ((it + 1) % kSlots) * slot_floats, TT, NL, tid, NV);
     __syncthreads();
   }
 
@@ -363,14 +463,22 @@ hipError_t launch_split(const ScanArgs& a, int chains, hipStream_t stream) {
   using L = TileLayout<D, 1, CG>;
   static_assert(L::R >= 1, "layout");
   const int NV = 3 + a.r;
+  const bool fused = a.fused != 0;
+  const int NL = fused ? 3 : NV;
+  const int slots = fused ? kFusedSlots : kSplitSlots;
   // Every stage fits the staging registers of the workgroup.
-  if (8 * NV * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kStageThreads) return hipErrorInvalidValue;
-  const size_t lds = split_lds_bytes<TIn, D>(NV);
+  if (8 * NL * (D / Elem<TIn>::kPer16B) > kMaxStageVecs * kStageThreads) return hipErrorInvalidValue;
+  if (fused && (a.r > 4 || !a.W_u)) return hipErrorInvalidValue;
+  const size_t lds = split_lds_bytes<TIn, D>(NV, NL, slots);
   const dim3 grid(static_cast<unsigned>(chains));
-  if (a.residual)
-    hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, true>), grid, dim3(kSplitThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, false>), grid, dim3(kSplitThreads), lds, stream, a);
+#define VLA_SPLIT(RES_, FUSED_) \
+  hipLaunchKernelGGL((vla_scan_split_kernel<TIn, D, CG, RES_, FUSED_>), grid, dim3(kSplitThreads), lds, stream, a)
+  if (fused) {
+    if (a.residual) VLA_SPLIT(true, true); else VLA_SPLIT(false, true);
+  } else {
+    if (a.residual) VLA_SPLIT(true, false); else VLA_SPLIT(false, false);
+  }
+#undef VLA_SPLIT
   return hipGetLastError();
 }
 
@@ -384,6 +492,11 @@ hipError_t launch_scan_split(const ScanArgs& a, int d, bool bf16, int chains, hi
     case 64: return bf16 ? launch_split<uint16_t, 64, 4>(a, chains, stream) : launch_split<float, 64, 4>(a, chains, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_scan_split_fused(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream) {
+  if (!a.fused) return hipErrorInvalidValue;
+  return launch_scan_split(a, d, bf16, chains, stream);
 }
 
 }  // namespace vla

@@ -49,7 +49,39 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(GatherArgs g) {
   }
 }
 
+// Feature map ELU(x) + 1 (ELU with alpha = 1) of q_raw and k_raw
+// (blockIdx.y = 0, 1) into q and k, in the storage dtype (round to nearest
+// even for bfloat16): "Variational Linear Attention (VLA)" README, v3 notes
+// item 1.
+template <typename T>
+__global__ void __launch_bounds__(256) feature_map_kernel(const T* __restrict__ q_raw, const T* __restrict__ k_raw,
+                                                          T* __restrict__ q, T* __restrict__ k, int64_t n) {
+  const T* src = blockIdx.y == 0 ? q_raw : k_raw;
+  T* dst = blockIdx.y == 0 ? q : k;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float x = Elem<T>::load(src + i);
+    Elem<T>::store(dst + i, (x > 0.f ? x : expm1f(x)) + 1.f);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_feature_map(const void* q_raw, const void* k_raw, void* q, void* k, int64_t n, bool bf16,
+                              hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 8192 ? want : 8192);
+  if (bf16)
+    hipLaunchKernelGGL(feature_map_kernel<uint16_t>, dim3(grid, 2), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q_raw), static_cast<const uint16_t*>(k_raw),
+                       static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), n);
+  else
+    hipLaunchKernelGGL(feature_map_kernel<float>, dim3(grid, 2), dim3(256), 0, stream,
+                       static_cast<const float*>(q_raw), static_cast<const float*>(k_raw), static_cast<float*>(q),
+                       static_cast<float*>(k), n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t stream) {
   const int64_t nvec = g.rows * (g.row_bytes / 16);

@@ -826,6 +826,125 @@ vla_status_t vla_scan_backward(const vla_scan_params_t* p, const void* q, const 
   return VLA_OK;
 }
 
+namespace {
+// The fused entry point runs the prologue inside the two-wave sequential
+// kernel when the call takes it (d <= 64, more than 16 tokens, sequential
+// schedule); otherwise a prologue pass writes the features and u into the
+// workspace first.
+bool fused_in_kernel(const vla_scan_params_t* p) { return !plan_schedule(p).use && p->d <= 64 && p->T > 16; }
+
+size_t fused_prologue_bytes(const vla_scan_params_t* p) {
+  const size_t n = static_cast<size_t>(p->B) * p->H * p->T * p->d * dtype_size(p->in_dtype);
+  return align_up(n) * 2 + align_up(n * p->r);
+}
+
+vla_status_t check_fused(const vla_scan_params_t* p) {
+  const vla_status_t s = check_params(p);
+  if (s != VLA_OK) return s;
+  if (strided(p)) return fail(VLA_EUNSUPPORTED, "vla_scan_forward_fused takes contiguous inputs (strides 0)");
+  if (p->validate) return fail(VLA_EUNSUPPORTED, "vla_scan_forward_fused has no validation pre-pass");
+  return VLA_OK;
+}
+}  // namespace
+
+vla_status_t vla_scan_fused_workspace_size(const vla_scan_params_t* p, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(VLA_EINVAL, "bytes is NULL");
+  const vla_status_t s = check_fused(p);
+  if (s != VLA_OK) return s;
+  size_t need = 0;
+  const vla_status_t s2 = vla_scan_workspace_size(p, &need);
+  if (s2 != VLA_OK) return s2;
+  *bytes = fused_in_kernel(p) ? need : fused_prologue_bytes(p) + need;
+  return VLA_OK;
+}
+
+vla_status_t vla_scan_forward_fused(const vla_scan_params_t* p, const void* q_raw, const void* k_raw, const void* v,
+                                    const void* W_u, const float* A0, const float* S0, const float* n0, void* o,
+                                    float* A_T, float* S_T, float* n_T, int32_t* stats, void* workspace,
+                                    size_t workspace_bytes, void* stream_ptr) {
+  g_last_error.clear();
+  vla_status_t s = check_fused(p);
+  if (s != VLA_OK) return s;
+  const int64_t chains = static_cast<int64_t>(p->B) * p->H;
+  if (chains == 0) return VLA_OK;
+  const int d = p->d, r = p->r;
+  const size_t es = dtype_size(p->in_dtype);
+  const size_t n_tok = static_cast<size_t>(chains) * static_cast<size_t>(p->T);
+  const size_t b_seq = n_tok * d * es, b_w = static_cast<size_t>(r) * d * d * es;
+  const size_t b_mat = static_cast<size_t>(chains) * d * d * 4, b_vec = static_cast<size_t>(chains) * d * 4;
+  if (n_tok > 0 && (!q_raw || !k_raw || !v || !W_u || !o))
+    return fail(VLA_EINVAL, "q_raw, k_raw, v, W_u and o must be non-NULL");
+  if (!A_T || !S_T || !n_T) return fail(VLA_EINVAL, "A_T, S_T and n_T must be non-NULL");
+  const void* seq[5] = {q_raw, k_raw, v, W_u, o};
+  for (const void* x : seq)
+    if (n_tok > 0 && !aligned(x, 16)) return fail(VLA_EINVAL, "q_raw, k_raw, v, W_u, o must be 16-byte aligned");
+  if (!aligned(A0, 16) || !aligned(S0, 16) || !aligned(A_T, 16) || !aligned(S_T, 16) || !aligned(n0, 4) ||
+      !aligned(n_T, 4))
+    return fail(VLA_EINVAL, "state tensors misaligned (A, S: 16 bytes; n: 4 bytes)");
+  const struct { const void* p; size_t n; } ins[] = {{q_raw, b_seq}, {k_raw, b_seq}, {v, b_seq}, {W_u, b_w}};
+  const struct { const void* p; size_t n; const void* own; } outs[] = {
+      {o, b_seq, nullptr}, {A_T, b_mat, A0}, {S_T, b_mat, S0}, {n_T, b_vec, n0},
+      {stats, static_cast<size_t>(chains) * 16, nullptr}};
+  const int n_outs = static_cast<int>(sizeof(outs) / sizeof(outs[0]));
+  for (int oi = 0; oi < n_outs; ++oi) {
+    const auto& ot = outs[oi];
+    if (!ot.p) continue;
+    for (const auto& in : ins)
+      if (bad_alias(ot.p, ot.n, in.p, in.n, false)) return fail(VLA_EINVAL, "an output overlaps q_raw, k_raw, v or W_u");
+    const struct { const void* p; size_t n; } st[] = {{A0, b_mat}, {S0, b_mat}, {n0, b_vec}};
+    for (const auto& sx : st)
+      if (bad_alias(ot.p, ot.n, sx.p, sx.n, ot.own == sx.p)) return fail(VLA_EINVAL, "outputs overlap the state");
+    for (int oj = oi + 1; oj < n_outs; ++oj)
+      if (overlap(ot.p, ot.n, outs[oj].p, outs[oj].n)) return fail(VLA_EINVAL, "outputs overlap each other");
+  }
+  size_t need = 0;
+  if ((s = vla_scan_fused_workspace_size(p, &need)) != VLA_OK) return s;
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned(workspace, kAlign))))
+    return fail(VLA_EWORKSPACE, "workspace of %zu bytes (256-byte aligned) needed (got %zu)", need, workspace_bytes);
+  if (need > 0) {
+    for (const auto& in : ins)
+      if (overlap(workspace, need, in.p, in.n)) return fail(VLA_EINVAL, "workspace overlaps an input");
+    for (const auto& ot : outs)
+      if (overlap(workspace, need, ot.p, ot.n)) return fail(VLA_EINVAL, "workspace overlaps an output");
+    const struct { const void* p; size_t n; } st[] = {{A0, b_mat}, {S0, b_mat}, {n0, b_vec}};
+    for (const auto& sx : st)
+      if (overlap(workspace, need, sx.p, sx.n)) return fail(VLA_EINVAL, "workspace overlaps the state");
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const bool bf16 = p->in_dtype == VLA_BF16;
+  if (!fused_in_kernel(p)) {
+    // Prologue pass: q, k features and u into the workspace, then the scan.
+    char* ws = static_cast<char*>(workspace);
+    void* qf = ws;
+    void* kf = ws + align_up(b_seq);
+    void* uf = ws + 2 * align_up(b_seq);
+    const size_t pro = fused_prologue_bytes(p);
+    hipError_t e = vla::launch_feature_map(q_raw, k_raw, qf, kf, static_cast<int64_t>(n_tok) * d, bf16, stream);
+    if (e == hipSuccess && n_tok > 0)
+      e = vla::launch_project_u(static_cast<int64_t>(n_tok), d, r, bf16, bf16, W_u, k_raw, uf, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused prologue launch");
+    return vla_scan_forward(p, qf, kf, v, uf, A0, S0, n0, o, A_T, S_T, n_T, stats,
+                            need > pro ? ws + pro : nullptr, need - pro, stream_ptr);
+  }
+  vla::ScanArgs a{};
+  a.q = q_raw; a.k = k_raw; a.v = v; a.u = nullptr;
+  a.A0 = A0; a.S0 = S0; a.n0 = n0;
+  a.o = o; a.A_T = A_T; a.S_T = S_T; a.n_T = n_T; a.stats = stats;
+  a.T = p->T; a.r = r; a.eps = p->eps;
+  a.nudge_period = p->nudge_period;
+  a.nudge_phase0 = p->nudge_period > 0 ? static_cast<int32_t>((p->t0 + 1) % p->nudge_period) : 0;
+  a.cap_on = (p->s_cap > 0.f && std::isfinite(p->s_cap)) ? 1 : 0;
+  a.cap = a.cap_on ? p->s_cap : 0.f;
+  a.den_eps = p->den_eps;
+  a.residual = p->update == VLA_UPDATE_RESIDUAL ? 1 : 0;
+  a.fused = 1;
+  a.W_u = W_u;
+  const hipError_t e = vla::launch_scan_split_fused(a, d, bf16, static_cast<int>(chains), stream);
+  if (e != hipSuccess) return hip_fail(e, "fused scan launch");
+  return VLA_OK;
+}
+
 vla_status_t vla_scan_forward_noalloc(const vla_scan_params_t* p, const void* q, const void* k, const void* v,
                                       const void* u, const float* A0, const float* S0, const float* n0, void* o,
                                       float* A_T, float* S_T, float* n_T, int32_t* stats, void* stream_ptr) {

@@ -28,7 +28,15 @@ struct ScanArgs {
   int32_t cap_on;
   float den_eps;
   int32_t residual;       // nonzero: residual (delta-rule) state update; full recurrence only
+  // Fused prologue (two-wave kernel only): q and k hold the raw inputs, the
+  // kernel applies ELU+1 to them and projects u = normalize(W_u[i] k_raw)
+  // itself; u is unused.  Features and u are rounded to the storage dtype.
+  int32_t fused;
+  const void* W_u;        // [r][d][d] in the storage dtype
 };
+
+// Sequential scan with the fused prologue (d <= 64, the two-wave kernel).
+hipError_t launch_scan_split_fused(const ScanArgs& a, int d, bool bf16, int chains, hipStream_t stream);
 
 // Whole recurrence, one workgroup per chain.  only_if (nullable) restricts
 // the run to chains whose flag is nonzero.
@@ -141,6 +149,10 @@ struct GatherArgs {
   int32_t row_bytes;     // d * elem_bytes, a multiple of 16
 };
 hipError_t launch_gather_rows(const GatherArgs& g, hipStream_t stream);
+
+// q = ELU(q_raw) + 1 and k = ELU(k_raw) + 1 over n elements each, in the storage dtype.
+hipError_t launch_feature_map(const void* q_raw, const void* k_raw, void* q, void* k, int64_t n, bool bf16,
+                              hipStream_t stream);
 
 // Backward pass (backward.hip): inputs, cotangents, gradients and the tape.
 struct BwdArgs {

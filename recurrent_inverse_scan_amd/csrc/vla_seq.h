@@ -145,14 +145,19 @@ struct Stager {
     }
   }
 
-  __device__ __forceinline__ void store(float* stage, int TT, int n, int tid) const {
+  // Rows land at stage + (token * rows_per_token + row) * D; rows_per_token
+  // defaults to n (the rows loaded per token) and may be larger, leaving the
+  // remaining rows of each token for the caller to fill.
+  __device__ __forceinline__ void store(float* stage, int TT, int n, int tid, int rows_per_token = 0) const {
     const int nvec = TT * n * VPR;
+    const int rpt = rows_per_token > 0 ? rows_per_token : n;
 #pragma unroll
     for (int j = 0; j < kMaxStageVecs; ++j) {
       const int e = tid + j * NTH;
       if (e < nvec) {
         const int rho = e / VPR, c = e % VPR;
-        float* dst = stage + rho * D + c * EPV;
+        const int orow = rpt == n ? rho : (rho / n) * rpt + rho % n;
+        float* dst = stage + orow * D + c * EPV;
         if constexpr (EPV == 4) {
           *reinterpret_cast<uint4*>(dst) = reg[j];
         } else {

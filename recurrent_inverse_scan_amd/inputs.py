@@ -75,7 +75,7 @@ def _feature(x: torch.Tensor) -> torch.Tensor:
 def make_inputs(cfg: ScanConfig, seed: int = 0):
     """Return a dict of CPU tensors in the storage dtype.
 
-    Keys: q, k, v [B, H, T, d]; k_raw [B, H, T, d]; W_u [r, d, d].
+    Keys: q, k, v [B, H, T, d]; q_raw, k_raw [B, H, T, d]; W_u [r, d, d].
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
@@ -86,7 +86,6 @@ def make_inputs(cfg: ScanConfig, seed: int = 0):
         k_raw = torch.randn(shape, generator=g, dtype=torch.float32)
         v = torch.randn(shape, generator=g, dtype=torch.float32)
         q = _feature(q_raw)
-        del q_raw
     elif cfg.kind == "recall":
         npool = 24
         q_raw = torch.randn(shape, generator=g, dtype=torch.float32)
@@ -103,7 +102,6 @@ def make_inputs(cfg: ScanConfig, seed: int = 0):
         v = gather(vals, idx)
         q_raw[:, :, T - nq:, :] = gather(pool, qidx) + qnoise
         q = _feature(q_raw)
-        del q_raw
     else:
         raise ValueError(f"unknown workload kind {cfg.kind!r}")
     W_u = torch.randn((r, d, d), generator=g, dtype=torch.float32) / math.sqrt(d)
@@ -113,6 +111,7 @@ def make_inputs(cfg: ScanConfig, seed: int = 0):
         "q": q.to(dt).contiguous(),
         "k": k.to(dt).contiguous(),
         "v": v.to(dt).contiguous(),
+        "q_raw": q_raw.to(dt).contiguous(),
         "k_raw": k_raw.to(dt).contiguous(),
         "W_u": W_u.to(dt).contiguous(),
     }
