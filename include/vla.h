@@ -104,12 +104,18 @@ typedef struct {
                              and reads out the last); 0 = library picks (256),
                              < 0 = one segment */
   int32_t update;        /* vla_update_t (both schedules) */
+  int32_t para_segments; /* chunked schedule, additive update: the per-chain state
+                            pass cut into this many segments (2..16) that run in
+                            parallel from guessed starts, corrected by sweeps
+                            until the starts stop moving; 1 = one pass per chain
+                            (the segmented pipeline above); 0 = library picks
+                            (min(16, 256 / chains), at least 2 blocks per segment) */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
  * den_eps = 1e-6, t0 = 0, contiguous q, k, v (strides 0), automatic schedule,
- * no validation, chunk_len = 0, segment_blocks = 0, additive update.  Host
- * pointer. */
+ * no validation, chunk_len = 0, segment_blocks = 0, additive update,
+ * para_segments = 0.  Host pointer. */
 void vla_scan_params_init(vla_scan_params_t* p);
 
 /* Bytes of device workspace vla_scan_forward needs for these parameters

@@ -46,6 +46,7 @@ class ScanParams(ctypes.Structure):
         ("chunk_len", ctypes.c_int32),
         ("segment_blocks", ctypes.c_int32),
         ("update", ctypes.c_int32),
+        ("para_segments", ctypes.c_int32),
     ]
 
 

@@ -50,7 +50,7 @@ def _check_out(t, shape, dtype, dev, name):
 
 def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, den_eps=1e-6, t0=0,
                 schedule="auto", validate=False, chunk_len=0, segment_blocks=0,
-                update="additive", strides=(0, 0, 0)) -> _lib.ScanParams:
+                update="additive", strides=(0, 0, 0), para_segments=0) -> _lib.ScanParams:
     p = _lib.ScanParams()
     _lib.load().vla_scan_params_init(ctypes.byref(p))
     p.B, p.H, p.T, p.d, p.r = B, H, T, d, r
@@ -67,12 +67,13 @@ def make_params(B, H, T, d, r, dtype, *, eps=1e-6, nudge_period=0, s_cap=None, d
     p.chunk_len = chunk_len
     p.segment_blocks = segment_blocks
     p.update = {"additive": _lib.VLA_UPDATE_ADDITIVE, "residual": _lib.VLA_UPDATE_RESIDUAL}[update]
+    p.para_segments = para_segments
     return p
 
 
 def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_period=0, s_cap=None,
                  den_eps=1e-6, t0=0, schedule="auto", validate=False, chunk_len=0, segment_blocks=0, out=None,
-                 workspace=None, update="additive"):
+                 workspace=None, update="additive", para_segments=0):
     """Run vla_scan_forward.
 
     q, k, v: [B, H, T, d]; u: [B, H, T, r, d], all float32 or all bfloat16 on
@@ -83,8 +84,10 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     ``schedule`` is "auto", "sequential" or "chunked"; ``chunk_len`` 0 lets
     the library pick; ``segment_blocks`` (chunked schedule) sets the blocks of
     64 tokens per state-pass segment, 0 lets the library pick and -1 keeps one
-    segment.  ``update`` is "additive" or "residual" (the delta-rule state
-    step; both schedules).  ``out`` may pass preallocated (o, A_T, S_T, n_T,
+    segment.  ``para_segments`` (chunked schedule, additive update) cuts each
+    chain's state pass into that many segments iterated in parallel (2..16),
+    1 keeps one pass per chain, 0 lets the library pick.  ``update`` is
+    "additive" or "residual" (the delta-rule state step; both schedules).  ``out`` may pass preallocated (o, A_T, S_T, n_T,
     stats) tensors and ``workspace`` a preallocated uint8 device buffer of at
     least ``workspace_size(...)`` bytes.  Returns (o, A_T, S_T, n_T, stats).
     """
@@ -126,7 +129,7 @@ def scan_forward(q, k, v, u, A0=None, S0=None, n0=None, *, eps=1e-6, nudge_perio
     _need_cuda(q, k, v, u, A0, S0, n0, o, A_T, S_T, n_T, stats, workspace)
     p = make_params(B, H, T, d, r, dt, eps=eps, nudge_period=nudge_period, s_cap=s_cap, den_eps=den_eps,
                     t0=t0, schedule=schedule, validate=validate, chunk_len=chunk_len,
-                    segment_blocks=segment_blocks, update=update, strides=strides)
+                    segment_blocks=segment_blocks, update=update, strides=strides, para_segments=para_segments)
     lib = _lib.load()
     ws_bytes = ctypes.c_size_t(0)
     _lib.check(lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))

@@ -180,6 +180,50 @@ __device__ __forceinline__ void stage_rows(T* lds, const T* g, int nvalid, int t
   }
 }
 
+// A [64][64] tile in 16-byte pieces held in registers: thread tid holds
+// pieces tid + 256 j.  Loading every tile a block needs before storing any of
+// them to LDS puts all their global-memory latencies in one round.
+template <typename T>
+struct TileRegs {
+  static constexpr int EPV = 16 / static_cast<int>(sizeof(T));   // elements per piece
+  static constexpr int PPR = kD / EPV;                           // pieces per row
+  static constexpr int N = kLb * PPR / kThreads;                 // pieces per thread
+  uint4 r[N];
+  // Rows [0, nvalid) of the tile at g (rows of 64); later rows read as zero.
+  __device__ __forceinline__ void load(const T* g, int nvalid, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int e = tid + j * kThreads, row = e / PPR, c = (e % PPR) * EPV;
+      r[j] = row < nvalid ? *reinterpret_cast<const uint4*>(g + row * kD + c) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // As stored, rows of the given stride (elements of T).
+  __device__ __forceinline__ void store_rows(T* lds, int stride, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int e = tid + j * kThreads, row = e / PPR, c = (e % PPR) * EPV;
+      *reinterpret_cast<uint4*>(lds + row * stride + c) = r[j];
+    }
+  }
+  // Widened to float32 rows of stride kLd.
+  __device__ __forceinline__ void store_f32(float* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int e = tid + j * kThreads, row = e / PPR, c = (e % PPR) * EPV;
+      float* dst = lds + row * kLd + c;
+      if constexpr (EPV == 4) {
+        *reinterpret_cast<uint4*>(dst) = r[j];
+      } else {
+        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+        *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                                      __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                                          __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+      }
+    }
+  }
+};
+
 template <typename TIn>
 __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __restrict__ q, const TIn* __restrict__ k,
                                            const TIn* __restrict__ v, int b_lo, int nb, int64_t item) {
@@ -198,13 +242,25 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = b * kLb, tcount = min(kLb, pl.T - tb);
   const int64_t row0 = chain * pl.T + tb;
-  stage_rows<TIn>(Vb, v + row0 * kD, tcount, tid, kRd);
-  stage_rows<TIn>(Qb, q + row0 * kD, tcount, tid, kRd);
-  stage_rows<TIn>(Kb, k + row0 * kD, tcount, tid, kRd);
-  stage_block<float>(Af, pl.alpha + row0 * kD, tcount, tid);
-  if (b > 0) {   // uniform; the previous block is always full
-    stage_rows<TIn>(Vp, v + (row0 - kLb) * kD, kLb, tid, kRd);
-    stage_block<float>(Ap, pl.alpha + (row0 - kLb) * kD, kLb, tid);
+  {
+    TileRegs<TIn> rv, rq, rk, rvp;
+    TileRegs<float> ra, rap;
+    rv.load(v + row0 * kD, tcount, tid);
+    rq.load(q + row0 * kD, tcount, tid);
+    rk.load(k + row0 * kD, tcount, tid);
+    ra.load(pl.alpha + row0 * kD, tcount, tid);
+    if (b > 0) {   // uniform; the previous block is always full
+      rvp.load(v + (row0 - kLb) * kD, kLb, tid);
+      rap.load(pl.alpha + (row0 - kLb) * kD, kLb, tid);
+    }
+    rv.store_rows(Vb, kRd, tid);
+    rq.store_rows(Qb, kRd, tid);
+    rk.store_rows(Kb, kRd, tid);
+    ra.store_f32(Af, tid);
+    if (b > 0) {
+      rvp.store_rows(Vp, kRd, tid);
+      rap.store_f32(Ap, tid);
+    }
   }
   __syncthreads();
 
@@ -224,13 +280,15 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
     }
   }
   float* pack = pl.Kmat + blk * kPackFloats;
-  if (tid < kLb) {
+  __shared__ float ksum_part[4][kLb];   // key sums over 16-token quarters of the block
+  {
+    const int f = tid & 63, qt = tid >> 6;
     float acc = 0.f;
-    for (int t = 0; t < tcount; ++t) acc += Elem<TIn>::load(Kb + t * kRd + tid);
-    pack[kPackKs + tid] = acc;
-  } else if (tid < kLb + (kPackFloats - kPackKs - kLb)) {
-    pack[kPackKs + tid] = 0.f;   // padding
+#pragma unroll
+    for (int t = 16 * qt; t < 16 * qt + 16; ++t) acc += Elem<TIn>::load(Kb + t * kRd + f);   // rows >= tcount are 0
+    ksum_part[qt][f] = acc;
   }
+  if (tid >= kLb && tid < kLb + (kPackFloats - kPackKs - kLb)) pack[kPackKs + tid] = 0.f;   // padding
   // Matrix-core operands of the chain kernel's update for fp32 storage
   // (features of v and alpha_hat are LDS columns here); with bf16 storage the
   // chain kernel reads them from its own LDS rows.
@@ -264,23 +322,24 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
     Af[t * kLd + col] = gv[s] * ga[s];
   }
   __syncthreads();
-  if (tid < kLb) {
-    // Row t of K -> exclusive prefix sums in place.
-    const int t = tid;
-    float run = 0.f, e_t = 0.f;
-    for (int s = 0; s < kLb; ++s) {
-      const float x = Af[t * kLd + s];
-      e_t = (s == t) ? x : e_t;
-      Af[t * kLd + s] = run;
-      run += x;
+  // Rows of K: exclusive prefix sums in place, K(t,t) and the row totals; rows
+  // of the masked q.k products: their sums.  Wave w takes rows 16 w .. 16 w + 15,
+  // lane s column s, with DPP scans.
+  if (tid < kLb) pack[kPackKs + tid] = (ksum_part[0][tid] + ksum_part[1][tid]) + (ksum_part[2][tid] + ksum_part[3][tid]);
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int t = w * 16 + rr;   // wave-uniform
+    const float x = Af[t * kLd + lane];
+    const float inc = wave_incl_scan(x, lane);
+    Af[t * kLd + lane] = inc - x;
+    const float tot = readlane_f(inc, kLb - 1);
+    const float e_t = readlane_f(x, t);
+    const float ldt = wave_sum(Ap[t * kLd + lane]);
+    if (lane == 0) {
+      pack[kPackE + t] = e_t;
+      pack[kPackTot + t] = tot;
+      if (t < tcount) pl.ld[row0 + t] = ldt;
     }
-    pack[kPackE + t] = e_t;
-    pack[kPackTot + t] = run;
-  } else if (tid < 2 * kLb) {
-    const int t = tid - kLb;
-    float acc = 0.f;
-    for (int s = 0; s < kLb; ++s) acc += Ap[t * kLd + s];
-    if (t < tcount) pl.ld[row0 + t] = acc;
   }
   __syncthreads();
   for (int e = tid; e < kTriN; e += kThreads) {   // the triangle, row t at t(t+1)/2
@@ -551,7 +610,16 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   auto rows_ar = [&](int r) -> float4* { return r == 0 ? sAR0 : (r == 1 ? sAR1 : (r == 2 ? sAR2 : sAR3)); };
   auto rows_vr = [&](int r) -> float4* { return r == 0 ? sVR0 : (r == 1 ? sVR1 : (r == 2 ? sVR2 : sVR3)); };
 
-  const int64_t chain = blockIdx.x;
+  // Parallel-in-time mode: this workgroup's chain and segment.
+  const int nchains = sg.pr ? static_cast<int>(gridDim.x) / sg.nseg : static_cast<int>(gridDim.x);
+  const int seg = sg.pr ? static_cast<int>(blockIdx.x) / nchains : 0;
+  const int64_t chain = sg.pr ? static_cast<int64_t>(blockIdx.x) % nchains : static_cast<int64_t>(blockIdx.x);
+  if (sg.pr && sg.conv && sg.conv[chain]) return;   // uniform: its segment starts have converged
+  const int64_t pidx = chain * sg.nseg + seg;        // (chain, segment) record index
+  if (sg.pr && sg.active && !sg.active[pidx]) return;   // uniform: this segment's start has not moved
+  // The first pass of the parallel-in-time schedule runs segments >= 1 from
+  // S = 0 without the cap: it yields their plain sums of v alpha_hat^T.
+  cap_on = (sg.pr && sg.uncapped_tail && seg > 0) ? 0 : cap_on;
   // The wave index is uniform; saying so keeps LDS destinations and buffer
   // descriptors derived from it in scalar registers.
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
@@ -563,7 +631,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   const float cap2 = cap * cap;
   const int nblk = pl.nblk;
   const int64_t blk0 = chain * nblk;
-  const int b_lo = sg.b_lo, b_hi = sg.b_hi;
+  const int b_lo = sg.pr ? sg.bnd[seg] : sg.b_lo, b_hi = sg.pr ? sg.bnd[seg + 1] : sg.b_hi;
 
   // Buffer-to-LDS copies: this wave takes pieces m, m+4, ...; vo32 / vo16
   // are a lane's source offsets within a piece (fp32 / bf16 rows).
@@ -609,19 +677,19 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   UpdFrags<TIn> fr;
   UpdOffsets uoff;   // loop-invariant LDS offsets of the update's column reads
   uoff.init(ti, tj, lane);
-  float nvec = 0.f, N = 0.f, Nstart = 0.f;
+  float nvec = 0.f, N = 0.f, Nstart = 0.f, lsum = 0.f;
   int fires = 0, first = -1;
   bool bad = false;
 
   // ---- prologue: continue from S and n at block b_lo -------------------------
   if (rwave) {
-    nvec = sg.n_in[chain * sg.n_in_stride + lane];
-    if (b_lo > 0) {
+    nvec = sg.pr ? sg.n_in[pidx * kD + lane] : sg.n_in[chain * sg.n_in_stride + lane];
+    if (b_lo > 0 && !sg.pr) {
       fires = sg.counters[chain * 2];
       first = sg.counters[chain * 2 + 1];
     }
   } else {
-    const float* s0 = sg.S_in + chain * sg.S_in_stride;
+    const float* s0 = sg.pr ? sg.S_in + pidx * kD * kD : sg.S_in + chain * sg.S_in_stride;
     float part = 0.f;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
@@ -725,6 +793,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         ++fires;
         s0 = f + 1;
       }
+      lsum += L;
       sW[g][t] = (t < tcount) ? exp2f(L - lprev_t) : 0.f;
       if (t == 0) sSig[g] = exp2f(L);
       {
@@ -791,7 +860,17 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
     } else {
       rank_update<TIn>(X, fr, sW[g], sSig[g], h);
     }
-    if (sg.last) {
+    if (sg.pr) {
+      // S at the segment's end, for the sweep; the last segment's is S_T.
+      float* fo = sg.F + pidx * kD * kD;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) fo[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
+      if (seg + 1 == sg.nseg) {
+        float* st = S_T + chain * kD * kD;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
+      }
+    } else if (sg.last) {
       float* st = S_T + chain * kD * kD;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
@@ -804,6 +883,15 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 #pragma unroll
       for (int s = 0; s < 16; ++s) st[(ti * 32 + acc_row(s, h)) * kD + col] = X[s];
     }
+  } else if (sg.pr) {
+    if (seg + 1 == sg.nseg) n_T[chain * kD + lane] = nvec;
+    if (lane == 0) {
+      float* rc = sg.rec + pidx * 4;
+      rc[0] = lsum;
+      rc[1] = static_cast<float>(fires);
+      rc[2] = static_cast<float>(first);
+      rc[3] = 0.f;
+    }
   } else if (sg.last) {
     n_T[chain * kD + lane] = nvec;
     bad |= !isfinite(nvec);
@@ -814,7 +902,7 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
       sg.counters[chain * 2 + 1] = first;
     }
   }
-  if (!sg.last) return;   // uniform
+  if (!sg.last || sg.pr) return;   // uniform
   const bool wave_bad = __any(bad);
   if (lane == 0) sRed[w] = wave_bad ? 1.f : 0.f;
   __syncthreads();
@@ -867,29 +955,36 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   const int64_t blk = chain * pl.nblk + b;
   constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));   // elements per 16 bytes
   {
-    // q rows and v^T (v is read as rows and written transposed).
-    const TIn* qg = q + row0 * kD;
-    const TIn* vg = static_cast<const TIn*>(pl.v) + row0 * kD;
-    for (int e = tid; e < kLb * kD / EPV; e += kThreads) {
-      const int r = e / (kD / EPV), c = (e % (kD / EPV)) * EPV;
-      uint4 xq = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-      if (r < tcount) {
-        xq = *reinterpret_cast<const uint4*>(qg + r * kD + c);
-        xv = *reinterpret_cast<const uint4*>(vg + r * kD + c);
-      }
-      *reinterpret_cast<uint4*>(Qs + r * kQd + c) = xq;
-      const TIn* xe = reinterpret_cast<const TIn*>(&xv);
+    // Every global load of the block first, then the LDS stores: q rows,
+    // v^T (v is read as rows and written transposed), S_b, alpha_hat rows.
+    TileRegs<TIn> rq, rv;
+    TileRegs<float> rx, ra;
+    rq.load(q + row0 * kD, tcount, tid);
+    rv.load(static_cast<const TIn*>(pl.v) + row0 * kD, tcount, tid);
+    rx.load(pl.Xsnap + blk * kD * kD, kD, tid);
+    ra.load(pl.alpha + row0 * kD, tcount, tid);
+    float w0 = 0.f, w1 = 0.f, nb0 = 0.f;
+    if (tid < kLb) {
+      const bool ok = tid < tcount;
+      w0 = ok ? pl.wsig[2 * (row0 + tid)] : 0.f;
+      w1 = ok ? pl.wsig[2 * (row0 + tid) + 1] : 0.f;
+      nb0 = pl.nblock[blk * kD + tid];
+    }
+    rq.store_rows(Qs, kQd, tid);
+#pragma unroll
+    for (int j = 0; j < TileRegs<TIn>::N; ++j) {
+      const int e = tid + j * kThreads, r = e / TileRegs<TIn>::PPR, c = (e % TileRegs<TIn>::PPR) * EPV;
+      const TIn* xe = reinterpret_cast<const TIn*>(&rv.r[j]);
 #pragma unroll
       for (int k = 0; k < EPV; ++k) Vt[(c + k) * kQd + r] = xe[k];
     }
-    stage_block<float>(Xs, pl.Xsnap + blk * kD * kD, kD, tid);
-    stage_block<float>(As, pl.alpha + row0 * kD, tcount, tid);
-  }
-  if (tid < kLb) {
-    const bool ok = tid < tcount;
-    wl[tid] = ok ? pl.wsig[2 * (row0 + tid)] : 0.f;
-    sl[tid] = ok ? pl.wsig[2 * (row0 + tid) + 1] : 0.f;
-    nl[tid] = pl.nblock[blk * kD + tid];
+    rx.store_f32(Xs, tid);
+    ra.store_f32(As, tid);
+    if (tid < kLb) {
+      wl[tid] = w0;
+      sl[tid] = w1;
+      nl[tid] = nb0;
+    }
   }
   __syncthreads();
   if (tid < kLb) {
@@ -962,6 +1057,218 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
 
 }  // namespace
 
+// ---- parallel-in-time state pass: initial segment starts, the sweep, stats ----
+// The state recurrence over a segment of blocks is a map of its starting S
+// (the cap makes it nonlinear, but only through the per-token scales).  All
+// segments of all chains run at once from guessed starts (the chain kernel in
+// parallel-in-time mode); a sweep per chain then corrects the guesses in
+// segment order with a cheap linear model of each segment's map around its
+// last pass and the pass's exact end state (a parareal iteration):
+//     S'_{j+1} = F_j(S_j) + G_j(S'_j - S_j).
+// Once the cap binds, |S| stays at the cap, so a change of the start along S
+// is undone by the next fire while a change across it is carried along as
+// the state turns; G_j models exactly that: sigma_j (the segment's total cap
+// scale) times the rotation taking the start's direction a to the end's b in
+// their common plane, after removing the component along a.  Without a fire
+// in the segment G_j = identity.  A segment's start is exact once every
+// earlier segment's is, so with nseg segments the iteration is exact after
+// nseg passes; it stops as soon as no start moves by more than tol (relative).
+// The first pass runs segments >= 1 from zero without the cap, and the first
+// sweep chains their plain sums with the cap applied at segment ends.
+
+// Segment starts for the first pass and the normaliser at every segment start
+// (n is linear: n0 plus the key sums of the blocks before).  One workgroup
+// per chain.
+__global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StatePlan pl, const float* __restrict__ n_init,
+                                                             float* __restrict__ n_seg) {
+  __shared__ float part[kMaxParaSegs][kD];
+  const int64_t c = blockIdx.x;
+  const int tid = threadIdx.x, G = pp.nseg;
+  float* sit = pp.Sit + c * G * kD * kD;
+  const float* s0 = pp.S_init + c * kD * kD;
+  for (int e = tid; e < G * kD * kD; e += 1024) sit[e] = e < kD * kD ? s0[e] : 0.f;
+  if (tid == 0) pp.conv[c] = 0;
+  const int sg = tid >> 6, f = tid & 63;
+  if (sg < G) {
+    float acc = 0.f;
+    for (int b = pp.bnd[sg]; b < pp.bnd[sg + 1]; ++b) acc += pl.Kmat[(c * pl.nblk + b) * kPackFloats + kPackKs + f];
+    part[sg][f] = acc;
+  }
+  __syncthreads();
+  if (sg < G) {
+    float n = n_init[c * kD + f];
+    for (int j = 0; j < sg; ++j) n += part[j][f];
+    n_seg[(c * G + sg) * kD + f] = n;
+  }
+}
+
+// Sum of 8 values over the workgroup (256 threads); red holds [2][4][8]
+// (alternating halves, so one barrier per sum suffices).  The barrier waits
+// for LDS only: the caller's global loads of the next step stay in flight.
+__device__ __forceinline__ void para_sum8(float (&x)[8], float* red, int buf, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = wave_sum(x[i]);   // DPP row sums and readlanes, no LDS
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[(buf * 4 + (tid >> 6)) * 8 + i] = x[i];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float* r = red + buf * 32 + i;
+    x[i] = (r[0] + r[8]) + (r[16] + r[24]);
+  }
+}
+
+// The sweep over one chain's segments (one workgroup per chain, each thread
+// 16 entries of every 64 x 64 matrix).  first: the sweep after the first
+// pass (plain sums chained with the cap at segment ends).
+__global__ void __launch_bounds__(256) vla_para_sweep_kernel(ParaPlan pp, int first) {
+  __shared__ float red[2 * 4 * 8];
+  __shared__ float srec[kMaxParaSegs * 4];   // the segments' records, read once
+  const int64_t c = blockIdx.x;
+  if (!first && pp.conv[c]) return;   // uniform
+  const int tid = threadIdx.x, G = pp.nseg;
+  if (tid < G * 4) srec[tid] = pp.rec[c * G * 4 + tid];
+  const int64_t base = c * G * kD * kD;
+  const int e0 = tid * 16;
+  float nw[16], od[16], fj[16];
+  auto load16 = [](const float* p, float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(p)[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+  };
+  load16(pp.S_init + c * kD * kD + e0, nw);
+  float maxchg = 0.f;
+  // Segment j's start and end are loaded one step ahead (they do not depend
+  // on the sweep), so their latency hides behind step j - 1.
+  float odn[16], fjn[16];
+  load16(pp.Sit + base + e0, odn);
+  load16(pp.F + base + e0, fjn);
+  __syncthreads();   // srec
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      od[i] = odn[i];
+      fj[i] = fjn[i];
+    }
+    if (j + 1 < G) {
+      load16(pp.Sit + base + (j + 1) * kD * kD + e0, odn);
+      load16(pp.F + base + (j + 1) * kD * kD + e0, fjn);
+    }
+    const float lsum = srec[4 * j];
+    const bool fired = srec[4 * j + 1] > 0.f;
+    float nx[16];
+    float chg_j = 0.f;   // relative move of this segment's start
+    if (first) {
+      if (j == 0) {   // the first segment ran from the true start, with the cap
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nx[i] = fj[i];
+      } else {
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          nx[i] = nw[i] + fj[i];
+          x[0] = fmaf(nx[i], nx[i], x[0]);
+        }
+        para_sum8(x, red, j & 1, tid);
+        const float nrm = sqrtf(x[0]);
+        const float sc = (pp.cap_on && nrm > pp.cap) ? pp.cap / nrm : 1.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nx[i] *= sc;
+      }
+    } else {
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float E[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        E[i] = nw[i] - od[i];
+        x[0] = fmaf(E[i], od[i], x[0]);   // <E, old>
+        x[1] = fmaf(E[i], fj[i], x[1]);   // <E, F>
+        x[2] = fmaf(E[i], E[i], x[2]);    // |E|^2
+        x[3] = fmaf(nw[i], nw[i], x[3]);  // |new|^2
+        x[4] = fmaf(od[i], fj[i], x[4]);  // <old, F>
+        x[5] = fmaf(od[i], od[i], x[5]);  // |old|^2
+        x[6] = fmaf(fj[i], fj[i], x[6]);  // |F|^2
+      }
+      para_sum8(x, red, j & 1, tid);
+      const float sig = exp2f(lsum);
+      chg_j = sqrtf(x[2]) / fmaxf(sqrtf(x[3]), 1e-30f);
+      chg_j = chg_j == chg_j ? chg_j : 3.0e38f;   // NaN counts as moved
+      maxchg = fmaxf(maxchg, chg_j);
+      if (fired && x[5] > 0.f && x[6] > 0.f) {
+        const float no = sqrtf(x[5]), nf = sqrtf(x[6]);
+        const float ia = 1.f / no, ib = 1.f / nf;
+        const float cab = x[4] * ia * ib;          // cos of the angle between start and end
+        const float ea = x[0] * ia, eb = x[1] * ib;
+        if (1.f + cab > 1e-3f) {
+          const float g = (ea + eb) / (1.f + cab);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float a = od[i] * ia, b = fj[i] * ib;
+            // R E - (E.a) b with R the rotation a -> b: E - g (a + b) + 2 (E.a) b - (E.a) b
+            nx[i] = fmaf(sig, fmaf(ea, b, fmaf(-g, a + b, E[i])), fj[i]);
+          }
+        } else {   // (start and end nearly opposite: remove the component along the end only)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) nx[i] = fmaf(sig, fmaf(-eb, fj[i] * ib, E[i]), fj[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nx[i] = fmaf(sig, E[i], fj[i]);
+      }
+    }
+    // The next pass reruns a segment only if its start moved by more than
+    // tol_skip; a segment left out keeps the start its results came from.
+    // Segment 0 always starts at the true S and never reruns.
+    const bool run = j > 0 && (first || chg_j > pp.tol_skip);
+    if (tid == 0) pp.active[c * G + j] = run ? 1 : 0;
+    if (run) {
+      float4* dst = reinterpret_cast<float4*>(pp.Sit + base + j * kD * kD + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_float4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) nw[i] = nx[i];
+  }
+  if (!first && tid == 0) {
+    const bool done = maxchg <= pp.tol;
+    pp.conv[c] = done ? 1 : 0;
+    if (!done && pp.iter_last) pp.chain_info[c * 4 + kInfoFallback] = 1;
+  }
+}
+
+// Per-chain statistics of the parallel-in-time pass: cap fires summed over
+// segments, the first one, non-finite final state or inverse pass.
+__global__ void __launch_bounds__(256) vla_para_stats_kernel(ParaPlan pp, const float* __restrict__ S_T,
+                                                             const float* __restrict__ n_T, int32_t* __restrict__ stats) {
+  __shared__ int bad_any;
+  const int64_t c = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad_any = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int e = tid; e < kD * kD; e += 256) bad |= !isfinite(S_T[c * kD * kD + e]);
+  if (tid < kD) bad |= !isfinite(n_T[c * kD + tid]);
+  if (bad) atomicOr(&bad_any, 1);
+  __syncthreads();
+  if (tid == 0) {
+    int fires = 0, first = -1;
+    for (int j = 0; j < pp.nseg; ++j) {
+      const float* rc = pp.rec + (c * pp.nseg + j) * 4;
+      fires += static_cast<int>(rc[1]);
+      if (first < 0 && rc[2] >= 0.f) first = static_cast<int>(rc[2]);
+    }
+    int32_t* st = stats + c * 4;
+    st[0] = pp.chain_info[c * 4 + kInfoGuard];
+    st[1] = fires;
+    st[2] = (bad_any || pp.chain_info[c * 4 + kInfoNonfinite]) ? 1 : 0;
+    st[3] = first;
+  }
+}
+
 template <typename TIn>
 size_t state_prep_lds_bytes() { return PrepLds<TIn>::kBytes; }
 
@@ -1003,15 +1310,36 @@ hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains,
   return hipGetLastError();
 }
 
+hipError_t launch_para_init(const ParaPlan& pp, const StatePlan& pl, const float* n_init, float* n_seg,
+                            hipStream_t stream) {
+  if (pp.chains <= 0 || pp.nseg < 1 || pp.nseg > kMaxParaSegs) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vla_para_init_kernel, dim3(pp.chains), dim3(1024), 0, stream, pp, pl, n_init, n_seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_para_sweep(const ParaPlan& pp, int first, hipStream_t stream) {
+  hipLaunchKernelGGL(vla_para_sweep_kernel, dim3(pp.chains), dim3(256), 0, stream, pp, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_para_stats(const ParaPlan& pp, const float* S_T, const float* n_T, int32_t* stats,
+                             hipStream_t stream) {
+  if (!stats) return hipSuccess;
+  hipLaunchKernelGGL(vla_para_stats_kernel, dim3(pp.chains), dim3(256), 0, stream, pp, S_T, n_T, stats);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,
                               int chains, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   hipError_t e = hipSuccess;
+  if (sg.pr && (sg.nseg < 1 || sg.nseg > kMaxParaSegs)) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(sg.pr ? chains * sg.nseg : chains);
   if (ev_start && (e = hipEventRecord(ev_start, stream)) != hipSuccess) return e;
   if (pl.bf16)
-    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(chains), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
+    hipLaunchKernelGGL(vla_state_chain_kernel<uint16_t>, dim3(grid), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
                        a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   else
-    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(chains), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
+    hipLaunchKernelGGL(vla_state_chain_kernel<float>, dim3(grid), dim3(kChainThreads), 0, stream, pl, sg, a.S_T,
                        a.n_T, a.stats, chain_info, a.cap, a.cap_on);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_stop && (e = hipEventRecord(ev_stop, stream)) != hipSuccess) return e;

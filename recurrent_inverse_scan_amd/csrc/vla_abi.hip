@@ -201,6 +201,10 @@ struct ChunkLayout {
          off_alpha = 0, off_K = 0, off_Kx = 0, off_VT = 0, off_AT = 0, off_X = 0, off_wsig = 0, off_ld = 0, off_nb = 0,
          off_ncarry = 0, off_cnt = 0, off_flag = 0, off_gather = 0,
          total = 0;
+  // Parallel-in-time state pass (additive update): segments per chain, and
+  // its segment starts, segment ends, records, normalisers and flags.
+  int para = 1;
+  size_t off_pSit = 0, off_pF = 0, off_prec = 0, off_pn = 0, off_pconv = 0, off_pact = 0;
   // Residual update's state pass (replaces the additive one's buffers).
   size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0, off_rex = 0;
 };
@@ -223,6 +227,17 @@ ChunkLayout finish_layout(const vla_scan_params_t* p, ChunkLayout cl, size_t off
   if (p->validate) off += kValidateBytes;
   cl.total = off;
   return cl;
+}
+
+// Segments of the parallel-in-time state pass: enough to give every chain's
+// segments a compute unit of the 256 (one chain-kernel workgroup fills one),
+// at most 16, and at least two blocks each; 1 keeps one pass per chain.
+int para_segments(const vla_scan_params_t* p, int64_t chains, int nblk) {
+  if (p->update != VLA_UPDATE_ADDITIVE || chains <= 0) return 1;
+  int64_t G = p->para_segments;
+  if (G == 0) G = std::min<int64_t>(vla::kMaxParaSegs, 256 / chains);
+  G = std::min<int64_t>(G, std::min<int64_t>(vla::kMaxParaSegs, nblk / 2));
+  return G >= 2 ? static_cast<int>(G) : 1;
 }
 
 ChunkLayout plan_schedule(const vla_scan_params_t* p) {
@@ -290,6 +305,16 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       cl.off_rex = off; off = align_up(off + C * nb * 4);       // per-block exact cap-test flags
       return finish_layout(p, cl, off);
     }
+    cl.para = para_segments(p, chains, cl.nblk);
+    if (cl.para > 1) {
+      const size_t G = static_cast<size_t>(cl.para);
+      cl.off_pSit = off; off = align_up(off + C * G * d2 * 4);
+      cl.off_pF = off; off = align_up(off + C * G * d2 * 4);
+      cl.off_prec = off; off = align_up(off + C * G * 4 * 4);
+      cl.off_pn = off; off = align_up(off + C * G * 64 * 4);
+      cl.off_pconv = off; off = align_up(off + C * 4);
+      cl.off_pact = off; off = align_up(off + C * G * 4);
+    }
     cl.off_K = off; off = align_up(off + C * nb * 2304 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
     // Regrouped update operands: fp32 storage only (bf16 reads its LDS rows).
@@ -325,6 +350,8 @@ vla_status_t check_params(const vla_scan_params_t* p) {
   if (p->chunk_len < 0) return fail(VLA_EINVAL, "chunk_len must be >= 0");
   if (p->update != VLA_UPDATE_ADDITIVE && p->update != VLA_UPDATE_RESIDUAL)
     return fail(VLA_EUNSUPPORTED, "update %d unsupported", p->update);
+  if (p->para_segments < 0 || p->para_segments > vla::kMaxParaSegs)
+    return fail(VLA_EINVAL, "para_segments must be 0..%d (got %d)", vla::kMaxParaSegs, p->para_segments);
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
   if (chains > 0x7fffffff) return fail(VLA_EUNSUPPORTED, "B*H too large");
   if (strided(p)) {
@@ -697,7 +724,58 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     return sg;
   };
   const int nch = static_cast<int>(chains);
-  if (nseg == 1) {
+  if (cl.para > 1) {
+    // Parallel in time: prep of every block, a first pass of all segments
+    // (segment 0 from the true start; the others from zero, uncapped), then
+    // passes from the swept starts until they stop moving (at most
+    // kParaPasses; a chain that has not converged by then is recomputed by
+    // the sequential fallback below), then the readout of every block.
+    constexpr int kParaPasses = 8;
+    const int G = cl.para;
+    vla::ParaPlan pp{};
+    pp.chains = nch;
+    pp.nseg = G;
+    for (int sidx = 0; sidx <= G; ++sidx) pp.bnd[sidx] = static_cast<int>(static_cast<int64_t>(sidx) * nblk / G);
+    pp.S_init = pl.S_init;
+    pp.Sit = reinterpret_cast<float*>(ws + cl.off_pSit);
+    pp.F = reinterpret_cast<float*>(ws + cl.off_pF);
+    pp.rec = reinterpret_cast<float*>(ws + cl.off_prec);
+    pp.conv = reinterpret_cast<int32_t*>(ws + cl.off_pconv);
+    pp.chain_info = pl.chain_info;
+    pp.cap = a.cap;
+    pp.cap_on = a.cap_on;
+    pp.active = reinterpret_cast<int32_t*>(ws + cl.off_pact);
+    pp.tol = 1e-5f;
+    pp.tol_skip = 2e-6f;
+    float* n_seg = reinterpret_cast<float*>(ws + cl.off_pn);
+    if ((e = vla::launch_state_prep(sp, a, nch, 0, nblk, 0, stream)) != hipSuccess) return hip_fail(e, "state prep launch");
+    if ((e = vla::launch_para_init(pp, sp, pl.n_init, n_seg, stream)) != hipSuccess) return hip_fail(e, "para init launch");
+    vla::ChainSeg sg{};
+    sg.pr = 1;
+    sg.nseg = G;
+    for (int sidx = 0; sidx <= G; ++sidx) sg.bnd[sidx] = pp.bnd[sidx];
+    sg.S_in = pp.Sit;
+    sg.n_in = n_seg;
+    sg.F = reinterpret_cast<float*>(ws + cl.off_pF);
+    sg.rec = reinterpret_cast<float*>(ws + cl.off_prec);
+    sg.uncapped_tail = 1;
+    sg.conv = nullptr;
+    const int passes = std::min(G, kParaPasses);
+    for (int k = -1; k < passes; ++k) {
+      hipEvent_t ev0, ev1;
+      next_timing(&ev0, &ev1);
+      if ((e = vla::launch_state_chain(sp, sg, a, pl.chain_info, nch, stream, ev0, ev1)) != hipSuccess)
+        return hip_fail(e, "state chain launch");
+      pp.iter_last = k + 1 == passes ? 1 : 0;
+      if ((e = vla::launch_para_sweep(pp, k < 0 ? 1 : 0, stream)) != hipSuccess) return hip_fail(e, "para sweep launch");
+      sg.uncapped_tail = 0;
+      sg.conv = pp.conv;
+      sg.active = pp.active;
+    }
+    if ((e = vla::launch_para_stats(pp, a.S_T, a.n_T, stats, stream)) != hipSuccess) return hip_fail(e, "para stats launch");
+    if ((e = vla::launch_state_readout(sp, a, pl.chain_info, nch, 0, nblk, 0, stream)) != hipSuccess)
+      return hip_fail(e, "state readout launch");
+  } else if (nseg == 1) {
     if ((e = vla::launch_state_prep(sp, a, nch, 0, nblk, 0, stream)) != hipSuccess) return hip_fail(e, "state prep launch");
     hipEvent_t ev0, ev1;
     next_timing(&ev0, &ev1);

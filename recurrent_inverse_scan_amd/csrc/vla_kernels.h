@@ -95,6 +95,7 @@ struct StatePlan {
 // S at b_hi in Xsnap, n in n_carry and its counters for the next one; the last
 // writes S_T, n_T and stats (guard count and non-finite flag of the inverse
 // pass taken from chain_info).
+constexpr int kMaxParaSegs = 16;
 struct ChainSeg {
   int b_lo, b_hi;
   const float* S_in;      // S at block b_lo, chain c at S_in + c * S_in_stride
@@ -104,7 +105,40 @@ struct ChainSeg {
   float* n_carry;         // [chains][64] n after block b_hi - 1
   int32_t* counters;      // [chains][2] cap fires so far and the first cap step (-1: none)
   int last;
+  // Parallel-in-time mode (pr != 0): all segments of every chain at once;
+  // workgroup x runs segment x / chains of chain x % chains over blocks
+  // [bnd[seg], bnd[seg + 1]), from S_in + (c * nseg + seg) * 4096 and
+  // n_in + (c * nseg + seg) * 64, and leaves S at the segment's end in F and
+  // (log2 sigma over the segment, cap fires, first cap step) in rec.
+  int pr, nseg, uncapped_tail;   // uncapped_tail: segments >= 1 run without the cap
+  int bnd[kMaxParaSegs + 1];
+  float* F;               // [chains][nseg][64][64]
+  float* rec;             // [chains][nseg][4]
+  const int32_t* conv;    // [chains]: nonzero once the chain's segment starts have converged
+  const int32_t* active;  // [chains][nseg] (nullable): zero skips the segment (its start has not moved)
 };
+
+// Parallel-in-time state pass (state_pass.hip): the segment starts' sweep
+// between chain-kernel passes, the normaliser at the segment starts, and the
+// per-chain statistics.
+struct ParaPlan {
+  int chains, nseg, iter_last;   // iter_last: this sweep is the last one allowed
+  int bnd[kMaxParaSegs + 1];
+  const float* S_init;   // [chains][64][64]
+  float* Sit;            // [chains][nseg][64][64] segment starts of the next pass
+  const float* F;        // [chains][nseg][64][64]
+  const float* rec;      // [chains][nseg][4]
+  int32_t* conv;         // [chains]
+  int32_t* active;       // [chains][nseg]: segments whose start moved, to run in the next pass
+  int32_t* chain_info;   // [chains][4]: the fallback flag is set if a chain does not converge
+  float cap, tol, tol_skip;
+  int cap_on;
+};
+hipError_t launch_para_init(const ParaPlan& pp, const StatePlan& pl, const float* n_init, float* n_seg,
+                            hipStream_t stream);
+hipError_t launch_para_sweep(const ParaPlan& pp, int first, hipStream_t stream);
+hipError_t launch_para_stats(const ParaPlan& pp, const float* S_T, const float* n_T, int32_t* stats,
+                             hipStream_t stream);
 
 // Prep and readout of blocks [b_lo, b_lo + nb) of every chain (parallel, at
 // most max_wg workgroups if max_wg > 0); the readout flags non-finite outputs
@@ -113,8 +147,9 @@ hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains,
                              hipStream_t stream);
 hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t* chain_info, int chains, int b_lo,
                                 int nb, int max_wg, hipStream_t stream);
-// The chain kernel over one segment (one workgroup per chain).  Non-null
-// events are recorded on the stream right before and after it.
+// The chain kernel over one segment (one workgroup per chain), or in
+// parallel-in-time mode over all segments (chains * nseg workgroups).
+// Non-null events are recorded on the stream right before and after it.
 hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,
                               int chains, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 

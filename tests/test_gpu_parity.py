@@ -379,7 +379,7 @@ def test_chunked_segments_match_oracle(dtype, L, period, seg):
                                 nudge_period=period, s_cap=30.0)
     _say(f"case chunked L={L} segments {seg} {dtype}")
     x = case(cfg, seed=16)
-    out = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg, para_segments=1)
     ref = run_oracle(x, cfg)
     _, st = _check(cfg, out, ref)
     assert ref["cap_fires"].min() > 10
@@ -400,7 +400,7 @@ def test_chunked_segment_with_odd_start_block(dtype, T, seg):
                                 s_cap=3.0)
     _say(f"case chunked odd segment start T={T} seg={seg} {dtype}")
     x = case(cfg, seed=17)
-    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, segment_blocks=seg)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, segment_blocks=seg, para_segments=1)
     ref = run_oracle(x, cfg)
     _, st = _check(cfg, out, ref)
     assert ref["cap_fires"].min() > T // 2
@@ -427,7 +427,16 @@ def test_timing_hook_records_the_chain_kernel():
     timing_enable(True)
     try:
         for _ in range(2):
-            _gpu(x, cfg, schedule="chunked", segment_blocks=4)   # 10 blocks: segments of 2, 4, 4
+            # one pass per chain, 10 blocks: segments of 2, 4, 4
+            _gpu(x, cfg, schedule="chunked", segment_blocks=4, para_segments=1)
+        ms = timing_collect()
+    finally:
+        timing_enable(False)
+    assert len(ms) == 6 and all(t > 0 for t in ms), ms
+    timing_enable(True)
+    try:
+        # parallel in time, 5 segments: a first pass, then at most 5 more
+        _gpu(x, cfg, schedule="chunked", para_segments=5)
         ms = timing_collect()
     finally:
         timing_enable(False)
@@ -560,3 +569,30 @@ def test_scan_step_entry_point(update, dtype):
     ref = run_oracle(x, cfg, update=update)
     _check(cfg, (torch.cat(outs, dim=2), A, S, n, whole[4]), ref)
     assert np.abs(fires.reshape(-1) - ref["cap_fires"]).max() <= 1
+
+
+# ---------------------------------------------------------------------------
+# Parallel-in-time state pass: segments of each chain run at once from guessed
+# starts and are corrected by sweeps (the default for few chains); the
+# one-pass pipeline (para_segments = 1) is the reference schedule.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G,cap,T", [(2, 30.0, 1000), (5, 30.0, 2000), (16, 30.0, 3000), (16, None, 3000),
+                                     (8, 3.0, 1500), (16, 1e3, 9000)])
+def test_parallel_in_time_state_pass(dtype, G, cap, T):
+    """Against the oracle, and against the one-pass pipeline on the same
+    inputs: caps that bind early (30, 3: the sweeps must turn the starts
+    through many fires), no cap (the first sweep is already exact), a cap
+    that starts binding part-way (1e3 over 9000 tokens)."""
+    cfg = CONFIGS["long"].with_(name=f"para-G{G}-cap{cap}-{dtype}-T{T}", B=1, H=3, T=T, in_dtype=dtype,
+                                nudge_period=128, s_cap=cap)
+    _say(f"case para G={G} cap={cap} T={T} {dtype}")
+    x = case(cfg, seed=18 + G)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, para_segments=G)
+    ref = run_oracle(x, cfg)
+    _check(cfg, out, ref)
+    one = _gpu(x, cfg, schedule="chunked", chunk_len=64, para_segments=1)
+    for name, p_, q_ in zip("oASn", out[:4], one[:4]):
+        axes = (-2, -1) if name in "AS" else (-1,)
+        err = rel_err(p_, to64(q_), axes=axes)
+        assert err <= (1e-2 if name == "o" else 2e-4), (name, err)
