@@ -1033,16 +1033,35 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   }
   bool bad = false;
   const int fcol = ti * 32 + rl;
+  __syncthreads();   // every wave is done reading P'; its rows take the outputs now
 #pragma unroll
   for (int a = 0; a < 16; ++a) {
     const int t = tt * 32 + acc_row(a, h);
-    if (t < tcount) {
-      const float ov = Z[a] / dl[t];
-      bad |= !isfinite(ov);
-      Elem<TIn>::store(o + (row0 + t) * kD + fcol, ov);
-    }
+    const float ov = Z[a] / dl[t];
+    bad |= t < tcount && !isfinite(ov);
+    Ps[t * kLd + fcol] = ov;
   }
   if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
+  __syncthreads();
+  // Whole 16-byte pieces of o rows from the staged block.
+  constexpr int PPR = kD / EPV;
+#pragma unroll
+  for (int e = tid; e < kLb * PPR; e += kThreads) {
+    const int t = e / PPR, c = (e % PPR) * EPV;
+    if (t >= tcount) continue;
+    const float* src = Ps + t * kLd + c;
+    uint4 wv;
+    if constexpr (EPV == 4) {
+      wv = *reinterpret_cast<const uint4*>(src);
+    } else {
+      uint32_t hw[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        hw[k2] = static_cast<uint32_t>(f32_to_bf16(src[2 * k2])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * k2 + 1])) << 16);
+      wv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+    *reinterpret_cast<uint4*>(o + (row0 + t) * kD + c) = wv;
+  }
 }
 
 template <typename TIn>
@@ -1102,98 +1121,130 @@ __global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StateP
   }
 }
 
-// Sum of 8 values over the workgroup (256 threads); red holds [2][4][8]
-// (alternating halves, so one barrier per sum suffices).  The barrier waits
-// for LDS only: the caller's global loads of the next step stay in flight.
+constexpr int kSweepThreads = 512;                      // 8 waves: two per SIMD
+constexpr int kSweepWaves = kSweepThreads / 64;
+constexpr int kSweepEpt = kD * kD / kSweepThreads;      // matrix entries per thread
+
+// Sums of the first N of 8 values over the workgroup; red holds
+// [2][kSweepWaves][8] (alternating halves, so one barrier per sum suffices).
+// The barrier waits for LDS only: the caller's global loads of the next step
+// stay in flight.
+template <int N>
 __device__ __forceinline__ void para_sum8(float (&x)[8], float* red, int buf, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = wave_sum(x[i]);   // DPP row sums and readlanes, no LDS
+  for (int i = 0; i < N; ++i) x[i] = wave_sum(x[i]);   // DPP row sums and readlanes, no LDS
   if ((tid & 63) == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[(buf * 4 + (tid >> 6)) * 8 + i] = x[i];
+    for (int i = 0; i < N; ++i) red[(buf * kSweepWaves + (tid >> 6)) * 8 + i] = x[i];
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float* r = red + buf * 32 + i;
-    x[i] = (r[0] + r[8]) + (r[16] + r[24]);
+  for (int i = 0; i < N; ++i) {
+    const float* r = red + buf * kSweepWaves * 8 + i;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSweepWaves; ++w) t += r[8 * w];
+    x[i] = t;
   }
 }
 
 // The sweep over one chain's segments (one workgroup per chain, each thread
-// 16 entries of every 64 x 64 matrix).  first: the sweep after the first
-// pass (plain sums chained with the cap at segment ends).
-__global__ void __launch_bounds__(256) vla_para_sweep_kernel(ParaPlan pp, int first) {
-  __shared__ float red[2 * 4 * 8];
+// kSweepEpt consecutive entries of every 64 x 64 matrix).  first: the sweep
+// after the first pass (plain sums chained with the cap at segment ends).
+__global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan pp, int first) {
+  constexpr int E = kSweepEpt;
+  __shared__ float red[2 * kSweepWaves * 8];
   __shared__ float srec[kMaxParaSegs * 4];   // the segments' records, read once
   const int64_t c = blockIdx.x;
   if (!first && pp.conv[c]) return;   // uniform
   const int tid = threadIdx.x, G = pp.nseg;
   if (tid < G * 4) srec[tid] = pp.rec[c * G * 4 + tid];
   const int64_t base = c * G * kD * kD;
-  const int e0 = tid * 16;
-  float nw[16], od[16], fj[16];
-  auto load16 = [](const float* p, float (&x)[16]) {
+  const int e0 = tid * E;
+  float nw[E], od[E], fj[E];
+  auto load = [](const float* p, float (&x)[E]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < E / 4; ++q) {
       const float4 v = reinterpret_cast<const float4*>(p)[q];
       x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
     }
   };
-  load16(pp.S_init + c * kD * kD + e0, nw);
+  load(pp.S_init + c * kD * kD + e0, nw);
   float maxchg = 0.f;
   // Segment j's start and end are loaded one step ahead (they do not depend
   // on the sweep), so their latency hides behind step j - 1.
-  float odn[16], fjn[16];
-  load16(pp.Sit + base + e0, odn);
-  load16(pp.F + base + e0, fjn);
+  float odn[E], fjn[E];
+  load(pp.Sit + base + e0, odn);   // segment 0's start (the true one)
+  load(pp.F + base + e0, fjn);
   __syncthreads();   // srec
+  int nred = 0;      // sums so far: consecutive sums alternate halves of red
   for (int j = 0; j < G; ++j) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < E; ++i) {
       od[i] = odn[i];
       fj[i] = fjn[i];
     }
     if (j + 1 < G) {
-      load16(pp.Sit + base + (j + 1) * kD * kD + e0, odn);
-      load16(pp.F + base + (j + 1) * kD * kD + e0, fjn);
+      if (!first) load(pp.Sit + base + (j + 1) * kD * kD + e0, odn);   // the first sweep needs no starts
+      load(pp.F + base + (j + 1) * kD * kD + e0, fjn);
     }
     const float lsum = srec[4 * j];
     const bool fired = srec[4 * j + 1] > 0.f;
-    float nx[16];
+    float nx[E];
     float chg_j = 0.f;   // relative move of this segment's start
     if (first) {
       if (j == 0) {   // the first segment ran from the true start, with the cap
 #pragma unroll
-        for (int i = 0; i < 16; ++i) nx[i] = fj[i];
+        for (int i = 0; i < E; ++i) nx[i] = fj[i];
       } else {
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // The first pass ran segment j from zero without the cap, so its
+        // snapshots are the plain sums from the segment start: add them to
+        // the running state in four steps, applying the cap after each.
+        constexpr int kSub = 4;
+        const int blo = pp.bnd[j], len = pp.bnd[j + 1] - blo;
+        const int nsub = len < kSub ? len : kSub;
+        float prev[E], nxt[E];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          nx[i] = nw[i] + fj[i];
-          x[0] = fmaf(nx[i], nx[i], x[0]);
+        for (int i = 0; i < E; ++i) {
+          prev[i] = 0.f;
+          nx[i] = nw[i];
         }
-        para_sum8(x, red, j & 1, tid);
-        const float nrm = sqrtf(x[0]);
-        const float sc = (pp.cap_on && nrm > pp.cap) ? pp.cap / nrm : 1.f;
+        auto snap = [&](int sub) { return pp.Xsnap + (c * pp.nblk + blo + (sub * len) / nsub) * kD * kD + e0; };
+        if (nsub > 1) load(snap(1), nxt);   // each sub-step's snapshot is loaded one sub-step ahead
+        for (int sub = 1; sub <= nsub; ++sub) {
+          float cur[E];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) nx[i] *= sc;
+          for (int i = 0; i < E; ++i) cur[i] = sub < nsub ? nxt[i] : fj[i];
+          if (sub + 1 < nsub) load(snap(sub + 1), nxt);
+          float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            nx[i] += cur[i] - prev[i];
+            prev[i] = cur[i];
+            x[0] = fmaf(nx[i], nx[i], x[0]);
+          }
+          para_sum8<1>(x, red, nred++ & 1, tid);
+          const float nrm = sqrtf(x[0]);
+          const float sc = (pp.cap_on && nrm > pp.cap) ? pp.cap / nrm : 1.f;
+#pragma unroll
+          for (int i = 0; i < E; ++i) nx[i] *= sc;
+        }
       }
     } else {
       float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      float E[16];
+      float Ev[E];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        E[i] = nw[i] - od[i];
-        x[0] = fmaf(E[i], od[i], x[0]);   // <E, old>
-        x[1] = fmaf(E[i], fj[i], x[1]);   // <E, F>
-        x[2] = fmaf(E[i], E[i], x[2]);    // |E|^2
-        x[3] = fmaf(nw[i], nw[i], x[3]);  // |new|^2
-        x[4] = fmaf(od[i], fj[i], x[4]);  // <old, F>
-        x[5] = fmaf(od[i], od[i], x[5]);  // |old|^2
-        x[6] = fmaf(fj[i], fj[i], x[6]);  // |F|^2
+      for (int i = 0; i < E; ++i) {
+        Ev[i] = nw[i] - od[i];
+        x[0] = fmaf(Ev[i], od[i], x[0]);   // <E, old>
+        x[1] = fmaf(Ev[i], fj[i], x[1]);   // <E, F>
+        x[2] = fmaf(Ev[i], Ev[i], x[2]);   // |E|^2
+        x[3] = fmaf(nw[i], nw[i], x[3]);   // |new|^2
+        x[4] = fmaf(od[i], fj[i], x[4]);   // <old, F>
+        x[5] = fmaf(od[i], od[i], x[5]);   // |old|^2
+        x[6] = fmaf(fj[i], fj[i], x[6]);   // |F|^2
       }
-      para_sum8(x, red, j & 1, tid);
+      para_sum8<7>(x, red, nred++ & 1, tid);
       const float sig = exp2f(lsum);
       chg_j = sqrtf(x[2]) / fmaxf(sqrtf(x[3]), 1e-30f);
       chg_j = chg_j == chg_j ? chg_j : 3.0e38f;   // NaN counts as moved
@@ -1206,18 +1257,18 @@ __global__ void __launch_bounds__(256) vla_para_sweep_kernel(ParaPlan pp, int fi
         if (1.f + cab > 1e-3f) {
           const float g = (ea + eb) / (1.f + cab);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float a = od[i] * ia, b = fj[i] * ib;
+          for (int i = 0; i < E; ++i) {
+            const float av = od[i] * ia, bv = fj[i] * ib;
             // R E - (E.a) b with R the rotation a -> b: E - g (a + b) + 2 (E.a) b - (E.a) b
-            nx[i] = fmaf(sig, fmaf(ea, b, fmaf(-g, a + b, E[i])), fj[i]);
+            nx[i] = fmaf(sig, fmaf(ea, bv, fmaf(-g, av + bv, Ev[i])), fj[i]);
           }
         } else {   // (start and end nearly opposite: remove the component along the end only)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) nx[i] = fmaf(sig, fmaf(-eb, fj[i] * ib, E[i]), fj[i]);
+          for (int i = 0; i < E; ++i) nx[i] = fmaf(sig, fmaf(-eb, fj[i] * ib, Ev[i]), fj[i]);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) nx[i] = fmaf(sig, E[i], fj[i]);
+        for (int i = 0; i < E; ++i) nx[i] = fmaf(sig, Ev[i], fj[i]);
       }
     }
     // The next pass reruns a segment only if its start moved by more than
@@ -1228,10 +1279,10 @@ __global__ void __launch_bounds__(256) vla_para_sweep_kernel(ParaPlan pp, int fi
     if (run) {
       float4* dst = reinterpret_cast<float4*>(pp.Sit + base + j * kD * kD + e0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = make_float4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
+      for (int q = 0; q < E / 4; ++q) dst[q] = make_float4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) nw[i] = nx[i];
+    for (int i = 0; i < E; ++i) nw[i] = nx[i];
   }
   if (!first && tid == 0) {
     const bool done = maxchg <= pp.tol;
@@ -1318,7 +1369,7 @@ hipError_t launch_para_init(const ParaPlan& pp, const StatePlan& pl, const float
 }
 
 hipError_t launch_para_sweep(const ParaPlan& pp, int first, hipStream_t stream) {
-  hipLaunchKernelGGL(vla_para_sweep_kernel, dim3(pp.chains), dim3(256), 0, stream, pp, first);
+  hipLaunchKernelGGL(vla_para_sweep_kernel, dim3(pp.chains), dim3(kSweepThreads), 0, stream, pp, first);
   return hipGetLastError();
 }
 

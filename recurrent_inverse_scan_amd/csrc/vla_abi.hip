@@ -745,8 +745,15 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     pp.cap = a.cap;
     pp.cap_on = a.cap_on;
     pp.active = reinterpret_cast<int32_t*>(ws + cl.off_pact);
-    pp.tol = 1e-5f;
-    pp.tol_skip = 2e-6f;
+    // Stop once no start moves by more than 4e-5 of its norm in a sweep: each
+    // sweep shrinks the moves about tenfold, so the starts of the last pass
+    // are then within about that much of the exact ones (float32 sums over a
+    // segment differ by about 1e-5).  Segments whose start moved by less than
+    // 4e-6 are not rerun.
+    pp.tol = 4e-5f;
+    pp.tol_skip = 4e-6f;
+    pp.Xsnap = sp.Xsnap;
+    pp.nblk = nblk;
     float* n_seg = reinterpret_cast<float*>(ws + cl.off_pn);
     if ((e = vla::launch_state_prep(sp, a, nch, 0, nblk, 0, stream)) != hipSuccess) return hip_fail(e, "state prep launch");
     if ((e = vla::launch_para_init(pp, sp, pl.n_init, n_seg, stream)) != hipSuccess) return hip_fail(e, "para init launch");

@@ -133,6 +133,8 @@ struct ParaPlan {
   int32_t* chain_info;   // [chains][4]: the fallback flag is set if a chain does not converge
   float cap, tol, tol_skip;
   int cap_on;
+  const float* Xsnap;    // [chains][nblk][64][64]: S at each block start from the last pass
+  int nblk;
 };
 hipError_t launch_para_init(const ParaPlan& pp, const StatePlan& pl, const float* n_init, float* n_seg,
                             hipStream_t stream);
