@@ -83,7 +83,7 @@ typedef struct {
   int32_t T;             /* tokens in this call (0 copies the state through) */
   int32_t d;             /* head dimension: 16, 32, 64 or 128 */
   int32_t r;             /* penalty directions per token (Woodbury rank): 1..4 */
-  vla_dtype_t in_dtype;  /* storage of q, k, v, u and of the output o */
+  int32_t in_dtype;      /* vla_dtype_t: storage of q, k, v, u and of the output o */
   float eps;             /* guard threshold and nudge size (default 1e-6) */
   int32_t nudge_period;  /* eps*I added to A every nudge_period tokens; 0 = off */
   float s_cap;           /* Frobenius cap on S; <= 0 or +inf = off */
@@ -344,8 +344,8 @@ vla_status_t vla_scan_forward_noalloc(const vla_scan_params_t* p,
  * Products accumulate in float32 on the matrix cores; the norm, the scale and
  * the final cast are float32.
  */
-vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dtype,
-                           vla_dtype_t out_dtype, const void* W_u, const void* k_raw,
+vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, int32_t in_dtype,
+                           int32_t out_dtype, const void* W_u, const void* k_raw,
                            void* u, void* stream);
 
 /*

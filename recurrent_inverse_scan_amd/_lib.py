@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libvla.so")
+# VLA_LIB names another build of the same library (the host-sanitised one
+# that the CPU test suite makes); by default the in-tree libvla.so.
+LIB_PATH = os.environ.get("VLA_LIB") or os.path.join(_PKG, "libvla.so")
 
 VLA_OK, VLA_EINVAL, VLA_EUNSUPPORTED, VLA_EWORKSPACE, VLA_ENONFINITE, VLA_EHIP = range(6)
 VLA_F32, VLA_BF16 = 0, 1

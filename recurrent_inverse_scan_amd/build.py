@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 
@@ -19,8 +20,38 @@ SOURCES = ["vla_abi.hip", "scan_seq.hip", "chunked.hip", "state_pass.hip", "inve
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument", "-Werror",
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+# Kernels whose waits count outstanding vector-memory operations (s_waitcnt
+# vmcnt(N) with N > 0): a register spill would add scratch loads and stores
+# to that count, so the build fails if any of them uses scratch.
+COUNTED_WAIT_KERNELS = ["vla_res_chain_kernel"]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs|AGPRs|Dynamic Stack):\s*(\S+)")
+
+
+def resource_usage(remarks: str) -> dict:
+    """Per-kernel {vgprs, agprs, scratch, dynamic_stack} from kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(remarks):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[{"VGPRs": "vgprs", "AGPRs": "agprs", "Dynamic Stack": "dynamic_stack"}.get(key, "scratch")] = val
+    return out
+
+
+def check_counted_waits(usage: dict) -> None:
+    for name in COUNTED_WAIT_KERNELS:
+        hits = {k: v for k, v in usage.items() if name in k}
+        if not hits:
+            raise RuntimeError(f"kernel {name} not found in the resource-usage remarks")
+        for k, v in hits.items():
+            if v.get("scratch") != "0" or v.get("dynamic_stack") != "False":
+                raise RuntimeError(f"{k} uses scratch ({v}); its counted s_waitcnt vmcnt would be wrong")
 
 
 def hipcc() -> str:
@@ -51,8 +82,16 @@ def build(verbose: bool = False) -> str:
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         results = list(ex.map(compile_one, SOURCES))
+    usage = {}
+    for _, msg in results:
+        usage.update(resource_usage(msg))
+    check_counted_waits(usage)
+    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+        for k in sorted(usage):
+            f.write(f"{k} {usage[k]}\n")
     if verbose:
         for obj, msg in results:
+            msg = "\n".join(l for l in msg.splitlines() if "remark:" not in l and not re.match(r"\s*\d*\s*\|", l))
             if msg.strip():
                 print(msg)
     tmp = LIB + ".tmp"

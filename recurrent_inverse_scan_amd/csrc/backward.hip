@@ -119,7 +119,8 @@ __global__ void __launch_bounds__(kThr) vla_bwd_tape_kernel(BwdArgs a) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
-  const int T = a.T, r = a.r, nck = (T + kChk - 1) / kChk;
+  const int T = a.T, r = a.r;
+  const int64_t nck = (T + kChk - 1) / kChk;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
@@ -142,7 +143,7 @@ __global__ void __launch_bounds__(kThr) vla_bwd_tape_kernel(BwdArgs a) {
   for (int t = 0; t < T; ++t) {
     const int64_t row = c * T + t;
     if (t % kChk == 0) {   // checkpoint at the chunk start (state before token t)
-      const int ck = t / kChk;
+      const int64_t ck = t / kChk;
 #pragma unroll
       for (int j = 0; j < L::W; ++j) {
         ckA[(ck * D + i) * D + c0 + j] = sA[i * L::S + c0 + j];
@@ -234,7 +235,8 @@ __global__ void __launch_bounds__(kThr) vla_bwd_reverse_kernel(BwdArgs a) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
-  const int T = a.T, r = a.r, nck = (T + kChk - 1) / kChk;
+  const int T = a.T, r = a.r;
+  const int64_t nck = (T + kChk - 1) / kChk;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(kThr) vla_bwd_reverse_kernel(BwdArgs a) {
   float gn_own = 0.f;   // gn[tid] for tid < D
   if (tid < D) gn_own = a.gnT ? a.gnT[c * D + tid] : 0.f;
 
-  for (int ck = nck - 1; ck >= 0; --ck) {
+  for (int64_t ck = nck - 1; ck >= 0; --ck) {
     const int t_lo = ck * kChk, t_hi = min(T, t_lo + kChk);
     // S_t for the chunk's tokens, recomputed from the chunk-start checkpoint
     // with the recorded alpha_hat and cap scale (the forward's arithmetic).

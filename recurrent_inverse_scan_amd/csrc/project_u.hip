@@ -65,8 +65,10 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_b
   asm volatile("" ::: "memory");   // one wave's LDS operations complete in order
   constexpr int EPC = 16 / static_cast<int>(sizeof(TOut));   // elements per 16-byte piece
   constexpr int PPR = D / EPC;                                // pieces per row
+  static_assert((32 * PPR) % 64 == 0, "whole pieces per lane");
 #pragma unroll
-  for (int c = lane; c < 32 * PPR; c += 64) {
+  for (int it = 0; it < 32 * PPR / 64; ++it) {
+    const int c = lane + 64 * it;
     const int rl = c / PPR, pc = c % PPR;
     const int64_t row = row_base + rl;
     const float* src = tile + rl * LD + pc * EPC;

@@ -304,6 +304,7 @@ __global__ void __launch_bounds__(256) vla_res_chain_kernel(ResPlan pl, int b_lo
                                                             float* __restrict__ S_T, int32_t* __restrict__ stats,
                                                             const int32_t* __restrict__ chain_info, int last) {
   __shared__ uint4 sR0[kSlotVecs], sR1[kSlotVecs], sR2[kSlotVecs];   // operand ring
+  static_assert(kRing == 3, "the ring is sR0, sR1, sR2");
   __shared__ float sX0[kXFloats], sX1[kXFloats];                     // tile exchange, by block parity
   __shared__ int sbad[4];
   ChainLane cl;

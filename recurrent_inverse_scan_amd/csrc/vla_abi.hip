@@ -155,7 +155,7 @@ vla_status_t hip_fail(hipError_t e, const char* what) {
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-size_t dtype_size(vla_dtype_t t) { return t == VLA_BF16 ? 2 : 4; }
+size_t dtype_size(int32_t t) { return t == VLA_BF16 ? 2 : 4; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -243,7 +243,11 @@ int para_segments(const vla_scan_params_t* p, int64_t chains, int nblk) {
 ChunkLayout plan_schedule(const vla_scan_params_t* p) {
   ChunkLayout cl;
   const int64_t chains = static_cast<int64_t>(p->B) * p->H;
-  const bool possible = p->d == 64 && p->T > 0 && chains > 0;
+  // Grids of the chunked kernels hold one workgroup per 64-token block of
+  // every chain (at most 256 threads each, below HIP's 2^32 work-items per
+  // launch dimension); longer problems take the sequential schedule.
+  constexpr int64_t kMaxBlocks = int64_t{1} << 22;
+  const bool possible = p->d == 64 && p->T > 0 && chains > 0 && chains * ((p->T + int64_t{63}) / 64) <= kMaxBlocks;
   int L = 0;
   if (possible) {
     if (p->chunk_len > 0) {
@@ -1074,7 +1078,7 @@ vla_status_t vla_scan_step(const vla_scan_params_t* p, const void* q, const void
   return vla_scan_forward(p, q, k, v, u, A, S, n, o, A, S, n, stats, workspace, workspace_bytes, stream_ptr);
 }
 
-vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, vla_dtype_t in_dtype, vla_dtype_t out_dtype,
+vla_status_t vla_project_u(int64_t rows, int32_t d, int32_t r, int32_t in_dtype, int32_t out_dtype,
                            const void* W_u, const void* k_raw, void* u, void* stream_ptr) {
   g_last_error.clear();
   if (rows < 0) return fail(VLA_EINVAL, "rows must be >= 0");

@@ -354,3 +354,15 @@ def test_backward_rejects_bad_pointers_and_workspace(lib):
     assert _bwd(lib, p, g_v=ctypes.c_void_p(0x10000000 + 11 * 0x1000000)) == _lib.VLA_EINVAL      # g_v == g_q
     assert _bwd(lib, p) == _lib.VLA_EWORKSPACE
     assert "workspace" in lib.vla_last_error().decode()
+
+
+def test_chunked_schedule_grid_limit(lib):
+    """The chunked kernels launch a workgroup per 64-token block of every chain:
+    up to 2^22 blocks are planned, beyond that only the sequential schedule runs."""
+    n = ctypes.c_size_t(0)
+    p = _params(lib, B=1, H=1, T=64 * (1 << 22), schedule=_lib.VLA_SCHEDULE_CHUNKED, nudge_period=0)
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value > 0
+    p.T += 64
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
+    p.schedule = _lib.VLA_SCHEDULE_AUTO
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
