@@ -32,7 +32,9 @@
 //    block's tokens in order, S_t = S_{t-1} + e_t alpha_t^T,
 //    o_t = S_t q_t / (n_t . q_t + den_eps) and, with the cap on, |S_t|_F:
 //    a token over the cap flags the chain, and the sequential fallback then
-//    recomputes it with the cap applied.
+//    recomputes it with the cap applied, from the start of the chunk that
+//    holds the chain's first such token (the state there is exact: no token
+//    before it was over the cap).
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_residual.h"
@@ -663,7 +665,7 @@ __global__ void __launch_bounds__(512) vla_res_readout_kernel(ResPlan pl, float 
   }
   const bool any_over = __any(over), any_bad = __any(bad);
   if ((tid & 63) == 0) {
-    if (any_over) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
+    if (any_over) atomicMax(chain_info + chain * 4 + kInfoRestart, nblk - b);
     if (any_bad) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
   }
   __syncthreads();   // the next block overwrites the LDS this one read last
@@ -971,6 +973,47 @@ hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int c
     hipLaunchKernelGGL((vla_res_readout_kernel<float, true>), grid, dim3(512), lds, stream, pl, den_eps, cap2,
                        chains, b_lo, nb, chain_info, pl.exact);
   }
+  return hipGetLastError();
+}
+
+
+// Restart set-up for the sequential fallback of the residual update: a chain
+// with a token over the cap, and no other reason to rerun, restarts at the
+// start of the chunk holding its first such block, from the chunk-start
+// inverse and the exact state snapshot and normaliser there, written over
+// its initial-state snapshot (which nothing reads after this).  Its start
+// token goes to kInfoRestart and it is flagged for the fallback.  Chains
+// flagged otherwise (a guard fire or a failed chunk-start inverse) rerun from
+// token 0.
+__global__ void __launch_bounds__(256) vla_res_restart_kernel(ResPlan pl, ResRestart rs) {
+  const int64_t chain = blockIdx.x;
+  int32_t* info = rs.chain_info + chain * 4;
+  const int first = info[kInfoRestart];
+  const int other = info[kInfoFallback];
+  const int b = first > 0 ? pl.nblk - first : 0;
+  const int t_r = (first > 0 && !other) ? (b * kB / rs.chunk_len) * rs.chunk_len : 0;
+  if (t_r > 0) {
+    const int chunk = t_r / rs.chunk_len, blk = t_r / kB;
+    const float4* a = reinterpret_cast<const float4*>(rs.Ac + (chain * rs.nchunks + chunk) * kD * kD);
+    const float4* sn = reinterpret_cast<const float4*>(pl.Ssnap + (chain * pl.nblk + blk) * kD * kD);
+    float4* ad = reinterpret_cast<float4*>(rs.A_init + chain * kD * kD);
+    float4* sd = reinterpret_cast<float4*>(rs.S_init + chain * kD * kD);
+    for (int i = threadIdx.x; i < kD * kD / 4; i += blockDim.x) {
+      ad[i] = a[i];
+      sd[i] = sn[i];
+    }
+    if (threadIdx.x < kD) rs.n_init[chain * kD + threadIdx.x] = pl.nblock[(chain * pl.nblk + blk) * kD + threadIdx.x];
+  }
+  __syncthreads();   // every thread has read info
+  if (threadIdx.x == 0) {
+    info[kInfoRestart] = t_r;
+    if (first > 0) info[kInfoFallback] = 1;
+  }
+}
+
+hipError_t launch_res_restart(const ResPlan& pl, const ResRestart& rs, int chains, hipStream_t stream) {
+  if (chains <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vla_res_restart_kernel, dim3(chains), dim3(256), 0, stream, pl, rs);
   return hipGetLastError();
 }
 

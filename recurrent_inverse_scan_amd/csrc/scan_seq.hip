@@ -72,8 +72,13 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   if constexpr (kFull) {
     if (x.only_if && x.only_if[chain * 4 + kInfoFallback] == 0) return;   // uniform per workgroup
   }
-  // Tokens [tbeg, tend) of the chain.
-  const int tbeg = kInv ? chunk * x.chunk_len : 0;
+  // Tokens [tbeg, tend) of the chain.  A fallback run (only_if) starts at the
+  // chain's restart token, from the state the caller left for it in A0, S0
+  // and n0.
+  int tbeg = kInv ? chunk * x.chunk_len : 0;
+  if constexpr (kFull) {
+    if (x.only_if) tbeg = x.only_if[chain * 4 + kInfoRestart];
+  }
   const int tend = kInv ? min(a.T, tbeg + x.chunk_len) : a.T;
 
   const int tid = threadIdx.x;
@@ -632,6 +637,9 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
       bool any_bad = false;
       for (int ww = 0; ww < NW; ++ww) any_bad |= red[ww * 4] != 0.f;
       int32_t guards = guard_fires;
+      // A chain restarted past token 0 keeps the earlier outputs of the
+      // chunked passes (no guard fired and no cap applied there).
+      if (kFull && x.only_if && tbeg > 0) any_bad |= x.only_if[chain * 4 + kInfoNonfinite] != 0;
       if constexpr (!kFull) {
         guards = x.chain_info ? x.chain_info[chain * 4 + 0] : 0;
         any_bad |= x.chain_info && x.chain_info[chain * 4 + 2] != 0;

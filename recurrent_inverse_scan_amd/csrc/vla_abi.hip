@@ -683,6 +683,15 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     }
     if ((e = vla::launch_stats_finalize(stats, pl.chain_info, nch, stream)) != hipSuccess)
       return hip_fail(e, "stats launch");
+    vla::ResRestart rs{};
+    rs.chunk_len = cl.L;
+    rs.nchunks = cl.nchunks;
+    rs.Ac = pl.Ac;
+    rs.A_init = pl.A_init;
+    rs.S_init = pl.S_init;
+    rs.n_init = pl.n_init;
+    rs.chain_info = pl.chain_info;
+    if ((e = vla::launch_res_restart(rp, rs, nch, stream)) != hipSuccess) return hip_fail(e, "restart launch");
     e = vla::launch_scan_sequential(a, d, bf16, nch, pl.chain_info, stream);
     if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
     return VLA_OK;

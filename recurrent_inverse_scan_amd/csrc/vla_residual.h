@@ -39,6 +39,16 @@ hipError_t launch_res_nprefix(const ResPlan& pl, int b_lo, int b_hi, const float
 hipError_t launch_res_chain(const ResPlan& pl, int b_lo, int b_hi, const float* S_in, int64_t S_in_stride,
                             float* S_T, int32_t* stats, const int32_t* chain_info, int last, int chains,
                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+// Where the sequential fallback restarts a chain (see vla_res_restart_kernel).
+struct ResRestart {
+  int chunk_len, nchunks;
+  const float* Ac;       // [chains][nchunks][64][64] chunk-start inverses
+  float* A_init;         // [chains][64][64], overwritten for restarted chains
+  float* S_init;
+  float* n_init;         // [chains][64]
+  int32_t* chain_info;   // [chains][4]
+};
+hipError_t launch_res_restart(const ResPlan& pl, const ResRestart& rs, int chains, hipStream_t stream);
 hipError_t launch_res_readout(const ResPlan& pl, float den_eps, float cap, int cap_on, int chains, int b_lo, int nb,
                               int max_wg, int32_t* chain_info, hipStream_t stream);
 

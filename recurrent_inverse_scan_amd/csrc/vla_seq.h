@@ -14,6 +14,10 @@ enum class SeqMode { kFull, kStateOnly, kInverseOnly };
 constexpr int kInfoGuard = 0;      // guard fires in the inverse pass
 constexpr int kInfoFallback = 1;   // nonzero: redo this chain sequentially
 constexpr int kInfoNonfinite = 2;  // a non-finite alpha_hat or inverse appeared
+// Residual update with the cap: nblk - (first block with a token over the
+// cap), 0 = none; the restart set-up then turns it into the token from which
+// the sequential fallback reruns the chain.
+constexpr int kInfoRestart = 3;
 
 struct SeqExtra {
   const float* alpha;         // kStateOnly: alpha_hat per token, [chains][T][d] fp32

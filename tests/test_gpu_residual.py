@@ -233,3 +233,68 @@ def test_residual_chunked_segments_match_oracle(dtype, L, period, seg, cap):
     again = _gpu(x, cfg, schedule="chunked", chunk_len=L, segment_blocks=seg)
     for a_, b_ in zip(out, again):
         assert torch.equal(a_, b_)
+
+
+def _louder_tail(x, cfg, lo):
+    """Values doubled from token `lo` on (exact in both storage types): the
+    residual state follows its values, so its norm rises past its earlier
+    maximum only there."""
+    x = dict(x)
+    v = x["v"].clone()
+    v[..., lo:, :] *= 2
+    x["v"] = v
+    return x
+
+
+def _late_cap(norms, lo):
+    """A cap 5 % above the largest pre-cap norm (oracle, cap off) before token
+    `lo`, and the first token after it whose norm exceeds the cap."""
+    cap = 1.05 * float(norms[:lo].max())
+    over = np.nonzero(norms > cap)[0]
+    assert over.size and over[0] >= lo
+    return cap, int(over[0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_residual_cap_restarts_from_the_first_capped_chunk(dtype):
+    """A chain whose first cap fire comes late reruns sequentially from the
+    start of the chunk holding it (chunk-start inverse, state snapshot and
+    normaliser there); the result matches the oracle, cap statistics included."""
+    cfg = CONFIGS["long"].with_(name=f"res-late-cap-{dtype}", B=1, H=3, T=2400, nudge_period=128, s_cap=None,
+                                in_dtype=dtype)
+    lo = 1400
+    x = _louder_tail(case(cfg, seed=5), cfg, lo)
+    pre = run_oracle(x, cfg, chains=[0], update="residual")
+    cap, t_fire = _late_cap(pre["pre_cap_norm"][0], lo)
+    cfg = cfg.with_(s_cap=cap)
+    _say(f"case late cap {dtype} cap={cap:.4f}")
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=128)
+    ref = run_oracle(x, cfg, update="residual")
+    st = _check(cfg, out, ref)
+    assert ref["first_cap_step"][0] == t_fire and st[0, 1] > 0
+
+
+def test_residual_full_size_binding_cap():
+    """The 65536-token workload with the residual update, values doubled in
+    the second half and a cap that first binds there: the fallback reruns
+    only the tail."""
+    cfg = CONFIGS["long"]
+    sel = [0, 15]
+    x = _louder_tail(make_inputs(cfg, seed=0), cfg, cfg.T // 2)
+    u = project_u(x["W_u"].to(DEV), x["k_raw"].to(DEV))
+    C = cfg.B * cfg.H
+    kr = x["k_raw"].reshape(C, cfg.T, cfg.d)[sel]
+    u_ref = oracle_project_u(x["W_u"], kr.reshape(-1, cfg.d))
+    u_ref = torch.from_numpy(u_ref).to(x["q"].dtype).reshape(len(sel), cfg.T, cfg.r, cfg.d)
+    q, k, v = (x[n].reshape(C, cfg.T, cfg.d)[sel] for n in ("q", "k", "v"))
+    pre = oracle_scan(q[:1], k[:1], v[:1], u_ref[:1], nudge_period=cfg.nudge_period, s_cap=None, update="residual",
+                      trace_norms=True)
+    cap, t_fire = _late_cap(pre["pre_cap_norm"][0], cfg.T // 2)
+    cfg = cfg.with_(s_cap=cap)
+    _say(f"case full/long binding cap={cap:.4f}")
+    out = scan_forward(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), u, nudge_period=cfg.nudge_period,
+                       s_cap=cap, update="residual")
+    torch.cuda.synchronize()
+    ref = oracle_scan(q, k, v, u_ref, nudge_period=cfg.nudge_period, s_cap=cap, update="residual", trace_norms=True)
+    st = _check(cfg, out, ref, chains=sel)
+    assert ref["first_cap_step"][0] == t_fire and st[0, 1] > 0
