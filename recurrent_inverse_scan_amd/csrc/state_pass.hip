@@ -57,6 +57,11 @@ constexpr int kPackFloats = 2304;
 constexpr int kPackPieces = kPackFloats / 256;   // 1 KiB pieces
 static_assert(kPackKs + kLb <= kPackFloats, "pack layout");
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads and stores (a __syncthreads fence
+// would also drain the global loads still in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -262,7 +267,7 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
       rap.store_f32(Ap, tid);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   const int ti = w >> 1, tj = w & 1, rl = lane & 31;
   f32x16 gv = zero16(), ga = zero16(), pk = zero16(), xv = zero16(), xa = zero16();
@@ -314,24 +319,25 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
 #pragma unroll
     for (int s = 0; s < 16; ++s) Xout[(ti * 32 + acc_row(s, h)) * kLb + col] = xv[s] * xa[s];
   }
-  __syncthreads();   // Af and Ap are free from here on
+  lds_barrier();   // Af and Ap are free from here on
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const int t = ti * 32 + acc_row(s, h);
     Ap[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
     Af[t * kLd + col] = gv[s] * ga[s];
   }
-  __syncthreads();
-  // Rows of K: exclusive prefix sums in place, K(t,t) and the row totals; rows
-  // of the masked q.k products: their sums.  Wave w takes rows 16 w .. 16 w + 15,
-  // lane s column s, with DPP scans.
+  lds_barrier();
+  // Rows of K: exclusive prefix sums straight into the triangle (row t's
+  // j <= t at t(t+1)/2 + j), K(t,t) and the row totals; rows of the masked
+  // q.k products: their sums.  Wave w takes rows 16 w .. 16 w + 15, lane s
+  // column s, with DPP scans.
   if (tid < kLb) pack[kPackKs + tid] = (ksum_part[0][tid] + ksum_part[1][tid]) + (ksum_part[2][tid] + ksum_part[3][tid]);
 #pragma unroll 4
   for (int rr = 0; rr < 16; ++rr) {
     const int t = w * 16 + rr;   // wave-uniform
     const float x = Af[t * kLd + lane];
     const float inc = wave_incl_scan(x, lane);
-    Af[t * kLd + lane] = inc - x;
+    if (lane <= t) pack[t * (t + 1) / 2 + lane] = inc - x;
     const float tot = readlane_f(inc, kLb - 1);
     const float e_t = readlane_f(x, t);
     const float ldt = wave_sum(Ap[t * kLd + lane]);
@@ -340,13 +346,6 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
       pack[kPackTot + t] = tot;
       if (t < tcount) pl.ld[row0 + t] = ldt;
     }
-  }
-  __syncthreads();
-  for (int e = tid; e < kTriN; e += kThreads) {   // the triangle, row t at t(t+1)/2
-    int r = static_cast<int>((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-    r -= (r * (r + 1) / 2 > e) ? 1 : 0;
-    r += ((r + 1) * (r + 2) / 2 <= e) ? 1 : 0;
-    pack[e] = Af[r * kLd + (e - r * (r + 1) / 2)];
   }
 }
 
@@ -358,7 +357,7 @@ vla_state_prep_kernel(StatePlan pl, const TIn* __restrict__ q, const TIn* __rest
                       const TIn* __restrict__ v, int b_lo, int nb, int64_t items) {
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     prep_block<TIn>(pl, q, k, v, b_lo, nb, item);
-    __syncthreads();   // LDS is restaged by the next item
+    lds_barrier();   // LDS is restaged by the next item
   }
 }
 
@@ -954,6 +953,7 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   const int64_t row0 = chain * pl.T + tb;
   const int64_t blk = chain * pl.nblk + b;
   constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));   // elements per 16 bytes
+  float ldv = 0.f;
   {
     // Every global load of the block first, then the LDS stores: q rows,
     // v^T (v is read as rows and written transposed), S_b, alpha_hat rows.
@@ -969,6 +969,7 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
       w0 = ok ? pl.wsig[2 * (row0 + tid)] : 0.f;
       w1 = ok ? pl.wsig[2 * (row0 + tid) + 1] : 0.f;
       nb0 = pl.nblock[blk * kD + tid];
+      ldv = ok ? pl.ld[row0 + tid] : 0.f;
     }
     rq.store_rows(Qs, kQd, tid);
 #pragma unroll
@@ -986,11 +987,11 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
       nl[tid] = nb0;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < kLb) {
     float acc = 0.f;
     for (int i = 0; i < kD; ++i) acc = fmaf(Elem<TIn>::load(Qs + tid * kQd + i), nl[i], acc);
-    dl[tid] = acc + (tid < tcount ? pl.ld[row0 + tid] : 0.f) + den_eps;
+    dl[tid] = 1.f / (acc + ldv + den_eps);   // the outputs take 1 / den_t
   }
 
   const int tt = w >> 1, ti = w & 1;   // this wave's output tile; its P' tile is (tt, ts = ti)
@@ -1021,7 +1022,7 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   }
 #pragma unroll
   for (int a = 0; a < 16; ++a) Z[a] *= exp2f(sl[tt * 32 + acc_row(a, h)]);
-  __syncthreads();
+  lds_barrier();
   // + sum_s P'[t][s] v_s over the tiles ts <= tt: A = P' rows, B[k=s][n=i] = v^T[i][s].
   for (int ts = 0; ts <= tt; ++ts) {
 #pragma unroll
@@ -1033,16 +1034,16 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   }
   bool bad = false;
   const int fcol = ti * 32 + rl;
-  __syncthreads();   // every wave is done reading P'; its rows take the outputs now
+  lds_barrier();   // every wave is done reading P'; its rows take the outputs now
 #pragma unroll
   for (int a = 0; a < 16; ++a) {
     const int t = tt * 32 + acc_row(a, h);
-    const float ov = Z[a] / dl[t];
+    const float ov = Z[a] * dl[t];
     bad |= t < tcount && !isfinite(ov);
     Ps[t * kLd + fcol] = ov;
   }
   if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
-  __syncthreads();
+  lds_barrier();
   // Whole 16-byte pieces of o rows from the staged block.
   constexpr int PPR = kD / EPV;
 #pragma unroll
@@ -1070,7 +1071,7 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
                          int32_t* __restrict__ chain_info, int b_lo, int nb, int64_t items) {
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     readout_block<TIn>(pl, q, o, den_eps, chain_info, b_lo, nb, item);
-    __syncthreads();   // LDS is restaged by the next item
+    lds_barrier();   // LDS is restaged by the next item
   }
 }
 

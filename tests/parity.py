@@ -46,7 +46,7 @@ def log_margins(tag, cfg, errs, elem, extra=None):
     path = os.environ.get("VLA_PARITY_LOG")
     if not path:
         return
-    rec = {"case": tag, "workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "d": cfg.d, "r": cfg.r,
+    rec = {"case": tag, "test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "d": cfg.d, "r": cfg.r,
            "storage": cfg.in_dtype, "tol": TOL[cfg.in_dtype], "normwise": errs, "elementwise": elem}
     rec.update(extra or {})
     with open(path, "a") as f:
