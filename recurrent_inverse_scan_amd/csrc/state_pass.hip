@@ -616,9 +616,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
   if (sg.pr && sg.conv && sg.conv[chain]) return;   // uniform: its segment starts have converged
   const int64_t pidx = chain * sg.nseg + seg;        // (chain, segment) record index
   if (sg.pr && sg.active && !sg.active[pidx]) return;   // uniform: this segment's start has not moved
-  // The first pass of the parallel-in-time schedule runs segments >= 1 from
-  // S = 0 without the cap: it yields their plain sums of v alpha_hat^T.
-  cap_on = (sg.pr && sg.uncapped_tail && seg > 0) ? 0 : cap_on;
   // The wave index is uniform; saying so keeps LDS destinations and buffer
   // descriptors derived from it in scalar registers.
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
@@ -1093,20 +1090,17 @@ vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restric
 // in the segment G_j = identity.  A segment's start is exact once every
 // earlier segment's is, so with nseg segments the iteration is exact after
 // nseg passes; it stops as soon as no start moves by more than tol (relative).
-// The first pass runs segments >= 1 from zero without the cap, and the first
-// sweep chains their plain sums with the cap applied at segment ends.
+// The first guesses come from the plain sums of v alpha_hat^T over four
+// sub-steps of every segment (a parallel kernel), chained from the true start
+// with the cap applied after each sub-step.
 
-// Segment starts for the first pass and the normaliser at every segment start
-// (n is linear: n0 plus the key sums of the blocks before).  One workgroup
-// per chain.
+// The normaliser at every segment start (n is linear: n0 plus the key sums
+// of the blocks before).  One workgroup per chain.
 __global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StatePlan pl, const float* __restrict__ n_init,
                                                              float* __restrict__ n_seg) {
   __shared__ float part[kMaxParaSegs][kD];
   const int64_t c = blockIdx.x;
   const int tid = threadIdx.x, G = pp.nseg;
-  float* sit = pp.Sit + c * G * kD * kD;
-  const float* s0 = pp.S_init + c * kD * kD;
-  for (int e = tid; e < G * kD * kD; e += 1024) sit[e] = e < kD * kD ? s0[e] : 0.f;
   if (tid == 0) pp.conv[c] = 0;
   const int sg = tid >> 6, f = tid & 63;
   if (sg < G) {
@@ -1120,6 +1114,72 @@ __global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StateP
     for (int j = 0; j < sg; ++j) n += part[j][f];
     n_seg[(c * G + sg) * kD + f] = n;
   }
+}
+
+// Plain sums sum_t v_t alpha_hat_t^T over the blocks of one sub-step of one
+// segment: workgroup (c, j, sub), four waves each owning a 32 x 32 tile.
+// Block rows are staged in LDS (the next block's held in registers while the
+// current one is summed); the products contract over tokens, so the operands
+// are LDS column reads: v exact in bf16 (three-term splits for fp32 storage),
+// alpha_hat through three-term splits.
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads) vla_para_sums_kernel(ParaPlan pp, StatePlan pl) {
+  constexpr int kVd = sizeof(TIn) == 2 ? 72 : 68;   // row stride of the v rows (elements)
+  __shared__ TIn Vs[kLb * kVd];
+  __shared__ float As[kLb * kLd];
+  const int G = pp.nseg;
+  const int sub = static_cast<int>(blockIdx.x % kParaSub);
+  const int j = static_cast<int>((blockIdx.x / kParaSub) % G);
+  const int64_t c = blockIdx.x / (kParaSub * G);
+  const int blo = pp.bnd[j], len = pp.bnd[j + 1] - blo;
+  const int nsub = len < kParaSub ? len : kParaSub;
+  if (sub >= nsub) return;   // uniform
+  const int b0 = blo + (sub * len) / nsub, b1 = blo + ((sub + 1) * len) / nsub;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, rl = lane & 31;
+  const int m = __builtin_amdgcn_readfirstlane(tid >> 6), ti = m >> 1, tj = m & 1;
+  const TIn* v = static_cast<const TIn*>(pl.v);
+  TileRegs<TIn> rv;
+  TileRegs<float> ra;
+  auto load = [&](int b) {
+    const int tcount = min(kLb, pl.T - b * kLb);
+    const int64_t row0 = c * pl.T + static_cast<int64_t>(b) * kLb;
+    rv.load(v + row0 * kD, tcount, tid);
+    ra.load(pl.alpha + row0 * kD, tcount, tid);
+  };
+  f32x16 X = zero16();
+  load(b0);
+  for (int b = b0; b < b1; ++b) {
+    rv.store_rows(Vs, kVd, tid);
+    ra.store_f32(As, tid);
+    lds_barrier();
+    if (b + 1 < b1) load(b + 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float ax[8];
+      TIn vx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 16 * kb + 8 * h + e;
+        vx[e] = Vs[t * kVd + ti * 32 + rl];
+        ax[e] = As[t * kLd + tj * 32 + rl];
+      }
+      const Split3 B = split3(ax);
+      if constexpr (sizeof(TIn) == 2) {
+        const uint4 pv = make_uint4(vx[0] | (static_cast<uint32_t>(vx[1]) << 16), vx[2] | (static_cast<uint32_t>(vx[3]) << 16),
+                                    vx[4] | (static_cast<uint32_t>(vx[5]) << 16), vx[6] | (static_cast<uint32_t>(vx[7]) << 16));
+        X = mma_split(__builtin_bit_cast(bf16x8, pv), B, X);
+      } else {
+        float fx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fx[e] = vx[e];
+        X = mma_split(split3(fx), B, X);
+      }
+    }
+    lds_barrier();
+  }
+  float* out = pp.P + ((c * G + j) * kParaSub + sub) * kD * kD;
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) out[(ti * 32 + acc_row(s2, h)) * kD + tj * 32 + rl] = X[s2];
 }
 
 constexpr int kSweepThreads = 512;                      // 8 waves: two per SIMD
@@ -1151,7 +1211,7 @@ __device__ __forceinline__ void para_sum8(float (&x)[8], float* red, int buf, in
 
 // The sweep over one chain's segments (one workgroup per chain, each thread
 // kSweepEpt consecutive entries of every 64 x 64 matrix).  first: the sweep
-// after the first pass (plain sums chained with the cap at segment ends).
+// before the first pass (plain sums chained with the cap at sub-step ends).
 __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan pp, int first) {
   constexpr int E = kSweepEpt;
   __shared__ float red[2 * kSweepWaves * 8];
@@ -1159,7 +1219,7 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
   const int64_t c = blockIdx.x;
   if (!first && pp.conv[c]) return;   // uniform
   const int tid = threadIdx.x, G = pp.nseg;
-  if (tid < G * 4) srec[tid] = pp.rec[c * G * 4 + tid];
+  if (!first && tid < G * 4) srec[tid] = pp.rec[c * G * 4 + tid];
   const int64_t base = c * G * kD * kD;
   const int e0 = tid * E;
   float nw[E], od[E], fj[E];
@@ -1175,8 +1235,10 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
   // Segment j's start and end are loaded one step ahead (they do not depend
   // on the sweep), so their latency hides behind step j - 1.
   float odn[E], fjn[E];
-  load(pp.Sit + base + e0, odn);   // segment 0's start (the true one)
-  load(pp.F + base + e0, fjn);
+  if (!first) {
+    load(pp.Sit + base + e0, odn);   // segment 0's start (the true one)
+    load(pp.F + base + e0, fjn);
+  }
   __syncthreads();   // srec
   int nred = 0;      // sums so far: consecutive sums alternate halves of red
   for (int j = 0; j < G; ++j) {
@@ -1185,51 +1247,38 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
       od[i] = odn[i];
       fj[i] = fjn[i];
     }
-    if (j + 1 < G) {
-      if (!first) load(pp.Sit + base + (j + 1) * kD * kD + e0, odn);   // the first sweep needs no starts
+    if (!first && j + 1 < G) {   // the first sweep reads neither starts nor ends
+      load(pp.Sit + base + (j + 1) * kD * kD + e0, odn);
       load(pp.F + base + (j + 1) * kD * kD + e0, fjn);
     }
-    const float lsum = srec[4 * j];
-    const bool fired = srec[4 * j + 1] > 0.f;
     float nx[E];
     float chg_j = 0.f;   // relative move of this segment's start
     if (first) {
-      if (j == 0) {   // the first segment ran from the true start, with the cap
+      // The segment's plain sums over its sub-steps added to the running
+      // state, the cap applied after each (each sub-step's sum is loaded one
+      // sub-step ahead).
+      const int len = pp.bnd[j + 1] - pp.bnd[j];
+      const int nsub = len < kParaSub ? len : kParaSub;
+      const float* pj = pp.P + (c * G + j) * kParaSub * kD * kD + e0;
+      float cur[E], nxt[E];
 #pragma unroll
-        for (int i = 0; i < E; ++i) nx[i] = fj[i];
-      } else {
-        // The first pass ran segment j from zero without the cap, so its
-        // snapshots are the plain sums from the segment start: add them to
-        // the running state in four steps, applying the cap after each.
-        constexpr int kSub = 4;
-        const int blo = pp.bnd[j], len = pp.bnd[j + 1] - blo;
-        const int nsub = len < kSub ? len : kSub;
-        float prev[E], nxt[E];
+      for (int i = 0; i < E; ++i) nx[i] = nw[i];
+      load(pj, nxt);
+      for (int sub = 0; sub < nsub; ++sub) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) cur[i] = nxt[i];
+        if (sub + 1 < nsub) load(pj + (sub + 1) * kD * kD, nxt);
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          prev[i] = 0.f;
-          nx[i] = nw[i];
+          nx[i] += cur[i];
+          x[0] = fmaf(nx[i], nx[i], x[0]);
         }
-        auto snap = [&](int sub) { return pp.Xsnap + (c * pp.nblk + blo + (sub * len) / nsub) * kD * kD + e0; };
-        if (nsub > 1) load(snap(1), nxt);   // each sub-step's snapshot is loaded one sub-step ahead
-        for (int sub = 1; sub <= nsub; ++sub) {
-          float cur[E];
+        para_sum8<1>(x, red, nred++ & 1, tid);
+        const float nrm = sqrtf(x[0]);
+        const float sc = (pp.cap_on && nrm > pp.cap) ? pp.cap / nrm : 1.f;
 #pragma unroll
-          for (int i = 0; i < E; ++i) cur[i] = sub < nsub ? nxt[i] : fj[i];
-          if (sub + 1 < nsub) load(snap(sub + 1), nxt);
-          float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < E; ++i) {
-            nx[i] += cur[i] - prev[i];
-            prev[i] = cur[i];
-            x[0] = fmaf(nx[i], nx[i], x[0]);
-          }
-          para_sum8<1>(x, red, nred++ & 1, tid);
-          const float nrm = sqrtf(x[0]);
-          const float sc = (pp.cap_on && nrm > pp.cap) ? pp.cap / nrm : 1.f;
-#pragma unroll
-          for (int i = 0; i < E; ++i) nx[i] *= sc;
-        }
+        for (int i = 0; i < E; ++i) nx[i] *= sc;
       }
     } else {
       float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1246,7 +1295,8 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
         x[6] = fmaf(fj[i], fj[i], x[6]);   // |F|^2
       }
       para_sum8<7>(x, red, nred++ & 1, tid);
-      const float sig = exp2f(lsum);
+      const float sig = exp2f(srec[4 * j]);   // the segment's total cap scale
+      const bool fired = srec[4 * j + 1] > 0.f;
       chg_j = sqrtf(x[2]) / fmaxf(sqrtf(x[3]), 1e-30f);
       chg_j = chg_j == chg_j ? chg_j : 3.0e38f;   // NaN counts as moved
       maxchg = fmaxf(maxchg, chg_j);
@@ -1272,10 +1322,11 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
         for (int i = 0; i < E; ++i) nx[i] = fmaf(sig, Ev[i], fj[i]);
       }
     }
-    // The next pass reruns a segment only if its start moved by more than
-    // tol_skip; a segment left out keeps the start its results came from.
-    // Segment 0 always starts at the true S and never reruns.
-    const bool run = j > 0 && (first || chg_j > pp.tol_skip);
+    // The first pass runs every segment; a later one reruns a segment only
+    // if its start moved by more than tol_skip (one left out keeps the start
+    // its results came from).  Segment 0 starts at the true S: after the
+    // first pass it never reruns.
+    const bool run = first || (j > 0 && chg_j > pp.tol_skip);
     if (tid == 0) pp.active[c * G + j] = run ? 1 : 0;
     if (run) {
       float4* dst = reinterpret_cast<float4*>(pp.Sit + base + j * kD * kD + e0);
@@ -1359,6 +1410,16 @@ hipError_t launch_state_prep(const StatePlan& pl, const ScanArgs& a, int chains,
     hipLaunchKernelGGL(vla_state_prep_kernel<float>, dim3(blocks), dim3(kThreads), state_prep_lds_bytes<float>(), stream,
                        pl, static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                        static_cast<const float*>(a.v), b_lo, nb, items);
+  return hipGetLastError();
+}
+
+hipError_t launch_para_sums(const ParaPlan& pp, const StatePlan& pl, hipStream_t stream) {
+  if (pp.chains <= 0 || pp.nseg < 1 || pp.nseg > kMaxParaSegs) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(pp.chains * pp.nseg * kParaSub));
+  if (pl.bf16)
+    hipLaunchKernelGGL(vla_para_sums_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, pp, pl);
+  else
+    hipLaunchKernelGGL(vla_para_sums_kernel<float>, grid, dim3(kThreads), 0, stream, pp, pl);
   return hipGetLastError();
 }
 

@@ -204,7 +204,7 @@ struct ChunkLayout {
   // Parallel-in-time state pass (additive update): segments per chain, and
   // its segment starts, segment ends, records, normalisers and flags.
   int para = 1;
-  size_t off_pSit = 0, off_pF = 0, off_prec = 0, off_pn = 0, off_pconv = 0, off_pact = 0;
+  size_t off_pSit = 0, off_pF = 0, off_prec = 0, off_pn = 0, off_pconv = 0, off_pact = 0, off_pP = 0;
   // Residual update's state pass (replaces the additive one's buffers).
   size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0, off_rex = 0;
 };
@@ -318,6 +318,7 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       cl.off_pn = off; off = align_up(off + C * G * 64 * 4);
       cl.off_pconv = off; off = align_up(off + C * 4);
       cl.off_pact = off; off = align_up(off + C * G * 4);
+      cl.off_pP = off; off = align_up(off + C * G * vla::kParaSub * d2 * 4);
     }
     cl.off_K = off; off = align_up(off + C * nb * 2304 * 4);
     cl.off_Kx = off; off = align_up(off + C * nb * d2 * 4);
@@ -738,11 +739,12 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   };
   const int nch = static_cast<int>(chains);
   if (cl.para > 1) {
-    // Parallel in time: prep of every block, a first pass of all segments
-    // (segment 0 from the true start; the others from zero, uncapped), then
-    // passes from the swept starts until they stop moving (at most
-    // kParaPasses; a chain that has not converged by then is recomputed by
-    // the sequential fallback below), then the readout of every block.
+    // Parallel in time: prep of every block, the plain sums over the
+    // segments' sub-steps and the first sweep's guesses of the segment
+    // starts, then passes of all segments from the swept starts until they
+    // stop moving (at most kParaPasses; a chain that has not converged by
+    // then is recomputed by the sequential fallback below), then the readout
+    // of every block.
     constexpr int kParaPasses = 8;
     const int G = cl.para;
     vla::ParaPlan pp{};
@@ -765,11 +767,15 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     // 4e-6 are not rerun.
     pp.tol = 4e-5f;
     pp.tol_skip = 4e-6f;
-    pp.Xsnap = sp.Xsnap;
-    pp.nblk = nblk;
+    pp.P = reinterpret_cast<float*>(ws + cl.off_pP);
     float* n_seg = reinterpret_cast<float*>(ws + cl.off_pn);
+    // (Running the sums on the side stream beside the prep kernel gained
+    // nothing: the prep kernel slowed by as much.)
     if ((e = vla::launch_state_prep(sp, a, nch, 0, nblk, 0, stream)) != hipSuccess) return hip_fail(e, "state prep launch");
     if ((e = vla::launch_para_init(pp, sp, pl.n_init, n_seg, stream)) != hipSuccess) return hip_fail(e, "para init launch");
+    if ((e = vla::launch_para_sums(pp, sp, stream)) != hipSuccess) return hip_fail(e, "para sums launch");
+    pp.iter_last = 0;
+    if ((e = vla::launch_para_sweep(pp, 1, stream)) != hipSuccess) return hip_fail(e, "para sweep launch");
     vla::ChainSeg sg{};
     sg.pr = 1;
     sg.nseg = G;
@@ -778,19 +784,16 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
     sg.n_in = n_seg;
     sg.F = reinterpret_cast<float*>(ws + cl.off_pF);
     sg.rec = reinterpret_cast<float*>(ws + cl.off_prec);
-    sg.uncapped_tail = 1;
-    sg.conv = nullptr;
+    sg.conv = pp.conv;
+    sg.active = pp.active;
     const int passes = std::min(G, kParaPasses);
-    for (int k = -1; k < passes; ++k) {
+    for (int k = 0; k < passes; ++k) {
       hipEvent_t ev0, ev1;
       next_timing(&ev0, &ev1);
       if ((e = vla::launch_state_chain(sp, sg, a, pl.chain_info, nch, stream, ev0, ev1)) != hipSuccess)
         return hip_fail(e, "state chain launch");
       pp.iter_last = k + 1 == passes ? 1 : 0;
-      if ((e = vla::launch_para_sweep(pp, k < 0 ? 1 : 0, stream)) != hipSuccess) return hip_fail(e, "para sweep launch");
-      sg.uncapped_tail = 0;
-      sg.conv = pp.conv;
-      sg.active = pp.active;
+      if ((e = vla::launch_para_sweep(pp, 0, stream)) != hipSuccess) return hip_fail(e, "para sweep launch");
     }
     if ((e = vla::launch_para_stats(pp, a.S_T, a.n_T, stats, stream)) != hipSuccess) return hip_fail(e, "para stats launch");
     if ((e = vla::launch_state_readout(sp, a, pl.chain_info, nch, 0, nblk, 0, stream)) != hipSuccess)

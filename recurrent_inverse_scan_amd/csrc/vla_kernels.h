@@ -110,7 +110,7 @@ struct ChainSeg {
   // [bnd[seg], bnd[seg + 1]), from S_in + (c * nseg + seg) * 4096 and
   // n_in + (c * nseg + seg) * 64, and leaves S at the segment's end in F and
   // (log2 sigma over the segment, cap fires, first cap step) in rec.
-  int pr, nseg, uncapped_tail;   // uncapped_tail: segments >= 1 run without the cap
+  int pr, nseg;
   int bnd[kMaxParaSegs + 1];
   float* F;               // [chains][nseg][64][64]
   float* rec;             // [chains][nseg][4]
@@ -133,11 +133,14 @@ struct ParaPlan {
   int32_t* chain_info;   // [chains][4]: the fallback flag is set if a chain does not converge
   float cap, tol, tol_skip;
   int cap_on;
-  const float* Xsnap;    // [chains][nblk][64][64]: S at each block start from the last pass
-  int nblk;
+  float* P;              // [chains][nseg][kParaSub][64][64]: plain sums of v alpha_hat^T over the
+                         // sub-steps of each segment (the first sweep's input)
 };
+constexpr int kParaSub = 4;   // sub-steps per segment of the first sweep
 hipError_t launch_para_init(const ParaPlan& pp, const StatePlan& pl, const float* n_init, float* n_seg,
                             hipStream_t stream);
+// The plain sums pp.P (one workgroup per chain, segment and sub-step).
+hipError_t launch_para_sums(const ParaPlan& pp, const StatePlan& pl, hipStream_t stream);
 hipError_t launch_para_sweep(const ParaPlan& pp, int first, hipStream_t stream);
 hipError_t launch_para_stats(const ParaPlan& pp, const float* S_T, const float* n_T, int32_t* stats,
                              hipStream_t stream);

@@ -435,12 +435,13 @@ def test_timing_hook_records_the_chain_kernel():
     assert len(ms) == 6 and all(t > 0 for t in ms), ms
     timing_enable(True)
     try:
-        # parallel in time, 5 segments: a first pass, then at most 5 more
+        # parallel in time, 5 segments: at most 5 passes (then the segment
+        # starts are exact)
         _gpu(x, cfg, schedule="chunked", para_segments=5)
         ms = timing_collect()
     finally:
         timing_enable(False)
-    assert len(ms) == 6 and all(t > 0 for t in ms), ms
+    assert len(ms) == 5 and all(t > 0 for t in ms), ms
 
 
 # Short calls (T <= 16 tokens, the decode-like case) run the full scan with
