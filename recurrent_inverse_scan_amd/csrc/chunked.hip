@@ -22,9 +22,10 @@
 //                           each period's total, in parallel over elements
 //   vla_chunk_chain_kernel  per chain and column block, sequential over
 //                           periods, fp64: (N, D) at every period start
-//   vla_chunk_start_kernel  per chunk, fp64: A_c by Gauss-Jordan elimination
-//                           of [ D_c^T | N_p^T ]; a non-positive pivot flags
-//                           the chain for the sequential fallback
+//   vla_chunk_start_kernel  per chunk, fp64: A_c by blocked Gauss-Jordan
+//                           elimination of [ D_c^T | N_p^T ] on the fp64
+//                           matrix cores; a non-positive pivot flags the
+//                           chain for the sequential fallback
 #include "vla_common.h"
 #include "vla_kernels.h"
 #include "vla_seq.h"
@@ -251,121 +252,180 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
 }
 
 // ---- chunk-start inverses ---------------------------------------------------
-// One workgroup per (chain, chunk).  D_c = D_p + Gpre_c N_p, then Gauss-Jordan
-// elimination without pivoting turns [ D_c^T | N_p^T ] (64 x 128, thread t
-// owning rows 4*(t/16).. and columns 8*(t%16)..) into [ I | A_c^T ].
+// One workgroup (four waves) per (chain, chunk).  W = [ D_c^T | N_p^T ] (64 x
+// 128, fp64) lives in registers as 16 x 16 matrix-core tiles: wave w holds
+// rows 16 w .. 16 w + 15, tiles ct = 0..3 of the left block and 4..7 of the
+// right.  D_c^T = D_p^T + N_p^T Gpre_c^T on the fp64 matrix cores.  Gauss-
+// Jordan elimination without pivoting then turns W into [ I | A_c^T ], in
+// panels of 16 columns: wave p inverts its pivot block W11 (one pivot at a
+// time, with cross-lane broadcasts) and forms R = W11^-1 W[panel rows]; every
+// other wave w then subtracts C_w R (C_w its rows of the panel's columns).
+// Both products run on the matrix cores.  A non-positive or non-finite pivot
+// flags the chain for the sequential fallback.
+//
+// v_mfma_f64_16x16x4f64, wave64, D = A B + C with A 16x4, B 4x16:
+//   A operand  lane l holds A[l % 16][l / 16]
+//   B operand  lane l holds B[l / 16][l % 16]
+//   C / D      lane l slot i holds D[4 i + l / 16][l % 16]
+typedef double d4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ d4 mfma64(double a, double b, d4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+constexpr int kRPad = 2 * kD + 1;   // row stride (doubles) of the finished panel rows R
+
+// Panel P of the elimination (compile time, so every tile index is too).
+// Wave P inverts its pivot block W11 by Gauss-Jordan on [ W11 | I ] (one
+// pivot at a time, two tiles), then forms R = W11^-1 W[panel rows] for the
+// tiles right of the panel on the matrix cores; the other waves subtract
+// C_w R.  sI is the wave's 16 x 17 staging tile for transposed operand reads.
+template <int P>
+__device__ __forceinline__ void gj_panel(d4 (&W)[8], int w, int g, int col, double* sR, double* sI, bool& ok) {
+  if (w == P) {   // wave-uniform
+    d4 inv_t;     // becomes W11^-1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv_t[i] = (4 * i + g == col) ? 1.0 : 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      // Row k of the block sits in lanes 16 (k % 4) .., slot k / 4; the
+      // pivot is its entry in column k.
+      const double piv = readlane_d(W[P][k >> 2], 16 * (k & 3) + k);
+      ok = ok && (piv > 0.0) && isfinite(piv);
+      // 1/piv: the hardware reciprocal refined by one Newton step.
+      double inv = __builtin_amdgcn_rcp(piv);
+      inv = fma(inv, fma(-piv, inv, 1.0), inv);
+      double f[4];   // column k of this lane's rows 4 i + g
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = __shfl(W[P][i], 16 * g + k, 64);
+      const double ra = __shfl(W[P][k >> 2], 16 * (k & 3) + col, 64) * inv;
+      const double rb = __shfl(inv_t[k >> 2], 16 * (k & 3) + col, 64) * inv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool own = 4 * i + g == k;
+        W[P][i] = own ? ra : fma(-f[i], ra, W[P][i]);
+        inv_t[i] = own ? rb : fma(-f[i], rb, inv_t[i]);
+      }
+    }
+    // R = W11^-1 W[panel rows] tile by tile: the A operand of k step kk is
+    // W11^-1[l % 16][4 kk + l / 16] (a transposed read), the B operand is
+    // rows 4 kk + l / 16 of the tile, which is slot kk of this lane.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sI[(4 * i + g) * 17 + col] = inv_t[i];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // one wave: its own LDS writes first
+    double a[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = sI[col * 17 + 4 * kk + g];
+#pragma unroll
+    for (int ct = P + 1; ct < 8; ++ct) {
+      d4 r = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) r = mfma64(a[kk], W[ct][kk], r);
+      W[ct] = r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sR[(4 * i + g) * kRPad + 16 * ct + col] = r[i];
+    }
+  } else {
+    // This wave's rows of the panel's columns, staged for the transposed read.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sI[(4 * i + g) * 17 + col] = W[P][i];
+  }
+  __syncthreads();
+  if (w != P) {
+    double a[4];   // A operand of k step kk: -C[l % 16][4 kk + l / 16]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = -sI[col * 17 + 4 * kk + g];
+#pragma unroll
+    for (int ct = P + 1; ct < 8; ++ct)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) W[ct] = mfma64(a[kk], sR[(4 * kk + g) * kRPad + 16 * ct + col], W[ct]);
+  }
+  __syncthreads();   // sR and sI are rewritten by the next panel
+}
+
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
                        int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo, int c_cnt) {
-  // 65 KiB of LDS: Gpre^T and N_p for the product; afterwards the pivot row
-  // and column buffers reuse the N_p half, and the result block the first half.
-  __shared__ double smem[2 * kD * kPad];
-  double* sA = smem;                 // rows of kPad doubles
-  double* sB = smem + kD * kPad;
-  // Pivot rows at padded positions rbx(j) = j + 2 (j / 32): the 16 threads
-  // reading 8-double runs 8 cb + jj at once hit distinct banks.
-  double (*rowbuf)[2 * kD + 8] = reinterpret_cast<double (*)[2 * kD + 8]>(sB);
-  double (*colbuf)[kD] = reinterpret_cast<double (*)[kD]>(sB + 2 * (2 * kD + 8));
-  auto rbx = [](int j) { return j + 2 * (j >> 5); };
+  // 66.6 KiB of LDS: N_p and Gpre_c rows (padded); after the product the
+  // second half holds the finished panel rows and the per-wave panel-column
+  // tiles, and at the end the first half holds the result block.
+  __shared__ double sN[kD * kPad];
+  __shared__ double sG[kD * kPad];
+  double* sR = sG;                          // [16][kRPad]
+  double* sIw = sG + 16 * kRPad;            // [4 waves][16][17]
   const int64_t chain = blockIdx.x / c_cnt;
   const int c = c_lo + static_cast<int>(blockIdx.x % c_cnt);
   const int p = period_of(c, o, q);
-  const int t = threadIdx.x, rb = t >> 4, cb = t & 15;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const double* Np = ND + (chain * nperiods + p) * 2 * kD * kD;
   const double* Dp = Np + kD * kD;
   const double* gp = Gpre + (chain * nchunks + c) * kD * kD;
   // The first chunk of a period has no Gram prefix: D_c = D_p.
   const bool has_pre = c > 0 && (q == 0 || (o + c) % q != 0);
 
-  for (int e = t; e < kD * kD; e += kChunkThreads) {
-    const int i = e / kD, j = e % kD;
-    if (has_pre) sA[j * kPad + i] = gp[e];
-    sB[i * kPad + j] = Np[e];
+  // Every global load first (one round of latency), then the LDS stores.
+  constexpr int kPer = kD * kD / kChunkThreads;   // 16 elements per thread
+  double rn[kPer], rg[kPer], dp[16];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    rn[j] = Np[t + kChunkThreads * j];
+    rg[j] = has_pre ? gp[t + kChunkThreads * j] : 0.0;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)   // D_p^T, this lane's entries of the left block
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dp[4 * ct + i] = Dp[(16 * ct + col) * kD + 16 * w + 4 * i + g];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = t + kChunkThreads * j, i = e / kD, jj = e % kD;
+    sN[i * kPad + jj] = rn[j];
+    if (has_pre) sG[i * kPad + jj] = rg[j];
   }
   __syncthreads();
 
-  // W[i][j] for i in 4rb..4rb+3, j in 8cb..8cb+7.
-  double W[4][8];
-  if (cb < 8) {
-    // Left block: W[i][j] = D_c[j][i] = D_p[j][i] + sum_m Gpre[j][m] N_p[m][i].
+  d4 W[8];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+  for (int qb = 0; qb < 4; ++qb) {   // right block: N_p^T
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = Dp[(8 * cb + jj) * kD + 4 * rb + ii];
-    for (int m = 0; has_pre && m < kD; ++m) {
-      double gv[8], nv[4];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) gv[jj] = sA[m * kPad + 8 * cb + jj];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) nv[ii] = sB[m * kPad + 4 * rb + ii];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(gv[jj], nv[ii], W[ii][jj]);
-    }
-  } else {
-    // Right block: W[i][64 + j] = N_p[j][i].
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) W[ii][jj] = sB[(8 * (cb - 8) + jj) * kPad + 4 * rb + ii];
+    for (int i = 0; i < 4; ++i) W[4 + qb][i] = sN[(16 * qb + col) * kPad + 16 * w + 4 * i + g];
   }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {   // left block: D_p^T + N_p^T Gpre_c^T
+    d4 acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = dp[4 * ct + i];
+    if (has_pre) {
+#pragma unroll 4
+      for (int kk = 0; kk < kD / 4; ++kk)
+        acc = mfma64(sN[(4 * kk + g) * kPad + 16 * w + col], sG[(16 * ct + col) * kPad + 4 * kk + g], acc);
+    }
+    W[ct] = acc;
+  }
+  __syncthreads();   // sG is reused below
 
-  __syncthreads();   // every thread is done reading sB before it holds pivots
-  // Pivot k = 8 k8 + kk: unrolled over kk, so the pivot row's place in the
-  // owner's block (kk % 4) and the pivot column's (kk) are compile-time.
   bool ok = true;
-  for (int k8 = 0; k8 < kD / 8; ++k8) {
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = 8 * k8 + kk;
-      const int par = kk & 1;
-      const bool row_owner = rb == 2 * k8 + (kk >> 2);
-      if (row_owner) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) rowbuf[par][rbx(8 * cb + jj)] = W[kk & 3][jj];
-      }
-      if (cb == k8) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) colbuf[par][4 * rb + ii] = W[ii][kk];
-      }
-      __syncthreads();
-      const double piv = rowbuf[par][rbx(k)];
-      ok = ok && (piv > 0.0) && isfinite(piv);
-      // 1/piv: the hardware reciprocal refined by one Newton step.
-      double inv = __builtin_amdgcn_rcp(piv);
-      inv = fma(inv, fma(-piv, inv, 1.0), inv);
-      double rv[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) rv[jj] = rowbuf[par][rbx(8 * cb + jj)] * inv;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        if (row_owner && ii == (kk & 3)) {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) W[ii][jj] = rv[jj];
-        } else {
-          const double f = colbuf[par][4 * rb + ii];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) W[ii][jj] = fma(-f, rv[jj], W[ii][jj]);
-        }
-      }
-    }
-  }
-  if (!ok && t == 0) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
+  double* sI = sIw + w * 16 * 17;
+  gj_panel<0>(W, w, g, col, sR, sI, ok);
+  gj_panel<1>(W, w, g, col, sR, sI, ok);
+  gj_panel<2>(W, w, g, col, sR, sI, ok);
+  gj_panel<3>(W, w, g, col, sR, sI, ok);
+  if (!ok && lane == 0) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
 
-  // Symmetrise the result block (A_c^T, equal to A_c in exact arithmetic).
-  __syncthreads();
-  if (cb >= 8) {
+  // The result block (A_c^T, equal to A_c in exact arithmetic), symmetrised.
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+  for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sA[(4 * rb + ii) * kPad + 8 * (cb - 8) + jj] = W[ii][jj];
-  }
+    for (int i = 0; i < 4; ++i) sN[(16 * w + 4 * i + g) * kPad + 16 * qb + col] = W[4 + qb][i];
   __syncthreads();
   float* ac = Ac + (chain * nchunks + c) * kD * kD;
   for (int e = t; e < kD * kD; e += kChunkThreads) {
     const int i = e / kD, j = e % kD;
-    ac[e] = static_cast<float>(0.5 * (sA[i * kPad + j] + sA[j * kPad + i]));
+    ac[e] = static_cast<float>(0.5 * (sN[i * kPad + j] + sN[j * kPad + i]));
   }
 }
 
