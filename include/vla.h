@@ -109,7 +109,9 @@ typedef struct {
                             parallel from guessed starts, corrected by sweeps
                             until the starts stop moving; 1 = one pass per chain
                             (the segmented pipeline above); 0 = library picks
-                            (min(16, 256 / chains), at least 2 blocks per segment) */
+                            (min(16, 256 / chains, blocks / 32), blocks of 64
+                            tokens per chain; below 2 means one pass); an
+                            explicit count is capped at blocks / 2 */
 } vla_scan_params_t;
 
 /* Defaults: B = H = T = 0, d = 64, r = 1, f32, eps = 1e-6, no nudge, no cap,
