@@ -278,7 +278,7 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
     gv = mma_split(va, operand8(Vb + (tj * 32 + rl) * kRd + c0), gv);
     const Split3 aa = operand8(Af + (ti * 32 + rl) * kLd + c0);
     ga = mma_split(aa, operand8(Af + (tj * 32 + rl) * kLd + c0), ga);
-    pk = mma_split(operand8(Qb + (ti * 32 + rl) * kRd + c0), operand8(Kb + (tj * 32 + rl) * kRd + c0), pk);   // q_t . k_s
+    pk = mma_split(operand8(Kb + (ti * 32 + rl) * kRd + c0), operand8(Qb + (tj * 32 + rl) * kRd + c0), pk);   // k_s . q_t
     if (b > 0) {
       xv = mma_split(va, operand8(Vp + (tj * 32 + rl) * kRd + c0), xv);
       xa = mma_split(aa, operand8(Ap + (tj * 32 + rl) * kLd + c0), xa);
@@ -319,34 +319,103 @@ __device__ __forceinline__ void prep_block(const StatePlan& pl, const TIn* __res
 #pragma unroll
     for (int s = 0; s < 16; ++s) Xout[(ti * 32 + acc_row(s, h)) * kLb + col] = xv[s] * xa[s];
   }
-  lds_barrier();   // Af and Ap are free from here on
+  // This wave's tile of K = (v.v) o (alpha.alpha): rows s = 32 ti + slot
+  // rows, columns 32 tj + lane; K is symmetric, so lane (n, h) holds row
+  // t = 32 tj + n of K over s in block ti, down its slots.  The tile of pk
+  // is k_s . q_t in the same arrangement.
+  float Kt[16];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int t = ti * 32 + acc_row(s, h);
-    Ap[t * kLd + col] = (col <= t) ? pk[s] : 0.f;
-    Af[t * kLd + col] = gv[s] * ga[s];
-  }
-  lds_barrier();
-  // Rows of K: exclusive prefix sums straight into the triangle (row t's
-  // j <= t at t(t+1)/2 + j), K(t,t) and the row totals; rows of the masked
-  // q.k products: their sums.  Wave w takes rows 16 w .. 16 w + 15, lane s
-  // column s, with DPP scans.
-  if (tid < kLb) pack[kPackKs + tid] = (ksum_part[0][tid] + ksum_part[1][tid]) + (ksum_part[2][tid] + ksum_part[3][tid]);
-#pragma unroll 4
-  for (int rr = 0; rr < 16; ++rr) {
-    const int t = w * 16 + rr;   // wave-uniform
-    const float x = Af[t * kLd + lane];
-    const float inc = wave_incl_scan(x, lane);
-    if (lane <= t) pack[t * (t + 1) / 2 + lane] = inc - x;
-    const float tot = readlane_f(inc, kLb - 1);
-    const float e_t = readlane_f(x, t);
-    const float ldt = wave_sum(Ap[t * kLd + lane]);
-    if (lane == 0) {
-      pack[kPackE + t] = e_t;
-      pack[kPackTot + t] = tot;
-      if (t < tcount) pl.ld[row0 + t] = ldt;
+  for (int s2 = 0; s2 < 16; ++s2) Kt[s2] = gv[s2] * ga[s2];
+  __shared__ float sX[16 * 64];       // tile (1, 1)'s prefix over s < 32, [slot][lane]
+  __shared__ float sTot[kLb], sLd[kLb];   // row sums over s >= 32
+  const int trow = tj * 32 + rl;      // this lane's row t for the row sums
+  {
+    float tp = 0.f, lp = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      tp += Kt[s2];
+      lp += (ti * 32 + acc_row(s2, h) <= trow) ? pk[s2] : 0.f;
+    }
+    tp += __shfl_xor(tp, 32);
+    lp += __shfl_xor(lp, 32);
+    if (ti == 1 && h == 0) {
+      sTot[trow] = tp;
+      sLd[trow] = lp;
+    }
+    if (ti == tj) {   // the diagonal K(t, t)
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2)
+        if (acc_row(s2, h) == rl) pack[kPackE + ti * 32 + rl] = Kt[s2];
+    }
+    gv = zero16();   // reused below for the prefix tiles
+    if (ti == 0) {
+      lds_barrier();
+      if (h == 0) {
+        pack[kPackTot + trow] = tp + (tj == 1 ? sTot[trow] : 0.f);
+        if (trow < tcount) pl.ld[row0 + trow] = lp + (tj == 1 ? sLd[trow] : 0.f);
+      }
+    } else {
+      lds_barrier();
     }
   }
+  // Exclusive row prefixes CK[t][j] = sum_{s<j} K[t][s] on the matrix cores:
+  // the K tile, read as the A operand (slots 8 g .. 8 g + 7 as k step g),
+  // gives rows t = 32 tj + lane over s = 32 ti + 16 g + 8 (e / 4) + 4 h +
+  // e % 4; the B operand is the 0/1 matrix [s < j] in the same k order.
+  // Row block 0 needs s < 32 only (wave (0, 0)); row block 1 takes s < 32
+  // from wave (0, 1) and s >= 32 from wave (1, 1).
+  auto bmask = [&](int sb, int jb, int g) {   // [s < j], s = 32 sb + k order, j = 32 jb + lane
+    uint32_t wd[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int e = 2 * e2 + hh;
+        const int sx = 32 * sb + 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
+        x |= (sx < 32 * jb + rl) ? (0x3F80u << (16 * hh)) : 0u;
+      }
+      wd[e2] = x;
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+  };
+  const auto rpack = make_rsrc(pack, kPackFloats * 4);
+  auto store_tri = [&](const f32x16& D, int rb, int jb) {   // pack row t, column j <= t
+    const int j = 32 * jb + rl;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const int t = 32 * rb + acc_row(s2, h);
+      if (j <= t) buf_store_f32(rpack, 4 * (t * (t + 1) / 2 + j), D[s2]);
+    }
+  };
+  if (!(ti == 1 && tj == 0)) {
+    float k0[8], k1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      k0[e] = Kt[e];
+      k1[e] = Kt[8 + e];
+    }
+    const Split3 A0 = split3(k0), A1 = split3(k1);
+    if (ti == 0) {
+      f32x16 D = mma_split(A1, bmask(0, 0, 1), mma_split(A0, bmask(0, 0, 0), zero16()));
+      store_tri(D, tj, 0);   // tile (tj, 0): complete
+      if (tj == 1) {
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+        D = mma_split(A1, ones, mma_split(A0, ones, zero16()));
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) sX[s2 * 64 + lane] = D[s2];
+      }
+    } else {
+      gv = mma_split(A1, bmask(1, 1, 1), mma_split(A0, bmask(1, 1, 0), zero16()));
+    }
+  }
+  lds_barrier();
+  if (ti == 1 && tj == 1) {
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) gv[s2] += sX[s2 * 64 + lane];
+    store_tri(gv, 1, 1);
+  }
+  if (tid < kLb) pack[kPackKs + tid] = (ksum_part[0][tid] + ksum_part[1][tid]) + (ksum_part[2][tid] + ksum_part[3][tid]);
 }
 
 // Blocks [b_lo, b_lo + nb) of every chain; a grid smaller than chains * nb
