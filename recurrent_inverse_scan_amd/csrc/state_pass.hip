@@ -993,8 +993,20 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
 template <typename TIn>
 struct ReadoutLds {
   static constexpr int kQd = sizeof(TIn) == 2 ? 72 : 68;   // row stride (elements) of q and v^T rows
-  static constexpr size_t kBytes = 2 * kLb * kQd * sizeof(TIn) + 3 * kLb * kLd * sizeof(float) + 4 * kLb * sizeof(float);
+  // q rows and v^T, then two swizzled [64][64] fp32 matrices (S_b rows, which
+  // later stage the outputs; alpha_hat rows, which later hold P'), then four
+  // vectors: 51.4 KiB with bf16 storage, three workgroups per compute unit.
+  static constexpr size_t kBytes = 2 * kLb * kQd * sizeof(TIn) + 2 * kLb * kD * sizeof(float) + 4 * kLb * sizeof(float);
 };
+
+// Eight consecutive values (columns c0 .. c0 + 7, c0 a multiple of 8) of row r
+// of a swizzled [64][64] fp32 LDS matrix, as a three-term split.
+__device__ __forceinline__ Split3 swz_operand8(const float* m, int r, int c0) {
+  const float4 a = *reinterpret_cast<const float4*>(m + swz32(r, c0));
+  const float4 b = *reinterpret_cast<const float4*>(m + swz32(r, c0 + 4));
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split3(x);
+}
 
 template <typename TIn>
 __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __restrict__ q, TIn* __restrict__ o,
@@ -1004,12 +1016,12 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   extern __shared__ float4 smem4[];
   TIn* Qs = reinterpret_cast<TIn*>(smem4);          // [64 t][kQd] q rows
   TIn* Vt = Qs + kLb * kQd;                         // [64 i][kQd] v transposed (rows = features)
-  float* Xs = reinterpret_cast<float*>(Vt + kD * kQd);   // [64 i][kLd] S_b rows
-  float* As = Xs + kD * kLd;                        // [64 s][kLd] alpha_hat rows
-  float* Ps = As + kLb * kLd;                       // [64 t][kLd] P'
-  float* wl = Ps + kLb * kLd;                       // [64] log2 sigma_{s-1} (block-local)
+  float* Xs = reinterpret_cast<float*>(Vt + kD * kQd);   // swizzled [64 i][64] S_b rows; later the outputs
+  float* As = Xs + kD * kD;                         // swizzled [64 s][64] alpha_hat rows; later P'
+  float* Ps = As;
+  float* wl = As + kLb * kD;                        // [64] log2 sigma_{s-1} (block-local)
   float* sl = wl + kLb;                             // [64] log2 sigma_t
-  float* dl = sl + kLb;                             // [64] den_t
+  float* dl = sl + kLb;                             // [64] 1 / den_t
   float* nl = dl + kLb;                             // [64] n at the block start
   const int64_t chain = item / nb;
   const int b = b_lo + static_cast<int>(item % nb);
@@ -1045,8 +1057,12 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
 #pragma unroll
       for (int k = 0; k < EPV; ++k) Vt[(c + k) * kQd + r] = xe[k];
     }
-    rx.store_f32(Xs, tid);
-    ra.store_f32(As, tid);
+#pragma unroll
+    for (int j = 0; j < TileRegs<float>::N; ++j) {
+      const int e = tid + j * kThreads, r = e / TileRegs<float>::PPR, c = (e % TileRegs<float>::PPR) * 4;
+      *reinterpret_cast<uint4*>(Xs + swz32(r, c)) = rx.r[j];
+      *reinterpret_cast<uint4*>(As + swz32(r, c)) = ra.r[j];
+    }
     if (tid < kLb) {
       wl[tid] = w0;
       sl[tid] = w1;
@@ -1063,19 +1079,12 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   const int tt = w >> 1, ti = w & 1;   // this wave's output tile; its P' tile is (tt, ts = ti)
   const int rl = lane & 31;
   // P'(tt, ts) for ts <= tt: A = q rows of tile tt, B[k=j][n=s] = alpha_hat[s][j].
+  f32x16 P = zero16();
   if (ti <= tt) {
-    f32x16 P = zero16();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const auto a = operand8(Qs + (tt * 32 + rl) * kQd + 16 * kb + 8 * h);
-      const Split3 bb = operand8(As + (ti * 32 + rl) * kLd + 16 * kb + 8 * h);
-      P = mma_split(a, bb, P);
-    }
-    const int s = ti * 32 + rl;
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const int t = tt * 32 + acc_row(a, h);
-      Ps[t * kLd + s] = (s <= t) ? P[a] * exp2f(sl[t] - wl[s]) : 0.f;
+      P = mma_split(a, swz_operand8(As, ti * 32 + rl, 16 * kb + 8 * h), P);
     }
   }
   // sigma_t S_b q_t: A = q rows, B[k=j][n=i] = S_b[i][j].
@@ -1083,30 +1092,38 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const auto a = operand8(Qs + (tt * 32 + rl) * kQd + 16 * kb + 8 * h);
-    const Split3 bb = operand8(Xs + (ti * 32 + rl) * kLd + 16 * kb + 8 * h);
-    Z = mma_split(a, bb, Z);
+    Z = mma_split(a, swz_operand8(Xs, ti * 32 + rl, 16 * kb + 8 * h), Z);
   }
 #pragma unroll
   for (int a = 0; a < 16; ++a) Z[a] *= exp2f(sl[tt * 32 + acc_row(a, h)]);
+  lds_barrier();   // every wave is done with alpha_hat and S_b; P' takes alpha_hat's place
+  if (ti <= tt) {
+    const int s = ti * 32 + rl;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int t = tt * 32 + acc_row(a, h);
+      Ps[swz32(t, s)] = (s <= t) ? P[a] * exp2f(sl[t] - wl[s]) : 0.f;
+    }
+  }
   lds_barrier();
   // + sum_s P'[t][s] v_s over the tiles ts <= tt: A = P' rows, B[k=s][n=i] = v^T[i][s].
   for (int ts = 0; ts <= tt; ++ts) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const Split3 a = operand8(Ps + (tt * 32 + rl) * kLd + ts * 32 + 16 * kb + 8 * h);
+      const Split3 a = swz_operand8(Ps, tt * 32 + rl, ts * 32 + 16 * kb + 8 * h);
       const auto bb = operand8(Vt + (ti * 32 + rl) * kQd + ts * 32 + 16 * kb + 8 * h);
       Z = mma_split(a, bb, Z);
     }
   }
   bool bad = false;
   const int fcol = ti * 32 + rl;
-  lds_barrier();   // every wave is done reading P'; its rows take the outputs now
+  // The outputs are staged in S_b's place (free since the barrier above).
 #pragma unroll
   for (int a = 0; a < 16; ++a) {
     const int t = tt * 32 + acc_row(a, h);
     const float ov = Z[a] * dl[t];
     bad |= t < tcount && !isfinite(ov);
-    Ps[t * kLd + fcol] = ov;
+    Xs[swz32(t, fcol)] = ov;
   }
   if (__any(bad) && lane == 0) atomicOr(chain_info + chain * 4 + kInfoNonfinite, 1);
   lds_barrier();
@@ -1116,11 +1133,13 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   for (int e = tid; e < kLb * PPR; e += kThreads) {
     const int t = e / PPR, c = (e % PPR) * EPV;
     if (t >= tcount) continue;
-    const float* src = Ps + t * kLd + c;
     uint4 wv;
     if constexpr (EPV == 4) {
-      wv = *reinterpret_cast<const uint4*>(src);
+      wv = *reinterpret_cast<const uint4*>(Xs + swz32(t, c));
     } else {
+      const float4 lo = *reinterpret_cast<const float4*>(Xs + swz32(t, c));
+      const float4 hi = *reinterpret_cast<const float4*>(Xs + swz32(t, c + 4));
+      const float src[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       uint32_t hw[4];
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2)
@@ -1131,8 +1150,10 @@ __device__ __forceinline__ void readout_block(const StatePlan& pl, const TIn* __
   }
 }
 
+// Three workgroups per compute unit with bf16 storage (51.4 KiB of LDS
+// each): the register budget is held to three waves per SIMD.
 template <typename TIn>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 vla_state_readout_kernel(StatePlan pl, const TIn* __restrict__ q, TIn* __restrict__ o, float den_eps,
                          int32_t* __restrict__ chain_info, int b_lo, int nb, int64_t items) {
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
