@@ -1212,8 +1212,11 @@ __global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StateP
 // current one is summed); the products contract over tokens, so the operands
 // are LDS column reads: v exact in bf16 (three-term splits for fp32 storage),
 // alpha_hat through three-term splits.
+// (Four waves per SIMD: the 1,024 workgroups of 16 chains x 16 segments x 4
+// sub-steps then run in one round on 256 compute units.)
 template <typename TIn>
-__global__ void __launch_bounds__(kThreads) vla_para_sums_kernel(ParaPlan pp, StatePlan pl) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+vla_para_sums_kernel(ParaPlan pp, StatePlan pl) {
   constexpr int kVd = sizeof(TIn) == 2 ? 72 : 68;   // row stride of the v rows (elements)
   __shared__ TIn Vs[kLb * kVd];
   __shared__ float As[kLb * kLd];
