@@ -161,21 +161,24 @@ vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, do
 // The four waves of a workgroup each take a quarter of the product's inner
 // dimension (thread (q, rb, c): rows 4 rb.. of column c, inner indices
 // 16 q..); the waves' partial sums meet in LDS, where the first wave, which
-// owns (N, D), adds them.  The period's Gram total is staged in LDS
-// (transposed) and the next one is loaded while the current product runs.
+// owns (N, D), adds them.  The period's Gram total is symmetric, so it is
+// staged in LDS as it is stored (row m serves as column m: no transposed
+// stores); the next one is loaded while the current product runs, and the
+// LDS buffers alternate between periods, so a period needs two barriers.
 constexpr int kNdSplit = 16;
 constexpr int kNdCols = kD / kNdSplit;   // 4
-// fp64 LDS rows padded to 65 doubles: a column of a row-major 64x64 block
-// then spreads over the banks instead of landing on one (transposed stores,
-// column reads).
+// fp64 LDS rows of 68 doubles: 16-byte aligned, so a thread's four
+// consecutive entries move as two 16-byte accesses.
+constexpr int kPadG = kD + 4;
+// fp64 LDS rows padded to 65 doubles (the chunk-start kernel's staging).
 constexpr int kPad = kD + 1;
 
 __global__ void __launch_bounds__(kChunkThreads)
 vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
                        int nperiods, double eps) {
-  __shared__ double sG[kD * kPad];          // sG[m*kPad + i] = Gtot[i][m]
-  __shared__ double sN[kD * kNdCols];       // sN[m*kNdCols + c] = N[m][c0 + c]
-  __shared__ double sP[4][kD * kNdCols];    // partial products of each wave
+  __shared__ double sG[2][kD * kPadG];         // sG[m * kPadG + i] = Gtot[m][i] = Gtot[i][m]
+  __shared__ double sN[2][kD * kNdCols];       // sN[m * kNdCols + c] = N[m][c0 + c]
+  __shared__ double sP[2][4][kD * kNdCols];    // partial products of each wave
   const int64_t chain = blockIdx.x / kNdSplit;
   const int c0 = (blockIdx.x % kNdSplit) * kNdCols;
   const int t = threadIdx.x, q = t >> 6, rb = (t & 63) >> 2, cc = t & 3;
@@ -209,34 +212,38 @@ vla_chunk_chain_kernel(const double* __restrict__ Gtot, const float* __restrict_
       for (int j = 0; j < 4; ++j) g[4 * i + j] = gt[(4 * sr + i) * kD + 4 * sc + j];
   };
   auto advance = [&](double (&g)[16], int p) {
-    __syncthreads();   // the previous step is done with sG, sN and sP
+    // Buffers of parity p & 1: their last readers were in period p - 2, which
+    // every wave finished before the previous period's second barrier.
+    double* G = sG[p & 1];
+    double* Ns = sN[p & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sG[(4 * sc + j) * kPad + 4 * sr + i] = g[4 * i + j];
+      for (int j = 0; j < 4; ++j) G[(4 * sr + i) * kPadG + 4 * sc + j] = g[4 * i + j];
     if (owner) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sN[(4 * rb + i) * kNdCols + cc] = N[i];
+      for (int i = 0; i < 4; ++i) Ns[(4 * rb + i) * kNdCols + cc] = N[i];
     }
     __syncthreads();
     load_g(g, p + 2);
     double part[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
     for (int m = 16 * q; m < 16 * q + 16; ++m) {
-      const double nm = sN[m * kNdCols + cc];
+      const double nm = Ns[m * kNdCols + cc];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = fma(sG[m * kPad + 4 * rb + i], nm, part[i]);
+      for (int i = 0; i < 4; ++i) part[i] = fma(G[m * kPadG + 4 * rb + i], nm, part[i]);
     }
+    double (*P)[kD * kNdCols] = sP[p & 1];
     if (!owner) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sP[q][(4 * rb + i) * kNdCols + cc] = part[i];
+      for (int i = 0; i < 4; ++i) P[q][(4 * rb + i) * kNdCols + cc] = part[i];
     }
     __syncthreads();
     if (owner) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (4 * rb + i) * kNdCols + cc;
-        Dm[i] += (part[i] + sP[1][e]) + (sP[2][e] + sP[3][e]);
+        Dm[i] += (part[i] + P[1][e]) + (P[2][e] + P[3][e]);
         N[i] = fma(eps, Dm[i], N[i]);
       }
       store_nd(p + 1);
