@@ -1,4 +1,5 @@
-// Time-parallel ("chunked") schedule of the VLA inverse recurrence, d = 64.
+// Time-parallel ("chunked") schedule of the VLA inverse recurrence, d = 64
+// and d = 128.
 //
 // The pages fuse all T steps in one launch and mention a parallel
 // Blelloch-style formulation ("Variational Linear Attention: Stable
@@ -40,17 +41,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kD = 64;            // head dimension of this schedule
 constexpr int kChunkThreads = 256;
 
+template <int D>
 __global__ void snapshot_kernel(const float* __restrict__ A0, const float* __restrict__ S0,
                                 const float* __restrict__ n0, float* __restrict__ A_copy,
                                 float* __restrict__ S_copy, float* __restrict__ n_copy,
                                 int32_t* __restrict__ chain_info, int64_t chains) {
-  const int64_t mat = chains * kD * kD;
+  const int64_t mat = chains * D * D;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < mat;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t e = i % (kD * kD);
-    A_copy[i] = A0 ? A0[i] : ((e / kD) == (e % kD) ? 1.f : 0.f);
+    const int64_t e = i % (D * D);
+    A_copy[i] = A0 ? A0[i] : ((e / D) == (e % D) ? 1.f : 0.f);
     S_copy[i] = S0 ? S0[i] : 0.f;
-    if (i < chains * kD) n_copy[i] = n0 ? n0[i] : 0.f;
+    if (i < chains * D) n_copy[i] = n0 ? n0[i] : 0.f;
     if (i < chains * 4) chain_info[i] = 0;
   }
 }
@@ -120,38 +122,39 @@ vla_chunk_gram_kernel(const TIn* __restrict__ u, float* __restrict__ G, int T, i
 // the whole period's sum.  One thread per (chain, matrix element); the chunk
 // loop is sequential only through the running sum, so loads are issued eight
 // chunks ahead.
+template <int D>
 __global__ void __launch_bounds__(256)
 vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, double* __restrict__ Gtot,
                       int64_t chains, int nchunks, int nperiods, int o, int q) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= chains * kD * kD) return;
-  const int64_t chain = idx / (kD * kD);
-  const int e = static_cast<int>(idx % (kD * kD));
-  const float* g = G + chain * nchunks * kD * kD + e;
-  double* gp = Gpre + chain * nchunks * kD * kD + e;
-  double* gt = Gtot + chain * nperiods * kD * kD + e;
+  if (idx >= chains * D * D) return;
+  const int64_t chain = idx / (D * D);
+  const int e = static_cast<int>(idx % (D * D));
+  const float* g = G + chain * nchunks * D * D + e;
+  double* gp = Gpre + chain * nchunks * D * D + e;
+  double* gt = Gtot + chain * nperiods * D * D + e;
   double acc = 0.0;
   int p = 0;
   for (int c0 = 0; c0 < nchunks; c0 += 8) {
     float gv[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) gv[k] = (c0 + k < nchunks) ? g[static_cast<int64_t>(c0 + k) * kD * kD] : 0.f;
+    for (int k = 0; k < 8; ++k) gv[k] = (c0 + k < nchunks) ? g[static_cast<int64_t>(c0 + k) * D * D] : 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = c0 + k;
       if (c < nchunks) {
         const int pc = period_of(c, o, q);
         if (pc != p) {
-          gt[static_cast<int64_t>(p) * kD * kD] = acc;
+          gt[static_cast<int64_t>(p) * D * D] = acc;
           acc = 0.0;
           p = pc;
         }
-        gp[static_cast<int64_t>(c) * kD * kD] = acc;
+        gp[static_cast<int64_t>(c) * D * D] = acc;
         acc += static_cast<double>(gv[k]);
       }
     }
   }
-  gt[static_cast<int64_t>(p) * kD * kD] = acc;
+  gt[static_cast<int64_t>(p) * D * D] = acc;
 }
 
 // ---- (N, D) chain ---------------------------------------------------------
@@ -284,15 +287,19 @@ __device__ __forceinline__ double readlane_d(double x, int l) {
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
-constexpr int kRPad = 2 * kD + 1;   // row stride (doubles) of the finished panel rows R
+// Row stride (doubles) of the finished panel rows R with NT tiles per row.
+template <int NT>
+constexpr int rpad() { return 16 * NT + 1; }
+constexpr int kRPad = rpad<8>();
 
 // Panel P of the elimination (compile time, so every tile index is too).
 // Wave P inverts its pivot block W11 by Gauss-Jordan on [ W11 | I ] (one
 // pivot at a time, two tiles), then forms R = W11^-1 W[panel rows] for the
 // tiles right of the panel on the matrix cores; the other waves subtract
 // C_w R.  sI is the wave's 16 x 17 staging tile for transposed operand reads.
-template <int P>
-__device__ __forceinline__ void gj_panel(d4 (&W)[8], int w, int g, int col, double* sR, double* sI, bool& ok) {
+template <int NT, int P>
+__device__ __forceinline__ void gj_panel(d4 (&W)[NT], int w, int g, int col, double* sR, double* sI, bool& ok) {
+  constexpr int kRP = rpad<NT>();
   if (w == P) {   // wave-uniform
     d4 inv_t;     // becomes W11^-1
 #pragma unroll
@@ -328,13 +335,13 @@ __device__ __forceinline__ void gj_panel(d4 (&W)[8], int w, int g, int col, doub
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) a[kk] = sI[col * 17 + 4 * kk + g];
 #pragma unroll
-    for (int ct = P + 1; ct < 8; ++ct) {
+    for (int ct = P + 1; ct < NT; ++ct) {
       d4 r = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) r = mfma64(a[kk], W[ct][kk], r);
       W[ct] = r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sR[(4 * i + g) * kRPad + 16 * ct + col] = r[i];
+      for (int i = 0; i < 4; ++i) sR[(4 * i + g) * kRP + 16 * ct + col] = r[i];
     }
   } else {
     // This wave's rows of the panel's columns, staged for the transposed read.
@@ -347,9 +354,9 @@ __device__ __forceinline__ void gj_panel(d4 (&W)[8], int w, int g, int col, doub
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) a[kk] = -sI[col * 17 + 4 * kk + g];
 #pragma unroll
-    for (int ct = P + 1; ct < 8; ++ct)
+    for (int ct = P + 1; ct < NT; ++ct)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) W[ct] = mfma64(a[kk], sR[(4 * kk + g) * kRPad + 16 * ct + col], W[ct]);
+      for (int kk = 0; kk < 4; ++kk) W[ct] = mfma64(a[kk], sR[(4 * kk + g) * kRP + 16 * ct + col], W[ct]);
   }
   __syncthreads();   // sR and sI are rewritten by the next panel
 }
@@ -417,10 +424,10 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
 
   bool ok = true;
   double* sI = sIw + w * 16 * 17;
-  gj_panel<0>(W, w, g, col, sR, sI, ok);
-  gj_panel<1>(W, w, g, col, sR, sI, ok);
-  gj_panel<2>(W, w, g, col, sR, sI, ok);
-  gj_panel<3>(W, w, g, col, sR, sI, ok);
+  gj_panel<8, 0>(W, w, g, col, sR, sI, ok);
+  gj_panel<8, 1>(W, w, g, col, sR, sI, ok);
+  gj_panel<8, 2>(W, w, g, col, sR, sI, ok);
+  gj_panel<8, 3>(W, w, g, col, sR, sI, ok);
   if (!ok && lane == 0) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
 
   // The result block (A_c^T, equal to A_c in exact arithmetic), symmetrised.
@@ -436,18 +443,267 @@ vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict
   }
 }
 
+// ---- d = 128 ---------------------------------------------------------------
+// Gram matrices (bf16 storage): wave w accumulates the 32 x 32 tiles of row
+// block w, all four column blocks.  The rows of u pass through LDS transposed
+// (ut[column][row]), 64 rows at a time, so each operand is one 16-byte read
+// of eight consecutive rows of one column; the next 64 rows are loaded while
+// the current ones are multiplied.
+constexpr int kG128Rows = 64;
+constexpr int kG128Ld = kG128Rows + 8;   // bf16 per LDS row: 144 bytes
+
+__global__ void __launch_bounds__(kChunkThreads)
+vla_chunk_gram128_kernel(const uint16_t* __restrict__ u, float* __restrict__ G, int T, int r, int L, int nchunks) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t ut[2][D * kG128Ld];
+  const int64_t chain = blockIdx.x / nchunks;
+  const int c = blockIdx.x % nchunks;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+  const int t_lo = c * L, t_hi = min(T, t_lo + L);
+  const int nrows = (t_hi - t_lo) * r;
+  const uint16_t* U = u + (chain * T + t_lo) * static_cast<int64_t>(r) * D;
+  // Thread (row lr of the group, 16-byte pieces lp .. lp + 3 of that row).
+  const int lr = tid & 63, lp = (tid >> 6) * 4;
+  uint4 reg[4];
+  auto load = [&](int k0) {
+    const int k = k0 + lr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      reg[j] = k < nrows ? *reinterpret_cast<const uint4*>(U + static_cast<int64_t>(k) * D + 8 * (lp + j))
+                         : make_uint4(0, 0, 0, 0);
+  };
+  auto store = [&](uint16_t* dst) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t wv[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dst[(8 * (lp + j) + e) * kG128Ld + lr] = static_cast<uint16_t>(e & 1 ? wv[e >> 1] >> 16 : wv[e >> 1]);
+    }
+  };
+  f32x16 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+    acc[jb] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int ngroups = (nrows + kG128Rows - 1) / kG128Rows;
+  if (ngroups > 0) {
+    load(0);
+    store(ut[0]);
+  }
+  __syncthreads();
+  for (int gi = 0; gi < ngroups; ++gi) {
+    if (gi + 1 < ngroups) load((gi + 1) * kG128Rows);
+    const uint16_t* cur = ut[gi & 1];
+#pragma unroll
+    for (int kk = 0; kk < kG128Rows / 16; ++kk) {
+      const int off = 16 * kk + 8 * h;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(cur + (32 * w + c32) * kG128Ld + off));
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const bf16x8 b =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(cur + (32 * jb + c32) * kG128Ld + off));
+        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
+      }
+    }
+    if (gi + 1 < ngroups) store(ut[(gi + 1) & 1]);
+    __syncthreads();
+  }
+  float* gout = G + (chain * nchunks + c) * D * D;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) {
+      const int row = 32 * w + 8 * (sl / 4) + 4 * h + (sl % 4);
+      gout[row * D + 32 * jb + c32] = acc[jb][sl];
+    }
+}
+
+// (N, D) chain on the fp64 matrix cores.  One workgroup (four waves) per
+// chain and block of 32 columns; wave w owns rows 32 w .. 32 w + 31 of the
+// block's N and D as 16 x 16 tiles [row tile a][column tile b], slot i of
+// lane (g, col) at row 32 w + 16 a + 4 i + g, column c0 + 16 b + col.  Per
+// period D += Gtot_p N: the A operand Gtot[i][m] is read as Gtot[m][i]
+// (symmetric: rows of 16 consecutive doubles) from global memory, where the
+// chain's four workgroups share it through L2; the B operand N comes from
+// LDS, whose two buffers alternate between periods (one barrier a period).
+constexpr int kNd128Cols = 32;
+constexpr int kNd128Ld = kNd128Cols + 2;
+
+__global__ void __launch_bounds__(kChunkThreads)
+vla_chunk_chain128_kernel(const double* __restrict__ Gtot, const float* __restrict__ A0, double* __restrict__ ND,
+                          int nperiods, double eps) {
+  constexpr int D = 128;
+  __shared__ double sN[2][D * kNd128Ld];
+  const int64_t chain = blockIdx.x / (D / kNd128Cols);
+  const int c0 = (blockIdx.x % (D / kNd128Cols)) * kNd128Cols;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  d4 N[2][2], Dm[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 16 * a + 4 * i + g, cc = c0 + 16 * b + col;
+        N[a][b][i] = static_cast<double>(A0[(chain * D + row) * D + cc]);
+        Dm[a][b][i] = row == cc ? 1.0 : 0.0;
+      }
+  auto store_nd = [&](int p) {
+    double* nd = ND + (chain * nperiods + p) * 2 * D * D;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = (32 * w + 16 * a + 4 * i + g) * D + c0 + 16 * b + col;
+          nd[e] = N[a][b][i];
+          nd[D * D + e] = Dm[a][b][i];
+        }
+  };
+  auto put_n = [&](double* buf) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf[(32 * w + 16 * a + 4 * i + g) * kNd128Ld + 16 * b + col] = N[a][b][i];
+  };
+  store_nd(0);
+  put_n(sN[0]);
+  __syncthreads();
+  for (int p = 0; p + 1 < nperiods; ++p) {
+    const double* gt = Gtot + (chain * nperiods + p) * D * D;
+    const double* Ns = sN[p & 1];
+#pragma unroll 8
+    for (int kk = 0; kk < D / 4; ++kk) {
+      const double* grow = gt + (4 * kk + g) * D + 32 * w + col;
+      const double ga0 = grow[0], ga1 = grow[16];
+      const double nb0 = Ns[(4 * kk + g) * kNd128Ld + col], nb1 = Ns[(4 * kk + g) * kNd128Ld + 16 + col];
+      Dm[0][0] = mfma64(ga0, nb0, Dm[0][0]);
+      Dm[0][1] = mfma64(ga0, nb1, Dm[0][1]);
+      Dm[1][0] = mfma64(ga1, nb0, Dm[1][0]);
+      Dm[1][1] = mfma64(ga1, nb1, Dm[1][1]);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) N[a][b][i] = fma(eps, Dm[a][b][i], N[a][b][i]);
+    store_nd(p + 1);
+    // Buffer (p + 1) & 1 was last read in period p - 1, before the previous barrier.
+    put_n(sN[(p + 1) & 1]);
+    __syncthreads();
+  }
+}
+
+// Chunk-start inverses: eight waves per (chain, chunk); wave w holds rows
+// 16 w .. 16 w + 15 of W = [ D_c^T | N_p^T ] (128 x 256) as sixteen 16 x 16
+// tiles, read from global memory; D_c^T = D_p^T + N_p^T Gpre_c (Gpre_c
+// symmetric) on the fp64 matrix cores, then the elimination of the d = 64
+// kernel with eight panels.  LDS: the panel rows R (16 x 257) and each wave's
+// staging tile (16 x 17), and afterwards the result block in fp32 (128 x 129)
+// over them.
+constexpr int kStart128Threads = 512;
+constexpr int kStart128Lds = 128 * 129 * 4 > (16 * rpad<16>() + 8 * 16 * 17) * 8 ? 128 * 129 * 4
+                                                                                 : (16 * rpad<16>() + 8 * 16 * 17) * 8;
+
+__global__ void __launch_bounds__(kStart128Threads)
+vla_chunk_start128_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
+                          int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo,
+                          int c_cnt) {
+  constexpr int D = 128, NT = 16;
+  __shared__ double smem[kStart128Lds / 8];
+  const int64_t chain = blockIdx.x / c_cnt;
+  const int c = c_lo + static_cast<int>(blockIdx.x % c_cnt);
+  const int p = period_of(c, o, q);
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const double* Np = ND + (chain * nperiods + p) * 2 * D * D;
+  const double* Dp = Np + D * D;
+  const double* gp = Gpre + (chain * nchunks + c) * D * D;
+  const bool has_pre = c > 0 && (q == 0 || (o + c) % q != 0);
+
+  // W[ct] slot i: row 16 w + 4 i + g, column 16 ct + col; the transposes
+  // are read directly (left: D_p[col'][row'], right: N_p[col'][row']).
+  d4 W[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT / 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (16 * ct + col) * D + 16 * w + 4 * i + g;
+      W[ct][i] = Dp[e];
+      W[NT / 2 + ct][i] = Np[e];
+    }
+  if (has_pre) {
+#pragma unroll 2
+    for (int kk = 0; kk < D / 4; ++kk) {
+      const double a = Np[(4 * kk + g) * D + 16 * w + col];
+      const double* grow = gp + (4 * kk + g) * D + col;
+#pragma unroll
+      for (int ct = 0; ct < NT / 2; ++ct) W[ct] = mfma64(a, grow[16 * ct], W[ct]);
+    }
+  }
+
+  bool ok = true;
+  double* sR = smem;
+  double* sI = smem + 16 * rpad<NT>() + w * 16 * 17;
+  gj_panel<NT, 0>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 1>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 2>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 3>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 4>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 5>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 6>(W, w, g, col, sR, sI, ok);
+  gj_panel<NT, 7>(W, w, g, col, sR, sI, ok);
+  if (!ok && lane == 0) atomicOr(chain_info + chain * 4 + kInfoFallback, 1);
+
+  // The result block (A_c^T, equal to A_c in exact arithmetic), symmetrised
+  // in fp32 (the last panel's barrier freed the LDS).
+  float* sF = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int qb = 0; qb < NT / 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sF[(16 * w + 4 * i + g) * (D + 1) + 16 * qb + col] = static_cast<float>(W[NT / 2 + qb][i]);
+  __syncthreads();
+  float* ac = Ac + (chain * nchunks + c) * D * D;
+  for (int e = t; e < D * D; e += kStart128Threads) {
+    const int i = e / D, j = e % D;
+    ac[e] = 0.5f * (sF[i * (D + 1) + j] + sF[j * (D + 1) + i]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const float* S0, const float* n0,
                                  const void* u, bool bf16, hipStream_t stream) {
-  const int64_t mat = static_cast<int64_t>(pl.chains) * kD * kD;
+  if (pl.d != kD && !(pl.d == 128 && bf16)) return hipErrorInvalidValue;
+  const int64_t mat = static_cast<int64_t>(pl.chains) * pl.d * pl.d;
   const int64_t want = (mat + 255) / 256;
   const unsigned sgrid = static_cast<unsigned>(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(snapshot_kernel, dim3(sgrid), dim3(256), 0, stream, A0, S0, n0, pl.A_init, pl.S_init,
-                     pl.n_init, pl.chain_info, static_cast<int64_t>(pl.chains));
+  if (pl.d == 128)
+    hipLaunchKernelGGL(snapshot_kernel<128>, dim3(sgrid), dim3(256), 0, stream, A0, S0, n0, pl.A_init, pl.S_init,
+                       pl.n_init, pl.chain_info, static_cast<int64_t>(pl.chains));
+  else
+    hipLaunchKernelGGL(snapshot_kernel<kD>, dim3(sgrid), dim3(256), 0, stream, A0, S0, n0, pl.A_init, pl.S_init,
+                       pl.n_init, pl.chain_info, static_cast<int64_t>(pl.chains));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned units = static_cast<unsigned>(pl.chains * pl.nchunks);
+  if (pl.d == 128) {
+    hipLaunchKernelGGL(vla_chunk_gram128_kernel, dim3(units), dim3(kChunkThreads), 0, stream,
+                       static_cast<const uint16_t*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n = mat;
+    hipLaunchKernelGGL(vla_chunk_scan_kernel<128>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(vla_chunk_chain128_kernel, dim3(pl.chains * (128 / kNd128Cols)), dim3(kChunkThreads), 0, stream,
+                       pl.Gtot, pl.A_init, pl.ND, pl.nperiods, static_cast<double>(pl.eps));
+    return hipGetLastError();
+  }
   if (bf16)
     hipLaunchKernelGGL(vla_chunk_gram_kernel<uint16_t>, dim3(units), dim3(kChunkThreads), 0, stream,
                        static_cast<const uint16_t*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
@@ -457,7 +713,7 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const int64_t n = static_cast<int64_t>(pl.chains) * kD * kD;
-    hipLaunchKernelGGL(vla_chunk_scan_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(vla_chunk_scan_kernel<kD>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
                        pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -468,6 +724,12 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
 
 hipError_t launch_chunk_start(const ChunkPlan& pl, int c_lo, int c_cnt, hipStream_t stream) {
   if (c_cnt <= 0) return hipSuccess;
+  if (pl.d == 128) {
+    hipLaunchKernelGGL(vla_chunk_start128_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)),
+                       dim3(kStart128Threads), 0, stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks,
+                       pl.nperiods, pl.o, pl.q, c_lo, c_cnt);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)), dim3(kChunkThreads), 0,
                      stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q, c_lo, c_cnt);
   return hipGetLastError();

@@ -52,8 +52,16 @@ namespace vla {
 // Scalars of the blocked rank-r update: u_i . w_l (4 x 4) and k . w_l (4).
 constexpr int kBlkScalars = 20;
 
+// Waves per SIMD the register allocation must leave room for.  The inverse
+// pass at d = 128 runs thousands of chunks, one eight-wave workgroup each:
+// two workgroups per compute unit overlap one's barriers and scalar
+// recurrence with the other's matrix-vector sweeps.
+constexpr int seq_min_waves(int D, int NW, SeqMode m) {
+  return (m == SeqMode::kInverseOnly && D == 128) ? 2 * NW / 4 : 1;
+}
+
 template <typename TIn, int D, int NW, int CG, SeqMode MODE, bool RES>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(seq_min_waves(D, NW, MODE))))
 vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   static_assert(!RES || MODE == SeqMode::kFull, "the residual update runs in the full recurrence only");
   using L = TileLayout<D, NW, CG>;
@@ -163,8 +171,8 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   asrc.fix0 = asrc.fix1 = asrc.fix2 = asrc.ubase = kHasA ? nullptr : x.alpha + tok0 * D;
   asrc.ustride = D;
 
-  Stager<TIn, D, NTH> st;
-  Stager<float, D, NTH> ast;
+  Stager<TIn, D, NTH, seq_stage_slots<TIn, D, NW>(MODE)> st;
+  Stager<float, D, NTH, (kHasA ? 1 : kMaxStageVecs)> ast;
   const int nstage = (tend - tbeg + TT - 1) / TT;
   if (nstage > 0) {
     st.load(src, tbeg, TT, tend, tid);
@@ -455,20 +463,29 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
         }
         if constexpr (kInv) {
-          float an = 0.f;
+          float an = 0.f, kn = 0.f;
 #pragma unroll
-          for (int ii = 0; ii < R; ++ii) an = fmaf(alpha[ii], alpha[ii], an);
+          for (int ii = 0; ii < R; ++ii) {
+            an = fmaf(alpha[ii], alpha[ii], an);
+            kn = fmaf(kI[ii], kI[ii], kn);
+          }
           an = wave_total(cg == 0 ? an : 0.f);
-          static_assert(!kInv || NW == 1, "the inverse-only pass runs one wave per chunk");
+          if (a.residual) kn = wave_total(cg == 0 ? kn : 0.f);
+          if constexpr (NW > 1) {
+            // Sums over the waves, in slots 2 and 3 of the reduction buffer
+            // (the sub-updates use slots 0 and 1).  The next writes to these
+            // slots come a token later, past at least one more barrier.
+            if (lane == 0) { red[w * 4 + 2] = an; red[w * 4 + 3] = kn; }
+            __syncthreads();
+            an = 0.f; kn = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) { an += red[ww * 4 + 2]; kn += red[ww * 4 + 3]; }
+          }
           // alpha_hat of this token goes to HBM for the state pass: the
           // clamped coefficient, or for the residual update the unit vector
           // along A k_hat with k_hat = k / |k|.
           float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
           if (a.residual) {
-            float kn = 0.f;
-#pragma unroll
-            for (int ii = 0; ii < R; ++ii) kn = fmaf(kI[ii], kI[ii], kn);
-            kn = wave_total(cg == 0 ? kn : 0.f);
             const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
             ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
           }
@@ -617,15 +634,15 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   if constexpr (kInv) {
     // Guard fires break the chunk-start inverses of later chunks: flag the
     // chain for the sequential fallback.  Non-finite values are recorded.
+    // (Guard fires are the same in every wave; a non-finite value may show
+    // in any wave's rows.)
     const bool wave_bad = __any(bad);
-    if (tid == 0) {
-      int32_t* info = x.chain_info + chain * 4;
-      if (guard_fires > 0) {
-        atomicAdd(info + kInfoGuard, guard_fires);
-        atomicOr(info + kInfoFallback, 1);
-      }
-      if (wave_bad) atomicOr(info + kInfoNonfinite, 1);
+    int32_t* info = x.chain_info + chain * 4;
+    if (tid == 0 && guard_fires > 0) {
+      atomicAdd(info + kInfoGuard, guard_fires);
+      atomicOr(info + kInfoFallback, 1);
     }
+    if (lane == 0 && wave_bad) atomicOr(info + kInfoNonfinite, 1);
     return;
   }
   if (a.stats) {
@@ -710,6 +727,7 @@ static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int 
   } else {
     switch (d) {
       case 64: return launch_seq<TIn, 64, 1, 4, MODE>(a, x, chains, stream);
+      case 128: return launch_seq<TIn, 128, 8, 8, MODE>(a, x, chains, stream);
       default: return hipErrorInvalidValue;
     }
   }

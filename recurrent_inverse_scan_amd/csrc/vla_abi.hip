@@ -207,7 +207,18 @@ struct ChunkLayout {
   size_t off_pSit = 0, off_pF = 0, off_prec = 0, off_pn = 0, off_pconv = 0, off_pact = 0, off_pP = 0;
   // Residual update's state pass (replaces the additive one's buffers).
   size_t off_rW = 0, off_rU = 0, off_rN = 0, off_rQ = 0, off_rks = 0, off_rS = 0, off_rnb = 0, off_rnc = 0, off_rex = 0;
+  // d = 128: the linear state pass's chunk sums (then chunk starts) of S and n.
+  int ncs = 0;
+  size_t off_lS = 0, off_ln = 0;
 };
+
+// Whether the d = 128 time-parallel schedule applies: its state pass is the
+// plain prefix sum, valid only without the cap, for the additive update, and
+// its kernels read bf16 storage.
+bool linear_d128(const vla_scan_params_t* p) {
+  const bool cap_on = p->s_cap > 0.f && std::isfinite(p->s_cap);
+  return p->d == 128 && p->in_dtype == VLA_BF16 && p->update == VLA_UPDATE_ADDITIVE && !cap_on;
+}
 
 // Whether the chunked schedule can run these parameters with chunk length L.
 bool chunk_len_fits(const vla_scan_params_t* p, int L) {
@@ -251,7 +262,8 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
   // every chain (at most 256 threads each, below HIP's 2^32 work-items per
   // launch dimension); longer problems take the sequential schedule.
   constexpr int64_t kMaxBlocks = int64_t{1} << 22;
-  const bool possible = p->d == 64 && p->T > 0 && chains > 0 && chains * ((p->T + int64_t{63}) / 64) <= kMaxBlocks;
+  const bool possible = (p->d == 64 || linear_d128(p)) && p->T > 0 && chains > 0 &&
+                        chains * ((p->T + int64_t{63}) / 64) <= kMaxBlocks;
   int L = 0;
   if (possible) {
     if (p->chunk_len > 0) {
@@ -288,6 +300,25 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
     cl.q = p->nudge_period > 0 ? p->nudge_period / L : 0;
     // Periods touched: 1 + nudges at the ends of chunks 0 .. nchunks-2.
     cl.nperiods = 1 + (cl.q > 0 ? (cl.o + cl.nchunks - 1) / cl.q - cl.o / cl.q : 0);
+    if (p->d == 128) {
+      // Inverse side as at d = 64 (matrices of 128 x 128), then the linear
+      // state pass's chunk sums.
+      const size_t d = 128, d2 = d * d, C = static_cast<size_t>(chains), nch = cl.nchunks;
+      cl.ncs = (p->T + vla::kLinChunk - 1) / vla::kLinChunk;
+      cl.off_A = off; off = align_up(off + C * d2 * 4);
+      cl.off_S = off; off = align_up(off + C * d2 * 4);
+      cl.off_n = off; off = align_up(off + C * d * 4);
+      cl.off_info = off; off = align_up(off + C * 4 * 4);
+      cl.off_G = off; off = align_up(off + C * nch * d2 * 4);
+      cl.off_Gpre = off; off = align_up(off + C * nch * d2 * 8);
+      cl.off_Gtot = off; off = align_up(off + C * static_cast<size_t>(cl.nperiods) * d2 * 8);
+      cl.off_ND = off; off = align_up(off + C * static_cast<size_t>(cl.nperiods) * 2 * d2 * 8);
+      cl.off_Ac = off; off = align_up(off + C * nch * d2 * 4);
+      cl.off_alpha = off; off = align_up(off + C * static_cast<size_t>(p->T) * d * 4);
+      cl.off_lS = off; off = align_up(off + C * static_cast<size_t>(cl.ncs) * d2 * 4);
+      cl.off_ln = off; off = align_up(off + C * static_cast<size_t>(cl.ncs) * d * 4);
+      return finish_layout(p, cl, off);
+    }
     const size_t d2 = 64 * 64, C = static_cast<size_t>(chains), nch = cl.nchunks;
     cl.off_A = off; off = align_up(off + C * d2 * 4);
     cl.off_S = off; off = align_up(off + C * d2 * 4);
@@ -539,6 +570,7 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   pl.chains = static_cast<int>(chains);
   pl.T = p->T;
   pl.r = r;
+  pl.d = d;
   pl.L = cl.L;
   pl.nchunks = cl.nchunks;
   pl.nperiods = cl.nperiods;
@@ -585,13 +617,37 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
   // (The inverse pass below writes the residual update's unit gates when
   // a.residual is set.)
-  if (bf16 && p->r == 1)
+  if (bf16 && p->r == 1 && d == 64)
     e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
                                static_cast<int>(chains), stream);
   else
     e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,
                                         static_cast<int>(chains), stream);
   if (e != hipSuccess) return hip_fail(e, "chunked inverse launch");
+
+  if (d == 128) {
+    // Linear state pass (no cap), then the sequential rerun of any chain the
+    // inverse side flagged.
+    vla::LinPlan lp{};
+    lp.chains = static_cast<int>(chains);
+    lp.T = p->T;
+    lp.ncs = cl.ncs;
+    lp.q = q; lp.k = k; lp.v = v; lp.o = o;
+    lp.alpha = pl.alpha;
+    lp.dS = reinterpret_cast<float*>(ws + cl.off_lS);
+    lp.dn = reinterpret_cast<float*>(ws + cl.off_ln);
+    lp.S_init = pl.S_init;
+    lp.n_init = pl.n_init;
+    lp.S_T = S_T;
+    lp.n_T = n_T;
+    lp.chain_info = pl.chain_info;
+    lp.stats = stats;
+    lp.den_eps = p->den_eps;
+    if ((e = vla::launch_linear_state(lp, stream)) != hipSuccess) return hip_fail(e, "linear state pass launch");
+    e = vla::launch_scan_sequential(a, d, bf16, static_cast<int>(chains), pl.chain_info, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunked fallback launch");
+    return VLA_OK;
+  }
 
   if (p->update == VLA_UPDATE_RESIDUAL) {
     // Residual state pass: per-block affine maps of S, their chain, readout.

@@ -43,10 +43,11 @@ hipError_t launch_scan_split_fused(const ScanArgs& a, int d, bool bf16, int chai
 hipError_t launch_scan_sequential(const ScanArgs& a, int d, bool bf16, int chains, const int32_t* only_if,
                                   hipStream_t stream);
 
-// Time-parallel inverse schedule (d = 64): buffers live in the caller's
-// workspace; see chunked.hip.
+// Time-parallel inverse schedule (d = 64, and d = 128 with bf16 storage):
+// buffers live in the caller's workspace; see chunked.hip.  Matrices below
+// are d x d (shown for d = 64).
 struct ChunkPlan {
-  int chains, T, r;
+  int chains, T, r, d;
   int L;          // tokens per chunk
   int nchunks;    // ceil(T / L)
   int nperiods;   // nudge periods touched by this call
@@ -157,6 +158,28 @@ hipError_t launch_state_readout(const StatePlan& pl, const ScanArgs& a, int32_t*
 // Non-null events are recorded on the stream right before and after it.
 hipError_t launch_state_chain(const StatePlan& pl, const ChainSeg& sg, const ScanArgs& a, const int32_t* chain_info,
                               int chains, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// State pass at d = 128 without the cap (linear_state.hip): additive update,
+// bf16 storage, chunks of kLinChunk tokens.
+constexpr int kLinChunk = 256;
+struct LinPlan {
+  int chains, T, ncs;      // ncs = ceil(T / kLinChunk)
+  const void* q;           // [chains][T][128] bf16
+  const void* k;
+  const void* v;
+  void* o;
+  const float* alpha;      // [chains][T][128] alpha_hat from the inverse pass
+  float* dS;               // [chains][ncs][128][128]: chunk sums, then the chunk-start S
+  float* dn;               // [chains][ncs][128]: the same for n
+  const float* S_init;     // [chains][128][128]
+  const float* n_init;     // [chains][128]
+  float* S_T;
+  float* n_T;
+  int32_t* chain_info;     // [chains][4]: guard fires and flags of the inverse pass
+  int32_t* stats;          // nullable
+  float den_eps;
+};
+hipError_t launch_linear_state(const LinPlan& lp, hipStream_t stream);
 
 // Inverse recurrence of chunks [chunk_lo, chunk_lo + chunk_cnt) from their
 // chunk-start inverses; writes alpha_hat and, from each chain's last chunk, A_T.

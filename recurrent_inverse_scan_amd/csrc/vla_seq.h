@@ -126,18 +126,20 @@ struct RowSource {
 };
 
 // Streams TT tokens of row streams from HBM into an LDS stage [TT][n][D] of
-// float32 (bf16 widened exactly).  Each thread moves up to kMaxStageVecs
-// 16-byte vectors; tokens at or past T read as 0.
-template <typename TSrc, int D, int NTH>
+// float32 (bf16 widened exactly).  Each thread moves up to SLOTS (at most
+// kMaxStageVecs) 16-byte vectors; the caller sizes the stage to fit.  Tokens
+// at or past T read as 0.
+template <typename TSrc, int D, int NTH, int SLOTS = kMaxStageVecs>
 struct Stager {
   static constexpr int EPV = Elem<TSrc>::kPer16B;
   static constexpr int VPR = D / EPV;
-  uint4 reg[kMaxStageVecs];
+  static_assert(SLOTS >= 1 && SLOTS <= kMaxStageVecs, "staging slots");
+  uint4 reg[SLOTS];
 
   __device__ __forceinline__ void load(const RowSource<TSrc, D> s, int tb, int TT, int T, int tid) {
     const int nvec = TT * s.n * VPR;
 #pragma unroll
-    for (int j = 0; j < kMaxStageVecs; ++j) {
+    for (int j = 0; j < SLOTS; ++j) {
       const int e = tid + j * NTH;
       reg[j] = make_uint4(0, 0, 0, 0);
       if (e < nvec) {
@@ -156,7 +158,7 @@ struct Stager {
     const int nvec = TT * n * VPR;
     const int rpt = rows_per_token > 0 ? rows_per_token : n;
 #pragma unroll
-    for (int j = 0; j < kMaxStageVecs; ++j) {
+    for (int j = 0; j < SLOTS; ++j) {
       const int e = tid + j * NTH;
       if (e < nvec) {
         const int rho = e / VPR, c = e % VPR;
@@ -203,6 +205,17 @@ __host__ __device__ constexpr int seq_stage_tokens(SeqMode m, int r) {
   const int lds_cap = (48 * 1024) / (2 * nf * D * static_cast<int>(sizeof(float)));
   cap = cap < lds_cap ? cap : lds_cap;
   return cap >= 8 ? 8 : (cap < 1 ? 1 : cap);
+}
+
+// Staging slots per thread that every rank r <= 4 needs: a stage holds at
+// most 8 tokens of at most the mode's rows at r = 4, and never more vectors
+// than kMaxStageVecs per thread (seq_stage_tokens caps it there).
+template <typename TIn, int D, int NW>
+__host__ __device__ constexpr int seq_stage_slots(SeqMode m) {
+  const int nvmax = seq_rows_per_token<TIn, D, NW>(m, 4);
+  const int vecs = 8 * nvmax * (D / Elem<TIn>::kPer16B);
+  const int slots = (vecs + 64 * NW - 1) / (64 * NW);
+  return slots < kMaxStageVecs ? slots : kMaxStageVecs;
 }
 
 template <typename TIn, int D, int NW>

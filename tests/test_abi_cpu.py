@@ -168,6 +168,34 @@ def test_chunked_schedule_planning(lib):
         assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
 
 
+def test_d128_schedule_choice(lib):
+    """At d = 128 the time-parallel schedule needs bf16 storage, the additive
+    update and no cap (its state pass is a plain prefix sum); AUTO takes it
+    for the wide shape (128 chains of 8192 tokens, rank 4, nudge every 512)
+    and sizes its workspace from the per-chunk matrices and coefficients."""
+    n = ctypes.c_size_t(7)
+    wide = dict(B=8, H=16, T=8192, d=128, r=4, in_dtype=_lib.VLA_BF16, nudge_period=512)
+    p = _params(lib, **wide)
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK
+    C, T, d, L, P = 128, 8192, 128, 512, 512
+    nch, ncs, nper = T // L, T // 256, T // P
+    floor = C * d * d * (4 * nch + 8 * nch + 8 * nper + 16 * nper + 4 * nch + 4 * (T // 256)) + C * T * d * 4
+    assert n.value >= floor and n.value < floor + (64 << 20)
+    auto = n.value
+    p.schedule = _lib.VLA_SCHEDULE_CHUNKED
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value == auto
+    p.chunk_len = 256
+    assert lib.vla_scan_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.VLA_OK and n.value > auto
+    # sequential otherwise: fp32 storage, a cap, the residual update, or a forced choice
+    for kw in (dict(in_dtype=_lib.VLA_F32), dict(s_cap=1e3), dict(update=_lib.VLA_UPDATE_RESIDUAL)):
+        q = _params(lib, **{**wide, **kw})
+        assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+        q.schedule = _lib.VLA_SCHEDULE_CHUNKED
+        assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_EUNSUPPORTED
+    q = _params(lib, **{**wide, "schedule": _lib.VLA_SCHEDULE_SEQUENTIAL})
+    assert lib.vla_scan_workspace_size(ctypes.byref(q), ctypes.byref(n)) == _lib.VLA_OK and n.value == 0
+
+
 def test_residual_update_schedules(lib):
     """The residual update plans like the additive one: AUTO chunks few long
     chains at d = 64 (with its own state-pass buffers), stays sequential for
