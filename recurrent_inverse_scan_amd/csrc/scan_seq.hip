@@ -108,6 +108,9 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   float* red = abuf + 2 * D;                                 // [2][NW][4]
   float* zb4 = red + 2 * NW * 4;                             // [4][D] z rows of the blocked rank-r update
   float* scl = zb4 + 4 * D;                                  // [kBlkScalars][kBlkStride] row-group partials
+  // Inverse-only pass on several waves: each stage's alpha rows [2][TT][D],
+  // normalised and written out after the stage's closing barrier.
+  float* apend = scl + kBlkScalars * kBlkStride;
 
   // ---- initial state --------------------------------------------------
   float A[kHasA ? R : 1][kHasA ? C : 4];
@@ -462,6 +465,12 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           }
           phase = (phase + 1 == a.nudge_period) ? 0 : phase + 1;
         }
+        if constexpr (kInv && NW > 1) {
+          // The norm needs every wave's rows: the rows wait in LDS until the
+          // stage ends (below), so no barrier is spent on it here.
+          if (cg == 0) lds_store_rows<R>(apend + ((sidx & 1) * TT + tt) * D + row0, alpha);
+          continue;
+        }
         if constexpr (kInv) {
           float an = 0.f, kn = 0.f;
 #pragma unroll
@@ -471,16 +480,6 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
           }
           an = wave_total(cg == 0 ? an : 0.f);
           if (a.residual) kn = wave_total(cg == 0 ? kn : 0.f);
-          if constexpr (NW > 1) {
-            // Sums over the waves, in slots 2 and 3 of the reduction buffer
-            // (the sub-updates use slots 0 and 1).  The next writes to these
-            // slots come a token later, past at least one more barrier.
-            if (lane == 0) { red[w * 4 + 2] = an; red[w * 4 + 3] = kn; }
-            __syncthreads();
-            an = 0.f; kn = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) { an += red[ww * 4 + 2]; kn += red[ww * 4 + 3]; }
-          }
           // alpha_hat of this token goes to HBM for the state pass: the
           // clamped coefficient, or for the residual update the unit vector
           // along A k_hat with k_hat = k / |k|.
@@ -598,6 +597,38 @@ vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
       if constexpr (!kHasA) ast.store(astage + ((sidx + 1) & 1) * TT * D, TT, 1, tid);
     }
     __syncthreads();
+    if constexpr (kInv && NW > 1) {
+      // alpha_hat of the stage's tokens, wave w taking tokens w, w + NW, ...:
+      // the clamped coefficient, or for the residual update the unit vector
+      // along A k_hat with k_hat = k / |k|.  The rows and this stage's k stay
+      // in place until the next stage's first barrier (the buffers alternate
+      // by stage), which every wave reaches only after these reads.
+      constexpr int PL = D / 64;   // values per lane
+      for (int tt = w; tt < tcount; tt += NW) {
+        const float* arow = apend + ((sidx & 1) * TT + tt) * D + PL * lane;
+        const float* krow = sbuf + (tt * NV + row_k) * D + PL * lane;
+        float av[PL], an = 0.f, kn = 0.f;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          av[e] = arow[e];
+          an = fmaf(av[e], av[e], an);
+          kn = fmaf(krow[e], krow[e], kn);
+        }
+        an = wave_sum(an);
+        float ascale = an > 1.f ? 1.f / sqrtf(an) : 1.f;
+        if (a.residual) {
+          const float kinv = 1.f / fmaxf(sqrtf(wave_sum(kn)), 1e-12f);
+          ascale = kinv / fmaxf(kinv * sqrtf(an), 1e-12f);
+        }
+        float* dst = x.alpha_out + (tok0 + tb + tt) * D + PL * lane;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const float ah = av[e] * ascale;
+          bad |= !isfinite(ah);
+          dst[e] = ah;
+        }
+      }
+    }
   }
 
   // ---- final state and statistics ---------------------------------------
@@ -674,7 +705,8 @@ template <typename TIn, int D, int NW, int CG, SeqMode MODE>
 static hipError_t launch_seq(const ScanArgs& a, const SeqExtra& x, int chains, hipStream_t stream) {
   // The stages and vectors, then the blocked rank-r update's z rows and scalars.
   const size_t lds =
-      seq_lds_bytes<TIn, D, NW>(MODE, a.r) + sizeof(float) * (4 * D + kBlkScalars * (NW * 64 / CG + 4));
+      seq_lds_bytes<TIn, D, NW>(MODE, a.r) + sizeof(float) * (4 * D + kBlkScalars * (NW * 64 / CG + 4)) +
+      (MODE == SeqMode::kInverseOnly && NW > 1 ? sizeof(float) * 2 * seq_stage_tokens<TIn, D, NW>(MODE, a.r) * D : 0);
   const unsigned grid = MODE == SeqMode::kInverseOnly ? static_cast<unsigned>(chains * x.chunk_cnt)
                                                        : static_cast<unsigned>(chains);
   if constexpr (MODE == SeqMode::kFull) {
