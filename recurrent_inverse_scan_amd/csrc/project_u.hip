@@ -9,10 +9,8 @@
 // u out of HBM.  Each wave computes 32 rows x d columns of one direction with
 // 32x32 MFMA tiles (bf16: 32x32x16, fp32: 32x32x2, both accumulating in
 // fp32), keeps its k_raw rows in registers across the r directions, and
-// normalises in the epilogue: a row's d outputs live in the 32 lanes of one
-// half-wave (one column each, d/32 tiles), so its sum of squares is a
-// 32-lane reduction; the normalised tile goes through the wave's LDS so that
-// the stores are whole 16-byte pieces of rows.
+// normalises in the epilogue, after the tile has gone through the wave's LDS
+// into pieces of whole rows (see finish_tile).
 //
 // MFMA 32x32 accumulator layout: lane l holds column l % 32 of the tile and,
 // in accumulator slot a, row 8*(a/4) + 4*(l/32) + a%4.  Operand A holds row
@@ -30,22 +28,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kProjWaves = 4;
 
-template <typename TOut>
-__device__ __forceinline__ void store_out(TOut* p, float x) { Elem<TOut>::store(p, x); }
-
-// Sum over the 32 lanes of each half-wave.
-__device__ __forceinline__ float half_wave_sum(float x) {
-  x = group_sum<16>(x);
-  return x + __shfl_xor(x, 16, 64);
-}
-
 // LDS row stride (floats) of a wave's 32 x D staging tile.
 template <int D>
 constexpr int stage_ld() { return D + 4; }
 
-// Normalises the wave's 32 rows of direction i and writes them: through the
-// wave's LDS tile, so that each lane stores whole 16-byte pieces of rows
-// instead of one element of each of 16 rows.
+// Normalises the wave's 32 rows of direction i and writes them.  The raw
+// tile goes through the wave's LDS first; then each lane takes pieces of
+// eight consecutive values of a row (the lanes of one row are D/8
+// consecutive lanes), so a row's sum of squares is one short DPP group sum
+// and each lane normalises and stores whole 16-byte (bf16) or 32-byte
+// (fp32) pieces.  (Normalising in the accumulator layout took a 32-lane
+// reduction per accumulator slot, 16 per tile.)
 template <int D, typename TOut>
 __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_base, int64_t rows, int r,
                                             int i, int lane, TOut* u, float* tile) {
@@ -53,36 +46,41 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_b
   const int col = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    float ss = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) ss = fmaf(acc[nb][s], acc[nb][s], ss);
-    ss = half_wave_sum(ss);
-    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
     const int rl = 8 * (s / 4) + 4 * hi + (s % 4);
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) tile[rl * LD + nb * 32 + col] = acc[nb][s] * inv;
+    for (int nb = 0; nb < D / 32; ++nb) tile[rl * LD + nb * 32 + col] = acc[nb][s];
   }
   asm volatile("" ::: "memory");   // one wave's LDS operations complete in order
-  constexpr int EPC = 16 / static_cast<int>(sizeof(TOut));   // elements per 16-byte piece
-  constexpr int PPR = D / EPC;                                // pieces per row
-  static_assert((32 * PPR) % 64 == 0, "whole pieces per lane");
+  constexpr int PPR = D / 8;       // pieces of eight values per row
+  static_assert((32 * PPR) % 64 == 0 && 64 % PPR == 0, "whole rows per lane group");
 #pragma unroll
   for (int it = 0; it < 32 * PPR / 64; ++it) {
     const int c = lane + 64 * it;
     const int rl = c / PPR, pc = c % PPR;
-    const int64_t row = row_base + rl;
-    const float* src = tile + rl * LD + pc * EPC;
-    uint4 w;
-    if constexpr (EPC == 4) {
-      w = *reinterpret_cast<const uint4*>(src);
-    } else {
-      uint32_t h[4];
+    const float4 x0 = *reinterpret_cast<const float4*>(tile + rl * LD + pc * 8);
+    const float4 x1 = *reinterpret_cast<const float4*>(tile + rl * LD + pc * 8 + 4);
+    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        h[e] = static_cast<uint32_t>(f32_to_bf16(src[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * e + 1])) << 16);
-      w = make_uint4(h[0], h[1], h[2], h[3]);
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = group_sum<PPR>(ss);
+    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= inv;
+    const int64_t row = row_base + rl;
+    if (row < rows) {
+      TOut* dst = u + (row * r + i) * D + pc * 8;
+      if constexpr (sizeof(TOut) == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+      }
     }
-    if (row < rows) *reinterpret_cast<uint4*>(u + (row * r + i) * D + pc * EPC) = w;
   }
   asm volatile("" ::: "memory");   // the reads finish before the next direction's writes
 }
