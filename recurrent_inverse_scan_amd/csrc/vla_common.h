@@ -18,6 +18,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two values rounded to bf16 (nearest, ties to even; NaN stays NaN) and
+// packed, a in the low half: one v_cvt_pk_bf16_f32.
+typedef float vla_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 vla_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((vla_f32x2{a, b}), vla_bf16x2));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kPer16B = 4;
