@@ -20,7 +20,8 @@
 // Kernels, in stream order:
 //   vla_chunk_gram_kernel   G_c for every chunk (MFMA, fp32 accumulation)
 //   vla_chunk_scan_kernel   fp64 prefix sums of G inside each nudge period and
-//                           each period's total, in parallel over elements
+//                           each period's total, in parallel over periods and
+//                           elements
 //   vla_chunk_chain_kernel  per chain and column block, sequential over
 //                           periods, fp64: (N, D) at every period start
 //   vla_chunk_start_kernel  per chunk, fp64: A_c by blocked Gauss-Jordan
@@ -119,42 +120,46 @@ vla_chunk_gram_kernel(const TIn* __restrict__ u, float* __restrict__ G, int T, i
 // ---- Gram prefixes ----------------------------------------------------------
 // Segmented exclusive prefix over the chunks of each nudge period, in fp64:
 // Gpre_c = sum of G_c' over the earlier chunks c' of c's period, and Gtot_p =
-// the whole period's sum.  One thread per (chain, matrix element); the chunk
-// loop is sequential only through the running sum, so loads are issued eight
-// chunks ahead.
+// the whole period's sum.  One thread per (chain, period, matrix element),
+// sequential over the period's chunks.  A period's first chunk has no prefix
+// (the chunk-start kernels read none for it), so nothing is written there.
 template <int D>
 __global__ void __launch_bounds__(256)
 vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, double* __restrict__ Gtot,
                       int64_t chains, int nchunks, int nperiods, int o, int q) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= chains * D * D) return;
-  const int64_t chain = idx / (D * D);
+  if (idx >= chains * nperiods * D * D) return;
   const int e = static_cast<int>(idx % (D * D));
+  const int64_t cp = idx / (D * D);
+  const int p = static_cast<int>(cp % nperiods);
+  const int64_t chain = cp / nperiods;
+  // Chunks of period p: those c with period_of(c) = p.
+  int c_lo = 0, c_hi = nchunks;
+  if (q > 0) {
+    const int base = (o / q + p) * q - o;
+    c_lo = max(0, base);
+    c_hi = min(nchunks, base + q);
+  }
   const float* g = G + chain * nchunks * D * D + e;
   double* gp = Gpre + chain * nchunks * D * D + e;
-  double* gt = Gtot + chain * nperiods * D * D + e;
   double acc = 0.0;
-  int p = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += 8) {
+  for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
     float gv[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) gv[k] = (c0 + k < nchunks) ? g[static_cast<int64_t>(c0 + k) * D * D] : 0.f;
+    for (int k = 0; k < 8; ++k) {
+      gv[k] = 0.f;
+      if (c0 + k < c_hi) gv[k] = g[static_cast<int64_t>(c0 + k) * D * D];
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = c0 + k;
-      if (c < nchunks) {
-        const int pc = period_of(c, o, q);
-        if (pc != p) {
-          gt[static_cast<int64_t>(p) * D * D] = acc;
-          acc = 0.0;
-          p = pc;
-        }
-        gp[static_cast<int64_t>(c) * D * D] = acc;
+      if (c < c_hi) {
+        if (c > c_lo) gp[static_cast<int64_t>(c) * D * D] = acc;
         acc += static_cast<double>(gv[k]);
       }
     }
   }
-  gt[static_cast<int64_t>(p) * D * D] = acc;
+  Gtot[(chain * nperiods + p) * D * D + e] = acc;
 }
 
 // ---- (N, D) chain ---------------------------------------------------------
@@ -696,7 +701,7 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
     hipLaunchKernelGGL(vla_chunk_gram128_kernel, dim3(units), dim3(kChunkThreads), 0, stream,
                        static_cast<const uint16_t*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t n = mat;
+    const int64_t n = mat * pl.nperiods;
     hipLaunchKernelGGL(vla_chunk_scan_kernel<128>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
                        pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -712,7 +717,7 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
                        static_cast<const float*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    const int64_t n = static_cast<int64_t>(pl.chains) * kD * kD;
+    const int64_t n = static_cast<int64_t>(pl.chains) * pl.nperiods * kD * kD;
     hipLaunchKernelGGL(vla_chunk_scan_kernel<kD>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
                        pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
