@@ -272,9 +272,9 @@ ChunkLayout plan_schedule(const vla_scan_params_t* p) {
       // The longest chunk that still gives at least kMinChunks chunks over
       // all chains (the inverse pass keeps the SIMDs busy only with many
       // chunks side by side), else the shortest that fits: 512 tokens for 16
-      // chains of 65536, 128 for 32 chains of 2048 (0.52 against 0.64 ms
-      // with 256).
-      constexpr int64_t kMinChunks = 512;
+      // chains of 65536 and for 128 chains of 8192, 64 for 32 chains of
+      // 2048 (0.42 against 0.46 ms with 128 and 0.61 with 256).
+      constexpr int64_t kMinChunks = 1024;
       for (int cand : {512, 256, 128, 64}) {
         if (!chunk_len_fits(p, cand)) continue;
         L = cand;
