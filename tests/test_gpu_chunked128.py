@@ -152,3 +152,31 @@ def test_chunked128_nonfinite_input_is_flagged():
     st = out[4].reshape(2, 4).cpu().numpy()
     assert st[1, 2] == 1 and st[0, 2] == 0, st
     assert np.isfinite(to64(out[0].reshape(2, cfg.T, cfg.d)[0])).all()
+
+
+@pytest.mark.parametrize("T", [1, 17, 300])
+def test_chunked128_short_calls(T):
+    """Calls shorter than one chunk or one 32-token stage (16-token chunks):
+    a single token, a ragged 17, and 300 tokens over 19 chunks."""
+    cfg = _cfg(f"short-T{T}", B=1, H=2, T=T, r=4, nudge_period=0)
+    _say(f"case short call T={T}")
+    x = case(cfg, seed=27 + T)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=16)
+    check("gpu-chunked128", cfg, out, run_oracle(x, cfg), say=_say)
+
+
+def test_chunked128_strided_views():
+    """q, k, v sliced from one [B, T, H, 3d] tensor (gathered by the library
+    into its workspace) give the contiguous call's result bit for bit."""
+    cfg = _cfg("strided", B=1, H=3, T=640, r=2, nudge_period=128)
+    _say("case strided views")
+    x = case(cfg, seed=28)
+    d = cfg.d
+    packed = torch.cat([x["q"], x["k"], x["v"]], dim=-1).permute(0, 2, 1, 3).contiguous().to(DEV)
+    qs, ks, vs = (packed[..., i * d:(i + 1) * d].permute(0, 2, 1, 3) for i in range(3))
+    assert not qs.is_contiguous()
+    got = scan_forward(qs, ks, vs, x["u"].to(DEV), nudge_period=128, schedule="chunked", chunk_len=128)
+    want = _gpu(x, cfg, schedule="chunked", chunk_len=128)
+    for a_, b_ in zip(got, want):
+        assert torch.equal(a_, b_)
+    check("gpu-chunked128", cfg, got, run_oracle(x, cfg), say=_say)
