@@ -881,7 +881,6 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         else
           rank_update<TIn>(X, fr, sW[g ^ 1], sSig[g ^ 1], ln >> 5);
       }
-      if constexpr (!kBf) fr.load(pl, blk0 + b, ti, tj, ln);   // block b's, for the next update
       {
         const int xs_off = ((ti * 32 + 4 * (ln >> 5)) * kD + tj * 32 + (ln & 31)) * 4;
         const auto rs = make_rsrc(pl.Xsnap + (blk0 + b) * kD * kD, kD * kD * 4);
@@ -898,6 +897,10 @@ vla_state_chain_kernel(StatePlan pl, ChainSeg sg, float* __restrict__ S_T, float
         bilinear_terms<TIn>(X, reinterpret_cast<const char*>(rows_vr(RGp1)), reinterpret_cast<const float*>(rows_ar(RGp1)),
                             sH[g ^ 1] + m * kLb, ti, tj, ln);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies have landed
+      // fp32 storage: block b's update operands, for the next block's update,
+      // loaded only now so that they are not live through the bilinear terms
+      // (they land while the recursion wave runs the next block).
+      if constexpr (!kBf) fr.load(pl, blk0 + b, ti, tj, ln);
     }
     // The block's closing barrier, without the fence of __syncthreads: that
     // fence would also hold the recursion wave until its Kx copies land.
