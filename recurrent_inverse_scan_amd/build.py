@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["vla_abi.hip", "scan_seq.hip", "chunked.hip", "state_pass.hip", "inverse_wy.hip", "residual_pass.hip",
-           "decode.hip", "scan_split.hip", "project_u.hip", "validate.hip", "backward.hip", "linear_state.hip"]
+           "decode.hip", "scan_split.hip", "project_u.hip", "validate.hip", "backward.hip", "linear_state.hip",
+           "inverse_wy128.hip"]
 
 # Packed-FP32 instructions stay off: hipcc would otherwise form v_pk_fma_f32
 # and friends from ordinary float code.

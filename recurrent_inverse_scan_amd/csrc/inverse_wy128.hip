@@ -1,0 +1,423 @@
+// Inverse pass of the time-parallel schedule in blocked form at d = 128 (bf16
+// storage, any rank r <= 4), on the gfx950 matrix cores.
+//
+// Method ("Mathematical Primitives", sections 2-3: rank-1 Sherman-Morrison
+// tracking of A = M^{-1}, r sequential updates per token; section 4:
+// alpha_t = A_t k_t; "Variational Linear Attention (VLA)" README, v3 notes:
+// alpha_hat = alpha / max(|alpha|, 1)).  As in the d = 64 blocked pass
+// (inverse_wy.hip), a block of m = r B directions u_j (B tokens, r each, in
+// token order) starting from A_b composes exactly (Woodbury): with
+// C = U^T A_b U and I + C = L D L^T,
+//   delta_j = D_jj,
+//   alpha_t = A_b k_t - X_U G[:, t],   G = L^{-T} D^{-1} ((L^{-1} U^T A_b K) o M),
+//   M_jt = [j <= r t + r - 1]  (the directions of token t and the ones before),
+//   A_{b+1} = A_b - X_U W X_U^T,  W = (I + C)^{-1},  X_U = A_b U.
+// A guard fire (|delta| < eps) flags the chain for the sequential fallback.
+//
+// Four waves per chunk; B = 32 / r tokens per block (m <= 32 directions, one
+// 32-wide matrix-core tile).  Wave w holds the column slab of A_b with
+// feature block w, four 32 x 32 accumulator tiles (F, w), F = 0..3, in the
+// permuted feature basis of the d = 64 kernel (bits 2 and 3 of a feature
+// index swapped): A_b is symmetric, so a tile read as the A operand is the
+// block it transposes to, and u and k rows enter as plain 16-byte pieces.
+// Per block:
+//   1. X_U and X_K for the wave's feature block (products over all four of
+//      its tiles), and its share of C = U^T X_U and E = U^T X_K;
+//   2. wave 0 sums the shares and runs the LDL^T elimination of I + C (the
+//      d = 64 kernel's, two pivots per LDS round trip), forming W and G; the
+//      other waves transpose their X_U tile through LDS into X_U^T;
+//   3. P^T = W X_U^T and alpha = X_K - X_U G per feature block;
+//   4. A_b -= P^T X_U^T with every wave's P^T tile read from LDS, and
+//      alpha_hat written once the per-token norms are summed over the waves.
+// Products with fp32 operands use three-term bf16 splits (fp32-grade).
+#include "vla_common.h"
+#include "vla_kernels.h"
+#include "vla_mfma.h"
+#include "vla_seq.h"
+#include "vla_wide.h"
+
+namespace vla {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kM = 32;        // directions per block (one tile)
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXtLd = 36;     // row stride (floats) of the X_U transpose staging
+
+// Feature held at basis index b: bits 2 and 3 swapped (an involution).
+__host__ __device__ constexpr int feat(int b) { return (b & ~12) | ((b & 4) << 1) | ((b & 8) >> 1); }
+
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+// Workgroup barrier after this wave's LDS operations (global loads may stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// bf16 element e (0..7) of a 16-byte operand, as fp32.
+__device__ __forceinline__ float frag_elem(const uint4& f, int e) {
+  const uint32_t w = e < 2 ? f.x : e < 4 ? f.y : e < 6 ? f.z : f.w;
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+__device__ __forceinline__ uint4 as_u4(float4 a) {
+  return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
+}
+
+// An accumulator tile stored per lane (16 values), and read back.
+__device__ __forceinline__ void put_tile(float* p, const f32x16& x, int lane) {
+  float4* q = reinterpret_cast<float4*>(p + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+__device__ __forceinline__ f32x16 get_tile(const float* p, int lane) {
+  const float4* q = reinterpret_cast<const float4*>(p + 16 * lane);
+  f32x16 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = q[i];
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+  }
+  return x;
+}
+
+struct Lds128 {
+  float4 tok[2][8][64];              // [u / k][k step kp][lane (c, h)]: features 16 kp + 8 h .. of direction / key c
+  float part[2][kWaves - 1][64 * 16];  // waves 1..3's shares of C and E
+  float wg[2][64 * 16];               // W and G from wave 0
+  float xt[kWaves][32 * kXtLd];       // X_U transpose staging, later the wave's P^T tile
+  float nrm[kWaves][32];              // per-token |alpha|^2 over each wave's features
+  float xk0[64 * 16];                 // wave 0's X_K tile, held here through the elimination
+  float4 sCol[2][2][4];               // elimination (wave 0): pivot columns k, k + 1
+  float4 sRow[kM][2];                 // pivot rows k, k + 1 of (I + C, E, T) at column c
+  float sDinv[kM];                    // 1 / pivot
+};
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restrict__ ux,
+                         const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
+                         int32_t* __restrict__ chain_info, int T, int r, int L, int nchunks, int chunk_lo,
+                         int chunk_cnt, float eps, int nudge_period, int nudge_phase0) {
+  __shared__ __attribute__((aligned(16))) Lds128 sm;
+  const int64_t chain = blockIdx.x / chunk_cnt;
+  const int chunk = chunk_lo + static_cast<int>(blockIdx.x % chunk_cnt);
+  const int tbeg = chunk * L, tend = min(T, tbeg + L);
+  const int tid = threadIdx.x, lane0 = tid & 63, c0 = lane0 & 31, h0 = lane0 >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = kM / r;          // tokens per block
+  const int m = B * r;           // directions per block
+
+  // ---- A_b: tile F slot s = A[feat(32 F + acc_row(s, h))][feat(32 w + c)].
+  // Slot s = 4 q + e sits at row 32 F + 16 (q >> 1) + 8 h + 4 (q & 1) + e.
+  const int a_voff = (8 * h0 * kD + feat(c0)) * 4;
+  auto a_soff = [&](int F, int s) {
+    const int q = s >> 2, e = s & 3;
+    return ((32 * F + 16 * (q >> 1) + 4 * (q & 1) + e) * kD + 32 * w) * 4;
+  };
+  f32x16 Acc[4];
+  {
+    const auto ra = make_rsrc(a_start + (chain * nchunks + chunk) * kD * kD, kD * kD * 4);
+#pragma unroll
+    for (int F = 0; F < 4; ++F)
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        Acc[F][s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, a_voff, a_soff(F, s), 0));
+  }
+
+  // Token rows go from HBM straight into LDS: wave w copies k steps 2 w and
+  // 2 w + 1 of the block's u and k rows; lane (c, h) takes features
+  // 16 kp + 8 h .. + 7 of direction c (u) and of token c (k).  The buffers
+  // end at the chunk's last token, and lanes with no direction or token read
+  // past the end, so their rows are zero.
+  const int64_t row0 = chain * T + tbeg;
+  const int ubytes = (tend - tbeg) * r * kD * 2, kbytes = (tend - tbeg) * kD * 2;
+  const auto ru = make_rsrc(ux + row0 * r * kD, ubytes);
+  const auto rk = make_rsrc(kx + row0 * kD, kbytes);
+  auto copy_tokens = [&](int tb) {
+    const int ou = c0 < m ? (((tb - tbeg) * r + c0) * kD + 8 * h0) * 2 : ubytes;
+    const int ok = c0 < B ? ((tb - tbeg + c0) * kD + 8 * h0) * 2 : kbytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kp = 2 * w + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)&sm.tok[0][kp][0], 16, ou + 32 * kp, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&sm.tok[1][kp][0], 16, ok + 32 * kp, 0, 0, 0);
+    }
+  };
+
+  const bool nudge_last = nudge_period > 0 && tend > tbeg && (nudge_phase0 + tend - 1) % nudge_period == 0;
+  int guard = 0;
+  bool bad = false;
+  copy_tokens(tbeg);
+
+  for (int tb = tbeg; tb < tend; tb += B) {
+    int c = c0, h = h0;
+    asm volatile("" : "+v"(c), "+v"(h));
+    const int lane = c + 32 * h;
+    // Every wave's copies of the block's rows have landed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+
+    // ---- 1. X_U = A U and X_K = A K on this wave's feature block (rows:
+    // basis features 32 w.., columns: directions / tokens), and its shares
+    // of C = U^T X_U and E = U^T X_K.
+    f32x16 XU = zero16(), XK = zero16();
+#pragma unroll
+    for (int F = 0; F < 4; ++F)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int kp = 2 * F + g;
+        const bf16x8 ub = __builtin_bit_cast(bf16x8, as_u4(sm.tok[0][kp][lane]));
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, as_u4(sm.tok[1][kp][lane]));
+        const Split3 af = split_slots(Acc[F], g);
+        XU = mma_split(af, ub, XU);
+        XK = mma_split(af, kb, XK);
+        sched_fence();
+      }
+    f32x16 Cm = zero16(), Em = zero16();
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bf16x8 ub = __builtin_bit_cast(bf16x8, as_u4(sm.tok[0][2 * w + g][lane]));
+      Cm = mma_split(ub, split_slots(XU, g), Cm);
+      Em = mma_split(ub, split_slots(XK, g), Em);
+    }
+    if (w > 0) {
+      put_tile(sm.part[0][w - 1], Cm, lane);
+      put_tile(sm.part[1][w - 1], Em, lane);
+    }
+    lds_barrier();
+
+    // ---- 2. Wave 0: the elimination, W and G.  Every wave: X_U^T through
+    // its LDS staging tile, X_U^T[j][f] = X_U[f][j] (X_U is staged first, so
+    // it is not live through the elimination; nor is wave 0's X_K).
+    float* xt = sm.xt[w];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) xt[acc_row(s, h) * kXtLd + c] = XU[s];
+    if (w == 0) {
+      put_tile(sm.xk0, XK, lane);
+      // C and E summed over the waves in a fixed order.
+#pragma unroll
+      for (int j = 0; j < kWaves - 1; ++j) {
+        const f32x16 pc = get_tile(sm.part[0][j], lane), pe = get_tile(sm.part[1][j], lane);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          Cm[s] += pc[s];
+          Em[s] += pe[s];
+        }
+      }
+      // Lane (c, h) holds column c of I + C, E and T (the identity, becoming
+      // L^{-1}); pivot k sits in lane half (k >> 2) & 1, slot 4 (k >> 3) + (k & 3).
+      float cm[16], em[16], tm[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const bool dg = acc_row(s, h) == c;
+        cm[s] = Cm[s] + (dg ? 1.f : 0.f);
+        em[s] = Em[s];
+        tm[s] = dg ? 1.f : 0.f;
+      }
+      const float hf = static_cast<float>(h);
+      // Two pivots per LDS round trip: the lanes get columns k and k + 1 and
+      // rows k and k + 1 as they stood before pivot k, and apply pivot k to
+      // their copies of column and row k + 1 themselves.
+#pragma unroll
+      for (int k = 0; k < kM; k += 2) {
+        const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3);
+        if (c == k || c == k + 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            sm.sCol[c - k][h][q] = make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
+        }
+        if (h == hk) {
+          sm.sRow[c][0] = make_float4(cm[sk], em[sk], tm[sk], cm[sk + 1]);
+          sm.sRow[c][1] = make_float4(em[sk + 1], tm[sk + 1], 0.f, 0.f);
+        }
+        lds_order();
+        float na[16], nb[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = sm.sCol[0][h][q], u4 = sm.sCol[1][h][q];
+          na[4 * q] = v.x; na[4 * q + 1] = v.y; na[4 * q + 2] = v.z; na[4 * q + 3] = v.w;
+          nb[4 * q] = u4.x; nb[4 * q + 1] = u4.y; nb[4 * q + 2] = u4.z; nb[4 * q + 3] = u4.w;
+        }
+        const float2 pa = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[0][hk]) + sk);
+        const float2 pb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[1][hk]) + sk);
+        const float4 r0 = sm.sRow[c][0], r1 = sm.sRow[c][1];
+        float ia = __builtin_amdgcn_rcpf(pa.x);
+        ia = fmaf(fmaf(-pa.x, ia, 1.f), ia, ia);
+        const float a0 = r0.x * ia, a1 = r0.y * ia, a2 = r0.z * ia;
+        const float q0 = fmaf(-pa.y, a0, r0.w), q1 = fmaf(-pa.y, a1, r1.x), q2 = fmaf(-pa.y, a2, r1.y);
+        const float gab = pb.x * ia;
+        const float pk1 = fmaf(-pa.y, gab, pb.y);
+        float ib = __builtin_amdgcn_rcpf(pk1);
+        ib = fmaf(fmaf(-pk1, ib, 1.f), ib, ib);
+        const float b0 = q0 * ib, b1 = q1 * ib, b2 = q2 * ib;
+        guard += (fabsf(pa.x) < eps ? 1 : 0) + (fabsf(pk1) < eps ? 1 : 0);
+        asm volatile("" : "+v"(guard));
+        if (lane == 0) {
+          sm.sDinv[k] = ia;
+          sm.sDinv[k + 1] = ib;
+        }
+        lds_order();
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const int base = 8 * (s >> 2) + (s & 3);   // row of slot s is base + 4 h
+          if (base + 4 <= k) continue;
+          const float xa = base > k ? na[s] : na[s] * hf;
+          cm[s] = fmaf(-xa, a0, cm[s]);
+          em[s] = fmaf(-xa, a1, em[s]);
+          tm[s] = fmaf(-xa, a2, tm[s]);
+          if (base + 4 > k + 1) {
+            const float nk = fmaf(-na[s], gab, nb[s]);
+            const float xb = base > k + 1 ? nk : nk * hf;
+            cm[s] = fmaf(-xb, b0, cm[s]);
+            em[s] = fmaf(-xb, b1, em[s]);
+            tm[s] = fmaf(-xb, b2, tm[s]);
+          }
+          asm volatile("" : "+v"(cm[s]), "+v"(em[s]), "+v"(tm[s]));
+        }
+      }
+      // W = T^T D^{-1} T and G = T^T D^{-1} (F o M), T = L^{-1}, F = L^{-1} E,
+      // M_jt = [j <= r t + r - 1].
+      float dv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(sm.sDinv + 8 * q + 4 * h);
+        dv[4 * q] = v.x; dv[4 * q + 1] = v.y; dv[4 * q + 2] = v.z; dv[4 * q + 3] = v.w;
+      }
+      f32x16 Wm = zero16(), Gm = zero16();
+      const int jlast = r * c + r - 1;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float td[8], tt[8], ff[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = 8 * g + e;
+          td[e] = tm[s] * dv[s];
+          tt[e] = tm[s];
+          ff[e] = acc_row(s, h) <= jlast ? em[s] : 0.f;
+        }
+        const Split3 TD = split3(td);
+        Wm = mma_split(TD, split3(tt), Wm);
+        Gm = mma_split(TD, split3(ff), Gm);
+      }
+      put_tile(sm.wg[0], Wm, lane);
+      put_tile(sm.wg[1], Gm, lane);
+      lds_order();
+      XK = get_tile(sm.xk0, lane);
+    }
+    lds_order();
+    f32x16 XT;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(xt + c * kXtLd + 8 * q + 4 * h);
+      XT[4 * q] = v.x; XT[4 * q + 1] = v.y; XT[4 * q + 2] = v.z; XT[4 * q + 3] = v.w;
+    }
+    lds_barrier();
+
+    // ---- 3. P^T = W X_U^T (directions x features) and alpha = X_K - X_U G.
+    const f32x16 Wm = get_tile(sm.wg[0], lane), Gm = get_tile(sm.wg[1], lane);
+    Split3 XS[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) XS[g] = split_slots(XT, g);
+    f32x16 PT = zero16();
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      PT = mma_split(split_slots(Wm, g), XS[g], PT);
+      XK = mma_split(XS[g], split_slots(Gm, g, -1.f), XK);
+      sched_fence();
+    }
+    const int tcount = min(B, tend - tb);
+    const bool last_block = tb + B >= tend;
+    if (nudge_last && last_block && c == tcount - 1) {
+      // The chunk's last token is nudged: alpha = (A + eps I) k.
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint4 kf = as_u4(sm.tok[1][2 * w + (s >> 3)][lane]);
+        XK[s] = fmaf(eps, frag_elem(kf, s & 7), XK[s]);
+      }
+    }
+    {
+      float nrm = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) nrm = fmaf(XK[s], XK[s], nrm);
+      nrm += __shfl_xor(nrm, 32);
+      if (h == 0) sm.nrm[w][c] = nrm;
+    }
+    // The wave's P^T tile for every wave's update (over its own staging tile:
+    // its transpose reads are done).
+    put_tile(sm.xt[w], PT, lane);
+    lds_barrier();
+
+    // The next block's rows (every read of this block's rows is done).
+    if (!last_block) copy_tokens(tb + B);
+
+    // ---- 4. A_{b+1} = A_b - P^T X_U^T, and alpha_hat of the block's tokens.
+#pragma unroll
+    for (int F = 0; F < 4; ++F) {
+      const f32x16 PF = get_tile(sm.xt[F], lane);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) Acc[F] = mma_split(split_slots(PF, g, -1.f), XS[g], Acc[F]);
+      sched_fence();
+    }
+    if (c < tcount) {
+      const float n2 = (sm.nrm[0][c] + sm.nrm[1][c]) + (sm.nrm[2][c] + sm.nrm[3][c]);
+      const float ascale = n2 > 1.f ? 1.f / sqrtf(n2) : 1.f;
+      float* dst = alpha_out + (chain * T + tb + c) * kD;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = make_float4(XK[4 * q] * ascale, XK[4 * q + 1] * ascale, XK[4 * q + 2] * ascale,
+                                     XK[4 * q + 3] * ascale);
+        bad |= !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+        *reinterpret_cast<float4*>(dst + feat(32 * w + 4 * (2 * q + h))) = v;
+      }
+    }
+  }
+
+  // ---- the chunk's end state: nudge, and A_T from the last chunk.
+  if (nudge_last) {
+#pragma unroll
+    for (int F = 0; F < 4; ++F) {   // the diagonal tile (w, w); F stays a constant index
+      if (F == w) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) Acc[F][s] += acc_row(s, h0) == c0 ? eps : 0.f;
+      }
+    }
+  }
+  if (chunk == nchunks - 1) {
+    const auto rt = make_rsrc(A_T + chain * kD * kD, kD * kD * 4);
+#pragma unroll
+    for (int F = 0; F < 4; ++F)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const float v = Acc[F][s];
+        bad |= !isfinite(v);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rt, a_voff, a_soff(F, s), 0);
+      }
+  }
+  const bool wave_bad = __any(bad);
+  if (lane0 == 0) {
+    int32_t* info = chain_info + chain * 4;
+    if (guard > 0) {   // (only wave 0 counts pivots)
+      atomicAdd(info + kInfoGuard, guard);
+      atomicOr(info + kInfoFallback, 1);
+    }
+    if (wave_bad) atomicOr(info + kInfoNonfinite, 1);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_inverse_wy128(const ScanArgs& a, const float* a_start, float* alpha_out, int32_t* chain_info,
+                                int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, int chains,
+                                hipStream_t stream) {
+  if (chunk_cnt <= 0) return hipSuccess;
+  if (a.residual || a.r < 1 || a.r > 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vla_inverse_wy128_kernel, dim3(static_cast<unsigned>(chains * chunk_cnt)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.u), a_start, alpha_out,
+                     a.A_T, chain_info, a.T, a.r, chunk_len, nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period,
+                     a.nudge_phase0);
+  return hipGetLastError();
+}
+
+}  // namespace vla

@@ -11,6 +11,7 @@
 
 #include "../../include/vla.h"
 #include "vla_kernels.h"
+#include "vla_wide.h"
 #include "vla_residual.h"
 
 namespace {
@@ -617,7 +618,10 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
   // (The inverse pass below writes the residual update's unit gates when
   // a.residual is set.)
-  if (bf16 && p->r == 1 && d == 64)
+  if (d == 128)
+    e = vla::launch_inverse_wy128(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
+                                  static_cast<int>(chains), stream);
+  else if (bf16 && p->r == 1 && d == 64)
     e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
                                static_cast<int>(chains), stream);
   else
