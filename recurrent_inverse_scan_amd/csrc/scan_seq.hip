@@ -52,16 +52,8 @@ namespace vla {
 // Scalars of the blocked rank-r update: u_i . w_l (4 x 4) and k . w_l (4).
 constexpr int kBlkScalars = 20;
 
-// Waves per SIMD the register allocation must leave room for.  The inverse
-// pass at d = 128 runs thousands of chunks, one eight-wave workgroup each:
-// two workgroups per compute unit overlap one's barriers and scalar
-// recurrence with the other's matrix-vector sweeps.
-constexpr int seq_min_waves(int D, int NW, SeqMode m) {
-  return (m == SeqMode::kInverseOnly && D == 128) ? 2 * NW / 4 : 1;
-}
-
 template <typename TIn, int D, int NW, int CG, SeqMode MODE, bool RES>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(seq_min_waves(D, NW, MODE))))
+__global__ void __launch_bounds__(64 * NW)
 vla_scan_seq_kernel(ScanArgs a, SeqExtra x) {
   static_assert(!RES || MODE == SeqMode::kFull, "the residual update runs in the full recurrence only");
   using L = TileLayout<D, NW, CG>;
@@ -759,8 +751,7 @@ static hipError_t dispatch_seq(const ScanArgs& a, const SeqExtra& x, int d, int 
   } else {
     switch (d) {
       case 64: return launch_seq<TIn, 64, 1, 4, MODE>(a, x, chains, stream);
-      case 128: return launch_seq<TIn, 128, 8, 8, MODE>(a, x, chains, stream);
-      default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;   // d = 128 runs the blocked pass (inverse_wy128.hip)
     }
   }
 }
