@@ -66,18 +66,20 @@ __device__ __forceinline__ uint4 as_u4(float4 a) {
   return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
-// An accumulator tile stored per lane (16 values), and read back.
+// An accumulator tile stored per lane (16 values), and read back: slots
+// 4 i .. 4 i + 3 of every lane form one 1 KiB row (lane-consecutive 16-byte
+// pieces, so the accesses do not collide on LDS banks).
 __device__ __forceinline__ void put_tile(float* p, const f32x16& x, int lane) {
-  float4* q = reinterpret_cast<float4*>(p + 16 * lane);
+  float4* q = reinterpret_cast<float4*>(p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  for (int i = 0; i < 4; ++i) q[64 * i + lane] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
 }
 __device__ __forceinline__ f32x16 get_tile(const float* p, int lane) {
-  const float4* q = reinterpret_cast<const float4*>(p + 16 * lane);
+  const float4* q = reinterpret_cast<const float4*>(p);
   f32x16 x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 v = q[i];
+    const float4 v = q[64 * i + lane];
     x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
   }
   return x;
