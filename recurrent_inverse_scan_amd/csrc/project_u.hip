@@ -6,11 +6,12 @@
 //
 // As a GEMM: Out[rows, r*d] = K_raw[rows, d] . W^T with W = W_u viewed as
 // [r*d, d]; K = d is short, so the kernel is bound by streaming k_raw in and
-// u out of HBM.  Each wave computes 32 rows x d columns of one direction with
-// 32x32 MFMA tiles (bf16: 32x32x16, fp32: 32x32x2, both accumulating in
-// fp32), keeps its k_raw rows in registers across the r directions, and
-// normalises in the epilogue, after the tile has gone through the wave's LDS
-// into pieces of whole rows (see finish_tile).
+// u out of HBM.  A wave computes tiles of 32 rows x d columns of one direction
+// with 32x32 MFMA tiles (bf16: 32x32x16, fp32: 32x32x2, both accumulating in
+// fp32) and normalises them in the epilogue, after the tile has gone through
+// the wave's LDS into pieces of whole rows (see finish_tile).  The bf16
+// kernel holds one direction's W in registers over a run of row tiles; the
+// fp32 kernel (small workloads) keeps its k_raw rows across the r directions.
 //
 // MFMA 32x32 accumulator layout: lane l holds column l % 32 of the tile and,
 // in accumulator slot a, row 8*(a/4) + 4*(l/32) + a%4.  Operand A holds row
@@ -32,25 +33,18 @@ constexpr int kProjWaves = 4;
 template <int D>
 constexpr int stage_ld() { return D + 4; }
 
-// Normalises the wave's 32 rows of direction i and writes them.  The raw
-// tile goes through the wave's LDS first; then each lane takes pieces of
-// eight consecutive values of a row (the lanes of one row are D/8
-// consecutive lanes), so a row's sum of squares is one short DPP group sum
-// and each lane normalises and stores whole 16-byte (bf16) or 32-byte
-// (fp32) pieces.  (Normalising in the accumulator layout took a 32-lane
-// reduction per accumulator slot, 16 per tile.)
+// Normalises the wave's 32 rows of direction i, staged raw in the wave's LDS
+// tile, and writes them: each lane takes pieces of eight consecutive values of
+// a row (the lanes of one row are D/8 consecutive lanes), so a row's sum of
+// squares is one short DPP group sum and each lane normalises and stores
+// whole 16-byte (bf16) or 32-byte (fp32) pieces.  (Normalising in the
+// accumulator layout took a 32-lane reduction per accumulator slot, 16 per
+// tile.)
 template <int D, typename TOut>
-__device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_base, int64_t rows, int r,
-                                            int i, int lane, TOut* u, float* tile) {
-  constexpr int LD = stage_ld<D>();
-  const int col = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int rl = 8 * (s / 4) + 4 * hi + (s % 4);
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) tile[rl * LD + nb * 32 + col] = acc[nb][s];
-  }
+__device__ __forceinline__ void normalize_store(int64_t row_base, int64_t rows, int r, int i, int lane, TOut* u,
+                                                const float* tile) {
   asm volatile("" ::: "memory");   // one wave's LDS operations complete in order
+  constexpr int LD = stage_ld<D>();
   constexpr int PPR = D / 8;       // pieces of eight values per row
   static_assert((32 * PPR) % 64 == 0 && 64 % PPR == 0, "whole rows per lane group");
 #pragma unroll
@@ -82,38 +76,92 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_b
   asm volatile("" ::: "memory");   // the reads finish before the next direction's writes
 }
 
-// bf16 inputs: v_mfma_f32_32x32x16_bf16, 8 bf16 of k per lane per tile.
+// Column block nb of the raw tile into the wave's LDS staging tile.
+template <int D>
+__device__ __forceinline__ void stage_block(const f32x16& acc, int nb, int lane, float* tile) {
+  constexpr int LD = stage_ld<D>();
+  const int col = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) tile[(8 * (s / 4) + 4 * hi + (s % 4)) * LD + nb * 32 + col] = acc[s];
+}
+
+// The whole raw tile (D / 32 accumulator blocks) staged, normalised and stored.
 template <int D, typename TOut>
-__global__ void __launch_bounds__(64 * kProjWaves)
-project_u_bf16_kernel(int64_t rows, int r, const uint16_t* __restrict__ W, const uint16_t* __restrict__ kraw,
-                      TOut* __restrict__ u) {
-  constexpr int KB = D / 16;
+__device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_base, int64_t rows, int r,
+                                            int i, int lane, TOut* u, float* tile) {
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) stage_block<D>(acc[nb], nb, lane, tile);
+  normalize_store<D, TOut>(row_base, rows, r, i, lane, u, tile);
+}
+
+// Consecutive 32-row tiles per wave of the bf16 kernel (its W slice is loaded
+// once per run of tiles).
+template <int D>
+constexpr int proj_tiles_per_wave() { return D >= 128 ? 16 : 8; }
+
+// bf16 inputs: v_mfma_f32_32x32x16_bf16, 8 bf16 of k per lane per tile.  Each
+// wave owns one direction i and a run of consecutive 32-row tiles, and keeps
+// W_i (D x D, as B operands) in its registers for the whole run: W is read
+// once per run rather than once per tile (at d = 128, r = 4 the per-tile
+// reloads came to 128 KiB of cache reads per 32 rows, several times the
+// kernel's HBM bytes).  Consecutive waves take the r directions of the same
+// rows, so a workgroup's k_raw rows are shared through the cache.  The next
+// tile's k_raw rows are loaded while the current tile is normalised and stored.
+template <int D, typename TOut>
+__global__ void __launch_bounds__(64 * kProjWaves) __attribute__((amdgpu_waves_per_eu(2)))
+project_u_bf16_kernel(int64_t rows, int r, int64_t nruns, const uint16_t* __restrict__ W,
+                      const uint16_t* __restrict__ kraw, TOut* __restrict__ u) {
+  constexpr int KB = D / 16, NB = D / 32, TPW = proj_tiles_per_wave<D>();
+  constexpr int NP = NB >= 2 ? 2 : 1;   // column blocks per accumulation round
   __shared__ float tiles[kProjWaves][32 * stage_ld<D>()];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row_base = (static_cast<int64_t>(blockIdx.x) * kProjWaves + w) * 32;
-  const int64_t arow = row_base + (lane & 31);
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kProjWaves + w;
+  const int64_t run = g / r;
+  const int i = static_cast<int>(g - run * r);
+  // Waves past the last run have nothing to do (the kernel has no workgroup
+  // barrier: each wave stages through its own LDS tile).
+  if (run >= nruns) return;
   const int koff = 8 * (lane >> 5);
 
-  bf16x8 a[KB];
+  bf16x8 b[NB][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (arow < rows) x = *reinterpret_cast<const uint4*>(kraw + arow * D + kb * 16 + koff);
-    a[kb] = __builtin_bit_cast(bf16x8, x);
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint16_t* wrow = W + (static_cast<int64_t>(i) * D + nb * 32 + (lane & 31)) * D + koff;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) b[nb][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + kb * 16));
   }
-  for (int i = 0; i < r; ++i) {
-    f32x16 acc[D / 32];
+  const int64_t ntiles = (rows + 31) / 32;
+  const int64_t t0 = run * TPW, t1 = t0 + TPW < ntiles ? t0 + TPW : ntiles;
+  bf16x8 a[KB];
+  auto load_a = [&](int64_t t) {
+    const int64_t arow = t * 32 + (lane & 31);
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) {
-      acc[nb] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const uint16_t* wrow = W + (static_cast<int64_t>(i) * D + nb * 32 + (lane & 31)) * D + koff;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + kb * 16));
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b, acc[nb], 0, 0, 0);
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (arow < rows) x = *reinterpret_cast<const uint4*>(kraw + arow * D + kb * 16 + koff);
+      a[kb] = __builtin_bit_cast(bf16x8, x);
     }
-    finish_tile<D, TOut>(acc, row_base, rows, r, i, lane, u, tiles[w]);
+  };
+  load_a(t0);
+  for (int64_t t = t0; t < t1; ++t) {
+    // Two column blocks at a time (two independent accumulation chains),
+    // staged as soon as they are done: two accumulator tiles live beside W_i.
+#pragma unroll
+    for (int nb = 0; nb < NB; nb += NP) {
+      f32x16 acc[NP];
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        acc[j] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b[nb + j][kb], acc[j], 0, 0, 0);
+      if (nb + NP == NB && t + 1 < t1) load_a(t + 1);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) stage_block<D>(acc[j], nb + j, lane, tiles[w]);
+    }
+    normalize_store<D, TOut>(t * 32, rows, r, i, lane, u, tiles[w]);
   }
 }
 
@@ -182,11 +230,14 @@ hipError_t launch_proj(int64_t rows, int r, const void* W, const void* kraw, voi
     hipLaunchKernelGGL((project_u_d16_kernel<TIn, TOut>), dim3(grid), dim3(256), 0, s, rows, r,
                        static_cast<const TIn*>(W), static_cast<const TIn*>(kraw), static_cast<TOut*>(u));
   } else {
-    const unsigned grid = static_cast<unsigned>((rows + 32 * kProjWaves - 1) / (32 * kProjWaves));
     if constexpr (sizeof(TIn) == 2) {
-      hipLaunchKernelGGL((project_u_bf16_kernel<D, TOut>), dim3(grid), dim3(64 * kProjWaves), 0, s, rows, r,
+      constexpr int TPW = proj_tiles_per_wave<D>();
+      const int64_t nruns = ((rows + 31) / 32 + TPW - 1) / TPW;
+      const unsigned grid = static_cast<unsigned>((nruns * r + kProjWaves - 1) / kProjWaves);
+      hipLaunchKernelGGL((project_u_bf16_kernel<D, TOut>), dim3(grid), dim3(64 * kProjWaves), 0, s, rows, r, nruns,
                          static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(kraw), static_cast<TOut*>(u));
     } else {
+      const unsigned grid = static_cast<unsigned>((rows + 32 * kProjWaves - 1) / (32 * kProjWaves));
       hipLaunchKernelGGL((project_u_f32_kernel<D, TOut>), dim3(grid), dim3(64 * kProjWaves), 0, s, rows, r,
                          static_cast<const float*>(W), static_cast<const float*>(kraw), static_cast<TOut*>(u));
     }
