@@ -26,6 +26,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kProjWaves = 4;
 
@@ -40,9 +41,8 @@ constexpr int stage_ld() { return D + 4; }
 // whole 16-byte (bf16) or 32-byte (fp32) pieces.  (Normalising in the
 // accumulator layout took a 32-lane reduction per accumulator slot, 16 per
 // tile.)
-template <int D, typename TOut>
-__device__ __forceinline__ void normalize_store(int64_t row_base, int64_t rows, int r, int i, int lane, TOut* u,
-                                                const float* tile) {
+template <int D, typename Store>
+__device__ __forceinline__ void normalize_rows(int lane, const float* tile, Store&& store) {
   asm volatile("" ::: "memory");   // one wave's LDS operations complete in order
   constexpr int LD = stage_ld<D>();
   constexpr int PPR = D / 8;       // pieces of eight values per row
@@ -61,19 +61,33 @@ __device__ __forceinline__ void normalize_store(int64_t row_base, int64_t rows, 
     const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= inv;
-    const int64_t row = row_base + rl;
-    if (row < rows) {
-      TOut* dst = u + (row * r + i) * D + pc * 8;
-      if constexpr (sizeof(TOut) == 4) {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-      }
-    }
+    store(rl, pc, v);
   }
-  asm volatile("" ::: "memory");   // the reads finish before the next direction's writes
+  asm volatile("" ::: "memory");   // the reads finish before the next tile's writes
+}
+
+// Eight output values as 16 (bf16) or 32 (fp32) bytes.
+template <typename TOut>
+__device__ __forceinline__ void put8(TOut* dst, const float (&v)[8]) {
+  if constexpr (sizeof(TOut) == 4) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  }
+}
+template <typename TOut>
+__device__ __forceinline__ void buf_put8(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[8]) {
+  if constexpr (sizeof(TOut) == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                 __float_as_uint(v[3])}, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                                 __float_as_uint(v[7])}, rs, off + 16, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])}, rs, off, 0, 0);
+  }
 }
 
 // Column block nb of the raw tile into the wave's LDS staging tile.
@@ -91,7 +105,10 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[D / 32], int64_t row_b
                                             int i, int lane, TOut* u, float* tile) {
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) stage_block<D>(acc[nb], nb, lane, tile);
-  normalize_store<D, TOut>(row_base, rows, r, i, lane, u, tile);
+  normalize_rows<D>(lane, tile, [&](int rl, int pc, const float (&v)[8]) {
+    const int64_t row = row_base + rl;
+    if (row < rows) put8<TOut>(u + (row * r + i) * D + pc * 8, v);
+  });
 }
 
 // Consecutive 32-row tiles per wave of the bf16 kernel (its W slice is loaded
@@ -114,7 +131,7 @@ project_u_bf16_kernel(int64_t rows, int r, int64_t nruns, const uint16_t* __rest
   constexpr int KB = D / 16, NB = D / 32, TPW = proj_tiles_per_wave<D>();
   constexpr int NP = NB >= 2 ? 2 : 1;   // column blocks per accumulation round
   __shared__ float tiles[kProjWaves][32 * stage_ld<D>()];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kProjWaves + w;
   const int64_t run = g / r;
   const int i = static_cast<int>(g - run * r);
@@ -130,20 +147,23 @@ project_u_bf16_kernel(int64_t rows, int r, int64_t nruns, const uint16_t* __rest
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) b[nb][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + kb * 16));
   }
-  const int64_t ntiles = (rows + 31) / 32;
-  const int64_t t0 = run * TPW, t1 = t0 + TPW < ntiles ? t0 + TPW : ntiles;
+  // The run's rows through buffer resources over just those rows: loads past
+  // the last row read zeros and stores there are dropped, so the loop has no
+  // branches and its waits count only the k_raw loads it needs (stores also
+  // count toward vmcnt here).
+  const int64_t row0 = run * TPW * 32;
+  const int64_t nrow = rows - row0 < TPW * 32 ? rows - row0 : TPW * 32;
+  const int ntl = static_cast<int>((nrow + 31) / 32);
+  const auto rk = make_rsrc(kraw + row0 * D, static_cast<int>(nrow * D * 2));
+  const auto ru = make_rsrc(u + (row0 * r + i) * D, static_cast<int>(((nrow - 1) * r + 1) * D * sizeof(TOut)));
   bf16x8 a[KB];
-  auto load_a = [&](int64_t t) {
-    const int64_t arow = t * 32 + (lane & 31);
+  auto load_a = [&](int tl) {
+    const int off = ((tl * 32 + (lane & 31)) * D + koff) * 2;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (arow < rows) x = *reinterpret_cast<const uint4*>(kraw + arow * D + kb * 16 + koff);
-      a[kb] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int kb = 0; kb < KB; ++kb) a[kb] = __builtin_bit_cast(bf16x8, buf_load16(rk, off + 32 * kb));
   };
-  load_a(t0);
-  for (int64_t t = t0; t < t1; ++t) {
+  load_a(0);
+  for (int tl = 0; tl < ntl; ++tl) {
     // Two column blocks at a time (two independent accumulation chains),
     // staged as soon as they are done: two accumulator tiles live beside W_i.
 #pragma unroll
@@ -157,11 +177,13 @@ project_u_bf16_kernel(int64_t rows, int r, int64_t nruns, const uint16_t* __rest
 #pragma unroll
         for (int j = 0; j < NP; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b[nb + j][kb], acc[j], 0, 0, 0);
-      if (nb + NP == NB && t + 1 < t1) load_a(t + 1);
+      if (nb + NP == NB) load_a(tl + 1);   // past the run: zeros, unused
 #pragma unroll
       for (int j = 0; j < NP; ++j) stage_block<D>(acc[j], nb + j, lane, tiles[w]);
     }
-    normalize_store<D, TOut>(t * 32, rows, r, i, lane, u, tiles[w]);
+    normalize_rows<D>(lane, tiles[w], [&](int rl, int pc, const float (&v)[8]) {
+      buf_put8<TOut>(ru, (((tl * 32 + rl) * r) * D + pc * 8) * static_cast<int>(sizeof(TOut)), v);
+    });
   }
 }
 
