@@ -29,6 +29,8 @@
 //   3. P^T = W X_U^T and alpha = X_K - X_U G per feature block;
 //   4. A_b -= P^T X_U^T with every wave's P^T tile read from LDS, and
 //      alpha_hat written once the per-token norms are summed over the waves.
+// Tiles that every wave multiplies (W, G, P^T) cross LDS as three-term
+// splits made once by the wave that produced them.
 // Products with fp32 operands use three-term bf16 splits (fp32-grade).
 #include "vla_common.h"
 #include "vla_kernels.h"
@@ -85,11 +87,38 @@ __device__ __forceinline__ f32x16 get_tile(const float* p, int lane) {
   return x;
 }
 
+// A tile's three-term split as MFMA operands, [k step g][term][lane]: each
+// tile is split once, by the wave that produced it, and every wave reads the
+// terms (16 lane-consecutive bytes per read).
+typedef uint4 SplitTile[2][3][64];
+
+__device__ __forceinline__ void put_split(SplitTile& p, const f32x16& x, float scale, int lane) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const Split3 t = split_slots(x, g, scale);
+    p[g][0][lane] = __builtin_bit_cast(uint4, t.t1);
+    p[g][1][lane] = __builtin_bit_cast(uint4, t.t2);
+    p[g][2][lane] = __builtin_bit_cast(uint4, t.t3);
+  }
+}
+__device__ __forceinline__ Split3 get_split(const SplitTile& p, int g, int lane) {
+  Split3 t;
+  t.t1 = __builtin_bit_cast(bf16x8, p[g][0][lane]);
+  t.t2 = __builtin_bit_cast(bf16x8, p[g][1][lane]);
+  t.t3 = __builtin_bit_cast(bf16x8, p[g][2][lane]);
+  return t;
+}
+
 struct Lds128 {
   float4 tok[2][8][64];              // [u / k][k step kp][lane (c, h)]: features 16 kp + 8 h .. of direction / key c
-  float part[2][kWaves - 1][64 * 16];  // waves 1..3's shares of C and E
-  float wg[2][64 * 16];               // W and G from wave 0
-  float xt[kWaves][32 * kXtLd];       // X_U transpose staging, later the wave's P^T tile
+  union {
+    float part[2][kWaves - 1][64 * 16];   // phases 1-2: waves 1..3's shares of C and E
+    SplitTile wg[2];                      // phases 2-3: W and -G from wave 0 (after it has read the shares)
+  } pw;
+  union {
+    float xt[32 * kXtLd];             // X_U transpose staging
+    SplitTile pt;                     // then -P^T of the wave's feature block
+  } xp[kWaves];
   float nrm[kWaves][32];              // per-token |alpha|^2 over each wave's features
   float xk0[64 * 16];                 // wave 0's X_K tile, held here through the elimination
   float4 sCol[2][2][4];               // elimination (wave 0): pivot columns k, k + 1
@@ -185,15 +214,15 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
       Em = mma_split(ub, split_slots(XK, g), Em);
     }
     if (w > 0) {
-      put_tile(sm.part[0][w - 1], Cm, lane);
-      put_tile(sm.part[1][w - 1], Em, lane);
+      put_tile(sm.pw.part[0][w - 1], Cm, lane);
+      put_tile(sm.pw.part[1][w - 1], Em, lane);
     }
     lds_barrier();
 
     // ---- 2. Wave 0: the elimination, W and G.  Every wave: X_U^T through
     // its LDS staging tile, X_U^T[j][f] = X_U[f][j] (X_U is staged first, so
     // it is not live through the elimination; nor is wave 0's X_K).
-    float* xt = sm.xt[w];
+    float* xt = sm.xp[w].xt;
 #pragma unroll
     for (int s = 0; s < 16; ++s) xt[acc_row(s, h) * kXtLd + c] = XU[s];
     if (w == 0) {
@@ -201,7 +230,7 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
       // C and E summed over the waves in a fixed order.
 #pragma unroll
       for (int j = 0; j < kWaves - 1; ++j) {
-        const f32x16 pc = get_tile(sm.part[0][j], lane), pe = get_tile(sm.part[1][j], lane);
+        const f32x16 pc = get_tile(sm.pw.part[0][j], lane), pe = get_tile(sm.pw.part[1][j], lane);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           Cm[s] += pc[s];
@@ -303,8 +332,8 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
         Wm = mma_split(TD, split3(tt), Wm);
         Gm = mma_split(TD, split3(ff), Gm);
       }
-      put_tile(sm.wg[0], Wm, lane);
-      put_tile(sm.wg[1], Gm, lane);
+      put_split(sm.pw.wg[0], Wm, 1.f, lane);
+      put_split(sm.pw.wg[1], Gm, -1.f, lane);
       lds_order();
       XK = get_tile(sm.xk0, lane);
     }
@@ -318,15 +347,14 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
     lds_barrier();
 
     // ---- 3. P^T = W X_U^T (directions x features) and alpha = X_K - X_U G.
-    const f32x16 Wm = get_tile(sm.wg[0], lane), Gm = get_tile(sm.wg[1], lane);
     Split3 XS[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) XS[g] = split_slots(XT, g);
     f32x16 PT = zero16();
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      PT = mma_split(split_slots(Wm, g), XS[g], PT);
-      XK = mma_split(XS[g], split_slots(Gm, g, -1.f), XK);
+      PT = mma_split(get_split(sm.pw.wg[0], g, lane), XS[g], PT);
+      XK = mma_split(XS[g], get_split(sm.pw.wg[1], g, lane), XK);
       sched_fence();
     }
     const int tcount = min(B, tend - tb);
@@ -346,9 +374,9 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
       nrm += __shfl_xor(nrm, 32);
       if (h == 0) sm.nrm[w][c] = nrm;
     }
-    // The wave's P^T tile for every wave's update (over its own staging tile:
-    // its transpose reads are done).
-    put_tile(sm.xt[w], PT, lane);
+    // The wave's -P^T tile, split, for every wave's update (over its own
+    // staging tile: its transpose reads are done).
+    put_split(sm.xp[w].pt, PT, -1.f, lane);
     lds_barrier();
 
     // The next block's rows (every read of this block's rows is done).
@@ -357,9 +385,8 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
     // ---- 4. A_{b+1} = A_b - P^T X_U^T, and alpha_hat of the block's tokens.
 #pragma unroll
     for (int F = 0; F < 4; ++F) {
-      const f32x16 PF = get_tile(sm.xt[F], lane);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) Acc[F] = mma_split(split_slots(PF, g, -1.f), XS[g], Acc[F]);
+      for (int g = 0; g < 2; ++g) Acc[F] = mma_split(get_split(sm.xp[F].pt, g, lane), XS[g], Acc[F]);
       sched_fence();
     }
     if (c < tcount) {
