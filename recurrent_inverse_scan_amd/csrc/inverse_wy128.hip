@@ -23,9 +23,11 @@
 // Per block:
 //   1. X_U and X_K for the wave's feature block (products over all four of
 //      its tiles), and its share of C = U^T X_U and E = U^T X_K;
-//   2. wave 0 sums the shares and runs the LDL^T elimination of I + C (the
-//      d = 64 kernel's, two pivots per LDS round trip), forming W and G; the
-//      other waves transpose their X_U tile through LDS into X_U^T;
+//   2. the LDL^T elimination of I + C (the d = 64 kernel's, two pivots per
+//      LDS round trip) on three waves in step, one barrier per pivot pair:
+//      wave 0 carries I + C, wave 1 E and wave 2 the identity (giving L^{-1}
+//      E and L^{-1}); then wave 2 forms W and wave 1 G; every wave
+//      transposes its X_U tile through LDS into X_U^T;
 //   3. P^T = W X_U^T and alpha = X_K - X_U G per feature block;
 //   4. A_b -= P^T X_U^T with every wave's P^T tile read from LDS, and
 //      alpha_hat written once the per-token norms are summed over the waves.
@@ -120,9 +122,8 @@ struct Lds128 {
     SplitTile pt;                     // then -P^T of the wave's feature block
   } xp[kWaves];
   float nrm[kWaves][32];              // per-token |alpha|^2 over each wave's features
-  float xk0[64 * 16];                 // wave 0's X_K tile, held here through the elimination
-  float4 sCol[2][2][4];               // elimination (wave 0): pivot columns k, k + 1
-  float4 sRow[kM][2];                 // pivot rows k, k + 1 of (I + C, E, T) at column c
+  float4 sCol[2][2][2][4];            // elimination, by pivot pair parity: columns k, k + 1 of I + C
+  float2 sRow[2][3][kM];              // rows k, k + 1 of I + C, E and T at column c
   float sDinv[kM];                    // 1 / pivot
 };
 
@@ -213,129 +214,145 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
       Cm = mma_split(ub, split_slots(XU, g), Cm);
       Em = mma_split(ub, split_slots(XK, g), Em);
     }
-    if (w > 0) {
-      put_tile(sm.pw.part[0][w - 1], Cm, lane);
-      put_tile(sm.pw.part[1][w - 1], Em, lane);
-    }
+    // Shares for the elimination: C to wave 0 (from waves 1..3), E to wave 1
+    // (from waves 0, 2, 3).
+    if (w > 0) put_tile(sm.pw.part[0][w - 1], Cm, lane);
+    if (w != 1) put_tile(sm.pw.part[1][w == 0 ? 0 : w - 1], Em, lane);
     lds_barrier();
 
-    // ---- 2. Wave 0: the elimination, W and G.  Every wave: X_U^T through
-    // its LDS staging tile, X_U^T[j][f] = X_U[f][j] (X_U is staged first, so
-    // it is not live through the elimination; nor is wave 0's X_K).
+    // ---- 2. The elimination, on three waves: wave 0 carries I + C, wave 1
+    // E and wave 2 T (the identity, becoming L^{-1}); each applies the same
+    // pivots to its matrix.  Every wave: X_U^T through its LDS staging tile,
+    // X_U^T[j][f] = X_U[f][j] (X_U is staged first, so it is not live through
+    // the elimination).
     float* xt = sm.xp[w].xt;
 #pragma unroll
     for (int s = 0; s < 16; ++s) xt[acc_row(s, h) * kXtLd + c] = XU[s];
+    // Lane (c, h) holds column c of its matrix; pivot k sits in lane half
+    // (k >> 2) & 1, slot 4 (k >> 3) + (k & 3).  C and E are summed over the
+    // waves in a fixed order (wave 0's share first).
+    float mt[16];
     if (w == 0) {
-      put_tile(sm.xk0, XK, lane);
-      // C and E summed over the waves in a fixed order.
 #pragma unroll
       for (int j = 0; j < kWaves - 1; ++j) {
-        const f32x16 pc = get_tile(sm.pw.part[0][j], lane), pe = get_tile(sm.pw.part[1][j], lane);
+        const f32x16 pc = get_tile(sm.pw.part[0][j], lane);
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          Cm[s] += pc[s];
-          Em[s] += pe[s];
-        }
+        for (int s = 0; s < 16; ++s) Cm[s] += pc[s];
       }
-      // Lane (c, h) holds column c of I + C, E and T (the identity, becoming
-      // L^{-1}); pivot k sits in lane half (k >> 2) & 1, slot 4 (k >> 3) + (k & 3).
-      float cm[16], em[16], tm[16];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const bool dg = acc_row(s, h) == c;
-        cm[s] = Cm[s] + (dg ? 1.f : 0.f);
-        em[s] = Em[s];
-        tm[s] = dg ? 1.f : 0.f;
+      for (int s = 0; s < 16; ++s) mt[s] = Cm[s] + (acc_row(s, h) == c ? 1.f : 0.f);
+    } else if (w == 1) {
+      const f32x16 p0 = get_tile(sm.pw.part[1][0], lane);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) Em[s] += p0[s];
+#pragma unroll
+      for (int j = 1; j < kWaves - 1; ++j) {
+        const f32x16 pe = get_tile(sm.pw.part[1][j], lane);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) Em[s] += pe[s];
       }
-      const float hf = static_cast<float>(h);
-      // Two pivots per LDS round trip: the lanes get columns k and k + 1 and
-      // rows k and k + 1 as they stood before pivot k, and apply pivot k to
-      // their copies of column and row k + 1 themselves.
 #pragma unroll
-      for (int k = 0; k < kM; k += 2) {
-        const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3);
-        if (c == k || c == k + 1) {
+      for (int s = 0; s < 16; ++s) mt[s] = Em[s];
+    } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sm.sCol[c - k][h][q] = make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
-        }
-        if (h == hk) {
-          sm.sRow[c][0] = make_float4(cm[sk], em[sk], tm[sk], cm[sk + 1]);
-          sm.sRow[c][1] = make_float4(em[sk + 1], tm[sk + 1], 0.f, 0.f);
-        }
-        lds_order();
-        float na[16], nb[16];
+      for (int s = 0; s < 16; ++s) mt[s] = (w == 2 && acc_row(s, h) == c) ? 1.f : 0.f;
+    }
+    const float hf = static_cast<float>(h);
+    const int ws = w < 3 ? w : 2;   // wave 3 follows the barriers only (its rows are not read)
+    // Two pivots per LDS round trip: the lanes get columns k and k + 1 of
+    // I + C and rows k and k + 1 of their own matrix as they stood before
+    // pivot k, and apply pivot k to their copies of column and row k + 1
+    // themselves.  Buffers alternate by pivot pair, so one barrier per pair
+    // orders every wave's reads of a pair before the writes two pairs later.
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = sm.sCol[0][h][q], u4 = sm.sCol[1][h][q];
-          na[4 * q] = v.x; na[4 * q + 1] = v.y; na[4 * q + 2] = v.z; na[4 * q + 3] = v.w;
-          nb[4 * q] = u4.x; nb[4 * q + 1] = u4.y; nb[4 * q + 2] = u4.z; nb[4 * q + 3] = u4.w;
-        }
-        const float2 pa = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[0][hk]) + sk);
-        const float2 pb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[1][hk]) + sk);
-        const float4 r0 = sm.sRow[c][0], r1 = sm.sRow[c][1];
-        float ia = __builtin_amdgcn_rcpf(pa.x);
-        ia = fmaf(fmaf(-pa.x, ia, 1.f), ia, ia);
-        const float a0 = r0.x * ia, a1 = r0.y * ia, a2 = r0.z * ia;
-        const float q0 = fmaf(-pa.y, a0, r0.w), q1 = fmaf(-pa.y, a1, r1.x), q2 = fmaf(-pa.y, a2, r1.y);
-        const float gab = pb.x * ia;
-        const float pk1 = fmaf(-pa.y, gab, pb.y);
-        float ib = __builtin_amdgcn_rcpf(pk1);
-        ib = fmaf(fmaf(-pk1, ib, 1.f), ib, ib);
-        const float b0 = q0 * ib, b1 = q1 * ib, b2 = q2 * ib;
+    for (int k = 0; k < kM; k += 2) {
+      const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3), pp = (k >> 1) & 1;
+      if (w == 0 && (c == k || c == k + 1)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sm.sCol[pp][c - k][h][q] = make_float4(mt[4 * q], mt[4 * q + 1], mt[4 * q + 2], mt[4 * q + 3]);
+      }
+      if (w < 3 && h == hk) sm.sRow[pp][w][c] = make_float2(mt[sk], mt[sk + 1]);
+      lds_barrier();
+      float na[16], nb[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = sm.sCol[pp][0][h][q], u4 = sm.sCol[pp][1][h][q];
+        na[4 * q] = v.x; na[4 * q + 1] = v.y; na[4 * q + 2] = v.z; na[4 * q + 3] = v.w;
+        nb[4 * q] = u4.x; nb[4 * q + 1] = u4.y; nb[4 * q + 2] = u4.z; nb[4 * q + 3] = u4.w;
+      }
+      const float2 pa = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[pp][0][hk]) + sk);
+      const float2 pb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sm.sCol[pp][1][hk]) + sk);
+      const float2 rw = sm.sRow[pp][ws][c];
+      float ia = __builtin_amdgcn_rcpf(pa.x);
+      ia = fmaf(fmaf(-pa.x, ia, 1.f), ia, ia);
+      const float a0 = rw.x * ia;
+      const float q0 = fmaf(-pa.y, a0, rw.y);
+      const float gab = pb.x * ia;
+      const float pk1 = fmaf(-pa.y, gab, pb.y);
+      float ib = __builtin_amdgcn_rcpf(pk1);
+      ib = fmaf(fmaf(-pk1, ib, 1.f), ib, ib);
+      const float b0 = q0 * ib;
+      if (w == 0) {
         guard += (fabsf(pa.x) < eps ? 1 : 0) + (fabsf(pk1) < eps ? 1 : 0);
         asm volatile("" : "+v"(guard));
         if (lane == 0) {
           sm.sDinv[k] = ia;
           sm.sDinv[k + 1] = ib;
         }
-        lds_order();
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const int base = 8 * (s >> 2) + (s & 3);   // row of slot s is base + 4 h
-          if (base + 4 <= k) continue;
-          const float xa = base > k ? na[s] : na[s] * hf;
-          cm[s] = fmaf(-xa, a0, cm[s]);
-          em[s] = fmaf(-xa, a1, em[s]);
-          tm[s] = fmaf(-xa, a2, tm[s]);
-          if (base + 4 > k + 1) {
-            const float nk = fmaf(-na[s], gab, nb[s]);
-            const float xb = base > k + 1 ? nk : nk * hf;
-            cm[s] = fmaf(-xb, b0, cm[s]);
-            em[s] = fmaf(-xb, b1, em[s]);
-            tm[s] = fmaf(-xb, b2, tm[s]);
-          }
-          asm volatile("" : "+v"(cm[s]), "+v"(em[s]), "+v"(tm[s]));
-        }
       }
-      // W = T^T D^{-1} T and G = T^T D^{-1} (F o M), T = L^{-1}, F = L^{-1} E,
-      // M_jt = [j <= r t + r - 1].
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int base = 8 * (s >> 2) + (s & 3);   // row of slot s is base + 4 h
+        if (base + 4 <= k) continue;
+        const float xa = base > k ? na[s] : na[s] * hf;
+        mt[s] = fmaf(-xa, a0, mt[s]);
+        if (base + 4 > k + 1) {
+          const float nk = fmaf(-na[s], gab, nb[s]);
+          const float xb = base > k + 1 ? nk : nk * hf;
+          mt[s] = fmaf(-xb, b0, mt[s]);
+        }
+        asm volatile("" : "+v"(mt[s]));
+      }
+    }
+    // W = T^T D^{-1} T on wave 2 and G = T^T D^{-1} (F o M) on wave 1, T =
+    // L^{-1}, F = L^{-1} E, M_jt = [j <= r t + r - 1]; wave 2 passes T to
+    // wave 1 through the space of E's shares (read before the first pivot).
+    if (w == 2) {
+      f32x16 tv;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) tv[s] = mt[s];
+      put_tile(sm.pw.part[1][0], tv, lane);
+    }
+    lds_barrier();   // T, and the last pivots of D^{-1}
+    if (w == 1 || w == 2) {
       float dv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(sm.sDinv + 8 * q + 4 * h);
         dv[4 * q] = v.x; dv[4 * q + 1] = v.y; dv[4 * q + 2] = v.z; dv[4 * q + 3] = v.w;
       }
-      f32x16 Wm = zero16(), Gm = zero16();
+      f32x16 tmv;
+      if (w == 1) {
+        tmv = get_tile(sm.pw.part[1][0], lane);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) tmv[s] = mt[s];
+      }
       const int jlast = r * c + r - 1;
+      f32x16 Xm = zero16();
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        float td[8], tt[8], ff[8];
+        float td[8], xr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int s = 8 * g + e;
-          td[e] = tm[s] * dv[s];
-          tt[e] = tm[s];
-          ff[e] = acc_row(s, h) <= jlast ? em[s] : 0.f;
+          td[e] = tmv[s] * dv[s];
+          xr[e] = w == 2 ? tmv[s] : (acc_row(s, h) <= jlast ? mt[s] : 0.f);
         }
-        const Split3 TD = split3(td);
-        Wm = mma_split(TD, split3(tt), Wm);
-        Gm = mma_split(TD, split3(ff), Gm);
+        Xm = mma_split(split3(td), split3(xr), Xm);
       }
-      put_split(sm.pw.wg[0], Wm, 1.f, lane);
-      put_split(sm.pw.wg[1], Gm, -1.f, lane);
-      lds_order();
-      XK = get_tile(sm.xk0, lane);
+      put_split(sm.pw.wg[w == 2 ? 0 : 1], Xm, w == 2 ? 1.f : -1.f, lane);
     }
     lds_order();
     f32x16 XT;
