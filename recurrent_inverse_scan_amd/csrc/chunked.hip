@@ -30,6 +30,7 @@
 //                           chain for the sequential fallback
 #include "vla_common.h"
 #include "vla_kernels.h"
+#include "vla_wide.h"
 #include "vla_seq.h"
 
 namespace vla {
@@ -618,11 +619,11 @@ constexpr int kStart128Lds = 128 * 129 * 4 > (16 * rpad<16>() + 8 * 16 * 17) * 8
 __global__ void __launch_bounds__(kStart128Threads)
 vla_chunk_start128_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
                           int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo,
-                          int c_cnt) {
+                          int c_cnt, int c_step) {
   constexpr int D = 128, NT = 16;
   __shared__ double smem[kStart128Lds / 8];
   const int64_t chain = blockIdx.x / c_cnt;
-  const int c = c_lo + static_cast<int>(blockIdx.x % c_cnt);
+  const int c = (c_lo + static_cast<int>(blockIdx.x % c_cnt)) * c_step;
   const int p = period_of(c, o, q);
   const int t = threadIdx.x, lane = t & 63, g = lane >> 4, col = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -727,14 +728,18 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
   return hipGetLastError();
 }
 
+hipError_t launch_chunk_start128(const ChunkPlan& pl, int c_lo, int c_cnt, int c_step, hipStream_t stream) {
+  if (c_cnt <= 0) return hipSuccess;
+  if (pl.d != 128 || c_step < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vla_chunk_start128_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)), dim3(kStart128Threads),
+                     0, stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q, c_lo, c_cnt,
+                     c_step);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_start(const ChunkPlan& pl, int c_lo, int c_cnt, hipStream_t stream) {
   if (c_cnt <= 0) return hipSuccess;
-  if (pl.d == 128) {
-    hipLaunchKernelGGL(vla_chunk_start128_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)),
-                       dim3(kStart128Threads), 0, stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks,
-                       pl.nperiods, pl.o, pl.q, c_lo, c_cnt);
-    return hipGetLastError();
-  }
+  if (pl.d == 128) return launch_chunk_start128(pl, c_lo, c_cnt, 1, stream);
   hipLaunchKernelGGL(vla_chunk_start_kernel, dim3(static_cast<unsigned>(pl.chains * c_cnt)), dim3(kChunkThreads), 0,
                      stream, pl.Gpre, pl.ND, pl.Ac, pl.chain_info, pl.nchunks, pl.nperiods, pl.o, pl.q, c_lo, c_cnt);
   return hipGetLastError();

@@ -130,16 +130,17 @@ struct Lds128 {
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restrict__ ux,
                          const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
-                         int32_t* __restrict__ chain_info, int T, int r, int L, int nchunks, int chunk_lo,
-                         int chunk_cnt, float eps, int nudge_period, int nudge_phase0) {
+                         int32_t* __restrict__ chain_info, int T, int r, int L, int nchunks, int cm, int inv_lo,
+                         int inv_cnt, float eps, int nudge_period, int nudge_phase0) {
   __shared__ __attribute__((aligned(16))) Lds128 sm;
-  const int64_t chain = blockIdx.x / chunk_cnt;
-  const int chunk = chunk_lo + static_cast<int>(blockIdx.x % chunk_cnt);
-  const int tbeg = chunk * L, tend = min(T, tbeg + L);
+  // The workgroup's span: cm consecutive chunks of L tokens from chunk0
+  // (fewer at the end of the chain), starting from chunk0's start inverse.
+  const int64_t chain = blockIdx.x / inv_cnt;
+  const int chunk0 = (inv_lo + static_cast<int>(blockIdx.x % inv_cnt)) * cm;
+  const int tbeg = chunk0 * L, tend = min(T, (chunk0 + cm) * L);
   const int tid = threadIdx.x, lane0 = tid & 63, c0 = lane0 & 31, h0 = lane0 >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int B = kM / r;          // tokens per block
-  const int m = B * r;           // directions per block
 
   // ---- A_b: tile F slot s = A[feat(32 F + acc_row(s, h))][feat(32 w + c)].
   // Slot s = 4 q + e sits at row 32 F + 16 (q >> 1) + 8 h + 4 (q & 1) + e.
@@ -150,7 +151,7 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
   };
   f32x16 Acc[4];
   {
-    const auto ra = make_rsrc(a_start + (chain * nchunks + chunk) * kD * kD, kD * kD * 4);
+    const auto ra = make_rsrc(a_start + (chain * nchunks + chunk0) * kD * kD, kD * kD * 4);
 #pragma unroll
     for (int F = 0; F < 4; ++F)
 #pragma unroll
@@ -160,16 +161,16 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
 
   // Token rows go from HBM straight into LDS: wave w copies k steps 2 w and
   // 2 w + 1 of the block's u and k rows; lane (c, h) takes features
-  // 16 kp + 8 h .. + 7 of direction c (u) and of token c (k).  The buffers
-  // end at the chunk's last token, and lanes with no direction or token read
-  // past the end, so their rows are zero.
+  // 16 kp + 8 h .. + 7 of direction c (u) and of token c (k).  Lanes with no
+  // direction or token in the block (the last block of a chunk may be short)
+  // read past the end of the buffers, so their rows are zero.
   const int64_t row0 = chain * T + tbeg;
   const int ubytes = (tend - tbeg) * r * kD * 2, kbytes = (tend - tbeg) * kD * 2;
   const auto ru = make_rsrc(ux + row0 * r * kD, ubytes);
   const auto rk = make_rsrc(kx + row0 * kD, kbytes);
-  auto copy_tokens = [&](int tb) {
-    const int ou = c0 < m ? (((tb - tbeg) * r + c0) * kD + 8 * h0) * 2 : ubytes;
-    const int ok = c0 < B ? ((tb - tbeg + c0) * kD + 8 * h0) * 2 : kbytes;
+  auto copy_tokens = [&](int tb, int cnt) {
+    const int ou = c0 < cnt * r ? (((tb - tbeg) * r + c0) * kD + 8 * h0) * 2 : ubytes;
+    const int ok = c0 < cnt ? ((tb - tbeg + c0) * kD + 8 * h0) * 2 : kbytes;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int kp = 2 * w + j;
@@ -178,12 +179,21 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
     }
   };
 
-  const bool nudge_last = nudge_period > 0 && tend > tbeg && (nudge_phase0 + tend - 1) % nudge_period == 0;
   int guard = 0;
   bool bad = false;
-  copy_tokens(tbeg);
+  // Blocks run chunk by chunk: a chunk's last block may be short, and the
+  // nudge, when it falls on a chunk's last token (no nudge falls inside a
+  // chunk), is applied before the next chunk's first block.
+  int sub_end = min(tend, tbeg + L);
+  copy_tokens(tbeg, min(B, sub_end - tbeg));
 
-  for (int tb = tbeg; tb < tend; tb += B) {
+  for (int tb = tbeg; tb < tend;) {
+    const int tcount = min(B, sub_end - tb);
+    const bool sub_last = tb + B >= sub_end;
+    const bool last_block = sub_last && sub_end == tend;
+    const bool nudged = sub_last && nudge_period > 0 && (nudge_phase0 + sub_end - 1) % nudge_period == 0;
+    const int tb_next = sub_last ? sub_end : tb + B;
+    const int sub_end_next = sub_last ? min(tend, sub_end + L) : sub_end;
     int c = c0, h = h0;
     asm volatile("" : "+v"(c), "+v"(h));
     const int lane = c + 32 * h;
@@ -374,9 +384,7 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
       XK = mma_split(XS[g], get_split(sm.pw.wg[1], g, lane), XK);
       sched_fence();
     }
-    const int tcount = min(B, tend - tb);
-    const bool last_block = tb + B >= tend;
-    if (nudge_last && last_block && c == tcount - 1) {
+    if (nudged && c == tcount - 1) {
       // The chunk's last token is nudged: alpha = (A + eps I) k.
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
@@ -397,7 +405,7 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
     lds_barrier();
 
     // The next block's rows (every read of this block's rows is done).
-    if (!last_block) copy_tokens(tb + B);
+    if (!last_block) copy_tokens(tb_next, min(B, sub_end_next - tb_next));
 
     // ---- 4. A_{b+1} = A_b - P^T X_U^T, and alpha_hat of the block's tokens.
 #pragma unroll
@@ -418,19 +426,22 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
         *reinterpret_cast<float4*>(dst + feat(32 * w + 4 * (2 * q + h))) = v;
       }
     }
-  }
-
-  // ---- the chunk's end state: nudge, and A_T from the last chunk.
-  if (nudge_last) {
+    // The chunk's end state after a nudge: A + eps I.
+    if (nudged) {
 #pragma unroll
-    for (int F = 0; F < 4; ++F) {   // the diagonal tile (w, w); F stays a constant index
-      if (F == w) {
+      for (int F = 0; F < 4; ++F) {   // the diagonal tile (w, w); F stays a constant index
+        if (F == w) {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) Acc[F][s] += acc_row(s, h0) == c0 ? eps : 0.f;
+          for (int s = 0; s < 16; ++s) Acc[F][s] += acc_row(s, h) == c ? eps : 0.f;
+        }
       }
     }
+    tb = tb_next;
+    sub_end = sub_end_next;
   }
-  if (chunk == nchunks - 1) {
+
+  // ---- A_T from the chain's last chunk.
+  if (chunk0 + cm >= nchunks) {
     const auto rt = make_rsrc(A_T + chain * kD * kD, kD * kD * 4);
 #pragma unroll
     for (int F = 0; F < 4; ++F)
@@ -455,13 +466,13 @@ vla_inverse_wy128_kernel(const uint16_t* __restrict__ kx, const uint16_t* __rest
 }  // namespace
 
 hipError_t launch_inverse_wy128(const ScanArgs& a, const float* a_start, float* alpha_out, int32_t* chain_info,
-                                int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, int chains,
+                                int chunk_len, int nchunks, int cm, int inv_lo, int inv_cnt, int chains,
                                 hipStream_t stream) {
-  if (chunk_cnt <= 0) return hipSuccess;
-  if (a.residual || a.r < 1 || a.r > 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(vla_inverse_wy128_kernel, dim3(static_cast<unsigned>(chains * chunk_cnt)), dim3(kThreads), 0,
+  if (inv_cnt <= 0) return hipSuccess;
+  if (a.residual || a.r < 1 || a.r > 4 || cm < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vla_inverse_wy128_kernel, dim3(static_cast<unsigned>(chains * inv_cnt)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.u), a_start, alpha_out,
-                     a.A_T, chain_info, a.T, a.r, chunk_len, nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period,
+                     a.A_T, chain_info, a.T, a.r, chunk_len, nchunks, cm, inv_lo, inv_cnt, a.eps, a.nudge_period,
                      a.nudge_phase0);
   return hipGetLastError();
 }

@@ -241,6 +241,16 @@ ChunkLayout finish_layout(const vla_scan_params_t* p, ChunkLayout cl, size_t off
   return cl;
 }
 
+// Chunks per workgroup of the d = 128 blocked inverse pass: the largest of
+// 1, 2, 4, 8 that keeps at least 512 spans over all chains (two workgroups
+// per compute unit).  Wide workload (2048 chunks of 512 tokens), ms per
+// scan: spans of one chunk 5.67, two 5.53, four 5.42.
+int inverse_span_chunks(int64_t chains, int nchunks) {
+  int cm = 1;
+  while (cm < 8 && chains * ((nchunks + 2 * cm - 1) / (2 * cm)) >= 512) cm *= 2;
+  return cm;
+}
+
 // Segments of the parallel-in-time state pass: enough to give every chain's
 // segments a compute unit of the 256 (one chain-kernel workgroup fills one),
 // at most 16, and at least two blocks each; 1 keeps one pass per chain.
@@ -437,8 +447,8 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes) 
   const vla_status_t s = check_params(p);
   if (s != VLA_OK) return s;
   if (p->schedule == VLA_SCHEDULE_CHUNKED && !plan_schedule(p).use)
-    return fail(VLA_EUNSUPPORTED, "chunked schedule needs d = 64, T > 0 and a chunk length dividing "
-                                  "nudge_period and t0");
+    return fail(VLA_EUNSUPPORTED, "chunked schedule needs d = 64 (or d = 128 with bf16 storage, the additive "
+                                  "update and no cap), T > 0 and a chunk length dividing nudge_period and t0");
   *bytes = plan_schedule(p).total;
   return VLA_OK;
 }
@@ -615,13 +625,20 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
   // pass keeps every SIMD busy only with all chunks side by side: on a part
   // of them (a segment's) it takes nearly as long, so it is not pipelined
   // with the chain kernel below.
-  if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) return hip_fail(e, "chunk-start launch");
-  // (The inverse pass below writes the residual update's unit gates when
-  // a.residual is set.)
-  if (d == 128)
-    e = vla::launch_inverse_wy128(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
+  if (d == 128) {
+    // The blocked pass at d = 128 takes spans of cm chunks per workgroup
+    // (nudges at chunk ends are applied inside the span): each span needs
+    // one start inverse, a 128 x 128 fp64 inversion (wide workload: 2048
+    // chunks of 512 tokens in 512 spans of four).
+    const int cm = inverse_span_chunks(chains, cl.nchunks);
+    const int nspan = (cl.nchunks + cm - 1) / cm;
+    if ((e = vla::launch_chunk_start128(pl, 0, nspan, cm, stream)) != hipSuccess)
+      return hip_fail(e, "chunk-start launch");
+    e = vla::launch_inverse_wy128(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, cm, 0, nspan,
                                   static_cast<int>(chains), stream);
-  else if (bf16 && p->r == 1 && d == 64)
+  } else if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) {
+    return hip_fail(e, "chunk-start launch");
+  } else if (bf16 && p->r == 1 && d == 64)
     e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
                                static_cast<int>(chains), stream);
   else

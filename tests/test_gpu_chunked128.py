@@ -56,6 +56,36 @@ def test_chunked128_matches_oracle(name, over, L):
     assert (st[:, 1] == 0).all() and (st[:, 3] == -1).all()
 
 
+SPANS = [
+    # (name, overrides, chunk_len): enough chains that the blocked inverse
+    # pass takes spans of four chunks per workgroup, a nudge on every chunk's
+    # last token (so one inside each span), and chunks ending in a short
+    # block (r = 3: blocks of 10 tokens in 32-token chunks; r = 1: blocks of
+    # 32 in 48-token chunks).
+    ("rank3-spans", dict(B=2, H=64, T=512, r=3, nudge_period=32), 32),
+    ("rank1-spans", dict(B=1, H=128, T=768, r=1, nudge_period=48), 48),
+]
+
+
+@pytest.mark.parametrize("name,over,L", SPANS, ids=[c[0] for c in SPANS])
+def test_chunked128_spans_match_oracle(name, over, L):
+    cfg = _cfg(name, **over)
+    C = cfg.B * cfg.H
+    sel = [0, 77, C - 1]
+    _say(f"case {name} chains={C} T={cfg.T} r={cfg.r} P={cfg.nudge_period} L={L}, oracle on {sel}")
+    x = case(cfg, seed=29)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=L)
+    ref = run_oracle(x, cfg, chains=sel)
+    check("gpu-chunked128", cfg, out, ref, chains=sel, say=_say)
+    seq = _gpu(x, cfg, schedule="sequential")
+    for nm, p, q_ in zip("oASn", out[:4], seq[:4]):
+        axes = (-2, -1) if nm in "AS" else (-1,)
+        err = rel_err(p, to64(q_), axes=axes)
+        _say(f"{name}: chunked vs sequential {nm} over all chains: {err}")
+        assert err <= (1e-2 if nm == "o" else 1e-4), (nm, err)
+    assert torch.equal(out[4], seq[4])
+
+
 def test_chunked128_initial_state_and_offset():
     cfg = _cfg("state", B=1, H=2, T=900, r=4, nudge_period=256)
     _say("case initial state, t0 = 512")
