@@ -38,7 +38,6 @@ constexpr int kTile = 32;          // tokens per LDS stage
 constexpr int kLdT16 = kTile + 8;  // bf16 per transposed row ([column][token]): 80 bytes
 constexpr int kLdT32 = kTile + 4;  // fp32 per transposed row: 144 bytes
 constexpr int kLdR16 = kD + 8;     // bf16 per token row: 272 bytes
-constexpr int kLdR32 = kD + 4;     // fp32 per row: 528 bytes
 
 __device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -205,20 +204,50 @@ vla_lin_prefix_kernel(LinPlan lp) {
 //      The normaliser's in-chunk part sum_{s<=t} k_s . q_t comes from
 //      K_st Q^T the same way, summed over s.
 //   3. o = O / (n_c . q + in-chunk part + den_eps).
-// Every stage of 32 tokens (alpha_hat rows in fp32, k rows, v transposed)
-// goes through LDS once for all waves; the next is loaded while the current
-// one multiplies.
+// Every stage of 32 tokens (alpha_hat rows, k rows, v transposed) goes
+// through LDS once for all waves; the next is loaded while the current one
+// multiplies.  The fp32 operands shared by the waves (alpha_hat, and S_c in
+// two halves of 64 rows) are split into their three bf16 terms once, as
+// they enter LDS, instead of by every wave that reads them.
+constexpr int kPieces = kD / 8;     // 16-byte pieces (eight values) per row
+constexpr int kPLd = kPieces + 1;   // padded: consecutive rows start one bank group apart
+
 struct ReadoutStage {
-  float A[kTile * kLdR32];       // alpha_hat rows
+  uint4 As[3][kTile][kPLd];      // alpha_hat rows: [term][token][piece]
   uint16_t K[kTile * kLdR16];    // k rows
   uint16_t Vt[kD * kLdT16];      // v columns
 };
+
+// Split terms of four consecutive values, each term four bf16 (8 bytes);
+// the same terms as split3 gives for them.
+__device__ __forceinline__ void split3_words4(const float4& x, uint2 (&t)[3]) {
+#pragma clang fp contract(off)
+  const float v[4] = {x.x, x.y, x.z, x.w};
+  uint32_t a[4], r[4], c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = __float_as_uint(v[e]);
+    const float rf = v[e] - __uint_as_float(a[e] & 0xffff0000u);
+    r[e] = __float_as_uint(rf);
+    c[e] = __float_as_uint(rf - __uint_as_float(r[e] & 0xffff0000u));
+  }
+  t[0] = make_uint2(pack_hi16(a[0], a[1]), pack_hi16(a[2], a[3]));
+  t[1] = make_uint2(pack_hi16(r[0], r[1]), pack_hi16(r[2], r[3]));
+  t[2] = make_uint2(pack_hi16(c[0], c[1]), pack_hi16(c[2], c[3]));
+}
+__device__ __forceinline__ Split3 get_split(const uint4 (*p)[kPLd], int row, int piece, int stride) {
+  Split3 t;
+  t.t1 = __builtin_bit_cast(bf16x8, p[row][piece]);
+  t.t2 = __builtin_bit_cast(bf16x8, p[stride + row][piece]);
+  t.t3 = __builtin_bit_cast(bf16x8, p[2 * stride + row][piece]);
+  return t;
+}
 
 __device__ __forceinline__ int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 __global__ void __launch_bounds__(kLinThreads)
 vla_lin_readout_kernel(LinPlan lp) {
-  __shared__ __attribute__((aligned(16))) float sS[kD * kLdR32];
+  __shared__ __attribute__((aligned(16))) uint4 sSs[3][64][kPLd];   // half of S_c: [term][row][piece]
   __shared__ __attribute__((aligned(16))) ReadoutStage st[2];
   __shared__ float sDen[8][kTile];
   const int64_t chain = blockIdx.x / lp.ncs;
@@ -260,31 +289,68 @@ vla_lin_readout_kernel(LinPlan lp) {
     rv = load16_or_zero(V + static_cast<int64_t>(tv) * kD + 8 * (tid >> 5), tv < ntok);
   };
   auto store = [&](ReadoutStage& sg) {
-    *reinterpret_cast<uint4*>(&sg.A[(tid >> 5) * kLdR32 + 4 * (tid & 31)]) = ra0;
-    *reinterpret_cast<uint4*>(&sg.A[((tid >> 5) + 16) * kLdR32 + 4 * (tid & 31)]) = ra1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint2 tw[3];
+      const uint4 ra = j ? ra1 : ra0;
+      split3_words4(make_float4(__uint_as_float(ra.x), __uint_as_float(ra.y), __uint_as_float(ra.z),
+                                __uint_as_float(ra.w)), tw);
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+        reinterpret_cast<uint2*>(&sg.As[tm][(tid >> 5) + 16 * j][(tid & 31) >> 1])[tid & 1] = tw[tm];
+    }
     *reinterpret_cast<uint4*>(&sg.K[(tid >> 4) * kLdR16 + 8 * (tid & 15)]) = rk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg.Vt[(8 * (tid >> 5) + e) * kLdT16 + (tid & 31)] = half16(rv, e);
   };
 
-  // S_c into LDS (fp32 rows) and the first stage.
-  if (ntile > 0) load(0);
+  // S_c by halves of 64 rows: each thread splits two pieces of eight values
+  // (row pc / 16, piece pc % 16); the second half's values are loaded while
+  // the first half multiplies.
+  float4 sx[2][2];
+  auto load_half = [&](int hf) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int pc = tid + kLinThreads * j;   // 16-byte piece: row pc / 32, columns 4 (pc % 32) ..
-    const float4 x = *reinterpret_cast<const float4*>(Sc + (pc >> 5) * kD + 4 * (pc & 31));
-    *reinterpret_cast<float4*>(&sS[(pc >> 5) * kLdR32 + 4 * (pc & 31)]) = x;
-  }
+    for (int j = 0; j < 2; ++j) {
+      const int pc = tid + kLinThreads * j;
+      const float* src = Sc + (64 * hf + (pc >> 4)) * kD + 8 * (pc & 15);
+      sx[j][0] = *reinterpret_cast<const float4*>(src);
+      sx[j][1] = *reinterpret_cast<const float4*>(src + 4);
+    }
+  };
+  auto store_half = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pc = tid + kLinThreads * j;
+      const float v[8] = {sx[j][0].x, sx[j][0].y, sx[j][0].z, sx[j][0].w,
+                          sx[j][1].x, sx[j][1].y, sx[j][1].z, sx[j][1].w};
+      const Split3 t = split3(v);
+      sSs[0][pc >> 4][pc & 15] = __builtin_bit_cast(uint4, t.t1);
+      sSs[1][pc >> 4][pc & 15] = __builtin_bit_cast(uint4, t.t2);
+      sSs[2][pc >> 4][pc & 15] = __builtin_bit_cast(uint4, t.t3);
+    }
+  };
+  load_half(0);
+  if (ntile > 0) load(0);
+  store_half();
+  load_half(1);
   if (ntile > 0) store(st[0]);
   __syncthreads();
 
-  // 1. O = Q S_c^T.
+  // 1. O = Q S_c^T, rows i of S_c (column tiles ib of O) by halves.
   f32x16 O[4] = {zero16(), zero16(), zero16(), zero16()};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
+  for (int hf = 0; hf < 2; ++hf) {
+    if (hf == 1) {
+      __syncthreads();   // every wave is done with the first half
+      store_half();
+      __syncthreads();
+    }
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-      O[ib] = mma_split(qop[kk], lds_split8(&sS[(32 * ib + c32) * kLdR32 + 16 * kk + 8 * h]), O[ib]);
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int ib = 2 * hf; ib < 2 * hf + 2; ++ib)
+        O[ib] = mma_split(qop[kk], get_split(sSs[0], 32 * (ib - 2 * hf) + c32, 2 * kk + h, 64), O[ib]);
+  }
 
   // n_c . q_t for this lane's token, over its columns (completed across the
   // lane halves below).
@@ -308,7 +374,7 @@ vla_lin_readout_kernel(LinPlan lp) {
       f32x16 P = zero16(), Pk = zero16();
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        P = mma_split(lds_split8(&sg.A[sm * kLdR32 + 16 * kk + 8 * h]), qop[kk], P);
+        P = mma_split(get_split(sg.As[0], sm, 2 * kk + h, kTile), qop[kk], P);
         Pk = mfma_bf16(lds_bf16x8(&sg.K[c32 * kLdR16 + 16 * kk + 8 * h]), qop[kk], Pk);
       }
       if (tile == rt) {   // causal mask on the diagonal tile: token s > token t
