@@ -58,9 +58,9 @@ CHAIN = {
 
 def chunked_kernel_name(d: int) -> str:
     """The dominant kernel of the time-parallel schedule: the state-chain
-    kernel at d = 64; at d = 128 (no cap, linear state pass) the inverse
-    recurrence per chunk."""
-    return "vla_state_chain_kernel" if d == 64 else "vla_scan_seq_kernel (inverse-only, one chunk per workgroup)"
+    kernel at d = 64; at d = 128 (no cap, linear state pass) the blocked
+    inverse pass over spans of chunks."""
+    return "vla_state_chain_kernel" if d == 64 else "vla_inverse_wy128_kernel (blocked inverse pass)"
 
 
 def seq_kernel_name(d: int, T: int) -> str:

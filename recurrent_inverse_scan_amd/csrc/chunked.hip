@@ -127,13 +127,14 @@ vla_chunk_gram_kernel(const TIn* __restrict__ u, float* __restrict__ G, int T, i
 template <int D>
 __global__ void __launch_bounds__(256)
 vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, double* __restrict__ Gtot,
-                      int64_t chains, int nchunks, int nperiods, int o, int q) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= chains * nperiods * D * D) return;
-  const int e = static_cast<int>(idx % (D * D));
-  const int64_t cp = idx / (D * D);
+                      int nchunks, int nperiods, int o, int q) {
+  // Grid: x = (chain, period), y = slices of 1024 matrix elements, four
+  // consecutive ones per thread (one 16-byte load per chunk), so the bases
+  // below are wave-uniform and each wave keeps 4 KiB of loads in flight.
+  const int64_t cp = blockIdx.x;
   const int p = static_cast<int>(cp % nperiods);
   const int64_t chain = cp / nperiods;
+  const int e = 4 * (blockIdx.y * 256 + threadIdx.x);
   // Chunks of period p: those c with period_of(c) = p.
   int c_lo = 0, c_hi = nchunks;
   if (q > 0) {
@@ -141,26 +142,35 @@ vla_chunk_scan_kernel(const float* __restrict__ G, double* __restrict__ Gpre, do
     c_lo = max(0, base);
     c_hi = min(nchunks, base + q);
   }
-  const float* g = G + chain * nchunks * D * D + e;
-  double* gp = Gpre + chain * nchunks * D * D + e;
-  double acc = 0.0;
-  for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
-    float gv[8];
+  const float* g = G + (chain * nchunks + c_lo) * D * D + e;
+  double* gp = Gpre + (chain * nchunks + c_lo) * D * D + e;
+  const int n = c_hi - c_lo;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int i0 = 0; i0 < n; i0 += 4) {
+    float4 gv[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      gv[k] = 0.f;
-      if (c0 + k < c_hi) gv[k] = g[static_cast<int64_t>(c0 + k) * D * D];
-    }
+    for (int k = 0; k < 4; ++k)
+      gv[k] = i0 + k < n ? *reinterpret_cast<const float4*>(g + static_cast<int64_t>(i0 + k) * D * D)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = c0 + k;
-      if (c < c_hi) {
-        if (c > c_lo) gp[static_cast<int64_t>(c) * D * D] = acc;
-        acc += static_cast<double>(gv[k]);
+    for (int k = 0; k < 4; ++k) {
+      const int i = i0 + k;
+      if (i < n) {
+        if (i > 0) {
+          double2* dst = reinterpret_cast<double2*>(gp + static_cast<int64_t>(i) * D * D);
+          dst[0] = make_double2(acc[0], acc[1]);
+          dst[1] = make_double2(acc[2], acc[3]);
+        }
+        acc[0] += static_cast<double>(gv[k].x);
+        acc[1] += static_cast<double>(gv[k].y);
+        acc[2] += static_cast<double>(gv[k].z);
+        acc[3] += static_cast<double>(gv[k].w);
       }
     }
   }
-  Gtot[(chain * nperiods + p) * D * D + e] = acc;
+  double2* dt = reinterpret_cast<double2*>(Gtot + cp * D * D + e);
+  dt[0] = make_double2(acc[0], acc[1]);
+  dt[1] = make_double2(acc[2], acc[3]);
 }
 
 // ---- (N, D) chain ---------------------------------------------------------
@@ -702,9 +712,8 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
     hipLaunchKernelGGL(vla_chunk_gram128_kernel, dim3(units), dim3(kChunkThreads), 0, stream,
                        static_cast<const uint16_t*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t n = mat * pl.nperiods;
-    hipLaunchKernelGGL(vla_chunk_scan_kernel<128>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                       pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
+    hipLaunchKernelGGL(vla_chunk_scan_kernel<128>, dim3(static_cast<unsigned>(pl.chains * pl.nperiods), 128 * 128 / 1024),
+                       dim3(256), 0, stream, pl.G, pl.Gpre, pl.Gtot, pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(vla_chunk_chain128_kernel, dim3(pl.chains * (128 / kNd128Cols)), dim3(kChunkThreads), 0, stream,
                        pl.Gtot, pl.A_init, pl.ND, pl.nperiods, static_cast<double>(pl.eps));
@@ -718,9 +727,8 @@ hipError_t launch_chunk_prologue(const ChunkPlan& pl, const float* A0, const flo
                        static_cast<const float*>(u), pl.G, pl.T, pl.r, pl.L, pl.nchunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    const int64_t n = static_cast<int64_t>(pl.chains) * pl.nperiods * kD * kD;
-    hipLaunchKernelGGL(vla_chunk_scan_kernel<kD>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                       pl.G, pl.Gpre, pl.Gtot, static_cast<int64_t>(pl.chains), pl.nchunks, pl.nperiods, pl.o, pl.q);
+    hipLaunchKernelGGL(vla_chunk_scan_kernel<kD>, dim3(static_cast<unsigned>(pl.chains * pl.nperiods), kD * kD / 1024),
+                       dim3(256), 0, stream, pl.G, pl.Gpre, pl.Gtot, pl.nchunks, pl.nperiods, pl.o, pl.q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(vla_chunk_chain_kernel, dim3(pl.chains * kNdSplit), dim3(kChunkThreads), 0, stream, pl.Gtot,
