@@ -478,20 +478,21 @@ vla_chunk_gram128_kernel(const uint16_t* __restrict__ u, float* __restrict__ G, 
   const int t_lo = c * L, t_hi = min(T, t_lo + L);
   const int nrows = (t_hi - t_lo) * r;
   const uint16_t* U = u + (chain * T + t_lo) * static_cast<int64_t>(r) * D;
-  // Thread (row lr of the group, 16-byte pieces lp .. lp + 3 of that row).
+  // Thread (row lr of the group, 16-byte pieces lp .. lp + 3 of that row);
+  // loads run two groups ahead of the products (two register sets).
   const int lr = tid & 63, lp = (tid >> 6) * 4;
-  uint4 reg[4];
-  auto load = [&](int k0) {
+  uint4 reg[2][4];
+  auto load = [&](int k0, uint4 (&rg)[4]) {
     const int k = k0 + lr;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      reg[j] = k < nrows ? *reinterpret_cast<const uint4*>(U + static_cast<int64_t>(k) * D + 8 * (lp + j))
-                         : make_uint4(0, 0, 0, 0);
+      rg[j] = k < nrows ? *reinterpret_cast<const uint4*>(U + static_cast<int64_t>(k) * D + 8 * (lp + j))
+                        : make_uint4(0, 0, 0, 0);
   };
-  auto store = [&](uint16_t* dst) {
+  auto store = [&](uint16_t* dst, const uint4 (&rg)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t wv[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
+      const uint32_t wv[4] = {rg[j].x, rg[j].y, rg[j].z, rg[j].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         dst[(8 * (lp + j) + e) * kG128Ld + lr] = static_cast<uint16_t>(e & 1 ? wv[e >> 1] >> 16 : wv[e >> 1]);
@@ -503,12 +504,15 @@ vla_chunk_gram128_kernel(const uint16_t* __restrict__ u, float* __restrict__ G, 
     acc[jb] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int ngroups = (nrows + kG128Rows - 1) / kG128Rows;
   if (ngroups > 0) {
-    load(0);
-    store(ut[0]);
+    load(0, reg[0]);
+    if (ngroups > 1) load(kG128Rows, reg[1]);
+    store(ut[0], reg[0]);
   }
   __syncthreads();
-  for (int gi = 0; gi < ngroups; ++gi) {
-    if (gi + 1 < ngroups) load((gi + 1) * kG128Rows);
+  auto group = [&](int gi, const uint4 (&nxt)[4], uint4 (&fut)[4]) {
+    // Group gi + 1's rows are in nxt; group gi + 2's go into fut, the set
+    // gi's rows came from (stored to LDS in the previous step).
+    if (gi + 2 < ngroups) load((gi + 2) * kG128Rows, fut);
     const uint16_t* cur = ut[gi & 1];
 #pragma unroll
     for (int kk = 0; kk < kG128Rows / 16; ++kk) {
@@ -521,8 +525,12 @@ vla_chunk_gram128_kernel(const uint16_t* __restrict__ u, float* __restrict__ G, 
         acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
       }
     }
-    if (gi + 1 < ngroups) store(ut[(gi + 1) & 1]);
+    if (gi + 1 < ngroups) store(ut[(gi + 1) & 1], nxt);
     __syncthreads();
+  };
+  for (int gi = 0; gi < ngroups; gi += 2) {
+    group(gi, reg[1], reg[0]);
+    if (gi + 1 < ngroups) group(gi + 1, reg[0], reg[1]);
   }
   float* gout = G + (chain * nchunks + c) * D * D;
 #pragma unroll
