@@ -86,6 +86,37 @@ def test_chunked128_spans_match_oracle(name, over, L):
     assert torch.equal(out[4], seq[4])
 
 
+def test_chunked128_spans_ragged_with_state_and_offset():
+    """Spans of four chunks where the chain ends in a short span and a short
+    chunk (T = 1100, 64-token chunks: 18 chunks), from a given initial state
+    at t0 = 192, so the nudges (every 128 tokens) fall at odd chunk ends
+    inside the spans; the oracle on sampled chains, the sequential schedule
+    on all."""
+    cfg = _cfg("spans-ragged", B=2, H=64, T=1100, r=2, nudge_period=128)
+    C, d = cfg.B * cfg.H, cfg.d
+    sel = [1, 64, C - 1]
+    _say(f"case spans-ragged chains={C} T={cfg.T} t0=192, oracle on {sel}")
+    x = case(cfg, seed=30)
+    g = torch.Generator().manual_seed(30)
+    X = torch.randn(C, d, d, generator=g) / d ** 0.5
+    A0 = (0.3 * torch.eye(d) + X @ X.transpose(-1, -2) / 4).reshape(cfg.B, cfg.H, d, d).contiguous()
+    S0 = torch.randn(cfg.B, cfg.H, d, d, generator=g)
+    n0 = torch.rand(cfg.B, cfg.H, d, generator=g)
+    t0 = 192
+    kw = dict(A0=A0.to(DEV), S0=S0.to(DEV), n0=n0.to(DEV), t0=t0)
+    out = _gpu(x, cfg, schedule="chunked", chunk_len=64, **kw)
+    ref = run_oracle(x, cfg, chains=sel, A0=A0.reshape(C, d, d)[sel], S0=S0.reshape(C, d, d)[sel],
+                     n0=n0.reshape(C, d)[sel], t0=t0)
+    check("gpu-chunked128", cfg, out, ref, chains=sel, say=_say)
+    seq = _gpu(x, cfg, schedule="sequential", **kw)
+    for nm, p, q_ in zip("oASn", out[:4], seq[:4]):
+        axes = (-2, -1) if nm in "AS" else (-1,)
+        err = rel_err(p, to64(q_), axes=axes)
+        _say(f"spans-ragged: chunked vs sequential {nm} over all chains: {err}")
+        assert err <= (1e-2 if nm == "o" else 1e-4), (nm, err)
+    assert torch.equal(out[4], seq[4])
+
+
 def test_chunked128_initial_state_and_offset():
     cfg = _cfg("state", B=1, H=2, T=900, r=4, nudge_period=256)
     _say("case initial state, t0 = 512")
