@@ -177,20 +177,25 @@ vla_status_t vla_scan_workspace_size(const vla_scan_params_t* p, size_t* bytes);
  * State is float32 throughout; products accumulate in float32.
  *
  * Schedules.  SEQUENTIAL runs each chain in one workgroup, token after token.
- * CHUNKED (d = 64) splits the tokens into chunks of chunk_len: while no guard
- * fires, A_t is the inverse of the accumulated penalty M_t = A0^{-1} + sum
- * u u^T ("Mathematical Primitives", section 2), so each chunk's starting
- * inverse follows in parallel from per-chunk Gram matrices (in float64,
- * carrying the nudges exactly), the inverse recurrence of every chunk runs in
- * parallel, and a per-chain pass applies the state update, cap and readout.
- * A chain where the guard fires, or whose chunk-start inverse is not
- * positive definite, is recomputed sequentially in the same call, so the
- * result does not depend on the schedule beyond float32 rounding.  The
- * per-chain pass runs in segments of segment_blocks blocks of 64 tokens: a
- * segment's chain kernel overlaps the next segment's preparation and the
- * previous one's readout on the side stream.  CHUNKED
- * needs chunk_len to divide nudge_period (when nonzero) and t0; AUTO uses it
- * for d = 64 when there are few chains and long sequences.
+ * CHUNKED (d = 64; or d = 128 with bf16 storage, the additive update and no
+ * cap) splits the tokens into chunks of chunk_len: while no guard fires, A_t
+ * is the inverse of the accumulated penalty M_t = A0^{-1} + sum u u^T
+ * ("Mathematical Primitives", section 2), so each chunk's starting inverse
+ * follows in parallel from per-chunk Gram matrices (in float64, carrying the
+ * nudges exactly), the inverse recurrence of every chunk runs in parallel
+ * (at d = 128 a workgroup may carry A over a span of consecutive chunks),
+ * and a state pass applies the state update, cap and readout.  A chain where
+ * the guard fires, or whose chunk-start inverse is not positive definite, is
+ * recomputed sequentially in the same call, so the result does not depend on
+ * the schedule beyond float32 rounding.  At d = 64 the state pass runs either
+ * parallel in time (para_segments segments of every chain at once from
+ * guessed starts, corrected by per-chain sweeps until they stop moving) or
+ * per chain in segments of segment_blocks blocks of 64 tokens, a segment's
+ * chain kernel overlapping the next segment's preparation and the previous
+ * one's readout on the side stream; at d = 128, without the cap, it is a
+ * prefix sum over chunks with a chunked readout.  CHUNKED needs chunk_len to
+ * divide nudge_period (when nonzero) and t0; AUTO uses it when there are few
+ * chains and long sequences.
  *
  * With update = RESIDUAL the chunked schedule's inverse pass writes the unit
  * gates, and the state pass uses that, inside a block of 64 tokens, the
