@@ -257,11 +257,12 @@ int inverse_span_chunks(int64_t chains, int nchunks) {
 int para_segments(const vla_scan_params_t* p, int64_t chains, int nblk) {
   if (p->update != VLA_UPDATE_ADDITIVE || chains <= 0) return 1;
   int64_t G = p->para_segments;
-  // By default one workgroup per compute unit, and segments of at least 32
-  // blocks: a pass and a sweep cost about 8 us of launches and setup, so
-  // shorter chains run faster in one pass (32 chains of 32 blocks: 0.48 ms
-  // in one pass against 0.53 with eight segments).
-  if (G == 0) G = std::min<int64_t>(std::min<int64_t>(vla::kMaxParaSegs, 256 / chains), nblk / 32);
+  // By default one workgroup per compute unit, and segments of at least 8
+  // blocks: a pass and a sweep cost a few microseconds of launches and
+  // setup, so short chains gain little from more segments (32 chains of 32
+  // blocks: 0.427 ms in one pass, 0.422 with two segments, 0.403 with four,
+  // 0.424 with eight).
+  if (G == 0) G = std::min<int64_t>(std::min<int64_t>(vla::kMaxParaSegs, 256 / chains), nblk / 8);
   G = std::min<int64_t>(G, std::min<int64_t>(vla::kMaxParaSegs, nblk / 2));
   return G >= 2 ? static_cast<int>(G) : 1;
 }
