@@ -66,8 +66,8 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
                       const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
                       int32_t* __restrict__ chain_info, int T, int L, int nchunks, int chunk_lo, int chunk_cnt,
                       float eps, int nudge_period, int nudge_phase0) {
-  __shared__ float4 sCol[2][2][4];   // pivot columns k, k + 1: [which][lane half][16 rows in slot order]
-  __shared__ float4 sRow[kM][2];     // pivot rows k, k + 1 of (I + C, E, T) at column t
+  __shared__ float4 sColQ[2][16];    // pivot columns k .. k + 3 of I + C: [lane half][slot], component = column
+  __shared__ float4 sRowQ[kM][3];    // pivot rows k .. k + 3 of (I + C, E, T) at column t
   __shared__ __align__(16) float sDinv[kM];     // 1 / pivot
   __shared__ float4 sTok[2][4][kD];   // the block's u and k operands: [u / k][k step][lane]
 
@@ -187,67 +187,96 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
       em[s] = Em[s];
       tm[s] = dg ? 1.f : 0.f;
     }
-    const float hf = static_cast<float>(h);
-    // Two pivots per LDS round trip: the lanes get columns k and k + 1 and
-    // rows k and k + 1 as they stood before pivot k, and apply pivot k to
-    // their copies of column and row k + 1 themselves.
+    // Four pivots per LDS round trip, k = 4 j: the Schur complement of the
+    // pivot block P = S[K][K], K = k .. k + 3, S the current I + C.  With
+    // P = L_P U_P (unit lower L_P; U_P's diagonal holds the four pivots),
+    // column c of each of S, E and T (X below) becomes, for rows i past K,
+    //   X[i][c] - S[i][K] w,   w = P^{-1} X[K][c],
+    // and, in the rows of K, y = L_P^{-1} X[K][c] (what the one-at-a-time
+    // elimination leaves there).  Lanes k .. k + 3 hold the columns S[.][K]
+    // and publish them slot by slot; the rows X[K][c] sit in slots
+    // 4 (k >> 3) .. + 3 of lane half (k >> 2) & 1.  Reading the columns a
+    // slot at a time keeps them out of registers.
 #pragma unroll
-    for (int k = 0; k < kM; k += 2) {
-      const int hk = (k >> 2) & 1, sk = 4 * (k >> 3) + (k & 3);   // pivots k, k + 1: slots sk, sk + 1
-      if (c == k || c == k + 1) {
+    for (int k = 0; k < kM; k += 4) {
+      const int hk = (k >> 2) & 1, sq = 4 * (k >> 3);
+      lds_order();   // the previous block of pivots has read the buffers
+      if (c >= k && c < k + 4) {
+        float* col = reinterpret_cast<float*>(&sColQ[h][0]) + (c - k);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          sCol[c - k][h][q] = make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
+        for (int s = 0; s < 16; ++s) col[4 * s] = cm[s];
       }
       if (h == hk) {
-        sRow[c][0] = make_float4(cm[sk], em[sk], tm[sk], cm[sk + 1]);
-        sRow[c][1] = make_float4(em[sk + 1], tm[sk + 1], 0.f, 0.f);
+        sRowQ[c][0] = make_float4(cm[sq], cm[sq + 1], cm[sq + 2], cm[sq + 3]);
+        sRowQ[c][1] = make_float4(em[sq], em[sq + 1], em[sq + 2], em[sq + 3]);
+        sRowQ[c][2] = make_float4(tm[sq], tm[sq + 1], tm[sq + 2], tm[sq + 3]);
       }
       lds_order();
-      float na[16], nb[16];
+      // P[a][b] = S[k + a][k + b]: slot sq + a of half hk, component b.
+      float P[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = sCol[0][h][q], w = sCol[1][h][q];
-        na[4 * q] = v.x; na[4 * q + 1] = v.y; na[4 * q + 2] = v.z; na[4 * q + 3] = v.w;
-        nb[4 * q] = w.x; nb[4 * q + 1] = w.y; nb[4 * q + 2] = w.z; nb[4 * q + 3] = w.w;
+      for (int a2 = 0; a2 < 4; ++a2) {
+        const float4 v = sColQ[hk][sq + a2];
+        P[a2][0] = v.x; P[a2][1] = v.y; P[a2][2] = v.z; P[a2][3] = v.w;
       }
-      // M[k][k], M[k+1][k] from column k; M[k][k+1], M[k+1][k+1] from column k + 1.
-      const float2 pa = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sCol[0][hk]) + sk);
-      const float2 pb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(sCol[1][hk]) + sk);
-      const float4 r0 = sRow[c][0], r1 = sRow[c][1];
-      float ia = __builtin_amdgcn_rcpf(pa.x);
-      ia = fmaf(fmaf(-pa.x, ia, 1.f), ia, ia);
-      const float a0 = r0.x * ia, a1 = r0.y * ia, a2 = r0.z * ia;
-      // Row k + 1 at column c and pivot k + 1, as pivot k leaves them.
-      const float q0 = fmaf(-pa.y, a0, r0.w), q1 = fmaf(-pa.y, a1, r1.x), q2 = fmaf(-pa.y, a2, r1.y);
-      const float gab = pb.x * ia;
-      const float pk1 = fmaf(-pa.y, gab, pb.y);
-      float ib = __builtin_amdgcn_rcpf(pk1);
-      ib = fmaf(fmaf(-pk1, ib, 1.f), ib, ib);
-      const float b0 = q0 * ib, b1 = q1 * ib, b2 = q2 * ib;
-      guard += (fabsf(pa.x) < eps ? 1 : 0) + (fabsf(pk1) < eps ? 1 : 0);
+      auto rcp = [](float x) {
+        float r = __builtin_amdgcn_rcpf(x);
+        return fmaf(fmaf(-x, r, 1.f), r, r);
+      };
+      // P = L_P U_P, column by column.
+      const float i0 = rcp(P[0][0]);
+      const float l10 = P[1][0] * i0, l20 = P[2][0] * i0, l30 = P[3][0] * i0;
+      const float p11 = fmaf(-l10, P[0][1], P[1][1]), p12 = fmaf(-l10, P[0][2], P[1][2]),
+                  p13 = fmaf(-l10, P[0][3], P[1][3]);
+      const float p21 = fmaf(-l20, P[0][1], P[2][1]), p22 = fmaf(-l20, P[0][2], P[2][2]),
+                  p23 = fmaf(-l20, P[0][3], P[2][3]);
+      const float p31 = fmaf(-l30, P[0][1], P[3][1]), p32 = fmaf(-l30, P[0][2], P[3][2]),
+                  p33 = fmaf(-l30, P[0][3], P[3][3]);
+      const float i1 = rcp(p11);
+      const float l21 = p21 * i1, l31 = p31 * i1;
+      const float q22 = fmaf(-l21, p12, p22), q23 = fmaf(-l21, p13, p23);
+      const float q32 = fmaf(-l31, p12, p32), q33 = fmaf(-l31, p13, p33);
+      const float i2 = rcp(q22);
+      const float l32 = q32 * i2;
+      const float u33 = fmaf(-l32, q23, q33);
+      const float i3 = rcp(u33);
+      guard += (fabsf(P[0][0]) < eps ? 1 : 0) + (fabsf(p11) < eps ? 1 : 0) + (fabsf(q22) < eps ? 1 : 0) +
+               (fabsf(u33) < eps ? 1 : 0);
       asm volatile("" : "+v"(guard));
-      if (lane == 0) {
-        sDinv[k] = ia;
-        sDinv[k + 1] = ib;
+      if (lane == 0) *reinterpret_cast<float4*>(sDinv + k) = make_float4(i0, i1, i2, i3);
+      // y = L_P^{-1} X[K][c], w = U_P^{-1} y, for X = S, E, T.
+      float ys[3][4], ws[3][4];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const float4 rv = sRowQ[c][m];
+        const float y0 = rv.x;
+        const float y1 = fmaf(-l10, y0, rv.y);
+        const float y2 = fmaf(-l21, y1, fmaf(-l20, y0, rv.z));
+        const float y3 = fmaf(-l32, y2, fmaf(-l31, y1, fmaf(-l30, y0, rv.w)));
+        const float w3 = y3 * i3;
+        const float w2 = fmaf(-q23, w3, y2) * i2;
+        const float w1 = fmaf(-p13, w3, fmaf(-p12, w2, y1)) * i1;
+        const float w0 = fmaf(-P[0][3], w3, fmaf(-P[0][2], w2, fmaf(-P[0][1], w1, y0))) * i0;
+        ys[m][0] = y0; ys[m][1] = y1; ys[m][2] = y2; ys[m][3] = y3;
+        ws[m][0] = w0; ws[m][1] = w1; ws[m][2] = w2; ws[m][3] = w3;
       }
-      lds_order();
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const int base = 8 * (s >> 2) + (s & 3);   // row of slot s is base + 4 h
-        if (base + 4 <= k) continue;                // row <= k in both halves
-        // Pivot k on the rows below it.
-        const float xa = base > k ? na[s] : na[s] * hf;
-        cm[s] = fmaf(-xa, a0, cm[s]);
-        em[s] = fmaf(-xa, a1, em[s]);
-        tm[s] = fmaf(-xa, a2, tm[s]);
-        // Pivot k + 1 on the rows below it, with column k + 1 as pivot k left it.
-        if (base + 4 > k + 1) {
-          const float nk = fmaf(-na[s], gab, nb[s]);
-          const float xb = base > k + 1 ? nk : nk * hf;
-          cm[s] = fmaf(-xb, b0, cm[s]);
-          em[s] = fmaf(-xb, b1, em[s]);
-          tm[s] = fmaf(-xb, b2, tm[s]);
+        const int g = s >> 2;   // rows 8 g + 4 h + (s & 3)
+        if (8 * g + 7 < k) continue;   // rows before K in both halves: done
+        const float4 nv = sColQ[h][s];
+        float* xs[3] = {&cm[s], &em[s], &tm[s]};
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          const float upd =
+              fmaf(-nv.w, ws[m][3], fmaf(-nv.z, ws[m][2], fmaf(-nv.y, ws[m][1], fmaf(-nv.x, ws[m][0], *xs[m]))));
+          if (g == (k >> 3)) {
+            // The block of K: its rows in half hk, the rows past it (hk = 0)
+            // or before it (hk = 1) in the other half.
+            *xs[m] = h == hk ? ys[m][s & 3] : (hk == 0 ? upd : *xs[m]);
+          } else {
+            *xs[m] = upd;
+          }
         }
         // Pin the updated values: left alone, the compiler defers these
         // products to the values' next uses and keeps every factor live.
