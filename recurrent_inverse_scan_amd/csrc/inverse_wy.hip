@@ -47,6 +47,14 @@ __host__ __device__ constexpr int feat(int b) { return (b & ~12) | ((b & 4) << 1
 // stores); the hardware completes one wave's LDS operations in issue order.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+// This lane's index, recomputed where it is used (volatile: the compiler may
+// not keep one copy live across the block loop, where it would spill).
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Keeps the scheduler from hoisting the next group's operand splits above the
 // current group's products, which would hold several split operands live at
 // once and exceed the register budget of two waves per SIMD.
@@ -74,13 +82,13 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
   const int64_t chain = blockIdx.x / chunk_cnt;
   const int chunk = chunk_lo + static_cast<int>(blockIdx.x % chunk_cnt);
   const int tbeg = chunk * L, tend = min(T, tbeg + L);
-  const int lane0 = threadIdx.x, c0 = lane0 & 31, h0 = lane0 >> 5;
+  const int lane0 = threadIdx.x, c0 = lane0 & 31, h0 = lane0 >> 5;   // (before the block loop only)
 
   // ---- A_b: tile (F, I) slot s = A[feat(32F + acc_row(s, h))][feat(32I + c)].
   // Slot s = 4 q + e sits at row 32F + 16 (q >> 1) + 8 h + 4 (q & 1) + e: a
   // per-lane byte offset plus a constant one, passed as the buffer access's
   // scalar offset so no per-element address stays live.
-  const int a_voff = (8 * h0 * kD + feat(c0)) * 4;
+  const int a_voff0 = (8 * h0 * kD + feat(c0)) * 4;
   auto a_soff = [](int F, int I, int s) {
     const int q = s >> 2, e = s & 3;
     return ((32 * F + 16 * (q >> 1) + 4 * (q & 1) + e) * kD + 32 * I) * 4;
@@ -94,7 +102,7 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
       for (int I = 0; I < 2; ++I)
 #pragma unroll
         for (int s = 0; s < 16; ++s)
-          Acc[F][I][s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, a_voff, a_soff(F, I, s), 0));
+          Acc[F][I][s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, a_voff0, a_soff(F, I, s), 0));
   }
 
   // Token rows go from HBM straight into LDS (buffer-to-LDS copies, no
@@ -107,7 +115,8 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
   const auto ru = make_rsrc(ux + row0 * kD, (tend - tbeg) * kD * 2);
   const auto rk = make_rsrc(kx + row0 * kD, (tend - tbeg) * kD * 2);
   auto copy_tokens = [&](int tb) {
-    const int vo = ((tb - tbeg + c0) * kD + 8 * h0) * 2;
+    const int ln = fresh_lane();
+    const int vo = ((tb - tbeg + (ln & 31)) * kD + 8 * (ln >> 5)) * 2;
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)&sTok[0][kp][0], 16, vo + 32 * kp, 0, 0, 0);
@@ -123,7 +132,8 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
   for (int tb = tbeg; tb < tend; tb += kM) {
     // Lane indices laundered per block: values derived from them are then
     // recomputed in each block instead of being hoisted and kept live.
-    int c = c0, h = h0;
+    const int ln = fresh_lane();
+    int c = ln & 31, h = ln >> 5;
     asm volatile("" : "+v"(c), "+v"(h));
     const int lane = c + 32 * h;
     // This wave's copies of the block's rows have landed (the compiler does
@@ -376,14 +386,16 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
   }
 
   // ---- the chunk's end state: nudge, and A_T from the last chunk.
+  const int le = fresh_lane(), ce = le & 31, he = le >> 5;
   if (nudge_last) {
 #pragma unroll
     for (int F = 0; F < 2; ++F)
 #pragma unroll
-      for (int s = 0; s < 16; ++s) Acc[F][F][s] += acc_row(s, h0) == c0 ? eps : 0.f;
+      for (int s = 0; s < 16; ++s) Acc[F][F][s] += acc_row(s, he) == ce ? eps : 0.f;
   }
   if (chunk == nchunks - 1) {
     const auto rt = make_rsrc(A_T + chain * kD * kD, kD * kD * 4);
+    const int a_voff = (8 * he * kD + feat(ce)) * 4;
 #pragma unroll
     for (int F = 0; F < 2; ++F)
 #pragma unroll
@@ -396,7 +408,7 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
         }
   }
   const bool wave_bad = __any(bad);
-  if (lane0 == 0) {
+  if (le == 0) {
     int32_t* info = chain_info + chain * 4;
     if (guard > 0) {
       atomicAdd(info + kInfoGuard, guard);
