@@ -320,25 +320,45 @@ __device__ __forceinline__ void gj_panel(d4 (&W)[NT], int w, int g, int col, dou
     d4 inv_t;     // becomes W11^-1
 #pragma unroll
     for (int i = 0; i < 4; ++i) inv_t[i] = (4 * i + g == col) ? 1.0 : 0.0;
+    auto rcp64 = [](double x) {   // the hardware reciprocal refined by one Newton step
+      const double r = __builtin_amdgcn_rcp(x);
+      return fma(r, fma(-x, r, 1.0), r);
+    };
+    // Two pivots per round of cross-lane reads.  Row k of the block sits in
+    // lanes 16 (k % 4) .., slot k / 4 (rows k and k + 1 share the slot); the
+    // lanes fetch columns k and k + 1 of their rows and rows k and k + 1 at
+    // their column as they stand before pivot k, then apply pivot k to their
+    // copies of column and row k + 1 themselves (the same operations, in the
+    // same order, as one pivot at a time).
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      // Row k of the block sits in lanes 16 (k % 4) .., slot k / 4; the
-      // pivot is its entry in column k.
-      const double piv = readlane_d(W[P][k >> 2], 16 * (k & 3) + k);
-      ok = ok && (piv > 0.0) && isfinite(piv);
-      // 1/piv: the hardware reciprocal refined by one Newton step.
-      double inv = __builtin_amdgcn_rcp(piv);
-      inv = fma(inv, fma(-piv, inv, 1.0), inv);
-      double f[4];   // column k of this lane's rows 4 i + g
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = __shfl(W[P][i], 16 * g + k, 64);
-      const double ra = __shfl(W[P][k >> 2], 16 * (k & 3) + col, 64) * inv;
-      const double rb = __shfl(inv_t[k >> 2], 16 * (k & 3) + col, 64) * inv;
+    for (int k = 0; k < 16; k += 2) {
+      const int sk = k >> 2, lk = 16 * (k & 3), lk1 = 16 * ((k + 1) & 3);
+      const double pa = readlane_d(W[P][sk], lk + k), pb = readlane_d(W[P][sk], lk + k + 1);
+      const double pc = readlane_d(W[P][sk], lk1 + k), pd = readlane_d(W[P][sk], lk1 + k + 1);
+      double fk[4], fk1[4];   // columns k and k + 1 of this lane's rows 4 i + g
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool own = 4 * i + g == k;
-        W[P][i] = own ? ra : fma(-f[i], ra, W[P][i]);
-        inv_t[i] = own ? rb : fma(-f[i], rb, inv_t[i]);
+        fk[i] = __shfl(W[P][i], 16 * g + k, 64);
+        fk1[i] = __shfl(W[P][i], 16 * g + k + 1, 64);
+      }
+      const double Rk = __shfl(W[P][sk], lk + col, 64), Rk1 = __shfl(W[P][sk], lk1 + col, 64);
+      const double Ik = __shfl(inv_t[sk], lk + col, 64), Ik1 = __shfl(inv_t[sk], lk1 + col, 64);
+      ok = ok && (pa > 0.0) && isfinite(pa);
+      const double ia = rcp64(pa);
+      const double ra = Rk * ia, rb = Ik * ia;       // row k after pivot k
+      const double bk = pb * ia;                      // its entry in column k + 1
+      const double pd1 = fma(-pc, bk, pd);            // pivot k + 1 after pivot k
+      ok = ok && (pd1 > 0.0) && isfinite(pd1);
+      const double id = rcp64(pd1);
+      const double sa = fma(-pc, ra, Rk1) * id, sb = fma(-pc, rb, Ik1) * id;   // row k + 1 after both
+      const double ra2 = fma(-bk, sa, ra), rb2 = fma(-bk, sb, rb);             // row k after both
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + g;
+        const double fk1p = fma(-fk[i], bk, fk1[i]);   // column k + 1 after pivot k
+        const double w1 = fma(-fk[i], ra, W[P][i]), v1 = fma(-fk[i], rb, inv_t[i]);
+        W[P][i] = row == k ? ra2 : (row == k + 1 ? sa : fma(-fk1p, sa, w1));
+        inv_t[i] = row == k ? rb2 : (row == k + 1 ? sb : fma(-fk1p, sb, v1));
       }
     }
     // R = W11^-1 W[panel rows] tile by tile: the A operand of k step kk is
@@ -377,7 +397,7 @@ __device__ __forceinline__ void gj_panel(d4 (&W)[NT], int w, int g, int col, dou
   __syncthreads();   // sR and sI are rewritten by the next panel
 }
 
-__global__ void __launch_bounds__(kChunkThreads)
+__global__ void __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(2)))
 vla_chunk_start_kernel(const double* __restrict__ Gpre, const double* __restrict__ ND, float* __restrict__ Ac,
                        int32_t* __restrict__ chain_info, int nchunks, int nperiods, int o, int q, int c_lo, int c_cnt) {
   // 66.6 KiB of LDS: N_p and Gpre_c rows (padded); after the product the
