@@ -1,5 +1,5 @@
 // Inverse pass of the time-parallel schedule in blocked form (d = 64, one
-// direction per token, bf16 storage), on the gfx950 matrix cores.
+// direction per token, bf16 or fp32 storage), on the gfx950 matrix cores.
 //
 // Method ("Mathematical Primitives", section 2: rank-1 Sherman-Morrison
 // tracking of A = M^{-1}; section 4: alpha_t = A_t k_t; "Variational Linear
@@ -23,7 +23,8 @@
 // 16-byte load, while accumulator tiles feed the products directly (A is
 // symmetric, so a tile read as the A operand is the block it transposes to).
 // Products with fp32 operands use three-term bf16 splits (fp32-grade); u and
-// k enter exactly.  The LDL^T elimination of I + C, carried along on E =
+// k enter exactly: as they are with bf16 storage, as three-term splits (which
+// represent an fp32 value exactly) with fp32 storage.  The LDL^T elimination of I + C, carried along on E =
 // U^T A_b K and on the identity (giving L^{-1} E and L^{-1}), runs in the
 // wave over 32 pivots, two per round trip: pivot columns and rows reach
 // every lane through LDS.
@@ -68,16 +69,27 @@ __device__ __forceinline__ float frag_elem(const uint4& f, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-template <bool UNIT_GATE>
+// The eight fp32 values of a 16-feature operand fragment (two 16-byte
+// pieces) as a three-term split.
+__device__ __forceinline__ Split3 split_pieces(const float4& a, const float4& b) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split3(v);
+}
+
+// F32: u and k stored as fp32 (else bf16).
+template <bool UNIT_GATE, bool F32>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restrict__ ux,
+vla_inverse_wy_kernel(const void* __restrict__ kx, const void* __restrict__ ux,
                       const float* __restrict__ a_start, float* __restrict__ alpha_out, float* __restrict__ A_T,
                       int32_t* __restrict__ chain_info, int T, int L, int nchunks, int chunk_lo, int chunk_cnt,
                       float eps, int nudge_period, int nudge_phase0) {
   __shared__ float4 sColQ[2][16];    // pivot columns k .. k + 3 of I + C: [lane half][slot], component = column
   __shared__ float4 sRowQ[kM][3];    // pivot rows k .. k + 3 of (I + C, E, T) at column t
   __shared__ __align__(16) float sDinv[kM];     // 1 / pivot
-  __shared__ float4 sTok[2][4][kD];   // the block's u and k operands: [u / k][k step][lane]
+  constexpr int kEB = F32 ? 4 : 2;        // bytes per stored element
+  constexpr int kPieces = F32 ? 2 : 1;    // 16-byte pieces per lane and k step
+  __shared__ float4 sTok[2][4][kPieces][kD];   // the block's u and k operands: [u / k][k step][piece][lane]
+  __shared__ float sKn[F32 && UNIT_GATE ? kD : 1];   // per lane: its half of |k|^2 (fp32 storage)
 
   const int64_t chain = blockIdx.x / chunk_cnt;
   const int chunk = chunk_lo + static_cast<int>(blockIdx.x % chunk_cnt);
@@ -107,21 +119,25 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 
   // Token rows go from HBM straight into LDS (buffer-to-LDS copies, no
   // registers held while they fly): lane (c, h) takes features 16 kappa +
-  // 8 h .. + 7 of token c of the block for k step kappa.  The buffers end at
+  // 8 h .. + 7 of token c of the block for k step kappa (fp32: in two
+  // 16-byte pieces).  The buffers end at
   // the chunk's last token, so rows past it read as zero.
   // Both buffers start at the chunk's first token, so their extents and
   // offsets stay below one chunk (at most 512 tokens) whatever T is.
   const int64_t row0 = chain * T + tbeg;
-  const auto ru = make_rsrc(ux + row0 * kD, (tend - tbeg) * kD * 2);
-  const auto rk = make_rsrc(kx + row0 * kD, (tend - tbeg) * kD * 2);
+  const auto ru = make_rsrc(static_cast<const char*>(ux) + row0 * kD * kEB, (tend - tbeg) * kD * kEB);
+  const auto rk = make_rsrc(static_cast<const char*>(kx) + row0 * kD * kEB, (tend - tbeg) * kD * kEB);
   auto copy_tokens = [&](int tb) {
     const int ln = fresh_lane();
-    const int vo = ((tb - tbeg + (ln & 31)) * kD + 8 * (ln >> 5)) * 2;
+    const int vo = ((tb - tbeg + (ln & 31)) * kD + 8 * (ln >> 5)) * kEB;
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)&sTok[0][kp][0], 16, vo + 32 * kp, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&sTok[1][kp][0], 16, vo + 32 * kp, 0, 0, 0);
-    }
+    for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+      for (int pc = 0; pc < kPieces; ++pc) {
+        const int off = vo + 16 * kEB * kp + 16 * pc;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void*)&sTok[0][kp][pc][0], 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&sTok[1][kp][pc][0], 16, off, 0, 0, 0);
+      }
   };
 
   const bool nudge_last = nudge_period > 0 && tend > tbeg && (nudge_phase0 + tend - 1) % nudge_period == 0;
@@ -139,13 +155,41 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
     // This wave's copies of the block's rows have landed (the compiler does
     // not order LDS reads after buffer-to-LDS copies by itself).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // bf16: the operands stay in registers for the block.  fp32: they are
+    // split from LDS where they are used (the next block's copy starts only
+    // after the last such use; the last block's rows stay for the nudge).
     uint4 uf[4], kf[4];
+    if constexpr (!F32) {
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      const float4 a = sTok[0][kp][lane], b = sTok[1][kp][lane];
-      uf[kp] = make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
-      kf[kp] = make_uint4(__float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w));
+      for (int kp = 0; kp < 4; ++kp) {
+        const float4 a = sTok[0][kp][0][lane], b = sTok[1][kp][0][lane];
+        uf[kp] = make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
+        kf[kp] = make_uint4(__float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w));
+      }
+    } else if constexpr (UNIT_GATE) {
+      // The gate's |k|^2 before the rows are overwritten, kept in LDS.
+      float kn = 0.f;
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const float4 b = sTok[1][kp][pc][lane];
+          kn = fmaf(b.x, b.x, kn); kn = fmaf(b.y, b.y, kn); kn = fmaf(b.z, b.z, kn); kn = fmaf(b.w, b.w, kn);
+        }
+      sKn[lane] = kn;
     }
+    auto u_op = [&](int kp) {
+      if constexpr (F32)
+        return split_pieces(sTok[0][kp][0][lane], sTok[0][kp][1][lane]);
+      else
+        return __builtin_bit_cast(bf16x8, uf[kp]);
+    };
+    auto k_op = [&](int kp) {
+      if constexpr (F32)
+        return split_pieces(sTok[1][kp][0][lane], sTok[1][kp][1][lane]);
+      else
+        return __builtin_bit_cast(bf16x8, kf[kp]);
+    };
     // ---- X_U = A U, X_K = A K (rows: basis features, columns: tokens) and
     // X_U^T (rows: tokens, columns: basis features).
     f32x16 XU[2] = {zero16(), zero16()}, XK[2] = {zero16(), zero16()}, XUT[2] = {zero16(), zero16()};
@@ -154,7 +198,7 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int kp = 2 * F + g;
-        const bf16x8 ub = __builtin_bit_cast(bf16x8, uf[kp]), kb = __builtin_bit_cast(bf16x8, kf[kp]);
+        const auto ub = u_op(kp), kb = k_op(kp);
 #pragma unroll
         for (int I = 0; I < 2; ++I) {
           const Split3 af = split_slots(Acc[F][I], g);
@@ -171,7 +215,7 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
     for (int I = 0; I < 2; ++I)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const bf16x8 ub = __builtin_bit_cast(bf16x8, uf[2 * I + g]);
+        const auto ub = u_op(2 * I + g);
         Cm = mma_split(ub, split_slots(XU[I], g), Cm);
         Em = mma_split(ub, split_slots(XK[I], g), Em);
         sched_fence();
@@ -181,6 +225,8 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
     // registers; the last block keeps them for the nudge).
     if (tb + kM < tend) {
       lds_order();
+      // fp32: this block's row reads have returned before the rows are overwritten.
+      if constexpr (F32) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       copy_tokens(tb + kM);
     }
 
@@ -341,7 +387,14 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 #pragma unroll
       for (int I = 0; I < 2; ++I)
 #pragma unroll
-        for (int s = 0; s < 16; ++s) XK[I][s] = fmaf(eps, frag_elem(kf[2 * I + (s >> 3)], s & 7), XK[I][s]);
+        for (int s = 0; s < 16; ++s) {
+          float kv;
+          if constexpr (F32)
+            kv = reinterpret_cast<const float*>(&sTok[1][2 * I + (s >> 3)][(s & 7) >> 2][lane])[s & 3];
+          else
+            kv = frag_elem(kf[2 * I + (s >> 3)], s & 7);
+          XK[I][s] = fmaf(eps, kv, XK[I][s]);
+        }
     }
     float nrm = 0.f;
 #pragma unroll
@@ -353,10 +406,14 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
     if constexpr (UNIT_GATE) {
       // The residual update's gate: the unit vector along A k_hat, k_hat = k / |k|.
       float kn = 0.f;
+      if constexpr (F32) {
+        kn = sKn[lane];
+      } else {
 #pragma unroll
-      for (int kp = 0; kp < 4; ++kp)
+        for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kn = fmaf(frag_elem(kf[kp], e), frag_elem(kf[kp], e), kn);
+          for (int e = 0; e < 8; ++e) kn = fmaf(frag_elem(kf[kp], e), frag_elem(kf[kp], e), kn);
+      }
       kn += __shfl_xor(kn, 32);
       const float kinv = 1.f / fmaxf(sqrtf(kn), 1e-12f);
       ascale = kinv / fmaxf(kinv * sqrtf(nrm), 1e-12f);
@@ -421,17 +478,14 @@ vla_inverse_wy_kernel(const uint16_t* __restrict__ kx, const uint16_t* __restric
 }  // namespace
 
 hipError_t launch_inverse_wy(const ScanArgs& a, const float* a_start, float* alpha_out, int32_t* chain_info,
-                             int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, int chains, hipStream_t stream) {
+                             int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, bool bf16, int chains,
+                             hipStream_t stream) {
   if (chunk_cnt <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(chains * chunk_cnt));
-  if (a.residual)
-    hipLaunchKernelGGL(vla_inverse_wy_kernel<true>, grid, dim3(64), 0, stream, static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.u), a_start, alpha_out, a.A_T, chain_info, a.T, chunk_len,
-                       nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period, a.nudge_phase0);
-  else
-    hipLaunchKernelGGL(vla_inverse_wy_kernel<false>, grid, dim3(64), 0, stream, static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.u), a_start, alpha_out, a.A_T, chain_info, a.T, chunk_len,
-                       nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period, a.nudge_phase0);
+  auto kernel = a.residual ? (bf16 ? vla_inverse_wy_kernel<true, false> : vla_inverse_wy_kernel<true, true>)
+                           : (bf16 ? vla_inverse_wy_kernel<false, false> : vla_inverse_wy_kernel<false, true>);
+  hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a.k, a.u, a_start, alpha_out, a.A_T, chain_info, a.T,
+                     chunk_len, nchunks, chunk_lo, chunk_cnt, a.eps, a.nudge_period, a.nudge_phase0);
   return hipGetLastError();
 }
 

@@ -639,8 +639,8 @@ vla_status_t vla_scan_forward(const vla_scan_params_t* p, const void* q, const v
                                   static_cast<int>(chains), stream);
   } else if ((e = vla::launch_chunk_start(pl, 0, cl.nchunks, stream)) != hipSuccess) {
     return hip_fail(e, "chunk-start launch");
-  } else if (bf16 && p->r == 1 && d == 64)
-    e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks,
+  } else if (p->r == 1 && d == 64)
+    e = vla::launch_inverse_wy(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, bf16,
                                static_cast<int>(chains), stream);
   else
     e = vla::launch_scan_inverse_chunks(a, pl.Ac, pl.alpha, pl.chain_info, cl.L, cl.nchunks, 0, cl.nchunks, d, bf16,

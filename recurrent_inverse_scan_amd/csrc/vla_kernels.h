@@ -187,10 +187,11 @@ hipError_t launch_scan_inverse_chunks(const ScanArgs& a, const float* a_start, f
                                       int32_t* chain_info, int chunk_len, int nchunks, int chunk_lo, int chunk_cnt,
                                       int d, bool bf16, int chains, hipStream_t stream);
 
-// The same pass in blocked form on the matrix cores (inverse_wy.hip): bf16
-// storage, d = 64, r = 1 only.
+// The same pass in blocked form on the matrix cores (inverse_wy.hip): d = 64,
+// r = 1 only, bf16 or fp32 storage.
 hipError_t launch_inverse_wy(const ScanArgs& a, const float* a_start, float* alpha_out, int32_t* chain_info,
-                             int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, int chains, hipStream_t stream);
+                             int chunk_len, int nchunks, int chunk_lo, int chunk_cnt, bool bf16, int chains,
+                             hipStream_t stream);
 
 hipError_t launch_project_u(int64_t rows, int d, int r, bool in_bf16, bool out_bf16, const void* W,
                             const void* kraw, void* u, hipStream_t stream);

@@ -280,11 +280,13 @@ CHUNKED = [
     ("f32-rank3", dict(B=1, H=2, T=300, r=3, in_dtype="f32", nudge_period=32, s_cap=None), 32),
     ("bf16-rank4-nonudge", dict(B=1, H=2, T=333, r=4, in_dtype="bf16", nudge_period=0, s_cap=None), 64),
     ("f32-cap-binding", dict(B=1, H=2, T=513, in_dtype="f32", nudge_period=0, s_cap=3.0), 128),
-    # bf16 with one direction per token takes the blocked (32-token) inverse
-    # pass: a chunk of 48 ends in a half block, and the last chunk is ragged.
+    # One direction per token takes the blocked (32-token) inverse pass: a
+    # chunk of 48 ends in a half block, and the last chunk is ragged.
     ("bf16-blocked-half-block", dict(B=1, H=2, T=500, in_dtype="bf16", nudge_period=96, s_cap=30.0), 48),
+    ("f32-blocked-half-block", dict(B=1, H=2, T=500, in_dtype="f32", nudge_period=96, s_cap=30.0), 48),
     # Long chunks with the nudge on every other chunk's last token.
     ("bf16-blocked-long-chunks", dict(B=1, H=2, T=2100, in_dtype="bf16", nudge_period=1024, s_cap=None), 512),
+    ("f32-blocked-long-chunks", dict(B=1, H=2, T=2100, in_dtype="f32", nudge_period=1024, s_cap=None), 512),
 ]
 
 
