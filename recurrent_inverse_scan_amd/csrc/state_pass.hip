@@ -1197,8 +1197,19 @@ __global__ void __launch_bounds__(1024) vla_para_init_kernel(ParaPlan pp, StateP
   if (tid == 0) pp.conv[c] = 0;
   const int sg = tid >> 6, f = tid & 63;
   if (sg < G) {
+    // Eight loads in flight at a time, added in block order.
+    const float* ks = pl.Kmat + c * pl.nblk * kPackFloats + kPackKs + f;
+    const int be = pp.bnd[sg + 1];
     float acc = 0.f;
-    for (int b = pp.bnd[sg]; b < pp.bnd[sg + 1]; ++b) acc += pl.Kmat[(c * pl.nblk + b) * kPackFloats + kPackKs + f];
+    int b = pp.bnd[sg];
+    for (; b + 8 <= be; b += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = ks[static_cast<int64_t>(b + i) * kPackFloats];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += x[i];
+    }
+    for (; b < be; ++b) acc += ks[static_cast<int64_t>(b) * kPackFloats];
     part[sg][f] = acc;
   }
   __syncthreads();
@@ -1444,9 +1455,15 @@ __global__ void __launch_bounds__(kSweepThreads) vla_para_sweep_kernel(ParaPlan 
 __global__ void __launch_bounds__(256) vla_para_stats_kernel(ParaPlan pp, const float* __restrict__ S_T,
                                                              const float* __restrict__ n_T, int32_t* __restrict__ stats) {
   __shared__ int bad_any;
+  __shared__ int s_fires[kMaxParaSegs], s_first[kMaxParaSegs];
   const int64_t c = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid == 0) bad_any = 0;
+  if (tid < pp.nseg) {   // the segments' records, read in parallel
+    const float* rc = pp.rec + (c * pp.nseg + tid) * 4;
+    s_fires[tid] = static_cast<int>(rc[1]);
+    s_first[tid] = rc[2] >= 0.f ? static_cast<int>(rc[2]) : -1;
+  }
   __syncthreads();
   bool bad = false;
   for (int e = tid; e < kD * kD; e += 256) bad |= !isfinite(S_T[c * kD * kD + e]);
@@ -1456,9 +1473,8 @@ __global__ void __launch_bounds__(256) vla_para_stats_kernel(ParaPlan pp, const 
   if (tid == 0) {
     int fires = 0, first = -1;
     for (int j = 0; j < pp.nseg; ++j) {
-      const float* rc = pp.rec + (c * pp.nseg + j) * 4;
-      fires += static_cast<int>(rc[1]);
-      if (first < 0 && rc[2] >= 0.f) first = static_cast<int>(rc[2]);
+      fires += s_fires[j];
+      if (first < 0) first = s_first[j];
     }
     int32_t* st = stats + c * 4;
     st[0] = pp.chain_info[c * 4 + kInfoGuard];
